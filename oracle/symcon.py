@@ -1,0 +1,177 @@
+"""Symmetric contraction, degrees 1..3 (oracle side).
+
+What is computed (e3nn-course Lesson 12a, section 21.4.1, and the
+cuequivariance-torch skill document, "Other operations and layers"): the
+descriptor ``symmetric_contraction(irreps_in, irreps_out, [1, 2, 3])`` has one
+row per degree nu, ``[]*a[u]*b[u]...*b[u] -> C[u]`` with nu copies of b: every
+channel u is contracted with itself only, the weights ``a`` carry the channel
+index, and the weights are chosen per atom by an element (species) index.
+Multiplicities must be uniform.  The degrees are summed into one output.
+
+For one channel u let v in R^n be the components of all input blocks of that
+channel, block after block (n = sum 2l+1; 16 for 0e+1o+2e+3o).  For degree nu
+and output irrep L (each output block), a basis {U^{nu,L,k}} of the
+symmetric equivariant maps Sym^nu(R^n) -> R^{2L+1} is built by this
+procedure (the pages fix no basis; this is the reading used on both sides):
+
+1. candidates, in this order: ordered block tuples (b1..bnu) in
+   lexicographic order; for nu = 3 also the intermediate L12 ascending;
+   kept when the parities multiply to the parity of L and the triangle
+   rules hold.  The candidate tensor is the real coupling embedded at the
+   blocks' component offsets: nu=1 the identity on a block of type L,
+   nu=2 C(l1,l2,L), nu=3 sum_a C(l1,l2,L12)[i,j,a] C(L12,l3,L)[a,k,M]
+   (C from :func:`oracle.cg.real_cg`);
+2. symmetrise over all nu! permutations of the nu input slots;
+3. accept it when its Gram-Schmidt residual against the tensors accepted so
+   far exceeds 1e-8 of its norm; the accepted tensor is the symmetrised
+   candidate itself (not the residual);
+4. scale it so that its output components are orthonormal:
+   sum_{m1..mnu} U[m.., M] U[m.., M'] = delta_MM'.
+
+Then  out[a, L block, M, u] = sum_nu sum_k w[species_a, woff(nu, L, k) + u]
+            * sum_{m1..mnu} U^{nu,L,k}[m1..mnu, M] * prod_i v_a,u[m_i],
+weight segments ordered by nu ascending, then output block, then k, each
+``mul`` channels wide.
+"""
+
+import itertools
+import math
+
+import numpy as np
+
+from . import irreps as ir
+from .cg import real_cg
+from .layout import split_blocks, join_blocks
+
+ACCEPT_TOL = 1e-8
+
+
+def _embed_candidates(blocks, nu, L, pL):
+    """Yield candidate tensors of shape (n,)*nu + (2L+1,) in the canonical order."""
+    offs = np.cumsum([0] + [2 * l + 1 for _, l, _ in blocks])
+    n = offs[-1]
+    nb = len(blocks)
+    for tup in itertools.product(range(nb), repeat=nu):
+        ls = [blocks[b][1] for b in tup]
+        par = 1
+        for b in tup:
+            par *= blocks[b][2]
+        if par != pL:
+            continue
+        if nu == 1:
+            if ls[0] != L:
+                continue
+            t = np.zeros((n, 2 * L + 1))
+            t[offs[tup[0]]:offs[tup[0]] + 2 * L + 1, :] = np.eye(2 * L + 1)
+            yield t
+        elif nu == 2:
+            if not abs(ls[0] - ls[1]) <= L <= ls[0] + ls[1]:
+                continue
+            t = np.zeros((n, n, 2 * L + 1))
+            t[offs[tup[0]]:offs[tup[0]] + 2 * ls[0] + 1,
+              offs[tup[1]]:offs[tup[1]] + 2 * ls[1] + 1, :] = real_cg(ls[0], ls[1], L)
+            yield t
+        elif nu == 3:
+            for l12 in range(abs(ls[0] - ls[1]), ls[0] + ls[1] + 1):
+                if not abs(l12 - ls[2]) <= L <= l12 + ls[2]:
+                    continue
+                c = np.einsum("ija,akM->ijkM", real_cg(ls[0], ls[1], l12), real_cg(l12, ls[2], L))
+                t = np.zeros((n, n, n, 2 * L + 1))
+                t[offs[tup[0]]:offs[tup[0]] + 2 * ls[0] + 1,
+                  offs[tup[1]]:offs[tup[1]] + 2 * ls[1] + 1,
+                  offs[tup[2]]:offs[tup[2]] + 2 * ls[2] + 1, :] = c
+                yield t
+        else:
+            raise ValueError("degrees 1..3 only")
+
+
+def _symmetrize(t, nu):
+    perms = list(itertools.permutations(range(nu)))
+    s = np.zeros_like(t)
+    for p in perms:
+        s += np.transpose(t, p + (nu,))
+    return s / len(perms)
+
+
+def coupling_basis(blocks, nu, L, pL):
+    """The accepted, scaled basis tensors for degree nu and output type (L, pL)."""
+    accepted = []     # as returned
+    ortho = []        # orthonormal (Frobenius) copy of their span, for the test
+    for t in _embed_candidates(blocks, nu, L, pL):
+        s = _symmetrize(t, nu)
+        ns = np.linalg.norm(s)
+        if ns < 1e-12:
+            continue
+        r = s.copy()
+        for q in ortho:
+            r -= np.vdot(q, r) * q
+        nr = np.linalg.norm(r)
+        if nr <= ACCEPT_TOL * ns:
+            continue
+        ortho.append(r / nr)
+        accepted.append(s * (math.sqrt(2 * L + 1) / ns))
+    return accepted
+
+
+class SymmetricContraction:
+    def __init__(self, irreps_in, irreps_out, degrees=(1, 2, 3)):
+        self.inp = ir.parse(irreps_in)
+        self.out = ir.parse(irreps_out)
+        muls = {m for m, _, _ in self.inp} | {m for m, _, _ in self.out}
+        if len(muls) != 1:
+            raise ValueError("symmetric contraction needs one multiplicity for all blocks")
+        self.mul = muls.pop()
+        self.degrees = tuple(degrees)
+        self.n = sum(2 * l + 1 for _, l, _ in self.inp)
+        # basis[(nu, out block)] = list of U tensors
+        self.basis = {}
+        self.segments = []    # (nu, out block, k) in weight order
+        for nu in self.degrees:
+            for ob, (_, L, pL) in enumerate(self.out):
+                us = coupling_basis(self.inp, nu, L, pL)
+                self.basis[(nu, ob)] = us
+                self.segments.extend((nu, ob, k) for k in range(len(us)))
+        self.weight_numel = self.mul * len(self.segments)
+        self.dim_in = ir.dim(self.inp)
+        self.dim_out = ir.dim(self.out)
+
+    def counts(self):
+        """{(nu, out block): K} numbers of couplings."""
+        return {key: len(v) for key, v in self.basis.items()}
+
+    def num_paths(self, nu):
+        """Non-zero entries of the coupling tensors of degree nu, summed over
+        output blocks and couplings (each (k, m1..mnu, M) is one path)."""
+        return int(sum(np.count_nonzero(np.abs(u) > 1e-12)
+                       for (d, _), us in self.basis.items() if d == nu for u in us))
+
+    def weight_fan_in(self):
+        """Per weight column: K of its (nu, output block)."""
+        k = self.counts()
+        return np.concatenate([np.full(self.mul, k[(nu, ob)]) for nu, ob, _ in self.segments]) \
+            if self.segments else np.zeros(0)
+
+    def eval(self, x, species, w, layout="ir_mul", absolute=False):
+        """x [n_atoms, dim_in] in ``layout``; species [n_atoms] integers;
+        w [num_elements, weight_numel].  Returns float64 [n_atoms, dim_out]."""
+        x = np.asarray(x, dtype=np.float64)
+        w = np.asarray(w, dtype=np.float64)
+        species = np.asarray(species, dtype=np.int64)
+        if absolute:
+            x, w = np.abs(x), np.abs(w)
+        v = np.concatenate(split_blocks(x, self.inp, layout), axis=1)   # [A, n, mul]
+        wa = w[species]                                                  # [A, numel]
+        parts = [np.zeros((x.shape[0], 2 * L + 1, self.mul)) for _, L, _ in self.out]
+        for s_idx, (nu, ob, k) in enumerate(self.segments):
+            u = self.basis[(nu, ob)][k]
+            if absolute:
+                u = np.abs(u)
+            if nu == 1:
+                p = np.einsum("mM,amu->aMu", u, v)
+            elif nu == 2:
+                p = np.einsum("mnM,amu,anu->aMu", u, v, v, optimize=True)
+            else:
+                p = np.einsum("mnoM,amu,anu,aou->aMu", u, v, v, v, optimize=True)
+            ws = wa[:, s_idx * self.mul:(s_idx + 1) * self.mul]
+            parts[ob] += p * ws[:, None, :]
+        return join_blocks(parts, layout)
