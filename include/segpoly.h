@@ -1,0 +1,228 @@
+/*
+ * segpoly.h -- C ABI of the fused equivariant segmented tensor products on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * Two operations, each one kernel launch:
+ *
+ *  - the channelwise ("uvu") Clebsch-Gordan tensor-product convolution:
+ *    gather node features by source index, couple them with per-edge
+ *    spherical harmonics through every (l1, l2, lo) path at once, scale by
+ *    per-edge per-path per-channel weights, and sum-scatter into destination
+ *    nodes.  Defined by the descriptor [ijk]*a[uv]*b[iu]*c[jv] -> D[kuv]
+ *    (e3nn-course "Lesson 12a: Foundations of cuEquivariance", section 21.4)
+ *    executed with source/destination indices as in the cuequivariance-torch
+ *    skill document, sections "Channelwise product with external per-example
+ *    weights" and "SegmentedPolynomial: gather and scatter".
+ *
+ *  - the symmetric contraction of degrees 1..3 with element-indexed weights
+ *    (Lesson 12a, section 21.4.1; skill document, "Other operations and
+ *    layers", SymmetricContraction).
+ *
+ * Conventions common to every function:
+ *  - Every function returns SEGPOLY_OK (0) or a negative status; no C++
+ *    exception crosses this boundary.  After a failure,
+ *    segpoly_last_error() returns a message for the calling thread.
+ *  - Device pointers are plain addresses of device memory owned by the
+ *    caller; the library never frees them, never keeps them after a call
+ *    returns, and never allocates on the forward path except the one-time
+ *    upload of coefficient tables described at tp_conv_fwd / symcon_fwd.
+ *  - `stream` is a hipStream_t (NULL: the default stream).  Forward calls
+ *    are asynchronous and stream-ordered; they do not synchronise unless the
+ *    VALIDATE flag is set.
+ *  - Handles hold only host state (descriptor, tables) and may be created,
+ *    queried and destroyed on a machine without a GPU.  A handle may be used
+ *    from several threads for forward calls; create/destroy are not
+ *    concurrent with other uses of the same handle.
+ *  - Irreps strings: O(3) irreps "MULxLP + ..." with P = e or o, e.g.
+ *    "32x0e + 32x1o" (Lesson 12a, section 21.2).
+ *  - Layouts (Lesson 12a, section 21.3): SEGPOLY_MUL_IR stores each block as
+ *    [mul][2l+1], SEGPOLY_IR_MUL as [2l+1][mul].  The layout is part of the
+ *    handle; passing data in the other layout is not detectable and gives
+ *    wrong numbers, as on the pages.
+ */
+#ifndef SEGPOLY_H
+#define SEGPOLY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* status codes */
+#define SEGPOLY_OK 0
+#define SEGPOLY_E_INVALID (-1)     /* null pointer, negative size, bad enum, mismatched sizes */
+#define SEGPOLY_E_PARSE (-2)       /* malformed irreps string */
+#define SEGPOLY_E_UNSUPPORTED (-3) /* outside the supported envelope: fails closed, never falls back */
+#define SEGPOLY_E_UNSORTED (-4)    /* VALIDATE: destination indices not sorted ascending */
+#define SEGPOLY_E_HIP (-5)         /* a HIP runtime call or kernel launch failed */
+#define SEGPOLY_E_OOM (-6)         /* host or device allocation failed */
+#define SEGPOLY_E_RANGE (-7)       /* VALIDATE: an index outside its range */
+
+/* layouts, dtypes, index dtypes */
+#define SEGPOLY_MUL_IR 0
+#define SEGPOLY_IR_MUL 1
+#define SEGPOLY_F32 0
+#define SEGPOLY_F64 1
+#define SEGPOLY_I32 0
+#define SEGPOLY_I64 1
+
+/* flags */
+#define SEGPOLY_SHARED_WEIGHTS 1u /* weights are one row [1, numel] shared by every edge */
+#define SEGPOLY_VALIDATE 2u       /* check index ranges and dst order on the host (synchronises) */
+#define SEGPOLY_FORCE_GENERIC 4u  /* use the table-driven kernel even if a specialised one exists */
+
+/* query keys */
+#define SEGPOLY_Q_DIM_IN1 0
+#define SEGPOLY_Q_DIM_IN2 1
+#define SEGPOLY_Q_DIM_OUT 2
+#define SEGPOLY_Q_WEIGHT_NUMEL 3
+#define SEGPOLY_Q_NUM_PATHS 4
+#define SEGPOLY_Q_CG_NNZ 5
+#define SEGPOLY_Q_SPECIALIZED 6 /* 1 if a generated kernel serves this handle, 0 for the generic one */
+#define SEGPOLY_Q_MUL 7         /* the uniform multiplicity, 0 if multiplicities differ */
+#define SEGPOLY_Q_DIM_IN 8      /* symcon: input width */
+#define SEGPOLY_Q_NUM_COUPLINGS 9
+#define SEGPOLY_Q_NUM_TERMS 10  /* symcon: sorted-monomial terms per channel */
+#define SEGPOLY_Q_NUM_ELEMENTS 11
+
+typedef struct segpoly_tp* tp_handle;
+typedef struct segpoly_symcon* symcon_handle;
+
+/* ------------------------------------------------------------------ TP */
+
+/*
+ * tp_create: build the descriptor of a channelwise tensor product.
+ *   irreps_in1  features of the source nodes, e.g. "128x0e+128x1o+128x2e".
+ *   irreps_in2  per-edge operand (spherical harmonics), every block of
+ *               multiplicity 1, e.g. "0e+1o+2e+3o".
+ *   irreps_out  the irrep TYPES to keep (multiplicities are ignored): every
+ *               path (in1 block, in2 block, lo) with |l1-l2| <= lo <= l1+l2 and
+ *               parity p1*p2 whose type is listed gets its own output block
+ *               of multiplicity mul(in1 block).  The actual output irreps are
+ *               read back with tp_irreps_out (skill document, "Layouts and
+ *               weights": the filter selects types, not multiplicities).
+ *   layout      SEGPOLY_MUL_IR or SEGPOLY_IR_MUL, for x and out (sh has
+ *               multiplicity 1, so both layouts coincide for it).
+ *   dtype       SEGPOLY_F32 or SEGPOLY_F64: data and arithmetic type.
+ *   flags       SEGPOLY_SHARED_WEIGHTS, SEGPOLY_VALIDATE, SEGPOLY_FORCE_GENERIC.
+ * Path order: in1 block, in2 block, lo ascending, then a stable sort by
+ * output type (l, natural parity (-1)^l first); the weight row holds one
+ * segment of mul channels per path in that order.  Coefficients: real-basis
+ * Clebsch-Gordan tensors scaled so that sum_ij C_ijk C_ijk' = delta_kk'.
+ * Errors: E_PARSE (string), E_UNSUPPORTED (in2 multiplicity != 1, l > 8),
+ * E_INVALID (null out, bad enum).  Touches no GPU.
+ */
+int tp_create(const char* irreps_in1, const char* irreps_in2, const char* irreps_out, int layout,
+              int dtype, unsigned flags, tp_handle* out);
+
+/* tp_query: one of the SEGPOLY_Q_* sizes of the descriptor into *value. */
+int tp_query(tp_handle h, int key, int64_t* value);
+
+/* tp_irreps_out: the actual output irreps ("32x0e+32x0e+32x1o+...") into
+ * buf (NUL-terminated); E_INVALID if cap is too small. */
+int tp_irreps_out(tp_handle h, char* buf, size_t cap);
+
+/* tp_path_info: path p (0 <= p < NUM_PATHS) as 10 integers: in1 block,
+ * in2 block, l1, l2, lo, parity, mul, output element offset, weight offset,
+ * number of non-zero coefficients. */
+int tp_path_info(tp_handle h, int p, int64_t* info10);
+
+/* tp_path_cg: the dense coefficient tensor of path p, row-major
+ * [2l1+1][2l2+1][2lo+1], as doubles. */
+int tp_path_cg(tp_handle h, int p, double* out);
+
+/* tp_kernel_name: name of the kernel that serves this handle. */
+int tp_kernel_name(tp_handle h, char* buf, size_t cap);
+
+/*
+ * tp_conv_fwd: out[n] = sum over edges e with dst[e] == n of the product
+ * of x[src[e]], sh[e] and w[e] through every path; rows with no edge are
+ * written as zeros.  `out` is fully overwritten.
+ *   x       [n_src, DIM_IN1] device, layout of the handle.
+ *   sh      [n_edges, DIM_IN2] device.
+ *   w       [n_edges, WEIGHT_NUMEL] device, or [1, WEIGHT_NUMEL] with
+ *           SEGPOLY_SHARED_WEIGHTS.
+ *   src,dst [n_edges] device, int32 or int64 per idx_dtype.  dst must be
+ *           sorted ascending (precondition; checked only with VALIDATE).
+ *           Sources outside [0, n_src) and destinations outside
+ *           [0, n_nodes) contribute nothing (VALIDATE reports them as
+ *           E_RANGE).  Both NULL selects batch mode: edge e feeds row e, and
+ *           n_edges must equal n_nodes and not exceed n_src.
+ *   out     [n_nodes, DIM_OUT] device, layout of the handle.
+ * A descriptor served by the generic kernel uploads its coefficient table
+ * to the current device once (hipMalloc + hipMemcpy at the first call on
+ * that device; freed by tp_destroy).  Sizes: n_nodes < 2^31.
+ */
+int tp_conv_fwd(tp_handle h, const void* x, int64_t n_src, const void* sh, const void* w,
+                const void* src, const void* dst, int idx_dtype, int64_t n_edges, int64_t n_nodes,
+                void* out, void* stream);
+
+/* tp_destroy: free the handle (NULL is a no-op). */
+int tp_destroy(tp_handle h);
+
+/* ------------------------------------------------------------------ symcon */
+
+/*
+ * symcon_create: symmetric contraction of degrees 1..max_degree (1..3).
+ *   irreps_in, irreps_out  every block with the same multiplicity.
+ *   num_elements           number of species (rows of the weight table).
+ * Coupling basis per (degree nu, output block): candidates are the
+ * real-coupling tensors of ordered block tuples in lexicographic order (and,
+ * for nu = 3, the intermediate l ascending), symmetrised over the nu input
+ * slots; a candidate is kept when its Gram-Schmidt residual against those
+ * kept before exceeds 1e-8 of its norm; each kept tensor is scaled so that
+ * its output components are orthonormal.  Weight segments: degree, then
+ * output block, then coupling, each mul channels.
+ * Errors: E_PARSE, E_UNSUPPORTED (non-uniform multiplicities, l > 6, degree
+ * outside 1..3), E_INVALID.  Touches no GPU.
+ */
+int symcon_create(const char* irreps_in, const char* irreps_out, int max_degree, int num_elements,
+                  int layout, int dtype, unsigned flags, symcon_handle* out);
+
+/* symcon_query: DIM_IN, DIM_OUT, WEIGHT_NUMEL (per element), NUM_COUPLINGS,
+ * NUM_TERMS, SPECIALIZED, MUL, NUM_ELEMENTS. */
+int symcon_query(symcon_handle h, int key, int64_t* value);
+
+/* symcon_coupling_info: coupling c (weight-segment order) as 4 integers:
+ * degree, output block, index k within (degree, block), output l. */
+int symcon_coupling_info(symcon_handle h, int c, int64_t* info4);
+
+/* symcon_coupling_dense: coupling c as a dense row-major tensor
+ * [n]^degree x [2L+1] (n = input components per channel), doubles. */
+int symcon_coupling_dense(symcon_handle h, int c, double* out);
+
+/*
+ * symcon_fwd: out[a] = sum over degrees and couplings of
+ * w[species[a], segment] * coupling(x[a], ..., x[a]) per channel.
+ *   x        [n_atoms, DIM_IN] device, layout of the handle.
+ *   species  [n_atoms] device, int32 or int64 per idx_dtype; an element
+ *            outside [0, num_elements) gives a zero row (E_RANGE with
+ *            VALIDATE).  Need not be sorted.
+ *   w        [num_elements, WEIGHT_NUMEL] device.
+ *   out      [n_atoms, DIM_OUT] device, fully overwritten.
+ * Generic-kernel tables are uploaded once per device as for tp_conv_fwd.
+ */
+int symcon_fwd(symcon_handle h, const void* x, const void* species, int idx_dtype, const void* w,
+               int64_t n_atoms, void* out, void* stream);
+
+int symcon_destroy(symcon_handle h);
+
+/* ------------------------------------------------------------------ misc */
+
+/* segpoly_real_cg: the real coupling tensor of l1 x l2 -> l3 (the same
+ * coefficients the paths use), row-major [2l1+1][2l2+1][2l3+1]. */
+int segpoly_real_cg(int l1, int l2, int l3, double* out);
+
+/* Message of the last failure on the calling thread ("" if none). */
+const char* segpoly_last_error(void);
+
+/* Library version string. */
+const char* segpoly_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SEGPOLY_H */

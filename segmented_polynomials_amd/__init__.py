@@ -1,0 +1,309 @@
+"""Python binding of ``libsegpoly.so`` (argument marshalling only).
+
+The functions keep the names of the C ABI in ``include/segpoly.h``:
+``tp_create`` / ``tp_conv_fwd`` / ``symcon_create`` / ``symcon_fwd``.  Every
+step of the computation runs in the library's HIP kernels; PyTorch only
+supplies device memory and the current stream.  There is no CPU fallback:
+importing this package fails loudly if the library has not been built.
+"""
+
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libsegpoly.so")
+
+OK = 0
+E_INVALID, E_PARSE, E_UNSUPPORTED, E_UNSORTED, E_HIP, E_OOM, E_RANGE = -1, -2, -3, -4, -5, -6, -7
+MUL_IR, IR_MUL = 0, 1
+F32, F64 = 0, 1
+I32, I64 = 0, 1
+SHARED_WEIGHTS, VALIDATE, FORCE_GENERIC = 1, 2, 4
+(Q_DIM_IN1, Q_DIM_IN2, Q_DIM_OUT, Q_WEIGHT_NUMEL, Q_NUM_PATHS, Q_CG_NNZ, Q_SPECIALIZED, Q_MUL,
+ Q_DIM_IN, Q_NUM_COUPLINGS, Q_NUM_TERMS, Q_NUM_ELEMENTS) = range(12)
+
+_LAYOUTS = {"mul_ir": MUL_IR, "ir_mul": IR_MUL}
+_DTYPES = {"f32": F32, "f64": F64}
+
+# every symbol include/segpoly.h declares
+EXPORTS = ("tp_create", "tp_query", "tp_irreps_out", "tp_path_info", "tp_path_cg", "tp_kernel_name",
+           "tp_conv_fwd", "tp_destroy", "symcon_create", "symcon_query", "symcon_coupling_info",
+           "symcon_coupling_dense", "symcon_fwd", "symcon_destroy", "segpoly_real_cg",
+           "segpoly_last_error", "segpoly_version")
+
+
+class SegpolyError(RuntimeError):
+    def __init__(self, code, msg):
+        super().__init__(f"segpoly error {code}: {msg}")
+        self.code = code
+
+
+def _hip_runtime_of_torch():
+    """Load PyTorch's HIP runtime first.  The library's dependency
+    libamdhip64.so.7 then resolves (by soname) to that same copy, so device
+    pointers and streams from PyTorch are valid in the library: one HIP
+    runtime per process."""
+    import torch  # noqa: F401
+    path = os.path.join(os.path.dirname(torch.__file__), "lib", "libamdhip64.so")
+    if os.path.exists(path):
+        ctypes.CDLL(path, mode=ctypes.RTLD_GLOBAL)
+
+
+def hip_runtimes_loaded():
+    """Distinct libamdhip64 files mapped into this process."""
+    with open("/proc/self/maps") as f:
+        return sorted({ln.split()[-1] for ln in f if "libamdhip64" in ln})
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with `python -m segmented_polynomials_amd.build`")
+    _hip_runtime_of_torch()
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i64, c_int, c_uint = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_uint
+    p64 = ctypes.POINTER(ctypes.c_int64)
+    pd = ctypes.POINTER(ctypes.c_double)
+    sig = {
+        "tp_create": [ctypes.c_char_p, ctypes.c_char_p, ctypes.c_char_p, c_int, c_int, c_uint, ctypes.POINTER(vp)],
+        "tp_query": [vp, c_int, p64],
+        "tp_irreps_out": [vp, ctypes.c_char_p, ctypes.c_size_t],
+        "tp_path_info": [vp, c_int, p64],
+        "tp_path_cg": [vp, c_int, pd],
+        "tp_kernel_name": [vp, ctypes.c_char_p, ctypes.c_size_t],
+        "tp_conv_fwd": [vp, vp, i64, vp, vp, vp, vp, c_int, i64, i64, vp, vp],
+        "tp_destroy": [vp],
+        "symcon_create": [ctypes.c_char_p, ctypes.c_char_p, c_int, c_int, c_int, c_int, c_uint, ctypes.POINTER(vp)],
+        "symcon_query": [vp, c_int, p64],
+        "symcon_coupling_info": [vp, c_int, p64],
+        "symcon_coupling_dense": [vp, c_int, pd],
+        "symcon_fwd": [vp, vp, vp, c_int, vp, i64, vp, vp],
+        "symcon_destroy": [vp],
+        "segpoly_real_cg": [c_int, c_int, c_int, pd],
+    }
+    for name, args in sig.items():
+        f = getattr(lib, name)
+        f.argtypes = args
+        f.restype = c_int
+    lib.segpoly_last_error.restype = ctypes.c_char_p
+    lib.segpoly_last_error.argtypes = []
+    lib.segpoly_version.restype = ctypes.c_char_p
+    lib.segpoly_version.argtypes = []
+    return lib
+
+
+lib = _load()
+
+
+def _check(rc):
+    if rc != OK:
+        raise SegpolyError(rc, lib.segpoly_last_error().decode())
+
+
+def version():
+    return lib.segpoly_version().decode()
+
+
+def real_cg(l1, l2, l3):
+    """The real coupling tensor of l1 x l2 -> l3 used by the paths, [2l1+1, 2l2+1, 2l3+1]."""
+    out = np.zeros((2 * l1 + 1) * (2 * l2 + 1) * (2 * l3 + 1))
+    _check(lib.segpoly_real_cg(l1, l2, l3, out.ctypes.data_as(ctypes.POINTER(ctypes.c_double))))
+    return out.reshape(2 * l1 + 1, 2 * l2 + 1, 2 * l3 + 1)
+
+
+def _str(fn, h, cap=1 << 16):
+    buf = ctypes.create_string_buffer(cap)
+    _check(fn(h, buf, cap))
+    return buf.value.decode()
+
+
+def _flags(shared_weights=False, validate=False, force_generic=False):
+    return (SHARED_WEIGHTS if shared_weights else 0) | (VALIDATE if validate else 0) | \
+        (FORCE_GENERIC if force_generic else 0)
+
+
+def _stream_ptr(device):
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+# ---------------------------------------------------------------- TP
+
+class TPHandle:
+    """Owns one ``tp_handle``; sizes are read back from the library."""
+
+    def __init__(self, raw, layout, dtype, shared_weights):
+        self._h = raw
+        self.layout = layout
+        self.dtype = dtype
+        self.shared_weights = shared_weights
+
+    def _q(self, key):
+        v = ctypes.c_int64()
+        _check(lib.tp_query(self._h, key, ctypes.byref(v)))
+        return v.value
+
+    dim_in1 = property(lambda s: s._q(Q_DIM_IN1))
+    dim_in2 = property(lambda s: s._q(Q_DIM_IN2))
+    dim_out = property(lambda s: s._q(Q_DIM_OUT))
+    weight_numel = property(lambda s: s._q(Q_WEIGHT_NUMEL))
+    num_paths = property(lambda s: s._q(Q_NUM_PATHS))
+    cg_nnz = property(lambda s: s._q(Q_CG_NNZ))
+    specialized = property(lambda s: bool(s._q(Q_SPECIALIZED)))
+    mul = property(lambda s: s._q(Q_MUL))
+    irreps_out = property(lambda s: _str(lib.tp_irreps_out, s._h))
+    kernel_name = property(lambda s: _str(lib.tp_kernel_name, s._h))
+
+    def path_info(self, p):
+        v = (ctypes.c_int64 * 10)()
+        _check(lib.tp_path_info(self._h, p, v))
+        keys = ("in1_block", "in2_block", "l1", "l2", "lo", "parity", "mul", "out_offset",
+                "weight_offset", "nnz")
+        return dict(zip(keys, list(v)))
+
+    def path_cg(self, p):
+        i = self.path_info(p)
+        shape = (2 * i["l1"] + 1, 2 * i["l2"] + 1, 2 * i["lo"] + 1)
+        out = np.zeros(int(np.prod(shape)))
+        _check(lib.tp_path_cg(self._h, p, out.ctypes.data_as(ctypes.POINTER(ctypes.c_double))))
+        return out.reshape(shape)
+
+    def __del__(self):
+        if getattr(self, "_h", None):
+            lib.tp_destroy(self._h)
+            self._h = None
+
+
+def tp_create(irreps_in1, irreps_in2, irreps_out, layout="mul_ir", dtype="f32", shared_weights=False,
+              validate=False, force_generic=False):
+    raw = ctypes.c_void_p()
+    _check(lib.tp_create(irreps_in1.encode(), irreps_in2.encode(), irreps_out.encode(), _LAYOUTS[layout],
+                         _DTYPES[dtype], _flags(shared_weights, validate, force_generic), ctypes.byref(raw)))
+    return TPHandle(raw, layout, dtype, shared_weights)
+
+
+def _index_dtype(t):
+    import torch
+    if t.dtype == torch.int32:
+        return I32
+    if t.dtype == torch.int64:
+        return I64
+    raise TypeError("indices must be int32 or int64")
+
+
+def _torch_dtype(dt):
+    import torch
+    return {"f32": torch.float32, "f64": torch.float64}[dt]
+
+
+def tp_conv_fwd(h, x, sh, w, src=None, dst=None, n_nodes=None, out=None):
+    """Gather x[src], couple with sh and w through every path, sum-scatter
+    to dst.  Device tensors, contiguous, of the handle's dtype; src/dst int32
+    or int64 (dst sorted) or both None (batch mode).  Returns ``out``
+    [n_nodes, dim_out] (allocated if not given)."""
+    import torch
+    t = _torch_dtype(h.dtype)
+    for name, a in (("x", x), ("sh", sh), ("w", w)):
+        if a.dtype != t or not a.is_cuda or not a.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous {t} device tensor")
+    n_src, n_edges = x.shape[0], sh.shape[0]
+    if x.shape[1] != h.dim_in1 or sh.shape[1] != h.dim_in2 or w.shape[-1] != h.weight_numel:
+        raise ValueError("operand widths do not match the descriptor")
+    if w.shape[0] != (1 if h.shared_weights else n_edges):
+        raise ValueError("weights must have one row per edge (or one row when shared)")
+    if (src is None) != (dst is None):
+        raise ValueError("give both src and dst or neither")
+    idx = I32
+    if src is not None:
+        if src.shape != (n_edges,) or dst.shape != (n_edges,) or src.dtype != dst.dtype:
+            raise ValueError("src and dst must be [n_edges] of one integer dtype")
+        if not (src.is_cuda and dst.is_cuda and src.is_contiguous() and dst.is_contiguous()):
+            raise ValueError("src and dst must be contiguous device tensors")
+        idx = _index_dtype(src)
+    if n_nodes is None:
+        if src is not None:
+            raise ValueError("n_nodes is required with indices")
+        n_nodes = n_edges
+    if out is None:
+        out = torch.empty((n_nodes, h.dim_out), dtype=t, device=x.device)
+    elif out.shape != (n_nodes, h.dim_out) or out.dtype != t or not out.is_contiguous():
+        raise ValueError("out has the wrong shape or dtype")
+    _check(lib.tp_conv_fwd(h._h, _ptr(x), n_src, _ptr(sh), _ptr(w), _ptr(src), _ptr(dst), idx, n_edges,
+                           n_nodes, _ptr(out), _stream_ptr(x.device)))
+    return out
+
+
+# ---------------------------------------------------------------- symcon
+
+class SymconHandle:
+    def __init__(self, raw, layout, dtype):
+        self._h = raw
+        self.layout = layout
+        self.dtype = dtype
+
+    def _q(self, key):
+        v = ctypes.c_int64()
+        _check(lib.symcon_query(self._h, key, ctypes.byref(v)))
+        return v.value
+
+    dim_in = property(lambda s: s._q(Q_DIM_IN))
+    dim_out = property(lambda s: s._q(Q_DIM_OUT))
+    weight_numel = property(lambda s: s._q(Q_WEIGHT_NUMEL))
+    num_couplings = property(lambda s: s._q(Q_NUM_COUPLINGS))
+    num_terms = property(lambda s: s._q(Q_NUM_TERMS))
+    specialized = property(lambda s: bool(s._q(Q_SPECIALIZED)))
+    mul = property(lambda s: s._q(Q_MUL))
+    num_elements = property(lambda s: s._q(Q_NUM_ELEMENTS))
+
+    def coupling_info(self, c):
+        v = (ctypes.c_int64 * 4)()
+        _check(lib.symcon_coupling_info(self._h, c, v))
+        return dict(zip(("degree", "out_block", "k", "l"), list(v)))
+
+    def coupling_dense(self, c, n_components):
+        i = self.coupling_info(c)
+        shape = (n_components,) * i["degree"] + (2 * i["l"] + 1,)
+        out = np.zeros(int(np.prod(shape)))
+        _check(lib.symcon_coupling_dense(self._h, c, out.ctypes.data_as(ctypes.POINTER(ctypes.c_double))))
+        return out.reshape(shape)
+
+    def __del__(self):
+        if getattr(self, "_h", None):
+            lib.symcon_destroy(self._h)
+            self._h = None
+
+
+def symcon_create(irreps_in, irreps_out, max_degree=3, num_elements=1, layout="ir_mul", dtype="f32",
+                  validate=False, force_generic=False):
+    raw = ctypes.c_void_p()
+    _check(lib.symcon_create(irreps_in.encode(), irreps_out.encode(), max_degree, num_elements,
+                             _LAYOUTS[layout], _DTYPES[dtype], _flags(False, validate, force_generic),
+                             ctypes.byref(raw)))
+    return SymconHandle(raw, layout, dtype)
+
+
+def symcon_fwd(h, x, species, w, out=None):
+    """Symmetric contraction of x [n_atoms, dim_in] with the weights of each
+    atom's element (species int32/int64 [n_atoms]); returns [n_atoms, dim_out]."""
+    import torch
+    t = _torch_dtype(h.dtype)
+    for name, a in (("x", x), ("w", w)):
+        if a.dtype != t or not a.is_cuda or not a.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous {t} device tensor")
+    n = x.shape[0]
+    if x.shape[1] != h.dim_in or w.shape != (h.num_elements, h.weight_numel):
+        raise ValueError("operand shapes do not match the descriptor")
+    if species.shape != (n,) or not species.is_cuda or not species.is_contiguous():
+        raise ValueError("species must be a contiguous [n_atoms] device tensor")
+    idx = _index_dtype(species)
+    if out is None:
+        out = torch.empty((n, h.dim_out), dtype=t, device=x.device)
+    elif out.shape != (n, h.dim_out) or out.dtype != t or not out.is_contiguous():
+        raise ValueError("out has the wrong shape or dtype")
+    _check(lib.symcon_fwd(h._h, _ptr(x), _ptr(species), idx, _ptr(w), n, _ptr(out), _stream_ptr(x.device)))
+    return out

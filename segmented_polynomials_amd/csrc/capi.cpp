@@ -1,0 +1,519 @@
+// C ABI of the library: handles, validation, kernel selection.  Host code.
+#include <hip/hip_runtime_api.h>
+
+#include <algorithm>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <new>
+#include <stdexcept>
+#include <string>
+#include <vector>
+
+#include "cg.hpp"
+#include "generic_tables.hpp"
+#include "launch.hpp"
+#include "segpoly.h"
+#include "symcon_descriptor.hpp"
+#include "tp_descriptor.hpp"
+
+using namespace segpoly;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const std::string& msg) {
+  g_last_error = msg;
+  return code;
+}
+
+int ok() {
+  g_last_error.clear();
+  return SEGPOLY_OK;
+}
+
+constexpr size_t kGenericLdsLimit = 64 * 1024;
+constexpr int64_t kMaxGrid = 2147483647;
+
+int copy_str(const std::string& s, char* buf, size_t cap) {
+  if (!buf) return fail(SEGPOLY_E_INVALID, "null buffer");
+  if (cap < s.size() + 1) return fail(SEGPOLY_E_INVALID, "buffer too small: need " + std::to_string(s.size() + 1));
+  std::memcpy(buf, s.c_str(), s.size() + 1);
+  return ok();
+}
+
+struct DeviceBuffer {
+  void* ptr = nullptr;
+};
+
+// Upload `bytes` of host data once per device; returns the device pointer
+// or null (error set) on failure.
+void* upload(std::map<int, DeviceBuffer>& cache, std::mutex& mu, const void* host, size_t bytes, int* status) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    *status = fail(SEGPOLY_E_HIP, std::string("hipGetDevice: ") + hipGetErrorString(e));
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> g(mu);
+  auto it = cache.find(dev);
+  if (it != cache.end()) return it->second.ptr;
+  void* p = nullptr;
+  e = hipMalloc(&p, bytes ? bytes : 16);
+  if (e != hipSuccess) {
+    *status = fail(SEGPOLY_E_OOM, std::string("hipMalloc (coefficient table): ") + hipGetErrorString(e));
+    return nullptr;
+  }
+  if (bytes) {
+    e = hipMemcpy(p, host, bytes, hipMemcpyHostToDevice);
+    if (e != hipSuccess) {
+      (void)hipFree(p);
+      *status = fail(SEGPOLY_E_HIP, std::string("hipMemcpy (coefficient table): ") + hipGetErrorString(e));
+      return nullptr;
+    }
+  }
+  cache[dev].ptr = p;
+  return p;
+}
+
+void free_all(std::map<int, DeviceBuffer>& cache) {
+  int cur = 0;
+  bool have = hipGetDevice(&cur) == hipSuccess;
+  for (auto& kv : cache) {
+    if (hipSetDevice(kv.first) == hipSuccess) (void)hipFree(kv.second.ptr);
+  }
+  if (have) (void)hipSetDevice(cur);
+  cache.clear();
+}
+
+// Host-side index checks of the VALIDATE flag.
+template <typename Index>
+int check_indices(const void* dsrc, const void* ddst, int64_t n_edges, int64_t n_src, int64_t n_nodes,
+                  void* stream) {
+  std::vector<Index> s(n_edges), d(n_edges);
+  hipError_t e = hipStreamSynchronize(static_cast<hipStream_t>(stream));
+  if (e == hipSuccess && n_edges) e = hipMemcpy(s.data(), dsrc, n_edges * sizeof(Index), hipMemcpyDeviceToHost);
+  if (e == hipSuccess && n_edges) e = hipMemcpy(d.data(), ddst, n_edges * sizeof(Index), hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return fail(SEGPOLY_E_HIP, std::string("validate copy: ") + hipGetErrorString(e));
+  for (int64_t i = 0; i < n_edges; ++i) {
+    if (s[i] < 0 || static_cast<int64_t>(s[i]) >= n_src)
+      return fail(SEGPOLY_E_RANGE, "src[" + std::to_string(i) + "] = " + std::to_string(s[i]) + " outside [0, n_src)");
+    if (d[i] < 0 || static_cast<int64_t>(d[i]) >= n_nodes)
+      return fail(SEGPOLY_E_RANGE, "dst[" + std::to_string(i) + "] = " + std::to_string(d[i]) + " outside [0, n_nodes)");
+    if (i && d[i] < d[i - 1])
+      return fail(SEGPOLY_E_UNSORTED, "dst is not sorted ascending at edge " + std::to_string(i));
+  }
+  return ok();
+}
+
+template <typename Index>
+int check_species(const void* dsp, int64_t n, int num_elements, void* stream) {
+  std::vector<Index> s(n);
+  hipError_t e = hipStreamSynchronize(static_cast<hipStream_t>(stream));
+  if (e == hipSuccess && n) e = hipMemcpy(s.data(), dsp, n * sizeof(Index), hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return fail(SEGPOLY_E_HIP, std::string("validate copy: ") + hipGetErrorString(e));
+  for (int64_t i = 0; i < n; ++i)
+    if (s[i] < 0 || static_cast<int64_t>(s[i]) >= num_elements)
+      return fail(SEGPOLY_E_RANGE, "species[" + std::to_string(i) + "] outside [0, num_elements)");
+  return ok();
+}
+
+}  // namespace
+
+struct segpoly_tp {
+  TPDescriptor d;
+  int layout = 0, dtype = 0;
+  unsigned flags = 0;
+  const TPSpecEntry* spec = nullptr;
+  std::string kernel_name;
+  std::vector<GPath> gpaths;
+  std::vector<GNz> gnz;
+  std::vector<unsigned char> blob;  // gpaths then gnz, uploaded once per device
+  int max_mul = 0;
+  std::mutex mu;
+  std::map<int, DeviceBuffer> dev;
+};
+
+struct segpoly_symcon {
+  SymconDescriptor d;
+  int layout = 0, dtype = 0, num_elements = 0;
+  unsigned flags = 0;
+  const SymconSpecEntry* spec = nullptr;
+  std::string kernel_name;
+  std::vector<GTerm> gterms;
+  std::vector<GBlock> gin, gout;
+  std::vector<unsigned char> blob;  // gterms, gin, gout
+  std::mutex mu;
+  std::map<int, DeviceBuffer> dev;
+};
+
+extern "C" {
+
+const char* segpoly_last_error(void) { return g_last_error.c_str(); }
+
+const char* segpoly_version(void) { return "segpoly 0.1.0 (gfx950)"; }
+
+int segpoly_real_cg(int l1, int l2, int l3, double* out) {
+  if (!out) return fail(SEGPOLY_E_INVALID, "null output");
+  if (l1 < 0 || l2 < 0 || l3 < 0 || l1 > kMaxL || l2 > kMaxL || l3 > 2 * kMaxL)
+    return fail(SEGPOLY_E_UNSUPPORTED, "l outside the supported range");
+  const auto& t = real_cg(l1, l2, l3);
+  std::memcpy(out, t.data(), t.size() * sizeof(double));
+  return ok();
+}
+
+// ------------------------------------------------------------------ TP
+
+int tp_create(const char* in1, const char* in2, const char* outs, int layout, int dtype, unsigned flags,
+              tp_handle* out) {
+  if (!out) return fail(SEGPOLY_E_INVALID, "null handle pointer");
+  *out = nullptr;
+  if (!in1 || !in2 || !outs) return fail(SEGPOLY_E_INVALID, "null irreps string");
+  if (layout != SEGPOLY_MUL_IR && layout != SEGPOLY_IR_MUL) return fail(SEGPOLY_E_INVALID, "bad layout");
+  if (dtype != SEGPOLY_F32 && dtype != SEGPOLY_F64) return fail(SEGPOLY_E_INVALID, "bad dtype");
+  if (flags & ~(SEGPOLY_SHARED_WEIGHTS | SEGPOLY_VALIDATE | SEGPOLY_FORCE_GENERIC))
+    return fail(SEGPOLY_E_INVALID, "unknown flag bits");
+  segpoly_tp* h = nullptr;
+  try {
+    h = new segpoly_tp();
+    h->d = build_tp(in1, in2, outs);
+  } catch (const ParseError& e) {
+    delete h;
+    return fail(SEGPOLY_E_PARSE, e.what());
+  } catch (const std::invalid_argument& e) {
+    delete h;
+    return fail(SEGPOLY_E_UNSUPPORTED, e.what());
+  } catch (const std::bad_alloc&) {
+    delete h;
+    return fail(SEGPOLY_E_OOM, "out of host memory");
+  } catch (const std::exception& e) {
+    delete h;
+    return fail(SEGPOLY_E_INVALID, e.what());
+  }
+  h->layout = layout;
+  h->dtype = dtype;
+  h->flags = flags;
+  const unsigned bit = dtype == SEGPOLY_F32 ? 1u : 2u;
+  if (!(flags & SEGPOLY_FORCE_GENERIC) && h->d.uniform_mul && h->d.mul > 0) {
+    for (int i = 0; i < kNumTPSpecs; ++i)
+      if ((kTPSpecs[i].dtypes & bit) && h->d.key == kTPSpecs[i].key) {
+        h->spec = &kTPSpecs[i];
+        break;
+      }
+  }
+  // generic tables
+  int kc = 0;
+  for (const auto& p : h->d.paths) {
+    GPath g{};
+    g.l1 = p.l1;
+    g.lo = p.lo;
+    g.mul = p.mul;
+    g.nz_begin = static_cast<int>(h->gnz.size());
+    for (const auto& z : p.nz) h->gnz.push_back({z.i, z.j, z.k, 0, z.c});
+    g.nz_end = static_cast<int>(h->gnz.size());
+    g.kcomp = kc;
+    kc += 2 * p.lo + 1;
+    g.off1 = p.off1;
+    g.off2 = p.off2;
+    g.offo = p.offo;
+    g.woff = p.woff;
+    h->gpaths.push_back(g);
+    h->max_mul = std::max(h->max_mul, p.mul);
+  }
+  {
+    const size_t bp = h->gpaths.size() * sizeof(GPath), bz = h->gnz.size() * sizeof(GNz);
+    h->blob.resize(bp + bz);
+    if (bp) std::memcpy(h->blob.data(), h->gpaths.data(), bp);
+    if (bz) std::memcpy(h->blob.data() + bp, h->gnz.data(), bz);
+  }
+  const size_t esz = dtype == SEGPOLY_F32 ? 4 : 8;
+  if (!h->spec && static_cast<size_t>(h->d.nk) * 64 * esz > kGenericLdsLimit) {
+    delete h;
+    return fail(SEGPOLY_E_UNSUPPORTED, "too many output components per channel for the generic kernel");
+  }
+  h->kernel_name = h->spec ? std::string("tp_conv_spec_") + h->spec->name : "tp_conv_generic";
+  *out = h;
+  return ok();
+}
+
+int tp_query(tp_handle h, int key, int64_t* value) {
+  if (!h || !value) return fail(SEGPOLY_E_INVALID, "null argument");
+  const auto& d = h->d;
+  switch (key) {
+    case SEGPOLY_Q_DIM_IN1: *value = d.dim1; break;
+    case SEGPOLY_Q_DIM_IN2: *value = d.dim2; break;
+    case SEGPOLY_Q_DIM_OUT: *value = d.dimo; break;
+    case SEGPOLY_Q_WEIGHT_NUMEL: *value = d.numel; break;
+    case SEGPOLY_Q_NUM_PATHS: *value = static_cast<int64_t>(d.paths.size()); break;
+    case SEGPOLY_Q_CG_NNZ: *value = d.cg_nnz(); break;
+    case SEGPOLY_Q_SPECIALIZED: *value = h->spec ? 1 : 0; break;
+    case SEGPOLY_Q_MUL: *value = d.uniform_mul ? d.mul : 0; break;
+    default: return fail(SEGPOLY_E_INVALID, "unknown query key");
+  }
+  return ok();
+}
+
+int tp_irreps_out(tp_handle h, char* buf, size_t cap) {
+  if (!h) return fail(SEGPOLY_E_INVALID, "null handle");
+  return copy_str(irreps_str(h->d.out), buf, cap);
+}
+
+int tp_kernel_name(tp_handle h, char* buf, size_t cap) {
+  if (!h) return fail(SEGPOLY_E_INVALID, "null handle");
+  return copy_str(h->kernel_name, buf, cap);
+}
+
+int tp_path_info(tp_handle h, int p, int64_t* info) {
+  if (!h || !info) return fail(SEGPOLY_E_INVALID, "null argument");
+  if (p < 0 || p >= static_cast<int>(h->d.paths.size())) return fail(SEGPOLY_E_INVALID, "path index out of range");
+  const auto& q = h->d.paths[p];
+  int64_t v[10] = {q.b1, q.b2, q.l1, q.l2, q.lo, q.po, q.mul, q.offo, q.woff, static_cast<int64_t>(q.nz.size())};
+  std::memcpy(info, v, sizeof v);
+  return ok();
+}
+
+int tp_path_cg(tp_handle h, int p, double* out) {
+  if (!h || !out) return fail(SEGPOLY_E_INVALID, "null argument");
+  if (p < 0 || p >= static_cast<int>(h->d.paths.size())) return fail(SEGPOLY_E_INVALID, "path index out of range");
+  const auto& q = h->d.paths[p];
+  const int d2 = 2 * q.l2 + 1, d3 = 2 * q.lo + 1;
+  std::memset(out, 0, sizeof(double) * (2 * q.l1 + 1) * d2 * d3);
+  for (const auto& z : q.nz) out[(static_cast<size_t>(z.i) * d2 + z.j) * d3 + z.k] = z.c;
+  return ok();
+}
+
+int tp_conv_fwd(tp_handle h, const void* x, int64_t n_src, const void* sh, const void* w, const void* src,
+                const void* dst, int idx_dtype, int64_t n_edges, int64_t n_nodes, void* out, void* stream) {
+  if (!h) return fail(SEGPOLY_E_INVALID, "null handle");
+  if (n_src < 0 || n_edges < 0 || n_nodes < 0) return fail(SEGPOLY_E_INVALID, "negative size");
+  if (idx_dtype != SEGPOLY_I32 && idx_dtype != SEGPOLY_I64) return fail(SEGPOLY_E_INVALID, "bad index dtype");
+  if ((src == nullptr) != (dst == nullptr))
+    return fail(SEGPOLY_E_INVALID, "src and dst must both be given or both be NULL");
+  const auto& d = h->d;
+  // NULL indices select batch mode, except that an empty edge list (whose
+  // index arrays may well be NULL) always means "no edges, all rows zero"
+  const bool batch = src == nullptr && n_edges > 0;
+  if (batch && (n_edges != n_nodes || n_src < n_edges))
+    return fail(SEGPOLY_E_INVALID, "batch mode needs n_edges == n_nodes <= n_src");
+  if (n_nodes > kMaxGrid) return fail(SEGPOLY_E_UNSUPPORTED, "n_nodes must be below 2^31");
+  if (n_nodes == 0 || d.dimo == 0) return ok();
+  if (!out) return fail(SEGPOLY_E_INVALID, "null out");
+  if (n_edges > 0) {
+    if (!sh && d.dim2 > 0) return fail(SEGPOLY_E_INVALID, "null sh");
+    if (!w) return fail(SEGPOLY_E_INVALID, "null w");
+    if (!x && n_src > 0) return fail(SEGPOLY_E_INVALID, "null x");
+  }
+  if ((h->flags & SEGPOLY_VALIDATE) && !batch) {
+    int st = idx_dtype == SEGPOLY_I32 ? check_indices<int32_t>(src, dst, n_edges, n_src, n_nodes, stream)
+                                      : check_indices<int64_t>(src, dst, n_edges, n_src, n_nodes, stream);
+    if (st != SEGPOLY_OK) return st;
+  }
+  TPArgs a{};
+  a.x = x;
+  a.sh = sh;
+  a.w = w;
+  a.src = src;
+  a.dst = dst;
+  a.out = out;
+  a.n_src = n_src;
+  a.n_edges = n_edges;
+  a.n_nodes = n_nodes;
+  a.w_stride = (h->flags & SEGPOLY_SHARED_WEIGHTS) ? 0 : d.numel;
+  a.mul = d.uniform_mul ? d.mul : 0;
+  a.batch = batch ? 1 : 0;
+  a.dtype = h->dtype;
+  a.idx = idx_dtype;
+  a.layout = h->layout;
+  a.stream = stream;
+  int rc;
+  if (h->spec) {
+    rc = h->spec->launch(a);
+  } else {
+    const size_t bp = h->gpaths.size() * sizeof(GPath);
+    int st = SEGPOLY_OK;
+    void* dp = upload(h->dev, h->mu, h->blob.data(), h->blob.size(), &st);
+    if (!dp) return st;
+    GenericTPInfo g{};
+    g.paths = static_cast<const GPath*>(dp);
+    g.nz = reinterpret_cast<const GNz*>(static_cast<unsigned char*>(dp) + bp);
+    g.np = static_cast<int>(h->gpaths.size());
+    g.nk = d.nk;
+    g.max_mul = h->max_mul;
+    g.dim1 = d.dim1;
+    g.dim2 = d.dim2;
+    g.dimo = d.dimo;
+    rc = launch_tp_generic(a, g);
+  }
+  if (rc != 0)
+    return fail(SEGPOLY_E_HIP, std::string("kernel launch failed: ") + hipGetErrorString(static_cast<hipError_t>(rc)));
+  return ok();
+}
+
+int tp_destroy(tp_handle h) {
+  if (!h) return ok();
+  free_all(h->dev);
+  delete h;
+  return ok();
+}
+
+// ------------------------------------------------------------------ symcon
+
+int symcon_create(const char* s_in, const char* s_out, int max_degree, int num_elements, int layout, int dtype,
+                  unsigned flags, symcon_handle* out) {
+  if (!out) return fail(SEGPOLY_E_INVALID, "null handle pointer");
+  *out = nullptr;
+  if (!s_in || !s_out) return fail(SEGPOLY_E_INVALID, "null irreps string");
+  if (layout != SEGPOLY_MUL_IR && layout != SEGPOLY_IR_MUL) return fail(SEGPOLY_E_INVALID, "bad layout");
+  if (dtype != SEGPOLY_F32 && dtype != SEGPOLY_F64) return fail(SEGPOLY_E_INVALID, "bad dtype");
+  if (num_elements < 1) return fail(SEGPOLY_E_INVALID, "num_elements must be >= 1");
+  if (max_degree < 1 || max_degree > 3) return fail(SEGPOLY_E_UNSUPPORTED, "max_degree must be 1, 2 or 3");
+  if (flags & ~(SEGPOLY_VALIDATE | SEGPOLY_FORCE_GENERIC)) return fail(SEGPOLY_E_INVALID, "unknown flag bits");
+  std::vector<int> deg;
+  for (int i = 1; i <= max_degree; ++i) deg.push_back(i);
+  segpoly_symcon* h = nullptr;
+  try {
+    h = new segpoly_symcon();
+    h->d = build_symcon(s_in, s_out, deg);
+  } catch (const ParseError& e) {
+    delete h;
+    return fail(SEGPOLY_E_PARSE, e.what());
+  } catch (const std::invalid_argument& e) {
+    delete h;
+    return fail(SEGPOLY_E_UNSUPPORTED, e.what());
+  } catch (const std::bad_alloc&) {
+    delete h;
+    return fail(SEGPOLY_E_OOM, "out of host memory");
+  } catch (const std::exception& e) {
+    delete h;
+    return fail(SEGPOLY_E_INVALID, e.what());
+  }
+  h->layout = layout;
+  h->dtype = dtype;
+  h->flags = flags;
+  h->num_elements = num_elements;
+  const unsigned bit = dtype == SEGPOLY_F32 ? 1u : 2u;
+  if (!(flags & SEGPOLY_FORCE_GENERIC))
+    for (int i = 0; i < kNumSymconSpecs; ++i)
+      if ((kSymconSpecs[i].dtypes & bit) && h->d.key == kSymconSpecs[i].key) {
+        h->spec = &kSymconSpecs[i];
+        break;
+      }
+  for (size_t s = 0; s < h->d.couplings.size(); ++s) {
+    const auto& cp = h->d.couplings[s];
+    for (const auto& t : cp.terms)
+      h->gterms.push_back({t.m[0], t.m[1], t.m[2], h->d.out_comp[cp.ob] + t.M, static_cast<int>(s), 0, t.c});
+  }
+  for (size_t b = 0; b < h->d.in.size(); ++b) h->gin.push_back({h->d.in[b].l, h->d.in_comp[b]});
+  for (size_t b = 0; b < h->d.out.size(); ++b) h->gout.push_back({h->d.out[b].l, h->d.out_comp[b]});
+  {
+    const size_t bt = h->gterms.size() * sizeof(GTerm), bi = h->gin.size() * sizeof(GBlock),
+                 bo = h->gout.size() * sizeof(GBlock);
+    h->blob.resize(bt + bi + bo);
+    if (bt) std::memcpy(h->blob.data(), h->gterms.data(), bt);
+    std::memcpy(h->blob.data() + bt, h->gin.data(), bi);
+    std::memcpy(h->blob.data() + bt + bi, h->gout.data(), bo);
+  }
+  const size_t esz = dtype == SEGPOLY_F32 ? 4 : 8;
+  if (!h->spec && static_cast<size_t>(h->d.n + h->d.nout) * 64 * esz > kGenericLdsLimit) {
+    delete h;
+    return fail(SEGPOLY_E_UNSUPPORTED, "too many components per channel for the generic kernel");
+  }
+  h->kernel_name = h->spec ? std::string("symcon_spec_") + h->spec->name : "symcon_generic";
+  *out = h;
+  return ok();
+}
+
+int symcon_query(symcon_handle h, int key, int64_t* value) {
+  if (!h || !value) return fail(SEGPOLY_E_INVALID, "null argument");
+  const auto& d = h->d;
+  switch (key) {
+    case SEGPOLY_Q_DIM_IN: *value = d.dim_in; break;
+    case SEGPOLY_Q_DIM_OUT: *value = d.dim_out; break;
+    case SEGPOLY_Q_WEIGHT_NUMEL: *value = d.numel; break;
+    case SEGPOLY_Q_NUM_COUPLINGS: *value = static_cast<int64_t>(d.couplings.size()); break;
+    case SEGPOLY_Q_NUM_TERMS: *value = d.num_terms(); break;
+    case SEGPOLY_Q_SPECIALIZED: *value = h->spec ? 1 : 0; break;
+    case SEGPOLY_Q_MUL: *value = d.mul; break;
+    case SEGPOLY_Q_NUM_ELEMENTS: *value = h->num_elements; break;
+    default: return fail(SEGPOLY_E_INVALID, "unknown query key");
+  }
+  return ok();
+}
+
+int symcon_coupling_info(symcon_handle h, int c, int64_t* info) {
+  if (!h || !info) return fail(SEGPOLY_E_INVALID, "null argument");
+  if (c < 0 || c >= static_cast<int>(h->d.couplings.size())) return fail(SEGPOLY_E_INVALID, "coupling index out of range");
+  const auto& cp = h->d.couplings[c];
+  int64_t v[4] = {cp.nu, cp.ob, cp.k, cp.L};
+  std::memcpy(info, v, sizeof v);
+  return ok();
+}
+
+int symcon_coupling_dense(symcon_handle h, int c, double* out) {
+  if (!h || !out) return fail(SEGPOLY_E_INVALID, "null argument");
+  if (c < 0 || c >= static_cast<int>(h->d.couplings.size())) return fail(SEGPOLY_E_INVALID, "coupling index out of range");
+  const auto& cp = h->d.couplings[c];
+  std::memcpy(out, cp.dense.data(), cp.dense.size() * sizeof(double));
+  return ok();
+}
+
+int symcon_fwd(symcon_handle h, const void* x, const void* species, int idx_dtype, const void* w, int64_t n_atoms,
+               void* out, void* stream) {
+  if (!h) return fail(SEGPOLY_E_INVALID, "null handle");
+  if (n_atoms < 0) return fail(SEGPOLY_E_INVALID, "negative size");
+  if (idx_dtype != SEGPOLY_I32 && idx_dtype != SEGPOLY_I64) return fail(SEGPOLY_E_INVALID, "bad index dtype");
+  if (n_atoms > kMaxGrid) return fail(SEGPOLY_E_UNSUPPORTED, "n_atoms must be below 2^31");
+  if (n_atoms == 0 || h->d.dim_out == 0) return ok();
+  if (!x || !species || !w || !out) return fail(SEGPOLY_E_INVALID, "null pointer");
+  if (h->flags & SEGPOLY_VALIDATE) {
+    int st = idx_dtype == SEGPOLY_I32 ? check_species<int32_t>(species, n_atoms, h->num_elements, stream)
+                                      : check_species<int64_t>(species, n_atoms, h->num_elements, stream);
+    if (st != SEGPOLY_OK) return st;
+  }
+  SymconArgs a{};
+  a.x = x;
+  a.species = species;
+  a.w = w;
+  a.out = out;
+  a.n_atoms = n_atoms;
+  a.num_elements = h->num_elements;
+  a.mul = h->d.mul;
+  a.dtype = h->dtype;
+  a.idx = idx_dtype;
+  a.layout = h->layout;
+  a.stream = stream;
+  int rc;
+  if (h->spec) {
+    rc = h->spec->launch(a);
+  } else {
+    const size_t bt = h->gterms.size() * sizeof(GTerm), bi = h->gin.size() * sizeof(GBlock);
+    int st = SEGPOLY_OK;
+    void* dp = upload(h->dev, h->mu, h->blob.data(), h->blob.size(), &st);
+    if (!dp) return st;
+    unsigned char* base = static_cast<unsigned char*>(dp);
+    GenericSymconInfo g{};
+    g.terms = reinterpret_cast<const GTerm*>(base);
+    g.in_blocks = reinterpret_cast<const GBlock*>(base + bt);
+    g.out_blocks = reinterpret_cast<const GBlock*>(base + bt + bi);
+    g.n_terms = static_cast<int>(h->gterms.size());
+    g.n_in_blocks = static_cast<int>(h->gin.size());
+    g.n_out_blocks = static_cast<int>(h->gout.size());
+    g.nv = h->d.n;
+    g.no = h->d.nout;
+    g.numel = h->d.numel;
+    rc = launch_symcon_generic(a, g);
+  }
+  if (rc != 0)
+    return fail(SEGPOLY_E_HIP, std::string("kernel launch failed: ") + hipGetErrorString(static_cast<hipError_t>(rc)));
+  return ok();
+}
+
+int symcon_destroy(symcon_handle h) {
+  if (!h) return ok();
+  free_all(h->dev);
+  delete h;
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,385 @@
+// Build-time generator of the specialised kernels.
+//
+// Reads a list of descriptors (specs.txt) and, for each, writes one HIP
+// translation unit with a struct whose device functions carry the coupling
+// coefficients of that descriptor as literal constants ("known at compile
+// time and mostly zero", e3nn-course Lesson 12a, section 21.1), plus a
+// registry mapping each descriptor's structure key to its launcher.  The
+// kernel skeletons themselves are hand-written (kernels/*.hpp); only the
+// per-descriptor arithmetic is emitted here.
+//
+// Spec lines:
+//   tp     NAME DTYPES | IRREPS_IN1 | IRREPS_IN2 | IRREPS_OUT_FILTER
+//   symcon NAME DTYPES | IRREPS_IN | IRREPS_OUT | DEGREES
+// DTYPES is f32, f64 or f32,f64.  Multiplicities in the strings only fix the
+// structure; the kernels take the multiplicity at run time.
+#include <cmath>
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+#include <fstream>
+#include <iostream>
+#include <map>
+#include <set>
+#include <sstream>
+#include <string>
+#include <tuple>
+#include <vector>
+
+#include "symcon_descriptor.hpp"
+#include "tp_descriptor.hpp"
+
+using namespace segpoly;
+
+namespace {
+
+std::string lit(double v) {
+  char buf[64];
+  std::snprintf(buf, sizeof buf, "T(%.17g)", v);
+  return buf;
+}
+
+std::string trim(const std::string& s) {
+  size_t a = s.find_first_not_of(" \t\r\n");
+  size_t b = s.find_last_not_of(" \t\r\n");
+  return a == std::string::npos ? "" : s.substr(a, b - a + 1);
+}
+
+std::vector<std::string> split(const std::string& s, char c) {
+  std::vector<std::string> out;
+  std::stringstream ss(s);
+  std::string item;
+  while (std::getline(ss, item, c)) out.push_back(trim(item));
+  return out;
+}
+
+unsigned dtype_mask(const std::string& s) {
+  unsigned m = 0;
+  for (const auto& t : split(s, ',')) {
+    if (t == "f32") m |= 1u;
+    else if (t == "f64") m |= 2u;
+    else throw std::runtime_error("bad dtype list " + s);
+  }
+  return m;
+}
+
+// ---------------------------------------------------------------- TP
+
+struct QTable {
+  // uniform coefficient products q[n] = |c| * sh[j]; |c| == 1 -> raw sh
+  std::map<std::pair<uint64_t, int>, int> index;
+  std::vector<std::pair<double, int>> entries;
+  int get(double absc, int j) {
+    uint64_t bits;
+    std::memcpy(&bits, &absc, sizeof bits);
+    auto key = std::make_pair(bits, j);
+    auto it = index.find(key);
+    if (it != index.end()) return it->second;
+    int id = static_cast<int>(entries.size());
+    index[key] = id;
+    entries.push_back({absc, j});
+    return id;
+  }
+};
+
+bool is_identity_l2_zero(const TPPath& p) {
+  if (p.l2 != 0 || p.l1 != p.lo) return false;
+  for (const auto& e : p.nz)
+    if (e.c != 1.0 || e.i != e.k || e.j != 0) return false;
+  return static_cast<int>(p.nz.size()) == 2 * p.l1 + 1;
+}
+
+bool is_identity_l1_zero(const TPPath& p) {
+  if (p.l1 != 0 || p.l2 != p.lo) return false;
+  for (const auto& e : p.nz)
+    if (e.c != 1.0 || e.j != e.k || e.i != 0) return false;
+  return static_cast<int>(p.nz.size()) == 2 * p.l2 + 1;
+}
+
+void emit_tp(const std::string& name, unsigned dtypes, const TPDescriptor& d, std::ostream& os) {
+  if (!d.uniform_mul) throw std::runtime_error("spec " + name + ": input-1 multiplicities must be uniform");
+  const std::string S = "TPSpec_" + name;
+  QTable q;
+  std::ostringstream edge;
+  for (size_t pi = 0; pi < d.paths.size(); ++pi) {
+    const TPPath& p = d.paths[pi];
+    const int X = p.xcomp, K = p.kcomp, J = static_cast<int>(p.off2);
+    edge << "    // path " << pi << ": " << p.l1 << " x " << p.l2 << " -> " << p.lo << " (" << p.nz.size()
+         << " non-zero)\n    {\n";
+    if (is_identity_l2_zero(p)) {
+      int qs = q.get(1.0, J);
+      edge << "      const T ws = wv[" << pi << "] * q[" << qs << "];\n";
+      for (int k = 0; k < 2 * p.lo + 1; ++k)
+        edge << "      acc[" << K + k << "] = fmadd(ws, xv[" << X + k << "], acc[" << K + k << "]);\n";
+    } else if (is_identity_l1_zero(p)) {
+      edge << "      const T xw = wv[" << pi << "] * xv[" << X << "];\n";
+      for (int k = 0; k < 2 * p.lo + 1; ++k) {
+        int qs = q.get(1.0, J + k);
+        edge << "      acc[" << K + k << "] = fmadd(xw, q[" << qs << "], acc[" << K + k << "]);\n";
+      }
+    } else if (2 * p.l1 + 1 < 2 * p.lo + 1) {
+      // fold the weight into the inputs: (2l1+1) products, then nnz FMAs
+      for (int i = 0; i < 2 * p.l1 + 1; ++i)
+        edge << "      const T xw" << i << " = wv[" << pi << "] * xv[" << X + i << "];\n";
+      for (const auto& e : p.nz) {
+        int qi = q.get(std::fabs(e.c), J + e.j);
+        edge << "      acc[" << K + e.k << "] = fmadd(" << (e.c < 0 ? "-" : "") << "q[" << qi << "], xw" << e.i
+             << ", acc[" << K + e.k << "]);\n";
+      }
+    } else {
+      // per output component: t = sum (c sh_j) x_i, then acc += w t
+      int cur = -1;
+      for (size_t n = 0; n < p.nz.size(); ++n) {
+        const auto& e = p.nz[n];
+        int qi = q.get(std::fabs(e.c), J + e.j);
+        std::string term = std::string(e.c < 0 ? "-" : "") + "q[" + std::to_string(qi) + "]";
+        if (e.k != cur) {
+          cur = e.k;
+          edge << "      T t" << e.k << " = " << term << " * xv[" << X + e.i << "];\n";
+        } else {
+          edge << "      t" << e.k << " = fmadd(" << term << ", xv[" << X + e.i << "], t" << e.k << ");\n";
+        }
+        bool last = (n + 1 == p.nz.size()) || p.nz[n + 1].k != e.k;
+        if (last)
+          edge << "      acc[" << K + e.k << "] = fmadd(wv[" << pi << "], t" << e.k << ", acc[" << K + e.k
+               << "]);\n";
+      }
+    }
+    edge << "    }\n";
+  }
+
+  os << "// Generated by codegen.cpp from the descriptor: " << irreps_str(d.in1) << " x " << irreps_str(d.in2)
+     << " -> " << irreps_str(d.out) << "\n// key " << d.key << "\n";
+  os << "#include \"kernels/tp_conv_spec.hpp\"\n\nnamespace segpoly {\nnamespace kern {\n\n";
+  os << "struct " << S << " {\n";
+  os << "  static constexpr int NX = " << d.nx << ";\n";
+  os << "  static constexpr int NK = " << d.nk << ";\n";
+  os << "  static constexpr int NP = " << d.paths.size() << ";\n";
+  os << "  static constexpr int D2 = " << d.dim2 << ";\n";
+  os << "  static constexpr int NQ = " << q.entries.size() << ";\n\n";
+  // coef
+  os << "  template <typename T>\n  __device__ __forceinline__ static void coef(const T* __restrict__ sh, T* q) {\n";
+  for (size_t n = 0; n < q.entries.size(); ++n) {
+    const auto& [c, j] = q.entries[n];
+    if (c == 1.0)
+      os << "    q[" << n << "] = sh[" << j << "];\n";
+    else
+      os << "    q[" << n << "] = " << lit(c) << " * sh[" << j << "];\n";
+  }
+  os << "  }\n\n";
+  // load_x
+  os << "  template <typename T, int LAYOUT>\n  __device__ __forceinline__ static void load_x(const T* __restrict__ row, int mul, int u, T* xv) {\n";
+  os << "    if constexpr (LAYOUT == kIrMul) {\n";
+  for (int m = 0; m < d.nx; ++m) os << "      xv[" << m << "] = row[" << m << " * mul + u];\n";
+  os << "    } else {\n";
+  for (size_t b = 0; b < d.in1.size(); ++b) {
+    int comp = 0;
+    for (size_t bb = 0; bb < b; ++bb) comp += 2 * d.in1[bb].l + 1;
+    const int dl = 2 * d.in1[b].l + 1;
+    os << "      {\n        const T* p = row + " << comp << " * mul + u * " << dl << ";\n";
+    for (int i = 0; i < dl; ++i) os << "        xv[" << comp + i << "] = p[" << i << "];\n";
+    os << "      }\n";
+  }
+  os << "    }\n  }\n\n";
+  // edge
+  os << "  template <typename T>\n  __device__ __forceinline__ static void edge(const T* xv, const T* q, const T* wv, T* acc) {\n";
+  os << edge.str();
+  os << "  }\n\n";
+  // store
+  os << "  template <typename T, int LAYOUT>\n  __device__ __forceinline__ static void store(T* __restrict__ row, int mul, int u, const T* acc) {\n";
+  os << "    if constexpr (LAYOUT == kIrMul) {\n";
+  for (int k = 0; k < d.nk; ++k) os << "      row[" << k << " * mul + u] = acc[" << k << "];\n";
+  os << "    } else {\n";
+  for (const auto& p : d.paths) {
+    const int dl = 2 * p.lo + 1;
+    os << "      {\n        T* p = row + " << p.kcomp << " * mul + u * " << dl << ";\n";
+    for (int k = 0; k < dl; ++k) os << "        p[" << k << "] = acc[" << p.kcomp + k << "];\n";
+    os << "      }\n";
+  }
+  os << "    }\n  }\n};\n\n}  // namespace kern\n\n";
+  os << "int launch_tp_" << name << "(const TPArgs& a) {\n";
+  if (dtypes & 1u) os << "  if (a.dtype == kF32) return kern::tp_conv_spec_dispatch<kern::" << S << ", float>(a);\n";
+  if (dtypes & 2u) os << "  if (a.dtype == kF64) return kern::tp_conv_spec_dispatch<kern::" << S << ", double>(a);\n";
+  os << "  return -1;\n}\n\n}  // namespace segpoly\n";
+}
+
+// ---------------------------------------------------------------- symcon
+
+void emit_symcon(const std::string& name, unsigned dtypes, const SymconDescriptor& d, std::ostream& os) {
+  const std::string S = "SymconSpec_" + name;
+  const int n = d.n;
+  const int ns = static_cast<int>(d.couplings.size());
+  // monomial -> [(segment, M, c)]
+  std::map<std::tuple<int, int, int>, std::vector<std::tuple<int, int, double>>> mono;
+  for (int s = 0; s < ns; ++s)
+    for (const auto& t : d.couplings[s].terms) mono[{t.m[0], t.m[1], t.m[2]}].push_back({s, t.M, t.c});
+  std::set<std::pair<int, int>> used_acc;
+  std::ostringstream body;
+  auto accum = [&](const std::string& m, const std::vector<std::tuple<int, int, double>>& terms) {
+    for (const auto& [s, M, c] : terms) {
+      const std::string a = "a" + std::to_string(s) + "_" + std::to_string(M);
+      if (!used_acc.count({s, M})) {
+        used_acc.insert({s, M});
+        body << "    T " << a << " = " << lit(c) << " * " << m << ";\n";
+      } else {
+        body << "    " << a << " = fmadd(" << lit(c) << ", " << m << ", " << a << ");\n";
+      }
+    }
+  };
+  // degree 1
+  for (int a = 0; a < n; ++a) {
+    auto it = mono.find({a, -1, -1});
+    if (it != mono.end()) accum("v[" + std::to_string(a) + "]", it->second);
+  }
+  // degrees 2 and 3, grouped by the sorted prefix (a, b)
+  for (int a = 0; a < n; ++a)
+    for (int b = a; b < n; ++b) {
+      bool need = mono.count({a, b, -1}) > 0;
+      for (int c = b; c < n && !need; ++c) need = mono.count({a, b, c}) > 0;
+      if (!need) continue;
+      const std::string p = "p" + std::to_string(a) + "_" + std::to_string(b);
+      body << "    const T " << p << " = v[" << a << "] * v[" << b << "];\n";
+      auto it = mono.find({a, b, -1});
+      if (it != mono.end()) accum(p, it->second);
+      for (int c = b; c < n; ++c) {
+        auto jt = mono.find({a, b, c});
+        if (jt == mono.end()) continue;
+        const std::string m = "m" + std::to_string(a) + "_" + std::to_string(b) + "_" + std::to_string(c);
+        body << "    const T " << m << " = " << p << " * v[" << c << "];\n";
+        accum(m, jt->second);
+      }
+    }
+  // outputs
+  for (size_t ob = 0; ob < d.out.size(); ++ob) {
+    const int dL = 2 * d.out[ob].l + 1;
+    for (int M = 0; M < dL; ++M) {
+      const int og = d.out_comp[ob] + M;
+      bool first = true;
+      for (int s = 0; s < ns; ++s) {
+        if (d.couplings[s].ob != static_cast<int>(ob) || !used_acc.count({s, M})) continue;
+        const std::string a = "a" + std::to_string(s) + "_" + std::to_string(M);
+        if (first)
+          body << "    o[" << og << "] = wv[" << s << "] * " << a << ";\n";
+        else
+          body << "    o[" << og << "] = fmadd(wv[" << s << "], " << a << ", o[" << og << "]);\n";
+        first = false;
+      }
+      if (first) body << "    o[" << og << "] = T(0);\n";
+    }
+  }
+
+  os << "// Generated by codegen.cpp from the descriptor: symmetric contraction " << irreps_str(d.in) << " -> "
+     << irreps_str(d.out) << "\n// key " << d.key << "\n// " << d.num_terms() << " sorted-monomial terms\n";
+  os << "#include \"kernels/symcon_spec.hpp\"\n\nnamespace segpoly {\nnamespace kern {\n\n";
+  os << "struct " << S << " {\n";
+  os << "  static constexpr int NV = " << n << ";\n";
+  os << "  static constexpr int NO = " << d.nout << ";\n";
+  os << "  static constexpr int NS = " << ns << ";\n\n";
+  os << "  template <typename T, int LAYOUT>\n  __device__ __forceinline__ static void load_v(const T* __restrict__ row, int mul, int u, T* v) {\n";
+  os << "    if constexpr (LAYOUT == kIrMul) {\n";
+  for (int m = 0; m < n; ++m) os << "      v[" << m << "] = row[" << m << " * mul + u];\n";
+  os << "    } else {\n";
+  for (size_t b = 0; b < d.in.size(); ++b) {
+    const int dl = 2 * d.in[b].l + 1, comp = d.in_comp[b];
+    os << "      {\n        const T* p = row + " << comp << " * mul + u * " << dl << ";\n";
+    for (int i = 0; i < dl; ++i) os << "        v[" << comp + i << "] = p[" << i << "];\n";
+    os << "      }\n";
+  }
+  os << "    }\n  }\n\n";
+  os << "  template <typename T>\n  __device__ __forceinline__ static void eval(const T* v, const T* wv, T* o) {\n";
+  os << body.str();
+  os << "  }\n\n";
+  os << "  template <typename T, int LAYOUT>\n  __device__ __forceinline__ static void store(T* __restrict__ row, int mul, int u, const T* o) {\n";
+  os << "    if constexpr (LAYOUT == kIrMul) {\n";
+  for (int k = 0; k < d.nout; ++k) os << "      row[" << k << " * mul + u] = o[" << k << "];\n";
+  os << "    } else {\n";
+  for (size_t b = 0; b < d.out.size(); ++b) {
+    const int dl = 2 * d.out[b].l + 1, comp = d.out_comp[b];
+    os << "      {\n        T* p = row + " << comp << " * mul + u * " << dl << ";\n";
+    for (int i = 0; i < dl; ++i) os << "        p[" << i << "] = o[" << comp + i << "];\n";
+    os << "      }\n";
+  }
+  os << "    }\n  }\n};\n\n}  // namespace kern\n\n";
+  os << "int launch_symcon_" << name << "(const SymconArgs& a) {\n";
+  if (dtypes & 1u) os << "  if (a.dtype == kF32) return kern::symcon_spec_dispatch<kern::" << S << ", float>(a);\n";
+  if (dtypes & 2u) os << "  if (a.dtype == kF64) return kern::symcon_spec_dispatch<kern::" << S << ", double>(a);\n";
+  os << "  return -1;\n}\n\n}  // namespace segpoly\n";
+}
+
+}  // namespace
+
+int main(int argc, char** argv) {
+  if (argc != 3) {
+    std::cerr << "usage: segpoly_codegen SPECS OUTDIR\n";
+    return 2;
+  }
+  std::ifstream in(argv[1]);
+  if (!in) {
+    std::cerr << "cannot read " << argv[1] << "\n";
+    return 2;
+  }
+  const std::string outdir = argv[2];
+  struct Reg {
+    std::string kind, name, key;
+    unsigned dtypes;
+  };
+  std::vector<Reg> regs;
+  std::string line;
+  try {
+    while (std::getline(in, line)) {
+      line = trim(line);
+      if (line.empty() || line[0] == '#') continue;
+      auto parts = split(line, '|');
+      if (parts.size() != 4) throw std::runtime_error("bad spec line: " + line);
+      auto head = split(parts[0], ' ');
+      std::vector<std::string> h;
+      for (auto& t : head)
+        if (!t.empty()) h.push_back(t);
+      if (h.size() != 3) throw std::runtime_error("bad spec head: " + parts[0]);
+      const std::string kind = h[0], name = h[1];
+      const unsigned dt = dtype_mask(h[2]);
+      const std::string path = outdir + "/" + kind + "_" + name + ".hip";
+      std::ofstream os(path);
+      if (kind == "tp") {
+        TPDescriptor d = build_tp(parts[1], parts[2], parts[3]);
+        emit_tp(name, dt, d, os);
+        regs.push_back({kind, name, d.key, dt});
+      } else if (kind == "symcon") {
+        std::vector<int> deg;
+        for (auto& t : split(parts[3], ',')) deg.push_back(std::stoi(t));
+        SymconDescriptor d = build_symcon(parts[1], parts[2], deg);
+        emit_symcon(name, dt, d, os);
+        regs.push_back({kind, name, d.key, dt});
+      } else {
+        throw std::runtime_error("unknown spec kind " + kind);
+      }
+      std::cout << path << "\n";
+    }
+  } catch (const std::exception& e) {
+    std::cerr << "codegen: " << e.what() << "\n";
+    return 1;
+  }
+  std::ofstream reg(outdir + "/registry.cpp");
+  reg << "// Generated by codegen.cpp: structure key -> specialised launcher.\n#include \"launch.hpp\"\n\nnamespace segpoly {\n\n";
+  for (const auto& r : regs)
+    reg << "int launch_" << r.kind << "_" << r.name << "(const " << (r.kind == "tp" ? "TPArgs" : "SymconArgs")
+        << "&);\n";
+  reg << "\nconst TPSpecEntry kTPSpecs[] = {\n";
+  int ntp = 0, nsc = 0;
+  for (const auto& r : regs)
+    if (r.kind == "tp") {
+      reg << "    {\"" << r.key << "\", \"" << r.name << "\", " << r.dtypes << "u, &launch_tp_" << r.name << "},\n";
+      ++ntp;
+    }
+  if (!ntp) reg << "    {\"\", \"\", 0u, nullptr},\n";
+  reg << "};\nconst int kNumTPSpecs = " << ntp << ";\n\nconst SymconSpecEntry kSymconSpecs[] = {\n";
+  for (const auto& r : regs)
+    if (r.kind == "symcon") {
+      reg << "    {\"" << r.key << "\", \"" << r.name << "\", " << r.dtypes << "u, &launch_symcon_" << r.name
+          << "},\n";
+      ++nsc;
+    }
+  if (!nsc) reg << "    {\"\", \"\", 0u, nullptr},\n";
+  reg << "};\nconst int kNumSymconSpecs = " << nsc << ";\n\n}  // namespace segpoly\n";
+  return 0;
+}

@@ -1,0 +1,192 @@
+"""The C ABI on the host (no GPU needed, no kernel launched): the library
+loads and exports every declared symbol; the C++ descriptor builder agrees
+with the oracle (paths, output irreps, coefficients, symmetric-contraction
+basis); invalid arguments fail closed with the documented status codes."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+from hypothesis import given, settings, strategies as st
+
+import segmented_polynomials_amd as sp
+from oracle import cg as ocg, irreps as oirreps, symcon as osymcon, tp as otp
+import workloads
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "segpoly.h")
+
+
+def test_one_hip_runtime_per_process():
+    # the library must use the HIP runtime PyTorch loaded, not a second copy
+    assert len(sp.hip_runtimes_loaded()) == 1, sp.hip_runtimes_loaded()
+
+
+def test_exports_every_declared_symbol():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = set(re.findall(r"^\s*(?:int|const char\*)\s+(\w+)\s*\(", text, flags=re.M))
+    assert names == set(sp.EXPORTS)
+    for n in names:
+        assert hasattr(sp.lib, n), n
+    assert "gfx950" in sp.version()
+
+
+@pytest.mark.parametrize("l1,l2", [(a, b) for a in range(5) for b in range(5)])
+def test_real_cg_matches_oracle(l1, l2):
+    for l3 in range(abs(l1 - l2), l1 + l2 + 1):
+        a = sp.real_cg(l1, l2, l3)
+        b = ocg.real_cg(l1, l2, l3)
+        assert np.abs(a - b).max() <= 2e-16 * max(1, np.abs(b).max()), (l1, l2, l3)
+        assert np.array_equal(a != 0, b != 0)
+
+
+def _compare_tp(in1, in2, filt, layout="mul_ir"):
+    h = sp.tp_create(in1, in2, filt, layout=layout)
+    o = otp.ChannelwiseTP(in1, in2, filt)
+    assert h.irreps_out == o.irreps_out
+    assert (h.num_paths, h.weight_numel, h.dim_in1, h.dim_in2, h.dim_out) == \
+        (o.num_paths, o.weight_numel, o.dim_in1, o.dim_in2, o.dim_out)
+    woff = 0
+    for p, (i, j, lo, po) in enumerate(o.paths):
+        info = h.path_info(p)
+        assert (info["in1_block"], info["in2_block"], info["lo"], info["parity"]) == (i, j, lo, po)
+        assert info["weight_offset"] == woff
+        woff += o.in1[i][0]
+        l1, l2 = o.in1[i][1], o.in2[j][1]
+        c = ocg.real_cg(l1, l2, lo)
+        assert np.abs(h.path_cg(p) - c).max() <= 2e-16
+        assert info["nnz"] == np.count_nonzero(c)
+    assert h.cg_nnz == sum(r[3] for r in o.path_table())
+    return h
+
+
+@pytest.mark.parametrize("n", [1, 2, 3, 4])
+def test_workload_descriptors_match_oracle_and_are_specialized(n):
+    wl = workloads.WORKLOADS[n]
+    for lay in wl.layouts:
+        h = _compare_tp(wl.irreps_in1, wl.irreps_in2, wl.irreps_out, lay)
+        assert h.specialized, h.kernel_name
+        g = sp.tp_create(wl.irreps_in1, wl.irreps_in2, wl.irreps_out, layout=lay, force_generic=True)
+        assert not g.specialized and g.kernel_name == "tp_conv_generic"
+
+
+def test_page_descriptor():
+    h = _compare_tp("32x0e+32x1o", "0e+1o", "32x0e+32x1o")
+    assert h.num_paths == 4 and h.weight_numel == 128
+    assert h.irreps_out == "32x0e+32x0e+32x1o+32x1o"
+
+
+_irrep = st.tuples(st.integers(1, 5), st.integers(0, 3), st.sampled_from("eo"))
+
+
+@settings(max_examples=60, deadline=None)
+@given(st.lists(_irrep, min_size=1, max_size=4), st.lists(st.tuples(st.integers(0, 3), st.sampled_from("eo")),
+                                                          min_size=1, max_size=4),
+       st.lists(st.tuples(st.integers(0, 4), st.sampled_from("eo")), min_size=1, max_size=6))
+def test_fuzz_tp_descriptor(b1, b2, bo):
+    in1 = "+".join(f"{m}x{l}{p}" for m, l, p in b1)
+    in2 = "+".join(f"{l}{p}" for l, p in b2)
+    filt = "+".join(f"{l}{p}" for l, p in bo)
+    _compare_tp(in1, in2, filt)
+
+
+@pytest.mark.parametrize("ins,outs", [
+    ("32x0e+32x1o", "32x0e"),
+    ("4x0e+4x1o+4x2e+4x3o", "4x0e+4x1o"),
+    ("3x0e+3x1o+3x2e", "3x0e+3x1o+3x2e"),
+    ("2x0o+2x1e", "2x0e+2x1o"),
+])
+def test_symcon_basis_matches_oracle(ins, outs):
+    h = sp.symcon_create(ins, outs, max_degree=3, num_elements=2)
+    o = osymcon.SymmetricContraction(ins, outs)
+    assert h.weight_numel == o.weight_numel and h.num_couplings == len(o.segments)
+    assert (h.dim_in, h.dim_out) == (o.dim_in, o.dim_out)
+    for c, (nu, ob, k) in enumerate(o.segments):
+        info = h.coupling_info(c)
+        assert (info["degree"], info["out_block"], info["k"]) == (nu, ob, k)
+        a = h.coupling_dense(c, o.n)
+        b = o.basis[(nu, ob)][k]
+        assert np.abs(a - b).max() < 1e-13
+    # the span (a basis-free quantity) agrees too
+    for (nu, ob), us in o.basis.items():
+        if not us:
+            continue
+        idx = [c for c, s in enumerate(o.segments) if s[:2] == (nu, ob)]
+        A = np.stack([h.coupling_dense(c, o.n).ravel() for c in idx], 1)
+        B = np.stack([u.ravel() for u in us], 1)
+        pa = A @ np.linalg.pinv(A)
+        pb = B @ np.linalg.pinv(B)
+        assert np.abs(pa - pb).max() < 1e-10
+
+
+def test_symcon_workload5_specialized():
+    wl = workloads.WORKLOADS[5]
+    h = sp.symcon_create(wl.irreps_in, wl.irreps_out, 3, wl.num_elements, layout="ir_mul")
+    assert h.specialized
+    assert h.weight_numel == 3712 and h.num_couplings == 29
+    assert h.num_terms == 550
+
+
+# ---------------------------------------------------------------- errors
+
+def _raw_create(*args):
+    raw = ctypes.c_void_p()
+    return sp.lib.tp_create(*args, ctypes.byref(raw)), raw
+
+
+def test_create_errors():
+    assert _raw_create(b"32x1q", b"0e", b"0e", 0, 0, 0)[0] == sp.E_PARSE
+    assert _raw_create(b"3x", b"0e", b"0e", 0, 0, 0)[0] == sp.E_PARSE
+    assert _raw_create(b"4x0e", b"2x1o", b"1o", 0, 0, 0)[0] == sp.E_UNSUPPORTED
+    assert _raw_create(b"4x9e", b"0e", b"9e", 0, 0, 0)[0] == sp.E_UNSUPPORTED
+    assert _raw_create(b"4x0e", b"0e", b"0e", 7, 0, 0)[0] == sp.E_INVALID
+    assert _raw_create(b"4x0e", b"0e", b"0e", 0, 5, 0)[0] == sp.E_INVALID
+    assert _raw_create(b"4x0e", b"0e", b"0e", 0, 0, 64)[0] == sp.E_INVALID
+    assert sp.lib.tp_create(None, b"0e", b"0e", 0, 0, 0, None) == sp.E_INVALID
+    assert sp.lib.segpoly_last_error()
+    with pytest.raises(sp.SegpolyError) as e:
+        sp.symcon_create("2x0e+3x1o", "2x0e")
+    assert e.value.code == sp.E_UNSUPPORTED
+    with pytest.raises(sp.SegpolyError):
+        sp.symcon_create("2x0e", "2x0e", max_degree=4)
+
+
+def test_query_errors():
+    h = sp.tp_create("4x0e+4x1o", "0e+1o", "0e+1o")
+    v = ctypes.c_int64()
+    assert sp.lib.tp_query(h._h, 99, ctypes.byref(v)) == sp.E_INVALID
+    assert sp.lib.tp_query(None, 0, ctypes.byref(v)) == sp.E_INVALID
+    buf = ctypes.create_string_buffer(3)
+    assert sp.lib.tp_irreps_out(h._h, buf, 3) == sp.E_INVALID
+    info = (ctypes.c_int64 * 10)()
+    assert sp.lib.tp_path_info(h._h, 99, info) == sp.E_INVALID
+
+
+def test_forward_argument_errors_fail_before_any_gpu_call():
+    h = sp.tp_create("4x0e+4x1o", "0e+1o", "0e+1o")
+    f = sp.lib.tp_conv_fwd
+    p = ctypes.c_void_p(16)   # never dereferenced: every call below fails validation
+    assert f(None, p, 1, p, p, p, p, 0, 1, 1, p, None) == sp.E_INVALID
+    assert f(h._h, p, -1, p, p, p, p, 0, 1, 1, p, None) == sp.E_INVALID
+    assert f(h._h, p, 1, p, p, p, None, 0, 1, 1, p, None) == sp.E_INVALID      # src without dst
+    assert f(h._h, p, 1, p, p, None, None, 0, 2, 2, p, None) == sp.E_INVALID   # batch: n_src < n_edges
+    assert f(h._h, p, 4, p, p, None, None, 0, 2, 3, p, None) == sp.E_INVALID   # batch: n_edges != n_nodes
+    assert f(h._h, p, 1, p, p, p, p, 9, 1, 1, p, None) == sp.E_INVALID         # index dtype
+    assert f(h._h, p, 1, p, p, p, p, 0, 1, 1, None, None) == sp.E_INVALID      # null out
+    assert f(h._h, p, 1, p, None, p, p, 0, 1, 1, p, None) == sp.E_INVALID      # null w
+    assert f(h._h, p, 1, p, p, p, p, 0, 1, 1 << 31, p, None) == sp.E_UNSUPPORTED
+    # nothing to do: succeeds without touching a device
+    assert f(h._h, None, 0, None, None, None, None, 0, 0, 0, None, None) == sp.OK
+    s = sp.symcon_create("2x0e+2x1o", "2x0e", 3, 2)
+    g = sp.lib.symcon_fwd
+    assert g(s._h, p, p, 0, p, -1, p, None) == sp.E_INVALID
+    assert g(s._h, p, None, 0, p, 3, p, None) == sp.E_INVALID
+    assert g(s._h, p, p, 3, p, 3, p, None) == sp.E_INVALID
+    assert g(s._h, None, None, 0, None, 0, None, None) == sp.OK
+
+
+def test_destroy_null_is_noop():
+    assert sp.lib.tp_destroy(None) == sp.OK
+    assert sp.lib.symcon_destroy(None) == sp.OK
