@@ -1,0 +1,249 @@
+"""Benchmark of the fused channelwise tensor-product convolution on one MI355X.
+
+One step = one fused TP-conv forward over the large synthetic graph (20,000
+nodes, 600,000 edges, in-degree 30, dst-sorted; features
+128x0e+128x1o+128x2e, edge harmonics l <= 3, per-edge weights, output types
+0e+1o+2e): gather, all 13 paths, per-edge weights and the segmented
+sum-scatter in one kernel launch.  Inputs are resident in HBM before the
+timed region.  The symmetric contraction (second client, 50,000 atoms) and
+the other layout are timed in the same run and reported in their own
+objects; the oracle is timed on a bounded sample on the host cores.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--layout ir_mul|mul_ir]
+
+Prints one JSON line.
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0            # MI355X HBM3E, published
+FP32_VALU_PEAK_TFLOPS = 78.6      # 256 CU x 4 SIMD x 16 lanes x 2 flop x 2.4 GHz (no packed FP32)
+METRIC = "edges/sec + achieved HBM GB/s (fraction of peak) for fused equivariant TP-conv"
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--layout", default="ir_mul", choices=["ir_mul", "mul_ir"])
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-extras", action="store_true", help="skip the second layout and the symmetric contraction")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="also run a plain 1 GiB device copy (for the HBM counter scale factor)")
+    return p.parse_args()
+
+
+def kernel_source_hash():
+    """Hash of everything the timed kernel is generated from, to tell whether
+    stored hardware counters still describe it."""
+    h = hashlib.sha256()
+    base = os.path.join(ROOT, "segmented_polynomials_amd", "csrc")
+    for rel in ("kernels/tp_conv_spec.hpp", "kernels/common.hpp", "codegen.cpp", "specs.txt",
+                "tp_descriptor.cpp", "cg.cpp"):
+        with open(os.path.join(base, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(layout):
+    """HBM bytes per launch from the committed counter summary, or None if
+    the summary is missing or was taken on a different kernel."""
+    path = os.path.join(ROOT, "profiles", f"tp_conv_large_graph_{layout}_hbm_counters.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    mh = re.search(r"kernel_source_hash:\s*(\w+)", text)
+    mb = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not mh or not mb or mh.group(1) != kernel_source_hash():
+        return None
+    return float(mb.group(1))
+
+
+def time_launches(torch, fn, steps, warmup):
+    """Warm up, then time `steps` launches: total wall time bracketed by
+    synchronisations, and per-launch HIP events on the launch stream."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for a, b in ev:
+        a.record(stream)
+        fn()
+        b.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = sorted(a.elapsed_time(b) for a, b in ev)   # ms
+    return wall, per
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the multi-GPU design is described, not built).", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import segmented_polynomials_amd as sp
+    import workloads
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    wl = workloads.WORKLOADS[4]
+    layout = args.layout
+    h = sp.tp_create(wl.irreps_in1, wl.irreps_in2, wl.irreps_out, layout=layout)
+    fan_in = workloads.fan_in_from_irreps_out(h.irreps_out)
+    inp = workloads.tp_inputs(wl, fan_in)
+    N, E = inp["n_nodes"], inp["sh"].shape[0]
+    to = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    x, sh, w = to(inp["x"]), to(inp["sh"]), to(inp["w"])
+    src, dst = to(inp["src"]), to(inp["dst"])
+    out = torch.empty((N, h.dim_out), dtype=torch.float32, device=dev)
+    # keep only what the host-side baseline needs
+    sample_nodes = 1000
+    base_inp = dict(x=inp["x"], sh=inp["sh"][:sample_nodes * wl.degree], w=inp["w"][:sample_nodes * wl.degree],
+                    src=inp["src"][:sample_nodes * wl.degree], dst=inp["dst"][:sample_nodes * wl.degree],
+                    n_nodes=sample_nodes)
+    del inp
+
+    fwd = lambda: sp.tp_conv_fwd(h, x, sh, w, src, dst, n_nodes=N, out=out)
+    wall, per = time_launches(torch, fwd, args.steps, args.warmup)
+    ms_per_step = wall * 1e3 / args.steps
+    avg_kernel_ms = sum(per) / len(per)
+
+    # algorithmic bytes per launch: every operand read or written once
+    bytes_w = E * h.weight_numel * 4
+    bytes_sh = E * h.dim_in2 * 4
+    bytes_idx = 2 * E * 4
+    bytes_x = N * h.dim_in1 * 4
+    bytes_out = N * h.dim_out * 4
+    alg_bytes = bytes_w + bytes_sh + bytes_idx + bytes_x + bytes_out
+    alg_flops = E * (2 * h.mul * h.cg_nnz + h.mul * (h.dim_out // h.mul))
+    achieved_gbps = alg_bytes / (avg_kernel_ms * 1e-3) / 1e9
+    edges_per_s = E / (ms_per_step * 1e-3)
+    traffic = stored_traffic(layout)
+
+    result = {
+        "metric": METRIC,
+        "value": edges_per_s,
+        "unit": "edges/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "nodes": N, "edges": E, "in_degree": wl.degree,
+                   "irreps_in1": wl.irreps_in1, "irreps_sh": wl.irreps_in2, "irreps_out": h.irreps_out,
+                   "layout": layout, "index_dtype": "int32", "kernel": h.kernel_name},
+        "hbm_GBps_algorithmic": achieved_gbps,
+        "hbm_fraction_of_peak": achieved_gbps / HBM_PEAK_GBPS,
+        "kernel_ms": {"mean": avg_kernel_ms, "min": per[0], "median": per[len(per) // 2]},
+        "roofline": {"bound": "hbm", "achieved": achieved_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": achieved_gbps / HBM_PEAK_GBPS,
+                     "traffic": traffic,
+                     "algorithmic_bytes_per_launch": alg_bytes,
+                     "algorithmic_bytes_per_edge": alg_bytes / E,
+                     "algorithmic_flops_per_launch": alg_flops},
+    }
+
+    if not args.no_extras:
+        import gc
+        # the other layout (same inputs reinterpreted: timing only)
+        other = "mul_ir" if layout == "ir_mul" else "ir_mul"
+        h2 = sp.tp_create(wl.irreps_in1, wl.irreps_in2, wl.irreps_out, layout=other)
+        f2 = lambda: sp.tp_conv_fwd(h2, x, sh, w, src, dst, n_nodes=N, out=out)
+        wall2, per2 = time_launches(torch, f2, args.steps, args.warmup)
+        k2 = sum(per2) / len(per2)
+        result[f"tp_conv_{other}"] = {"edges_per_s": E / (wall2 / args.steps), "kernel_ms": k2,
+                                      "hbm_GBps_algorithmic": alg_bytes / (k2 * 1e-3) / 1e9,
+                                      "hbm_fraction_of_peak": alg_bytes / (k2 * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+                                      "kernel": h2.kernel_name, "traffic": stored_traffic(other)}
+        del x, sh, w, src, dst, out
+        gc.collect()
+        torch.cuda.empty_cache()
+
+        # symmetric contraction, 50,000 atoms
+        s5 = workloads.WORKLOADS[5]
+        hs = sp.symcon_create(s5.irreps_in, s5.irreps_out, 3, s5.num_elements, layout="ir_mul")
+        k = {}
+        for c in range(hs.num_couplings):
+            i = hs.coupling_info(c)
+            k[(i["degree"], i["out_block"])] = k.get((i["degree"], i["out_block"]), 0) + 1
+        sfan = np.concatenate([np.full(hs.mul, k[(hs.coupling_info(c)["degree"], hs.coupling_info(c)["out_block"])])
+                               for c in range(hs.num_couplings)])
+        si = workloads.symcon_inputs(s5, sfan)
+        sx, ssp, sw = to(si["x"]), to(si["species"]), to(si["w"])
+        sout = torch.empty((s5.n_atoms, hs.dim_out), dtype=torch.float32, device=dev)
+        fs = lambda: sp.symcon_fwd(hs, sx, ssp, sw, out=sout)
+        wall3, per3 = time_launches(torch, fs, args.steps, args.warmup)
+        k3 = sum(per3) / len(per3)
+        A = s5.n_atoms
+        s_bytes = A * hs.dim_in * 4 + A * hs.dim_out * 4 + A * 4 + s5.num_elements * hs.weight_numel * 4
+        seg_out = sum(2 * hs.coupling_info(c)["l"] + 1 for c in range(hs.num_couplings))
+        s_flops = A * hs.mul * (2 * hs.num_terms + hs.num_monomial_products + 2 * seg_out)
+        result["symcon"] = {
+            "workload": s5.name, "atoms_per_s": A / (wall3 / args.steps), "kernel_ms": k3,
+            "kernel": "symcon_spec" if hs.specialized else "symcon_generic",
+            "hbm": {"achieved": s_bytes / (k3 * 1e-3) / 1e9, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                    "frac": s_bytes / (k3 * 1e-3) / 1e9 / HBM_PEAK_GBPS, "algorithmic_bytes": s_bytes},
+            "alu": {"achieved": s_flops / (k3 * 1e-3) / 1e12, "peak": FP32_VALU_PEAK_TFLOPS, "unit": "TFLOP/s",
+                    "frac": s_flops / (k3 * 1e-3) / 1e12 / FP32_VALU_PEAK_TFLOPS, "algorithmic_flops": s_flops},
+        }
+        del sx, ssp, sw, sout
+
+    if args.copy_calibration:
+        a = torch.empty(1 << 28, dtype=torch.float32, device=dev)   # 1 GiB
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        result["copy_calibration_bytes"] = {"read": a.numel() * 4, "write": b.numel() * 4}
+        del a, b
+
+    if not args.no_cpu_baseline:
+        from threadpoolctl import threadpool_limits
+
+        from oracle import tp as otp
+        o = otp.ChannelwiseTP(wl.irreps_in1, wl.irreps_in2, wl.irreps_out)
+        with threadpool_limits(1):
+            t0 = time.perf_counter()
+            o.conv(base_inp["x"], base_inp["sh"], base_inp["w"], base_inp["src"], base_inp["dst"],
+                   base_inp["n_nodes"], layout=layout)
+            dt = time.perf_counter() - t0
+        n_e = base_inp["sh"].shape[0]
+        result["cpu_baseline"] = {"value": n_e / dt, "unit": "edges/s", "cores": 1, "kind": "oracle",
+                                  "sample": f"first {sample_nodes} destination nodes of the same graph "
+                                            f"({n_e} edges, all 13 paths), float64 NumPy, {dt:.1f} s",
+                                  "host_cpu": _cpu_model(), "host_nproc": os.cpu_count()}
+
+    print(json.dumps(result), flush=True)
+
+
+def _cpu_model():
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.startswith("model name"):
+                return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+if __name__ == "__main__":
+    main()

@@ -86,6 +86,7 @@ extern "C" {
 #define SEGPOLY_Q_NUM_COUPLINGS 9
 #define SEGPOLY_Q_NUM_TERMS 10  /* symcon: sorted-monomial terms per channel */
 #define SEGPOLY_Q_NUM_ELEMENTS 11
+#define SEGPOLY_Q_NUM_MONOMIALS 12 /* symcon: monomial products per channel (pairs and triples) */
 
 typedef struct segpoly_tp* tp_handle;
 typedef struct segpoly_symcon* symcon_handle;
@@ -148,8 +149,10 @@ int tp_kernel_name(tp_handle h, char* buf, size_t cap);
  *           sorted ascending (precondition; checked only with VALIDATE).
  *           Sources outside [0, n_src) and destinations outside
  *           [0, n_nodes) contribute nothing (VALIDATE reports them as
- *           E_RANGE).  Both NULL selects batch mode: edge e feeds row e, and
- *           n_edges must equal n_nodes and not exceed n_src.
+ *           E_RANGE).  Both NULL with n_edges > 0 selects batch mode: edge e
+ *           feeds row e, and n_edges must equal n_nodes and not exceed
+ *           n_src.  With n_edges == 0 every row is zero, whatever the index
+ *           pointers.
  *   out     [n_nodes, DIM_OUT] device, layout of the handle.
  * A descriptor served by the generic kernel uploads its coefficient table
  * to the current device once (hipMalloc + hipMemcpy at the first call on
@@ -182,7 +185,7 @@ int symcon_create(const char* irreps_in, const char* irreps_out, int max_degree,
                   int layout, int dtype, unsigned flags, symcon_handle* out);
 
 /* symcon_query: DIM_IN, DIM_OUT, WEIGHT_NUMEL (per element), NUM_COUPLINGS,
- * NUM_TERMS, SPECIALIZED, MUL, NUM_ELEMENTS. */
+ * NUM_TERMS, SPECIALIZED, MUL, NUM_ELEMENTS, NUM_MONOMIALS. */
 int symcon_query(symcon_handle h, int key, int64_t* value);
 
 /* symcon_coupling_info: coupling c (weight-segment order) as 4 integers:

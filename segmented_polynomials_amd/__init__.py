@@ -22,7 +22,7 @@ F32, F64 = 0, 1
 I32, I64 = 0, 1
 SHARED_WEIGHTS, VALIDATE, FORCE_GENERIC = 1, 2, 4
 (Q_DIM_IN1, Q_DIM_IN2, Q_DIM_OUT, Q_WEIGHT_NUMEL, Q_NUM_PATHS, Q_CG_NNZ, Q_SPECIALIZED, Q_MUL,
- Q_DIM_IN, Q_NUM_COUPLINGS, Q_NUM_TERMS, Q_NUM_ELEMENTS) = range(12)
+ Q_DIM_IN, Q_NUM_COUPLINGS, Q_NUM_TERMS, Q_NUM_ELEMENTS, Q_NUM_MONOMIALS) = range(13)
 
 _LAYOUTS = {"mul_ir": MUL_IR, "ir_mul": IR_MUL}
 _DTYPES = {"f32": F32, "f64": F64}
@@ -174,7 +174,7 @@ class TPHandle:
         return out.reshape(shape)
 
     def __del__(self):
-        if getattr(self, "_h", None):
+        if getattr(self, "_h", None) and lib is not None:
             lib.tp_destroy(self._h)
             self._h = None
 
@@ -259,6 +259,7 @@ class SymconHandle:
     specialized = property(lambda s: bool(s._q(Q_SPECIALIZED)))
     mul = property(lambda s: s._q(Q_MUL))
     num_elements = property(lambda s: s._q(Q_NUM_ELEMENTS))
+    num_monomial_products = property(lambda s: s._q(Q_NUM_MONOMIALS))
 
     def coupling_info(self, c):
         v = (ctypes.c_int64 * 4)()
@@ -273,7 +274,7 @@ class SymconHandle:
         return out.reshape(shape)
 
     def __del__(self):
-        if getattr(self, "_h", None):
+        if getattr(self, "_h", None) and lib is not None:
             lib.symcon_destroy(self._h)
             self._h = None
 

@@ -436,6 +436,7 @@ int symcon_query(symcon_handle h, int key, int64_t* value) {
     case SEGPOLY_Q_SPECIALIZED: *value = h->spec ? 1 : 0; break;
     case SEGPOLY_Q_MUL: *value = d.mul; break;
     case SEGPOLY_Q_NUM_ELEMENTS: *value = h->num_elements; break;
+    case SEGPOLY_Q_NUM_MONOMIALS: *value = d.num_monomial_products(); break;
     default: return fail(SEGPOLY_E_INVALID, "unknown query key");
   }
   return ok();

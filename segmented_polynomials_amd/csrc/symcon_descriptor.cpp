@@ -4,6 +4,8 @@
 #include <cmath>
 #include <cstdlib>
 #include <numeric>
+#include <set>
+#include <tuple>
 #include <stdexcept>
 
 #include "cg.hpp"
@@ -14,6 +16,17 @@ int64_t SymconDescriptor::num_terms() const {
   int64_t t = 0;
   for (const auto& c : couplings) t += static_cast<int64_t>(c.terms.size());
   return t;
+}
+
+int64_t SymconDescriptor::num_monomial_products() const {
+  std::set<std::pair<int, int>> pairs;
+  std::set<std::tuple<int, int, int>> triples;
+  for (const auto& c : couplings)
+    for (const auto& t : c.terms) {
+      if (t.m[1] >= 0) pairs.insert({t.m[0], t.m[1]});
+      if (t.m[2] >= 0) triples.insert({t.m[0], t.m[1], t.m[2]});
+    }
+  return static_cast<int64_t>(pairs.size() + triples.size());
 }
 
 namespace {

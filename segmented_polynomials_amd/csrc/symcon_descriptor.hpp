@@ -52,6 +52,10 @@ struct SymconDescriptor {
   int64_t dim_in = 0, dim_out = 0, numel = 0;
   std::string key;
   int64_t num_terms() const;
+  // products a per-channel evaluation forms: one per distinct sorted pair
+  // (m1, m2) that a degree-2 term or a degree-3 prefix needs, plus one per
+  // distinct sorted triple
+  int64_t num_monomial_products() const;
 };
 
 // Throws ParseError / std::invalid_argument (non-uniform multiplicities,
