@@ -96,56 +96,67 @@ bool is_identity_l1_zero(const TPPath& p) {
   return static_cast<int>(p.nz.size()) == 2 * p.l2 + 1;
 }
 
+// Per-path body: `qn(absc, j)` names the uniform product |c| * sh_j, `X(i)`,
+// `W()`, `A(k)` name input-1 component i of the path's block, the path's
+// weight and output component k of the path's block.
+template <class QN, class XN, class WN, class AN>
+void emit_path_body(const TPPath& p, QN qn, XN X, WN W, AN A, const std::string& ind, std::ostream& e) {
+  if (is_identity_l2_zero(p)) {
+    e << ind << "const T ws = " << W() << " * " << qn(1.0, 0) << ";\n";
+    for (int k = 0; k < 2 * p.lo + 1; ++k) e << ind << A(k) << " = fmadd(ws, " << X(k) << ", " << A(k) << ");\n";
+  } else if (is_identity_l1_zero(p)) {
+    e << ind << "const T xw = " << W() << " * " << X(0) << ";\n";
+    for (int k = 0; k < 2 * p.lo + 1; ++k) e << ind << A(k) << " = fmadd(xw, " << qn(1.0, k) << ", " << A(k) << ");\n";
+  } else if (2 * p.l1 + 1 < 2 * p.lo + 1) {
+    // fold the weight into the inputs: (2l1+1) products, then nnz FMAs
+    for (int i = 0; i < 2 * p.l1 + 1; ++i) e << ind << "const T xw" << i << " = " << W() << " * " << X(i) << ";\n";
+    for (const auto& z : p.nz)
+      e << ind << A(z.k) << " = fmadd(" << (z.c < 0 ? "-" : "") << qn(std::fabs(z.c), z.j) << ", xw" << z.i << ", "
+        << A(z.k) << ");\n";
+  } else {
+    // per output component: t = sum (c sh_j) x_i, then acc += w t
+    int cur = -1;
+    for (size_t n = 0; n < p.nz.size(); ++n) {
+      const auto& z = p.nz[n];
+      std::string term = std::string(z.c < 0 ? "-" : "") + qn(std::fabs(z.c), z.j);
+      if (z.k != cur) {
+        cur = z.k;
+        e << ind << "T t" << z.k << " = " << term << " * " << X(z.i) << ";\n";
+      } else {
+        e << ind << "t" << z.k << " = fmadd(" << term << ", " << X(z.i) << ", t" << z.k << ");\n";
+      }
+      bool last = (n + 1 == p.nz.size()) || p.nz[n + 1].k != z.k;
+      if (last) e << ind << A(z.k) << " = fmadd(" << W() << ", t" << z.k << ", " << A(z.k) << ");\n";
+    }
+  }
+}
+
 void emit_tp(const std::string& name, unsigned dtypes, const TPDescriptor& d, std::ostream& os) {
   if (!d.uniform_mul) throw std::runtime_error("spec " + name + ": input-1 multiplicities must be uniform");
   const std::string S = "TPSpec_" + name;
-  QTable q;
+  // edge<CPL>(): per path, its uniform products |c| * sh_j (formed right
+  // before use from the raw sh row), then the channel slots
   std::ostringstream edge;
   for (size_t pi = 0; pi < d.paths.size(); ++pi) {
     const TPPath& p = d.paths[pi];
     const int X = p.xcomp, K = p.kcomp, J = static_cast<int>(p.off2);
     edge << "    // path " << pi << ": " << p.l1 << " x " << p.l2 << " -> " << p.lo << " (" << p.nz.size()
          << " non-zero)\n    {\n";
-    if (is_identity_l2_zero(p)) {
-      int qs = q.get(1.0, J);
-      edge << "      const T ws = wv[" << pi << "] * q[" << qs << "];\n";
-      for (int k = 0; k < 2 * p.lo + 1; ++k)
-        edge << "      acc[" << K + k << "] = fmadd(ws, xv[" << X + k << "], acc[" << K + k << "]);\n";
-    } else if (is_identity_l1_zero(p)) {
-      edge << "      const T xw = wv[" << pi << "] * xv[" << X << "];\n";
-      for (int k = 0; k < 2 * p.lo + 1; ++k) {
-        int qs = q.get(1.0, J + k);
-        edge << "      acc[" << K + k << "] = fmadd(xw, q[" << qs << "], acc[" << K + k << "]);\n";
-      }
-    } else if (2 * p.l1 + 1 < 2 * p.lo + 1) {
-      // fold the weight into the inputs: (2l1+1) products, then nnz FMAs
-      for (int i = 0; i < 2 * p.l1 + 1; ++i)
-        edge << "      const T xw" << i << " = wv[" << pi << "] * xv[" << X + i << "];\n";
-      for (const auto& e : p.nz) {
-        int qi = q.get(std::fabs(e.c), J + e.j);
-        edge << "      acc[" << K + e.k << "] = fmadd(" << (e.c < 0 ? "-" : "") << "q[" << qi << "], xw" << e.i
-             << ", acc[" << K + e.k << "]);\n";
-      }
-    } else {
-      // per output component: t = sum (c sh_j) x_i, then acc += w t
-      int cur = -1;
-      for (size_t n = 0; n < p.nz.size(); ++n) {
-        const auto& e = p.nz[n];
-        int qi = q.get(std::fabs(e.c), J + e.j);
-        std::string term = std::string(e.c < 0 ? "-" : "") + "q[" + std::to_string(qi) + "]";
-        if (e.k != cur) {
-          cur = e.k;
-          edge << "      T t" << e.k << " = " << term << " * xv[" << X + e.i << "];\n";
-        } else {
-          edge << "      t" << e.k << " = fmadd(" << term << ", xv[" << X + e.i << "], t" << e.k << ");\n";
-        }
-        bool last = (n + 1 == p.nz.size()) || p.nz[n + 1].k != e.k;
-        if (last)
-          edge << "      acc[" << K + e.k << "] = fmadd(wv[" << pi << "], t" << e.k << ", acc[" << K + e.k
-               << "]);\n";
-      }
+    QTable lq;
+    std::ostringstream body;
+    emit_path_body(
+        p, [&](double c, int j) { return "q" + std::to_string(lq.get(c, J + j)); },
+        [&](int i) { return "xv[s][" + std::to_string(X + i) + "]"; },
+        [&]() { return "wv[s][" + std::to_string(pi) + "]"; },
+        [&](int k) { return "acc[s][" + std::to_string(K + k) + "]"; }, "        ", body);
+    for (size_t n = 0; n < lq.entries.size(); ++n) {
+      const auto& [c, j] = lq.entries[n];
+      if (c == 1.0)
+        edge << "      const T q" << n << " = sh[" << j << "];\n";
+      else
+        edge << "      const T q" << n << " = " << lit(c) << " * sh[" << j << "];\n";
     }
-    edge << "    }\n";
+    edge << "#pragma unroll\n      for (int s = 0; s < CPL; ++s) {\n" << body.str() << "      }\n    }\n";
   }
 
   os << "// Generated by codegen.cpp from the descriptor: " << irreps_str(d.in1) << " x " << irreps_str(d.in2)
@@ -155,51 +166,79 @@ void emit_tp(const std::string& name, unsigned dtypes, const TPDescriptor& d, st
   os << "  static constexpr int NX = " << d.nx << ";\n";
   os << "  static constexpr int NK = " << d.nk << ";\n";
   os << "  static constexpr int NP = " << d.paths.size() << ";\n";
-  os << "  static constexpr int D2 = " << d.dim2 << ";\n";
-  os << "  static constexpr int NQ = " << q.entries.size() << ";\n\n";
-  // coef
-  os << "  template <typename T>\n  __device__ __forceinline__ static void coef(const T* __restrict__ sh, T* q) {\n";
-  for (size_t n = 0; n < q.entries.size(); ++n) {
-    const auto& [c, j] = q.entries[n];
-    if (c == 1.0)
-      os << "    q[" << n << "] = sh[" << j << "];\n";
-    else
-      os << "    q[" << n << "] = " << lit(c) << " * sh[" << j << "];\n";
-  }
-  os << "  }\n\n";
-  // load_x
-  os << "  template <typename T, int LAYOUT>\n  __device__ __forceinline__ static void load_x(const T* __restrict__ row, int mul, int u, T* xv) {\n";
-  os << "    if constexpr (LAYOUT == kIrMul) {\n";
-  for (int m = 0; m < d.nx; ++m) os << "      xv[" << m << "] = row[" << m << " * mul + u];\n";
-  os << "    } else {\n";
+  os << "  static constexpr int D2 = " << d.dim2 << ";\n\n";
+  // load_xs / store_s: CPL (1 or 2) adjacent channels ub, ub+1 per lane;
+  // with CPL = 2 every access is one aligned pair (no staging arrays, so
+  // everything stays in registers)
+  auto pair_ld = [](std::ostream& o, const std::string& addr, const std::string& d0, const std::string& d1) {
+    o << "        { const auto t = ld2<T, NTX>(" << addr << "); " << d0 << " = t.x; " << d1 << " = t.y; }\n";
+  };
+  auto pair_st = [](std::ostream& o, const std::string& addr, const std::string& s0, const std::string& s1) {
+    o << "        st2<T>(" << addr << ", " << s0 << ", " << s1 << ");\n";
+  };
+  os << "  template <typename T, int LAYOUT, int CPL, bool NTX = false>\n  __device__ __forceinline__ static void load_xs(const T* __restrict__ row, int mul, int ub, T (&xv)[CPL][NX]) {\n";
+  os << "    static_assert(CPL == 1 || CPL == 2, \"one or two channels per lane\");\n";
+  os << "    if constexpr (LAYOUT == kIrMul) {\n      if constexpr (CPL == 2) {\n";
+  for (int m = 0; m < d.nx; ++m)
+    pair_ld(os, "row + " + std::to_string(m) + " * mul + ub", "xv[0][" + std::to_string(m) + "]",
+            "xv[1][" + std::to_string(m) + "]");
+  os << "      } else {\n";
+  for (int m = 0; m < d.nx; ++m) os << "        xv[0][" << m << "] = row[" << m << " * mul + ub];\n";
+  os << "      }\n    } else {\n      if constexpr (CPL == 2) {\n";
   for (size_t b = 0; b < d.in1.size(); ++b) {
     int comp = 0;
     for (size_t bb = 0; bb < b; ++bb) comp += 2 * d.in1[bb].l + 1;
     const int dl = 2 * d.in1[b].l + 1;
-    os << "      {\n        const T* p = row + " << comp << " * mul + u * " << dl << ";\n";
-    for (int i = 0; i < dl; ++i) os << "        xv[" << comp + i << "] = p[" << i << "];\n";
-    os << "      }\n";
+    // channels ub, ub+1 hold 2*dl consecutive values: element q -> slot q / dl, comp q % dl
+    for (int pq = 0; pq < dl; ++pq) {
+      int q0 = 2 * pq, q1 = 2 * pq + 1;
+      pair_ld(os, "row + " + std::to_string(comp) + " * mul + ub * " + std::to_string(dl) + " + " + std::to_string(q0),
+              "xv[" + std::to_string(q0 / dl) + "][" + std::to_string(comp + q0 % dl) + "]",
+              "xv[" + std::to_string(q1 / dl) + "][" + std::to_string(comp + q1 % dl) + "]");
+    }
   }
-  os << "    }\n  }\n\n";
-  // edge
-  os << "  template <typename T>\n  __device__ __forceinline__ static void edge(const T* xv, const T* q, const T* wv, T* acc) {\n";
-  os << edge.str();
-  os << "  }\n\n";
-  // store
-  os << "  template <typename T, int LAYOUT>\n  __device__ __forceinline__ static void store(T* __restrict__ row, int mul, int u, const T* acc) {\n";
-  os << "    if constexpr (LAYOUT == kIrMul) {\n";
-  for (int k = 0; k < d.nk; ++k) os << "      row[" << k << " * mul + u] = acc[" << k << "];\n";
-  os << "    } else {\n";
+  os << "      } else {\n";
+  for (size_t b = 0; b < d.in1.size(); ++b) {
+    int comp = 0;
+    for (size_t bb = 0; bb < b; ++bb) comp += 2 * d.in1[bb].l + 1;
+    const int dl = 2 * d.in1[b].l + 1;
+    for (int i = 0; i < dl; ++i)
+      os << "        xv[0][" << comp + i << "] = row[" << comp << " * mul + ub * " << dl << " + " << i << "];\n";
+  }
+  os << "      }\n    }\n  }\n\n";
+  os << "  template <typename T, int LAYOUT, int CPL>\n  __device__ __forceinline__ static void store_s(T* __restrict__ row, int mul, int ub, const T (&acc)[CPL][NK]) {\n";
+  os << "    if constexpr (LAYOUT == kIrMul) {\n      if constexpr (CPL == 2) {\n";
+  // two plain stores: a pair store built from acc[0][k] and acc[1][k] keeps
+  // part of acc out of registers (private memory) on this compiler
+  for (int k = 0; k < d.nk; ++k)
+    os << "        row[" << k << " * mul + ub] = acc[0][" << k << "]; row[" << k << " * mul + ub + 1] = acc[1][" << k
+       << "];\n";
+  os << "      } else {\n";
+  for (int k = 0; k < d.nk; ++k) os << "        row[" << k << " * mul + ub] = acc[0][" << k << "];\n";
+  os << "      }\n    } else {\n      if constexpr (CPL == 2) {\n";
   for (const auto& p : d.paths) {
     const int dl = 2 * p.lo + 1;
-    os << "      {\n        T* p = row + " << p.kcomp << " * mul + u * " << dl << ";\n";
-    for (int k = 0; k < dl; ++k) os << "        p[" << k << "] = acc[" << p.kcomp + k << "];\n";
-    os << "      }\n";
+    for (int pq = 0; pq < dl; ++pq) {
+      int q0 = 2 * pq, q1 = 2 * pq + 1;
+      pair_st(os, "row + " + std::to_string(p.kcomp) + " * mul + ub * " + std::to_string(dl) + " + " + std::to_string(q0),
+              "acc[" + std::to_string(q0 / dl) + "][" + std::to_string(p.kcomp + q0 % dl) + "]",
+              "acc[" + std::to_string(q1 / dl) + "][" + std::to_string(p.kcomp + q1 % dl) + "]");
+    }
   }
-  os << "    }\n  }\n};\n\n}  // namespace kern\n\n";
+  os << "      } else {\n";
+  for (const auto& p : d.paths) {
+    const int dl = 2 * p.lo + 1;
+    for (int k = 0; k < dl; ++k)
+      os << "        row[" << p.kcomp << " * mul + ub * " << dl << " + " << k << "] = acc[0][" << p.kcomp + k << "];\n";
+  }
+  os << "      }\n    }\n  }\n\n";
+  os << "  template <typename T, int CPL>\n  __device__ __forceinline__ static void edge(const T (&xv)[CPL][NX], const T* __restrict__ sh,\n"
+        "                                                   const T (&wv)[CPL][NP], T (&acc)[CPL][NK]) {\n";
+  os << edge.str();
+  os << "  }\n};\n\n}  // namespace kern\n\n";
   os << "int launch_tp_" << name << "(const TPArgs& a) {\n";
-  if (dtypes & 1u) os << "  if (a.dtype == kF32) return kern::tp_conv_spec_dispatch<kern::" << S << ", float>(a);\n";
-  if (dtypes & 2u) os << "  if (a.dtype == kF64) return kern::tp_conv_spec_dispatch<kern::" << S << ", double>(a);\n";
+  if (dtypes & 1u) os << "  if (a.dtype == kF32) return kern::tp_conv_dispatch<kern::" << S << ", float>(a);\n";
+  if (dtypes & 2u) os << "  if (a.dtype == kF64) return kern::tp_conv_dispatch<kern::" << S << ", double>(a);\n";
   os << "  return -1;\n}\n\n}  // namespace segpoly\n";
 }
 

@@ -33,13 +33,7 @@ tp_conv_generic_kernel(const T* __restrict__ x, const T* __restrict__ sh, const 
   for (int k = 0; k < nk; ++k) acc[k * kGW + lane] = T(0);
 
   int64_t e0, e1;
-  if (batch) {
-    e0 = node;
-    e1 = node + 1;
-  } else {
-    e0 = lower_bound_idx(dst, 0, n_edges, node);
-    e1 = lower_bound_idx(dst, e0, n_edges, node + 1);
-  }
+  edge_range(dst, n_edges, batch, node, e0, e1);
   for (int64_t e = e0; e < e1; ++e) {
     const int64_t s = batch ? e : static_cast<int64_t>(src[e]);
     if (s < 0 || s >= n_src) continue;

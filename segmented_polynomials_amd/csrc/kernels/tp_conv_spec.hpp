@@ -10,24 +10,25 @@
 // scatter": repeated receivers sum, receivers without edges stay zero).
 //
 // Work decomposition: one wavefront (64 lanes) per (destination node,
-// channel tile of 64*CPL channels); lane = channel, CPL channels per lane.
-// The wave finds its node's edge range [e0, e1) in the dst-sorted edge list
-// by two uniform binary searches, then walks the edges in order keeping
+// channel tile of 64*CPL channels); each lane owns CPL adjacent channels
+// (CPL = 2: every operand row is read as one aligned pair per lane).  The
+// wave finds its node's edge range [e0, e1) in the dst-sorted edge list with
+// a wave-cooperative 64-ary search, then walks the edges in order keeping
 // every output component of its channels in registers, and writes each
 // output row exactly once (zeros for an isolated node).  No atomics: the
 // reduction order is the edge order, so results are deterministic.
 //
-// Per edge: src[e] and sh[e, :] are wave-uniform (scalar loads); the
-// uniform products c * sh_j of the coupling coefficients are formed once per
-// edge (S::coef) and shared by all channels of the wave; the weights
-// w[e, p*mul + u] and the gathered features x[src, ...] are channel-
-// contiguous vector loads.  The coupling coefficients are literal constants
-// in S::coef / S::edge (generated per descriptor), so zeros cost nothing.
+// Per edge the loads of the next edge (its weights, the gathered source row,
+// its harmonics) are issued before the current edge is computed, so one
+// edge of traffic per wave is always in flight.  The weights are streamed
+// once and carry the non-temporal hint.  Each path forms its uniform
+// coefficient products c * sh_j just before use; the coefficients are
+// literal constants in the generated S::edge, so zeros cost nothing.
 //
-// S (generated) provides: NX (input-1 components per channel), NK (output
-// components per channel), NP (paths), D2 (width of sh), NQ (uniform
-// products); coef(sh_row, q); load_x<T, LAYOUT>(x_row, mul, u, xv);
-// edge(xv, q, wv, acc); store<T, LAYOUT>(out_row, mul, u, acc).
+// S (generated) provides NX (input-1 components per channel), NK (output
+// components per channel), NP (paths), D2 (width of sh);
+// load_xs<T, LAYOUT, CPL>(x_row, mul, u0, xv), edge<T, CPL>(xv, sh, wv, acc),
+// store_s<T, LAYOUT, CPL>(out_row, mul, u0, acc).
 #pragma once
 #include <hip/hip_runtime.h>
 
@@ -41,80 +42,125 @@ namespace kern {
 
 constexpr int kWave = 64;
 
-// First e in [lo, hi) with dst[e] >= key, dst sorted ascending.  All
-// operands are wave-uniform, so this runs on the scalar unit.
+// First e in [lo, hi) with dst[e] >= key, dst sorted ascending, found by
+// the whole wave: each round every lane probes one of 64 evenly spaced
+// positions and a ballot narrows [lo, hi) 64-fold, so about four dependent
+// loads cover 10^6 edges.  Must be called by all 64 lanes together.
 template <typename Index>
-__device__ __forceinline__ int64_t lower_bound_idx(const Index* __restrict__ dst, int64_t lo,
-                                                   int64_t hi, int64_t key) {
-  while (lo < hi) {
-    const int64_t mid = lo + ((hi - lo) >> 1);
-    if (static_cast<int64_t>(dst[mid]) < key)
-      lo = mid + 1;
-    else
-      hi = mid;
+__device__ __forceinline__ int64_t lower_bound_wave(const Index* __restrict__ dst, int64_t lo, int64_t hi,
+                                                    int64_t key) {
+  const int lane = threadIdx.x & (kWave - 1);
+  while (hi - lo > kWave) {
+    const int64_t step = (hi - lo + kWave - 1) / kWave;
+    const int64_t idx = lo + lane * step;
+    const bool below = idx < hi && static_cast<int64_t>(dst[idx]) < key;
+    const int c = __popcll(__ballot(below));  // probes 0..c-1 are below key
+    const int64_t nlo = c == 0 ? lo : lo + (c - 1) * step + 1;
+    const int64_t nhi = lo + c * step < hi ? lo + c * step : hi;
+    lo = nlo;
+    hi = nhi;
   }
-  return lo;
+  const int64_t idx = lo + lane;
+  const bool below = idx < hi && static_cast<int64_t>(dst[idx]) < key;
+  return lo + __popcll(__ballot(below));
 }
 
-template <class S, typename T, typename Index, int LAYOUT, int CPL>
-__global__ void __launch_bounds__(kWave)
-tp_conv_spec_kernel(const T* __restrict__ x, const T* __restrict__ sh, const T* __restrict__ w,
-                    const Index* __restrict__ src, const Index* __restrict__ dst, int64_t n_src,
-                    int64_t n_edges, int64_t w_stride, int mul, int batch, T* __restrict__ out) {
-  const int64_t node = blockIdx.x;
-  const int lane = threadIdx.x;
-  const int tile0 = blockIdx.y * (kWave * CPL);
-
-  int64_t e0, e1;
-  if (batch) {  // batch mode: edge e is node e
+// Edge range of `node` (batch mode: edge e is node e).
+template <typename Index>
+__device__ __forceinline__ void edge_range(const Index* __restrict__ dst, int64_t n_edges, int batch, int64_t node,
+                                           int64_t& e0, int64_t& e1) {
+  if (batch) {
     e0 = node;
     e1 = node + 1;
   } else {
-    e0 = lower_bound_idx(dst, 0, n_edges, node);
-    e1 = lower_bound_idx(dst, e0, n_edges, node + 1);
+    e0 = lower_bound_wave(dst, 0, n_edges, node);
+    e1 = lower_bound_wave(dst, e0, n_edges, node + 1);
   }
+}
 
+// Requires mul % CPL == 0 and x, w, out aligned to CPL * sizeof(T).
+template <class S, typename T, typename Index, int LAYOUT, int CPL>
+__global__ void __launch_bounds__(kWave)
+tp_conv_kernel(const T* __restrict__ x, const T* __restrict__ sh, const T* __restrict__ w,
+               const Index* __restrict__ src, const Index* __restrict__ dst, int64_t n_src, int64_t n_edges,
+               int64_t w_stride, int mul, int batch, T* __restrict__ out) {
+  const int64_t node = blockIdx.x;
+  const int ub = blockIdx.y * (kWave * CPL) + threadIdx.x * CPL;
+  const bool active = ub < mul;
+  const int ubl = active ? ub : 0;  // idle lanes load channel 0 and store nothing
+
+  int64_t e0, e1;
+  edge_range(dst, n_edges, batch, node, e0, e1);
   const int64_t dim1 = static_cast<int64_t>(mul) * S::NX;
+
   T acc[CPL][S::NK];
 #pragma unroll
   for (int c = 0; c < CPL; ++c)
 #pragma unroll
     for (int k = 0; k < S::NK; ++k) acc[c][k] = T(0);
 
-  for (int64_t e = e0; e < e1; ++e) {
-    const int64_t s = batch ? e : static_cast<int64_t>(src[e]);
-    if (s < 0 || s >= n_src) continue;  // out-of-range sources contribute nothing
-    T q[S::NQ];
-    S::template coef<T>(sh + e * S::D2, q);
-    const T* xrow = x + s * dim1;
-    const T* wrow = w + e * w_stride;
+  auto source = [&](int64_t e) -> int64_t { return batch ? e : static_cast<int64_t>(src[e]); };
+  auto load = [&](int64_t e, int64_t s, T (&xv)[CPL][S::NX], T (&wv)[CPL][S::NP], T (&shv)[S::D2]) {
+    const int64_t sc = (s >= 0 && s < n_src) ? s : 0;
+    S::template load_xs<T, LAYOUT, CPL>(x + sc * dim1, mul, ubl, xv);
+    const T* wrow = w + e * w_stride + ubl;
 #pragma unroll
-    for (int c = 0; c < CPL; ++c) {
-      const int u = tile0 + c * kWave + lane;
-      if (u < mul) {
-        T xv[S::NX];
-        T wv[S::NP];
-        S::template load_x<T, LAYOUT>(xrow, mul, u, xv);
-#pragma unroll
-        for (int p = 0; p < S::NP; ++p) wv[p] = wrow[p * mul + u];
-        S::template edge<T>(xv, q, wv, acc[c]);
+    for (int p = 0; p < S::NP; ++p) {
+      if constexpr (CPL == 2) {
+        const auto t = ld2<T, true>(wrow + p * mul);
+        wv[0][p] = t.x;
+        wv[1][p] = t.y;
+      } else {
+        wv[0][p] = __builtin_nontemporal_load(wrow + p * mul);
       }
     }
+    const T* shrow = sh + e * S::D2;
+#pragma unroll
+    for (int j = 0; j < S::D2; ++j) shv[j] = shrow[j];
+  };
+
+  // next edge's operands (in flight while the current edge is computed)
+  T xv[CPL][S::NX];
+  T wv[CPL][S::NP];
+  T shv[S::D2];
+  int64_t s_next = 0, s_after = 0;
+  if (e0 < e1) {
+    s_next = source(e0);
+    s_after = e0 + 1 < e1 ? source(e0 + 1) : 0;
+    load(e0, s_next, xv, wv, shv);
+  }
+  for (int64_t e = e0; e < e1; ++e) {
+    const int64_t s_cur = s_next;
+    T xc[CPL][S::NX];
+    T wc[CPL][S::NP];
+    T shc[S::D2];
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+#pragma unroll
+      for (int i = 0; i < S::NX; ++i) xc[c][i] = xv[c][i];
+#pragma unroll
+      for (int p = 0; p < S::NP; ++p) wc[c][p] = wv[c][p];
+    }
+#pragma unroll
+    for (int j = 0; j < S::D2; ++j) shc[j] = shv[j];
+    if (e + 1 < e1) {
+      s_next = s_after;
+      load(e + 1, s_next, xv, wv, shv);
+      s_after = e + 2 < e1 ? source(e + 2) : 0;
+    }
+    if (s_cur >= 0 && s_cur < n_src)  // out-of-range sources contribute nothing
+      S::template edge<T, CPL>(xc, shc, wc, acc);
   }
 
-  T* orow = out + node * (static_cast<int64_t>(mul) * S::NK);
-#pragma unroll
-  for (int c = 0; c < CPL; ++c) {
-    const int u = tile0 + c * kWave + lane;
-    if (u < mul) S::template store<T, LAYOUT>(orow, mul, u, acc[c]);
-  }
+  if (active)
+    S::template store_s<T, LAYOUT, CPL>(out + node * (static_cast<int64_t>(mul) * S::NK), mul, ub, acc);
 }
 
 template <class S, typename T, typename Index, int LAYOUT, int CPL>
-int tp_conv_spec_launch(const TPArgs& a) {
+int tp_conv_launch(const TPArgs& a) {
   const int per_tile = kWave * CPL;
   dim3 grid(static_cast<unsigned>(a.n_nodes), static_cast<unsigned>((a.mul + per_tile - 1) / per_tile));
-  hipLaunchKernelGGL((tp_conv_spec_kernel<S, T, Index, LAYOUT, CPL>), grid, dim3(kWave), 0,
+  hipLaunchKernelGGL((tp_conv_kernel<S, T, Index, LAYOUT, CPL>), grid, dim3(kWave), 0,
                      static_cast<hipStream_t>(a.stream), static_cast<const T*>(a.x),
                      static_cast<const T*>(a.sh), static_cast<const T*>(a.w),
                      static_cast<const Index*>(a.src), static_cast<const Index*>(a.dst), a.n_src,
@@ -122,20 +168,26 @@ int tp_conv_spec_launch(const TPArgs& a) {
   return static_cast<int>(hipGetLastError());
 }
 
+inline bool aligned(const void* p, size_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
+
+// Two channels per lane when the multiplicity fills more than one wave with
+// single channels and the pair accesses are aligned; one otherwise.
 template <class S, typename T, typename Index, int LAYOUT>
-int tp_conv_spec_dispatch_cpl(const TPArgs& a) {
-  if (a.mul > kWave) return tp_conv_spec_launch<S, T, Index, LAYOUT, 2>(a);
-  return tp_conv_spec_launch<S, T, Index, LAYOUT, 1>(a);
+int tp_conv_dispatch_cpl(const TPArgs& a) {
+  const size_t pa = 2 * sizeof(T);
+  if (a.mul > kWave && a.mul % 2 == 0 && aligned(a.x, pa) && aligned(a.w, pa) && aligned(a.out, pa))
+    return tp_conv_launch<S, T, Index, LAYOUT, 2>(a);
+  return tp_conv_launch<S, T, Index, LAYOUT, 1>(a);
 }
 
 template <class S, typename T>
-int tp_conv_spec_dispatch(const TPArgs& a) {
+int tp_conv_dispatch(const TPArgs& a) {
   if (a.idx == kI32) {
-    if (a.layout == kMulIr) return tp_conv_spec_dispatch_cpl<S, T, int32_t, kMulIr>(a);
-    return tp_conv_spec_dispatch_cpl<S, T, int32_t, kIrMul>(a);
+    if (a.layout == kMulIr) return tp_conv_dispatch_cpl<S, T, int32_t, kMulIr>(a);
+    return tp_conv_dispatch_cpl<S, T, int32_t, kIrMul>(a);
   }
-  if (a.layout == kMulIr) return tp_conv_spec_dispatch_cpl<S, T, int64_t, kMulIr>(a);
-  return tp_conv_spec_dispatch_cpl<S, T, int64_t, kIrMul>(a);
+  if (a.layout == kMulIr) return tp_conv_dispatch_cpl<S, T, int64_t, kMulIr>(a);
+  return tp_conv_dispatch_cpl<S, T, int64_t, kIrMul>(a);
 }
 
 }  // namespace kern
