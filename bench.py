@@ -208,6 +208,9 @@ def main():
         }
         del sx, ssp, sw, sout
 
+    if not args.no_extras:
+        result["other_workloads"] = other_workloads(torch, sp, workloads, dev, args)
+
     if args.copy_calibration:
         a = torch.empty(1 << 28, dtype=torch.float32, device=dev)   # 1 GiB
         b = torch.empty_like(a)
@@ -233,6 +236,75 @@ def main():
                                   "host_cpu": _cpu_model(), "host_nproc": os.cpu_count()}
 
     print(json.dumps(result), flush=True)
+
+
+def other_workloads(torch, sp, workloads, dev, args):
+    """The smaller workloads: microseconds per call (eager, and replayed from
+    a HIP graph for the launch-bound molecular batch) and edges/s; the
+    medium graph is timed cold by rotating four input sets (4 x 187 MB >
+    the 256 MB Infinity Cache)."""
+    import numpy as np
+    to = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    out = {}
+    for n in (1, 2, 3):
+        wl = workloads.WORKLOADS[n]
+        h = sp.tp_create(wl.irreps_in1, wl.irreps_in2, wl.irreps_out, layout=wl.layouts[0], dtype=wl.dtype)
+        fan = workloads.fan_in_from_irreps_out(h.irreps_out)
+        sets = []
+        for r in range(4 if n == 3 else 1):
+            inp = workloads.tp_inputs(wl, fan, seed=1000 + n + 100 * r)
+            t = dict(x=to(inp["x"]), sh=to(inp["sh"]), w=to(inp["w"]),
+                     src=to(inp["src"]) if inp["src"] is not None else None,
+                     dst=to(inp["dst"]) if inp["dst"] is not None else None)
+            t["out"] = torch.empty((inp["n_nodes"], h.dim_out), dtype=t["x"].dtype, device=dev)
+            sets.append(t)
+        N, E = inp["n_nodes"], inp["sh"].shape[0]
+        k = [0]
+
+        def fwd():
+            t = sets[k[0] % len(sets)]
+            k[0] += 1
+            sp.tp_conv_fwd(h, t["x"], t["sh"], t["w"], t["src"], t["dst"], n_nodes=N, out=t["out"])
+        steps = max(args.steps, 200)
+        wall, per = time_launches(torch, fwd, steps, args.warmup)
+        rec = {"workload": wl.name, "layout": wl.layouts[0], "dtype": wl.dtype, "nodes": N, "edges": E,
+               "kernel": h.kernel_name, "us_per_call": wall * 1e6 / steps,
+               "kernel_us_mean": 1e3 * sum(per) / len(per), "edges_per_s": E * steps / wall}
+        if n == 3:
+            b = E * (h.weight_numel + h.dim_in2 + 2) * 4 + N * (h.dim_in1 + h.dim_out) * 4
+            rec["cold_input_sets"] = len(sets)
+            rec["hbm_GBps_algorithmic"] = b / (sum(per) / len(per) * 1e-3) / 1e9
+        if n == 2:
+            # HIP graph replay of 20 calls (the path has no memset or host work)
+            t = sets[0]
+            ref = t["out"].clone()
+            g = torch.cuda.CUDAGraph()
+            s = torch.cuda.Stream()
+            s.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(s):
+                fwd()
+            torch.cuda.current_stream().wait_stream(s)
+            torch.cuda.synchronize()
+            with torch.cuda.graph(g):
+                for _ in range(20):
+                    sp.tp_conv_fwd(h, t["x"], t["sh"], t["w"], t["src"], t["dst"], n_nodes=N, out=t["out"])
+            ok = True
+            for _ in range(3):
+                t["out"].zero_()
+                g.replay()
+                torch.cuda.synchronize()
+                ok = ok and bool(torch.equal(t["out"], ref))
+            reps = 20
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(reps):
+                g.replay()
+            torch.cuda.synchronize()
+            rec["graph_us_per_call"] = (time.perf_counter() - t0) * 1e6 / (reps * 20)
+            rec["graph_replays_match_eager"] = ok
+        out[wl.name] = rec
+        del sets
+    return out
 
 
 def _cpu_model():

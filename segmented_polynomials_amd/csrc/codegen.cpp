@@ -174,7 +174,7 @@ void emit_tp(const std::string& name, unsigned dtypes, const TPDescriptor& d, st
     o << "        { const auto t = ld2<T, NTX>(" << addr << "); " << d0 << " = t.x; " << d1 << " = t.y; }\n";
   };
   auto pair_st = [](std::ostream& o, const std::string& addr, const std::string& s0, const std::string& s1) {
-    o << "        st2<T>(" << addr << ", " << s0 << ", " << s1 << ");\n";
+    o << "        st2<T, NTS>(" << addr << ", " << s0 << ", " << s1 << ");\n";
   };
   os << "  template <typename T, int LAYOUT, int CPL, bool NTX = false>\n  __device__ __forceinline__ static void load_xs(const T* __restrict__ row, int mul, int ub, T (&xv)[CPL][NX]) {\n";
   os << "    static_assert(CPL == 1 || CPL == 2, \"one or two channels per lane\");\n";
@@ -206,15 +206,15 @@ void emit_tp(const std::string& name, unsigned dtypes, const TPDescriptor& d, st
       os << "        xv[0][" << comp + i << "] = row[" << comp << " * mul + ub * " << dl << " + " << i << "];\n";
   }
   os << "      }\n    }\n  }\n\n";
-  os << "  template <typename T, int LAYOUT, int CPL>\n  __device__ __forceinline__ static void store_s(T* __restrict__ row, int mul, int ub, const T (&acc)[CPL][NK]) {\n";
+  os << "  template <typename T, int LAYOUT, int CPL, bool NTS>\n  __device__ __forceinline__ static void store_s(T* __restrict__ row, int mul, int ub, const T (&acc)[CPL][NK]) {\n";
   os << "    if constexpr (LAYOUT == kIrMul) {\n      if constexpr (CPL == 2) {\n";
   // two plain stores: a pair store built from acc[0][k] and acc[1][k] keeps
   // part of acc out of registers (private memory) on this compiler
   for (int k = 0; k < d.nk; ++k)
-    os << "        row[" << k << " * mul + ub] = acc[0][" << k << "]; row[" << k << " * mul + ub + 1] = acc[1][" << k
-       << "];\n";
+    os << "        st1<T, NTS>(row + " << k << " * mul + ub, acc[0][" << k << "]); st1<T, NTS>(row + " << k
+       << " * mul + ub + 1, acc[1][" << k << "]);\n";
   os << "      } else {\n";
-  for (int k = 0; k < d.nk; ++k) os << "        row[" << k << " * mul + ub] = acc[0][" << k << "];\n";
+  for (int k = 0; k < d.nk; ++k) os << "        st1<T, NTS>(row + " << k << " * mul + ub, acc[0][" << k << "]);\n";
   os << "      }\n    } else {\n      if constexpr (CPL == 2) {\n";
   for (const auto& p : d.paths) {
     const int dl = 2 * p.lo + 1;
@@ -229,7 +229,8 @@ void emit_tp(const std::string& name, unsigned dtypes, const TPDescriptor& d, st
   for (const auto& p : d.paths) {
     const int dl = 2 * p.lo + 1;
     for (int k = 0; k < dl; ++k)
-      os << "        row[" << p.kcomp << " * mul + ub * " << dl << " + " << k << "] = acc[0][" << p.kcomp + k << "];\n";
+      os << "        st1<T, NTS>(row + " << p.kcomp << " * mul + ub * " << dl << " + " << k << ", acc[0][" << p.kcomp + k
+         << "]);\n";
   }
   os << "      }\n    }\n  }\n\n";
   os << "  template <typename T, int CPL>\n  __device__ __forceinline__ static void edge(const T (&xv)[CPL][NX], const T* __restrict__ sh,\n"

@@ -20,12 +20,23 @@ __device__ __forceinline__ pair_t<T> ld2(const T* __restrict__ p) {
     return *reinterpret_cast<const pair_t<T>*>(p);
 }
 
-template <typename T>
+template <typename T, bool NT>
 __device__ __forceinline__ void st2(T* __restrict__ p, T a, T b) {
   pair_t<T> t;
   t.x = a;
   t.y = b;
-  *reinterpret_cast<pair_t<T>*>(p) = t;
+  if constexpr (NT)
+    __builtin_nontemporal_store(t, reinterpret_cast<pair_t<T>*>(p));
+  else
+    *reinterpret_cast<pair_t<T>*>(p) = t;
+}
+
+template <typename T, bool NT>
+__device__ __forceinline__ void st1(T* __restrict__ p, T a) {
+  if constexpr (NT)
+    __builtin_nontemporal_store(a, p);
+  else
+    *p = a;
 }
 
 }  // namespace kern

@@ -49,7 +49,7 @@ constexpr int kWave = 64;
 template <typename Index>
 __device__ __forceinline__ int64_t lower_bound_wave(const Index* __restrict__ dst, int64_t lo, int64_t hi,
                                                     int64_t key) {
-  const int lane = threadIdx.x & (kWave - 1);
+  const int lane = threadIdx.x % kWave;
   while (hi - lo > kWave) {
     const int64_t step = (hi - lo + kWave - 1) / kWave;
     const int64_t idx = lo + lane * step;
@@ -78,8 +78,10 @@ __device__ __forceinline__ void edge_range(const Index* __restrict__ dst, int64_
   }
 }
 
-// Requires mul % CPL == 0 and x, w, out aligned to CPL * sizeof(T).
-template <class S, typename T, typename Index, int LAYOUT, int CPL>
+// Requires mul % CPL == 0 and x, w, out aligned to CPL * sizeof(T).  NTS:
+// non-temporal output stores (measured neutral on the 600k-edge graph, so
+// off by default).
+template <class S, typename T, typename Index, int LAYOUT, int CPL, bool NTS = false>
 __global__ void __launch_bounds__(kWave)
 tp_conv_kernel(const T* __restrict__ x, const T* __restrict__ sh, const T* __restrict__ w,
                const Index* __restrict__ src, const Index* __restrict__ dst, int64_t n_src, int64_t n_edges,
@@ -153,14 +155,14 @@ tp_conv_kernel(const T* __restrict__ x, const T* __restrict__ sh, const T* __res
   }
 
   if (active)
-    S::template store_s<T, LAYOUT, CPL>(out + node * (static_cast<int64_t>(mul) * S::NK), mul, ub, acc);
+    S::template store_s<T, LAYOUT, CPL, NTS>(out + node * (static_cast<int64_t>(mul) * S::NK), mul, ub, acc);
 }
 
-template <class S, typename T, typename Index, int LAYOUT, int CPL>
+template <class S, typename T, typename Index, int LAYOUT, int CPL, bool NTS = false>
 int tp_conv_launch(const TPArgs& a) {
   const int per_tile = kWave * CPL;
   dim3 grid(static_cast<unsigned>(a.n_nodes), static_cast<unsigned>((a.mul + per_tile - 1) / per_tile));
-  hipLaunchKernelGGL((tp_conv_kernel<S, T, Index, LAYOUT, CPL>), grid, dim3(kWave), 0,
+  hipLaunchKernelGGL((tp_conv_kernel<S, T, Index, LAYOUT, CPL, NTS>), grid, dim3(kWave), 0,
                      static_cast<hipStream_t>(a.stream), static_cast<const T*>(a.x),
                      static_cast<const T*>(a.sh), static_cast<const T*>(a.w),
                      static_cast<const Index*>(a.src), static_cast<const Index*>(a.dst), a.n_src,
