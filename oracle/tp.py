@@ -140,3 +140,48 @@ class ChannelwiseTP:
             out_parts.append(blk)
             woff += mul
         return join_blocks(out_parts, layout)
+
+    def conv_vjp(self, x, sh, w, src, dst, n_nodes, g, layout="mul_ir", shared_weights=False):
+        """Vector-Jacobian product of :meth:`conv` (per-edge weights, or one
+        shared row with ``shared_weights``): given g = dL/d(out) [n_nodes,
+        dim_out] in ``layout``, return (dL/dx [n_src, dim_in1] in ``layout``,
+        dL/dsh [n_edges, dim_in2], dL/dw [n_edges or 1, weight_numel]).
+
+        From the definition, per path p and channel u (the forward is linear
+        in each operand):
+            dw[e, p, u]     = sum_k g[dst_e, p, k, u] sum_ij C[i,j,k] x[src_e, i, u] sh[e, j]
+            dsh[e, blk2_p, j] += sum_u w[e, p, u] sum_ik C[i,j,k] x[src_e, i, u] g[dst_e, p, k, u]
+            dx[src_e, blk1_p, i, u] += w[e, p, u] sum_jk C[i,j,k] sh[e, j] g[dst_e, p, k, u]"""
+        x = np.asarray(x, dtype=np.float64)
+        sh = np.asarray(sh, dtype=np.float64)
+        w = np.asarray(w, dtype=np.float64)
+        g = np.asarray(g, dtype=np.float64)
+        n_edges = sh.shape[0]
+        if src is None:
+            src = np.arange(n_edges)
+            dst = np.arange(n_edges)
+        src = np.asarray(src, dtype=np.int64)
+        dst = np.asarray(dst, dtype=np.int64)
+        x1 = split_blocks(x, self.in1, layout)          # per block [n_src, 2l+1, mul]
+        x2 = split_blocks(sh, self.in2, "ir_mul")       # per block [n_edges, 2l+1, 1]
+        gb = split_blocks(g, self.out, layout)          # per path [n_nodes, 2lo+1, mul]
+        dx1 = [np.zeros_like(b) for b in x1]
+        dsh = np.zeros_like(sh)
+        dw = np.zeros((n_edges, self.weight_numel))
+        off2 = np.cumsum([0] + [2 * l + 1 for _, l, _ in self.in2])
+        woff = 0
+        for p, (i, j, lo, _) in enumerate(self.paths):
+            mul, l1, _ = self.in1[i]
+            l2 = self.in2[j][1]
+            c = real_cg(l1, l2, lo)
+            a = x1[i][src]                               # [E, 2l1+1, mul]
+            b = x2[j][:, :, 0]                           # [E, 2l2+1]
+            ge = gb[p][dst]                              # [E, 2lo+1, mul]
+            ww = np.broadcast_to(w[:, woff:woff + mul], (n_edges, mul))
+            dw[:, woff:woff + mul] = np.einsum("ijk,eiu,ej,eku->eu", c, a, b, ge)
+            dsh[:, off2[j]:off2[j + 1]] += np.einsum("ijk,eiu,eku,eu->ej", c, a, ge, ww)
+            np.add.at(dx1[i], src, np.einsum("ijk,ej,eku,eu->eiu", c, b, ge, ww))
+            woff += mul
+        if shared_weights:
+            dw = dw.sum(axis=0, keepdims=True)
+        return join_blocks(dx1, layout), dsh, dw
