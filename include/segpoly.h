@@ -24,14 +24,14 @@
  *    segpoly_last_error() returns a message for the calling thread.
  *  - Device pointers are plain addresses of device memory owned by the
  *    caller; the library never frees them, never keeps them after a call
- *    returns, and never allocates on the forward path except the one-time
+ *    returns, and never allocates on the compute calls except the one-time
  *    upload of coefficient tables described at tp_conv_fwd / symcon_fwd.
- *  - `stream` is a hipStream_t (NULL: the default stream).  Forward calls
+ *  - `stream` is a hipStream_t (NULL: the default stream).  Compute calls
  *    are asynchronous and stream-ordered; they do not synchronise unless the
  *    VALIDATE flag is set.
  *  - Handles hold only host state (descriptor, tables) and may be created,
  *    queried and destroyed on a machine without a GPU.  A handle may be used
- *    from several threads for forward calls; create/destroy are not
+ *    from several threads for compute calls; create/destroy are not
  *    concurrent with other uses of the same handle.
  *  - Irreps strings: O(3) irreps "MULxLP + ..." with P = e or o, e.g.
  *    "32x0e + 32x1o" (Lesson 12a, section 21.2).
@@ -161,6 +161,53 @@ int tp_kernel_name(tp_handle h, char* buf, size_t cap);
 int tp_conv_fwd(tp_handle h, const void* x, int64_t n_src, const void* sh, const void* w,
                 const void* src, const void* dst, int idx_dtype, int64_t n_edges, int64_t n_nodes,
                 void* out, void* stream);
+
+/*
+ * tp_conv_bwd_workspace: device workspace tp_conv_bwd needs for n_edges
+ * edges: n_edges * DIM_IN1 elements of the handle's dtype (one source
+ * message per edge).  Batch mode needs none.
+ */
+int tp_conv_bwd_workspace(tp_handle h, int64_t n_edges, size_t* bytes);
+
+/*
+ * tp_conv_bwd: vector-Jacobian product of tp_conv_fwd, the gradients of
+ * every operand that the pages' examples check ("cuequivariance-torch"
+ * skill document, "CPU tensor product and backward" and "SegmentedPolynomial:
+ * gather and scatter": gradients of features, vectors and weights; the
+ * gradient of a gathered input sums over the edges that read it).  With
+ * g = dL/d(out):
+ *   grad_w[e]  = g[dst[e]] contracted with the path products of
+ *                x[src[e]] and sh[e];
+ *   grad_sh[e] = sum over paths and channels of w[e] x[src[e]] g[dst[e]]
+ *                contracted with the coupling;
+ *   grad_x[s]  = sum over edges e with src[e] == s of w[e] sh[e] g[dst[e]]
+ *                contracted with the coupling (zero for a source without
+ *                edges).
+ * Every element of grad_x, grad_sh and grad_w is overwritten.  Edges whose
+ * source or destination lies outside its range get zero gradients and add
+ * nothing to grad_x.
+ *   x, sh, w, src, dst, idx_dtype, n_src, n_edges, n_nodes: as tp_conv_fwd
+ *              (per-edge weights only).
+ *   src_perm   [n_edges] device, idx_dtype: the edge ids ordered by src
+ *              ascending (a stable argsort of src: the order within one
+ *              source is the order in which its messages are summed, so a
+ *              fixed perm gives bitwise-reproducible grad_x).  A permutation
+ *              is a precondition, checked only with VALIDATE (E_RANGE).  NULL
+ *              in batch mode.
+ *   grad_out   [n_nodes, DIM_OUT] device, layout of the handle.
+ *   grad_x     [n_src, DIM_IN1] device.  grad_sh [n_edges, DIM_IN2] device.
+ *   grad_w     [n_edges, WEIGHT_NUMEL] device.
+ *   workspace  device, at least tp_conv_bwd_workspace() bytes, aligned like
+ *              the operands; may be NULL in batch mode or with no edges.
+ * Two launches on `stream` (one in batch mode), no atomics: results are
+ * deterministic.  Fails closed with E_UNSUPPORTED for shared weights, for a
+ * descriptor without a specialised kernel, and for a multiplicity above 64
+ * that is odd, above 128, or whose operands are not aligned to two elements.
+ */
+int tp_conv_bwd(tp_handle h, const void* x, int64_t n_src, const void* sh, const void* w, const void* src,
+                const void* dst, const void* src_perm, int idx_dtype, int64_t n_edges, int64_t n_nodes,
+                const void* grad_out, void* grad_x, void* grad_sh, void* grad_w, void* workspace,
+                size_t workspace_bytes, void* stream);
 
 /* tp_destroy: free the handle (NULL is a no-op). */
 int tp_destroy(tp_handle h);

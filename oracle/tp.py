@@ -141,7 +141,8 @@ class ChannelwiseTP:
             woff += mul
         return join_blocks(out_parts, layout)
 
-    def conv_vjp(self, x, sh, w, src, dst, n_nodes, g, layout="mul_ir", shared_weights=False):
+    def conv_vjp(self, x, sh, w, src, dst, n_nodes, g, layout="mul_ir", shared_weights=False,
+                 absolute=False):
         """Vector-Jacobian product of :meth:`conv` (per-edge weights, or one
         shared row with ``shared_weights``): given g = dL/d(out) [n_nodes,
         dim_out] in ``layout``, return (dL/dx [n_src, dim_in1] in ``layout``,
@@ -151,11 +152,16 @@ class ChannelwiseTP:
         in each operand):
             dw[e, p, u]     = sum_k g[dst_e, p, k, u] sum_ij C[i,j,k] x[src_e, i, u] sh[e, j]
             dsh[e, blk2_p, j] += sum_u w[e, p, u] sum_ik C[i,j,k] x[src_e, i, u] g[dst_e, p, k, u]
-            dx[src_e, blk1_p, i, u] += w[e, p, u] sum_jk C[i,j,k] sh[e, j] g[dst_e, p, k, u]"""
+            dx[src_e, blk1_p, i, u] += w[e, p, u] sum_jk C[i,j,k] sh[e, j] g[dst_e, p, k, u]
+
+        ``absolute`` evaluates the same sums over |x|, |sh|, |w|, |g| and |C|:
+        the scale of the rounding error of any summation order."""
         x = np.asarray(x, dtype=np.float64)
         sh = np.asarray(sh, dtype=np.float64)
         w = np.asarray(w, dtype=np.float64)
         g = np.asarray(g, dtype=np.float64)
+        if absolute:
+            x, sh, w, g = np.abs(x), np.abs(sh), np.abs(w), np.abs(g)
         n_edges = sh.shape[0]
         if src is None:
             src = np.arange(n_edges)
@@ -174,13 +180,15 @@ class ChannelwiseTP:
             mul, l1, _ = self.in1[i]
             l2 = self.in2[j][1]
             c = real_cg(l1, l2, lo)
+            if absolute:
+                c = np.abs(c)
             a = x1[i][src]                               # [E, 2l1+1, mul]
             b = x2[j][:, :, 0]                           # [E, 2l2+1]
             ge = gb[p][dst]                              # [E, 2lo+1, mul]
             ww = np.broadcast_to(w[:, woff:woff + mul], (n_edges, mul))
-            dw[:, woff:woff + mul] = np.einsum("ijk,eiu,ej,eku->eu", c, a, b, ge)
-            dsh[:, off2[j]:off2[j + 1]] += np.einsum("ijk,eiu,eku,eu->ej", c, a, ge, ww)
-            np.add.at(dx1[i], src, np.einsum("ijk,ej,eku,eu->eiu", c, b, ge, ww))
+            dw[:, woff:woff + mul] = np.einsum("ijk,eiu,ej,eku->eu", c, a, b, ge, optimize=True)
+            dsh[:, off2[j]:off2[j + 1]] += np.einsum("ijk,eiu,eku,eu->ej", c, a, ge, ww, optimize=True)
+            np.add.at(dx1[i], src, np.einsum("ijk,ej,eku,eu->eiu", c, b, ge, ww, optimize=True))
             woff += mul
         if shared_weights:
             dw = dw.sum(axis=0, keepdims=True)

@@ -1,7 +1,7 @@
 """Python binding of ``libsegpoly.so`` (argument marshalling only).
 
 The functions keep the names of the C ABI in ``include/segpoly.h``:
-``tp_create`` / ``tp_conv_fwd`` / ``symcon_create`` / ``symcon_fwd``.  Every
+``tp_create`` / ``tp_conv_fwd`` / ``tp_conv_bwd`` / ``symcon_create`` / ``symcon_fwd``.  Every
 step of the computation runs in the library's HIP kernels; PyTorch only
 supplies device memory and the current stream.  There is no CPU fallback:
 importing this package fails loudly if the library has not been built.
@@ -29,7 +29,7 @@ _DTYPES = {"f32": F32, "f64": F64}
 
 # every symbol include/segpoly.h declares
 EXPORTS = ("tp_create", "tp_query", "tp_irreps_out", "tp_path_info", "tp_path_cg", "tp_kernel_name",
-           "tp_conv_fwd", "tp_destroy", "symcon_create", "symcon_query", "symcon_coupling_info",
+           "tp_conv_fwd", "tp_conv_bwd_workspace", "tp_conv_bwd", "tp_destroy", "symcon_create", "symcon_query", "symcon_coupling_info",
            "symcon_coupling_dense", "symcon_fwd", "symcon_destroy", "segpoly_real_cg",
            "segpoly_last_error", "segpoly_version")
 
@@ -59,7 +59,7 @@ def hip_runtimes_loaded():
 
 def _load():
     if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is missing: build it with `python -m segmented_polynomials_amd.build`")
+        raise ImportError(f"{LIB_PATH} is missing: build it with `python segmented_polynomials_amd/build.py`")
     _hip_runtime_of_torch()
     lib = ctypes.CDLL(LIB_PATH)
     vp, i64, c_int, c_uint = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_uint
@@ -73,6 +73,8 @@ def _load():
         "tp_path_cg": [vp, c_int, pd],
         "tp_kernel_name": [vp, ctypes.c_char_p, ctypes.c_size_t],
         "tp_conv_fwd": [vp, vp, i64, vp, vp, vp, vp, c_int, i64, i64, vp, vp],
+        "tp_conv_bwd_workspace": [vp, i64, ctypes.POINTER(ctypes.c_size_t)],
+        "tp_conv_bwd": [vp, vp, i64, vp, vp, vp, vp, vp, c_int, i64, i64, vp, vp, vp, vp, vp, ctypes.c_size_t, vp],
         "tp_destroy": [vp],
         "symcon_create": [ctypes.c_char_p, ctypes.c_char_p, c_int, c_int, c_int, c_int, c_uint, ctypes.POINTER(vp)],
         "symcon_query": [vp, c_int, p64],
@@ -236,6 +238,53 @@ def tp_conv_fwd(h, x, sh, w, src=None, dst=None, n_nodes=None, out=None):
     _check(lib.tp_conv_fwd(h._h, _ptr(x), n_src, _ptr(sh), _ptr(w), _ptr(src), _ptr(dst), idx, n_edges,
                            n_nodes, _ptr(out), _stream_ptr(x.device)))
     return out
+
+
+def tp_conv_bwd_workspace(h, n_edges):
+    """Bytes of device workspace ``tp_conv_bwd`` needs for ``n_edges`` edges."""
+    v = ctypes.c_size_t()
+    _check(lib.tp_conv_bwd_workspace(h._h, n_edges, ctypes.byref(v)))
+    return v.value
+
+
+def tp_conv_bwd(h, x, sh, w, grad_out, src=None, dst=None, src_perm=None, n_nodes=None, workspace=None):
+    """Gradients (grad_x, grad_sh, grad_w) of ``tp_conv_fwd`` for the output
+    gradient ``grad_out`` [n_nodes, dim_out].  ``src_perm`` lists the edge ids
+    ordered by src (a stable argsort of src), part of the graph like the
+    sorted dst.  The workspace is allocated if not given."""
+    import torch
+    t = _torch_dtype(h.dtype)
+    for name, a in (("x", x), ("sh", sh), ("w", w), ("grad_out", grad_out)):
+        if a.dtype != t or not a.is_cuda or not a.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous {t} device tensor")
+    n_src, n_edges = x.shape[0], sh.shape[0]
+    if x.shape[1] != h.dim_in1 or sh.shape[1] != h.dim_in2 or w.shape != (n_edges, h.weight_numel):
+        raise ValueError("operand widths do not match the descriptor")
+    if not (src is None) == (dst is None) == (src_perm is None):
+        raise ValueError("give src, dst and src_perm, or none of them")
+    idx = I32
+    if src is not None:
+        for name, a in (("src", src), ("dst", dst), ("src_perm", src_perm)):
+            if a.shape != (n_edges,) or a.dtype != src.dtype or not a.is_cuda or not a.is_contiguous():
+                raise ValueError(f"{name} must be a contiguous [n_edges] device tensor of the index dtype")
+        idx = _index_dtype(src)
+    if n_nodes is None:
+        if src is not None:
+            raise ValueError("n_nodes is required with indices")
+        n_nodes = n_edges
+    if grad_out.shape != (n_nodes, h.dim_out):
+        raise ValueError("grad_out must be [n_nodes, dim_out]")
+    gx = torch.empty_like(x)
+    gsh = torch.empty_like(sh)
+    gw = torch.empty_like(w)
+    need = tp_conv_bwd_workspace(h, n_edges) if src is not None else 0
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.tp_conv_bwd(h._h, _ptr(x), n_src, _ptr(sh), _ptr(w), _ptr(src), _ptr(dst), _ptr(src_perm), idx,
+                           n_edges, n_nodes, _ptr(grad_out), _ptr(gx), _ptr(gsh), _ptr(gw), _ptr(workspace),
+                           wbytes, _stream_ptr(x.device)))
+    return gx, gsh, gw
 
 
 # ---------------------------------------------------------------- symcon

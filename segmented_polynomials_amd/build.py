@@ -7,7 +7,8 @@ with hipcc (``--offload-arch=gfx950``, packed-FP32 instructions disabled);
 link the shared library next to this file.  Every call rebuilds from
 scratch; objects go to ``_build/`` (not part of the sources).
 
-Run ``python -m segmented_polynomials_amd.build`` or call :func:`build`.
+Run ``python segmented_polynomials_amd/build.py`` (it does not import the
+package, whose import needs the built library) or call :func:`build`.
 """
 
 import concurrent.futures as cf

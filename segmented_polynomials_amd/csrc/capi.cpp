@@ -107,6 +107,27 @@ int check_indices(const void* dsrc, const void* ddst, int64_t n_edges, int64_t n
   return ok();
 }
 
+// VALIDATE for the backward: perm is a permutation of the edges with
+// src[perm[.]] ascending.
+template <typename Index>
+int check_perm(const void* dsrc, const void* dperm, int64_t n_edges, void* stream) {
+  std::vector<Index> s(n_edges), p(n_edges);
+  hipError_t e = hipStreamSynchronize(static_cast<hipStream_t>(stream));
+  if (e == hipSuccess && n_edges) e = hipMemcpy(s.data(), dsrc, n_edges * sizeof(Index), hipMemcpyDeviceToHost);
+  if (e == hipSuccess && n_edges) e = hipMemcpy(p.data(), dperm, n_edges * sizeof(Index), hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return fail(SEGPOLY_E_HIP, std::string("validate copy: ") + hipGetErrorString(e));
+  std::vector<char> seen(n_edges, 0);
+  for (int64_t i = 0; i < n_edges; ++i) {
+    const int64_t q = static_cast<int64_t>(p[i]);
+    if (q < 0 || q >= n_edges || seen[q])
+      return fail(SEGPOLY_E_RANGE, "src_perm is not a permutation of the edges (entry " + std::to_string(i) + ")");
+    seen[q] = 1;
+    if (i && s[q] < s[p[i - 1]])
+      return fail(SEGPOLY_E_UNSORTED, "src[src_perm[.]] is not ascending at entry " + std::to_string(i));
+  }
+  return ok();
+}
+
 template <typename Index>
 int check_species(const void* dsp, int64_t n, int num_elements, void* stream) {
   std::vector<Index> s(n);
@@ -345,6 +366,88 @@ int tp_conv_fwd(tp_handle h, const void* x, int64_t n_src, const void* sh, const
     g.dimo = d.dimo;
     rc = launch_tp_generic(a, g);
   }
+  if (rc != 0)
+    return fail(SEGPOLY_E_HIP, std::string("kernel launch failed: ") + hipGetErrorString(static_cast<hipError_t>(rc)));
+  return ok();
+}
+
+int tp_conv_bwd_workspace(tp_handle h, int64_t n_edges, size_t* bytes) {
+  if (!h || !bytes) return fail(SEGPOLY_E_INVALID, "null argument");
+  if (n_edges < 0) return fail(SEGPOLY_E_INVALID, "negative size");
+  const size_t esz = h->dtype == SEGPOLY_F32 ? 4 : 8;
+  *bytes = static_cast<size_t>(n_edges) * static_cast<size_t>(h->d.dim1) * esz;
+  return ok();
+}
+
+int tp_conv_bwd(tp_handle h, const void* x, int64_t n_src, const void* sh, const void* w, const void* src,
+                const void* dst, const void* src_perm, int idx_dtype, int64_t n_edges, int64_t n_nodes,
+                const void* grad_out, void* grad_x, void* grad_sh, void* grad_w, void* workspace,
+                size_t workspace_bytes, void* stream) {
+  if (!h) return fail(SEGPOLY_E_INVALID, "null handle");
+  if (n_src < 0 || n_edges < 0 || n_nodes < 0) return fail(SEGPOLY_E_INVALID, "negative size");
+  if (idx_dtype != SEGPOLY_I32 && idx_dtype != SEGPOLY_I64) return fail(SEGPOLY_E_INVALID, "bad index dtype");
+  if ((src == nullptr) != (dst == nullptr) || (src == nullptr) != (src_perm == nullptr))
+    return fail(SEGPOLY_E_INVALID, "src, dst and src_perm must all be given or all be NULL");
+  const auto& d = h->d;
+  if (h->flags & SEGPOLY_SHARED_WEIGHTS)
+    return fail(SEGPOLY_E_UNSUPPORTED, "backward with shared weights is not supported");
+  if (!h->spec || !h->spec->launch_bwd)
+    return fail(SEGPOLY_E_UNSUPPORTED, "backward needs a specialised kernel for this descriptor");
+  const bool batch = src == nullptr && n_edges > 0;
+  if (batch && (n_edges != n_nodes || n_src < n_edges))
+    return fail(SEGPOLY_E_INVALID, "batch mode needs n_edges == n_nodes <= n_src");
+  if (n_nodes > kMaxGrid || n_src > kMaxGrid) return fail(SEGPOLY_E_UNSUPPORTED, "n_nodes and n_src must be below 2^31");
+  if (n_src > 0 && !grad_x) return fail(SEGPOLY_E_INVALID, "null grad_x");
+  if (n_edges > 0) {
+    if (!grad_w || (!grad_sh && d.dim2 > 0)) return fail(SEGPOLY_E_INVALID, "null grad_sh or grad_w");
+    if (n_nodes > 0) {
+      if (!sh && d.dim2 > 0) return fail(SEGPOLY_E_INVALID, "null sh");
+      if (!w) return fail(SEGPOLY_E_INVALID, "null w");
+      if (!x && n_src > 0) return fail(SEGPOLY_E_INVALID, "null x");
+      if (!grad_out) return fail(SEGPOLY_E_INVALID, "null grad_out");
+    }
+    if (!batch) {
+      size_t need = 0;
+      tp_conv_bwd_workspace(h, n_edges, &need);
+      if (!workspace || workspace_bytes < need)
+        return fail(SEGPOLY_E_INVALID, "workspace missing or smaller than tp_conv_bwd_workspace()");
+    }
+  }
+  if ((h->flags & SEGPOLY_VALIDATE) && !batch) {
+    int st = idx_dtype == SEGPOLY_I32 ? check_indices<int32_t>(src, dst, n_edges, n_src, n_nodes, stream)
+                                      : check_indices<int64_t>(src, dst, n_edges, n_src, n_nodes, stream);
+    if (st == SEGPOLY_OK)
+      st = idx_dtype == SEGPOLY_I32 ? check_perm<int32_t>(src, src_perm, n_edges, stream)
+                                    : check_perm<int64_t>(src, src_perm, n_edges, stream);
+    if (st != SEGPOLY_OK) return st;
+  }
+  if (n_src == 0 && n_edges == 0) return ok();
+  TPBwdArgs a{};
+  a.x = x;
+  a.sh = sh;
+  a.w = w;
+  a.src = src;
+  a.dst = dst;
+  a.perm = src_perm;
+  a.g = grad_out;
+  a.dx = grad_x;
+  a.dsh = grad_sh;
+  a.dw = grad_w;
+  a.workspace = workspace;
+  a.n_src = n_src;
+  a.n_edges = n_edges;
+  a.n_nodes = n_nodes;
+  a.mul = d.mul;
+  a.batch = batch ? 1 : 0;
+  a.dtype = h->dtype;
+  a.idx = idx_dtype;
+  a.layout = h->layout;
+  a.stream = stream;
+  const int rc = h->spec->launch_bwd(a);
+  if (rc == -2)
+    return fail(SEGPOLY_E_UNSUPPORTED,
+                "backward covers up to 64 channels, or up to 128 in pairs (even multiplicity, operands aligned "
+                "to two elements)");
   if (rc != 0)
     return fail(SEGPOLY_E_HIP, std::string("kernel launch failed: ") + hipGetErrorString(static_cast<hipError_t>(rc)));
   return ok();

@@ -131,6 +131,121 @@ void emit_path_body(const TPPath& p, QN qn, XN X, WN W, AN A, const std::string&
   }
 }
 
+// Row load/store of a per-channel component array in either layout, with
+// CPL (1 or 2) adjacent channels ub, ub+1 per lane.  `blocks` lists
+// (component offset, 2l+1) of the row's blocks; `n` is the array width
+// constant (NX or NK).  With CPL = 2 every load is one aligned pair; ir_mul
+// stores stay two plain stores (a pair store assembled from two slots of the
+// register array keeps part of it out of registers on this compiler).
+void emit_row_io(std::ostream& os, const std::string& fname, const std::string& n,
+                 const std::vector<std::pair<int, int>>& blocks, int nc, bool load) {
+  const std::string arr = "v";
+  if (load)
+    os << "  template <typename T, int LAYOUT, int CPL, bool NT = false>\n  __device__ __forceinline__ static void "
+       << fname << "(const T* __restrict__ row, int mul, int ub, T (&v)[CPL][" << n << "]) {\n";
+  else
+    os << "  template <typename T, int LAYOUT, int CPL, bool NT = false>\n  __device__ __forceinline__ static void "
+       << fname << "(T* __restrict__ row, int mul, int ub, const T (&v)[CPL][" << n << "]) {\n";
+  os << "    static_assert(CPL == 1 || CPL == 2, \"one or two channels per lane\");\n";
+  auto at = [](int s, int c) { return "v[" + std::to_string(s) + "][" + std::to_string(c) + "]"; };
+  os << "    if constexpr (LAYOUT == kIrMul) {\n      if constexpr (CPL == 2) {\n";
+  for (int m = 0; m < nc; ++m) {
+    const std::string a0 = "row + " + std::to_string(m) + " * mul + ub";
+    if (load)
+      os << "        { const auto t = ld2<T, NT>(" << a0 << "); " << at(0, m) << " = t.x; " << at(1, m) << " = t.y; }\n";
+    else
+      os << "        st1<T, NT>(" << a0 << ", " << at(0, m) << "); st1<T, NT>(" << a0 << " + 1, " << at(1, m) << ");\n";
+  }
+  os << "      } else {\n";
+  for (int m = 0; m < nc; ++m) {
+    const std::string a0 = "row + " + std::to_string(m) + " * mul + ub";
+    if (load)
+      os << "        " << at(0, m) << " = ld1<T, NT>(" << a0 << ");\n";
+    else
+      os << "        st1<T, NT>(" << a0 << ", " << at(0, m) << ");\n";
+  }
+  os << "      }\n    } else {\n      if constexpr (CPL == 2) {\n";
+  for (const auto& [comp, dl] : blocks) {
+    // channels ub, ub+1 hold 2*dl consecutive values: element q -> slot q / dl, component q % dl
+    for (int pq = 0; pq < dl; ++pq) {
+      const int q0 = 2 * pq, q1 = 2 * pq + 1;
+      const std::string a = "row + " + std::to_string(comp) + " * mul + ub * " + std::to_string(dl) + " + " + std::to_string(q0);
+      if (load)
+        os << "        { const auto t = ld2<T, NT>(" << a << "); " << at(q0 / dl, comp + q0 % dl) << " = t.x; "
+           << at(q1 / dl, comp + q1 % dl) << " = t.y; }\n";
+      else
+        os << "        st2<T, NT>(" << a << ", " << at(q0 / dl, comp + q0 % dl) << ", " << at(q1 / dl, comp + q1 % dl)
+           << ");\n";
+    }
+  }
+  os << "      } else {\n";
+  for (const auto& [comp, dl] : blocks)
+    for (int i = 0; i < dl; ++i) {
+      const std::string a = "row + " + std::to_string(comp) + " * mul + ub * " + std::to_string(dl) + " + " + std::to_string(i);
+      if (load)
+        os << "        " << at(0, comp + i) << " = ld1<T, NT>(" << a << ");\n";
+      else
+        os << "        st1<T, NT>(" << a << ", " << at(0, comp + i) << ");\n";
+    }
+  os << "      }\n    }\n  }\n\n";
+}
+
+// Backward per path: r_k = w g_k; dw = sum_k g_k t_k with t_k the forward
+// contraction; the source message m_i += sum_{j,k} c sh_j r_k; the harmonics
+// gradient h_j += sum_{i,k} c x_i r_k (summed over the lane's channels).
+void emit_path_bwd(const TPPath& p, int pi, std::ostream& e) {
+  const int X = p.xcomp, K = p.kcomp, J = static_cast<int>(p.off2), dl = 2 * p.lo + 1;
+  QTable lq;
+  std::ostringstream body;
+  const std::string ind = "        ";
+  auto x = [&](int i) { return "xv[s][" + std::to_string(X + i) + "]"; };
+  auto gk = [&](int k) { return "gv[s][" + std::to_string(K + k) + "]"; };
+  for (int k = 0; k < dl; ++k) body << ind << "const T r" << k << " = wv[s][" << pi << "] * " << gk(k) << ";\n";
+  // t_k and dw
+  int cur = -1;
+  for (size_t n = 0; n < p.nz.size(); ++n) {
+    const auto& z = p.nz[n];
+    std::string q = std::string(z.c < 0 ? "-" : "") + "q" + std::to_string(lq.get(std::fabs(z.c), J + z.j));
+    if (z.k != cur) {
+      cur = z.k;
+      body << ind << "T t" << z.k << " = " << q << " * " << x(z.i) << ";\n";
+    } else {
+      body << ind << "t" << z.k << " = fmadd(" << q << ", " << x(z.i) << ", t" << z.k << ");\n";
+    }
+  }
+  body << ind << "T dw = T(0);\n";
+  for (int k = 0; k < dl; ++k) {
+    bool has = false;
+    for (const auto& z : p.nz) has = has || z.k == k;
+    if (has) body << ind << "dw = fmadd(" << gk(k) << ", t" << k << ", dw);\n";
+  }
+  body << ind << "dwv[s][" << pi << "] = dw;\n";
+  // source message
+  for (const auto& z : p.nz) {
+    std::string q = std::string(z.c < 0 ? "-" : "") + "q" + std::to_string(lq.get(std::fabs(z.c), J + z.j));
+    body << ind << "mxv[s][" << X + z.i << "] = fmadd(" << q << ", r" << z.k << ", mxv[s][" << X + z.i << "]);\n";
+  }
+  // harmonics gradient, one product x_i r_k per (i, k)
+  int ck = -1, ci = -1;
+  for (const auto& z : p.nz) {
+    if (z.k != ck || z.i != ci) {
+      ck = z.k;
+      ci = z.i;
+      body << ind << "const T xr" << z.i << "_" << z.k << " = " << x(z.i) << " * r" << z.k << ";\n";
+    }
+    body << ind << "hsh[" << J + z.j << "] = fmadd(" << lit(z.c) << ", xr" << z.i << "_" << z.k << ", hsh[" << J + z.j
+         << "]);\n";
+  }
+  for (size_t n = 0; n < lq.entries.size(); ++n) {
+    const auto& [c, j] = lq.entries[n];
+    if (c == 1.0)
+      e << "      const T q" << n << " = sh[" << j << "];\n";
+    else
+      e << "      const T q" << n << " = " << lit(c) << " * sh[" << j << "];\n";
+  }
+  e << "#pragma unroll\n      for (int s = 0; s < CPL; ++s) {\n" << body.str() << "      }\n";
+}
+
 void emit_tp(const std::string& name, unsigned dtypes, const TPDescriptor& d, std::ostream& os) {
   if (!d.uniform_mul) throw std::runtime_error("spec " + name + ": input-1 multiplicities must be uniform");
   const std::string S = "TPSpec_" + name;
@@ -161,78 +276,36 @@ void emit_tp(const std::string& name, unsigned dtypes, const TPDescriptor& d, st
 
   os << "// Generated by codegen.cpp from the descriptor: " << irreps_str(d.in1) << " x " << irreps_str(d.in2)
      << " -> " << irreps_str(d.out) << "\n// key " << d.key << "\n";
-  os << "#include \"kernels/tp_conv_spec.hpp\"\n\nnamespace segpoly {\nnamespace kern {\n\n";
+  os << "#include \"kernels/tp_conv_spec.hpp\"\n#include \"kernels/tp_conv_bwd.hpp\"\n\nnamespace segpoly {\nnamespace kern {\n\n";
   os << "struct " << S << " {\n";
   os << "  static constexpr int NX = " << d.nx << ";\n";
   os << "  static constexpr int NK = " << d.nk << ";\n";
   os << "  static constexpr int NP = " << d.paths.size() << ";\n";
   os << "  static constexpr int D2 = " << d.dim2 << ";\n\n";
-  // load_xs / store_s: CPL (1 or 2) adjacent channels ub, ub+1 per lane;
-  // with CPL = 2 every access is one aligned pair (no staging arrays, so
-  // everything stays in registers)
-  auto pair_ld = [](std::ostream& o, const std::string& addr, const std::string& d0, const std::string& d1) {
-    o << "        { const auto t = ld2<T, NTX>(" << addr << "); " << d0 << " = t.x; " << d1 << " = t.y; }\n";
-  };
-  auto pair_st = [](std::ostream& o, const std::string& addr, const std::string& s0, const std::string& s1) {
-    o << "        st2<T, NTS>(" << addr << ", " << s0 << ", " << s1 << ");\n";
-  };
-  os << "  template <typename T, int LAYOUT, int CPL, bool NTX = false>\n  __device__ __forceinline__ static void load_xs(const T* __restrict__ row, int mul, int ub, T (&xv)[CPL][NX]) {\n";
-  os << "    static_assert(CPL == 1 || CPL == 2, \"one or two channels per lane\");\n";
-  os << "    if constexpr (LAYOUT == kIrMul) {\n      if constexpr (CPL == 2) {\n";
-  for (int m = 0; m < d.nx; ++m)
-    pair_ld(os, "row + " + std::to_string(m) + " * mul + ub", "xv[0][" + std::to_string(m) + "]",
-            "xv[1][" + std::to_string(m) + "]");
-  os << "      } else {\n";
-  for (int m = 0; m < d.nx; ++m) os << "        xv[0][" << m << "] = row[" << m << " * mul + ub];\n";
-  os << "      }\n    } else {\n      if constexpr (CPL == 2) {\n";
-  for (size_t b = 0; b < d.in1.size(); ++b) {
+  std::vector<std::pair<int, int>> in_blocks, out_blocks;
+  {
     int comp = 0;
-    for (size_t bb = 0; bb < b; ++bb) comp += 2 * d.in1[bb].l + 1;
-    const int dl = 2 * d.in1[b].l + 1;
-    // channels ub, ub+1 hold 2*dl consecutive values: element q -> slot q / dl, comp q % dl
-    for (int pq = 0; pq < dl; ++pq) {
-      int q0 = 2 * pq, q1 = 2 * pq + 1;
-      pair_ld(os, "row + " + std::to_string(comp) + " * mul + ub * " + std::to_string(dl) + " + " + std::to_string(q0),
-              "xv[" + std::to_string(q0 / dl) + "][" + std::to_string(comp + q0 % dl) + "]",
-              "xv[" + std::to_string(q1 / dl) + "][" + std::to_string(comp + q1 % dl) + "]");
+    for (const auto& r : d.in1) {
+      in_blocks.push_back({comp, 2 * r.l + 1});
+      comp += 2 * r.l + 1;
     }
+    for (const auto& p : d.paths) out_blocks.push_back({p.kcomp, 2 * p.lo + 1});
   }
-  os << "      } else {\n";
-  for (size_t b = 0; b < d.in1.size(); ++b) {
-    int comp = 0;
-    for (size_t bb = 0; bb < b; ++bb) comp += 2 * d.in1[bb].l + 1;
-    const int dl = 2 * d.in1[b].l + 1;
-    for (int i = 0; i < dl; ++i)
-      os << "        xv[0][" << comp + i << "] = row[" << comp << " * mul + ub * " << dl << " + " << i << "];\n";
+  emit_row_io(os, "load_xs", "NX", in_blocks, d.nx, true);
+  emit_row_io(os, "store_xs", "NX", in_blocks, d.nx, false);
+  emit_row_io(os, "load_gs", "NK", out_blocks, d.nk, true);
+  emit_row_io(os, "store_s", "NK", out_blocks, d.nk, false);
+  os << "  template <typename T, int CPL>\n  __device__ __forceinline__ static void bwd(const T (&xv)[CPL][NX], const T* __restrict__ sh,\n"
+        "      const T (&wv)[CPL][NP], const T (&gv)[CPL][NK], T (&dwv)[CPL][NP], T (&mxv)[CPL][NX], T (&hsh)[D2]) {\n";
+  os << "#pragma unroll\n    for (int s = 0; s < CPL; ++s)\n#pragma unroll\n      for (int i = 0; i < NX; ++i) mxv[s][i] = T(0);\n";
+  os << "#pragma unroll\n    for (int j = 0; j < D2; ++j) hsh[j] = T(0);\n";
+  for (size_t pi = 0; pi < d.paths.size(); ++pi) {
+    const TPPath& p = d.paths[pi];
+    os << "    // path " << pi << ": " << p.l1 << " x " << p.l2 << " -> " << p.lo << "\n    {\n";
+    emit_path_bwd(p, static_cast<int>(pi), os);
+    os << "    }\n";
   }
-  os << "      }\n    }\n  }\n\n";
-  os << "  template <typename T, int LAYOUT, int CPL, bool NTS>\n  __device__ __forceinline__ static void store_s(T* __restrict__ row, int mul, int ub, const T (&acc)[CPL][NK]) {\n";
-  os << "    if constexpr (LAYOUT == kIrMul) {\n      if constexpr (CPL == 2) {\n";
-  // two plain stores: a pair store built from acc[0][k] and acc[1][k] keeps
-  // part of acc out of registers (private memory) on this compiler
-  for (int k = 0; k < d.nk; ++k)
-    os << "        st1<T, NTS>(row + " << k << " * mul + ub, acc[0][" << k << "]); st1<T, NTS>(row + " << k
-       << " * mul + ub + 1, acc[1][" << k << "]);\n";
-  os << "      } else {\n";
-  for (int k = 0; k < d.nk; ++k) os << "        st1<T, NTS>(row + " << k << " * mul + ub, acc[0][" << k << "]);\n";
-  os << "      }\n    } else {\n      if constexpr (CPL == 2) {\n";
-  for (const auto& p : d.paths) {
-    const int dl = 2 * p.lo + 1;
-    for (int pq = 0; pq < dl; ++pq) {
-      int q0 = 2 * pq, q1 = 2 * pq + 1;
-      pair_st(os, "row + " + std::to_string(p.kcomp) + " * mul + ub * " + std::to_string(dl) + " + " + std::to_string(q0),
-              "acc[" + std::to_string(q0 / dl) + "][" + std::to_string(p.kcomp + q0 % dl) + "]",
-              "acc[" + std::to_string(q1 / dl) + "][" + std::to_string(p.kcomp + q1 % dl) + "]");
-    }
-  }
-  os << "      } else {\n";
-  for (const auto& p : d.paths) {
-    const int dl = 2 * p.lo + 1;
-    for (int k = 0; k < dl; ++k)
-      os << "        st1<T, NTS>(row + " << p.kcomp << " * mul + ub * " << dl << " + " << k << ", acc[0][" << p.kcomp + k
-         << "]);\n";
-  }
-  os << "      }\n    }\n  }\n\n";
+  os << "  }\n\n";
   os << "  template <typename T, int CPL>\n  __device__ __forceinline__ static void edge(const T (&xv)[CPL][NX], const T* __restrict__ sh,\n"
         "                                                   const T (&wv)[CPL][NP], T (&acc)[CPL][NK]) {\n";
   os << edge.str();
@@ -240,6 +313,10 @@ void emit_tp(const std::string& name, unsigned dtypes, const TPDescriptor& d, st
   os << "int launch_tp_" << name << "(const TPArgs& a) {\n";
   if (dtypes & 1u) os << "  if (a.dtype == kF32) return kern::tp_conv_dispatch<kern::" << S << ", float>(a);\n";
   if (dtypes & 2u) os << "  if (a.dtype == kF64) return kern::tp_conv_dispatch<kern::" << S << ", double>(a);\n";
+  os << "  return -1;\n}\n\n";
+  os << "int launch_tp_bwd_" << name << "(const TPBwdArgs& a) {\n";
+  if (dtypes & 1u) os << "  if (a.dtype == kF32) return kern::tp_bwd_dispatch<kern::" << S << ", float>(a);\n";
+  if (dtypes & 2u) os << "  if (a.dtype == kF64) return kern::tp_bwd_dispatch<kern::" << S << ", double>(a);\n";
   os << "  return -1;\n}\n\n}  // namespace segpoly\n";
 }
 
@@ -401,17 +478,20 @@ int main(int argc, char** argv) {
   }
   std::ofstream reg(outdir + "/registry.cpp");
   reg << "// Generated by codegen.cpp: structure key -> specialised launcher.\n#include \"launch.hpp\"\n\nnamespace segpoly {\n\n";
-  for (const auto& r : regs)
+  for (const auto& r : regs) {
     reg << "int launch_" << r.kind << "_" << r.name << "(const " << (r.kind == "tp" ? "TPArgs" : "SymconArgs")
         << "&);\n";
+    if (r.kind == "tp") reg << "int launch_tp_bwd_" << r.name << "(const TPBwdArgs&);\n";
+  }
   reg << "\nconst TPSpecEntry kTPSpecs[] = {\n";
   int ntp = 0, nsc = 0;
   for (const auto& r : regs)
     if (r.kind == "tp") {
-      reg << "    {\"" << r.key << "\", \"" << r.name << "\", " << r.dtypes << "u, &launch_tp_" << r.name << "},\n";
+      reg << "    {\"" << r.key << "\", \"" << r.name << "\", " << r.dtypes << "u, &launch_tp_" << r.name << ", &launch_tp_bwd_"
+          << r.name << "},\n";
       ++ntp;
     }
-  if (!ntp) reg << "    {\"\", \"\", 0u, nullptr},\n";
+  if (!ntp) reg << "    {\"\", \"\", 0u, nullptr, nullptr},\n";
   reg << "};\nconst int kNumTPSpecs = " << ntp << ";\n\nconst SymconSpecEntry kSymconSpecs[] = {\n";
   for (const auto& r : regs)
     if (r.kind == "symcon") {

@@ -32,6 +32,14 @@ __device__ __forceinline__ void st2(T* __restrict__ p, T a, T b) {
 }
 
 template <typename T, bool NT>
+__device__ __forceinline__ T ld1(const T* __restrict__ p) {
+  if constexpr (NT)
+    return __builtin_nontemporal_load(p);
+  else
+    return *p;
+}
+
+template <typename T, bool NT>
 __device__ __forceinline__ void st1(T* __restrict__ p, T a) {
   if constexpr (NT)
     __builtin_nontemporal_store(a, p);

@@ -24,6 +24,26 @@ struct TPArgs {
   void* stream;
 };
 
+// Backward of the TP-conv (per-edge weights, specialised kernels only).
+struct TPBwdArgs {
+  const void* x;      // [n_src, dim1]
+  const void* sh;     // [n_edges, dim2]
+  const void* w;      // [n_edges, numel]
+  const void* src;    // [n_edges] or null (batch mode)
+  const void* dst;    // [n_edges], sorted ascending, or null (batch mode)
+  const void* perm;   // [n_edges] edge ids ordered by src, or null (batch mode)
+  const void* g;      // [n_nodes, dim_out] gradient of the output
+  void* dx;           // [n_src, dim1]
+  void* dsh;          // [n_edges, dim2]
+  void* dw;           // [n_edges, numel]
+  void* workspace;    // [n_edges, dim1] per-edge source messages (unused in batch mode)
+  int64_t n_src, n_edges, n_nodes;
+  int mul;
+  int batch;
+  int dtype, idx, layout;
+  void* stream;
+};
+
 struct SymconArgs {
   const void* x;        // [n_atoms, dim_in]
   const void* species;  // [n_atoms]
@@ -39,12 +59,14 @@ struct SymconArgs {
 // Returns 0 or a hipError_t value of the launch.
 using TPLaunchFn = int (*)(const TPArgs&);
 using SymconLaunchFn = int (*)(const SymconArgs&);
+using TPBwdLaunchFn = int (*)(const TPBwdArgs&);
 
 struct TPSpecEntry {
   const char* key;
   const char* name;
   unsigned dtypes;  // bit 0: f32, bit 1: f64
   TPLaunchFn launch;
+  TPBwdLaunchFn launch_bwd;
 };
 
 struct SymconSpecEntry {

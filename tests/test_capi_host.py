@@ -190,3 +190,34 @@ def test_forward_argument_errors_fail_before_any_gpu_call():
 def test_destroy_null_is_noop():
     assert sp.lib.tp_destroy(None) == sp.OK
     assert sp.lib.symcon_destroy(None) == sp.OK
+
+
+def test_backward_argument_errors_fail_before_any_gpu_call():
+    h = sp.tp_create("32x0e+32x1o", "0e+1o", "0e+1o")
+    assert h.specialized
+    n = ctypes.c_size_t()
+    assert sp.lib.tp_conv_bwd_workspace(h._h, 10, ctypes.byref(n)) == sp.OK
+    assert n.value == 10 * h.dim_in1 * 4
+    assert sp.lib.tp_conv_bwd_workspace(h._h, -1, ctypes.byref(n)) == sp.E_INVALID
+    f = sp.lib.tp_conv_bwd
+    p = ctypes.c_void_p(16)   # never dereferenced: every call below fails validation
+    big = 1 << 40
+    # h, x, n_src, sh, w, src, dst, perm, idx, n_edges, n_nodes, g, gx, gsh, gw, ws, ws_bytes, stream
+    assert f(None, p, 1, p, p, p, p, p, 0, 1, 1, p, p, p, p, p, big, None) == sp.E_INVALID
+    assert f(h._h, p, -1, p, p, p, p, p, 0, 1, 1, p, p, p, p, p, big, None) == sp.E_INVALID
+    assert f(h._h, p, 1, p, p, p, p, None, 0, 1, 1, p, p, p, p, p, big, None) == sp.E_INVALID  # no perm
+    assert f(h._h, p, 1, p, p, p, p, p, 7, 1, 1, p, p, p, p, p, big, None) == sp.E_INVALID     # index dtype
+    assert f(h._h, p, 1, p, p, p, p, p, 0, 1, 1, p, None, p, p, p, big, None) == sp.E_INVALID  # grad_x
+    assert f(h._h, p, 1, p, p, p, p, p, 0, 1, 1, p, p, p, None, p, big, None) == sp.E_INVALID  # grad_w
+    assert f(h._h, p, 1, p, p, p, p, p, 0, 1, 1, None, p, p, p, p, big, None) == sp.E_INVALID  # grad_out
+    assert f(h._h, p, 1, p, p, p, p, p, 0, 1, 1, p, p, p, p, p, 8, None) == sp.E_INVALID       # workspace small
+    assert f(h._h, p, 1, p, p, p, p, p, 0, 1, 1, p, p, p, p, None, big, None) == sp.E_INVALID  # no workspace
+    assert f(h._h, p, 1, p, p, None, None, None, 0, 2, 2, p, p, p, p, None, 0, None) == sp.E_INVALID  # batch
+    # shared weights and generic descriptors fail closed
+    hs = sp.tp_create("32x0e+32x1o", "0e+1o", "0e+1o", shared_weights=True)
+    assert f(hs._h, p, 1, p, p, p, p, p, 0, 1, 1, p, p, p, p, p, big, None) == sp.E_UNSUPPORTED
+    hg = sp.tp_create("32x0e+32x1o", "0e+1o", "0e+1o", force_generic=True)
+    assert f(hg._h, p, 1, p, p, p, p, p, 0, 1, 1, p, p, p, p, p, big, None) == sp.E_UNSUPPORTED
+    # nothing to do: succeeds without touching a device
+    assert f(h._h, None, 0, None, None, None, None, None, 0, 0, 0, None, None, None, None, None, 0,
+             None) == sp.OK

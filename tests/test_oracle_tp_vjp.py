@@ -69,3 +69,19 @@ def test_isolated_sources_get_zero_gradient():
     dx, _, _ = d.conv_vjp(x, sh, w, src, dst, n, g)
     unused = np.setdiff1d(np.arange(x.shape[0]), src)
     assert np.all(dx[unused] == 0)
+
+
+def test_absolute_mode_bounds_and_adjoint():
+    """The error scale: elementwise at least |VJP| (triangle inequality),
+    and the adjoint of the forward's absolute mode (both take |operands| and
+    |C|), operand by operand."""
+    d, x, sh, w, src, dst, n, g, rng = _case(4)
+    dx, dsh, dw = d.conv_vjp(x, sh, w, src, dst, n, g)
+    ax, ash, aw = d.conv_vjp(x, sh, w, src, dst, n, g, absolute=True)
+    for a, b in ((ax, dx), (ash, dsh), (aw, dw)):
+        assert np.all(a >= np.abs(b) - 1e-12)
+    vx, vs, vw = np.abs(rng.normal(size=x.shape)), np.abs(rng.normal(size=sh.shape)), np.abs(rng.normal(size=w.shape))
+    ag = np.abs(g)
+    assert np.isclose(np.sum(ag * d.conv(vx, sh, w, src, dst, n, absolute=True)), np.sum(ax * vx), rtol=1e-12)
+    assert np.isclose(np.sum(ag * d.conv(x, vs, w, src, dst, n, absolute=True)), np.sum(ash * vs), rtol=1e-12)
+    assert np.isclose(np.sum(ag * d.conv(x, sh, vw, src, dst, n, absolute=True)), np.sum(aw * vw), rtol=1e-12)

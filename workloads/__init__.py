@@ -268,3 +268,16 @@ def integer_tp_inputs(n_src, n_edges, dim1, dim2, numel, n_nodes, seed, max_degr
     w = rng.integers(-4, 5, size=(n_edges, numel)).astype(np.float32)
     return dict(x=x, sh=sh, w=w, src=src.astype(np.int32), dst=dst.astype(np.int32),
                 n_nodes=n_nodes, n_src=n_src)
+
+
+def output_gradient(n_nodes, dim_out, dtype, seed):
+    """A seeded standard-normal gradient of the convolution's output
+    [n_nodes, dim_out] (the input of the backward pass)."""
+    rng = np.random.default_rng(seed)
+    return _normal(rng, (n_nodes, dim_out), dtype).astype(_np_dtype(dtype), copy=False)
+
+
+def src_permutation(src):
+    """Edge ids ordered by source, ties in edge order (a stable argsort):
+    graph structure the backward pass takes with the sorted destinations."""
+    return np.argsort(np.asarray(src), kind="stable").astype(np.asarray(src).dtype)
