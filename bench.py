@@ -38,33 +38,40 @@ def parse():
     p.add_argument("--layout", default="ir_mul", choices=["ir_mul", "mul_ir"])
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-extras", action="store_true", help="skip the second layout and the symmetric contraction")
+    p.add_argument("--with-backward", action="store_true",
+                   help="time the backward on the same graph also under --no-extras")
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run a plain 1 GiB device copy (for the HBM counter scale factor)")
     return p.parse_args()
 
 
-def kernel_source_hash():
-    """Hash of everything the timed kernel is generated from, to tell whether
-    stored hardware counters still describe it."""
+FWD_SOURCES = ("kernels/tp_conv_spec.hpp", "kernels/common.hpp", "codegen.cpp", "specs.txt",
+               "tp_descriptor.cpp", "cg.cpp")
+BWD_SOURCES = FWD_SOURCES + ("kernels/tp_conv_bwd.hpp",)
+
+
+def kernel_source_hash(kind="fwd"):
+    """Hash of everything the timed kernels are generated from, to tell
+    whether stored hardware counters still describe them."""
     h = hashlib.sha256()
     base = os.path.join(ROOT, "segmented_polynomials_amd", "csrc")
-    for rel in ("kernels/tp_conv_spec.hpp", "kernels/common.hpp", "codegen.cpp", "specs.txt",
-                "tp_descriptor.cpp", "cg.cpp"):
+    for rel in (FWD_SOURCES if kind == "fwd" else BWD_SOURCES):
         with open(os.path.join(base, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def stored_traffic(layout):
-    """HBM bytes per launch from the committed counter summary, or None if
-    the summary is missing or was taken on a different kernel."""
-    path = os.path.join(ROOT, "profiles", f"tp_conv_large_graph_{layout}_hbm_counters.md")
+def stored_traffic(layout, kind="fwd"):
+    """HBM bytes per call from the committed counter summary, or None if
+    the summary is missing or was taken on different kernels."""
+    name = "tp_conv" if kind == "fwd" else "tp_conv_bwd"
+    path = os.path.join(ROOT, "profiles", f"{name}_large_graph_{layout}_hbm_counters.md")
     if not os.path.exists(path):
         return None
     text = open(path).read()
     mh = re.search(r"kernel_source_hash:\s*(\w+)", text)
     mb = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
-    if not mh or not mb or mh.group(1) != kernel_source_hash():
+    if not mh or not mb or mh.group(1) != kernel_source_hash(kind):
         return None
     return float(mb.group(1))
 
@@ -175,7 +182,13 @@ def main():
                                       "hbm_GBps_algorithmic": alg_bytes / (k2 * 1e-3) / 1e9,
                                       "hbm_fraction_of_peak": alg_bytes / (k2 * 1e-3) / 1e9 / HBM_PEAK_GBPS,
                                       "kernel": h2.kernel_name, "traffic": stored_traffic(other)}
-        del x, sh, w, src, dst, out
+    if not args.no_extras or args.with_backward:
+        del out
+        result["tp_conv_bwd"] = backward(torch, sp, workloads, h, x, sh, w, src, dst, N, E, args)
+
+    if not args.no_extras:
+        import gc
+        del x, sh, w, src, dst
         gc.collect()
         torch.cuda.empty_cache()
 
@@ -236,6 +249,32 @@ def main():
                                   "host_cpu": _cpu_model(), "host_nproc": os.cpu_count()}
 
     print(json.dumps(result), flush=True)
+
+
+def backward(torch, sp, workloads, h, x, sh, w, src, dst, N, E, args):
+    """Vector-Jacobian product on the same graph: both kernels per call.
+    Bytes: the operands and gradients once each (x, g and dx per node; w,
+    sh, dw, dsh and the three index arrays per edge) plus the per-edge
+    source messages written by the first kernel and read by the second."""
+    g = torch.from_numpy(workloads.output_gradient(N, h.dim_out, "f32", seed=74)).to(x.device)
+    perm = torch.argsort(src, stable=True).to(src.dtype)
+    gx, gsh, gw = torch.empty_like(x), torch.empty_like(sh), torch.empty_like(w)
+    ws = torch.empty(sp.tp_conv_bwd_workspace(h, E), dtype=torch.uint8, device=x.device)
+    fb = lambda: sp.tp_conv_bwd(h, x, sh, w, g, src, dst, perm, n_nodes=N, workspace=ws,
+                                grad_x=gx, grad_sh=gsh, grad_w=gw)
+    wall, per = time_launches(torch, fb, args.steps, args.warmup)
+    kms = sum(per) / len(per)
+    operands = (2 * E * h.weight_numel * 4 + 2 * E * h.dim_in2 * 4 + 3 * E * 4 +
+                2 * N * h.dim_in1 * 4 + N * h.dim_out * 4)
+    messages = 2 * E * h.dim_in1 * 4
+    gbps = (operands + messages) / (kms * 1e-3) / 1e9
+    r = {"edges_per_s": E / (wall / args.steps), "ms_per_call": kms,
+         "algorithmic_bytes": {"operands": operands, "messages": messages},
+         "hbm": {"achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": gbps / HBM_PEAK_GBPS,
+                 "traffic": stored_traffic(h.layout, "bwd")},
+         "kernels": ["tp_bwd_edge_kernel", "tp_bwd_src_kernel"]}
+    del g, perm, gx, gsh, gw, ws
+    return r
 
 
 def other_workloads(torch, sp, workloads, dev, args):

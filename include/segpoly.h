@@ -163,11 +163,14 @@ int tp_conv_fwd(tp_handle h, const void* x, int64_t n_src, const void* sh, const
                 void* out, void* stream);
 
 /*
- * tp_conv_bwd_workspace: device workspace tp_conv_bwd needs for n_edges
- * edges: n_edges * DIM_IN1 elements of the handle's dtype (one source
- * message per edge).  Batch mode needs none.
+ * tp_conv_bwd_workspace: bytes of device workspace tp_conv_bwd needs for
+ * n_edges edges, in indexed mode (batch == 0) or batch mode (batch != 0):
+ * one source message per edge (n_edges * DIM_IN1 elements of the handle's
+ * dtype, indexed mode only), rounded up to 256 bytes, plus, when the
+ * multiplicity exceeds 64, ceil(mul / 64) * n_edges * DIM_IN2 elements of
+ * per-tile harmonic-gradient partials.  0 means no workspace is needed.
  */
-int tp_conv_bwd_workspace(tp_handle h, int64_t n_edges, size_t* bytes);
+int tp_conv_bwd_workspace(tp_handle h, int64_t n_edges, int batch, size_t* bytes);
 
 /*
  * tp_conv_bwd: vector-Jacobian product of tp_conv_fwd, the gradients of
@@ -185,7 +188,8 @@ int tp_conv_bwd_workspace(tp_handle h, int64_t n_edges, size_t* bytes);
  *                edges).
  * Every element of grad_x, grad_sh and grad_w is overwritten.  Edges whose
  * source or destination lies outside its range get zero gradients and add
- * nothing to grad_x.
+ * nothing to grad_x (for an out-of-range source: given finite sh and
+ * grad_out, since its x and w enter as zeros).
  *   x, sh, w, src, dst, idx_dtype, n_src, n_edges, n_nodes: as tp_conv_fwd
  *              (per-edge weights only).
  *   src_perm   [n_edges] device, idx_dtype: the edge ids ordered by src
@@ -197,12 +201,13 @@ int tp_conv_bwd_workspace(tp_handle h, int64_t n_edges, size_t* bytes);
  *   grad_out   [n_nodes, DIM_OUT] device, layout of the handle.
  *   grad_x     [n_src, DIM_IN1] device.  grad_sh [n_edges, DIM_IN2] device.
  *   grad_w     [n_edges, WEIGHT_NUMEL] device.
- *   workspace  device, at least tp_conv_bwd_workspace() bytes, aligned like
- *              the operands; may be NULL in batch mode or with no edges.
- * Two launches on `stream` (one in batch mode), no atomics: results are
- * deterministic.  Fails closed with E_UNSUPPORTED for shared weights, for a
- * descriptor without a specialised kernel, and for a multiplicity above 64
- * that is odd, above 128, or whose operands are not aligned to two elements.
+ *   workspace  device, at least tp_conv_bwd_workspace() bytes, 256-byte
+ *              aligned; may be NULL when that size is 0.  Its contents on
+ *              entry do not matter.
+ * Two to three launches on `stream`, no atomics: results are deterministic
+ * (bitwise, for fixed inputs and src_perm).  Fails closed with
+ * E_UNSUPPORTED for shared weights and for a descriptor without a
+ * specialised kernel.  Sizes: n_nodes, n_src < 2^31.
  */
 int tp_conv_bwd(tp_handle h, const void* x, int64_t n_src, const void* sh, const void* w, const void* src,
                 const void* dst, const void* src_perm, int idx_dtype, int64_t n_edges, int64_t n_nodes,

@@ -73,7 +73,7 @@ def _load():
         "tp_path_cg": [vp, c_int, pd],
         "tp_kernel_name": [vp, ctypes.c_char_p, ctypes.c_size_t],
         "tp_conv_fwd": [vp, vp, i64, vp, vp, vp, vp, c_int, i64, i64, vp, vp],
-        "tp_conv_bwd_workspace": [vp, i64, ctypes.POINTER(ctypes.c_size_t)],
+        "tp_conv_bwd_workspace": [vp, i64, c_int, ctypes.POINTER(ctypes.c_size_t)],
         "tp_conv_bwd": [vp, vp, i64, vp, vp, vp, vp, vp, c_int, i64, i64, vp, vp, vp, vp, vp, ctypes.c_size_t, vp],
         "tp_destroy": [vp],
         "symcon_create": [ctypes.c_char_p, ctypes.c_char_p, c_int, c_int, c_int, c_int, c_uint, ctypes.POINTER(vp)],
@@ -240,18 +240,20 @@ def tp_conv_fwd(h, x, sh, w, src=None, dst=None, n_nodes=None, out=None):
     return out
 
 
-def tp_conv_bwd_workspace(h, n_edges):
-    """Bytes of device workspace ``tp_conv_bwd`` needs for ``n_edges`` edges."""
+def tp_conv_bwd_workspace(h, n_edges, batch=False):
+    """Bytes of device workspace ``tp_conv_bwd`` needs for ``n_edges`` edges
+    (indexed mode, or batch mode with ``batch``)."""
     v = ctypes.c_size_t()
-    _check(lib.tp_conv_bwd_workspace(h._h, n_edges, ctypes.byref(v)))
+    _check(lib.tp_conv_bwd_workspace(h._h, n_edges, 1 if batch else 0, ctypes.byref(v)))
     return v.value
 
 
-def tp_conv_bwd(h, x, sh, w, grad_out, src=None, dst=None, src_perm=None, n_nodes=None, workspace=None):
+def tp_conv_bwd(h, x, sh, w, grad_out, src=None, dst=None, src_perm=None, n_nodes=None, workspace=None,
+                grad_x=None, grad_sh=None, grad_w=None):
     """Gradients (grad_x, grad_sh, grad_w) of ``tp_conv_fwd`` for the output
     gradient ``grad_out`` [n_nodes, dim_out].  ``src_perm`` lists the edge ids
     ordered by src (a stable argsort of src), part of the graph like the
-    sorted dst.  The workspace is allocated if not given."""
+    sorted dst.  The workspace and the gradients are allocated if not given."""
     import torch
     t = _torch_dtype(h.dtype)
     for name, a in (("x", x), ("sh", sh), ("w", w), ("grad_out", grad_out)):
@@ -274,10 +276,13 @@ def tp_conv_bwd(h, x, sh, w, grad_out, src=None, dst=None, src_perm=None, n_node
         n_nodes = n_edges
     if grad_out.shape != (n_nodes, h.dim_out):
         raise ValueError("grad_out must be [n_nodes, dim_out]")
-    gx = torch.empty_like(x)
-    gsh = torch.empty_like(sh)
-    gw = torch.empty_like(w)
-    need = tp_conv_bwd_workspace(h, n_edges) if src is not None else 0
+    gx = torch.empty_like(x) if grad_x is None else grad_x
+    gsh = torch.empty_like(sh) if grad_sh is None else grad_sh
+    gw = torch.empty_like(w) if grad_w is None else grad_w
+    for name, a, ref in (("grad_x", gx, x), ("grad_sh", gsh, sh), ("grad_w", gw, w)):
+        if a.shape != ref.shape or a.dtype != t or not a.is_contiguous():
+            raise ValueError(f"{name} has the wrong shape or dtype")
+    need = tp_conv_bwd_workspace(h, n_edges, batch=src is None and n_edges > 0)
     if workspace is None and need:
         workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
     wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()

@@ -371,11 +371,20 @@ int tp_conv_fwd(tp_handle h, const void* x, int64_t n_src, const void* sh, const
   return ok();
 }
 
-int tp_conv_bwd_workspace(tp_handle h, int64_t n_edges, size_t* bytes) {
+// Messages [n_edges][DIM_IN1] (indexed mode), then 256-byte aligned the
+// harmonic-gradient partials [tiles][n_edges][DIM_IN2] when one wave of
+// single channels does not cover the multiplicity (tiles = ceil(mul / 64),
+// the most any launch uses).
+int tp_conv_bwd_workspace(tp_handle h, int64_t n_edges, int batch, size_t* bytes) {
   if (!h || !bytes) return fail(SEGPOLY_E_INVALID, "null argument");
   if (n_edges < 0) return fail(SEGPOLY_E_INVALID, "negative size");
   const size_t esz = h->dtype == SEGPOLY_F32 ? 4 : 8;
-  *bytes = static_cast<size_t>(n_edges) * static_cast<size_t>(h->d.dim1) * esz;
+  const size_t e = static_cast<size_t>(n_edges);
+  size_t msg = batch ? 0 : e * static_cast<size_t>(h->d.dim1) * esz;
+  msg = (msg + 255) / 256 * 256;
+  const int mul = h->d.uniform_mul ? h->d.mul : 0;
+  const size_t tiles = static_cast<size_t>((mul + 63) / 64);
+  *bytes = msg + (tiles > 1 ? tiles * e * static_cast<size_t>(h->d.dim2) * esz : 0);
   return ok();
 }
 
@@ -406,12 +415,10 @@ int tp_conv_bwd(tp_handle h, const void* x, int64_t n_src, const void* sh, const
       if (!x && n_src > 0) return fail(SEGPOLY_E_INVALID, "null x");
       if (!grad_out) return fail(SEGPOLY_E_INVALID, "null grad_out");
     }
-    if (!batch) {
-      size_t need = 0;
-      tp_conv_bwd_workspace(h, n_edges, &need);
-      if (!workspace || workspace_bytes < need)
-        return fail(SEGPOLY_E_INVALID, "workspace missing or smaller than tp_conv_bwd_workspace()");
-    }
+    size_t need = 0;
+    tp_conv_bwd_workspace(h, n_edges, batch ? 1 : 0, &need);
+    if (need && (!workspace || workspace_bytes < need))
+      return fail(SEGPOLY_E_INVALID, "workspace missing or smaller than tp_conv_bwd_workspace()");
   }
   if ((h->flags & SEGPOLY_VALIDATE) && !batch) {
     int st = idx_dtype == SEGPOLY_I32 ? check_indices<int32_t>(src, dst, n_edges, n_src, n_nodes, stream)
@@ -444,10 +451,6 @@ int tp_conv_bwd(tp_handle h, const void* x, int64_t n_src, const void* sh, const
   a.layout = h->layout;
   a.stream = stream;
   const int rc = h->spec->launch_bwd(a);
-  if (rc == -2)
-    return fail(SEGPOLY_E_UNSUPPORTED,
-                "backward covers up to 64 channels, or up to 128 in pairs (even multiplicity, operands aligned "
-                "to two elements)");
   if (rc != 0)
     return fail(SEGPOLY_E_HIP, std::string("kernel launch failed: ") + hipGetErrorString(static_cast<hipError_t>(rc)));
   return ok();

@@ -196,9 +196,16 @@ def test_backward_argument_errors_fail_before_any_gpu_call():
     h = sp.tp_create("32x0e+32x1o", "0e+1o", "0e+1o")
     assert h.specialized
     n = ctypes.c_size_t()
-    assert sp.lib.tp_conv_bwd_workspace(h._h, 10, ctypes.byref(n)) == sp.OK
-    assert n.value == 10 * h.dim_in1 * 4
-    assert sp.lib.tp_conv_bwd_workspace(h._h, -1, ctypes.byref(n)) == sp.E_INVALID
+    assert sp.lib.tp_conv_bwd_workspace(h._h, 10, 0, ctypes.byref(n)) == sp.OK
+    assert n.value == (10 * h.dim_in1 * 4 + 255) // 256 * 256
+    assert sp.lib.tp_conv_bwd_workspace(h._h, 10, 1, ctypes.byref(n)) == sp.OK and n.value == 0
+    assert sp.lib.tp_conv_bwd_workspace(h._h, -1, 0, ctypes.byref(n)) == sp.E_INVALID
+    # multiplicity 200: four tiles of harmonic-gradient partials
+    h2 = sp.tp_create("200x0e+200x1o", "0e+1o", "0e+1o")
+    assert sp.lib.tp_conv_bwd_workspace(h2._h, 7, 1, ctypes.byref(n)) == sp.OK
+    assert n.value == 4 * 7 * h2.dim_in2 * 4
+    assert sp.lib.tp_conv_bwd_workspace(h2._h, 7, 0, ctypes.byref(n)) == sp.OK
+    assert n.value == (7 * h2.dim_in1 * 4 + 255) // 256 * 256 + 4 * 7 * h2.dim_in2 * 4
     f = sp.lib.tp_conv_bwd
     p = ctypes.c_void_p(16)   # never dereferenced: every call below fails validation
     big = 1 << 40

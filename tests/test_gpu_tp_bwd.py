@@ -93,10 +93,13 @@ def test_full_size_workload4_sampled(layout):
         assert np.all(np.isfinite(a))
 
 
-@pytest.mark.parametrize("mul,layout", [(40, "mul_ir"), (64, "ir_mul"), (80, "ir_mul"), (128, "mul_ir")])
+@pytest.mark.parametrize("mul,layout", [(40, "mul_ir"), (64, "ir_mul"), (80, "ir_mul"), (128, "mul_ir"),
+                                        (200, "ir_mul"), (77, "mul_ir")])
 def test_ragged_graph_and_partial_tiles(mul, layout):
     """In-degrees 0..6 with isolated destinations, sources that no edge
-    reads, partial channel tiles; int64 indices for one case."""
+    reads, partial channel tiles, several tiles (200 channels: two tiles of
+    pairs; 77, odd: two tiles of single channels) with the harmonic
+    gradient folded from per-tile partials; int64 indices for one case."""
     sp = _sp()
     import torch
     in1 = f"{mul}x0e+{mul}x1o+{mul}x2e"
@@ -207,18 +210,3 @@ def test_deterministic_and_layouts_agree():
     assert np.array_equal(c[1], a[1])
 
 
-def test_unsupported_multiplicity_fails_closed():
-    sp = _sp()
-    import torch
-    in1 = "200x0e+200x1o+200x2e"
-    h = sp.tp_create(in1, "0e+1o+2e+3o", "0e+1o+2e")
-    assert h.specialized
-    x = torch.randn(3, h.dim_in1, device="cuda")
-    s = torch.randn(2, h.dim_in2, device="cuda")
-    w = torch.randn(2, h.weight_numel, device="cuda")
-    g = torch.randn(3, h.dim_out, device="cuda")
-    i = torch.tensor([0, 1], dtype=torch.int32, device="cuda")
-    announce("tp bwd unsupported multiplicity")
-    with pytest.raises(sp.SegpolyError) as e:
-        sp.tp_conv_bwd(h, x, s, w, g, i, i, i, n_nodes=3)
-    assert e.value.code == sp.E_UNSUPPORTED
