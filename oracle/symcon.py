@@ -175,3 +175,56 @@ class SymmetricContraction:
             ws = wa[:, s_idx * self.mul:(s_idx + 1) * self.mul]
             parts[ob] += p * ws[:, None, :]
         return join_blocks(parts, layout)
+
+    def eval_vjp(self, x, species, w, g, layout="ir_mul", absolute=False):
+        """Vector-Jacobian product of :meth:`eval`: given g = dL/d(out)
+        [n_atoms, dim_out] in ``layout``, return (dL/dx [n_atoms, dim_in] in
+        ``layout``, dL/dw [num_elements, weight_numel]), num_elements =
+        w.shape[0].
+
+        From the definition, with p_k[a, M, u] = sum U^k[m1..mnu, M] prod_i
+        v[a, m_i, u] (U^k the coupling of weight segment k):
+            dw[s, k, u]  = sum over atoms a of species s of sum_M g[a, M, u] p_k[a, M, u]
+            dv[a, m, u] += w[s_a, k, u] sum_M g[a, M, u] dp_k[a, M, u] / dv[a, m, u],
+        the derivative of the degree-nu product by the product rule: one
+        term per input slot, that slot left free and the others contracted
+        with v (no use is made of the basis being symmetric).  Species
+        outside [0, num_elements) select no weights: zero dx, nothing
+        added to dw.  ``absolute`` evaluates the same sums over |x|, |w|,
+        |g| and |U|."""
+        x = np.asarray(x, dtype=np.float64)
+        w = np.asarray(w, dtype=np.float64)
+        g = np.asarray(g, dtype=np.float64)
+        species = np.asarray(species, dtype=np.int64)
+        if absolute:
+            x, w, g = np.abs(x), np.abs(w), np.abs(g)
+        n_el = w.shape[0]
+        valid = (species >= 0) & (species < n_el)
+        sp = np.where(valid, species, 0)
+        v = np.concatenate(split_blocks(x, self.inp, layout), axis=1)   # [A, n, mul]
+        gb = split_blocks(g, self.out, layout)                           # per output block [A, 2L+1, mul]
+        wa = w[sp] * valid[:, None]                                      # [A, numel], zero rows if invalid
+        dv = np.zeros_like(v)
+        dw = np.zeros_like(w)
+        slot_specs = {1: ["mM,aMu->amu"],
+                      2: ["mnM,anu,aMu->amu", "nmM,anu,aMu->amu"],
+                      3: ["mnoM,anu,aou,aMu->amu", "nmoM,anu,aou,aMu->amu", "nomM,anu,aou,aMu->amu"]}
+        for s_idx, (nu, ob, k) in enumerate(self.segments):
+            u = self.basis[(nu, ob)][k]
+            if absolute:
+                u = np.abs(u)
+            if nu == 1:
+                p = np.einsum("mM,amu->aMu", u, v)
+            elif nu == 2:
+                p = np.einsum("mnM,amu,anu->aMu", u, v, v, optimize=True)
+            else:
+                p = np.einsum("mnoM,amu,anu,aou->aMu", u, v, v, v, optimize=True)
+            cols = slice(s_idx * self.mul, (s_idx + 1) * self.mul)
+            contrib = np.einsum("aMu,aMu->au", gb[ob], p) * valid[:, None]
+            np.add.at(dw[:, cols], sp, contrib)
+            gw = gb[ob] * wa[:, None, cols]                              # [A, 2L+1, mul]
+            for spec in slot_specs[nu]:
+                dv += np.einsum(spec, u, *([v] * (nu - 1)), gw, optimize=True)
+        dims = [2 * l + 1 for _, l, _ in self.inp]
+        parts = np.split(dv, np.cumsum(dims)[:-1], axis=1)
+        return join_blocks(parts, layout), dw
