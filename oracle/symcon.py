@@ -151,30 +151,91 @@ class SymmetricContraction:
         return np.concatenate([np.full(self.mul, k[(nu, ob)]) for nu, ob, _ in self.segments]) \
             if self.segments else np.zeros(0)
 
-    def eval(self, x, species, w, layout="ir_mul", absolute=False):
-        """x [n_atoms, dim_in] in ``layout``; species [n_atoms] integers;
-        w [num_elements, weight_numel].  Returns float64 [n_atoms, dim_out]."""
+    def _entries(self, nu, ob, k, absolute):
+        """Non-zero entries of a coupling tensor: (slot component indices
+        [nu][nnz], output component M [nnz], value c [nnz])."""
+        u = self.basis[(nu, ob)][k]
+        if absolute:
+            u = np.abs(u)
+        nz = np.nonzero(u)
+        return [nz[i] for i in range(nu)], nz[nu], u[nz]
+
+    def _per_atom(self, x, species, w, layout, absolute, g=None, chunk=128):
+        """Forward (g None) or forward plus vector-Jacobian product, as the
+        sum over the non-zero entries (m1..mnu, M, c) of every coupling
+        tensor.  Every (atom, channel) pair is one row b of a batch (atoms
+        in chunks); gathering the entries' components and scattering to
+        output (or input) components are products with 0/1 matrices."""
         x = np.asarray(x, dtype=np.float64)
         w = np.asarray(w, dtype=np.float64)
         species = np.asarray(species, dtype=np.int64)
         if absolute:
             x, w = np.abs(x), np.abs(w)
-        v = np.concatenate(split_blocks(x, self.inp, layout), axis=1)   # [A, n, mul]
-        wa = w[species]                                                  # [A, numel]
-        parts = [np.zeros((x.shape[0], 2 * L + 1, self.mul)) for _, L, _ in self.out]
-        for s_idx, (nu, ob, k) in enumerate(self.segments):
-            u = self.basis[(nu, ob)][k]
+        n_el, mul, A = w.shape[0], self.mul, x.shape[0]
+        valid = (species >= 0) & (species < n_el)
+        sp = np.where(valid, species, 0)
+        # [A, n, mul] -> rows b = (atom, channel): [A * mul, n]
+        v_all = np.concatenate(split_blocks(x, self.inp, layout), axis=1).transpose(0, 2, 1).reshape(A * mul, -1)
+        out = [np.zeros((A * mul, 2 * L + 1)) for _, L, _ in self.out]
+        if g is not None:
+            g = np.asarray(g, dtype=np.float64)
             if absolute:
-                u = np.abs(u)
-            if nu == 1:
-                p = np.einsum("mM,amu->aMu", u, v)
-            elif nu == 2:
-                p = np.einsum("mnM,amu,anu->aMu", u, v, v, optimize=True)
-            else:
-                p = np.einsum("mnoM,amu,anu,aou->aMu", u, v, v, v, optimize=True)
-            ws = wa[:, s_idx * self.mul:(s_idx + 1) * self.mul]
-            parts[ob] += p * ws[:, None, :]
-        return join_blocks(parts, layout)
+                g = np.abs(g)
+            g_all = [b.transpose(0, 2, 1).reshape(A * mul, -1) for b in split_blocks(g, self.out, layout)]
+            dv_all = np.zeros_like(v_all)
+            dw = np.zeros_like(w)
+        n = v_all.shape[1]
+        entries = []
+        for nu, ob, k in self.segments:
+            slots, M, c = self._entries(nu, ob, k, absolute)
+            to_M = np.zeros((len(c), out[ob].shape[1]))
+            to_M[np.arange(len(c)), M] = 1.0
+            to_m = []
+            for i in range(nu):
+                t = np.zeros((len(c), n))
+                t[np.arange(len(c)), slots[i]] = 1.0
+                to_m.append(t)
+            entries.append((slots, M, c, to_M, to_m))
+        for a0 in range(0, A, chunk):
+            a1 = min(A, a0 + chunk)
+            rows = slice(a0 * mul, a1 * mul)
+            v = v_all[rows]
+            # per row: the weights of its atom's species and channel
+            wa = (w[sp[a0:a1]] * valid[a0:a1, None]).reshape(a1 - a0, -1, mul)   # [a, seg, mul]
+            for s_idx, ((nu, ob, _), (slots, M, c, to_M, to_m)) in enumerate(zip(self.segments, entries)):
+                ws = wa[:, s_idx, :].reshape(-1)                                  # [b]
+                factors = [v[:, m] for m in slots]                               # each [b, nnz]
+                prod = c[None, :] * factors[0]
+                for f in factors[1:]:
+                    prod = prod * f
+                p = prod @ to_M                                                  # [b, 2L+1]
+                out[ob][rows] += p * ws[:, None]
+                if g is None:
+                    continue
+                gb = g_all[ob][rows]
+                contrib = np.sum(gb * p, axis=1).reshape(a1 - a0, mul) * valid[a0:a1, None]
+                np.add.at(dw[:, s_idx * mul:(s_idx + 1) * mul], sp[a0:a1], contrib)
+                gw = (gb * ws[:, None])[:, M] * c[None, :]                         # [b, nnz]
+                for i in range(nu):                                              # product rule, slot i free
+                    rest = gw
+                    for j in range(nu):
+                        if j != i:
+                            rest = rest * factors[j]
+                    dv_all[rows] += rest @ to_m[i]
+        back = lambda t, irreps: join_blocks(
+            [b.reshape(A, mul, -1).transpose(0, 2, 1)
+             for b in np.split(t, np.cumsum([2 * l + 1 for _, l, _ in irreps])[:-1], axis=1)], layout)
+        res = join_blocks([o.reshape(A, mul, -1).transpose(0, 2, 1) for o in out], layout)
+        if g is None:
+            return res
+        return back(dv_all, self.inp), dw
+
+    def eval(self, x, species, w, layout="ir_mul", absolute=False):
+        """x [n_atoms, dim_in] in ``layout``; species [n_atoms] integers;
+        w [num_elements, weight_numel].  Returns float64 [n_atoms, dim_out].
+        An atom whose species is outside [0, num_elements) gets a zero row.
+        ``absolute`` evaluates the same sums over |x|, |w| and |U|."""
+        return self._per_atom(x, species, w, layout, absolute)
 
     def eval_vjp(self, x, species, w, g, layout="ir_mul", absolute=False):
         """Vector-Jacobian product of :meth:`eval`: given g = dL/d(out)
@@ -192,39 +253,4 @@ class SymmetricContraction:
         outside [0, num_elements) select no weights: zero dx, nothing
         added to dw.  ``absolute`` evaluates the same sums over |x|, |w|,
         |g| and |U|."""
-        x = np.asarray(x, dtype=np.float64)
-        w = np.asarray(w, dtype=np.float64)
-        g = np.asarray(g, dtype=np.float64)
-        species = np.asarray(species, dtype=np.int64)
-        if absolute:
-            x, w, g = np.abs(x), np.abs(w), np.abs(g)
-        n_el = w.shape[0]
-        valid = (species >= 0) & (species < n_el)
-        sp = np.where(valid, species, 0)
-        v = np.concatenate(split_blocks(x, self.inp, layout), axis=1)   # [A, n, mul]
-        gb = split_blocks(g, self.out, layout)                           # per output block [A, 2L+1, mul]
-        wa = w[sp] * valid[:, None]                                      # [A, numel], zero rows if invalid
-        dv = np.zeros_like(v)
-        dw = np.zeros_like(w)
-        slot_specs = {1: ["mM,aMu->amu"],
-                      2: ["mnM,anu,aMu->amu", "nmM,anu,aMu->amu"],
-                      3: ["mnoM,anu,aou,aMu->amu", "nmoM,anu,aou,aMu->amu", "nomM,anu,aou,aMu->amu"]}
-        for s_idx, (nu, ob, k) in enumerate(self.segments):
-            u = self.basis[(nu, ob)][k]
-            if absolute:
-                u = np.abs(u)
-            if nu == 1:
-                p = np.einsum("mM,amu->aMu", u, v)
-            elif nu == 2:
-                p = np.einsum("mnM,amu,anu->aMu", u, v, v, optimize=True)
-            else:
-                p = np.einsum("mnoM,amu,anu,aou->aMu", u, v, v, v, optimize=True)
-            cols = slice(s_idx * self.mul, (s_idx + 1) * self.mul)
-            contrib = np.einsum("aMu,aMu->au", gb[ob], p) * valid[:, None]
-            np.add.at(dw[:, cols], sp, contrib)
-            gw = gb[ob] * wa[:, None, cols]                              # [A, 2L+1, mul]
-            for spec in slot_specs[nu]:
-                dv += np.einsum(spec, u, *([v] * (nu - 1)), gw, optimize=True)
-        dims = [2 * l + 1 for _, l, _ in self.inp]
-        parts = np.split(dv, np.cumsum(dims)[:-1], axis=1)
-        return join_blocks(parts, layout), dw
+        return self._per_atom(x, species, w, layout, absolute, g=g)
