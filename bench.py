@@ -50,14 +50,21 @@ FWD_SOURCES = ("kernels/tp_conv_spec.hpp", "kernels/common.hpp", "codegen.cpp", 
 BWD_SOURCES = FWD_SOURCES + ("kernels/tp_conv_bwd.hpp",)
 
 
+CODEGEN_SYMCON_MARK = b"// ---------------------------------------------------------------- symcon"
+
+
 def kernel_source_hash(kind="fwd"):
-    """Hash of everything the timed kernels are generated from, to tell
-    whether stored hardware counters still describe them."""
+    """Hash of everything the timed TP-conv kernels are generated from (of
+    the generator, the part before its symmetric-contraction section), to
+    tell whether stored hardware counters still describe them."""
     h = hashlib.sha256()
     base = os.path.join(ROOT, "segmented_polynomials_amd", "csrc")
     for rel in (FWD_SOURCES if kind == "fwd" else BWD_SOURCES):
         with open(os.path.join(base, rel), "rb") as f:
-            h.update(f.read())
+            data = f.read()
+        if rel == "codegen.cpp":
+            data = data.split(CODEGEN_SYMCON_MARK)[0]
+        h.update(data)
     return h.hexdigest()[:16]
 
 
@@ -111,7 +118,9 @@ def main():
     torch.cuda.set_device(dev)
     wl = workloads.WORKLOADS[4]
     layout = args.layout
+    t_create = time.perf_counter()
     h = sp.tp_create(wl.irreps_in1, wl.irreps_in2, wl.irreps_out, layout=layout)
+    create_ms = (time.perf_counter() - t_create) * 1e3
     fan_in = workloads.fan_in_from_irreps_out(h.irreps_out)
     inp = workloads.tp_inputs(wl, fan_in)
     N, E = inp["n_nodes"], inp["sh"].shape[0]
@@ -119,11 +128,11 @@ def main():
     x, sh, w = to(inp["x"]), to(inp["sh"]), to(inp["w"])
     src, dst = to(inp["src"]), to(inp["dst"])
     out = torch.empty((N, h.dim_out), dtype=torch.float32, device=dev)
-    # keep only what the host-side baseline needs
-    sample_nodes = 1000
-    base_inp = dict(x=inp["x"], sh=inp["sh"][:sample_nodes * wl.degree], w=inp["w"][:sample_nodes * wl.degree],
-                    src=inp["src"][:sample_nodes * wl.degree], dst=inp["dst"][:sample_nodes * wl.degree],
-                    n_nodes=sample_nodes)
+    # keep only what the host-side baselines need (first destination nodes)
+    sample_nodes, par_nodes = 1000, 4000
+    par_e = par_nodes * wl.degree
+    base_inp = dict(x=inp["x"], sh=inp["sh"][:par_e].copy(), w=inp["w"][:par_e].copy(),
+                    src=inp["src"][:par_e].copy(), dst=inp["dst"][:par_e].copy(), n_nodes=par_nodes)
     del inp
 
     fwd = lambda: sp.tp_conv_fwd(h, x, sh, w, src, dst, n_nodes=N, out=out)
@@ -162,6 +171,7 @@ def main():
         "hbm_GBps_algorithmic": achieved_gbps,
         "hbm_fraction_of_peak": achieved_gbps / HBM_PEAK_GBPS,
         "kernel_ms": {"mean": avg_kernel_ms, "min": per[0], "median": per[len(per) // 2]},
+        "create_ms": create_ms,
         "roofline": {"bound": "hbm", "achieved": achieved_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved_gbps / HBM_PEAK_GBPS,
                      "traffic": traffic,
@@ -182,6 +192,17 @@ def main():
                                       "hbm_GBps_algorithmic": alg_bytes / (k2 * 1e-3) / 1e9,
                                       "hbm_fraction_of_peak": alg_bytes / (k2 * 1e-3) / 1e9 / HBM_PEAK_GBPS,
                                       "kernel": h2.kernel_name, "traffic": stored_traffic(other)}
+    if not args.no_extras:
+        # practical ceiling: a plain device copy of the weight tensor (4 GB read + 4 GB written)
+        wc = torch.empty_like(w)
+        cwall, cper = time_launches(torch, lambda: wc.copy_(w), max(5, args.steps // 4), 2)
+        cms = sum(cper) / len(cper)
+        copy_gbps = 2 * w.numel() * 4 / (cms * 1e-3) / 1e9
+        result["copy_ceiling"] = {"what": "device copy of the 3.99 GB weight tensor", "ms": cms,
+                                  "GBps": copy_gbps, "frac_of_peak": copy_gbps / HBM_PEAK_GBPS}
+        result["roofline"]["frac_of_copy"] = achieved_gbps / copy_gbps
+        del wc
+
     if not args.no_extras or args.with_backward:
         del out
         result["tp_conv_bwd"] = backward(torch, sp, workloads, h, x, sh, w, src, dst, N, E, args)
@@ -219,7 +240,21 @@ def main():
             "alu": {"achieved": s_flops / (k3 * 1e-3) / 1e12, "peak": FP32_VALU_PEAK_TFLOPS, "unit": "TFLOP/s",
                     "frac": s_flops / (k3 * 1e-3) / 1e12 / FP32_VALU_PEAK_TFLOPS, "algorithmic_flops": s_flops},
         }
-        del sx, ssp, sw, sout
+        # backward of the symmetric contraction on the same atoms
+        sg = torch.from_numpy(workloads.output_gradient(s5.n_atoms, hs.dim_out, "f32", seed=59)).to(dev)
+        sperm = torch.argsort(ssp, stable=True).to(ssp.dtype)
+        sgx, sgw = torch.empty_like(sx), torch.empty_like(sw)
+        sws = torch.empty(sp.symcon_bwd_workspace(hs, s5.n_atoms), dtype=torch.uint8, device=dev)
+        fb = lambda: sp.symcon_bwd(hs, sx, ssp, sw, sg, sperm, workspace=sws, grad_x=sgx, grad_w=sgw)
+        wall4, per4 = time_launches(torch, fb, args.steps, args.warmup)
+        k4 = sum(per4) / len(per4)
+        b_bytes = 2 * A * hs.dim_in * 4 + A * hs.dim_out * 4 + 2 * A * 4 + 2 * s5.num_elements * hs.weight_numel * 4
+        result["symcon_bwd"] = {
+            "atoms_per_s": A / (wall4 / args.steps), "ms_per_call": k4,
+            "kernels": ["symcon_table_kernel", "symcon_bwd_kernel", "symcon_fold_kernel"],
+            "hbm": {"achieved": b_bytes / (k4 * 1e-3) / 1e9, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                    "frac": b_bytes / (k4 * 1e-3) / 1e9 / HBM_PEAK_GBPS, "algorithmic_bytes": b_bytes}}
+        del sx, ssp, sw, sout, sg, sperm, sgx, sgw, sws
 
     if not args.no_extras:
         result["other_workloads"] = other_workloads(torch, sp, workloads, dev, args)
@@ -237,18 +272,76 @@ def main():
 
         from oracle import tp as otp
         o = otp.ChannelwiseTP(wl.irreps_in1, wl.irreps_in2, wl.irreps_out)
+        n_e = sample_nodes * wl.degree
         with threadpool_limits(1):
             t0 = time.perf_counter()
-            o.conv(base_inp["x"], base_inp["sh"], base_inp["w"], base_inp["src"], base_inp["dst"],
-                   base_inp["n_nodes"], layout=layout)
+            o.conv(base_inp["x"], base_inp["sh"][:n_e], base_inp["w"][:n_e], base_inp["src"][:n_e],
+                   base_inp["dst"][:n_e], sample_nodes, layout=layout)
             dt = time.perf_counter() - t0
-        n_e = base_inp["sh"].shape[0]
         result["cpu_baseline"] = {"value": n_e / dt, "unit": "edges/s", "cores": 1, "kind": "oracle",
                                   "sample": f"first {sample_nodes} destination nodes of the same graph "
                                             f"({n_e} edges, all 13 paths), float64 NumPy, {dt:.1f} s",
                                   "host_cpu": _cpu_model(), "host_nproc": os.cpu_count()}
+        result["cpu_baseline_parallel"] = parallel_oracle(wl, base_inp, layout)
 
     print(json.dumps(result), flush=True)
+
+
+def _oracle_warm(_):
+    """Start-up of a parallel-oracle worker: the imports, then a short wait
+    so that every worker takes one of these tasks."""
+    import threadpoolctl  # noqa: F401
+
+    import oracle.tp  # noqa: F401
+    time.sleep(0.5)
+    return os.getpid()
+
+
+def _oracle_chunk(a):
+    """One worker of the parallel oracle run: the destinations [n0, n1)."""
+    from threadpoolctl import threadpool_limits
+
+    from oracle import tp as otp
+    irreps, x, sh, w, src, dst, n0, n1, layout = a
+    o = otp.ChannelwiseTP(*irreps)
+    with threadpool_limits(1):
+        t0 = time.perf_counter()
+        o.conv(x, sh, w, src, dst - n0, n1 - n0, layout=layout)
+        return time.perf_counter() - t0
+
+
+def parallel_oracle(wl, inp, layout):
+    """The oracle as it stands, split by destination range over the host
+    cores (at most 16 worker processes); wall time from handing out the
+    chunks to the last result (worker start-up excluded)."""
+    import concurrent.futures as cf
+    import multiprocessing as mp
+
+    import numpy as np
+    workers = max(1, min(16, os.cpu_count() or 1))
+    n, deg = inp["n_nodes"], wl.degree
+    bounds = np.linspace(0, n, workers + 1).astype(int)
+    chunks = []
+    for a, b in zip(bounds[:-1], bounds[1:]):
+        e0, e1 = a * deg, b * deg
+        # each worker receives only the source rows its edges read (renumbered)
+        rows, src_local = np.unique(inp["src"][e0:e1], return_inverse=True)
+        chunks.append(((wl.irreps_in1, wl.irreps_in2, wl.irreps_out), inp["x"][rows], inp["sh"][e0:e1],
+                       inp["w"][e0:e1], src_local, inp["dst"][e0:e1], int(a), int(b), layout))
+    ex = cf.ProcessPoolExecutor(max_workers=workers, mp_context=mp.get_context("spawn"))
+    try:
+        list(ex.map(_oracle_warm, range(workers), timeout=120))   # start the workers
+        t0 = time.perf_counter()
+        list(ex.map(_oracle_chunk, chunks, timeout=300))
+        wall = time.perf_counter() - t0
+    except Exception as err:   # a worker that cannot start must not cost the bench line
+        ex.shutdown(wait=False, cancel_futures=True)
+        return {"error": f"{type(err).__name__}: {err}"}
+    ex.shutdown()
+    e = n * deg
+    return {"value": e / wall, "unit": "edges/s", "cores": workers, "kind": "oracle",
+            "sample": f"first {n} destination nodes of the same graph ({e} edges) split by destination range "
+                      f"over {workers} processes of one thread each, {wall:.1f} s"}
 
 
 def backward(torch, sp, workloads, h, x, sh, w, src, dst, N, E, args):

@@ -262,6 +262,44 @@ int symcon_coupling_dense(symcon_handle h, int c, double* out);
 int symcon_fwd(symcon_handle h, const void* x, const void* species, int idx_dtype, const void* w,
                int64_t n_atoms, void* out, void* stream);
 
+/*
+ * symcon_bwd_workspace: bytes of device workspace symcon_bwd needs for
+ * n_atoms atoms: a segment table of 2 * (num_elements + 3) int64 values
+ * (rounded up to 256 bytes), then per-chunk weight-gradient partials of
+ * (ceil(n_atoms / 16) + num_elements + 2) * WEIGHT_NUMEL elements of the
+ * handle's dtype.
+ */
+int symcon_bwd_workspace(symcon_handle h, int64_t n_atoms, size_t* bytes);
+
+/*
+ * symcon_bwd: vector-Jacobian product of symcon_fwd (the pages check the
+ * gradients of every input: "cuequivariance-torch" skill document, "CPU
+ * tensor product and backward"; the polynomial of e3nn-course Lesson 12a,
+ * section 21.4.1).  With g = dL/d(out):
+ *   grad_x[a] = per channel, the derivative of the degree-1..3 polynomial
+ *               of x[a] (product rule) contracted with w[species[a]] and g[a];
+ *   grad_w[e] = sum over the atoms a of element e of g[a] contracted with
+ *               the polynomial of x[a] (zero for an element without atoms).
+ *   x, species, idx_dtype, w, n_atoms: as symcon_fwd.
+ *   species_perm [n_atoms] device, idx_dtype: the atom ids ordered by
+ *               element ascending (a stable argsort of species); the order
+ *               within an element is the order in which grad_w sums them, so
+ *               a fixed perm gives bitwise-reproducible grad_w.  Atoms whose
+ *               element is out of range get grad_x = 0 and add nothing.
+ *               A permutation sorted by element is a precondition, checked
+ *               only with VALIDATE (E_RANGE / E_UNSORTED).
+ *   grad_out    [n_atoms, DIM_OUT] device, layout of the handle.
+ *   grad_x      [n_atoms, DIM_IN] device, fully overwritten.
+ *   grad_w      [num_elements, WEIGHT_NUMEL] device, fully overwritten.
+ *   workspace   device, at least symcon_bwd_workspace() bytes, 256-byte
+ *               aligned; its contents on entry do not matter.
+ * Three launches on `stream`, no atomics.  Fails closed with E_UNSUPPORTED
+ * for a descriptor without a specialised kernel.  Sizes: n_atoms < 2^31.
+ */
+int symcon_bwd(symcon_handle h, const void* x, const void* species, const void* species_perm, int idx_dtype,
+               const void* w, const void* grad_out, int64_t n_atoms, void* grad_x, void* grad_w, void* workspace,
+               size_t workspace_bytes, void* stream);
+
 int symcon_destroy(symcon_handle h);
 
 /* ------------------------------------------------------------------ misc */

@@ -1,7 +1,8 @@
 """Python binding of ``libsegpoly.so`` (argument marshalling only).
 
 The functions keep the names of the C ABI in ``include/segpoly.h``:
-``tp_create`` / ``tp_conv_fwd`` / ``tp_conv_bwd`` / ``symcon_create`` / ``symcon_fwd``.  Every
+``tp_create`` / ``tp_conv_fwd`` / ``tp_conv_bwd`` / ``symcon_create`` / ``symcon_fwd`` /
+``symcon_bwd``.  Every
 step of the computation runs in the library's HIP kernels; PyTorch only
 supplies device memory and the current stream.  There is no CPU fallback:
 importing this package fails loudly if the library has not been built.
@@ -30,7 +31,7 @@ _DTYPES = {"f32": F32, "f64": F64}
 # every symbol include/segpoly.h declares
 EXPORTS = ("tp_create", "tp_query", "tp_irreps_out", "tp_path_info", "tp_path_cg", "tp_kernel_name",
            "tp_conv_fwd", "tp_conv_bwd_workspace", "tp_conv_bwd", "tp_destroy", "symcon_create", "symcon_query", "symcon_coupling_info",
-           "symcon_coupling_dense", "symcon_fwd", "symcon_destroy", "segpoly_real_cg",
+           "symcon_coupling_dense", "symcon_fwd", "symcon_bwd_workspace", "symcon_bwd", "symcon_destroy", "segpoly_real_cg",
            "segpoly_last_error", "segpoly_version")
 
 
@@ -81,6 +82,8 @@ def _load():
         "symcon_coupling_info": [vp, c_int, p64],
         "symcon_coupling_dense": [vp, c_int, pd],
         "symcon_fwd": [vp, vp, vp, c_int, vp, i64, vp, vp],
+        "symcon_bwd_workspace": [vp, i64, ctypes.POINTER(ctypes.c_size_t)],
+        "symcon_bwd": [vp, vp, vp, vp, c_int, vp, vp, i64, vp, vp, vp, ctypes.c_size_t, vp],
         "symcon_destroy": [vp],
         "segpoly_real_cg": [c_int, c_int, c_int, pd],
     }
@@ -362,3 +365,38 @@ def symcon_fwd(h, x, species, w, out=None):
         raise ValueError("out has the wrong shape or dtype")
     _check(lib.symcon_fwd(h._h, _ptr(x), _ptr(species), idx, _ptr(w), n, _ptr(out), _stream_ptr(x.device)))
     return out
+
+
+def symcon_bwd_workspace(h, n_atoms):
+    """Bytes of device workspace ``symcon_bwd`` needs for ``n_atoms`` atoms."""
+    v = ctypes.c_size_t()
+    _check(lib.symcon_bwd_workspace(h._h, n_atoms, ctypes.byref(v)))
+    return v.value
+
+
+def symcon_bwd(h, x, species, w, grad_out, species_perm, workspace=None, grad_x=None, grad_w=None):
+    """Gradients (grad_x, grad_w) of ``symcon_fwd`` for ``grad_out``
+    [n_atoms, dim_out].  ``species_perm`` lists the atom ids ordered by
+    element (a stable argsort of species).  The workspace and the gradients
+    are allocated if not given."""
+    import torch
+    t = _torch_dtype(h.dtype)
+    for name, a in (("x", x), ("w", w), ("grad_out", grad_out)):
+        if a.dtype != t or not a.is_cuda or not a.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous {t} device tensor")
+    n = x.shape[0]
+    if x.shape[1] != h.dim_in or grad_out.shape != (n, h.dim_out) or w.shape != (h.num_elements, h.weight_numel):
+        raise ValueError("operand shapes do not match the descriptor")
+    for name, a in (("species", species), ("species_perm", species_perm)):
+        if a.shape != (n,) or a.dtype != species.dtype or not a.is_cuda or not a.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous [n_atoms] device tensor of one integer dtype")
+    gx = torch.empty_like(x) if grad_x is None else grad_x
+    gw = torch.empty_like(w) if grad_w is None else grad_w
+    if gx.shape != x.shape or gw.shape != w.shape or gx.dtype != t or gw.dtype != t:
+        raise ValueError("gradient buffers have the wrong shape or dtype")
+    if workspace is None:
+        workspace = torch.empty(symcon_bwd_workspace(h, n), dtype=torch.uint8, device=x.device)
+    wbytes = workspace.numel() * workspace.element_size()
+    _check(lib.symcon_bwd(h._h, _ptr(x), _ptr(species), _ptr(species_perm), _index_dtype(species), _ptr(w),
+                          _ptr(grad_out), n, _ptr(gx), _ptr(gw), _ptr(workspace), wbytes, _stream_ptr(x.device)))
+    return gx, gw

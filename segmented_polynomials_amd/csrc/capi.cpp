@@ -128,6 +128,27 @@ int check_perm(const void* dsrc, const void* dperm, int64_t n_edges, void* strea
   return ok();
 }
 
+// VALIDATE for the symmetric-contraction backward: perm is a permutation
+// of the atoms with species[perm[.]] ascending.
+template <typename Index>
+int check_species_perm(const void* dsp, const void* dperm, int64_t n, void* stream) {
+  std::vector<Index> s(n), p(n);
+  hipError_t e = hipStreamSynchronize(static_cast<hipStream_t>(stream));
+  if (e == hipSuccess && n) e = hipMemcpy(s.data(), dsp, n * sizeof(Index), hipMemcpyDeviceToHost);
+  if (e == hipSuccess && n) e = hipMemcpy(p.data(), dperm, n * sizeof(Index), hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return fail(SEGPOLY_E_HIP, std::string("validate copy: ") + hipGetErrorString(e));
+  std::vector<char> seen(n, 0);
+  for (int64_t i = 0; i < n; ++i) {
+    const int64_t q = static_cast<int64_t>(p[i]);
+    if (q < 0 || q >= n || seen[q])
+      return fail(SEGPOLY_E_RANGE, "species_perm is not a permutation of the atoms (entry " + std::to_string(i) + ")");
+    seen[q] = 1;
+    if (i && s[q] < s[p[i - 1]])
+      return fail(SEGPOLY_E_UNSORTED, "species[species_perm[.]] is not ascending at entry " + std::to_string(i));
+  }
+  return ok();
+}
+
 template <typename Index>
 int check_species(const void* dsp, int64_t n, int num_elements, void* stream) {
   std::vector<Index> s(n);
@@ -380,8 +401,7 @@ int tp_conv_bwd_workspace(tp_handle h, int64_t n_edges, int batch, size_t* bytes
   if (n_edges < 0) return fail(SEGPOLY_E_INVALID, "negative size");
   const size_t esz = h->dtype == SEGPOLY_F32 ? 4 : 8;
   const size_t e = static_cast<size_t>(n_edges);
-  size_t msg = batch ? 0 : e * static_cast<size_t>(h->d.dim1) * esz;
-  msg = (msg + 255) / 256 * 256;
+  const size_t msg = static_cast<size_t>(round_up_256(static_cast<int64_t>(batch ? 0 : e * h->d.dim1 * esz)));
   const int mul = h->d.uniform_mul ? h->d.mul : 0;
   const size_t tiles = static_cast<size_t>((mul + 63) / 64);
   *bytes = msg + (tiles > 1 ? tiles * e * static_cast<size_t>(h->d.dim2) * esz : 0);
@@ -611,6 +631,62 @@ int symcon_fwd(symcon_handle h, const void* x, const void* species, int idx_dtyp
     g.numel = h->d.numel;
     rc = launch_symcon_generic(a, g);
   }
+  if (rc != 0)
+    return fail(SEGPOLY_E_HIP, std::string("kernel launch failed: ") + hipGetErrorString(static_cast<hipError_t>(rc)));
+  return ok();
+}
+
+int symcon_bwd_workspace(symcon_handle h, int64_t n_atoms, size_t* bytes) {
+  if (!h || !bytes) return fail(SEGPOLY_E_INVALID, "null argument");
+  if (n_atoms < 0) return fail(SEGPOLY_E_INVALID, "negative size");
+  const size_t esz = h->dtype == SEGPOLY_F32 ? 4 : 8;
+  const size_t table = static_cast<size_t>(symcon_bwd_table_bytes(h->num_elements));
+  const size_t chunks = static_cast<size_t>(symcon_bwd_max_chunks(n_atoms, h->num_elements));
+  *bytes = table + chunks * static_cast<size_t>(h->d.numel) * esz;
+  return ok();
+}
+
+int symcon_bwd(symcon_handle h, const void* x, const void* species, const void* species_perm, int idx_dtype,
+               const void* w, const void* grad_out, int64_t n_atoms, void* grad_x, void* grad_w, void* workspace,
+               size_t workspace_bytes, void* stream) {
+  if (!h) return fail(SEGPOLY_E_INVALID, "null handle");
+  if (n_atoms < 0) return fail(SEGPOLY_E_INVALID, "negative size");
+  if (idx_dtype != SEGPOLY_I32 && idx_dtype != SEGPOLY_I64) return fail(SEGPOLY_E_INVALID, "bad index dtype");
+  if (!h->spec || !h->spec->launch_bwd)
+    return fail(SEGPOLY_E_UNSUPPORTED, "backward needs a specialised kernel for this descriptor");
+  if (n_atoms > kMaxGrid) return fail(SEGPOLY_E_UNSUPPORTED, "n_atoms must be below 2^31");
+  if (!grad_w) return fail(SEGPOLY_E_INVALID, "null grad_w");
+  if (n_atoms > 0 && (!x || !species || !species_perm || !w || !grad_out || !grad_x))
+    return fail(SEGPOLY_E_INVALID, "null pointer");
+  size_t need = 0;
+  symcon_bwd_workspace(h, n_atoms, &need);
+  if (!workspace || workspace_bytes < need)
+    return fail(SEGPOLY_E_INVALID, "workspace missing or smaller than symcon_bwd_workspace()");
+  if ((h->flags & SEGPOLY_VALIDATE) && n_atoms > 0) {
+    int st = idx_dtype == SEGPOLY_I32 ? check_species<int32_t>(species, n_atoms, h->num_elements, stream)
+                                      : check_species<int64_t>(species, n_atoms, h->num_elements, stream);
+    if (st == SEGPOLY_OK)
+      st = idx_dtype == SEGPOLY_I32 ? check_species_perm<int32_t>(species, species_perm, n_atoms, stream)
+                                    : check_species_perm<int64_t>(species, species_perm, n_atoms, stream);
+    if (st != SEGPOLY_OK) return st;
+  }
+  SymconBwdArgs a{};
+  a.x = x;
+  a.species = species;
+  a.perm = species_perm;
+  a.w = w;
+  a.g = grad_out;
+  a.dx = grad_x;
+  a.dw = grad_w;
+  a.workspace = workspace;
+  a.n_atoms = n_atoms;
+  a.num_elements = h->num_elements;
+  a.mul = h->d.mul;
+  a.dtype = h->dtype;
+  a.idx = idx_dtype;
+  a.layout = h->layout;
+  a.stream = stream;
+  const int rc = h->spec->launch_bwd(a);
   if (rc != 0)
     return fail(SEGPOLY_E_HIP, std::string("kernel launch failed: ") + hipGetErrorString(static_cast<hipError_t>(rc)));
   return ok();

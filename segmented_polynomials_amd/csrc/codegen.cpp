@@ -385,9 +385,114 @@ void emit_symcon(const std::string& name, unsigned dtypes, const SymconDescripto
     }
   }
 
+  // backward, per atom and channel, in two functions (fewer live registers):
+  // bwd_w: the forward accumulators a_{s,M} (same code as above), then
+  //    dw[s] += g[M] a_{s,M};
+  // bwd_x: gw_{s,M} = w[s] g[M]; per monomial B = sum of c gw over its terms;
+  //    dx by the product rule, grouped by the sorted prefix (a, b):
+  //    S_ab = B_ab + sum_c B_abc v[c], dx[c] += B_abc v[a] v[b],
+  //    dx[a] += v[b] S_ab, dx[b] += v[a] S_ab; degree 1: dx[a] += B_a.
+  std::ostringstream bwd;
+  std::string bwd_w, bwd_x;
+  {
+    std::set<std::pair<int, int>> used1;
+    auto acc1 = [&](const std::string& m, const std::vector<std::tuple<int, int, double>>& terms) {
+      for (const auto& [sg, M, c] : terms) {
+        const std::string a = "a" + std::to_string(sg) + "_" + std::to_string(M);
+        if (!used1.count({sg, M})) {
+          used1.insert({sg, M});
+          bwd << "      T " << a << " = " << lit(c) << " * " << m << ";\n";
+        } else {
+          bwd << "      " << a << " = fmadd(" << lit(c) << ", " << m << ", " << a << ");\n";
+        }
+      }
+    };
+    bwd << "    {\n";
+    for (int a = 0; a < n; ++a) {
+      auto it = mono.find({a, -1, -1});
+      if (it != mono.end()) acc1("v[" + std::to_string(a) + "]", it->second);
+    }
+    for (int a = 0; a < n; ++a)
+      for (int b = a; b < n; ++b) {
+        bool need = mono.count({a, b, -1}) > 0;
+        for (int c = b; c < n && !need; ++c) need = mono.count({a, b, c}) > 0;
+        if (!need) continue;
+        const std::string p = "p" + std::to_string(a) + "_" + std::to_string(b);
+        bwd << "      const T " << p << " = v[" << a << "] * v[" << b << "];\n";
+        auto it = mono.find({a, b, -1});
+        if (it != mono.end()) acc1(p, it->second);
+        for (int c = b; c < n; ++c) {
+          auto jt = mono.find({a, b, c});
+          if (jt == mono.end()) continue;
+          const std::string m = "m" + std::to_string(a) + "_" + std::to_string(b) + "_" + std::to_string(c);
+          bwd << "      const T " << m << " = " << p << " * v[" << c << "];\n";
+          acc1(m, jt->second);
+        }
+      }
+    for (const auto& [sg, M] : used1) {
+      const int og = d.out_comp[d.couplings[sg].ob] + M;
+      bwd << "      dw[" << sg << "] = fmadd(g[" << og << "], a" << sg << "_" << M << ", dw[" << sg << "]);\n";
+    }
+    bwd << "    }\n";
+    bwd_w = bwd.str();
+    bwd.str("");
+    bwd << "    {\n";
+    for (const auto& [sg, M] : used1) {
+      const int og = d.out_comp[d.couplings[sg].ob] + M;
+      bwd << "      const T gw" << sg << "_" << M << " = wv[" << sg << "] * g[" << og << "];\n";
+    }
+    for (int i = 0; i < n; ++i) bwd << "      dx[" << i << "] = T(0);\n";
+    auto adj = [&](const std::string& B, const std::vector<std::tuple<int, int, double>>& terms) {
+      bool first = true;
+      for (const auto& [sg, M, c] : terms) {
+        const std::string gw = "gw" + std::to_string(sg) + "_" + std::to_string(M);
+        if (first)
+          bwd << "      T " << B << " = " << lit(c) << " * " << gw << ";\n";
+        else
+          bwd << "      " << B << " = fmadd(" << lit(c) << ", " << gw << ", " << B << ");\n";
+        first = false;
+      }
+    };
+    for (int a = 0; a < n; ++a) {
+      auto it = mono.find({a, -1, -1});
+      if (it == mono.end()) continue;
+      const std::string B = "b" + std::to_string(a);
+      bwd << "      {\n";
+      adj(B, it->second);
+      bwd << "      dx[" << a << "] += " << B << ";\n      }\n";
+    }
+    for (int a = 0; a < n; ++a)
+      for (int b = a; b < n; ++b) {
+        const bool has2 = mono.count({a, b, -1}) > 0;
+        bool has3 = false;
+        for (int c = b; c < n && !has3; ++c) has3 = mono.count({a, b, c}) > 0;
+        if (!has2 && !has3) continue;
+        bwd << "      {\n";
+        if (has2) {
+          adj("S", mono.at({a, b, -1}));
+        } else {
+          bwd << "      T S = T(0);\n";
+        }
+        if (has3) bwd << "      const T p = v[" << a << "] * v[" << b << "];\n";
+        for (int c = b; c < n; ++c) {
+          auto jt = mono.find({a, b, c});
+          if (jt == mono.end()) continue;
+          const std::string B = "b" + std::to_string(c);
+          bwd << "      {\n";
+          adj(B, jt->second);
+          bwd << "      S = fmadd(" << B << ", v[" << c << "], S);\n";
+          bwd << "      dx[" << c << "] = fmadd(" << B << ", p, dx[" << c << "]);\n      }\n";
+        }
+        bwd << "      dx[" << a << "] = fmadd(v[" << b << "], S, dx[" << a << "]);\n";
+        bwd << "      dx[" << b << "] = fmadd(v[" << a << "], S, dx[" << b << "]);\n      }\n";
+      }
+    bwd << "    }\n";
+    bwd_x = bwd.str();
+  }
+
   os << "// Generated by codegen.cpp from the descriptor: symmetric contraction " << irreps_str(d.in) << " -> "
      << irreps_str(d.out) << "\n// key " << d.key << "\n// " << d.num_terms() << " sorted-monomial terms\n";
-  os << "#include \"kernels/symcon_spec.hpp\"\n\nnamespace segpoly {\nnamespace kern {\n\n";
+  os << "#include \"kernels/symcon_spec.hpp\"\n#include \"kernels/symcon_bwd.hpp\"\n\nnamespace segpoly {\nnamespace kern {\n\n";
   os << "struct " << S << " {\n";
   os << "  static constexpr int NV = " << n << ";\n";
   os << "  static constexpr int NO = " << d.nout << ";\n";
@@ -403,6 +508,37 @@ void emit_symcon(const std::string& name, unsigned dtypes, const SymconDescripto
     os << "      }\n";
   }
   os << "    }\n  }\n\n";
+  // gradient-row load (output layout) and input-gradient store (input layout)
+  os << "  template <typename T, int LAYOUT>\n  __device__ __forceinline__ static void load_o(const T* __restrict__ row, int mul, int u, T* o) {\n";
+  os << "    if constexpr (LAYOUT == kIrMul) {\n";
+  for (int k = 0; k < d.nout; ++k) os << "      o[" << k << "] = row[" << k << " * mul + u];\n";
+  os << "    } else {\n";
+  for (size_t b = 0; b < d.out.size(); ++b) {
+    const int dl = 2 * d.out[b].l + 1, comp = d.out_comp[b];
+    os << "      {\n        const T* p = row + " << comp << " * mul + u * " << dl << ";\n";
+    for (int i = 0; i < dl; ++i) os << "        o[" << comp + i << "] = p[" << i << "];\n";
+    os << "      }\n";
+  }
+  os << "    }\n  }\n\n";
+  os << "  template <typename T, int LAYOUT>\n  __device__ __forceinline__ static void store_v(T* __restrict__ row, int mul, int u, const T* v) {\n";
+  os << "    if constexpr (LAYOUT == kIrMul) {\n";
+  for (int m = 0; m < n; ++m) os << "      row[" << m << " * mul + u] = v[" << m << "];\n";
+  os << "    } else {\n";
+  for (size_t b = 0; b < d.in.size(); ++b) {
+    const int dl = 2 * d.in[b].l + 1, comp = d.in_comp[b];
+    os << "      {\n        T* p = row + " << comp << " * mul + u * " << dl << ";\n";
+    for (int i = 0; i < dl; ++i) os << "        p[" << i << "] = v[" << comp + i << "];\n";
+    os << "      }\n";
+  }
+  os << "    }\n  }\n\n";
+  os << "  // dw[s] += d<g, out>/dw[s]\n";
+  os << "  template <typename T>\n  __device__ __forceinline__ static void bwd_w(const T* v, const T* g, T* dw) {\n";
+  os << bwd_w;
+  os << "  }\n\n";
+  os << "  // dx = d<g, out>/dv (overwritten)\n";
+  os << "  template <typename T>\n  __device__ __forceinline__ static void bwd_x(const T* v, const T* g, const T* wv, T* dx) {\n";
+  os << bwd_x;
+  os << "  }\n\n";
   os << "  template <typename T>\n  __device__ __forceinline__ static void eval(const T* v, const T* wv, T* o) {\n";
   os << body.str();
   os << "  }\n\n";
@@ -420,6 +556,10 @@ void emit_symcon(const std::string& name, unsigned dtypes, const SymconDescripto
   os << "int launch_symcon_" << name << "(const SymconArgs& a) {\n";
   if (dtypes & 1u) os << "  if (a.dtype == kF32) return kern::symcon_spec_dispatch<kern::" << S << ", float>(a);\n";
   if (dtypes & 2u) os << "  if (a.dtype == kF64) return kern::symcon_spec_dispatch<kern::" << S << ", double>(a);\n";
+  os << "  return -1;\n}\n\n";
+  os << "int launch_symcon_bwd_" << name << "(const SymconBwdArgs& a) {\n";
+  if (dtypes & 1u) os << "  if (a.dtype == kF32) return kern::symcon_bwd_dispatch<kern::" << S << ", float>(a);\n";
+  if (dtypes & 2u) os << "  if (a.dtype == kF64) return kern::symcon_bwd_dispatch<kern::" << S << ", double>(a);\n";
   os << "  return -1;\n}\n\n}  // namespace segpoly\n";
 }
 
@@ -482,6 +622,7 @@ int main(int argc, char** argv) {
     reg << "int launch_" << r.kind << "_" << r.name << "(const " << (r.kind == "tp" ? "TPArgs" : "SymconArgs")
         << "&);\n";
     if (r.kind == "tp") reg << "int launch_tp_bwd_" << r.name << "(const TPBwdArgs&);\n";
+    if (r.kind == "symcon") reg << "int launch_symcon_bwd_" << r.name << "(const SymconBwdArgs&);\n";
   }
   reg << "\nconst TPSpecEntry kTPSpecs[] = {\n";
   int ntp = 0, nsc = 0;
@@ -496,10 +637,10 @@ int main(int argc, char** argv) {
   for (const auto& r : regs)
     if (r.kind == "symcon") {
       reg << "    {\"" << r.key << "\", \"" << r.name << "\", " << r.dtypes << "u, &launch_symcon_" << r.name
-          << "},\n";
+          << ", &launch_symcon_bwd_" << r.name << "},\n";
       ++nsc;
     }
-  if (!nsc) reg << "    {\"\", \"\", 0u, nullptr},\n";
+  if (!nsc) reg << "    {\"\", \"\", 0u, nullptr, nullptr},\n";
   reg << "};\nconst int kNumSymconSpecs = " << nsc << ";\n\n}  // namespace segpoly\n";
   return 0;
 }

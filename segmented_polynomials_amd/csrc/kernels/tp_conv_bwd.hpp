@@ -292,8 +292,6 @@ __global__ void __launch_bounds__(256) fill_zero_kernel(T* __restrict__ p, int64
     p[i] = T(0);
 }
 
-inline int64_t round_up_256(int64_t n) { return (n + 255) / 256 * 256; }
-
 template <typename T>
 void fill_zero(T* p, int64_t n, hipStream_t st) {
   if (n <= 0) return;
@@ -325,7 +323,7 @@ int tp_bwd_launch(const TPBwdArgs& a) {
   unsigned char* ws = static_cast<unsigned char*>(a.workspace);
   T* const msg = a.batch ? dx : reinterpret_cast<T*>(ws);
   T* const part =
-      tiles > 1 ? reinterpret_cast<T*>(ws + (a.batch ? 0 : round_up_256(a.n_edges * dim1 * sizeof(T)))) : dsh;
+      tiles > 1 ? reinterpret_cast<T*>(ws + (a.batch ? 0 : round_up_256(a.n_edges * dim1 * static_cast<int64_t>(sizeof(T))))) : dsh;
   hipLaunchKernelGGL((tp_bwd_edge_kernel<S, T, Index, LAYOUT, CPL>),
                      dim3(static_cast<unsigned>(a.n_nodes), static_cast<unsigned>(tiles)), dim3(kWave), 0, st,
                      static_cast<const T*>(a.x), static_cast<const T*>(a.sh), static_cast<const T*>(a.w),

@@ -56,10 +56,41 @@ struct SymconArgs {
   void* stream;
 };
 
+// Backward of the symmetric contraction (specialised kernels only).
+struct SymconBwdArgs {
+  const void* x;        // [n_atoms, dim_in]
+  const void* species;  // [n_atoms]
+  const void* perm;     // [n_atoms] atom ids ordered by species
+  const void* w;        // [num_elements, numel]
+  const void* g;        // [n_atoms, dim_out] gradient of the output
+  void* dx;             // [n_atoms, dim_in]
+  void* dw;             // [num_elements, numel]
+  void* workspace;      // segment table, then per-chunk weight-gradient partials
+  int64_t n_atoms;
+  int num_elements;
+  int mul;
+  int dtype, idx, layout;
+  void* stream;
+};
+
+// Workspace layouts of the backward calls, shared by the C ABI (sizes) and
+// the launchers (offsets).
+inline int64_t round_up_256(int64_t n) { return (n + 255) / 256 * 256; }
+
+// Symmetric contraction: a segment table of 2 * (E + 3) int64, then one
+// partial weight-gradient row per chunk of kSymconBwdChunk atoms (each
+// element segment adds at most one partial chunk, so E + 2 extra rows).
+constexpr int kSymconBwdChunk = 8;
+inline int64_t symcon_bwd_table_bytes(int num_elements) { return round_up_256(16 * (num_elements + 3)); }
+inline int64_t symcon_bwd_max_chunks(int64_t n_atoms, int num_elements) {
+  return (n_atoms + kSymconBwdChunk - 1) / kSymconBwdChunk + num_elements + 2;
+}
+
 // Returns 0 or a hipError_t value of the launch.
 using TPLaunchFn = int (*)(const TPArgs&);
 using SymconLaunchFn = int (*)(const SymconArgs&);
 using TPBwdLaunchFn = int (*)(const TPBwdArgs&);
+using SymconBwdLaunchFn = int (*)(const SymconBwdArgs&);
 
 struct TPSpecEntry {
   const char* key;
@@ -74,6 +105,7 @@ struct SymconSpecEntry {
   const char* name;
   unsigned dtypes;
   SymconLaunchFn launch;
+  SymconBwdLaunchFn launch_bwd;
 };
 
 // generated registry

@@ -228,3 +228,26 @@ def test_backward_argument_errors_fail_before_any_gpu_call():
     # nothing to do: succeeds without touching a device
     assert f(h._h, None, 0, None, None, None, None, None, 0, 0, 0, None, None, None, None, None, 0,
              None) == sp.OK
+
+
+def test_symcon_backward_argument_errors_fail_before_any_gpu_call():
+    s = sp.symcon_create("32x0e+32x1o", "32x0e", 3, 4)
+    assert s.specialized
+    n = ctypes.c_size_t()
+    assert sp.lib.symcon_bwd_workspace(s._h, 100, ctypes.byref(n)) == sp.OK
+    table = (16 * (4 + 3) + 255) // 256 * 256
+    assert n.value == table + ((100 + 7) // 8 + 4 + 2) * s.weight_numel * 4
+    assert sp.lib.symcon_bwd_workspace(s._h, -1, ctypes.byref(n)) == sp.E_INVALID
+    f = sp.lib.symcon_bwd
+    p = ctypes.c_void_p(16)   # never dereferenced: every call below fails validation
+    big = 1 << 40
+    # h, x, species, perm, idx, w, g, n_atoms, gx, gw, ws, ws_bytes, stream
+    assert f(None, p, p, p, 0, p, p, 3, p, p, p, big, None) == sp.E_INVALID
+    assert f(s._h, p, p, p, 0, p, p, -3, p, p, p, big, None) == sp.E_INVALID
+    assert f(s._h, p, p, p, 5, p, p, 3, p, p, p, big, None) == sp.E_INVALID       # index dtype
+    assert f(s._h, p, p, None, 0, p, p, 3, p, p, p, big, None) == sp.E_INVALID    # no perm
+    assert f(s._h, p, p, p, 0, p, p, 3, p, None, p, big, None) == sp.E_INVALID    # no grad_w
+    assert f(s._h, p, p, p, 0, p, p, 3, p, p, p, 16, None) == sp.E_INVALID        # workspace small
+    assert f(s._h, p, p, p, 0, p, p, 1 << 31, p, p, p, big, None) == sp.E_UNSUPPORTED
+    sg = sp.symcon_create("32x0e+32x1o", "32x0e", 3, 4, force_generic=True)
+    assert f(sg._h, p, p, p, 0, p, p, 3, p, p, p, big, None) == sp.E_UNSUPPORTED

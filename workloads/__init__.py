@@ -281,3 +281,9 @@ def src_permutation(src):
     """Edge ids ordered by source, ties in edge order (a stable argsort):
     graph structure the backward pass takes with the sorted destinations."""
     return np.argsort(np.asarray(src), kind="stable").astype(np.asarray(src).dtype)
+
+
+def species_permutation(species):
+    """Atom ids ordered by element, ties in atom order (a stable argsort):
+    what the symmetric contraction's backward takes with the species."""
+    return np.argsort(np.asarray(species), kind="stable").astype(np.asarray(species).dtype)
