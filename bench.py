@@ -27,6 +27,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0            # MI355X HBM3E, published
 FP32_VALU_PEAK_TFLOPS = 78.6      # 256 CU x 4 SIMD x 16 lanes x 2 flop x 2.4 GHz (no packed FP32)
+FP32_MFMA_PEAK_TFLOPS = 157.3     # MI355X dense FP32 matrix, published
 METRIC = "edges/sec + achieved HBM GB/s (fraction of peak) for fused equivariant TP-conv"
 
 
@@ -258,6 +259,7 @@ def main():
 
     if not args.no_extras:
         result["other_workloads"] = other_workloads(torch, sp, workloads, dev, args)
+        result["linear"] = linear_layers(torch, sp, workloads, dev, args)
 
     if args.copy_calibration:
         a = torch.empty(1 << 28, dtype=torch.float32, device=dev)   # 1 GiB
@@ -368,6 +370,54 @@ def backward(torch, sp, workloads, h, x, sh, w, src, dst, N, E, args):
          "kernels": ["tp_bwd_edge_kernel", "tp_bwd_src_kernel"]}
     del g, perm, gx, gsh, gw, ws
     return r
+
+
+def linear_layers(torch, sp, workloads, dev, args):
+    """The equivariant linear layers on the matrix cores: the layer after
+    the 600k-edge convolution (shared weights; forward and backward) and
+    the species-indexed layer on 50k atoms (10 sorted classes).  flops =
+    2 * sum over weight segments of mul_in * mul_out * (2l + 1) per sample
+    (the dense products; the backward does twice that)."""
+    import numpy as np
+
+    from oracle import irreps as oir   # sizes only: block multiplicities and l
+    res = {}
+    for num in (6, 7):
+        wl = workloads.WORKLOADS[num]
+        h = sp.linear_create(wl.irreps_in, wl.irreps_out, layout=wl.layouts[0])
+        inp = workloads.linear_inputs(wl, h.weight_numel)
+        x, w = (torch.from_numpy(np.ascontiguousarray(inp[k])).to(dev) for k in ("x", "w"))
+        cls = None if inp["classes"] is None else torch.from_numpy(inp["classes"]).to(dev)
+        out = torch.empty((wl.n, h.dim_out), dtype=torch.float32, device=dev)
+        f = lambda: sp.linear_fwd(h, x, w, classes=cls, out=out)
+        wall, per = time_launches(torch, f, args.steps, args.warmup)
+        kms = sum(per) / len(per)
+        blocks_in, blocks_out = oir.parse(wl.irreps_in), oir.parse(wl.irreps_out)
+        macs = sum(mi * mo * (2 * li + 1) for mi, li, pi in blocks_in for mo, lo, po in blocks_out
+                   if (li, pi) == (lo, po))
+        flops = 2.0 * macs * wl.n
+        nbytes = (h.dim_in + h.dim_out) * wl.n * 4 + w.numel() * 4 + (0 if cls is None else wl.n * 4)
+        tf = flops / (kms * 1e-3) / 1e12
+        r = {"workload": wl.name, "layout": wl.layouts[0], "samples": wl.n, "ms_per_call": kms,
+             "samples_per_s": wl.n / (wall / args.steps),
+             "roofline": {"bound": "mfma", "achieved": tf, "peak": FP32_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                          "frac": tf / FP32_MFMA_PEAK_TFLOPS, "algorithmic_flops": flops},
+             "hbm": {"achieved": nbytes / (kms * 1e-3) / 1e9, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "algorithmic_bytes": nbytes}}
+        if cls is None:
+            g = torch.from_numpy(workloads.output_gradient(wl.n, h.dim_out, "f32", seed=66)).to(dev)
+            ws = torch.empty(max(1, sp.linear_bwd_workspace(h, wl.n)), dtype=torch.uint8, device=dev)
+            fb = lambda: sp.linear_bwd(h, x, w, g, workspace=ws)
+            wallb, perb = time_launches(torch, fb, args.steps, args.warmup)
+            kb = sum(perb) / len(perb)
+            tfb = 2 * flops / (kb * 1e-3) / 1e12
+            r["backward"] = {"ms_per_call": kb, "roofline": {"bound": "mfma", "achieved": tfb,
+                                                            "peak": FP32_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                                                            "frac": tfb / FP32_MFMA_PEAK_TFLOPS}}
+            del g, ws
+        res[wl.name] = r
+        del x, w, out, cls
+    return res
 
 
 def other_workloads(torch, sp, workloads, dev, args):

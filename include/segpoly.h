@@ -90,6 +90,7 @@ extern "C" {
 
 typedef struct segpoly_tp* tp_handle;
 typedef struct segpoly_symcon* symcon_handle;
+typedef struct segpoly_linear* linear_handle;
 
 /* ------------------------------------------------------------------ TP */
 
@@ -303,6 +304,64 @@ int symcon_bwd(symcon_handle h, const void* x, const void* species, const void* 
 int symcon_destroy(symcon_handle h);
 
 /* ------------------------------------------------------------------ misc */
+
+/* ------------------------------------------------------------------ linear */
+
+/*
+ * linear_create: the equivariant linear layer irreps_in -> irreps_out
+ * ("cuequivariance-torch" skill document, "Linear: layout conversion and
+ * rotations"; "Other operations and layers" for class-indexed weights).
+ * Blocks of equal irrep type mix channel by channel with one matrix per
+ * (input block, output block) pair, the same for every component m:
+ *   out[n, o, m, v] = alpha_t sum over input blocks i of type t of
+ *                     sum_u W_io[u, v] x[n, i, m, u],
+ * alpha_t = 1 / sqrt(sum of the multiplicities of the input blocks of type
+ * t); an output block whose type no input has is zero.  Weight segments:
+ * pairs in the order i, then o, each mul_i x mul_o with v fastest
+ * (WEIGHT_NUMEL in total).  flags: SEGPOLY_VALIDATE only.  E_UNSUPPORTED
+ * beyond 32 blocks on a side or 32 pairs.  Touches no GPU.
+ */
+int linear_create(const char* irreps_in, const char* irreps_out, int layout, int dtype, unsigned flags,
+                  linear_handle* out);
+
+/* linear_query: SEGPOLY_Q_DIM_IN, SEGPOLY_Q_DIM_OUT, SEGPOLY_Q_WEIGHT_NUMEL,
+ * SEGPOLY_Q_NUM_PATHS (the number of weight segments). */
+int linear_query(linear_handle h, int key, int64_t* value);
+
+/*
+ * linear_fwd: out = linear(x) for n samples, on the matrix cores.
+ *   x        [n, DIM_IN] device, layout of the handle.
+ *   w        [1, WEIGHT_NUMEL] device (shared), or with `classes`
+ *            [num_classes, WEIGHT_NUMEL]: sample n uses row classes[n].
+ *   classes  NULL, or [n] device, int32 or int64 per idx_dtype; a class
+ *            outside [0, num_classes) gives a zero row (E_RANGE with
+ *            VALIDATE).  Sorted classes run fastest (a tile of rows of one
+ *            class costs one pass); any order is correct.
+ *   out      [n, DIM_OUT] device, fully overwritten.
+ */
+int linear_fwd(linear_handle h, const void* x, const void* w, const void* classes, int idx_dtype, int num_classes,
+               int64_t n, void* out, void* stream);
+
+/* linear_bwd_workspace: bytes of workspace linear_bwd needs for the weight
+ * gradient of n samples (per-chunk partial sums). */
+int linear_bwd_workspace(linear_handle h, int64_t n, size_t* bytes);
+
+/*
+ * linear_bwd: vector-Jacobian product of linear_fwd for g = dL/d(out):
+ *   grad_x[n, i, m, u] = alpha_t sum over pairs (i, o) of sum_v W_io[u, v] g[n, o, m, v]
+ *   grad_w[W_io][u, v] = alpha_t sum over samples n and components m of x[n, i, m, u] g[n, o, m, v]
+ * grad_x [n, DIM_IN] is fully overwritten.  grad_w [1, WEIGHT_NUMEL] may be
+ * NULL (not computed; x and the workspace are then not used); with
+ * `classes` it must be NULL (E_UNSUPPORTED otherwise).  The weight gradient
+ * sums fixed chunks of 2048 rows and then the chunks in order:
+ * deterministic.  Other arguments as linear_fwd.
+ */
+int linear_bwd(linear_handle h, const void* x, const void* w, const void* grad_out, const void* classes,
+               int idx_dtype, int num_classes, int64_t n, void* grad_x, void* grad_w, void* workspace,
+               size_t workspace_bytes, void* stream);
+
+/* linear_destroy: free the handle (NULL is a no-op). */
+int linear_destroy(linear_handle h);
 
 /* segpoly_real_cg: the real coupling tensor of l1 x l2 -> l3 (the same
  * coefficients the paths use), row-major [2l1+1][2l2+1][2l3+1]. */

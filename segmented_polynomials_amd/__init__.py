@@ -2,7 +2,7 @@
 
 The functions keep the names of the C ABI in ``include/segpoly.h``:
 ``tp_create`` / ``tp_conv_fwd`` / ``tp_conv_bwd`` / ``symcon_create`` / ``symcon_fwd`` /
-``symcon_bwd``.  Every
+``symcon_bwd`` / ``linear_create`` / ``linear_fwd`` / ``linear_bwd``.  Every
 step of the computation runs in the library's HIP kernels; PyTorch only
 supplies device memory and the current stream.  There is no CPU fallback:
 importing this package fails loudly if the library has not been built.
@@ -31,7 +31,8 @@ _DTYPES = {"f32": F32, "f64": F64}
 # every symbol include/segpoly.h declares
 EXPORTS = ("tp_create", "tp_query", "tp_irreps_out", "tp_path_info", "tp_path_cg", "tp_kernel_name",
            "tp_conv_fwd", "tp_conv_bwd_workspace", "tp_conv_bwd", "tp_destroy", "symcon_create", "symcon_query", "symcon_coupling_info",
-           "symcon_coupling_dense", "symcon_fwd", "symcon_bwd_workspace", "symcon_bwd", "symcon_destroy", "segpoly_real_cg",
+           "symcon_coupling_dense", "symcon_fwd", "symcon_bwd_workspace", "symcon_bwd", "symcon_destroy", "linear_create", "linear_query", "linear_fwd",
+           "linear_bwd_workspace", "linear_bwd", "linear_destroy", "segpoly_real_cg",
            "segpoly_last_error", "segpoly_version")
 
 
@@ -85,6 +86,12 @@ def _load():
         "symcon_bwd_workspace": [vp, i64, ctypes.POINTER(ctypes.c_size_t)],
         "symcon_bwd": [vp, vp, vp, vp, c_int, vp, vp, i64, vp, vp, vp, ctypes.c_size_t, vp],
         "symcon_destroy": [vp],
+        "linear_create": [ctypes.c_char_p, ctypes.c_char_p, c_int, c_int, c_uint, ctypes.POINTER(vp)],
+        "linear_query": [vp, c_int, p64],
+        "linear_fwd": [vp, vp, vp, vp, c_int, c_int, i64, vp, vp],
+        "linear_bwd_workspace": [vp, i64, ctypes.POINTER(ctypes.c_size_t)],
+        "linear_bwd": [vp, vp, vp, vp, vp, c_int, c_int, i64, vp, vp, vp, ctypes.c_size_t, vp],
+        "linear_destroy": [vp],
         "segpoly_real_cg": [c_int, c_int, c_int, pd],
     }
     for name, args in sig.items():
@@ -399,4 +406,93 @@ def symcon_bwd(h, x, species, w, grad_out, species_perm, workspace=None, grad_x=
     wbytes = workspace.numel() * workspace.element_size()
     _check(lib.symcon_bwd(h._h, _ptr(x), _ptr(species), _ptr(species_perm), _index_dtype(species), _ptr(w),
                           _ptr(grad_out), n, _ptr(gx), _ptr(gw), _ptr(workspace), wbytes, _stream_ptr(x.device)))
+    return gx, gw
+
+
+# ---------------------------------------------------------------- linear
+
+class LinearHandle:
+    def __init__(self, raw, layout, dtype):
+        self._h = raw
+        self.layout = layout
+        self.dtype = dtype
+
+    def _q(self, key):
+        v = ctypes.c_int64()
+        _check(lib.linear_query(self._h, key, ctypes.byref(v)))
+        return v.value
+
+    dim_in = property(lambda s: s._q(Q_DIM_IN))
+    dim_out = property(lambda s: s._q(Q_DIM_OUT))
+    weight_numel = property(lambda s: s._q(Q_WEIGHT_NUMEL))
+    num_segments = property(lambda s: s._q(Q_NUM_PATHS))
+
+    def __del__(self):
+        if getattr(self, "_h", None) and lib is not None:
+            lib.linear_destroy(self._h)
+            self._h = None
+
+
+def linear_create(irreps_in, irreps_out, layout="ir_mul", dtype="f32", validate=False):
+    raw = ctypes.c_void_p()
+    _check(lib.linear_create(irreps_in.encode(), irreps_out.encode(), _LAYOUTS[layout], _DTYPES[dtype],
+                             VALIDATE if validate else 0, ctypes.byref(raw)))
+    return LinearHandle(raw, layout, dtype)
+
+
+def _lin_common(h, x, w, classes, num_classes):
+    t = _torch_dtype(h.dtype)
+    for name, a in (("x", x), ("w", w)):
+        if a.dtype != t or not a.is_cuda or not a.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous {t} device tensor")
+    n = x.shape[0]
+    if x.shape[1] != h.dim_in or w.shape[-1] != h.weight_numel:
+        raise ValueError("operand widths do not match the descriptor")
+    idx, nc = I32, 1
+    if classes is not None:
+        if classes.shape != (n,) or not classes.is_cuda or not classes.is_contiguous():
+            raise ValueError("classes must be a contiguous [n] device tensor")
+        idx = _index_dtype(classes)
+        nc = w.shape[0] if num_classes is None else num_classes
+        if w.shape[0] != nc:
+            raise ValueError("class-indexed weights are [num_classes, weight_numel]")
+    elif w.shape[0] != 1:
+        raise ValueError("shared weights are one row [1, weight_numel]")
+    return t, n, idx, nc
+
+
+def linear_fwd(h, x, w, classes=None, num_classes=None, out=None):
+    """Equivariant linear map of x [n, dim_in] with shared weights [1,
+    weight_numel] or class-indexed weights [num_classes, weight_numel]
+    (``classes`` [n] int32/int64)."""
+    import torch
+    t, n, idx, nc = _lin_common(h, x, w, classes, num_classes)
+    if out is None:
+        out = torch.empty((n, h.dim_out), dtype=t, device=x.device)
+    elif out.shape != (n, h.dim_out) or out.dtype != t or not out.is_contiguous():
+        raise ValueError("out has the wrong shape or dtype")
+    _check(lib.linear_fwd(h._h, _ptr(x), _ptr(w), _ptr(classes), idx, nc, n, _ptr(out), _stream_ptr(x.device)))
+    return out
+
+
+def linear_bwd_workspace(h, n):
+    v = ctypes.c_size_t()
+    _check(lib.linear_bwd_workspace(h._h, n, ctypes.byref(v)))
+    return v.value
+
+
+def linear_bwd(h, x, w, grad_out, classes=None, num_classes=None, need_dw=True, workspace=None):
+    """Gradients (grad_x, grad_w or None) of ``linear_fwd`` for ``grad_out``
+    [n, dim_out]; the weight gradient needs shared weights."""
+    import torch
+    t, n, idx, nc = _lin_common(h, x, w, classes, num_classes)
+    if grad_out.shape != (n, h.dim_out) or grad_out.dtype != t or not grad_out.is_contiguous():
+        raise ValueError("grad_out has the wrong shape or dtype")
+    gx = torch.empty_like(x)
+    gw = torch.empty_like(w) if need_dw else None
+    if need_dw and workspace is None:
+        workspace = torch.empty(max(1, linear_bwd_workspace(h, n)), dtype=torch.uint8, device=x.device)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.linear_bwd(h._h, _ptr(x), _ptr(w), _ptr(grad_out), _ptr(classes), idx, nc, n, _ptr(gx), _ptr(gw),
+                          _ptr(workspace), wbytes, _stream_ptr(x.device)))
     return gx, gw

@@ -63,12 +63,12 @@ def build(verbose=False, jobs=None):
 
     # 2. compile
     jobs_list = []
-    for s in HOST_SOURCES + ["capi.cpp"]:
+    for s in HOST_SOURCES + ["capi.cpp", "capi_linear.cpp"]:
         jobs_list.append(["g++", *HOST_FLAGS, *inc, "-c", os.path.join(CSRC, s),
                           "-o", os.path.join(obj, s + ".o")])
     jobs_list.append(["g++", *HOST_FLAGS, *inc, "-c", os.path.join(gen, "registry.cpp"),
                       "-o", os.path.join(obj, "registry.cpp.o")])
-    for h in [os.path.join(CSRC, "kernels", "generic.hip")] + gen_hip:
+    for h in [os.path.join(CSRC, "kernels", "generic.hip"), os.path.join(CSRC, "kernels", "linear.hip")] + gen_hip:
         jobs_list.append([hipcc, *HIP_FLAGS, *inc, "-c", h,
                           "-o", os.path.join(obj, os.path.basename(h) + ".o")])
     with cf.ThreadPoolExecutor(jobs) as ex:

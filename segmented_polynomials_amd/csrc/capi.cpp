@@ -10,6 +10,7 @@
 #include <string>
 #include <vector>
 
+#include "capi_util.hpp"
 #include "cg.hpp"
 #include "generic_tables.hpp"
 #include "launch.hpp"
@@ -19,19 +20,11 @@
 
 using namespace segpoly;
 
-namespace {
-
+namespace segpoly {
 thread_local std::string g_last_error;
+}  // namespace segpoly
 
-int fail(int code, const std::string& msg) {
-  g_last_error = msg;
-  return code;
-}
-
-int ok() {
-  g_last_error.clear();
-  return SEGPOLY_OK;
-}
+namespace {
 
 constexpr size_t kGenericLdsLimit = 64 * 1024;
 constexpr int64_t kMaxGrid = 2147483647;

@@ -1,0 +1,469 @@
+// Equivariant linear layer on the matrix cores (gfx950 MFMA).
+//
+// cuequivariance-torch skill document, "Linear: layout conversion and
+// rotations" and "Other operations and layers" (species-indexed Linear):
+// only blocks of one irrep type mix, channel by channel, with the same matrix
+// for every component m.  For an output block o of type t (d = 2l + 1
+// components, alpha_t = 1 / sqrt(sum of the input multiplicities of type t)):
+//   out[n, o, m, v] = alpha_t * sum over input blocks i of type t of
+//                     sum_u W_io[u, v] * x[n, i, m, u].
+// Per output block this is a dense GEMM with rows r = (n, m) (n * d rows),
+// K = the concatenated input channels of its type, columns v.  The same
+// kernel computes the backward's dx = alpha G W^T (TRANSW: the weight
+// segment is read transposed).
+//
+// Tiling: a workgroup of 4 waves owns a 64 x 128 tile of one output block's
+// GEMM; the K loop stages 64 x 32 of A (rows of x) and 32 x 128 of B (the
+// weight segment) in LDS; each wave computes 32 x 64 with eight
+// v_mfma_*_16x16x4 per 4 k.  Class-indexed weights (one row of weights per
+// sample picked by an index, sorted in practice): the tile runs one masked
+// pass per class present among its rows (rows of other classes read as
+// zero), so a tile inside one class costs one pass.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "../launch.hpp"
+#include "../linear_tables.hpp"
+
+namespace segpoly {
+namespace kern {
+
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef double v4d __attribute__((ext_vector_type(4)));
+
+template <typename T>
+struct Mfma;
+
+// v_mfma_f32_16x16x4f32: lane l supplies A[l % 16][l / 16], B[l / 16][l % 16];
+// accumulator j of lane l is C[4 (l / 16) + j][l % 16].
+template <>
+struct Mfma<float> {
+  using acc_t = v4f;
+  __device__ __forceinline__ static acc_t mma(float a, float b, acc_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+  }
+  __device__ __forceinline__ static int row(int lane, int j) { return 4 * (lane / 16) + j; }
+};
+
+// v_mfma_f64_16x16x4f64: same operands; accumulator j of lane l is
+// C[4 j + l / 16][l % 16].
+template <>
+struct Mfma<double> {
+  using acc_t = v4d;
+  __device__ __forceinline__ static acc_t mma(double a, double b, acc_t c) {
+    return __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, c, 0, 0, 0);
+  }
+  __device__ __forceinline__ static int row(int lane, int j) { return 4 * j + lane / 16; }
+};
+
+constexpr int kLinTM = kLinTileRows, kLinTN = kLinTileCols, kLinTK = 32, kLinThreads = 256;
+// 4 waves as 2 x 2; each wave owns (kLinTM / 2) x (kLinTN / 2) = kMT x kNT
+// MFMA tiles of 16 x 16
+constexpr int kMT = kLinTM / 32, kNT = kLinTN / 32;
+static_assert(kLinTM % 32 == 0 && kLinTN % 32 == 0, "tiles are multiples of two 16-wide MFMA tiles");
+
+// LDS row padding: A rows of 36 and B rows of 144 elements keep the MFMA
+// operand reads free of bank conflicts (64 banks).
+constexpr int kLinPadA = 4, kLinPadB = 16;
+constexpr int kARows = kLinTM * kLinTK / kLinThreads;   // A rows staged per thread
+constexpr int kBElems = kLinTK * kLinTN / kLinThreads;  // B elements staged per thread
+
+template <typename T, typename Index, int LAYOUT, bool TRANSW, bool CLASSES>
+__global__ void __launch_bounds__(kLinThreads)
+linear_kernel(const T* __restrict__ x, const T* __restrict__ w, const Index* __restrict__ cls,
+              T* __restrict__ out, int64_t n, int64_t dim_in, int64_t dim_out, int64_t numel, int num_classes,
+              LinTable tab) {
+  using M = Mfma<T>;
+  __shared__ T As[kLinTM][kLinTK + kLinPadA];
+  __shared__ T Bs[kLinTK][kLinTN + kLinPadB];
+  __shared__ int cls_range[2];
+
+  // which output block and tile
+  const int bid = blockIdx.x;
+  int ob = 0;
+  while (ob + 1 < tab.n_out && tab.outs[ob + 1].tile_begin <= bid) ++ob;
+  const LinOut O = tab.outs[ob];
+  const int tile = bid - O.tile_begin;
+  const int row0 = (tile / O.col_tiles) * kLinTM;  // rows n * d < 2^31 (checked on the host)
+  const int col0 = (tile % O.col_tiles) * kLinTN;
+  const int d = O.d;
+  const int R = static_cast<int>(n) * d;
+
+  const int tid = threadIdx.x;
+  const int lane = tid % 64;
+  const int wave = tid / 64;
+  const int wr = wave / 2, wc = wave % 2;  // wave tile: rows 32 wr.., cols 64 wc..
+
+  // the A rows this thread stages: r = e * 8 + tid / 32, channel tid % 32
+  // (decomposed once: sample base address, component, class)
+  const int kk_a = tid % kLinTK;
+  int64_t a_base[kARows];
+  int a_m[kARows];
+  bool a_ok[kARows];
+  int a_cls[CLASSES ? kARows : 1];
+#pragma unroll
+  for (int e = 0; e < kARows; ++e) {
+    const int row = row0 + e * (kLinThreads / kLinTK) + tid / kLinTK;
+    a_ok[e] = row < R;
+    const int nn = a_ok[e] ? row / d : 0;
+    a_m[e] = a_ok[e] ? row - nn * d : 0;
+    a_base[e] = static_cast<int64_t>(nn) * dim_in;
+    if constexpr (CLASSES) {
+      const int64_t c = a_ok[e] ? static_cast<int64_t>(cls[nn]) : -1;
+      a_cls[e] = (c >= 0 && c < num_classes) ? static_cast<int>(c) : -1;
+    }
+  }
+
+  // classes present among the tile's rows
+  int cmin = 0, cmax = 0;
+  if constexpr (CLASSES) {
+    if (tid == 0) {
+      cls_range[0] = num_classes;
+      cls_range[1] = -1;
+    }
+    __syncthreads();
+    if (kk_a == 0) {
+#pragma unroll
+      for (int e = 0; e < kARows; ++e)
+        if (a_cls[e] >= 0) {
+          atomicMin(&cls_range[0], a_cls[e]);
+          atomicMax(&cls_range[1], a_cls[e]);
+        }
+    }
+    __syncthreads();
+    cmin = cls_range[0];
+    cmax = cls_range[1];
+  }
+
+  typename M::acc_t acc[kMT][kNT];
+#pragma unroll
+  for (int a = 0; a < kMT; ++a)
+#pragma unroll
+    for (int b = 0; b < kNT; ++b) acc[a][b] = typename M::acc_t{0, 0, 0, 0};
+
+  // The K loop runs over the flattened sequence (class, pair, chunk of
+  // kLinTK channels); the next chunk's global loads are issued into
+  // registers before the current chunk's MFMAs, so their latency hides
+  // behind the matrix work.
+  T ra[kARows], rb[kBElems];
+  auto fetch = [&](int c, int p, int k0) {
+    const LinPair P = tab.pairs[p];
+    const T* wc_base = CLASSES ? w + static_cast<int64_t>(c) * numel : w;
+    const int u = k0 + kk_a;
+#pragma unroll
+    for (int e = 0; e < kARows; ++e) {
+      bool take = a_ok[e] && u < P.k_ext;
+      if constexpr (CLASSES) take = take && a_cls[e] == c;
+      T v = T(0);
+      if (take) {
+        const int64_t off = LAYOUT == kIrMul ? P.in_off + static_cast<int64_t>(a_m[e]) * P.k_ext + u
+                                             : P.in_off + static_cast<int64_t>(u) * d + a_m[e];
+        v = x[a_base[e] + off];
+      }
+      ra[e] = v;
+    }
+#pragma unroll
+    for (int e = 0; e < kBElems; ++e) {
+      const int idx = e * kLinThreads + tid;
+      const int kk = TRANSW ? idx % kLinTK : idx / kLinTN;
+      const int cc = TRANSW ? idx / kLinTK : idx % kLinTN;
+      const int uu = k0 + kk, v = col0 + cc;
+      T val = T(0);
+      if (uu < P.k_ext && v < O.n_ext)
+        val = TRANSW ? wc_base[P.w_off + static_cast<int64_t>(v) * P.k_ext + uu]
+                     : wc_base[P.w_off + static_cast<int64_t>(uu) * O.n_ext + v];
+      rb[e] = val;
+    }
+  };
+  // advance (c, p, k0) to the next chunk; false at the end
+  auto next = [&](int& c, int& p, int& k0) -> bool {
+    k0 += kLinTK;
+    if (k0 < tab.pairs[p].k_ext) return true;
+    k0 = 0;
+    if (++p < O.pair_end) return true;
+    p = O.pair_begin;
+    return ++c <= cmax;
+  };
+  int c = cmin, p = O.pair_begin, k0 = 0;
+  bool have = c <= cmax && O.pair_begin < O.pair_end;
+  if (have) fetch(c, p, k0);
+  while (have) {
+    __syncthreads();  // the previous chunk's operands are no longer read
+#pragma unroll
+    for (int e = 0; e < kARows; ++e) As[e * (kLinThreads / kLinTK) + tid / kLinTK][kk_a] = ra[e];
+#pragma unroll
+    for (int e = 0; e < kBElems; ++e) {
+      const int idx = e * kLinThreads + tid;
+      const int kk = TRANSW ? idx % kLinTK : idx / kLinTN;
+      const int cc = TRANSW ? idx / kLinTK : idx % kLinTN;
+      Bs[kk][cc] = rb[e];
+    }
+    __syncthreads();
+    have = next(c, p, k0);
+    if (have) fetch(c, p, k0);
+#pragma unroll
+    for (int s = 0; s < kLinTK / 4; ++s) {
+      const int kq = s * 4 + lane / 16;
+      T a[kMT], b[kNT];
+#pragma unroll
+      for (int i = 0; i < kMT; ++i) a[i] = As[wr * (kLinTM / 2) + i * 16 + lane % 16][kq];
+#pragma unroll
+      for (int j = 0; j < kNT; ++j) b[j] = Bs[kq][wc * (kLinTN / 2) + j * 16 + lane % 16];
+#pragma unroll
+      for (int i = 0; i < kMT; ++i)
+#pragma unroll
+        for (int j = 0; j < kNT; ++j) acc[i][j] = M::mma(a[i], b[j], acc[i][j]);
+    }
+  }
+
+  // epilogue: scale and store (rows of no class in range stay zero)
+  const T alpha = static_cast<T>(O.alpha);
+#pragma unroll
+  for (int i = 0; i < kMT; ++i)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int row = row0 + wr * (kLinTM / 2) + i * 16 + M::row(lane, q);
+      if (row >= R) continue;
+      const int nn = row / d, m = row - nn * d;
+      T* orow = out + static_cast<int64_t>(nn) * dim_out + O.out_off;
+#pragma unroll
+      for (int j = 0; j < kNT; ++j) {
+        const int v = col0 + wc * (kLinTN / 2) + j * 16 + lane % 16;
+        if (v < O.n_ext) {
+          const int64_t off = LAYOUT == kIrMul ? static_cast<int64_t>(m) * O.n_ext + v : static_cast<int64_t>(v) * d + m;
+          orow[off] = alpha * acc[i][j][q];
+        }
+      }
+    }
+}
+
+// Weight gradient of one pair, one (64 u x 128 v) tile and one chunk of
+// kLinDwRows rows: part[chunk][u][v] = sum over the chunk's rows (n, m) of
+// x[n, i, m, u] g[n, o, m, v] (A = x^T staged as [u][row], B = g as [row][v]).
+template <typename T, int LAYOUT>
+__global__ void __launch_bounds__(kLinThreads)
+linear_dw_kernel(const T* __restrict__ x, const T* __restrict__ g, T* __restrict__ part, int64_t n, int64_t dim_in,
+                 int64_t dim_out, LinDwTable tab) {
+  using M = Mfma<T>;
+  __shared__ T As[kLinTM][kLinTK + kLinPadA];   // [u][row]
+  __shared__ T Bs[kLinTK][kLinTN + kLinPadB];   // [row][v]
+  const int bid = blockIdx.x;
+  int pi = 0;
+  while (pi + 1 < tab.n_pairs && tab.pairs[pi + 1].tile_begin <= bid) ++pi;
+  const LinDwPair P = tab.pairs[pi];
+  int t = bid - P.tile_begin;
+  const int chunk = t / (P.u_tiles * P.v_tiles);
+  t %= P.u_tiles * P.v_tiles;
+  const int u0 = (t / P.v_tiles) * kLinTM, v0 = (t % P.v_tiles) * kLinTN;
+  const int d = P.d;
+  const int R = static_cast<int>(n) * d;
+  const int r_begin = chunk * kLinDwRows;
+  const int r_end = r_begin + kLinDwRows < R ? r_begin + kLinDwRows : R;
+  const int tid = threadIdx.x, lane = tid % 64, wave = tid / 64;
+  const int wr = wave / 2, wc = wave % 2;
+  // rows staged by this thread: A row rk_a + 4 e' ... as (sample, component),
+  // advanced by kLinTK rows per step without dividing
+  constexpr int kAStep = kLinThreads / kLinTM;   // rows of A per pass (4)
+  constexpr int kBStep = kLinThreads / kLinTN;   // rows of B per pass (2)
+  const int uu_a = tid % kLinTM, rk_a = tid / kLinTM;
+  const int vv_b = tid % kLinTN, rk_b = tid / kLinTN;
+  int a_n = (r_begin + rk_a) / d, a_m = (r_begin + rk_a) - a_n * d;
+  int b_n = (r_begin + rk_b) / d, b_m = (r_begin + rk_b) - b_n * d;
+  const int step_n = kLinTK / d, step_m = kLinTK - step_n * d;      // divmod(kLinTK, d)
+  const int sa_n = kAStep / d, sa_m = kAStep - sa_n * d;            // divmod(kAStep, d)
+  const int sb_n = kBStep / d, sb_m = kBStep - sb_n * d;            // divmod(kBStep, d)
+  typename M::acc_t acc[kMT][kNT];
+#pragma unroll
+  for (int a = 0; a < kMT; ++a)
+#pragma unroll
+    for (int b = 0; b < kNT; ++b) acc[a][b] = typename M::acc_t{0, 0, 0, 0};
+  const int u = u0 + uu_a, v = v0 + vv_b;
+  // the next chunk of rows is loaded into registers while the current one
+  // is multiplied
+  T ra[kLinTK / kAStep], rb[kLinTK / kBStep];
+  auto fetch = [&](int k0) {
+    int nn = a_n, m = a_m;
+#pragma unroll
+    for (int e = 0; e < kLinTK / kAStep; ++e) {
+      const int row = k0 + rk_a + e * kAStep;
+      T val = T(0);
+      if (row < r_end && u < P.mul_in) {
+        const int64_t off = LAYOUT == kIrMul ? P.x_off + static_cast<int64_t>(m) * P.mul_in + u
+                                             : P.x_off + static_cast<int64_t>(u) * d + m;
+        val = x[static_cast<int64_t>(nn) * dim_in + off];
+      }
+      ra[e] = val;
+      nn += sa_n;
+      m += sa_m;
+      if (m >= d) {
+        m -= d;
+        ++nn;
+      }
+    }
+    nn = b_n;
+    m = b_m;
+#pragma unroll
+    for (int e = 0; e < kLinTK / kBStep; ++e) {
+      const int row = k0 + rk_b + e * kBStep;
+      T val = T(0);
+      if (row < r_end && v < P.mul_out) {
+        const int64_t off = LAYOUT == kIrMul ? P.g_off + static_cast<int64_t>(m) * P.mul_out + v
+                                             : P.g_off + static_cast<int64_t>(v) * d + m;
+        val = g[static_cast<int64_t>(nn) * dim_out + off];
+      }
+      rb[e] = val;
+      nn += sb_n;
+      m += sb_m;
+      if (m >= d) {
+        m -= d;
+        ++nn;
+      }
+    }
+    // advance the staged rows by kLinTK for the next fetch
+    a_n += step_n;
+    a_m += step_m;
+    if (a_m >= d) {
+      a_m -= d;
+      ++a_n;
+    }
+    b_n += step_n;
+    b_m += step_m;
+    if (b_m >= d) {
+      b_m -= d;
+      ++b_n;
+    }
+  };
+  int k0 = r_begin;
+  if (k0 < r_end) fetch(k0);
+  while (k0 < r_end) {
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < kLinTK / kAStep; ++e) As[uu_a][rk_a + e * kAStep] = ra[e];
+#pragma unroll
+    for (int e = 0; e < kLinTK / kBStep; ++e) Bs[rk_b + e * kBStep][vv_b] = rb[e];
+    __syncthreads();
+    k0 += kLinTK;
+    if (k0 < r_end) fetch(k0);
+#pragma unroll
+    for (int s = 0; s < kLinTK / 4; ++s) {
+      const int kq = s * 4 + lane / 16;
+      T a[kMT], b[kNT];
+#pragma unroll
+      for (int i = 0; i < kMT; ++i) a[i] = As[wr * (kLinTM / 2) + i * 16 + lane % 16][kq];
+#pragma unroll
+      for (int j = 0; j < kNT; ++j) b[j] = Bs[kq][wc * (kLinTN / 2) + j * 16 + lane % 16];
+#pragma unroll
+      for (int i = 0; i < kMT; ++i)
+#pragma unroll
+        for (int j = 0; j < kNT; ++j) acc[i][j] = M::mma(a[i], b[j], acc[i][j]);
+    }
+  }
+  T* prow = part + P.part_off + static_cast<int64_t>(chunk) * P.mul_in * P.mul_out;
+#pragma unroll
+  for (int i = 0; i < kMT; ++i)
+#pragma unroll
+    for (int j = 0; j < kNT; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int uo = u0 + wr * (kLinTM / 2) + i * 16 + M::row(lane, q);
+        const int vo = v0 + wc * (kLinTN / 2) + j * 16 + lane % 16;
+        if (uo < P.mul_in && vo < P.mul_out) prow[static_cast<int64_t>(uo) * P.mul_out + vo] = acc[i][j][q];
+      }
+}
+
+// dw[w_off + e] = alpha * sum over the pair's chunks (in order) of part[chunk][e].
+template <typename T>
+__global__ void __launch_bounds__(256)
+linear_dw_fold_kernel(const T* __restrict__ part, LinDwTable tab, T* __restrict__ dw) {
+  const int pi = blockIdx.y;
+  const LinDwPair P = tab.pairs[pi];
+  const int64_t sz = static_cast<int64_t>(P.mul_in) * P.mul_out;
+  for (int64_t e = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; e < sz;
+       e += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    T acc = T(0);
+    for (int c = 0; c < P.chunks; ++c) acc += part[P.part_off + c * sz + e];
+    dw[P.w_off + e] = static_cast<T>(P.alpha) * acc;
+  }
+}
+
+template <typename T, int LAYOUT>
+int linear_dw_launch(const LinearDwArgs& a, const LinDwTable& tab) {
+  const hipStream_t st = static_cast<hipStream_t>(a.stream);
+  T* part = static_cast<T*>(a.workspace);
+  if (tab.total_tiles > 0)
+    hipLaunchKernelGGL((linear_dw_kernel<T, LAYOUT>), dim3(static_cast<unsigned>(tab.total_tiles)), dim3(kLinThreads),
+                       0, st, static_cast<const T*>(a.x), static_cast<const T*>(a.g), part, a.n, a.dim_in, a.dim_out,
+                       tab);
+  int rc = static_cast<int>(hipGetLastError());
+  if (rc || tab.n_pairs == 0) return rc;
+  hipLaunchKernelGGL((linear_dw_fold_kernel<T>), dim3(64, static_cast<unsigned>(tab.n_pairs)), dim3(256), 0, st,
+                     static_cast<const T*>(part), tab, static_cast<T*>(a.dw));
+  return static_cast<int>(hipGetLastError());
+}
+
+template <typename T, typename Index, int LAYOUT, bool TRANSW>
+int linear_launch(const LinearArgs& a, const LinTable& tab) {
+  if (tab.total_tiles == 0 || a.n == 0) return 0;
+  const dim3 grid(static_cast<unsigned>(tab.total_tiles));
+  const hipStream_t st = static_cast<hipStream_t>(a.stream);
+  if (a.classes)
+    hipLaunchKernelGGL((linear_kernel<T, Index, LAYOUT, TRANSW, true>), grid, dim3(kLinThreads), 0, st,
+                       static_cast<const T*>(a.x), static_cast<const T*>(a.w), static_cast<const Index*>(a.cls),
+                       static_cast<T*>(a.out), a.n, a.dim_in, a.dim_out, a.numel, a.num_classes, tab);
+  else
+    hipLaunchKernelGGL((linear_kernel<T, Index, LAYOUT, TRANSW, false>), grid, dim3(kLinThreads), 0, st,
+                       static_cast<const T*>(a.x), static_cast<const T*>(a.w), static_cast<const Index*>(a.cls),
+                       static_cast<T*>(a.out), a.n, a.dim_in, a.dim_out, a.numel, a.num_classes, tab);
+  return static_cast<int>(hipGetLastError());
+}
+
+template <typename T, bool TRANSW>
+int linear_dispatch(const LinearArgs& a, const LinTable& tab) {
+  if (a.idx == kI64) {
+    if (a.layout == kMulIr) return linear_launch<T, int64_t, kMulIr, TRANSW>(a, tab);
+    return linear_launch<T, int64_t, kIrMul, TRANSW>(a, tab);
+  }
+  if (a.layout == kMulIr) return linear_launch<T, int32_t, kMulIr, TRANSW>(a, tab);
+  return linear_launch<T, int32_t, kIrMul, TRANSW>(a, tab);
+}
+
+}  // namespace kern
+
+namespace kern {
+template <typename T>
+__global__ void __launch_bounds__(256) lin_fill_zero_kernel(T* __restrict__ p, int64_t n) {
+  for (int64_t i = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; i < n;
+       i += static_cast<int64_t>(gridDim.x) * blockDim.x)
+    p[i] = T(0);
+}
+}  // namespace kern
+
+int launch_fill_zero(void* p, int64_t n, int dtype, void* stream) {
+  using namespace kern;
+  if (n <= 0) return 0;
+  const int64_t blocks = (n + 255) / 256;
+  const dim3 grid(static_cast<unsigned>(blocks < 1024 ? blocks : 1024));
+  if (dtype == kF32)
+    hipLaunchKernelGGL((lin_fill_zero_kernel<float>), grid, dim3(256), 0, static_cast<hipStream_t>(stream),
+                       static_cast<float*>(p), n);
+  else
+    hipLaunchKernelGGL((lin_fill_zero_kernel<double>), grid, dim3(256), 0, static_cast<hipStream_t>(stream),
+                       static_cast<double*>(p), n);
+  return static_cast<int>(hipGetLastError());
+}
+
+int launch_linear_dw(const LinearDwArgs& a, const LinDwTable& tab) {
+  using namespace kern;
+  if (a.dtype == kF32)
+    return a.layout == kMulIr ? linear_dw_launch<float, kMulIr>(a, tab) : linear_dw_launch<float, kIrMul>(a, tab);
+  return a.layout == kMulIr ? linear_dw_launch<double, kMulIr>(a, tab) : linear_dw_launch<double, kIrMul>(a, tab);
+}
+
+int launch_linear(const LinearArgs& a, const LinTable& tab, bool transw) {
+  using namespace kern;
+  if (a.dtype == kF32) return transw ? linear_dispatch<float, true>(a, tab) : linear_dispatch<float, false>(a, tab);
+  return transw ? linear_dispatch<double, true>(a, tab) : linear_dispatch<double, false>(a, tab);
+}
+
+}  // namespace segpoly

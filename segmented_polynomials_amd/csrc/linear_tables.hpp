@@ -1,0 +1,89 @@
+// Tables of the equivariant linear layer shared by the C ABI (host, built
+// from the descriptor) and the MFMA kernels (passed by value as a kernel
+// argument).  One GEMM per output block: rows (sample, component), K the
+// concatenated input channels of its irrep type, columns its channels.
+#pragma once
+#include <cstdint>
+
+namespace segpoly {
+
+struct LinPair {
+  int64_t in_off;  // offset of the input block in a row
+  int64_t w_off;   // offset of the weight segment in a weight row
+  int k_ext;       // channels of the input block (the pair's share of K)
+  int pad;
+};
+
+struct LinOut {
+  int64_t out_off;  // offset of the output block in a row
+  double alpha;     // 1 / sqrt(fan-in of the block's irrep type)
+  int n_ext;        // channels of the output block
+  int d;            // 2l + 1
+  int pair_begin, pair_end;  // its pairs in LinTable::pairs
+  int tile_begin, col_tiles;  // first workgroup of its GEMM; column tiles
+};
+
+// GEMM tile of one workgroup: rows x columns (the weight-gradient GEMM:
+// input channels x output channels), shared by the launchers' grid sizes
+// and the kernels.
+constexpr int kLinTileRows = 128;
+constexpr int kLinTileCols = 128;
+
+constexpr int kLinMaxOut = 32;
+constexpr int kLinMaxPairs = 64;
+
+struct LinTable {
+  int n_out;
+  int total_tiles;
+  LinOut outs[kLinMaxOut];
+  LinPair pairs[kLinMaxPairs];
+};
+
+// Weight-gradient GEMMs of the backward: one per (input block, output
+// block) pair, split over chunks of kLinDwRows rows.
+struct LinDwPair {
+  int64_t x_off, g_off, w_off;
+  int mul_in, mul_out, d;
+  int chunks;            // row chunks of this pair
+  int64_t part_off;      // first element of its partials in the workspace
+  int tile_begin;        // first workgroup
+  int u_tiles, v_tiles;  // tiles of mul_in x mul_out
+  double alpha;
+};
+
+constexpr int kLinDwRows = 2048;
+
+struct LinDwTable {
+  int n_pairs;
+  int total_tiles;
+  LinDwPair pairs[kLinMaxPairs / 2];
+};
+
+struct LinearArgs {
+  const void* x;    // [n, dim_in] (backward dx: the output gradient)
+  const void* w;    // [1 or num_classes, numel]
+  const void* cls;  // [n] class of each sample, or null
+  void* out;        // [n, dim_out]
+  int64_t n, dim_in, dim_out, numel;
+  int num_classes;
+  int classes;      // 1: class-indexed weights
+  int dtype, idx, layout;
+  void* stream;
+};
+
+struct LinearDwArgs {
+  const void* x;  // [n, dim_in] forward input
+  const void* g;  // [n, dim_out] output gradient
+  void* dw;       // [numel]
+  void* workspace;
+  int64_t n, dim_in, dim_out, numel;
+  int dtype, layout;
+  void* stream;
+};
+
+int launch_linear(const LinearArgs& a, const LinTable& tab, bool transw);
+int launch_linear_dw(const LinearDwArgs& a, const LinDwTable& tab);
+// p[0..n) = 0 with a kernel (stream-ordered, safe under graph capture)
+int launch_fill_zero(void* p, int64_t n, int dtype, void* stream);
+
+}  // namespace segpoly

@@ -251,3 +251,29 @@ def test_symcon_backward_argument_errors_fail_before_any_gpu_call():
     assert f(s._h, p, p, p, 0, p, p, 1 << 31, p, p, p, big, None) == sp.E_UNSUPPORTED
     sg = sp.symcon_create("32x0e+32x1o", "32x0e", 3, 4, force_generic=True)
     assert f(sg._h, p, p, p, 0, p, p, 3, p, p, p, big, None) == sp.E_UNSUPPORTED
+
+
+def test_linear_descriptor_and_errors():
+    h = sp.linear_create("3x0e+2x1o", "2x0e+4x1o")
+    assert (h.dim_in, h.dim_out, h.weight_numel, h.num_segments) == (9, 14, 14, 2)
+    h2 = sp.linear_create(workloads.CONV4_OUT, "128x0e+128x1o+128x2e")
+    assert h2.dim_in == 5504 and h2.weight_numel == 13 * 128 * 128
+    # the conv's actual output irreps are what the linear workload takes
+    t = sp.tp_create(workloads.WORKLOADS[4].irreps_in1, workloads.WORKLOADS[4].irreps_in2,
+                     workloads.WORKLOADS[4].irreps_out)
+    assert t.irreps_out == workloads.CONV4_OUT
+    raw = ctypes.c_void_p()
+    assert sp.lib.linear_create(b"3x0e", b"3x0e", 7, 0, 0, ctypes.byref(raw)) == sp.E_INVALID
+    assert sp.lib.linear_create(b"3x0q", b"3x0e", 0, 0, 0, ctypes.byref(raw)) == sp.E_PARSE
+    assert sp.lib.linear_create(b"3x0e", b"3x0e", 0, 0, 1, ctypes.byref(raw)) == sp.E_INVALID   # flag
+    big = "+".join(["1x0e"] * 40)
+    assert sp.lib.linear_create(big.encode(), b"1x0e", 0, 0, 0, ctypes.byref(raw)) == sp.E_UNSUPPORTED
+    p = ctypes.c_void_p(16)
+    f = sp.lib.linear_fwd
+    assert f(h._h, p, p, None, 0, 1, -1, p, None) == sp.E_INVALID
+    assert f(h._h, p, p, p, 0, 0, 2, p, None) == sp.E_INVALID          # classes without num_classes
+    assert f(h._h, p, p, None, 0, 1, 2, None, None) == sp.E_INVALID    # null out
+    assert f(h._h, None, None, None, 0, 1, 0, None, None) == sp.OK     # nothing to do
+    b = sp.lib.linear_bwd
+    assert b(h._h, p, p, p, p, 0, 2, 2, p, p, p, 1 << 30, None) == sp.E_UNSUPPORTED   # dw with classes
+    assert b(h._h, p, p, p, None, 0, 1, 2, p, p, p, 8, None) == sp.E_INVALID          # workspace small

@@ -1,0 +1,175 @@
+"""GPU parity of the equivariant linear layer on the matrix cores (forward
+and backward), called through the C ABI, against the float64 oracle on the
+same seeded inputs.  Tolerance: scaled error (oracle.metrics) <= 1e-5 in
+float32, <= 1e-12 in float64."""
+
+import numpy as np
+import pytest
+
+import workloads
+from oracle import layout as ol
+from oracle import linear as olin
+from tests._gpu import announce, check_scaled, dev, need_gpu
+
+pytestmark = pytest.mark.gpu
+
+
+def _sp():
+    need_gpu()
+    import segmented_polynomials_amd as sp
+    return sp
+
+
+def _fwd(sp, h, x, w, classes=None):
+    import torch
+    td = torch.float32 if h.dtype == "f32" else torch.float64
+    c = None if classes is None else dev(classes)
+    out = sp.linear_fwd(h, dev(x, td), dev(w, td), classes=c, num_classes=None if classes is None else w.shape[0])
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def _bwd(sp, h, x, w, g, classes=None, need_dw=True):
+    import torch
+    td = torch.float32 if h.dtype == "f32" else torch.float64
+    c = None if classes is None else dev(classes)
+    gx, gw = sp.linear_bwd(h, dev(x, td), dev(w, td), dev(g, td), classes=c,
+                           num_classes=None if classes is None else w.shape[0], need_dw=need_dw)
+    torch.cuda.synchronize()
+    return gx.cpu().numpy(), None if gw is None else gw.cpu().numpy()
+
+
+def test_page_example_f64_both_layouts():
+    """The skill document's Linear example: 3x0 + 2x1 -> 2x0 + 4x1, 14
+    weights; mul_ir and ir_mul agree after transposition."""
+    sp = _sp()
+    ins, outs = "3x0e+2x1o", "2x0e+4x1o"
+    o = olin.Linear(ins, outs)
+    rng = np.random.default_rng(1)
+    x = rng.standard_normal((2, o.dim_in))
+    w = rng.standard_normal((1, o.weight_numel))
+    res = {}
+    for lay in ("mul_ir", "ir_mul"):
+        h = sp.linear_create(ins, outs, layout=lay, dtype="f64")
+        assert h.weight_numel == 14
+        xl = ol.transpose(x, o.inp, "mul_ir", lay)
+        announce(f"linear page example {lay}")
+        got = _fwd(sp, h, xl, w)
+        check_scaled(got, o.fwd(xl, w, layout=lay), o.fwd(xl, w, layout=lay, absolute=True), "f64", f"page {lay}")
+        res[lay] = ol.transpose(got, o.out, lay, "mul_ir")
+    assert np.allclose(res["mul_ir"], res["ir_mul"], atol=1e-14)
+
+
+@pytest.mark.parametrize("layout", ["ir_mul", "mul_ir"])
+def test_workload6_forward_and_backward(layout):
+    sp = _sp()
+    wl = workloads.WORKLOADS[6]
+    o = olin.Linear(wl.irreps_in, wl.irreps_out)
+    h = sp.linear_create(wl.irreps_in, wl.irreps_out, layout=layout)
+    inp = workloads.linear_inputs(wl, o.weight_numel, n=300)
+    g = workloads.output_gradient(300, o.dim_out, "f32", seed=61)
+    announce(f"linear workload 6 {layout} n=300")
+    got = _fwd(sp, h, inp["x"], inp["w"])
+    check_scaled(got, o.fwd(inp["x"], inp["w"], layout=layout),
+                 o.fwd(inp["x"], inp["w"], layout=layout, absolute=True), "f32", f"linear fwd {layout}")
+    gx, gw = _bwd(sp, h, inp["x"], inp["w"], g)
+    (rx, rw), (sx, sw) = (o.vjp(inp["x"], inp["w"], g, layout=layout),
+                          o.vjp(inp["x"], inp["w"], g, layout=layout, absolute=True))
+    check_scaled(gx, rx, sx, "f32", f"linear dx {layout}")
+    check_scaled(gw, rw, sw, "f32", f"linear dw {layout}")
+
+
+def test_workload6_full_size_sampled_rows():
+    sp = _sp()
+    wl = workloads.WORKLOADS[6]
+    o = olin.Linear(wl.irreps_in, wl.irreps_out)
+    h = sp.linear_create(wl.irreps_in, wl.irreps_out, layout="ir_mul")
+    inp = workloads.linear_inputs(wl, o.weight_numel)
+    announce("linear workload 6 full size")
+    got = _fwd(sp, h, inp["x"], inp["w"])
+    rows = np.unique(np.concatenate([[0, wl.n - 1], np.random.default_rng(6).integers(0, wl.n, 100)]))
+    check_scaled(got[rows], o.fwd(inp["x"][rows], inp["w"]), o.fwd(inp["x"][rows], inp["w"], absolute=True),
+                 "f32", f"linear full size ({len(rows)} rows)")
+    assert np.all(np.isfinite(got))
+
+
+@pytest.mark.parametrize("layout", ["ir_mul", "mul_ir"])
+def test_ragged_tiles(layout):
+    """Multiplicities that leave partial row, column and K tiles, two column
+    tiles, several input blocks of one type and an output type no input
+    has (zero block)."""
+    sp = _sp()
+    ins, outs = "77x0e+33x1o+20x1o+5x2e", "50x0e+130x1o+3x3o"
+    o = olin.Linear(ins, outs)
+    h = sp.linear_create(ins, outs, layout=layout)
+    rng = np.random.default_rng(9)
+    x = rng.standard_normal((37, o.dim_in), dtype=np.float32)
+    w = rng.standard_normal((1, o.weight_numel), dtype=np.float32)
+    g = rng.standard_normal((37, o.dim_out), dtype=np.float32)
+    announce(f"linear ragged {layout}")
+    got = _fwd(sp, h, x, w)
+    check_scaled(got, o.fwd(x, w, layout=layout), o.fwd(x, w, layout=layout, absolute=True), "f32", "ragged fwd")
+    gx, gw = _bwd(sp, h, x, w, g)
+    (rx, rw), (sx, sw) = o.vjp(x, w, g, layout=layout), o.vjp(x, w, g, layout=layout, absolute=True)
+    check_scaled(gx, rx, sx, "f32", "ragged dx")
+    check_scaled(gw, rw, sw, "f32", "ragged dw")
+
+
+@pytest.mark.parametrize("order", ["sorted", "unsorted"])
+def test_class_indexed(order):
+    """Species-indexed weights: sorted classes (the pages' contract) and an
+    unsorted order (still exact), an out-of-range class (zero row, zero
+    dx), int64 indices for the unsorted case."""
+    sp = _sp()
+    wl = workloads.WORKLOADS[7]
+    o = olin.Linear(wl.irreps_in, wl.irreps_out)
+    h = sp.linear_create(wl.irreps_in, wl.irreps_out, layout="ir_mul")
+    inp = workloads.linear_inputs(wl, o.weight_numel, n=400)
+    cls = inp["classes"].copy()
+    if order == "unsorted":
+        cls = np.random.default_rng(3).permutation(cls).astype(np.int64)
+    cls[5] = wl.num_classes          # out of range
+    g = workloads.output_gradient(400, o.dim_out, "f32", seed=71)
+    announce(f"linear class-indexed {order}")
+    got = _fwd(sp, h, inp["x"], inp["w"], cls)
+    check_scaled(got, o.fwd(inp["x"], inp["w"], indices=cls), o.fwd(inp["x"], inp["w"], indices=cls, absolute=True),
+                 "f32", f"class-indexed fwd {order}")
+    assert np.count_nonzero(got[5]) == 0
+    gx, gw = _bwd(sp, h, inp["x"], inp["w"], g, cls, need_dw=False)
+    assert gw is None
+    rx, _ = o.vjp(inp["x"], inp["w"], g, indices=cls)
+    sx, _ = o.vjp(inp["x"], inp["w"], g, indices=cls, absolute=True)
+    check_scaled(gx, rx, sx, "f32", f"class-indexed dx {order}")
+    assert np.count_nonzero(gx[5]) == 0
+
+
+def test_float64_backward_and_determinism():
+    sp = _sp()
+    ins, outs = "16x0e+8x1o+8x1o", "12x0e+20x1o"
+    o = olin.Linear(ins, outs)
+    h = sp.linear_create(ins, outs, layout="mul_ir", dtype="f64")
+    rng = np.random.default_rng(12)
+    x = rng.standard_normal((3000, o.dim_in))
+    w = rng.standard_normal((1, o.weight_numel))
+    g = rng.standard_normal((3000, o.dim_out))
+    announce("linear f64 backward")
+    gx, gw = _bwd(sp, h, x, w, g)
+    (rx, rw), (sx, sw) = o.vjp(x, w, g, layout="mul_ir"), o.vjp(x, w, g, layout="mul_ir", absolute=True)
+    check_scaled(gx, rx, sx, "f64", "f64 dx")
+    check_scaled(gw, rw, sw, "f64", "f64 dw (several row chunks)")
+    gx2, gw2 = _bwd(sp, h, x, w, g)
+    assert np.array_equal(gx, gx2) and np.array_equal(gw, gw2)
+
+
+def test_empty_batch():
+    sp = _sp()
+    import torch
+    h = sp.linear_create("4x0e+2x1o", "3x0e+2x1o")
+    x = torch.empty(0, h.dim_in, device="cuda")
+    w = torch.randn(1, h.weight_numel, device="cuda")
+    announce("linear empty batch")
+    out = sp.linear_fwd(h, x, w)
+    gx, gw = sp.linear_bwd(h, x, w, torch.empty(0, h.dim_out, device="cuda"))
+    torch.cuda.synchronize()
+    assert out.shape == (0, h.dim_out) and gx.shape == (0, h.dim_in)
+    assert torch.count_nonzero(gw).item() == 0

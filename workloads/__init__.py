@@ -59,6 +59,24 @@ class SymconWorkload:
     degrees: tuple = field(default=(1, 2, 3))
 
 
+@dataclass(frozen=True)
+class LinearWorkload:
+    number: int
+    name: str
+    irreps_in: str
+    irreps_out: str
+    layouts: tuple
+    dtype: str
+    n: int
+    num_classes: int = 0     # 0: shared weights; else class-indexed, classes sorted
+
+
+# the output irreps of the 600k-edge convolution (13 blocks, 5,504 values per
+# node), written out: the linear layer that follows the convolution mixes
+# them back to 128 channels per type
+CONV4_OUT = ("128x0e+128x0e+128x0e+128x1o+128x1o+128x1o+128x1o+128x1o+"
+             "128x2e+128x2e+128x2e+128x2e+128x2e")
+
 WORKLOADS = {
     1: TPWorkload(1, "single_tp_batch64_f64", "8x0e+8x1o", "0e+1o+2e",
                   "0e+0o+1e+1o+2e+2o", ("mul_ir",), "f64", "batch", batch=64,
@@ -75,6 +93,11 @@ WORKLOADS = {
     5: SymconWorkload(5, "symcon_50k_atoms_10_species", "128x0e+128x1o+128x2e+128x3o",
                       "128x0e+128x1o", ("ir_mul", "mul_ir"), "f32", n_atoms=50000,
                       num_elements=10),
+    6: LinearWorkload(6, "linear_after_conv_20k_nodes", CONV4_OUT, "128x0e+128x1o+128x2e",
+                      ("ir_mul", "mul_ir"), "f32", n=20000),
+    7: LinearWorkload(7, "species_linear_50k_atoms_10_species", "128x0e+128x1o+128x2e+128x3o",
+                      "128x0e+128x1o+128x2e+128x3o", ("ir_mul", "mul_ir"), "f32", n=50000,
+                      num_classes=10),
 }
 
 
@@ -287,3 +310,21 @@ def species_permutation(species):
     """Atom ids ordered by element, ties in atom order (a stable argsort):
     what the symmetric contraction's backward takes with the species."""
     return np.argsort(np.asarray(species), kind="stable").astype(np.asarray(species).dtype)
+
+
+def linear_inputs(wl, weight_numel, n=None, seed=None):
+    """Inputs of a linear-layer workload: x [n, dim_in] N(0,1), weights
+    N(0,1) ([1, numel] shared or [num_classes, numel]; the layer's own
+    1/sqrt(fan-in) keeps outputs at unit scale), and for class-indexed
+    weights the classes: uniform over num_classes, sorted ascending (the
+    pages' indexed linear takes sorted indices), int32."""
+    rng = np.random.default_rng(1000 + wl.number if seed is None else seed)
+    dt = _np_dtype(wl.dtype)
+    n = wl.n if n is None else n
+    x = _normal(rng, (n, _irreps_dim(wl.irreps_in)), wl.dtype).astype(dt, copy=False)
+    rows = wl.num_classes if wl.num_classes else 1
+    w = _normal(rng, (rows, weight_numel), wl.dtype).astype(dt, copy=False)
+    classes = None
+    if wl.num_classes:
+        classes = np.sort(rng.integers(0, wl.num_classes, size=n)).astype(np.int32)
+    return dict(x=x, w=w, classes=classes)
