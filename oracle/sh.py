@@ -63,3 +63,36 @@ def real_sh(ls, vecs, normalize=True):
     """Concatenation of :func:`real_sh_l` for each l in ``ls`` (the layout
     of an ``0e + 1o + 2e + ...`` operand with multiplicity one)."""
     return np.concatenate([real_sh_l(l, vecs, normalize) for l in ls], axis=-1)
+
+
+def real_sh_vjp(ls, vecs, g, normalize=True):
+    """Vector-Jacobian product of :func:`real_sh`: given g = dL/d(Y) with
+    the columns of ``real_sh(ls, vecs)``, return dL/d(vecs) [..., 3].
+
+    Without normalisation every column is a homogeneous polynomial of degree
+    l in (x, y, z), so its derivative along an axis at t = 0 of
+    Y(v + t e_a) is the derivative of a polynomial in t of degree l, which
+    the five-point quotient (8 (f(h) - f(-h)) - (f(2h) - f(-2h))) / (12 h)
+    gives exactly for l <= 4 (up to rounding).  With normalisation Y depends
+    on u = v / |v| only, and the chain rule gives
+    dY/dv = (I - u u^T) / |v| * grad P(u), P the polynomial of the
+    unnormalised harmonics (its radial part drops out)."""
+    if max(ls) > 4:
+        raise ValueError("the exact difference quotient covers l <= 4")
+    v = np.asarray(vecs, dtype=np.float64)
+    g = np.asarray(g, dtype=np.float64)
+    r = np.linalg.norm(v, axis=-1, keepdims=True)
+    base = v / r if normalize else v
+    h = 0.5 * np.maximum(np.abs(base).max(axis=-1, keepdims=True), 1e-3)
+    grad = np.zeros(v.shape[:-1] + (3,))          # grad of sum_j g_j P_j at base
+    for a in range(3):
+        e = np.zeros(3)
+        e[a] = 1.0
+        f = lambda t: np.sum(g * real_sh(ls, base + t * e, normalize=False), axis=-1)
+        grad[..., a] = (8 * (f(h[..., 0:1] * 1) - f(-h[..., 0:1] * 1)) - (f(2 * h[..., 0:1]) - f(-2 * h[..., 0:1]))) \
+            / (12 * h[..., 0])
+    if not normalize:
+        return grad
+    u = base
+    radial = np.sum(u * grad, axis=-1, keepdims=True)
+    return (grad - u * radial) / r
