@@ -128,6 +128,7 @@ def main():
     to = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
     x, sh, w = to(inp["x"]), to(inp["sh"]), to(inp["w"])
     src, dst = to(inp["src"]), to(inp["dst"])
+    vec = to(inp["vec"])
     out = torch.empty((N, h.dim_out), dtype=torch.float32, device=dev)
     # keep only what the host-side baselines need (first destination nodes)
     sample_nodes, par_nodes = 1000, 4000
@@ -194,6 +195,18 @@ def main():
                                       "hbm_fraction_of_peak": alg_bytes / (k2 * 1e-3) / 1e9 / HBM_PEAK_GBPS,
                                       "kernel": h2.kernel_name, "traffic": stored_traffic(other)}
     if not args.no_extras:
+        # the harmonics computed in the kernel from the edge vectors, against
+        # the two-call path (harmonics kernel, then the convolution)
+        fv = lambda: sp.tp_conv_fwd_vec(h, x, vec, w, src, dst, n_nodes=N, out=out)
+        wallv, perv = time_launches(torch, fv, args.steps, args.warmup)
+        shbuf = torch.empty_like(sh)
+        fs = lambda: sp.sh_fwd(vec, 3, out=shbuf)
+        walls, pers = time_launches(torch, fs, args.steps, args.warmup)
+        result["tp_conv_fused_sh"] = {"kernel_ms": sum(perv) / len(perv), "edges_per_s": E / (wallv / args.steps),
+                                      "sh_kernel_ms": sum(pers) / len(pers),
+                                      "two_call_ms": sum(pers) / len(pers) + avg_kernel_ms}
+        del shbuf
+
         # practical ceiling: a plain device copy of the weight tensor (4 GB read + 4 GB written)
         wc = torch.empty_like(w)
         cwall, cper = time_launches(torch, lambda: wc.copy_(w), max(5, args.steps // 4), 2)
@@ -210,7 +223,7 @@ def main():
 
     if not args.no_extras:
         import gc
-        del x, sh, w, src, dst
+        del x, sh, w, src, dst, vec
         gc.collect()
         torch.cuda.empty_cache()
 

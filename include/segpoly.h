@@ -215,6 +215,22 @@ int tp_conv_bwd(tp_handle h, const void* x, int64_t n_src, const void* sh, const
                 const void* grad_out, void* grad_x, void* grad_sh, void* grad_w, void* workspace,
                 size_t workspace_bytes, void* stream);
 
+/*
+ * tp_conv_fwd_vec: tp_conv_fwd with the second operand computed in the
+ * kernel from the edge vectors, as the harmonics of sh_fwd (the convolution
+ * of the pages' message passing takes sh(edge_vectors): "cuequivariance-
+ * torch" skill document, "Trainable message passing").  Input 2 of the
+ * handle must be 0e + 1o + 2e + ... + L (one copy each, L <= 6) and the
+ * descriptor specialised (E_UNSUPPORTED otherwise).
+ *   vec        [n_edges, 3] device, the handle's dtype.
+ *   normalize  != 0: harmonics of vec / |vec| (a zero vector gives Y_0 = 1,
+ *              zeros); 0: the homogeneous polynomials.
+ * Other arguments and results as tp_conv_fwd (batch mode included).
+ */
+int tp_conv_fwd_vec(tp_handle h, const void* x, int64_t n_src, const void* vec, int normalize, const void* w,
+                    const void* src, const void* dst, int idx_dtype, int64_t n_edges, int64_t n_nodes, void* out,
+                    void* stream);
+
 /* tp_destroy: free the handle (NULL is a no-op). */
 int tp_destroy(tp_handle h);
 
@@ -362,6 +378,30 @@ int linear_bwd(linear_handle h, const void* x, const void* w, const void* grad_o
 
 /* linear_destroy: free the handle (NULL is a no-op). */
 int linear_destroy(linear_handle h);
+
+/* ------------------------------------------------------- spherical harmonics */
+
+/*
+ * sh_fwd: real spherical harmonics of n vectors, degrees 0..lmax
+ * concatenated (the operand "0e + 1o + 2e + ..." of the convolution),
+ * "component" normalisation (sum over m of Y_lm^2 = 2l + 1 on the unit
+ * sphere); "cuequivariance-torch" skill document, "Spherical harmonics and a
+ * NumPy reference".  normalize != 0 evaluates on v / |v| (a zero vector
+ * gives Y_0 = 1 and zeros), normalize == 0 the homogeneous polynomial
+ * |v|^l Y_l(v / |v|).  Textbook real basis, index l^2 + l + m, m = -l..l,
+ * l = 1 is sqrt(3) (y, z, x).
+ *   vec  [n, 3] device, dtype per `dtype`.   out [n, (lmax + 1)^2] device.
+ * lmax in [0, 6] (E_UNSUPPORTED otherwise).
+ */
+int sh_fwd(int lmax, int normalize, int dtype, const void* vec, int64_t n, void* out, void* stream);
+
+/*
+ * sh_bwd: vector-Jacobian product of sh_fwd: grad_vec[i] = sum over j of
+ * grad_sh[i, j] dY_j(vec[i]) / dvec[i] (zero for a zero vector with
+ * normalisation).  grad_sh [n, (lmax + 1)^2], grad_vec [n, 3], device.
+ */
+int sh_bwd(int lmax, int normalize, int dtype, const void* vec, const void* grad_sh, int64_t n, void* grad_vec,
+           void* stream);
 
 /* segpoly_real_cg: the real coupling tensor of l1 x l2 -> l3 (the same
  * coefficients the paths use), row-major [2l1+1][2l2+1][2l3+1]. */

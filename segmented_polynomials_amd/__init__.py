@@ -30,9 +30,9 @@ _DTYPES = {"f32": F32, "f64": F64}
 
 # every symbol include/segpoly.h declares
 EXPORTS = ("tp_create", "tp_query", "tp_irreps_out", "tp_path_info", "tp_path_cg", "tp_kernel_name",
-           "tp_conv_fwd", "tp_conv_bwd_workspace", "tp_conv_bwd", "tp_destroy", "symcon_create", "symcon_query", "symcon_coupling_info",
+           "tp_conv_fwd", "tp_conv_fwd_vec", "tp_conv_bwd_workspace", "tp_conv_bwd", "tp_destroy", "symcon_create", "symcon_query", "symcon_coupling_info",
            "symcon_coupling_dense", "symcon_fwd", "symcon_bwd_workspace", "symcon_bwd", "symcon_destroy", "linear_create", "linear_query", "linear_fwd",
-           "linear_bwd_workspace", "linear_bwd", "linear_destroy", "segpoly_real_cg",
+           "linear_bwd_workspace", "linear_bwd", "linear_destroy", "sh_fwd", "sh_bwd", "segpoly_real_cg",
            "segpoly_last_error", "segpoly_version")
 
 
@@ -75,6 +75,7 @@ def _load():
         "tp_path_cg": [vp, c_int, pd],
         "tp_kernel_name": [vp, ctypes.c_char_p, ctypes.c_size_t],
         "tp_conv_fwd": [vp, vp, i64, vp, vp, vp, vp, c_int, i64, i64, vp, vp],
+        "tp_conv_fwd_vec": [vp, vp, i64, vp, c_int, vp, vp, vp, c_int, i64, i64, vp, vp],
         "tp_conv_bwd_workspace": [vp, i64, c_int, ctypes.POINTER(ctypes.c_size_t)],
         "tp_conv_bwd": [vp, vp, i64, vp, vp, vp, vp, vp, c_int, i64, i64, vp, vp, vp, vp, vp, ctypes.c_size_t, vp],
         "tp_destroy": [vp],
@@ -92,6 +93,8 @@ def _load():
         "linear_bwd_workspace": [vp, i64, ctypes.POINTER(ctypes.c_size_t)],
         "linear_bwd": [vp, vp, vp, vp, vp, c_int, c_int, i64, vp, vp, vp, ctypes.c_size_t, vp],
         "linear_destroy": [vp],
+        "sh_fwd": [c_int, c_int, c_int, vp, i64, vp, vp],
+        "sh_bwd": [c_int, c_int, c_int, vp, vp, i64, vp, vp],
         "segpoly_real_cg": [c_int, c_int, c_int, pd],
     }
     for name, args in sig.items():
@@ -247,6 +250,35 @@ def tp_conv_fwd(h, x, sh, w, src=None, dst=None, n_nodes=None, out=None):
         raise ValueError("out has the wrong shape or dtype")
     _check(lib.tp_conv_fwd(h._h, _ptr(x), n_src, _ptr(sh), _ptr(w), _ptr(src), _ptr(dst), idx, n_edges,
                            n_nodes, _ptr(out), _stream_ptr(x.device)))
+    return out
+
+
+def tp_conv_fwd_vec(h, x, vec, w, src=None, dst=None, n_nodes=None, normalize=True, out=None):
+    """tp_conv_fwd with the harmonics computed in the kernel from the edge
+    vectors vec [n_edges, 3] (input 2 must be 0e + 1o + 2e + ...)."""
+    import torch
+    t = _torch_dtype(h.dtype)
+    for name, a in (("x", x), ("vec", vec), ("w", w)):
+        if a.dtype != t or not a.is_cuda or not a.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous {t} device tensor")
+    n_src, n_edges = x.shape[0], vec.shape[0]
+    if x.shape[1] != h.dim_in1 or vec.shape[1] != 3 or w.shape[-1] != h.weight_numel:
+        raise ValueError("operand widths do not match the descriptor")
+    if w.shape[0] != (1 if h.shared_weights else n_edges):
+        raise ValueError("weights must have one row per edge (or one row when shared)")
+    idx = I32
+    if src is not None:
+        if src.shape != (n_edges,) or dst.shape != (n_edges,) or src.dtype != dst.dtype:
+            raise ValueError("src and dst must be [n_edges] of one integer dtype")
+        idx = _index_dtype(src)
+    if n_nodes is None:
+        if src is not None:
+            raise ValueError("n_nodes is required with indices")
+        n_nodes = n_edges
+    if out is None:
+        out = torch.empty((n_nodes, h.dim_out), dtype=t, device=x.device)
+    _check(lib.tp_conv_fwd_vec(h._h, _ptr(x), n_src, _ptr(vec), 1 if normalize else 0, _ptr(w), _ptr(src),
+                               _ptr(dst), idx, n_edges, n_nodes, _ptr(out), _stream_ptr(x.device)))
     return out
 
 
@@ -496,3 +528,39 @@ def linear_bwd(h, x, w, grad_out, classes=None, num_classes=None, need_dw=True, 
     _check(lib.linear_bwd(h._h, _ptr(x), _ptr(w), _ptr(grad_out), _ptr(classes), idx, nc, n, _ptr(gx), _ptr(gw),
                           _ptr(workspace), wbytes, _stream_ptr(x.device)))
     return gx, gw
+
+
+# ---------------------------------------------------------------- spherical harmonics
+
+def _sh_dtype(vec):
+    import torch
+    if vec.dtype == torch.float32:
+        return F32
+    if vec.dtype == torch.float64:
+        return F64
+    raise TypeError("vectors must be float32 or float64")
+
+
+def sh_fwd(vec, lmax, normalize=True, out=None):
+    """Real spherical harmonics of degrees 0..lmax of vec [n, 3] (device):
+    [n, (lmax + 1)^2]."""
+    import torch
+    if vec.dim() != 2 or vec.shape[1] != 3 or not vec.is_cuda or not vec.is_contiguous():
+        raise ValueError("vec must be a contiguous [n, 3] device tensor")
+    n = vec.shape[0]
+    if out is None:
+        out = torch.empty((n, (lmax + 1) ** 2), dtype=vec.dtype, device=vec.device)
+    _check(lib.sh_fwd(lmax, 1 if normalize else 0, _sh_dtype(vec), _ptr(vec), n, _ptr(out), _stream_ptr(vec.device)))
+    return out
+
+
+def sh_bwd(vec, grad_sh, lmax, normalize=True):
+    """dL/dvec [n, 3] for grad_sh = dL/dY [n, (lmax + 1)^2]."""
+    import torch
+    n = vec.shape[0]
+    if grad_sh.shape != (n, (lmax + 1) ** 2) or grad_sh.dtype != vec.dtype or not grad_sh.is_contiguous():
+        raise ValueError("grad_sh must be [n, (lmax + 1)^2] of the vectors' dtype")
+    out = torch.empty_like(vec)
+    _check(lib.sh_bwd(lmax, 1 if normalize else 0, _sh_dtype(vec), _ptr(vec), _ptr(grad_sh), n, _ptr(out),
+                      _stream_ptr(vec.device)))
+    return out

@@ -183,6 +183,12 @@ struct segpoly_symcon {
   std::map<int, DeviceBuffer> dev;
 };
 
+namespace {
+int tp_conv_fwd_impl(tp_handle h, const void* x, int64_t n_src, const void* sh, const void* vec, int normalize,
+                     const void* w, const void* src, const void* dst, int idx_dtype, int64_t n_edges,
+                     int64_t n_nodes, void* out, void* stream);
+}  // namespace
+
 extern "C" {
 
 const char* segpoly_last_error(void) { return g_last_error.c_str(); }
@@ -320,6 +326,31 @@ int tp_path_cg(tp_handle h, int p, double* out) {
 
 int tp_conv_fwd(tp_handle h, const void* x, int64_t n_src, const void* sh, const void* w, const void* src,
                 const void* dst, int idx_dtype, int64_t n_edges, int64_t n_nodes, void* out, void* stream) {
+  return tp_conv_fwd_impl(h, x, n_src, sh, nullptr, 0, w, src, dst, idx_dtype, n_edges, n_nodes, out, stream);
+}
+
+int tp_conv_fwd_vec(tp_handle h, const void* x, int64_t n_src, const void* vec, int normalize, const void* w,
+                    const void* src, const void* dst, int idx_dtype, int64_t n_edges, int64_t n_nodes, void* out,
+                    void* stream) {
+  if (!h) return fail(SEGPOLY_E_INVALID, "null handle");
+  if (!h->spec) return fail(SEGPOLY_E_UNSUPPORTED, "fused harmonics need a specialised kernel for this descriptor");
+  const auto& in2 = h->d.in2;
+  for (size_t i = 0; i < in2.size(); ++i)
+    if (in2[i].mul != 1 || in2[i].l != static_cast<int>(i) || in2[i].p != ((i % 2) ? -1 : 1))
+      return fail(SEGPOLY_E_UNSUPPORTED, "input 2 is not the harmonics 0e + 1o + 2e + ... (one copy each)");
+  if (in2.empty() || static_cast<int>(in2.size()) - 1 > kShMaxL)
+    return fail(SEGPOLY_E_UNSUPPORTED, "harmonics degree outside [0, 6]");
+  if (n_edges > 0 && !vec) return fail(SEGPOLY_E_INVALID, "null vec");
+  return tp_conv_fwd_impl(h, x, n_src, nullptr, vec ? vec : reinterpret_cast<const void*>(16), normalize, w, src,
+                          dst, idx_dtype, n_edges, n_nodes, out, stream);
+}
+
+}  // extern "C"
+
+namespace {
+int tp_conv_fwd_impl(tp_handle h, const void* x, int64_t n_src, const void* sh, const void* vec, int normalize,
+                     const void* w, const void* src, const void* dst, int idx_dtype, int64_t n_edges,
+                     int64_t n_nodes, void* out, void* stream) {
   if (!h) return fail(SEGPOLY_E_INVALID, "null handle");
   if (n_src < 0 || n_edges < 0 || n_nodes < 0) return fail(SEGPOLY_E_INVALID, "negative size");
   if (idx_dtype != SEGPOLY_I32 && idx_dtype != SEGPOLY_I64) return fail(SEGPOLY_E_INVALID, "bad index dtype");
@@ -335,7 +366,7 @@ int tp_conv_fwd(tp_handle h, const void* x, int64_t n_src, const void* sh, const
   if (n_nodes == 0 || d.dimo == 0) return ok();
   if (!out) return fail(SEGPOLY_E_INVALID, "null out");
   if (n_edges > 0) {
-    if (!sh && d.dim2 > 0) return fail(SEGPOLY_E_INVALID, "null sh");
+    if (!sh && !vec && d.dim2 > 0) return fail(SEGPOLY_E_INVALID, "null sh");
     if (!w) return fail(SEGPOLY_E_INVALID, "null w");
     if (!x && n_src > 0) return fail(SEGPOLY_E_INVALID, "null x");
   }
@@ -361,9 +392,13 @@ int tp_conv_fwd(tp_handle h, const void* x, int64_t n_src, const void* sh, const
   a.idx = idx_dtype;
   a.layout = h->layout;
   a.stream = stream;
+  a.vec = vec;
+  a.sh_normalize = normalize ? 1 : 0;
+  a.sh_consts = &sh_consts();
   int rc;
   if (h->spec) {
     rc = h->spec->launch(a);
+    if (rc == -2) return fail(SEGPOLY_E_UNSUPPORTED, "input 2 of this descriptor is not a harmonics set");
   } else {
     const size_t bp = h->gpaths.size() * sizeof(GPath);
     int st = SEGPOLY_OK;
@@ -384,6 +419,10 @@ int tp_conv_fwd(tp_handle h, const void* x, int64_t n_src, const void* sh, const
     return fail(SEGPOLY_E_HIP, std::string("kernel launch failed: ") + hipGetErrorString(static_cast<hipError_t>(rc)));
   return ok();
 }
+
+}  // namespace
+
+extern "C" {
 
 // Messages [n_edges][DIM_IN1] (indexed mode), then 256-byte aligned the
 // harmonic-gradient partials [tiles][n_edges][DIM_IN2] when one wave of

@@ -21,4 +21,8 @@ inline int ok() {
 
 constexpr int64_t kMaxGridX = 2147483647;
 
+struct ShConsts;
+// normalisation constants of the real harmonics (capi_sh.cpp)
+const ShConsts& sh_consts();
+
 }  // namespace segpoly

@@ -36,6 +36,7 @@
 
 #include "../launch.hpp"
 #include "common.hpp"
+#include "sh.hpp"
 
 namespace segpoly {
 namespace kern {
@@ -81,11 +82,21 @@ __device__ __forceinline__ void edge_range(const Index* __restrict__ dst, int64_
 // Requires mul % CPL == 0 and x, w, out aligned to CPL * sizeof(T).  NTS:
 // non-temporal output stores (measured neutral on the 600k-edge graph, so
 // off by default).
-template <class S, typename T, typename Index, int LAYOUT, int CPL, bool NTS = false>
+// l_max of a harmonics operand of width (l_max + 1)^2
+constexpr int sh_lmax_of(int d2) {
+  int l = 0;
+  while ((l + 2) * (l + 2) <= d2) ++l;
+  return l;
+}
+
+// SHV: the second operand is computed from the edge vectors vec [n_edges, 3]
+// (degrees 0..L with D2 = (L + 1)^2) as the edge's operands are loaded.
+template <class S, typename T, typename Index, int LAYOUT, int CPL, bool NTS = false, bool SHV = false>
 __global__ void __launch_bounds__(kWave)
 tp_conv_kernel(const T* __restrict__ x, const T* __restrict__ sh, const T* __restrict__ w,
                const Index* __restrict__ src, const Index* __restrict__ dst, int64_t n_src, int64_t n_edges,
-               int64_t w_stride, int mul, int batch, T* __restrict__ out) {
+               int64_t w_stride, int mul, int batch, T* __restrict__ out, const T* __restrict__ vec = nullptr,
+               int sh_normalize = 0, ShConsts shk = {}) {
   const int64_t node = blockIdx.x;
   const int ub = blockIdx.y * (kWave * CPL) + threadIdx.x * CPL;
   const bool active = ub < mul;
@@ -116,9 +127,15 @@ tp_conv_kernel(const T* __restrict__ x, const T* __restrict__ sh, const T* __res
         wv[0][p] = __builtin_nontemporal_load(wrow + p * mul);
       }
     }
-    const T* shrow = sh + e * S::D2;
+    if constexpr (SHV) {
+      static_assert((sh_lmax_of(S::D2) + 1) * (sh_lmax_of(S::D2) + 1) == S::D2, "operand 2 is not a harmonics set");
+      const T* vr = vec + e * 3;
+      sh_eval<T, sh_lmax_of(S::D2)>(vr[0], vr[1], vr[2], sh_normalize != 0, shk, shv);
+    } else {
+      const T* shrow = sh + e * S::D2;
 #pragma unroll
-    for (int j = 0; j < S::D2; ++j) shv[j] = shrow[j];
+      for (int j = 0; j < S::D2; ++j) shv[j] = shrow[j];
+    }
   };
 
   // next edge's operands (in flight while the current edge is computed)
@@ -162,6 +179,19 @@ template <class S, typename T, typename Index, int LAYOUT, int CPL, bool NTS = f
 int tp_conv_launch(const TPArgs& a) {
   const int per_tile = kWave * CPL;
   dim3 grid(static_cast<unsigned>(a.n_nodes), static_cast<unsigned>((a.mul + per_tile - 1) / per_tile));
+  if (a.vec) {
+    constexpr bool is_sh = (sh_lmax_of(S::D2) + 1) * (sh_lmax_of(S::D2) + 1) == S::D2 && sh_lmax_of(S::D2) <= kShMaxL;
+    if constexpr (is_sh) {
+      hipLaunchKernelGGL((tp_conv_kernel<S, T, Index, LAYOUT, CPL, NTS, true>), grid, dim3(kWave), 0,
+                         static_cast<hipStream_t>(a.stream), static_cast<const T*>(a.x), nullptr,
+                         static_cast<const T*>(a.w), static_cast<const Index*>(a.src),
+                         static_cast<const Index*>(a.dst), a.n_src, a.n_edges, a.w_stride, a.mul, a.batch,
+                         static_cast<T*>(a.out), static_cast<const T*>(a.vec), a.sh_normalize, *a.sh_consts);
+      return static_cast<int>(hipGetLastError());
+    } else {
+      return -2;  // operand 2 is not a harmonics set
+    }
+  }
   hipLaunchKernelGGL((tp_conv_kernel<S, T, Index, LAYOUT, CPL, NTS>), grid, dim3(kWave), 0,
                      static_cast<hipStream_t>(a.stream), static_cast<const T*>(a.x),
                      static_cast<const T*>(a.sh), static_cast<const T*>(a.w),

@@ -22,6 +22,11 @@ struct TPArgs {
   int batch;          // 1: batch mode, edge e feeds row e (src, dst unused)
   int dtype, idx, layout;
   void* stream;
+  // fused harmonics: with `vec` ([n_edges, 3]) set, sh is computed in the
+  // kernel from the edge vectors (degrees 0..L, D2 = (L+1)^2) instead of read
+  const void* vec;
+  int sh_normalize;
+  const struct ShConsts* sh_consts;
 };
 
 // Backward of the TP-conv (per-edge weights, specialised kernels only).
@@ -72,6 +77,29 @@ struct SymconBwdArgs {
   int dtype, idx, layout;
   void* stream;
 };
+
+constexpr int kShMaxL = 6;
+
+// N_l0 and sqrt2 N_lm (m > 0) of the real harmonics at index l (l + 1) / 2 + m,
+// computed on the host in extended precision.
+struct ShConsts {
+  double c[(kShMaxL + 1) * (kShMaxL + 2) / 2];
+};
+
+// Spherical harmonics of vectors: forward (grad null: out = Y [n, (lmax+1)^2])
+// or vector-Jacobian product (out = dL/dv [n, 3] for grad = dL/dY).
+struct ShArgs {
+  const void* vec;   // [n, 3]
+  const void* grad;  // [n, (lmax + 1)^2] or null
+  void* out;
+  int64_t n;
+  int lmax;
+  int normalize;
+  int dtype;
+  const ShConsts* consts;
+  void* stream;
+};
+int launch_sh(const ShArgs& a);
 
 // Workspace layouts of the backward calls, shared by the C ABI (sizes) and
 // the launchers (offsets).

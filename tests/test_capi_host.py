@@ -277,3 +277,14 @@ def test_linear_descriptor_and_errors():
     b = sp.lib.linear_bwd
     assert b(h._h, p, p, p, p, 0, 2, 2, p, p, p, 1 << 30, None) == sp.E_UNSUPPORTED   # dw with classes
     assert b(h._h, p, p, p, None, 0, 1, 2, p, p, p, 8, None) == sp.E_INVALID          # workspace small
+
+
+def test_sh_argument_errors():
+    p = ctypes.c_void_p(16)
+    assert sp.lib.sh_fwd(7, 1, 0, p, 4, p, None) == sp.E_UNSUPPORTED
+    assert sp.lib.sh_fwd(-1, 1, 0, p, 4, p, None) == sp.E_UNSUPPORTED
+    assert sp.lib.sh_fwd(3, 1, 5, p, 4, p, None) == sp.E_INVALID
+    assert sp.lib.sh_fwd(3, 1, 0, p, -4, p, None) == sp.E_INVALID
+    assert sp.lib.sh_fwd(3, 1, 0, None, 4, p, None) == sp.E_INVALID
+    assert sp.lib.sh_bwd(3, 1, 0, p, None, 4, p, None) == sp.E_INVALID
+    assert sp.lib.sh_fwd(3, 1, 0, None, 0, None, None) == sp.OK

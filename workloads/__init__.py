@@ -227,7 +227,8 @@ def tp_inputs(wl, fan_in=None, n_nodes=None, degree=None, graph=None, seed=None)
     by 1/sqrt(fan_in) when the workload asks for it.  ``n_nodes``/``degree``
     shrink a "graph" workload keeping its structure; ``graph="ragged"``
     replaces it by :func:`ragged_graph` with max in-degree ``degree``.
-    Returns dict(x, sh, w, src, dst, n_nodes, n_src)."""
+    Returns dict(x, sh, w, src, dst, n_nodes, n_src, vec); vec holds the
+    edge vectors the harmonics were computed from (cast to the run dtype)."""
     rng = np.random.default_rng(1000 + wl.number if seed is None else seed)
     dt = _np_dtype(wl.dtype)
     if wl.kind == "batch":
@@ -256,7 +257,7 @@ def tp_inputs(wl, fan_in=None, n_nodes=None, degree=None, graph=None, seed=None)
     if wl.fan_in_scaled:
         w = w * (1.0 / np.sqrt(fan_in)).astype(w.dtype)
     w = w.astype(dt, copy=False)
-    out = dict(x=x, sh=sh, w=w, n_nodes=n_out, n_src=n_src, src=None, dst=None)
+    out = dict(x=x, sh=sh, w=w, n_nodes=n_out, n_src=n_src, src=None, dst=None, vec=vec.astype(dt))
     if src is not None:
         out["src"] = src.astype(np.int32)
         out["dst"] = dst.astype(np.int32)
