@@ -87,7 +87,7 @@ class ChannelwiseTP:
         return np.concatenate([np.full(mul, cnt[(lo, po)]) for mul, lo, po in self.out])
 
     def conv(self, x, sh, w, src=None, dst=None, n_nodes=None, layout="mul_ir",
-             absolute=False, nodes=None):
+             absolute=False, nodes=None, reduce="sum"):
         """Gather, couple and sum-scatter.
 
         x   [n_src, dim_in1] in ``layout``;  sh [n_edges, dim_in2];
@@ -97,7 +97,12 @@ class ChannelwiseTP:
         absolute use |x|, |sh|, |w| and |C| (the forward-error scale);
         nodes    optional sorted array of destination rows to compute: only
                  edges whose dst is listed contribute and the result has
-                 len(nodes) rows in that order.
+                 len(nodes) rows in that order;
+        reduce   "sum", or "mean": each destination row divided by the number
+                 of edges whose dst it is (rows without edges stay zero) --
+                 the ``reduce="mean"`` option of the pages' convolution layer
+                 (cuequivariance-torch skill document, "Other operations and
+                 layers").
         Returns float64 [n_nodes or len(nodes), dim_out] in ``layout``."""
         x = np.asarray(x, dtype=np.float64)
         sh = np.asarray(sh, dtype=np.float64)
@@ -139,10 +144,16 @@ class ChannelwiseTP:
             np.add.at(blk, dst, m)                       # sum-scatter (index_add)
             out_parts.append(blk)
             woff += mul
+        if reduce == "mean":
+            deg = np.bincount(dst, minlength=n_rows)[:n_rows].astype(np.float64)
+            inv = np.where(deg > 0, 1.0 / np.maximum(deg, 1.0), 0.0)
+            out_parts = [b * inv[:, None, None] for b in out_parts]
+        elif reduce != "sum":
+            raise ValueError("reduce is 'sum' or 'mean'")
         return join_blocks(out_parts, layout)
 
     def conv_vjp(self, x, sh, w, src, dst, n_nodes, g, layout="mul_ir", shared_weights=False,
-                 absolute=False):
+                 absolute=False, reduce="sum"):
         """Vector-Jacobian product of :meth:`conv` (per-edge weights, or one
         shared row with ``shared_weights``): given g = dL/d(out) [n_nodes,
         dim_out] in ``layout``, return (dL/dx [n_src, dim_in1] in ``layout``,
@@ -155,7 +166,9 @@ class ChannelwiseTP:
             dx[src_e, blk1_p, i, u] += w[e, p, u] sum_jk C[i,j,k] sh[e, j] g[dst_e, p, k, u]
 
         ``absolute`` evaluates the same sums over |x|, |sh|, |w|, |g| and |C|:
-        the scale of the rounding error of any summation order."""
+        the scale of the rounding error of any summation order.  With
+        reduce="mean" the output row n is the sum over its edges divided by
+        their number, so g[n] enters divided by it."""
         x = np.asarray(x, dtype=np.float64)
         sh = np.asarray(sh, dtype=np.float64)
         w = np.asarray(w, dtype=np.float64)
@@ -168,6 +181,11 @@ class ChannelwiseTP:
             dst = np.arange(n_edges)
         src = np.asarray(src, dtype=np.int64)
         dst = np.asarray(dst, dtype=np.int64)
+        if reduce == "mean":
+            deg = np.bincount(dst, minlength=g.shape[0])[:g.shape[0]].astype(np.float64)
+            g = g * np.where(deg > 0, 1.0 / np.maximum(deg, 1.0), 0.0)[:, None]
+        elif reduce != "sum":
+            raise ValueError("reduce is 'sum' or 'mean'")
         x1 = split_blocks(x, self.in1, layout)          # per block [n_src, 2l+1, mul]
         x2 = split_blocks(sh, self.in2, "ir_mul")       # per block [n_edges, 2l+1, 1]
         gb = split_blocks(g, self.out, layout)          # per path [n_nodes, 2lo+1, mul]

@@ -169,3 +169,29 @@ def test_fan_in_from_string_matches_descriptor():
         wl = workloads.WORKLOADS[n]
         d = tp.ChannelwiseTP(wl.irreps_in1, wl.irreps_in2, wl.irreps_out)
         assert np.array_equal(workloads.fan_in_from_irreps_out(d.irreps_out), d.weight_fan_in())
+
+
+def test_mean_reduction():
+    """reduce="mean": a destination with identical incoming messages gets
+    that message; in general mean = sum / in-degree, isolated rows zero, and
+    the VJP is the sum's VJP with g divided by the in-degree (checked by the
+    adjoint identity in x)."""
+    d = tp.ChannelwiseTP("3x0e+2x1o", "0e+1o", "0e+1o")
+    rng = np.random.default_rng(31)
+    x = rng.normal(size=(5, d.dim_in1))
+    sh = rng.normal(size=(1, d.dim_in2)).repeat(4, axis=0)
+    w = rng.normal(size=(1, d.weight_numel)).repeat(4, axis=0)
+    src = np.array([2, 2, 2, 4])
+    dst = np.array([0, 0, 0, 3])
+    mean = d.conv(x, sh, w, src, dst, 5, reduce="mean")
+    one = d.conv(x, sh[:1], w[:1], src[:1], np.array([0]), 1)
+    assert np.allclose(mean[0], one[0], atol=1e-13)
+    s = d.conv(x, sh, w, src, dst, 5)
+    assert np.allclose(mean[3], s[3]) and np.count_nonzero(mean[[1, 2, 4]]) == 0
+    assert np.allclose(mean[0] * 3, s[0], atol=1e-13)
+    g = rng.normal(size=(5, d.dim_out))
+    dx, dsh, dw = d.conv_vjp(x, sh, w, src, dst, 5, g, reduce="mean")
+    vx = rng.normal(size=x.shape)
+    assert np.isclose(np.sum(g * d.conv(vx, sh, w, src, dst, 5, reduce="mean")), np.sum(dx * vx), rtol=1e-12)
+    vw = rng.normal(size=w.shape)
+    assert np.isclose(np.sum(g * d.conv(x, sh, vw, src, dst, 5, reduce="mean")), np.sum(dw * vw), rtol=1e-12)
