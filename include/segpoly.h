@@ -72,6 +72,10 @@ extern "C" {
 #define SEGPOLY_SHARED_WEIGHTS 1u /* weights are one row [1, numel] shared by every edge */
 #define SEGPOLY_VALIDATE 2u       /* check index ranges and dst order on the host (synchronises) */
 #define SEGPOLY_FORCE_GENERIC 4u  /* use the table-driven kernel even if a specialised one exists */
+#define SEGPOLY_REDUCE_MEAN 8u    /* convolution: each output row is the mean over its edges, not the sum
+                                     (rows without edges stay zero); the convolution layer's reduce="mean"
+                                     of the "cuequivariance-torch" skill document, "Other operations and
+                                     layers".  The backward takes the same flag from the handle. */
 
 /* query keys */
 #define SEGPOLY_Q_DIM_IN1 0

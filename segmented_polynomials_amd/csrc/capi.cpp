@@ -213,7 +213,7 @@ int tp_create(const char* in1, const char* in2, const char* outs, int layout, in
   if (!in1 || !in2 || !outs) return fail(SEGPOLY_E_INVALID, "null irreps string");
   if (layout != SEGPOLY_MUL_IR && layout != SEGPOLY_IR_MUL) return fail(SEGPOLY_E_INVALID, "bad layout");
   if (dtype != SEGPOLY_F32 && dtype != SEGPOLY_F64) return fail(SEGPOLY_E_INVALID, "bad dtype");
-  if (flags & ~(SEGPOLY_SHARED_WEIGHTS | SEGPOLY_VALIDATE | SEGPOLY_FORCE_GENERIC))
+  if (flags & ~(SEGPOLY_SHARED_WEIGHTS | SEGPOLY_VALIDATE | SEGPOLY_FORCE_GENERIC | SEGPOLY_REDUCE_MEAN))
     return fail(SEGPOLY_E_INVALID, "unknown flag bits");
   segpoly_tp* h = nullptr;
   try {
@@ -388,6 +388,7 @@ int tp_conv_fwd_impl(tp_handle h, const void* x, int64_t n_src, const void* sh, 
   a.w_stride = (h->flags & SEGPOLY_SHARED_WEIGHTS) ? 0 : d.numel;
   a.mul = d.uniform_mul ? d.mul : 0;
   a.batch = batch ? 1 : 0;
+  a.mean = (h->flags & SEGPOLY_REDUCE_MEAN) ? 1 : 0;
   a.dtype = h->dtype;
   a.idx = idx_dtype;
   a.layout = h->layout;
@@ -498,6 +499,7 @@ int tp_conv_bwd(tp_handle h, const void* x, int64_t n_src, const void* sh, const
   a.n_nodes = n_nodes;
   a.mul = d.mul;
   a.batch = batch ? 1 : 0;
+  a.mean = (h->flags & SEGPOLY_REDUCE_MEAN) ? 1 : 0;
   a.dtype = h->dtype;
   a.idx = idx_dtype;
   a.layout = h->layout;

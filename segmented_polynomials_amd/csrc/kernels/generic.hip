@@ -24,7 +24,7 @@ tp_conv_generic_kernel(const T* __restrict__ x, const T* __restrict__ sh, const 
                        const Index* __restrict__ src, const Index* __restrict__ dst,
                        const GPath* __restrict__ paths, const GNz* __restrict__ nz, int np, int nk,
                        int64_t dim1, int64_t dim2, int64_t dimo, int64_t n_src, int64_t n_edges,
-                       int64_t w_stride, int batch, T* __restrict__ out) {
+                       int64_t w_stride, int batch, int mean, T* __restrict__ out) {
   extern __shared__ unsigned char smem_raw[];
   T* acc = reinterpret_cast<T*>(smem_raw);
   const int64_t node = blockIdx.x;
@@ -55,12 +55,13 @@ tp_conv_generic_kernel(const T* __restrict__ x, const T* __restrict__ sh, const 
     }
   }
   T* orow = out + node * dimo;
+  const T scale = (mean && e1 > e0) ? T(1) / static_cast<T>(e1 - e0) : T(1);
   for (int p = 0; p < np; ++p) {
     const GPath P = paths[p];
     if (u >= P.mul) continue;
     const int dl = 2 * P.lo + 1;
     for (int k = 0; k < dl; ++k) {
-      const T v = acc[(P.kcomp + k) * kGW + lane];
+      const T v = scale * acc[(P.kcomp + k) * kGW + lane];
       if (LAYOUT == kIrMul)
         orow[P.offo + static_cast<int64_t>(k) * P.mul + u] = v;
       else
@@ -77,7 +78,7 @@ int tp_generic_launch(const TPArgs& a, const GenericTPInfo& g) {
                      static_cast<hipStream_t>(a.stream), static_cast<const T*>(a.x),
                      static_cast<const T*>(a.sh), static_cast<const T*>(a.w),
                      static_cast<const Index*>(a.src), static_cast<const Index*>(a.dst), g.paths, g.nz,
-                     g.np, g.nk, g.dim1, g.dim2, g.dimo, a.n_src, a.n_edges, a.w_stride, a.batch,
+                     g.np, g.nk, g.dim1, g.dim2, g.dimo, a.n_src, a.n_edges, a.w_stride, a.batch, a.mean,
                      static_cast<T*>(a.out));
   return static_cast<int>(hipGetLastError());
 }

@@ -90,8 +90,8 @@ template <class S, typename T, typename Index, int LAYOUT, int CPL>
 __global__ void __launch_bounds__(kWave)
 tp_bwd_edge_kernel(const T* __restrict__ x, const T* __restrict__ sh, const T* __restrict__ w,
                    const Index* __restrict__ src, const Index* __restrict__ dst, const T* __restrict__ g,
-                   int64_t n_src, int64_t n_edges, int64_t n_nodes, int mul, int batch, T* __restrict__ dw,
-                   T* __restrict__ dsh_out, T* __restrict__ msg) {
+                   int64_t n_src, int64_t n_edges, int64_t n_nodes, int mul, int batch, int mean,
+                   T* __restrict__ dw, T* __restrict__ dsh_out, T* __restrict__ msg) {
   constexpr int DP = Pow2Ceil<S::D2>::value;
   constexpr bool PF = CPL == 2;
   const int64_t node = blockIdx.x;
@@ -133,6 +133,13 @@ tp_bwd_edge_kernel(const T* __restrict__ x, const T* __restrict__ sh, const T* _
 
   T gv[CPL][S::NK];
   S::template load_gs<T, LAYOUT, CPL>(g + node * (static_cast<int64_t>(mul) * S::NK), mul, ubl, gv);
+  if (mean && e1 > e0) {  // the forward divided the row by its number of edges
+    const T inv = T(1) / static_cast<T>(e1 - e0);
+#pragma unroll
+    for (int c = 0; c < CPL; ++c)
+#pragma unroll
+      for (int k = 0; k < S::NK; ++k) gv[c][k] *= inv;
+  }
 
   auto source = [&](int64_t e) -> int64_t { return batch ? e : static_cast<int64_t>(src[e]); };
   auto load = [&](int64_t e, int64_t s, T (&xv)[CPL][S::NX], T (&wv)[CPL][S::NP], T (&shv)[S::D2]) {
@@ -328,7 +335,7 @@ int tp_bwd_launch(const TPBwdArgs& a) {
                      dim3(static_cast<unsigned>(a.n_nodes), static_cast<unsigned>(tiles)), dim3(kWave), 0, st,
                      static_cast<const T*>(a.x), static_cast<const T*>(a.sh), static_cast<const T*>(a.w),
                      static_cast<const Index*>(a.src), static_cast<const Index*>(a.dst), static_cast<const T*>(a.g),
-                     a.n_src, a.n_edges, a.n_nodes, a.mul, a.batch, static_cast<T*>(a.dw), part, msg);
+                     a.n_src, a.n_edges, a.n_nodes, a.mul, a.batch, a.mean, static_cast<T*>(a.dw), part, msg);
   int rc = static_cast<int>(hipGetLastError());
   if (rc) return rc;
   if (tiles > 1) {

@@ -95,8 +95,8 @@ template <class S, typename T, typename Index, int LAYOUT, int CPL, bool NTS = f
 __global__ void __launch_bounds__(kWave)
 tp_conv_kernel(const T* __restrict__ x, const T* __restrict__ sh, const T* __restrict__ w,
                const Index* __restrict__ src, const Index* __restrict__ dst, int64_t n_src, int64_t n_edges,
-               int64_t w_stride, int mul, int batch, T* __restrict__ out, const T* __restrict__ vec = nullptr,
-               int sh_normalize = 0, ShConsts shk = {}) {
+               int64_t w_stride, int mul, int batch, int mean, T* __restrict__ out,
+               const T* __restrict__ vec = nullptr, int sh_normalize = 0, ShConsts shk = {}) {
   const int64_t node = blockIdx.x;
   const int ub = blockIdx.y * (kWave * CPL) + threadIdx.x * CPL;
   const bool active = ub < mul;
@@ -171,6 +171,13 @@ tp_conv_kernel(const T* __restrict__ x, const T* __restrict__ sh, const T* __res
       S::template edge<T, CPL>(xc, shc, wc, acc);
   }
 
+  if (mean && e1 > e0) {  // reduce="mean": divide by the node's number of edges
+    const T inv = T(1) / static_cast<T>(e1 - e0);
+#pragma unroll
+    for (int c = 0; c < CPL; ++c)
+#pragma unroll
+      for (int k = 0; k < S::NK; ++k) acc[c][k] *= inv;
+  }
   if (active)
     S::template store_s<T, LAYOUT, CPL, NTS>(out + node * (static_cast<int64_t>(mul) * S::NK), mul, ub, acc);
 }
@@ -185,7 +192,7 @@ int tp_conv_launch(const TPArgs& a) {
       hipLaunchKernelGGL((tp_conv_kernel<S, T, Index, LAYOUT, CPL, NTS, true>), grid, dim3(kWave), 0,
                          static_cast<hipStream_t>(a.stream), static_cast<const T*>(a.x), nullptr,
                          static_cast<const T*>(a.w), static_cast<const Index*>(a.src),
-                         static_cast<const Index*>(a.dst), a.n_src, a.n_edges, a.w_stride, a.mul, a.batch,
+                         static_cast<const Index*>(a.dst), a.n_src, a.n_edges, a.w_stride, a.mul, a.batch, a.mean,
                          static_cast<T*>(a.out), static_cast<const T*>(a.vec), a.sh_normalize, *a.sh_consts);
       return static_cast<int>(hipGetLastError());
     } else {
@@ -196,7 +203,7 @@ int tp_conv_launch(const TPArgs& a) {
                      static_cast<hipStream_t>(a.stream), static_cast<const T*>(a.x),
                      static_cast<const T*>(a.sh), static_cast<const T*>(a.w),
                      static_cast<const Index*>(a.src), static_cast<const Index*>(a.dst), a.n_src,
-                     a.n_edges, a.w_stride, a.mul, a.batch, static_cast<T*>(a.out));
+                     a.n_edges, a.w_stride, a.mul, a.batch, a.mean, static_cast<T*>(a.out));
   return static_cast<int>(hipGetLastError());
 }
 

@@ -20,6 +20,7 @@ struct TPArgs {
   int64_t w_stride;   // numel, or 0 for shared weights
   int mul;            // channels of every input-1 block (specialised kernels)
   int batch;          // 1: batch mode, edge e feeds row e (src, dst unused)
+  int mean;           // 1: each output row divided by its number of edges
   int dtype, idx, layout;
   void* stream;
   // fused harmonics: with `vec` ([n_edges, 3]) set, sh is computed in the
@@ -45,6 +46,7 @@ struct TPBwdArgs {
   int64_t n_src, n_edges, n_nodes;
   int mul;
   int batch;
+  int mean;           // 1: the forward divided each row by its number of edges
   int dtype, idx, layout;
   void* stream;
 };

@@ -245,3 +245,25 @@ def test_equivariance_on_gpu():
     a = _run(sp, h, base)
     b = _run(sp, h, rot)
     assert np.allclose(b, a @ wigner.wigner_d_irreps(o.out, aa).T, atol=1e-11)
+
+
+@pytest.mark.parametrize("force_generic", [False, True])
+def test_mean_reduction(force_generic):
+    """reduce="mean" on a ragged graph with isolated destinations (those
+    rows stay zero), specialised and generic kernels."""
+    sp = _sp()
+    wl = workloads.WORKLOADS[4]
+    in1 = "32x0e+32x1o+32x2e"
+    o = otp.ChannelwiseTP(in1, wl.irreps_in2, wl.irreps_out)
+    h = sp.tp_create(in1, wl.irreps_in2, wl.irreps_out, layout="ir_mul", reduce="mean",
+                     force_generic=force_generic)
+    wl2 = workloads.TPWorkload(**{**wl.__dict__, "irreps_in1": in1})
+    inp = workloads.tp_inputs(wl2, o.weight_fan_in(), n_nodes=120, degree=20, graph="ragged", seed=77)
+    announce(f"tp mean reduction generic={force_generic}")
+    got = _run(sp, h, inp)
+    args = (inp["x"], inp["sh"], inp["w"], inp["src"], inp["dst"], inp["n_nodes"])
+    ref = o.conv(*args, layout="ir_mul", reduce="mean")
+    scale = o.conv(*args, layout="ir_mul", absolute=True, reduce="mean")
+    check_scaled(got, ref, scale, "f32", f"mean generic={force_generic}")
+    iso = np.bincount(inp["dst"], minlength=120) == 0
+    assert iso.any() and np.count_nonzero(got[iso]) == 0

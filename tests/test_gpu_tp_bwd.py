@@ -210,3 +210,18 @@ def test_deterministic_and_layouts_agree():
     assert np.array_equal(c[1], a[1])
 
 
+
+
+def test_mean_reduction_backward():
+    sp = _sp()
+    wl = workloads.WORKLOADS[4]
+    o = otp.ChannelwiseTP(wl.irreps_in1, wl.irreps_in2, wl.irreps_out)
+    h = sp.tp_create(wl.irreps_in1, wl.irreps_in2, wl.irreps_out, layout="ir_mul", reduce="mean")
+    inp = workloads.tp_inputs(wl, o.weight_fan_in(), n_nodes=150, degree=12, graph="ragged", seed=78)
+    g = workloads.output_gradient(150, o.dim_out, "f32", seed=79)
+    announce("tp bwd mean reduction")
+    got = _bwd(sp, h, inp, g)
+    args = (inp["x"], inp["sh"], inp["w"], inp["src"], inp["dst"], inp["n_nodes"], g)
+    ref = o.conv_vjp(*args, layout="ir_mul", reduce="mean")
+    scale = o.conv_vjp(*args, layout="ir_mul", absolute=True, reduce="mean")
+    _check_all(got, ref, scale, "f32", "mean reduction")
