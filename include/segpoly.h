@@ -95,6 +95,7 @@ extern "C" {
 typedef struct segpoly_tp* tp_handle;
 typedef struct segpoly_symcon* symcon_handle;
 typedef struct segpoly_linear* linear_handle;
+typedef struct segpoly_fctp* fctp_handle;
 
 /* ------------------------------------------------------------------ TP */
 
@@ -382,6 +383,66 @@ int linear_bwd(linear_handle h, const void* x, const void* w, const void* grad_o
 
 /* linear_destroy: free the handle (NULL is a no-op). */
 int linear_destroy(linear_handle h);
+
+/* ------------------------------------------------- fully connected product */
+
+/*
+ * fctp_create: the fully connected ("uvw") tensor product
+ * irreps_in1 x irreps_in2 -> irreps_out ("cuequivariance-torch" skill
+ * document, "CPU tensor product and backward" and "Channelwise product with
+ * external per-example weights"; e3nn-course Lesson 12a, exercise 1: the
+ * weights carry three channel indices).  Paths: every (input-1 block i,
+ * input-2 block j, output block o) with |l1 - l2| <= l3 <= l1 + l2 and
+ * p3 = p1 p2, in the order i, then j, then o; the output irreps are taken
+ * as given.  Terms without a parity letter ("0 + 1") are SO(3) irreps: no
+ * parity rule (all three strings must then be SO(3)).
+ *   out[n, o, k, w] = alpha_o sum over paths (i, j, o) of
+ *                     sum_(u, v) W_p[u, v, w] sum_(a, b) C[a, b, k] x1[n, i, a, u] x2[n, j, b, v]
+ * with the coupling of tp_create (segpoly_real_cg) and
+ * alpha_o = 1 / sqrt(sum over the paths into o of mul1 mul2) (0 for an
+ * output block no path reaches: its rows are zero).  Weights: one segment
+ * per path of mul1 * mul2 * mul3 values, (u, v, w) row-major, shared by all
+ * samples ([1, WEIGHT_NUMEL]).  flags: SEGPOLY_VALIDATE accepted (nothing
+ * to validate: no indices).  E_UNSUPPORTED for l > 6, more than 32 blocks on
+ * a side, more than 64 paths, or blocks too wide for one workgroup's LDS.
+ * Touches no GPU.
+ */
+int fctp_create(const char* irreps_in1, const char* irreps_in2, const char* irreps_out, int layout, int dtype,
+                unsigned flags, fctp_handle* out);
+
+/* fctp_query: SEGPOLY_Q_DIM_IN1, SEGPOLY_Q_DIM_IN2, SEGPOLY_Q_DIM_OUT,
+ * SEGPOLY_Q_WEIGHT_NUMEL, SEGPOLY_Q_NUM_PATHS. */
+int fctp_query(fctp_handle h, int key, int64_t* value);
+
+/* fctp_path_info: path p as {i, j, o, weight offset}. */
+int fctp_path_info(fctp_handle h, int p, int64_t* info4);
+
+/*
+ * fctp_fwd: out = fctp(x1, x2; w) for n samples, on the matrix cores.
+ *   x1 [n, DIM_IN1], x2 [n, DIM_IN2] device, layout of the handle.
+ *   w  [1, WEIGHT_NUMEL] device.
+ *   out [n, DIM_OUT] device, fully overwritten.  n == 0 does nothing.
+ */
+int fctp_fwd(fctp_handle h, const void* x1, const void* x2, const void* w, int64_t n, void* out, void* stream);
+
+/* fctp_bwd_workspace: bytes of workspace fctp_bwd needs for the weight
+ * gradient of n samples (per-chunk partial sums). */
+int fctp_bwd_workspace(fctp_handle h, int64_t n, size_t* bytes);
+
+/*
+ * fctp_bwd: vector-Jacobian product of fctp_fwd for g = dL/d(out):
+ *   grad_x1 [n, DIM_IN1], grad_x2 [n, DIM_IN2], grad_w [1, WEIGHT_NUMEL],
+ * each fully overwritten, or NULL (not computed).  grad_w needs
+ * `workspace` of fctp_bwd_workspace(n) bytes; it sums fixed chunks of 2048
+ * samples and then the chunks in order (deterministic).  Inputs a requested
+ * gradient does not read may be NULL (grad_x1 reads x2, g, w; grad_x2 reads
+ * x1, g, w; grad_w reads x1, x2, g).
+ */
+int fctp_bwd(fctp_handle h, const void* x1, const void* x2, const void* w, const void* grad_out, int64_t n,
+             void* grad_x1, void* grad_x2, void* grad_w, void* workspace, size_t workspace_bytes, void* stream);
+
+/* fctp_destroy: free the handle (NULL is a no-op). */
+int fctp_destroy(fctp_handle h);
 
 /* ------------------------------------------------------- spherical harmonics */
 

@@ -122,3 +122,27 @@ class FullyConnectedTP:
             dW = al * np.einsum("abk,nau,nbv,nkw->uvw", c, a[i], b[j], gb[o], optimize=True)
             dw[0, off:off + dW.size] = dW.reshape(-1)
         return join_blocks(da, layout), join_blocks(db, layout), dw
+
+    def dw_entries(self, x1, x2, g, flat, layout="mul_ir", absolute=False):
+        """Selected entries of the weight gradient (the ``dw`` of
+        :meth:`vjp`) at flat weight indices ``flat``, each from its
+        definition alpha_o sum_n sum_(a, b, k) C[a, b, k] x1[n, i, a, u]
+        x2[n, j, b, v] g[n, o, k, w]: the whole batch, one entry at a time."""
+        x1, x2, g = (np.asarray(a, dtype=np.float64) for a in (x1, x2, g))
+        if absolute:
+            x1, x2, g = np.abs(x1), np.abs(x2), np.abs(g)
+        a = split_blocks(x1, self.in1, layout)
+        b = split_blocks(x2, self.in2, layout)
+        gb = split_blocks(g, self.out, layout)
+        out = np.zeros(len(flat))
+        for r, e in enumerate(flat):
+            p = max(q for q in range(len(self.paths)) if self.paths[q][3] <= e)
+            i, j, o, off = self.paths[p]
+            m2, m3 = self.in2[j][0], self.out[o][0]
+            u, rem = divmod(e - off, m2 * m3)
+            v, w = divmod(rem, m3)
+            c = real_cg(self.in1[i][1], self.in2[j][1], self.out[o][1])
+            if absolute:
+                c = np.abs(c)
+            out[r] = self.alpha[o] * np.einsum("abk,na,nb,nk->", c, a[i][:, :, u], b[j][:, :, v], gb[o][:, :, w])
+        return out

@@ -2,7 +2,8 @@
 
 The functions keep the names of the C ABI in ``include/segpoly.h``:
 ``tp_create`` / ``tp_conv_fwd`` / ``tp_conv_bwd`` / ``symcon_create`` / ``symcon_fwd`` /
-``symcon_bwd`` / ``linear_create`` / ``linear_fwd`` / ``linear_bwd``.  Every
+``symcon_bwd`` / ``linear_create`` / ``linear_fwd`` / ``linear_bwd`` / ``fctp_create`` /
+``fctp_fwd`` / ``fctp_bwd`` / ``sh_fwd`` / ``sh_bwd``.  Every
 step of the computation runs in the library's HIP kernels; PyTorch only
 supplies device memory and the current stream.  There is no CPU fallback:
 importing this package fails loudly if the library has not been built.
@@ -32,7 +33,8 @@ _DTYPES = {"f32": F32, "f64": F64}
 EXPORTS = ("tp_create", "tp_query", "tp_irreps_out", "tp_path_info", "tp_path_cg", "tp_kernel_name",
            "tp_conv_fwd", "tp_conv_fwd_vec", "tp_conv_bwd_workspace", "tp_conv_bwd", "tp_destroy", "symcon_create", "symcon_query", "symcon_coupling_info",
            "symcon_coupling_dense", "symcon_fwd", "symcon_bwd_workspace", "symcon_bwd", "symcon_destroy", "linear_create", "linear_query", "linear_fwd",
-           "linear_bwd_workspace", "linear_bwd", "linear_destroy", "sh_fwd", "sh_bwd", "segpoly_real_cg",
+           "linear_bwd_workspace", "linear_bwd", "linear_destroy", "fctp_create", "fctp_query", "fctp_path_info",
+           "fctp_fwd", "fctp_bwd_workspace", "fctp_bwd", "fctp_destroy", "sh_fwd", "sh_bwd", "segpoly_real_cg",
            "segpoly_last_error", "segpoly_version")
 
 
@@ -93,6 +95,13 @@ def _load():
         "linear_bwd_workspace": [vp, i64, ctypes.POINTER(ctypes.c_size_t)],
         "linear_bwd": [vp, vp, vp, vp, vp, c_int, c_int, i64, vp, vp, vp, ctypes.c_size_t, vp],
         "linear_destroy": [vp],
+        "fctp_create": [ctypes.c_char_p, ctypes.c_char_p, ctypes.c_char_p, c_int, c_int, c_uint, ctypes.POINTER(vp)],
+        "fctp_query": [vp, c_int, p64],
+        "fctp_path_info": [vp, c_int, p64],
+        "fctp_fwd": [vp, vp, vp, vp, i64, vp, vp],
+        "fctp_bwd_workspace": [vp, i64, ctypes.POINTER(ctypes.c_size_t)],
+        "fctp_bwd": [vp, vp, vp, vp, vp, i64, vp, vp, vp, vp, ctypes.c_size_t, vp],
+        "fctp_destroy": [vp],
         "sh_fwd": [c_int, c_int, c_int, vp, i64, vp, vp],
         "sh_bwd": [c_int, c_int, c_int, vp, vp, i64, vp, vp],
         "segpoly_real_cg": [c_int, c_int, c_int, pd],
@@ -531,6 +540,99 @@ def linear_bwd(h, x, w, grad_out, classes=None, num_classes=None, need_dw=True, 
     _check(lib.linear_bwd(h._h, _ptr(x), _ptr(w), _ptr(grad_out), _ptr(classes), idx, nc, n, _ptr(gx), _ptr(gw),
                           _ptr(workspace), wbytes, _stream_ptr(x.device)))
     return gx, gw
+
+
+# ---------------------------------------------------------------- fully connected product
+
+class FctpHandle:
+    def __init__(self, raw, layout, dtype):
+        self._h = raw
+        self.layout = layout
+        self.dtype = dtype
+
+    def _q(self, key):
+        v = ctypes.c_int64()
+        _check(lib.fctp_query(self._h, key, ctypes.byref(v)))
+        return v.value
+
+    dim_in1 = property(lambda s: s._q(Q_DIM_IN1))
+    dim_in2 = property(lambda s: s._q(Q_DIM_IN2))
+    dim_out = property(lambda s: s._q(Q_DIM_OUT))
+    weight_numel = property(lambda s: s._q(Q_WEIGHT_NUMEL))
+    num_paths = property(lambda s: s._q(Q_NUM_PATHS))
+
+    def path_info(self, p):
+        """(i, j, o, weight offset) of path p."""
+        info = (ctypes.c_int64 * 4)()
+        _check(lib.fctp_path_info(self._h, p, info))
+        return tuple(info)
+
+    def __del__(self):
+        if getattr(self, "_h", None) and lib is not None:
+            lib.fctp_destroy(self._h)
+            self._h = None
+
+
+def fctp_create(irreps_in1, irreps_in2, irreps_out, layout="mul_ir", dtype="f32", validate=False):
+    """Fully connected (uvw) tensor product with shared weights."""
+    raw = ctypes.c_void_p()
+    _check(lib.fctp_create(irreps_in1.encode(), irreps_in2.encode(), irreps_out.encode(), _LAYOUTS[layout],
+                           _DTYPES[dtype], VALIDATE if validate else 0, ctypes.byref(raw)))
+    return FctpHandle(raw, layout, dtype)
+
+
+def _fc_check(h, **tensors):
+    t = _torch_dtype(h.dtype)
+    n = None
+    widths = {"x1": h.dim_in1, "x2": h.dim_in2, "grad_out": h.dim_out}
+    for name, a in tensors.items():
+        if a is None:
+            continue
+        if a.dtype != t or not a.is_cuda or not a.is_contiguous() or a.dim() != 2:
+            raise ValueError(f"{name} must be a contiguous 2-d {t} device tensor")
+        if name == "w":
+            if a.shape != (1, h.weight_numel):
+                raise ValueError("weights are one shared row [1, weight_numel]")
+            continue
+        if a.shape[1] != widths[name]:
+            raise ValueError(f"{name} width does not match the descriptor")
+        if n is not None and a.shape[0] != n:
+            raise ValueError("operands have different sample counts")
+        n = a.shape[0]
+    return t, n
+
+
+def fctp_fwd(h, x1, x2, w, out=None):
+    """out [n, dim_out] for x1 [n, dim_in1], x2 [n, dim_in2], w [1, weight_numel]."""
+    import torch
+    t, n = _fc_check(h, x1=x1, x2=x2, w=w)
+    if out is None:
+        out = torch.empty((n, h.dim_out), dtype=t, device=x1.device)
+    elif out.shape != (n, h.dim_out) or out.dtype != t or not out.is_contiguous():
+        raise ValueError("out has the wrong shape or dtype")
+    _check(lib.fctp_fwd(h._h, _ptr(x1), _ptr(x2), _ptr(w), n, _ptr(out), _stream_ptr(x1.device)))
+    return out
+
+
+def fctp_bwd_workspace(h, n):
+    v = ctypes.c_size_t()
+    _check(lib.fctp_bwd_workspace(h._h, n, ctypes.byref(v)))
+    return v.value
+
+
+def fctp_bwd(h, x1, x2, w, grad_out, need=(True, True, True), workspace=None):
+    """(grad_x1, grad_x2, grad_w), each None where ``need`` is False."""
+    import torch
+    _, n = _fc_check(h, x1=x1, x2=x2, w=w, grad_out=grad_out)
+    g1 = torch.empty_like(x1) if need[0] else None
+    g2 = torch.empty_like(x2) if need[1] else None
+    gw = torch.empty_like(w) if need[2] else None
+    if need[2] and workspace is None:
+        workspace = torch.empty(max(1, fctp_bwd_workspace(h, n)), dtype=torch.uint8, device=x1.device)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.fctp_bwd(h._h, _ptr(x1), _ptr(x2), _ptr(w), _ptr(grad_out), n, _ptr(g1), _ptr(g2), _ptr(gw),
+                        _ptr(workspace), wbytes, _stream_ptr(x1.device)))
+    return g1, g2, gw
 
 
 # ---------------------------------------------------------------- spherical harmonics

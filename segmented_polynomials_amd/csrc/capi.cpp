@@ -36,50 +36,6 @@ int copy_str(const std::string& s, char* buf, size_t cap) {
   return ok();
 }
 
-struct DeviceBuffer {
-  void* ptr = nullptr;
-};
-
-// Upload `bytes` of host data once per device; returns the device pointer
-// or null (error set) on failure.
-void* upload(std::map<int, DeviceBuffer>& cache, std::mutex& mu, const void* host, size_t bytes, int* status) {
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) {
-    *status = fail(SEGPOLY_E_HIP, std::string("hipGetDevice: ") + hipGetErrorString(e));
-    return nullptr;
-  }
-  std::lock_guard<std::mutex> g(mu);
-  auto it = cache.find(dev);
-  if (it != cache.end()) return it->second.ptr;
-  void* p = nullptr;
-  e = hipMalloc(&p, bytes ? bytes : 16);
-  if (e != hipSuccess) {
-    *status = fail(SEGPOLY_E_OOM, std::string("hipMalloc (coefficient table): ") + hipGetErrorString(e));
-    return nullptr;
-  }
-  if (bytes) {
-    e = hipMemcpy(p, host, bytes, hipMemcpyHostToDevice);
-    if (e != hipSuccess) {
-      (void)hipFree(p);
-      *status = fail(SEGPOLY_E_HIP, std::string("hipMemcpy (coefficient table): ") + hipGetErrorString(e));
-      return nullptr;
-    }
-  }
-  cache[dev].ptr = p;
-  return p;
-}
-
-void free_all(std::map<int, DeviceBuffer>& cache) {
-  int cur = 0;
-  bool have = hipGetDevice(&cur) == hipSuccess;
-  for (auto& kv : cache) {
-    if (hipSetDevice(kv.first) == hipSuccess) (void)hipFree(kv.second.ptr);
-  }
-  if (have) (void)hipSetDevice(cur);
-  cache.clear();
-}
-
 // Host-side index checks of the VALIDATE flag.
 template <typename Index>
 int check_indices(const void* dsrc, const void* ddst, int64_t n_edges, int64_t n_src, int64_t n_nodes,

@@ -1,0 +1,502 @@
+// C ABI of the fully connected (uvw) tensor product: descriptor, the three
+// GEMM passes' tables, the weight-gradient tables, validation, launches.
+// Host code.
+#include <hip/hip_runtime_api.h>
+
+#include <algorithm>
+#include <cctype>
+#include <cmath>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "capi_util.hpp"
+#include "cg.hpp"
+#include "fctp_tables.hpp"
+#include "irreps.hpp"
+#include "launch.hpp"
+#include "linear_tables.hpp"
+#include "segpoly.h"
+
+using namespace segpoly;
+
+namespace {
+
+constexpr size_t kLdsLimit = 64 * 1024;  // per workgroup (two workgroups fit a CU)
+constexpr int kMaxL = 6;
+
+// A term without a parity letter is an SO(3) irrep (parity 0: the parity
+// rule p3 = p1 p2 then holds for every triple); mixing the two is an error.
+std::vector<Irrep> parse_any(const std::string& s) {
+  try {
+    return parse_irreps(s);
+  } catch (const ParseError&) {
+  }
+  std::vector<Irrep> out;
+  size_t start = 0;
+  while (true) {
+    const size_t plus = s.find('+', start);
+    std::string term = s.substr(start, plus == std::string::npos ? std::string::npos : plus - start);
+    term.erase(std::remove_if(term.begin(), term.end(), [](unsigned char c) { return std::isspace(c); }), term.end());
+    int mul = 1;
+    const size_t x = term.find('x');
+    std::string ls = term;
+    if (x != std::string::npos) {
+      const std::string m = term.substr(0, x);
+      if (m.empty() || m.size() > 6 || !std::all_of(m.begin(), m.end(), ::isdigit))
+        throw ParseError("bad multiplicity in irreps term '" + term + "'");
+      mul = std::stoi(m);
+      ls = term.substr(x + 1);
+    }
+    if (ls.empty() || ls.size() > 3 || !std::all_of(ls.begin(), ls.end(), ::isdigit))
+      throw ParseError("bad irreps term '" + term + "' (expected MULxLP with P in {e, o}, or MULxL for SO(3))");
+    out.push_back({mul, std::stoi(ls), 0});
+    if (plus == std::string::npos) break;
+    start = plus + 1;
+  }
+  return out;
+}
+
+std::vector<int64_t> offsets(const std::vector<Irrep>& v) {
+  std::vector<int64_t> o(v.size() + 1, 0);
+  for (size_t i = 0; i < v.size(); ++i) o[i + 1] = o[i] + static_cast<int64_t>(v[i].mul) * (2 * v[i].l + 1);
+  return o;
+}
+
+struct FcPass {
+  std::vector<FcRes> res;
+  std::vector<FcTerm> terms;
+  int tn = 32;
+  size_t lds = 0;
+  int64_t dim_res = 0;
+  size_t res_off = 0, term_off = 0;  // within the device blob
+};
+
+}  // namespace
+
+struct segpoly_fctp {
+  std::vector<Irrep> in1, in2, out;
+  std::vector<int64_t> off1, off2, offo;
+  struct Path {
+    int i, j, o;
+    int64_t w_off;
+  };
+  std::vector<Path> paths;
+  std::vector<double> alpha;
+  std::vector<int> path_term;     // index of each path's term in the forward pass
+  int layout = 0, dtype = 0;
+  unsigned flags = 0;
+  int64_t dim1 = 0, dim2 = 0, dimo = 0, numel = 0;
+  FcPass pass[3];                 // forward, input-1 gradient, input-2 gradient
+  std::vector<FcDwPath> dw;
+  size_t dw_lds = 0, dw_off = 0, ent_off = 0;
+  std::vector<FcEnt> ents;
+  std::vector<unsigned char> blob;
+  std::map<int, DeviceBuffer> dev;
+  std::mutex mu;
+};
+
+namespace {
+
+size_t elt(int dtype) { return dtype == SEGPOLY_F32 ? 4 : 8; }
+
+// Entries of one term for result components 0..dr-1: coupling C[a, b, k]
+// of the path seen with the result index `which` (0: a, 1: b, 2: k) and the
+// other two as (P component, Q component).  Returns T, appends T * dr
+// entries (zero-padded) to `ents`.
+int add_entries(std::vector<FcEnt>& ents, const std::vector<double>& C, int d1, int d2, int d3, int which,
+                double scale) {
+  const int dr = which == 0 ? d1 : (which == 1 ? d2 : d3);
+  std::vector<std::vector<FcEnt>> per(dr);
+  for (int a = 0; a < d1; ++a)
+    for (int b = 0; b < d2; ++b)
+      for (int k = 0; k < d3; ++k) {
+        const double c = C[(static_cast<size_t>(a) * d2 + b) * d3 + k];
+        if (std::fabs(c) < 1e-13) continue;
+        if (which == 0) per[a].push_back({b, k, scale * c});
+        else if (which == 1) per[b].push_back({a, k, scale * c});
+        else per[k].push_back({a, b, scale * c});
+      }
+  int T = 1;
+  for (const auto& v : per) T = std::max<int>(T, static_cast<int>(v.size()));
+  if (T > kFcMaxT) return -1;
+  for (const auto& v : per)
+    for (int e = 0; e < T; ++e) ents.push_back(e < static_cast<int>(v.size()) ? v[e] : FcEnt{0, 0, 0.0});
+  return T;
+}
+
+// Samples per tile of result block R: whole samples, at most 128 rows,
+// LDS within the limit (rows 128, else 64, 32, 16).
+int pick_ts(int d, size_t per_sample, size_t budget) {
+  for (int rows : {kFcRowsMax, 64, 32, 16}) {
+    const int ts = std::max(1, rows / d);
+    if (static_cast<size_t>(ts) * per_sample <= budget) return ts;
+  }
+  const size_t ts = per_sample ? budget / per_sample : 1;
+  return ts >= 1 ? static_cast<int>(std::min<size_t>(ts, 16)) : 0;
+}
+
+int tn_for(int m) { return m <= 16 ? 16 : (m <= 32 ? 32 : 64); }
+
+size_t static_b_bytes(int tn, int dtype) {
+  const int stride = tn == 16 ? 16 : tn + 16;
+  return 2ull * 32 * stride * elt(dtype);
+}
+
+// Build pass `which` (0 forward, 1 dx1, 2 dx2).
+int build_pass(segpoly_fctp* h, int which) {
+  FcPass& P = h->pass[which];
+  const std::vector<Irrep>& rb = which == 0 ? h->out : (which == 1 ? h->in1 : h->in2);
+  const std::vector<int64_t>& roff = which == 0 ? h->offo : (which == 1 ? h->off1 : h->off2);
+  if (rb.size() > static_cast<size_t>(kFcMaxRes))
+    return fail(SEGPOLY_E_UNSUPPORTED, "more than 32 irreps blocks on one side");
+  P.dim_res = roff.back();
+  int mmax = 1;
+  for (const auto& b : rb) mmax = std::max(mmax, b.mul);
+  P.tn = tn_for(mmax);
+  const size_t budget = kLdsLimit - static_b_bytes(P.tn, h->dtype);
+  for (size_t r = 0; r < rb.size(); ++r) {
+    FcRes R{};
+    R.off = roff[r];
+    R.d = 2 * rb[r].l + 1;
+    R.m = rb[r].mul;
+    R.term_begin = static_cast<int>(P.terms.size());
+    size_t per_sample = 0;
+    for (const auto& pa : h->paths) {
+      const int blk = which == 0 ? pa.o : (which == 1 ? pa.i : pa.j);
+      if (blk != static_cast<int>(r)) continue;
+      const Irrep &a = h->in1[pa.i], &b = h->in2[pa.j], &o = h->out[pa.o];
+      const int d1 = 2 * a.l + 1, d2 = 2 * b.l + 1, d3 = 2 * o.l + 1;
+      const int64_t m1 = a.mul, m2 = b.mul, m3 = o.mul;
+      FcTerm t{};
+      t.w_off = pa.w_off;
+      if (which == 0) {  // P = x1 (a, u), Q = x2 (b, v), result (k, w)
+        t.p_op = 0, t.q_op = 1;
+        t.p_d = d1, t.p_m = a.mul, t.p_off = h->off1[pa.i];
+        t.q_d = d2, t.q_m = b.mul, t.q_off = h->off2[pa.j];
+        t.s_p = m2 * m3, t.s_q = m3, t.s_r = 1;
+      } else if (which == 1) {  // P = x2 (b, v), Q = g (k, w), result (a, u)
+        t.p_op = 1, t.q_op = 2;
+        t.p_d = d2, t.p_m = b.mul, t.p_off = h->off2[pa.j];
+        t.q_d = d3, t.q_m = o.mul, t.q_off = h->offo[pa.o];
+        t.s_p = m3, t.s_q = 1, t.s_r = m2 * m3;
+      } else {  // P = x1 (a, u), Q = g (k, w), result (b, v)
+        t.p_op = 0, t.q_op = 2;
+        t.p_d = d1, t.p_m = a.mul, t.p_off = h->off1[pa.i];
+        t.q_d = d3, t.q_m = o.mul, t.q_off = h->offo[pa.o];
+        t.s_p = m2 * m3, t.s_q = 1, t.s_r = m3;
+      }
+      if (static_cast<int64_t>(t.p_m) * t.q_m >= (1ll << 31))
+        return fail(SEGPOLY_E_UNSUPPORTED, "multiplicities too large (mul1 * mul2 must stay below 2^31)");
+      t.ent = static_cast<int>(h->ents.size());
+      const int which_idx = which == 0 ? 2 : (which == 1 ? 0 : 1);
+      t.T = add_entries(h->ents, real_cg(a.l, b.l, o.l), d1, d2, d3, which_idx, h->alpha[pa.o]);
+      if (t.T < 0) return fail(SEGPOLY_E_UNSUPPORTED, "more than 8 couplings per component in one path");
+      t.q_div = make_fast_div(std::max(1, t.q_m));
+      if (which == 0) h->path_term[&pa - h->paths.data()] = static_cast<int>(P.terms.size());
+      per_sample = std::max(per_sample, (static_cast<size_t>(t.p_d) * (t.p_m + kFcPad) +
+                                         static_cast<size_t>(t.q_d) * (t.q_m + kFcPad)) * elt(h->dtype));
+      P.terms.push_back(t);
+    }
+    R.term_end = static_cast<int>(P.terms.size());
+    R.ts = pick_ts(R.d, per_sample, budget);
+    if (R.ts < 1) return fail(SEGPOLY_E_UNSUPPORTED, "operand blocks too wide for the LDS of one workgroup");
+    R.col_tiles = (R.m + P.tn - 1) / P.tn;
+    if (R.m == 0) R.col_tiles = 0;
+    P.lds = std::max(P.lds, static_cast<size_t>(R.ts) * per_sample);
+    P.res.push_back(R);
+  }
+  return SEGPOLY_OK;
+}
+
+int build_dw(segpoly_fctp* h) {
+  if (h->paths.size() > static_cast<size_t>(kFcMaxPaths)) return fail(SEGPOLY_E_UNSUPPORTED, "more than 64 paths");
+  const FcPass& F = h->pass[0];
+  for (size_t pi = 0; pi < h->paths.size(); ++pi) {
+    const auto& pa = h->paths[pi];
+    const FcTerm* ft = &F.terms[h->path_term[pi]];  // the forward term of the path: its entries
+    const Irrep &a = h->in1[pa.i], &b = h->in2[pa.j], &o = h->out[pa.o];
+    FcDwPath q{};
+    q.p_d = 2 * a.l + 1, q.p_m = a.mul, q.q_d = 2 * b.l + 1, q.q_m = b.mul, q.g_d = 2 * o.l + 1, q.g_m = o.mul;
+    q.p_off = h->off1[pa.i], q.q_off = h->off2[pa.j], q.g_off = h->offo[pa.o], q.w_off = pa.w_off;
+    q.T = ft->T;
+    q.ent = ft->ent;
+    const size_t per = (static_cast<size_t>(q.p_d) * (q.p_m + kFcPad) + static_cast<size_t>(q.q_d) * (q.q_m + kFcPad) +
+                        static_cast<size_t>(q.g_d) * (q.g_m + kFcPad)) * elt(h->dtype);
+    int ts = static_cast<int>(std::min<size_t>(64, kLdsLimit / per)) & ~3;
+    if (ts < 4) return fail(SEGPOLY_E_UNSUPPORTED, "operand blocks too wide for the weight-gradient kernel");
+    q.ts = ts;
+    const int64_t K = static_cast<int64_t>(q.p_m) * q.q_m;
+    q.m_tiles = static_cast<int>((K + kFcDwRows - 1) / kFcDwRows);
+    q.col_tiles = (q.g_m + kFcDwCols - 1) / kFcDwCols;
+    q.q_div = make_fast_div(std::max(1, q.q_m));
+    h->dw_lds = std::max(h->dw_lds, static_cast<size_t>(ts) * per);
+    h->dw.push_back(q);
+  }
+  return SEGPOLY_OK;
+}
+
+template <typename V>
+size_t append(std::vector<unsigned char>& blob, const std::vector<V>& v) {
+  const size_t off = (blob.size() + 255) & ~size_t(255);
+  blob.resize(off + v.size() * sizeof(V));
+  if (!v.empty()) std::memcpy(blob.data() + off, v.data(), v.size() * sizeof(V));
+  return off;
+}
+
+// Per-call tile map of pass `which` for n samples; false if the grid would
+// not fit.
+bool fill_tiles(const FcPass& P, int64_t n, FcTiles& t) {
+  t.n_res = static_cast<int>(P.res.size());
+  int64_t acc = 0;
+  for (int r = 0; r < t.n_res; ++r) {
+    t.tile_begin[r] = static_cast<int>(acc);
+    const FcRes& R = P.res[r];
+    acc += (n + R.ts - 1) / R.ts * R.col_tiles;
+    if (acc >= kMaxGridX) return false;
+  }
+  t.tile_begin[t.n_res] = static_cast<int>(acc);
+  return true;
+}
+
+bool fill_dw_tiles(const segpoly_fctp* h, int64_t n, FcDwTiles& t) {
+  t.n_paths = static_cast<int>(h->dw.size());
+  const int64_t chunks = (n + kFcDwChunk - 1) / kFcDwChunk;
+  t.chunks = static_cast<int>(chunks);
+  int64_t acc = 0;
+  for (int p = 0; p < t.n_paths; ++p) {
+    t.tile_begin[p] = static_cast<int>(acc);
+    acc += chunks * h->dw[p].m_tiles * h->dw[p].col_tiles;
+    if (acc >= kMaxGridX) return false;
+  }
+  t.tile_begin[t.n_paths] = static_cast<int>(acc);
+  return true;
+}
+
+const unsigned char* device_blob(segpoly_fctp* h, int* st) {
+  return static_cast<const unsigned char*>(upload(h->dev, h->mu, h->blob.data(), h->blob.size(), st));
+}
+
+int run_pass(segpoly_fctp* h, const unsigned char* db, int which, const void* x1, const void* x2, const void* g,
+             const void* w, int64_t n, void* res, void* stream) {
+  const FcPass& P = h->pass[which];
+  FcTiles t{};
+  if (!fill_tiles(P, n, t)) return fail(SEGPOLY_E_UNSUPPORTED, "too many samples for one launch");
+  FcArgs a{};
+  a.op[0] = x1, a.op[1] = x2, a.op[2] = g;
+  a.dim[0] = h->dim1, a.dim[1] = h->dim2, a.dim[2] = h->dimo;
+  a.w = w;
+  a.res = res;
+  a.dim_res = P.dim_res;
+  a.n = n;
+  a.res_tab = reinterpret_cast<const FcRes*>(db + P.res_off);
+  a.terms = reinterpret_cast<const FcTerm*>(db + P.term_off);
+  a.ents = reinterpret_cast<const FcEnt*>(db + h->ent_off);
+  a.tn = P.tn;
+  a.lds_bytes = P.lds;
+  a.dtype = h->dtype;
+  a.layout = h->layout;
+  a.stream = stream;
+  const int rc = launch_fctp(a, t);
+  if (rc) return fail(SEGPOLY_E_HIP, std::string("fctp launch: ") + hipGetErrorString(static_cast<hipError_t>(rc)));
+  return SEGPOLY_OK;
+}
+
+size_t dw_workspace(const segpoly_fctp* h, int64_t n) {
+  const int64_t chunks = (n + kFcDwChunk - 1) / kFcDwChunk;
+  return static_cast<size_t>(round_up_256(chunks * h->numel * static_cast<int64_t>(elt(h->dtype))));
+}
+
+}  // namespace
+
+extern "C" {
+
+int fctp_create(const char* irreps_in1, const char* irreps_in2, const char* irreps_out, int layout, int dtype,
+                unsigned flags, fctp_handle* out) {
+  if (!out) return fail(SEGPOLY_E_INVALID, "null handle pointer");
+  *out = nullptr;
+  if (!irreps_in1 || !irreps_in2 || !irreps_out) return fail(SEGPOLY_E_INVALID, "null irreps string");
+  if (layout != SEGPOLY_MUL_IR && layout != SEGPOLY_IR_MUL) return fail(SEGPOLY_E_INVALID, "bad layout");
+  if (dtype != SEGPOLY_F32 && dtype != SEGPOLY_F64) return fail(SEGPOLY_E_INVALID, "bad dtype");
+  if (flags & ~SEGPOLY_VALIDATE) return fail(SEGPOLY_E_INVALID, "unknown flag bits");
+  segpoly_fctp* h = nullptr;
+  try {
+    h = new segpoly_fctp();
+    h->in1 = parse_any(irreps_in1);
+    h->in2 = parse_any(irreps_in2);
+    h->out = parse_any(irreps_out);
+  } catch (const ParseError& e) {
+    delete h;
+    return fail(SEGPOLY_E_PARSE, e.what());
+  } catch (const std::bad_alloc&) {
+    delete h;
+    return fail(SEGPOLY_E_OOM, "out of host memory");
+  } catch (const std::exception& e) {
+    delete h;
+    return fail(SEGPOLY_E_PARSE, e.what());
+  }
+  int so3 = 0, o3 = 0;
+  for (const auto* v : {&h->in1, &h->in2, &h->out})
+    for (const auto& b : *v) {
+      (b.p == 0 ? so3 : o3) = 1;
+      if (b.l > kMaxL) {
+        delete h;
+        return fail(SEGPOLY_E_UNSUPPORTED, "l above 6");
+      }
+    }
+  if (so3 && o3) {
+    delete h;
+    return fail(SEGPOLY_E_PARSE, "mixing SO(3) and O(3) irreps");
+  }
+  h->layout = layout;
+  h->dtype = dtype;
+  h->flags = flags;
+  h->off1 = offsets(h->in1);
+  h->off2 = offsets(h->in2);
+  h->offo = offsets(h->out);
+  h->dim1 = h->off1.back(), h->dim2 = h->off2.back(), h->dimo = h->offo.back();
+  // paths in the order input-1 block, input-2 block, output block; one
+  // weight segment of mul1 * mul2 * mul3 (w fastest) per path
+  std::vector<int64_t> fan(h->out.size(), 0);
+  int64_t woff = 0;
+  for (size_t i = 0; i < h->in1.size(); ++i)
+    for (size_t j = 0; j < h->in2.size(); ++j)
+      for (size_t o = 0; o < h->out.size(); ++o) {
+        const Irrep &a = h->in1[i], &b = h->in2[j], &c = h->out[o];
+        if (c.l < std::abs(a.l - b.l) || c.l > a.l + b.l || c.p != a.p * b.p) continue;
+        h->paths.push_back({static_cast<int>(i), static_cast<int>(j), static_cast<int>(o), woff});
+        woff += static_cast<int64_t>(a.mul) * b.mul * c.mul;
+        fan[o] += static_cast<int64_t>(a.mul) * b.mul;
+      }
+  h->numel = woff;
+  h->path_term.assign(h->paths.size(), 0);
+  for (size_t o = 0; o < h->out.size(); ++o) h->alpha.push_back(fan[o] ? 1.0 / std::sqrt(double(fan[o])) : 0.0);
+  int rc = SEGPOLY_OK;
+  try {
+    for (int w = 0; w < 3 && rc == SEGPOLY_OK; ++w) rc = build_pass(h, w);
+    if (rc == SEGPOLY_OK) rc = build_dw(h);
+    if (rc == SEGPOLY_OK) {
+      for (int w = 0; w < 3; ++w) {
+        h->pass[w].res_off = append(h->blob, h->pass[w].res);
+        h->pass[w].term_off = append(h->blob, h->pass[w].terms);
+      }
+      h->dw_off = append(h->blob, h->dw);
+      h->ent_off = append(h->blob, h->ents);
+    }
+  } catch (const std::bad_alloc&) {
+    rc = fail(SEGPOLY_E_OOM, "out of host memory");
+  }
+  if (rc != SEGPOLY_OK) {
+    delete h;
+    return rc;
+  }
+  *out = h;
+  return ok();
+}
+
+int fctp_query(fctp_handle h, int key, int64_t* value) {
+  if (!h || !value) return fail(SEGPOLY_E_INVALID, "null argument");
+  switch (key) {
+    case SEGPOLY_Q_DIM_IN1: *value = h->dim1; break;
+    case SEGPOLY_Q_DIM_IN2: *value = h->dim2; break;
+    case SEGPOLY_Q_DIM_OUT: *value = h->dimo; break;
+    case SEGPOLY_Q_WEIGHT_NUMEL: *value = h->numel; break;
+    case SEGPOLY_Q_NUM_PATHS: *value = static_cast<int64_t>(h->paths.size()); break;
+    default: return fail(SEGPOLY_E_INVALID, "unknown query key");
+  }
+  return ok();
+}
+
+int fctp_path_info(fctp_handle h, int p, int64_t* info4) {
+  if (!h || !info4) return fail(SEGPOLY_E_INVALID, "null argument");
+  if (p < 0 || p >= static_cast<int>(h->paths.size())) return fail(SEGPOLY_E_INVALID, "path index out of range");
+  info4[0] = h->paths[p].i;
+  info4[1] = h->paths[p].j;
+  info4[2] = h->paths[p].o;
+  info4[3] = h->paths[p].w_off;
+  return ok();
+}
+
+int fctp_fwd(fctp_handle h, const void* x1, const void* x2, const void* w, int64_t n, void* out, void* stream) {
+  if (!h) return fail(SEGPOLY_E_INVALID, "null handle");
+  if (n < 0) return fail(SEGPOLY_E_INVALID, "negative sample count");
+  if (n == 0) return ok();
+  if (!out || (h->numel > 0 && !w) || (h->dim1 > 0 && !x1) || (h->dim2 > 0 && !x2))
+    return fail(SEGPOLY_E_INVALID, "null buffer");
+  int st = SEGPOLY_OK;
+  const unsigned char* db = device_blob(h, &st);
+  if (!db) return st;
+  const int rc = run_pass(h, db, 0, x1, x2, nullptr, w, n, out, stream);
+  return rc ? rc : ok();
+}
+
+int fctp_bwd_workspace(fctp_handle h, int64_t n, size_t* bytes) {
+  if (!h || !bytes) return fail(SEGPOLY_E_INVALID, "null argument");
+  if (n < 0) return fail(SEGPOLY_E_INVALID, "negative sample count");
+  *bytes = dw_workspace(h, n);
+  return ok();
+}
+
+int fctp_bwd(fctp_handle h, const void* x1, const void* x2, const void* w, const void* grad_out, int64_t n,
+             void* grad_x1, void* grad_x2, void* grad_w, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!h) return fail(SEGPOLY_E_INVALID, "null handle");
+  if (n < 0) return fail(SEGPOLY_E_INVALID, "negative sample count");
+  if (grad_w && h->numel > 0 && workspace_bytes < dw_workspace(h, n))
+    return fail(SEGPOLY_E_INVALID, "workspace too small: need " + std::to_string(dw_workspace(h, n)) + " bytes");
+  if (grad_w && h->numel > 0 && n > 0 && !workspace) return fail(SEGPOLY_E_INVALID, "null workspace");
+  if (n > 0) {
+    if ((h->dimo > 0 && !grad_out) || (h->dim1 > 0 && !x1 && (grad_x2 || grad_w)) ||
+        (h->dim2 > 0 && !x2 && (grad_x1 || grad_w)) || (h->numel > 0 && !w && (grad_x1 || grad_x2)))
+      return fail(SEGPOLY_E_INVALID, "null buffer");
+  }
+  if (n == 0) {
+    if (grad_w && h->numel > 0) {
+      const int rc = launch_fill_zero(grad_w, h->numel, h->dtype, stream);
+      if (rc) return fail(SEGPOLY_E_HIP, std::string("fill: ") + hipGetErrorString(static_cast<hipError_t>(rc)));
+    }
+    return ok();
+  }
+  int st = SEGPOLY_OK;
+  const unsigned char* db = device_blob(h, &st);
+  if (!db) return st;
+  if (grad_x1) {
+    const int rc = run_pass(h, db, 1, x1, x2, grad_out, w, n, grad_x1, stream);
+    if (rc) return rc;
+  }
+  if (grad_x2) {
+    const int rc = run_pass(h, db, 2, x1, x2, grad_out, w, n, grad_x2, stream);
+    if (rc) return rc;
+  }
+  if (grad_w && h->numel > 0) {
+    FcDwTiles t{};
+    if (!fill_dw_tiles(h, n, t)) return fail(SEGPOLY_E_UNSUPPORTED, "too many samples for one launch");
+    FcDwArgs a{};
+    a.x1 = x1, a.x2 = x2, a.g = grad_out;
+    a.dim1 = h->dim1, a.dim2 = h->dim2, a.dimo = h->dimo;
+    a.part = workspace;
+    a.dw = grad_w;
+    a.numel = h->numel;
+    a.n = n;
+    a.paths = reinterpret_cast<const FcDwPath*>(db + h->dw_off);
+    a.ents = reinterpret_cast<const FcEnt*>(db + h->ent_off);
+    a.lds_bytes = h->dw_lds;
+    a.dtype = h->dtype;
+    a.layout = h->layout;
+    a.stream = stream;
+    const int rc = launch_fctp_dw(a, t);
+    if (rc) return fail(SEGPOLY_E_HIP, std::string("fctp dw launch: ") + hipGetErrorString(static_cast<hipError_t>(rc)));
+  }
+  return ok();
+}
+
+int fctp_destroy(fctp_handle h) {
+  if (!h) return ok();
+  free_all(h->dev);
+  delete h;
+  return ok();
+}
+
+}  // extern "C"

@@ -1,5 +1,9 @@
 // Status helpers shared by the C ABI translation units (host code).
 #pragma once
+#include <hip/hip_runtime_api.h>
+
+#include <map>
+#include <mutex>
 #include <string>
 
 #include "segpoly.h"
@@ -17,6 +21,51 @@ inline int fail(int code, const std::string& msg) {
 inline int ok() {
   g_last_error.clear();
   return SEGPOLY_OK;
+}
+
+// Coefficient tables kept on each device a handle has run on.
+struct DeviceBuffer {
+  void* ptr = nullptr;
+};
+
+// Upload `bytes` of host data once per device; returns the device pointer
+// or null (error set) on failure.
+inline void* upload(std::map<int, DeviceBuffer>& cache, std::mutex& mu, const void* host, size_t bytes, int* status) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    *status = fail(SEGPOLY_E_HIP, std::string("hipGetDevice: ") + hipGetErrorString(e));
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> g(mu);
+  auto it = cache.find(dev);
+  if (it != cache.end()) return it->second.ptr;
+  void* p = nullptr;
+  e = hipMalloc(&p, bytes ? bytes : 16);
+  if (e != hipSuccess) {
+    *status = fail(SEGPOLY_E_OOM, std::string("hipMalloc (coefficient table): ") + hipGetErrorString(e));
+    return nullptr;
+  }
+  if (bytes) {
+    e = hipMemcpy(p, host, bytes, hipMemcpyHostToDevice);
+    if (e != hipSuccess) {
+      (void)hipFree(p);
+      *status = fail(SEGPOLY_E_HIP, std::string("hipMemcpy (coefficient table): ") + hipGetErrorString(e));
+      return nullptr;
+    }
+  }
+  cache[dev].ptr = p;
+  return p;
+}
+
+inline void free_all(std::map<int, DeviceBuffer>& cache) {
+  int cur = 0;
+  bool have = hipGetDevice(&cur) == hipSuccess;
+  for (auto& kv : cache) {
+    if (hipSetDevice(kv.first) == hipSuccess) (void)hipFree(kv.second.ptr);
+  }
+  if (have) (void)hipSetDevice(cur);
+  cache.clear();
 }
 
 constexpr int64_t kMaxGridX = 2147483647;

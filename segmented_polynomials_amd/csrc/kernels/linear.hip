@@ -25,37 +25,10 @@
 
 #include "../launch.hpp"
 #include "../linear_tables.hpp"
+#include "mfma.hpp"
 
 namespace segpoly {
 namespace kern {
-
-typedef float v4f __attribute__((ext_vector_type(4)));
-typedef double v4d __attribute__((ext_vector_type(4)));
-
-template <typename T>
-struct Mfma;
-
-// v_mfma_f32_16x16x4f32: lane l supplies A[l % 16][l / 16], B[l / 16][l % 16];
-// accumulator j of lane l is C[4 (l / 16) + j][l % 16].
-template <>
-struct Mfma<float> {
-  using acc_t = v4f;
-  __device__ __forceinline__ static acc_t mma(float a, float b, acc_t c) {
-    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
-  }
-  __device__ __forceinline__ static int row(int lane, int j) { return 4 * (lane / 16) + j; }
-};
-
-// v_mfma_f64_16x16x4f64: same operands; accumulator j of lane l is
-// C[4 j + l / 16][l % 16].
-template <>
-struct Mfma<double> {
-  using acc_t = v4d;
-  __device__ __forceinline__ static acc_t mma(double a, double b, acc_t c) {
-    return __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, c, 0, 0, 0);
-  }
-  __device__ __forceinline__ static int row(int lane, int j) { return 4 * j + lane / 16; }
-};
 
 constexpr int kLinTM = kLinTileRows, kLinTN = kLinTileCols, kLinTK = 32, kLinThreads = 256;
 // 4 waves as 2 x 2; each wave owns (kLinTM / 2) x (kLinTN / 2) = kMT x kNT

@@ -12,7 +12,7 @@ import pytest
 from hypothesis import given, settings, strategies as st
 
 import segmented_polynomials_amd as sp
-from oracle import cg as ocg, irreps as oirreps, symcon as osymcon, tp as otp
+from oracle import cg as ocg, fctp as ofctp, irreps as oirreps, symcon as osymcon, tp as otp
 import workloads
 
 HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "segpoly.h")
@@ -277,6 +277,48 @@ def test_linear_descriptor_and_errors():
     b = sp.lib.linear_bwd
     assert b(h._h, p, p, p, p, 0, 2, 2, p, p, p, 1 << 30, None) == sp.E_UNSUPPORTED   # dw with classes
     assert b(h._h, p, p, p, None, 0, 1, 2, p, p, p, 8, None) == sp.E_INVALID          # workspace small
+
+
+@pytest.mark.parametrize("a,b,c", [("0 + 1", "0 + 1", "0 + 1"), ("32x0e+32x1o", "32x0e+32x1o", "32x0e+32x1o"),
+                                   ("3x0e+2x1o+1x2e", "2x0e+1x1o+2x1e", "2x0e+3x1o+2x1e+1x2e+1x2o"),
+                                   ("2x0e+1x1o", "1x0e", "2x0e+1x1o+2x2e"), ("4x2e+0x1o", "2x2e", "3x0e+0x1e+2x4e")])
+def test_fctp_descriptor_matches_oracle(a, b, c):
+    h = sp.fctp_create(a, b, c)
+    f = ofctp.FullyConnectedTP(a, b, c)
+    assert (h.dim_in1, h.dim_in2, h.dim_out, h.weight_numel) == (f.dim_in1, f.dim_in2, f.dim_out, f.weight_numel)
+    assert [h.path_info(p) for p in range(h.num_paths)] == [tuple(p) for p in f.paths]
+
+
+def test_fctp_errors_and_workspace():
+    raw = ctypes.c_void_p()
+    c = sp.lib.fctp_create
+    assert c(b"2x0e", b"2x0e", b"2x0e", 7, 0, 0, ctypes.byref(raw)) == sp.E_INVALID      # layout
+    assert c(b"2x0e", b"2x0e", b"2x0e", 0, 3, 0, ctypes.byref(raw)) == sp.E_INVALID      # dtype
+    assert c(b"2x0e", b"2x0e", b"2x0e", 0, 0, 4, ctypes.byref(raw)) == sp.E_INVALID      # flag
+    assert c(b"2x0q", b"2x0e", b"2x0e", 0, 0, 0, ctypes.byref(raw)) == sp.E_PARSE
+    assert c(b"0 + 1", b"0e", b"0e", 0, 0, 0, ctypes.byref(raw)) == sp.E_PARSE           # SO(3) with O(3)
+    assert c(b"1x7o", b"1x0e", b"1x7o", 0, 0, 0, ctypes.byref(raw)) == sp.E_UNSUPPORTED  # l > 6
+    # 3 x 3 -> 3 couples up to 10 component pairs per component: beyond 8
+    assert c(b"2x3o", b"1x3o", b"2x2e", 0, 0, 0, ctypes.byref(raw)) == sp.E_UNSUPPORTED
+    h = sp.fctp_create("32x0e+32x1o", "32x0e+32x1o", "32x0e+32x1o")
+    info = (ctypes.c_int64 * 4)()
+    assert sp.lib.fctp_path_info(h._h, 4, info) == sp.E_INVALID
+    assert sp.lib.fctp_query(h._h, 99, ctypes.byref(ctypes.c_int64())) == sp.E_INVALID
+    p = ctypes.c_void_p(16)
+    assert sp.lib.fctp_fwd(h._h, p, p, p, -1, p, None) == sp.E_INVALID
+    assert sp.lib.fctp_fwd(h._h, p, p, p, 3, None, None) == sp.E_INVALID
+    assert sp.lib.fctp_fwd(h._h, None, None, None, 0, None, None) == sp.OK
+    assert sp.lib.fctp_fwd(None, p, p, p, 3, p, None) == sp.E_INVALID
+    # weight gradient workspace: one partial row of weight_numel per chunk of 2048 samples
+    assert sp.fctp_bwd_workspace(h, 0) == 0
+    assert sp.fctp_bwd_workspace(h, 1) == 131072 * 4
+    assert sp.fctp_bwd_workspace(h, 4097) == 3 * 131072 * 4
+    b = sp.lib.fctp_bwd
+    assert b(h._h, p, p, p, p, 5000, None, None, p, p, 8, None) == sp.E_INVALID          # workspace small
+    assert b(h._h, p, p, p, p, 5000, None, None, p, None, 1 << 30, None) == sp.E_INVALID  # null workspace
+    assert b(h._h, p, p, None, p, 5000, p, None, None, None, 0, None) == sp.E_INVALID     # dx1 needs w
+    assert b(h._h, None, None, None, None, 0, None, None, None, None, 0, None) == sp.OK
+    assert sp.lib.fctp_destroy(None) == sp.OK
 
 
 def test_sh_argument_errors():

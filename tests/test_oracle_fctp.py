@@ -185,3 +185,18 @@ def test_output_without_paths_is_zero_and_absolute_bounds():
     y = f.fwd(x1, x2, w)
     assert f.alpha[2] == 0.0 and np.count_nonzero(y[:, 5:]) == 0
     assert np.all(np.abs(y) <= f.fwd(x1, x2, w, absolute=True) + 1e-15)
+
+
+def test_dw_entries_match_vjp():
+    f = fctp.FullyConnectedTP("3x0e+2x1o", "2x0e+1x1o", "2x0e+2x1o+1x1e")
+    rng = np.random.default_rng(8)
+    x1 = rng.normal(size=(6, f.dim_in1))
+    x2 = rng.normal(size=(6, f.dim_in2))
+    w = rng.normal(size=(1, f.weight_numel))
+    g = rng.normal(size=(6, f.dim_out))
+    for lay in ("mul_ir", "ir_mul"):
+        _, _, dw = f.vjp(x1, x2, w, g, layout=lay)
+        flat = np.arange(f.weight_numel)
+        assert np.allclose(f.dw_entries(x1, x2, g, flat, layout=lay), dw[0], atol=1e-12)
+        assert np.allclose(f.dw_entries(x1, x2, g, flat, layout=lay, absolute=True),
+                           f.vjp(x1, x2, w, g, layout=lay, absolute=True)[2][0], atol=1e-12)

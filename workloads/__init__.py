@@ -71,6 +71,18 @@ class LinearWorkload:
     num_classes: int = 0     # 0: shared weights; else class-indexed, classes sorted
 
 
+@dataclass(frozen=True)
+class FCWorkload:
+    number: int
+    name: str
+    irreps_in1: str
+    irreps_in2: str
+    irreps_out: str
+    layouts: tuple
+    dtype: str
+    n: int
+
+
 # the output irreps of the 600k-edge convolution (13 blocks, 5,504 values per
 # node), written out: the linear layer that follows the convolution mixes
 # them back to 128 channels per type
@@ -98,6 +110,11 @@ WORKLOADS = {
     7: LinearWorkload(7, "species_linear_50k_atoms_10_species", "128x0e+128x1o+128x2e+128x3o",
                       "128x0e+128x1o+128x2e+128x3o", ("ir_mul", "mul_ir"), "f32", n=50000,
                       num_classes=10),
+    # the fully connected product of the skill document's example (irreps x
+    # irreps -> irreps) at the 32-channel scalar + vector irreps of Lesson
+    # 12a's exercise 1, one row per node of a 100k-node batch
+    8: FCWorkload(8, "fctp_uvw_32x0e+32x1o_100k", "32x0e+32x1o", "32x0e+32x1o", "32x0e+32x1o",
+                  ("mul_ir", "ir_mul"), "f32", n=100000),
 }
 
 
@@ -329,3 +346,16 @@ def linear_inputs(wl, weight_numel, n=None, seed=None):
     if wl.num_classes:
         classes = np.sort(rng.integers(0, wl.num_classes, size=n)).astype(np.int32)
     return dict(x=x, w=w, classes=classes)
+
+
+def fc_inputs(wl, weight_numel, n=None, seed=None):
+    """Inputs of a fully connected product workload: x1 [n, dim_in1] and
+    x2 [n, dim_in2] N(0,1), shared weights [1, weight_numel] N(0,1) (the
+    product's own 1/sqrt(fan-in) keeps outputs at unit scale)."""
+    rng = np.random.default_rng(1000 + wl.number if seed is None else seed)
+    dt = _np_dtype(wl.dtype)
+    n = wl.n if n is None else n
+    x1 = _normal(rng, (n, _irreps_dim(wl.irreps_in1)), wl.dtype).astype(dt, copy=False)
+    x2 = _normal(rng, (n, _irreps_dim(wl.irreps_in2)), wl.dtype).astype(dt, copy=False)
+    w = _normal(rng, (1, weight_numel), wl.dtype).astype(dt, copy=False)
+    return dict(x1=x1, x2=x2, w=w)
