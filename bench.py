@@ -84,6 +84,14 @@ def stored_traffic(layout, kind="fwd"):
     return float(mb.group(1))
 
 
+_T0 = time.perf_counter()
+
+
+def note(what):
+    """Progress line on stderr (the JSON result is the only stdout line)."""
+    print(f"[bench] {what} ({time.perf_counter() - _T0:.1f} s)", file=sys.stderr, flush=True)
+
+
 def time_launches(torch, fn, steps, warmup):
     """Warm up, then time `steps` launches: total wall time bracketed by
     synchronisations, and per-launch HIP events on the launch stream."""
@@ -137,8 +145,10 @@ def main():
                     src=inp["src"][:par_e].copy(), dst=inp["dst"][:par_e].copy(), n_nodes=par_nodes)
     del inp
 
+    note("inputs ready")
     fwd = lambda: sp.tp_conv_fwd(h, x, sh, w, src, dst, n_nodes=N, out=out)
     wall, per = time_launches(torch, fwd, args.steps, args.warmup)
+    note("forward timed")
     ms_per_step = wall * 1e3 / args.steps
     avg_kernel_ms = sum(per) / len(per)
 
@@ -271,8 +281,13 @@ def main():
         del sx, ssp, sw, sout, sg, sperm, sgx, sgw, sws
 
     if not args.no_extras:
+        note("convolution variants and symmetric contraction timed")
         result["other_workloads"] = other_workloads(torch, sp, workloads, dev, args)
+        note("smaller workloads timed")
         result["linear"] = linear_layers(torch, sp, workloads, dev, args)
+        note("linear layers timed")
+        result["fctp"] = fc_product(torch, sp, workloads, dev, args)
+        note("fully connected product timed")
 
     if args.copy_calibration:
         a = torch.empty(1 << 28, dtype=torch.float32, device=dev)   # 1 GiB
@@ -297,7 +312,9 @@ def main():
                                   "sample": f"first {sample_nodes} destination nodes of the same graph "
                                             f"({n_e} edges, all 13 paths), float64 NumPy, {dt:.1f} s",
                                   "host_cpu": _cpu_model(), "host_nproc": os.cpu_count()}
+        note("oracle timed on one core")
         result["cpu_baseline_parallel"] = parallel_oracle(wl, base_inp, layout)
+        note("oracle timed on all cores")
 
     print(json.dumps(result), flush=True)
 
@@ -430,6 +447,52 @@ def linear_layers(torch, sp, workloads, dev, args):
             del g, ws
         res[wl.name] = r
         del x, w, out, cls
+    return res
+
+
+def fc_product(torch, sp, workloads, dev, args):
+    """The fully connected (uvw) product on the matrix cores, 100k samples
+    of 32x0e+32x1o x 32x0e+32x1o -> 32x0e+32x1o, both layouts.  Algorithmic
+    flops: the dense contraction over (u, v) of each path, 2 * d_o * mul1 *
+    mul2 * mul3 per sample (the couplings that build its operand are not
+    counted); the backward's three products (dx1, dx2, dW) count
+    2 * (d1 + d2 + d_o) * mul1 * mul2 * mul3."""
+    import numpy as np
+
+    from oracle import fctp as ofc   # sizes only: the path list
+    wl = workloads.WORKLOADS[8]
+    f = ofc.FullyConnectedTP(wl.irreps_in1, wl.irreps_in2, wl.irreps_out)
+    fwd_macs = bwd_macs = 0
+    for i, j, o, _ in f.paths:
+        (m1, l1, _), (m2, l2, _), (m3, l3, _) = f.in1[i], f.in2[j], f.out[o]
+        fwd_macs += (2 * l3 + 1) * m1 * m2 * m3
+        bwd_macs += (2 * l1 + 1 + 2 * l2 + 1 + 2 * l3 + 1) * m1 * m2 * m3
+    res = {}
+    for lay in wl.layouts:
+        h = sp.fctp_create(wl.irreps_in1, wl.irreps_in2, wl.irreps_out, layout=lay, dtype=wl.dtype)
+        inp = workloads.fc_inputs(wl, h.weight_numel)
+        x1, x2, w = (torch.from_numpy(np.ascontiguousarray(inp[k])).to(dev) for k in ("x1", "x2", "w"))
+        g = torch.from_numpy(workloads.output_gradient(wl.n, h.dim_out, wl.dtype, seed=2008)).to(dev)
+        out = torch.empty((wl.n, h.dim_out), dtype=torch.float32, device=dev)
+        wall, per = time_launches(torch, lambda: sp.fctp_fwd(h, x1, x2, w, out=out), args.steps, args.warmup)
+        kms = sum(per) / len(per)
+        flops = 2.0 * fwd_macs * wl.n
+        tf = flops / (kms * 1e-3) / 1e12
+        ws = torch.empty(max(1, sp.fctp_bwd_workspace(h, wl.n)), dtype=torch.uint8, device=dev)
+        wallb, perb = time_launches(torch, lambda: sp.fctp_bwd(h, x1, x2, w, g, workspace=ws), args.steps,
+                                    args.warmup)
+        kb = sum(perb) / len(perb)
+        tfb = 2.0 * bwd_macs * wl.n / (kb * 1e-3) / 1e12
+        res[lay] = {"workload": wl.name, "samples": wl.n, "ms_per_call": kms, "samples_per_s": wl.n / (wall / args.steps),
+                    "kernel": "fctp_kernel",
+                    "roofline": {"bound": "mfma", "achieved": tf, "peak": FP32_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                                 "frac": tf / FP32_MFMA_PEAK_TFLOPS, "algorithmic_flops": flops},
+                    "backward": {"ms_per_call": kb, "kernels": ["fctp_kernel (dx1)", "fctp_kernel (dx2)",
+                                                                "fctp_dw_kernel", "fctp_dw_fold_kernel"],
+                                 "roofline": {"bound": "mfma", "achieved": tfb, "peak": FP32_MFMA_PEAK_TFLOPS,
+                                              "unit": "TFLOP/s", "frac": tfb / FP32_MFMA_PEAK_TFLOPS,
+                                              "algorithmic_flops": 2.0 * bwd_macs * wl.n}}}
+        del x1, x2, w, g, out, ws
     return res
 
 
