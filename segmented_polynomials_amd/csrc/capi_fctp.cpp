@@ -70,6 +70,7 @@ struct FcPass {
   std::vector<FcRes> res;
   std::vector<FcTerm> terms;
   int tn = 32;
+  int nt = 1;                        // entry class of the launch
   size_t lds = 0;
   int64_t dim_res = 0;
   size_t res_off = 0, term_off = 0;  // within the device blob
@@ -86,12 +87,12 @@ struct segpoly_fctp {
   };
   std::vector<Path> paths;
   std::vector<double> alpha;
-  std::vector<int> path_term;     // index of each path's term in the forward pass
   int layout = 0, dtype = 0;
   unsigned flags = 0;
   int64_t dim1 = 0, dim2 = 0, dimo = 0, numel = 0;
   FcPass pass[3];                 // forward, input-1 gradient, input-2 gradient
   std::vector<FcDwPath> dw;
+  int dw_nt = 1;                  // entry class of the weight-gradient launch
   size_t dw_lds = 0, dw_off = 0, ent_off = 0;
   std::vector<FcEnt> ents;
   std::vector<unsigned char> blob;
@@ -139,10 +140,10 @@ int pick_ts(int d, size_t per_sample, size_t budget) {
   return ts >= 1 ? static_cast<int>(std::min<size_t>(ts, 16)) : 0;
 }
 
-int tn_for(int m) { return m <= 16 ? 16 : (m <= 32 ? 32 : 64); }
+int tn_for(int m) { return m <= 32 ? 32 : 64; }
 
 size_t static_b_bytes(int tn, int dtype) {
-  const int stride = tn == 16 ? 16 : tn + 16;
+  const int stride = tn + 16;
   return 2ull * 32 * stride * elt(dtype);
 }
 
@@ -195,8 +196,15 @@ int build_pass(segpoly_fctp* h, int which) {
       const int which_idx = which == 0 ? 2 : (which == 1 ? 0 : 1);
       t.T = add_entries(h->ents, real_cg(a.l, b.l, o.l), d1, d2, d3, which_idx, h->alpha[pa.o]);
       if (t.T < 0) return fail(SEGPOLY_E_UNSUPPORTED, "more than 8 couplings per component in one path");
-      t.q_div = make_fast_div(std::max(1, t.q_m));
-      if (which == 0) h->path_term[&pa - h->paths.data()] = static_cast<int>(P.terms.size());
+      if (t.p_m > t.q_m) {  // Q, held in registers along K, is the side with more channels
+        std::swap(t.p_op, t.q_op);
+        std::swap(t.p_d, t.q_d);
+        std::swap(t.p_m, t.q_m);
+        std::swap(t.p_off, t.q_off);
+        std::swap(t.s_p, t.s_q);
+        for (size_t e = t.ent; e < h->ents.size(); ++e) std::swap(h->ents[e].pa, h->ents[e].qb);
+      }
+      P.nt = std::max(P.nt, fc_t_class(t.T));
       per_sample = std::max(per_sample, (static_cast<size_t>(t.p_d) * (t.p_m + kFcPad) +
                                          static_cast<size_t>(t.q_d) * (t.q_m + kFcPad)) * elt(h->dtype));
       P.terms.push_back(t);
@@ -214,25 +222,34 @@ int build_pass(segpoly_fctp* h, int which) {
 
 int build_dw(segpoly_fctp* h) {
   if (h->paths.size() > static_cast<size_t>(kFcMaxPaths)) return fail(SEGPOLY_E_UNSUPPORTED, "more than 64 paths");
-  const FcPass& F = h->pass[0];
-  for (size_t pi = 0; pi < h->paths.size(); ++pi) {
-    const auto& pa = h->paths[pi];
-    const FcTerm* ft = &F.terms[h->path_term[pi]];  // the forward term of the path: its entries
+  for (const auto& pa : h->paths) {
     const Irrep &a = h->in1[pa.i], &b = h->in2[pa.j], &o = h->out[pa.o];
+    const int d1 = 2 * a.l + 1, d2 = 2 * b.l + 1, d3 = 2 * o.l + 1;
     FcDwPath q{};
-    q.p_d = 2 * a.l + 1, q.p_m = a.mul, q.q_d = 2 * b.l + 1, q.q_m = b.mul, q.g_d = 2 * o.l + 1, q.g_m = o.mul;
+    q.p_op = 0, q.q_op = 1;
+    q.p_d = d1, q.p_m = a.mul, q.q_d = d2, q.q_m = b.mul, q.g_d = d3, q.g_m = o.mul;
     q.p_off = h->off1[pa.i], q.q_off = h->off2[pa.j], q.g_off = h->offo[pa.o], q.w_off = pa.w_off;
-    q.T = ft->T;
-    q.ent = ft->ent;
+    q.s_p = static_cast<int64_t>(b.mul) * o.mul, q.s_q = o.mul;
+    q.ent = static_cast<int>(h->ents.size());
+    q.T = add_entries(h->ents, real_cg(a.l, b.l, o.l), d1, d2, d3, 2, h->alpha[pa.o]);
+    if (q.T < 0) return fail(SEGPOLY_E_UNSUPPORTED, "more than 8 couplings per component in one path");
+    if (q.p_m > q.q_m) {  // Q, the 32-channel side of a tile, has more channels
+      std::swap(q.p_op, q.q_op);
+      std::swap(q.p_d, q.q_d);
+      std::swap(q.p_m, q.q_m);
+      std::swap(q.p_off, q.q_off);
+      std::swap(q.s_p, q.s_q);
+      for (size_t e = q.ent; e < h->ents.size(); ++e) std::swap(h->ents[e].pa, h->ents[e].qb);
+    }
     const size_t per = (static_cast<size_t>(q.p_d) * (q.p_m + kFcPad) + static_cast<size_t>(q.q_d) * (q.q_m + kFcPad) +
                         static_cast<size_t>(q.g_d) * (q.g_m + kFcPad)) * elt(h->dtype);
     int ts = static_cast<int>(std::min<size_t>(64, kLdsLimit / per)) & ~3;
     if (ts < 4) return fail(SEGPOLY_E_UNSUPPORTED, "operand blocks too wide for the weight-gradient kernel");
     q.ts = ts;
-    const int64_t K = static_cast<int64_t>(q.p_m) * q.q_m;
-    q.m_tiles = static_cast<int>((K + kFcDwRows - 1) / kFcDwRows);
+    h->dw_nt = std::max(h->dw_nt, fc_t_class(q.T));
+    q.u_tiles = (q.p_m + kFcDwU - 1) / kFcDwU;
+    q.v_tiles = (q.q_m + kFcDwV - 1) / kFcDwV;
     q.col_tiles = (q.g_m + kFcDwCols - 1) / kFcDwCols;
-    q.q_div = make_fast_div(std::max(1, q.q_m));
     h->dw_lds = std::max(h->dw_lds, static_cast<size_t>(ts) * per);
     h->dw.push_back(q);
   }
@@ -269,7 +286,7 @@ bool fill_dw_tiles(const segpoly_fctp* h, int64_t n, FcDwTiles& t) {
   int64_t acc = 0;
   for (int p = 0; p < t.n_paths; ++p) {
     t.tile_begin[p] = static_cast<int>(acc);
-    acc += chunks * h->dw[p].m_tiles * h->dw[p].col_tiles;
+    acc += chunks * h->dw[p].u_tiles * h->dw[p].v_tiles * h->dw[p].col_tiles;
     if (acc >= kMaxGridX) return false;
   }
   t.tile_begin[t.n_paths] = static_cast<int>(acc);
@@ -296,6 +313,7 @@ int run_pass(segpoly_fctp* h, const unsigned char* db, int which, const void* x1
   a.terms = reinterpret_cast<const FcTerm*>(db + P.term_off);
   a.ents = reinterpret_cast<const FcEnt*>(db + h->ent_off);
   a.tn = P.tn;
+  a.nt = P.nt;
   a.lds_bytes = P.lds;
   a.dtype = h->dtype;
   a.layout = h->layout;
@@ -372,7 +390,6 @@ int fctp_create(const char* irreps_in1, const char* irreps_in2, const char* irre
         fan[o] += static_cast<int64_t>(a.mul) * b.mul;
       }
   h->numel = woff;
-  h->path_term.assign(h->paths.size(), 0);
   for (size_t o = 0; o < h->out.size(); ++o) h->alpha.push_back(fan[o] ? 1.0 / std::sqrt(double(fan[o])) : 0.0);
   int rc = SEGPOLY_OK;
   try {
@@ -482,6 +499,7 @@ int fctp_bwd(fctp_handle h, const void* x1, const void* x2, const void* w, const
     a.n = n;
     a.paths = reinterpret_cast<const FcDwPath*>(db + h->dw_off);
     a.ents = reinterpret_cast<const FcEnt*>(db + h->ent_off);
+    a.nt = h->dw_nt;
     a.lds_bytes = h->dw_lds;
     a.dtype = h->dtype;
     a.layout = h->layout;

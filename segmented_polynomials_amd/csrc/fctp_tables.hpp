@@ -18,25 +18,10 @@
 
 namespace segpoly {
 
-// Division of a non-negative 31-bit integer by an invariant divisor d >= 1
-// with one high multiply, an add and a shift (Granlund and Montgomery,
-// "Division by invariant integers using multiplication", 1994, round-up
-// variant): shift = ceil(log2 d), magic = floor(2^32 (2^shift - d) / d) + 1,
-// n / d = (umulhi(n, magic) + n) >> shift.
-struct FastDiv {
-  uint32_t magic;
-  int shift;
-  int d;
-};
-
-inline FastDiv make_fast_div(int d) {
-  FastDiv f{};
-  f.d = d;
-  f.shift = 0;
-  while ((1ll << f.shift) < d) ++f.shift;
-  f.magic = static_cast<uint32_t>(((uint64_t(1) << 32) * ((uint64_t(1) << f.shift) - uint64_t(d))) / uint64_t(d) + 1);
-  return f;
-}
+// Entries per (term, result component) rounded up to a compiled class: a
+// launch runs one class, the largest among its terms (smaller terms are
+// zero-padded).
+constexpr int fc_t_class(int t) { return t <= 1 ? 1 : t <= 2 ? 2 : t <= 3 ? 3 : t <= 4 ? 4 : t <= 6 ? 6 : 8; }
 
 constexpr int kFcMaxT = 8;       // coupling entries per (term, result component)
 constexpr int kFcMaxRes = 32;    // result blocks per pass
@@ -44,6 +29,8 @@ constexpr int kFcRowsMax = 128;  // rows (sample, component) per tile
 constexpr int kFcPad = 1;        // LDS padding of each staged channel row
 constexpr int kFcDwChunk = 2048; // samples per weight-gradient partial sum
 
+// P is the operand with fewer channels (one channel per K chunk), Q the one
+// with more (a window of channels per K chunk, held in registers).
 struct FcTerm {
   int p_op, q_op;           // operand of P and Q: 0 = input 1, 1 = input 2, 2 = output gradient
   int p_d, p_m, q_d, q_m;   // components and channels of the two blocks
@@ -52,7 +39,6 @@ struct FcTerm {
   int64_t s_p, s_q, s_r;    // weight strides of channel p, channel q, result channel
   int T;                    // entries per result component (zero-padded)
   int ent;                  // first entry: [result component][T]
-  FastDiv q_div;            // division by q_m (K index -> (p, q))
 };
 
 struct FcEnt {
@@ -75,25 +61,31 @@ struct FcTiles {
   int tile_begin[kFcMaxRes + 1];
 };
 
-// Weight gradient: one term per path seen as a GEMM with rows (u, v) =
-// (input-1 channel, input-2 channel), K = (sample, output component) and
-// columns w (output channel); P = input 1, Q = input 2, G = output gradient.
+// Weight gradient: one term per path seen as a GEMM with rows (p, q) (a
+// channel of P and one of Q: input 1 and input 2, Q the one with more
+// channels), K = (output component, sample) and columns w (output channel):
+//   dW[w_off + p s_p + q s_q + w] = sum over samples n and components k of
+//       sum over the entries e of k of coef_e P[n, pa_e, p] Q[n, qb_e, q] g[n, o, k, w].
+// A workgroup tile is kFcDwU channels p x kFcDwV channels q x kFcDwCols
+// columns; each wave owns 2 p x 32 q.
 struct FcDwPath {
+  int p_op, q_op;           // 0 = input 1, 1 = input 2
   int p_d, p_m, q_d, q_m, g_d, g_m;
   int64_t p_off, q_off, g_off, w_off;
-  int T, ent;               // entries [output component][T] (the forward's)
+  int64_t s_p, s_q;         // weight strides of channel p and channel q
+  int T, ent;               // entries [output component][T]
   int ts;                   // samples staged at a time (a multiple of 4)
-  int m_tiles;              // tiles of kFcDwRows rows (u, v)
+  int u_tiles, v_tiles;     // tiles of kFcDwU channels p and kFcDwV channels q
   int col_tiles;            // tiles of kFcDwCols columns w
-  FastDiv q_div;            // division by q_m (row -> (u, v))
 };
 
-constexpr int kFcDwRows = 256;   // (u, v) rows per weight-gradient tile
+constexpr int kFcDwU = 8;        // P channels per weight-gradient tile (2 per wave)
+constexpr int kFcDwV = 32;       // Q channels per weight-gradient tile
 constexpr int kFcDwCols = 32;    // output channels per weight-gradient tile
 constexpr int kFcMaxPaths = 64;
 
 // Per call: path p owns tiles [tile_begin[p], tile_begin[p + 1]), ordered
-// (sample chunk, row tile, column tile).
+// (sample chunk, u tile, v tile, column tile).
 struct FcDwTiles {
   int n_paths;
   int chunks;                    // sample chunks of kFcDwChunk
@@ -110,7 +102,8 @@ struct FcArgs {
   const FcRes* res_tab;     // device tables
   const FcTerm* terms;
   const FcEnt* ents;
-  int tn;                   // column tile width: 16, 32 or 64
+  int tn;                   // column tile width: 32 or 64
+  int nt;                   // entry class (fc_t_class)
   size_t lds_bytes;
   int dtype, layout;
   void* stream;
@@ -127,12 +120,22 @@ struct FcDwArgs {
   int64_t n;
   const FcDwPath* paths;    // device
   const FcEnt* ents;
+  int nt;                   // entry class (fc_t_class)
   size_t lds_bytes;
   int dtype, layout;
   void* stream;
 };
 
-int launch_fctp(const FcArgs& a, const FcTiles& t);
-int launch_fctp_dw(const FcDwArgs& a, const FcDwTiles& t);
+int launch_fctp_f32(const FcArgs& a, const FcTiles& t);
+int launch_fctp_f64(const FcArgs& a, const FcTiles& t);
+int launch_fctp_dw_f32(const FcDwArgs& a, const FcDwTiles& t);
+int launch_fctp_dw_f64(const FcDwArgs& a, const FcDwTiles& t);
+
+inline int launch_fctp(const FcArgs& a, const FcTiles& t) {
+  return a.dtype == kF32 ? launch_fctp_f32(a, t) : launch_fctp_f64(a, t);
+}
+inline int launch_fctp_dw(const FcDwArgs& a, const FcDwTiles& t) {
+  return a.dtype == kF32 ? launch_fctp_dw_f32(a, t) : launch_fctp_dw_f64(a, t);
+}
 
 }  // namespace segpoly

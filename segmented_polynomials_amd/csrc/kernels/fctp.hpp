@@ -1,0 +1,523 @@
+// Fully connected ("uvw") tensor product on the matrix cores (gfx950 MFMA).
+//
+// cuequivariance-torch skill document, "CPU tensor product and backward"
+// (FullyConnectedTensorProduct with weights and gradients of both inputs)
+// and e3nn-course Lesson 12a, exercise 1 (every input-1 channel u couples
+// with every input-2 channel v into every output channel w, so a path holds
+// mul1 * mul2 * mul3 weights).  For an output block o:
+//   out[n, o, k, w] = sum over paths (i, j, o) of
+//                     sum_(u, v) W_p[u, v, w] A_p[n, k, (u, v)],
+//   A_p[n, k, (u, v)] = alpha_o sum_(a, b) C_p[a, b, k] x1[n, i, a, u] x2[n, j, b, v]:
+// per output block a GEMM with rows (n, k), K = (u, v) and columns w.  The
+// A operand never exists in memory: each lane builds its MFMA operand from
+// the two input blocks staged in LDS (a handful of non-zero couplings per
+// row), and the weight segment is the B operand.  The input gradients are
+// the same GEMM with other operands (fctp_tables.hpp): dx1 rows (n, a),
+// K = (v, w), A from x2 and the output gradient; dx2 likewise.
+//
+// fctp_kernel: a workgroup of 4 waves owns up to 128 rows (whole samples)
+// and TN columns of one result block; each wave owns two 16-row MFMA tiles
+// and all TN / 16 column tiles (v_mfma_*_16x16x4).  Per term the two
+// operand blocks of the tile's samples are staged in LDS once; the operand
+// with more channels (Q) is held in registers a window of channels at a
+// time (fc_term), and the weight segment streams through a double-buffered
+// LDS chunk.
+//
+// fctp_dw_kernel: the weight gradient dW_p[(u, v), w] = sum over samples and
+// output components (n, k) of A_p[n, k, (u, v)] g[n, o, k, w]: rows (u, v),
+// K = (k, n) in staged groups of samples, A^T built per lane from the
+// staged blocks (the K step keeps one k for all four lane groups, so the
+// coupling entries are wave-uniform), B = the staged output gradient.
+// Partial sums per chunk of samples, folded in chunk order.
+#pragma once
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "../fctp_tables.hpp"
+#include "../launch.hpp"
+#include "mfma.hpp"
+
+namespace segpoly {
+namespace kern {
+
+constexpr int kFcThreads = 256;
+constexpr int kFcTK = 32;  // K rows per staged weight chunk (8 MFMA steps)
+
+// B rows of TN + 16 elements: the four K rows one MFMA
+// step reads start 16 banks apart.
+template <int TN>
+struct FcB {
+  static constexpr int stride = TN + 16;
+};
+
+// Stage `ns` samples (rows s0 ..) of one operand block into LDS as
+// [sample][component][channel + kFcPad]; samples at or past n read as zero.
+template <typename T, int LAYOUT>
+__device__ __forceinline__ void fc_stage(const T* __restrict__ src, int64_t sdim, int64_t boff, int bd, int bm,
+                                         int64_t s0, int ns, int64_t n, T* dst, int tid) {
+  const int blk = bd * bm;
+  const int cstride = bm + kFcPad, sstride = bd * cstride;
+  if (blk <= kFcThreads) {
+    const int spp = kFcThreads / blk;  // samples per pass
+    const int sp = tid / blk, rem = tid - sp * blk;
+    if (sp >= spp) return;
+    int a, u;
+    if (LAYOUT == kIrMul) {
+      a = rem / bm;
+      u = rem - a * bm;
+    } else {
+      u = rem / bd;
+      a = rem - u * bd;
+    }
+    const int li = a * cstride + u;
+    for (int s = sp; s < ns; s += spp) {
+      const int64_t row = s0 + s;
+      dst[s * sstride + li] = row < n ? src[row * sdim + boff + rem] : T(0);
+    }
+  } else {
+    for (int rem = tid; rem < blk; rem += kFcThreads) {
+      int a, u;
+      if (LAYOUT == kIrMul) {
+        a = rem / bm;
+        u = rem - a * bm;
+      } else {
+        u = rem / bd;
+        a = rem - u * bd;
+      }
+      const int li = a * cstride + u;
+      for (int s = 0; s < ns; ++s) {
+        const int64_t row = s0 + s;
+        dst[s * sstride + li] = row < n ? src[row * sdim + boff + rem] : T(0);
+      }
+    }
+  }
+}
+
+// One term of a result tile: K runs over chunks (vc, u) -- vc outer, a
+// window of VK = 4 VS channels v of the register operand Q, u one channel
+// of the scalar operand P.  Per lane and row tile the window's Q values
+// (Qreg[t][s] = Q[sample, qb_t, v0 + 4 s + lane / 16]) stay in registers
+// while u runs, so one MFMA step costs NT FMAs: A = sum_t y_t Qreg[t][s]
+// with y_t = coef_t P[sample, pa_t, u] formed once per chunk.  The
+// weight rows of the next chunk are fetched into registers while the
+// current chunk multiplies, then written to the other LDS buffer.
+template <typename T, int TN, int NT>
+__device__ __forceinline__ void fc_term(const FcTerm& Tm, const FcEnt* __restrict__ ents, const T* __restrict__ w,
+                                        const T* Ps, const T* Qs, T (*Bs)[kFcTK][FcB<TN>::stride], int m_res,
+                                        int c0, const int (&sl)[2], const int (&kc)[2], const bool (&rv)[2],
+                                        bool has0, bool has1, int tid, int lane,
+                                        typename Mfma<T>::acc_t (&acc)[2][TN / 16]) {
+  using M = Mfma<T>;
+  constexpr int kNT = TN / 16;
+  constexpr int VS = NT <= 4 ? 8 : 4;       // MFMA steps per chunk
+  constexpr int VK = 4 * VS;                // K rows per chunk
+  constexpr int kBPer = VK * TN / kFcThreads;
+  static_assert(kBPer >= 1 && (VK * TN) % kFcThreads == 0, "weight chunk must split over the workgroup");
+  const int pcs = Tm.p_m + kFcPad, qcs = Tm.q_m + kFcPad;
+  const int pss = Tm.p_d * pcs, qss = Tm.q_d * qcs;
+
+  // entries of this lane's rows: P offset (without the channel), Q offset,
+  // coefficient (zero for padding and rows past the tile)
+  int po[2][NT], qo[2][NT];
+  T cf[2][NT];
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+    for (int e = 0; e < NT; ++e) {
+      po[rt][e] = 0;
+      qo[rt][e] = 0;
+      cf[rt][e] = T(0);
+      if (e < Tm.T) {
+        const FcEnt E = ents[Tm.ent + kc[rt] * Tm.T + e];
+        po[rt][e] = sl[rt] * pss + E.pa * pcs;
+        qo[rt][e] = sl[rt] * qss + E.qb * qcs;
+        cf[rt][e] = rv[rt] ? static_cast<T>(E.c) : T(0);
+      }
+    }
+
+  T qreg[2][NT][VS];
+  auto load_q = [&](int vc, int win) {
+#pragma unroll
+    for (int s = 0; s < VS; ++s) {
+      const int v = vc * win + 4 * s + lane / 16;
+      const bool ok = 4 * s < win && v < Tm.q_m;
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+        for (int e = 0; e < NT; ++e) qreg[rt][e][s] = ok ? Qs[qo[rt][e] + v] : T(0);
+    }
+  };
+
+  const bool c_fast = Tm.s_r == 1;
+  T rb[kBPer];
+  auto fetch = [&](int u, int vc, int win) {
+#pragma unroll
+    for (int i = 0; i < kBPer; ++i) {
+      const int e = i * kFcThreads + tid;
+      const int kk = c_fast ? e / TN : e % VK;
+      const int cc = c_fast ? e % TN : e / VK;
+      const int v = vc * win + kk, col = c0 + cc;
+      rb[i] = (kk < win && v < Tm.q_m && col < m_res) ? w[Tm.w_off + u * Tm.s_p + v * Tm.s_q + col * Tm.s_r]
+                                                       : T(0);
+    }
+  };
+  auto put = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < kBPer; ++i) {
+      const int e = i * kFcThreads + tid;
+      const int kk = c_fast ? e / TN : e % VK;
+      const int cc = c_fast ? e % TN : e / VK;
+      Bs[buf][kk][cc] = rb[i];
+    }
+  };
+
+  // window of the Q channels: VK, or q_m rounded up to 4 if smaller
+  const int win = Tm.q_m + 3 < VK ? ((Tm.q_m + 3) & ~3) : VK;
+  const int steps = win / 4;
+  const int nvc = (Tm.q_m + win - 1) / win;
+  const int nch = nvc * Tm.p_m;
+  if (nch == 0) return;
+  fetch(0, 0, win);
+  put(0);
+  __syncthreads();
+  load_q(0, win);
+  int u = 0, vc = 0;
+  for (int ch = 0; ch < nch; ++ch) {
+    int un = u + 1, vcn = vc;
+    if (un == Tm.p_m) {
+      un = 0;
+      ++vcn;
+    }
+    if (ch + 1 < nch) fetch(un, vcn, win);
+    const int buf = ch & 1;
+    T y[2][NT];
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+      for (int e = 0; e < NT; ++e) y[rt][e] = cf[rt][e] * Ps[po[rt][e] + u];
+#pragma unroll
+    for (int s = 0; s < VS; ++s) {
+      if (s >= steps) break;
+      T b[kNT];
+#pragma unroll
+      for (int j = 0; j < kNT; ++j) b[j] = Bs[buf][4 * s + lane / 16][j * 16 + lane % 16];
+      T a[2];
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt) {
+        T t = y[rt][0] * qreg[rt][0][s];
+#pragma unroll
+        for (int e = 1; e < NT; ++e) t += y[rt][e] * qreg[rt][e][s];
+        a[rt] = t;
+      }
+      if (has0) {
+#pragma unroll
+        for (int j = 0; j < kNT; ++j) acc[0][j] = M::mma(a[0], b[j], acc[0][j]);
+      }
+      if (has1) {
+#pragma unroll
+        for (int j = 0; j < kNT; ++j) acc[1][j] = M::mma(a[1], b[j], acc[1][j]);
+      }
+    }
+    if (ch + 1 < nch) put(buf ^ 1);
+    __syncthreads();
+    if (vcn != vc && ch + 1 < nch) load_q(vcn, win);
+    u = un;
+    vc = vcn;
+  }
+}
+
+template <typename T, int LAYOUT, int TN, int NT>
+__global__ void __launch_bounds__(kFcThreads)
+fctp_kernel(const T* __restrict__ op0, const T* __restrict__ op1, const T* __restrict__ op2, int64_t dim0,
+            int64_t dim1, int64_t dim2, const T* __restrict__ w, T* __restrict__ res, int64_t dim_res, int64_t n,
+            const FcRes* __restrict__ rtab, const FcTerm* __restrict__ terms, const FcEnt* __restrict__ ents,
+            FcTiles tiles) {
+  using M = Mfma<T>;
+  constexpr int kNT = TN / 16;
+  extern __shared__ __align__(16) unsigned char fc_smem[];
+  __shared__ T Bs[2][kFcTK][FcB<TN>::stride];
+
+  const int bid = blockIdx.x;
+  int r = 0;
+  while (r + 1 < tiles.n_res && tiles.tile_begin[r + 1] <= bid) ++r;
+  const FcRes R = rtab[r];
+  const int local = bid - tiles.tile_begin[r];
+  const int trow = local / R.col_tiles, tcol = local - trow * R.col_tiles;
+  const int64_t s0 = static_cast<int64_t>(trow) * R.ts;
+  const int ts = static_cast<int>(n - s0 < R.ts ? n - s0 : R.ts);  // samples in this tile (>= 1)
+  const int d = R.d;
+  const int rows = ts * d;
+  const int c0 = tcol * TN;
+
+  const int tid = threadIdx.x, lane = tid % 64, wave = tid / 64;
+  const bool has0 = wave * 16 < rows, has1 = (wave + 4) * 16 < rows;  // wave-uniform
+  int sl[2], kc[2];
+  bool rv[2];
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt) {
+    const int row = (wave + 4 * rt) * 16 + lane % 16;
+    rv[rt] = row < rows;
+    sl[rt] = rv[rt] ? row / d : 0;
+    kc[rt] = rv[rt] ? row - sl[rt] * d : 0;
+  }
+
+  typename M::acc_t acc[2][kNT];
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+    for (int j = 0; j < kNT; ++j) acc[rt][j] = typename M::acc_t{0, 0, 0, 0};
+
+  T* Ps = reinterpret_cast<T*>(fc_smem);
+  for (int t = R.term_begin; t < R.term_end; ++t) {
+    const FcTerm Tm = terms[t];
+    T* Qs = Ps + R.ts * (Tm.p_d * (Tm.p_m + kFcPad));
+    const T* P = Tm.p_op == 0 ? op0 : (Tm.p_op == 1 ? op1 : op2);
+    const T* Q = Tm.q_op == 0 ? op0 : (Tm.q_op == 1 ? op1 : op2);
+    const int64_t pdim = Tm.p_op == 0 ? dim0 : (Tm.p_op == 1 ? dim1 : dim2);
+    const int64_t qdim = Tm.q_op == 0 ? dim0 : (Tm.q_op == 1 ? dim1 : dim2);
+    __syncthreads();  // the previous term's LDS reads are done
+    fc_stage<T, LAYOUT>(P, pdim, Tm.p_off, Tm.p_d, Tm.p_m, s0, ts, n, Ps, tid);
+    fc_stage<T, LAYOUT>(Q, qdim, Tm.q_off, Tm.q_d, Tm.q_m, s0, ts, n, Qs, tid);
+    // (fc_term's first barrier publishes the staged blocks)
+    fc_term<T, TN, NT>(Tm, ents, w, Ps, Qs, Bs, R.m, c0, sl, kc, rv, has0, has1, tid, lane, acc);
+  }
+
+  // epilogue: rows (sample, component), columns c0 + ..
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt) {
+    if (!(rt == 0 ? has0 : has1)) continue;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int row = (wave + 4 * rt) * 16 + M::row(lane, q);
+      if (row >= rows) continue;
+      const int s = row / d, k = row - s * d;
+      T* orow = res + (s0 + s) * dim_res + R.off;
+#pragma unroll
+      for (int j = 0; j < kNT; ++j) {
+        const int col = c0 + j * 16 + lane % 16;
+        if (col < R.m) {
+          const int64_t off = LAYOUT == kIrMul ? static_cast<int64_t>(k) * R.m + col : static_cast<int64_t>(col) * d + k;
+          orow[off] = acc[rt][j][q];
+        }
+      }
+    }
+  }
+}
+
+// Weight-gradient partials of one tile: part[chunk][w_off + p s_p + q s_q + w].
+// The wave's rows are 2 channels p (u0, u0 + 1) x 32 channels q; a lane
+// owns q = v0 + lane % 16 and v0 + 16 + lane % 16, so its four row tiles
+// need 2 NT values of P and 2 NT of Q per K step (one sample, one output
+// component k: the entries of k are the same for the whole wave).
+template <typename T, int NT>
+__device__ __forceinline__ void fc_dw_tile(const FcDwPath& P, const FcEnt* __restrict__ ents, const T* Ps,
+                                           const T* Qs, const T* Gs, int nsp, int k, int u0, int v0, int col,
+                                           int lane, typename Mfma<T>::acc_t (&acc)[4][kFcDwCols / 16]) {
+  using M = Mfma<T>;
+  constexpr int kNT = kFcDwCols / 16;
+  const int pcs = P.p_m + kFcPad, qcs = P.q_m + kFcPad, gcs = P.g_m + kFcPad;
+  const int pss = P.p_d * pcs, qss = P.q_d * qcs, gss = P.g_d * gcs;
+  int pa[NT], qb[NT];
+  T cf[NT];
+#pragma unroll
+  for (int e = 0; e < NT; ++e) {
+    pa[e] = 0;
+    qb[e] = 0;
+    cf[e] = T(0);
+    if (e < P.T) {
+      const FcEnt E = ents[P.ent + k * P.T + e];
+      pa[e] = E.pa * pcs;
+      qb[e] = E.qb * qcs;
+      cf[e] = static_cast<T>(E.c);
+    }
+  }
+  // this lane's channels (clamped reads; invalid ones contribute zero)
+  bool pok[2], qok[2];
+  int pu[2], qv[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    pok[i] = u0 + i < P.p_m;
+    pu[i] = pok[i] ? u0 + i : 0;
+    qok[i] = v0 + 16 * i + lane % 16 < P.q_m;
+    qv[i] = qok[i] ? v0 + 16 * i + lane % 16 : 0;
+  }
+  bool gok[kNT];
+#pragma unroll
+  for (int j = 0; j < kNT; ++j) gok[j] = col + 16 * j < P.g_m;
+  for (int s4 = 0; s4 < nsp; s4 += 4) {
+    const int s = s4 + lane / 16;
+    T y[2][NT], z[2][NT];
+#pragma unroll
+    for (int e = 0; e < NT; ++e) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        y[i][e] = pok[i] ? cf[e] * Ps[s * pss + pa[e] + pu[i]] : T(0);
+        z[i][e] = qok[i] ? Qs[s * qss + qb[e] + qv[i]] : T(0);
+      }
+    }
+    T b[kNT];
+#pragma unroll
+    for (int j = 0; j < kNT; ++j) b[j] = gok[j] ? Gs[s * gss + k * gcs + col + 16 * j] : T(0);
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        T a = y[i][0] * z[h][0];
+#pragma unroll
+        for (int e = 1; e < NT; ++e) a += y[i][e] * z[h][e];
+#pragma unroll
+        for (int j = 0; j < kNT; ++j) acc[2 * i + h][j] = M::mma(a, b[j], acc[2 * i + h][j]);
+      }
+  }
+}
+
+template <typename T, int LAYOUT, int NT>
+__global__ void __launch_bounds__(kFcThreads)
+fctp_dw_kernel(const T* __restrict__ x1, const T* __restrict__ x2, const T* __restrict__ g, int64_t dim1,
+               int64_t dim2, int64_t dimo, T* __restrict__ part, int64_t numel, int64_t n,
+               const FcDwPath* __restrict__ paths, const FcEnt* __restrict__ ents, FcDwTiles tiles) {
+  using M = Mfma<T>;
+  constexpr int kNT = kFcDwCols / 16;
+  extern __shared__ __align__(16) unsigned char fc_smem[];
+
+  const int bid = blockIdx.x;
+  int pi = 0;
+  while (pi + 1 < tiles.n_paths && tiles.tile_begin[pi + 1] <= bid) ++pi;
+  const FcDwPath P = paths[pi];
+  int local = bid - tiles.tile_begin[pi];
+  const int per_chunk = P.u_tiles * P.v_tiles * P.col_tiles;
+  const int chunk = local / per_chunk;
+  local -= chunk * per_chunk;
+  const int ut = local / (P.v_tiles * P.col_tiles);
+  local -= ut * (P.v_tiles * P.col_tiles);
+  const int vt = local / P.col_tiles, ct = local - vt * P.col_tiles;
+  const int64_t n_begin = static_cast<int64_t>(chunk) * kFcDwChunk;
+  const int64_t n_end = n_begin + kFcDwChunk < n ? n_begin + kFcDwChunk : n;
+
+  const int tid = threadIdx.x, lane = tid % 64, wave = tid / 64;
+  const int u0 = ut * kFcDwU + 2 * wave, v0 = vt * kFcDwV, c0 = ct * kFcDwCols;
+  const int col = c0 + lane % 16;
+  const int pcs = P.p_m + kFcPad, qcs = P.q_m + kFcPad;
+  T* Ps = reinterpret_cast<T*>(fc_smem);
+  T* Qs = Ps + P.ts * (P.p_d * pcs);
+  T* Gs = Qs + P.ts * (P.q_d * qcs);
+  const T* Pg = P.p_op == 0 ? x1 : x2;
+  const T* Qg = P.q_op == 0 ? x1 : x2;
+  const int64_t pdim = P.p_op == 0 ? dim1 : dim2, qdim = P.q_op == 0 ? dim1 : dim2;
+  const bool wave_any = u0 < P.p_m;  // wave-uniform
+
+  typename M::acc_t acc[4][kNT];
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+#pragma unroll
+    for (int j = 0; j < kNT; ++j) acc[r][j] = typename M::acc_t{0, 0, 0, 0};
+
+  for (int64_t sb = n_begin; sb < n_end; sb += P.ts) {
+    const int ns = static_cast<int>(n_end - sb < P.ts ? n_end - sb : P.ts);
+    const int nsp = (ns + 3) & ~3;  // staged samples (zero rows up to a multiple of 4)
+    __syncthreads();
+    fc_stage<T, LAYOUT>(Pg, pdim, P.p_off, P.p_d, P.p_m, sb, nsp, n_end, Ps, tid);
+    fc_stage<T, LAYOUT>(Qg, qdim, P.q_off, P.q_d, P.q_m, sb, nsp, n_end, Qs, tid);
+    fc_stage<T, LAYOUT>(g, dimo, P.g_off, P.g_d, P.g_m, sb, nsp, n_end, Gs, tid);
+    __syncthreads();
+    if (!wave_any) continue;
+    for (int k = 0; k < P.g_d; ++k) {
+      fc_dw_tile<T, NT>(P, ents, Ps, Qs, Gs, nsp, k, u0, v0, col, lane, acc);
+    }
+  }
+  if (!wave_any) return;
+  // accumulator j of row tile (i, h): rows = the 16 q of half h for channel
+  // p = u0 + i (M::row gives the q within the half), column col + 16 j
+  T* prow = part + static_cast<int64_t>(chunk) * numel + P.w_off;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    if (u0 + i >= P.p_m) continue;
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int qq = v0 + 16 * h + M::row(lane, q);
+        if (qq >= P.q_m) continue;
+#pragma unroll
+        for (int j = 0; j < kNT; ++j) {
+          const int cj = col + 16 * j;
+          if (cj < P.g_m) prow[(u0 + i) * P.s_p + qq * P.s_q + cj] = acc[2 * i + h][j][q];
+        }
+      }
+  }
+}
+
+// dw[e] = sum over chunks c (in order) of part[c][e].
+template <typename T>
+__global__ void __launch_bounds__(256)
+fctp_dw_fold_kernel(const T* __restrict__ part, int chunks, int64_t numel, T* __restrict__ dw) {
+  for (int64_t e = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; e < numel;
+       e += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    T acc = T(0);
+    for (int c = 0; c < chunks; ++c) acc += part[c * numel + e];
+    dw[e] = acc;
+  }
+}
+
+template <typename T, int LAYOUT, int TN, int NT>
+int fctp_launch_k(const FcArgs& a, const FcTiles& t) {
+  const int total = t.tile_begin[t.n_res];
+  if (total == 0) return 0;
+  hipLaunchKernelGGL((fctp_kernel<T, LAYOUT, TN, NT>), dim3(static_cast<unsigned>(total)), dim3(kFcThreads),
+                     a.lds_bytes, static_cast<hipStream_t>(a.stream), static_cast<const T*>(a.op[0]),
+                     static_cast<const T*>(a.op[1]), static_cast<const T*>(a.op[2]), a.dim[0], a.dim[1], a.dim[2],
+                     static_cast<const T*>(a.w), static_cast<T*>(a.res), a.dim_res, a.n, a.res_tab, a.terms, a.ents,
+                     t);
+  return static_cast<int>(hipGetLastError());
+}
+
+template <typename T, int LAYOUT, int TN>
+int fctp_launch_tn(const FcArgs& a, const FcTiles& t) {
+  switch (a.nt) {
+    case 1: return fctp_launch_k<T, LAYOUT, TN, 1>(a, t);
+    case 2: return fctp_launch_k<T, LAYOUT, TN, 2>(a, t);
+    case 3: return fctp_launch_k<T, LAYOUT, TN, 3>(a, t);
+    case 4: return fctp_launch_k<T, LAYOUT, TN, 4>(a, t);
+    case 6: return fctp_launch_k<T, LAYOUT, TN, 6>(a, t);
+    default: return fctp_launch_k<T, LAYOUT, TN, 8>(a, t);
+  }
+}
+
+template <typename T, int LAYOUT>
+int fctp_launch(const FcArgs& a, const FcTiles& t) {
+  return a.tn == 32 ? fctp_launch_tn<T, LAYOUT, 32>(a, t) : fctp_launch_tn<T, LAYOUT, 64>(a, t);
+}
+
+template <typename T, int LAYOUT, int NT>
+int fctp_dw_launch_k(const FcDwArgs& a, const FcDwTiles& t) {
+  const int total = t.tile_begin[t.n_paths];
+  if (total == 0) return 0;
+  hipLaunchKernelGGL((fctp_dw_kernel<T, LAYOUT, NT>), dim3(static_cast<unsigned>(total)), dim3(kFcThreads),
+                     a.lds_bytes, static_cast<hipStream_t>(a.stream), static_cast<const T*>(a.x1),
+                     static_cast<const T*>(a.x2), static_cast<const T*>(a.g), a.dim1, a.dim2, a.dimo,
+                     static_cast<T*>(a.part), a.numel, a.n, a.paths, a.ents, t);
+  return static_cast<int>(hipGetLastError());
+}
+
+template <typename T, int LAYOUT>
+int fctp_dw_launch(const FcDwArgs& a, const FcDwTiles& t) {
+  int rc = 0;
+  switch (a.nt) {
+    case 1: rc = fctp_dw_launch_k<T, LAYOUT, 1>(a, t); break;
+    case 2: rc = fctp_dw_launch_k<T, LAYOUT, 2>(a, t); break;
+    case 3: rc = fctp_dw_launch_k<T, LAYOUT, 3>(a, t); break;
+    case 4: rc = fctp_dw_launch_k<T, LAYOUT, 4>(a, t); break;
+    case 6: rc = fctp_dw_launch_k<T, LAYOUT, 6>(a, t); break;
+    default: rc = fctp_dw_launch_k<T, LAYOUT, 8>(a, t); break;
+  }
+  if (rc || a.numel == 0) return rc;
+  const int64_t blocks = (a.numel + 255) / 256;
+  hipLaunchKernelGGL((fctp_dw_fold_kernel<T>), dim3(static_cast<unsigned>(blocks < 2048 ? blocks : 2048)),
+                     dim3(256), 0, static_cast<hipStream_t>(a.stream), static_cast<const T*>(a.part), t.chunks,
+                     a.numel, static_cast<T*>(a.dw));
+  return static_cast<int>(hipGetLastError());
+}
+
+}  // namespace kern
+}  // namespace segpoly
