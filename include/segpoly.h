@@ -433,7 +433,7 @@ int fctp_bwd_workspace(fctp_handle h, int64_t n, size_t* bytes);
  * fctp_bwd: vector-Jacobian product of fctp_fwd for g = dL/d(out):
  *   grad_x1 [n, DIM_IN1], grad_x2 [n, DIM_IN2], grad_w [1, WEIGHT_NUMEL],
  * each fully overwritten, or NULL (not computed).  grad_w needs
- * `workspace` of fctp_bwd_workspace(n) bytes; it sums fixed chunks of 2048
+ * `workspace` of fctp_bwd_workspace(n) bytes; it sums fixed chunks of 1024
  * samples and then the chunks in order (deterministic).  Inputs a requested
  * gradient does not read may be NULL (grad_x1 reads x2, g, w; grad_x2 reads
  * x1, g, w; grad_w reads x1, x2, g).

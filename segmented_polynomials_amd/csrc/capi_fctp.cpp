@@ -25,7 +25,7 @@ using namespace segpoly;
 
 namespace {
 
-constexpr size_t kLdsLimit = 64 * 1024;  // per workgroup (two workgroups fit a CU)
+constexpr size_t kLdsLimit = 52 * 1024;  // per workgroup (three workgroups fit a CU's 160 KB)
 constexpr int kMaxL = 6;
 
 // A term without a parity letter is an SO(3) irrep (parity 0: the parity
@@ -205,8 +205,7 @@ int build_pass(segpoly_fctp* h, int which) {
         for (size_t e = t.ent; e < h->ents.size(); ++e) std::swap(h->ents[e].pa, h->ents[e].qb);
       }
       P.nt = std::max(P.nt, fc_t_class(t.T));
-      per_sample = std::max(per_sample, (static_cast<size_t>(t.p_d) * (t.p_m + kFcPad) +
-                                         static_cast<size_t>(t.q_d) * (t.q_m + kFcPad)) * elt(h->dtype));
+      per_sample = std::max(per_sample, static_cast<size_t>(fc_sample_stride(t.p_d, t.p_m)) * elt(h->dtype));
       P.terms.push_back(t);
     }
     R.term_end = static_cast<int>(P.terms.size());
@@ -241,8 +240,8 @@ int build_dw(segpoly_fctp* h) {
       std::swap(q.s_p, q.s_q);
       for (size_t e = q.ent; e < h->ents.size(); ++e) std::swap(h->ents[e].pa, h->ents[e].qb);
     }
-    const size_t per = (static_cast<size_t>(q.p_d) * (q.p_m + kFcPad) + static_cast<size_t>(q.q_d) * (q.q_m + kFcPad) +
-                        static_cast<size_t>(q.g_d) * (q.g_m + kFcPad)) * elt(h->dtype);
+    const size_t per = (static_cast<size_t>(fc_sample_stride(q.p_d, q.p_m)) + fc_sample_stride(q.q_d, q.q_m) +
+                        fc_sample_stride(q.g_d, q.g_m)) * elt(h->dtype);
     int ts = static_cast<int>(std::min<size_t>(64, kLdsLimit / per)) & ~3;
     if (ts < 4) return fail(SEGPOLY_E_UNSUPPORTED, "operand blocks too wide for the weight-gradient kernel");
     q.ts = ts;

@@ -27,7 +27,16 @@ constexpr int kFcMaxT = 8;       // coupling entries per (term, result component
 constexpr int kFcMaxRes = 32;    // result blocks per pass
 constexpr int kFcRowsMax = 128;  // rows (sample, component) per tile
 constexpr int kFcPad = 1;        // LDS padding of each staged channel row
-constexpr int kFcDwChunk = 2048; // samples per weight-gradient partial sum
+constexpr int kFcDwChunk = 1024; // samples per weight-gradient partial sum
+
+// LDS stride of one staged sample ([component][channel + kFcPad]), rounded up
+// to 16 mod 32 elements: the four samples one MFMA step reads (lane / 16)
+// then start 16 banks apart in float (32 in double), so a 16-lane row of
+// consecutive channels never shares a bank with another sample's.
+constexpr int fc_sample_stride(int d, int m) {
+  const int base = d * (m + kFcPad);
+  return base + ((16 - base % 32) + 32) % 32;
+}
 
 // P is the operand with fewer channels (one channel per K chunk), Q the one
 // with more (a window of channels per K chunk, held in registers).

@@ -17,9 +17,9 @@
 //
 // fctp_kernel: a workgroup of 4 waves owns up to 128 rows (whole samples)
 // and TN columns of one result block; each wave owns two 16-row MFMA tiles
-// and all TN / 16 column tiles (v_mfma_*_16x16x4).  Per term the two
-// operand blocks of the tile's samples are staged in LDS once; the operand
-// with more channels (Q) is held in registers a window of channels at a
+// and all TN / 16 column tiles (v_mfma_*_16x16x4).  Per term the operand
+// block with fewer channels (P) of the tile's samples is staged in LDS; the
+// one with more channels (Q) is held in registers a window of channels at a
 // time (fc_term), and the weight segment streams through a double-buffered
 // LDS chunk.
 //
@@ -52,12 +52,13 @@ struct FcB {
 };
 
 // Stage `ns` samples (rows s0 ..) of one operand block into LDS as
-// [sample][component][channel + kFcPad]; samples at or past n read as zero.
+// [sample (fc_sample_stride)][component][channel + kFcPad]; samples at or
+// past n read as zero.
 template <typename T, int LAYOUT>
 __device__ __forceinline__ void fc_stage(const T* __restrict__ src, int64_t sdim, int64_t boff, int bd, int bm,
                                          int64_t s0, int ns, int64_t n, T* dst, int tid) {
   const int blk = bd * bm;
-  const int cstride = bm + kFcPad, sstride = bd * cstride;
+  const int cstride = bm + kFcPad, sstride = fc_sample_stride(bd, bm);
   if (blk <= kFcThreads) {
     const int spp = kFcThreads / blk;  // samples per pass
     const int sp = tid / blk, rem = tid - sp * blk;
@@ -97,79 +98,63 @@ __device__ __forceinline__ void fc_stage(const T* __restrict__ src, int64_t sdim
 // One term of a result tile: K runs over chunks (vc, u) -- vc outer, a
 // window of VK = 4 VS channels v of the register operand Q, u one channel
 // of the scalar operand P.  Per lane and row tile the window's Q values
-// (Qreg[t][s] = Q[sample, qb_t, v0 + 4 s + lane / 16]) stay in registers
-// while u runs, so one MFMA step costs NT FMAs: A = sum_t y_t Qreg[t][s]
-// with y_t = coef_t P[sample, pa_t, u] formed once per chunk.  The
-// weight rows of the next chunk are fetched into registers while the
-// current chunk multiplies, then written to the other LDS buffer.
-template <typename T, int TN, int NT>
+// (Qreg[t][s] = Q[sample, qb_t, v0 + 4 s + lane / 16], read from global
+// memory, where the tile's rows are L2-resident) stay in registers while u
+// runs, so one MFMA step costs NT FMAs: A = sum_t y_t Qreg[t][s] with
+// y_t = coef_t P[sample, pa_t, u] formed once per chunk from the P block
+// staged in LDS.  The weight rows of the next chunk are fetched into
+// registers while the current chunk multiplies, then written to the other
+// LDS buffer.
+template <typename T, int LAYOUT, int TN, int NT>
 __device__ __forceinline__ void fc_term(const FcTerm& Tm, const FcEnt* __restrict__ ents, const T* __restrict__ w,
-                                        const T* Ps, const T* Qs, T (*Bs)[kFcTK][FcB<TN>::stride], int m_res,
-                                        int c0, const int (&sl)[2], const int (&kc)[2], const bool (&rv)[2],
-                                        bool has0, bool has1, int tid, int lane,
-                                        typename Mfma<T>::acc_t (&acc)[2][TN / 16]) {
+                                        const T* Ps, const T* __restrict__ Qt, int64_t qdim,
+                                        T (*Bs)[kFcTK][FcB<TN>::stride], int m_res, int c0, const int (&sl)[2],
+                                        const int (&kc)[2], const bool (&rv)[2], bool has0, bool has1, int tid,
+                                        int lane, typename Mfma<T>::acc_t (&acc)[2][TN / 16]) {
   using M = Mfma<T>;
   constexpr int kNT = TN / 16;
   constexpr int VS = NT <= 4 ? 8 : 4;       // MFMA steps per chunk
   constexpr int VK = 4 * VS;                // K rows per chunk
   constexpr int kBPer = VK * TN / kFcThreads;
   static_assert(kBPer >= 1 && (VK * TN) % kFcThreads == 0, "weight chunk must split over the workgroup");
-  const int pcs = Tm.p_m + kFcPad, qcs = Tm.q_m + kFcPad;
-  const int pss = Tm.p_d * pcs, qss = Tm.q_d * qcs;
+  const int pcs = Tm.p_m + kFcPad;
+  const int pss = fc_sample_stride(Tm.p_d, Tm.p_m);
+  // Q element (row, component b, channel v) at Qt + qo + v * qvs
+  const int qvs = LAYOUT == kIrMul ? 1 : Tm.q_d;
 
-  // entries of this lane's rows: P offset (without the channel), Q offset,
+  // entries of this lane's rows: P offset in LDS (without the channel) and
   // coefficient (zero for padding and rows past the tile)
-  int po[2][NT], qo[2][NT];
+  int po[2][NT];
   T cf[2][NT];
 #pragma unroll
   for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
     for (int e = 0; e < NT; ++e) {
       po[rt][e] = 0;
-      qo[rt][e] = 0;
       cf[rt][e] = T(0);
       if (e < Tm.T) {
         const FcEnt E = ents[Tm.ent + kc[rt] * Tm.T + e];
         po[rt][e] = sl[rt] * pss + E.pa * pcs;
-        qo[rt][e] = sl[rt] * qss + E.qb * qcs;
         cf[rt][e] = rv[rt] ? static_cast<T>(E.c) : T(0);
       }
     }
 
+  // the Q window (re-reading the entries' Q components: this runs once per
+  // window, not per chunk)
   T qreg[2][NT][VS];
   auto load_q = [&](int vc, int win) {
 #pragma unroll
-    for (int s = 0; s < VS; ++s) {
-      const int v = vc * win + 4 * s + lane / 16;
-      const bool ok = 4 * s < win && v < Tm.q_m;
+    for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-      for (int rt = 0; rt < 2; ++rt)
+      for (int e = 0; e < NT; ++e) {
+        const int qb = e < Tm.T ? ents[Tm.ent + kc[rt] * Tm.T + e].qb : 0;
+        const T* qp = Qt + sl[rt] * qdim + Tm.q_off + (LAYOUT == kIrMul ? qb * Tm.q_m : qb);
 #pragma unroll
-        for (int e = 0; e < NT; ++e) qreg[rt][e][s] = ok ? Qs[qo[rt][e] + v] : T(0);
-    }
-  };
-
-  const bool c_fast = Tm.s_r == 1;
-  T rb[kBPer];
-  auto fetch = [&](int u, int vc, int win) {
-#pragma unroll
-    for (int i = 0; i < kBPer; ++i) {
-      const int e = i * kFcThreads + tid;
-      const int kk = c_fast ? e / TN : e % VK;
-      const int cc = c_fast ? e % TN : e / VK;
-      const int v = vc * win + kk, col = c0 + cc;
-      rb[i] = (kk < win && v < Tm.q_m && col < m_res) ? w[Tm.w_off + u * Tm.s_p + v * Tm.s_q + col * Tm.s_r]
-                                                       : T(0);
-    }
-  };
-  auto put = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < kBPer; ++i) {
-      const int e = i * kFcThreads + tid;
-      const int kk = c_fast ? e / TN : e % VK;
-      const int cc = c_fast ? e % TN : e / VK;
-      Bs[buf][kk][cc] = rb[i];
-    }
+        for (int s = 0; s < VS; ++s) {
+          const int v = vc * win + 4 * s + lane / 16;
+          qreg[rt][e][s] = (4 * s < win && v < Tm.q_m) ? qp[v * qvs] : T(0);
+        }
+      }
   };
 
   // window of the Q channels: VK, or q_m rounded up to 4 if smaller
@@ -178,10 +163,62 @@ __device__ __forceinline__ void fc_term(const FcTerm& Tm, const FcEnt* __restric
   const int nvc = (Tm.q_m + win - 1) / win;
   const int nch = nvc * Tm.p_m;
   if (nch == 0) return;
-  fetch(0, 0, win);
+
+  // weight chunk staging: element i of this thread is (kk, cc), cc fastest
+  // when the result channel is the contiguous weight index, else kk; its
+  // offset without the chunk's (u, vc) part is fixed for the term
+  const bool c_fast = Tm.s_r == 1;
+  auto kk_of = [&](int i) {
+    const int e = i * kFcThreads + tid;
+    return c_fast ? e / TN : e % VK;
+  };
+  auto cc_of = [&](int i) {
+    const int e = i * kFcThreads + tid;
+    return c_fast ? e % TN : e / VK;
+  };
+  int64_t wb[kBPer];
+#pragma unroll
+  for (int i = 0; i < kBPer; ++i)
+    wb[i] = (kk_of(i) < win && c0 + cc_of(i) < m_res) ? Tm.w_off + kk_of(i) * Tm.s_q + (c0 + cc_of(i)) * Tm.s_r
+                                                       : int64_t(-1);
+  T rb[kBPer];
+  auto fetch = [&](int u, int vc) {
+    const int64_t off = u * Tm.s_p + static_cast<int64_t>(vc) * win * Tm.s_q;
+#pragma unroll
+    for (int i = 0; i < kBPer; ++i)
+      rb[i] = (wb[i] >= 0 && vc * win + kk_of(i) < Tm.q_m) ? w[wb[i] + off] : T(0);
+  };
+  auto put = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < kBPer; ++i) Bs[buf][kk_of(i)][cc_of(i)] = rb[i];
+  };
+
+  auto step = [&](int buf, int s, const T (&y)[2][NT]) {
+    T b[kNT];
+#pragma unroll
+    for (int j = 0; j < kNT; ++j) b[j] = Bs[buf][4 * s + lane / 16][j * 16 + lane % 16];
+    T a[2];
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) {
+      T t = y[rt][0] * qreg[rt][0][s];
+#pragma unroll
+      for (int e = 1; e < NT; ++e) t += y[rt][e] * qreg[rt][e][s];
+      a[rt] = t;
+    }
+    if (has0) {
+#pragma unroll
+      for (int j = 0; j < kNT; ++j) acc[0][j] = M::mma(a[0], b[j], acc[0][j]);
+    }
+    if (has1) {
+#pragma unroll
+      for (int j = 0; j < kNT; ++j) acc[1][j] = M::mma(a[1], b[j], acc[1][j]);
+    }
+  };
+
+  fetch(0, 0);
   put(0);
-  __syncthreads();
   load_q(0, win);
+  __syncthreads();
   int u = 0, vc = 0;
   for (int ch = 0; ch < nch; ++ch) {
     int un = u + 1, vcn = vc;
@@ -189,35 +226,18 @@ __device__ __forceinline__ void fc_term(const FcTerm& Tm, const FcEnt* __restric
       un = 0;
       ++vcn;
     }
-    if (ch + 1 < nch) fetch(un, vcn, win);
+    if (ch + 1 < nch) fetch(un, vcn);
     const int buf = ch & 1;
     T y[2][NT];
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
       for (int e = 0; e < NT; ++e) y[rt][e] = cf[rt][e] * Ps[po[rt][e] + u];
+    if (steps == VS) {
 #pragma unroll
-    for (int s = 0; s < VS; ++s) {
-      if (s >= steps) break;
-      T b[kNT];
-#pragma unroll
-      for (int j = 0; j < kNT; ++j) b[j] = Bs[buf][4 * s + lane / 16][j * 16 + lane % 16];
-      T a[2];
-#pragma unroll
-      for (int rt = 0; rt < 2; ++rt) {
-        T t = y[rt][0] * qreg[rt][0][s];
-#pragma unroll
-        for (int e = 1; e < NT; ++e) t += y[rt][e] * qreg[rt][e][s];
-        a[rt] = t;
-      }
-      if (has0) {
-#pragma unroll
-        for (int j = 0; j < kNT; ++j) acc[0][j] = M::mma(a[0], b[j], acc[0][j]);
-      }
-      if (has1) {
-#pragma unroll
-        for (int j = 0; j < kNT; ++j) acc[1][j] = M::mma(a[1], b[j], acc[1][j]);
-      }
+      for (int s = 0; s < VS; ++s) step(buf, s, y);
+    } else {
+      for (int s = 0; s < steps; ++s) step(buf, s, y);
     }
     if (ch + 1 < nch) put(buf ^ 1);
     __syncthreads();
@@ -227,8 +247,16 @@ __device__ __forceinline__ void fc_term(const FcTerm& Tm, const FcEnt* __restric
   }
 }
 
+// Workgroups per CU the register allocation must allow: three for the
+// float kernels with 32 columns and up to three couplings (they fit without
+// spilling), otherwise what the allocation gives.
+template <typename T, int TN, int NT>
+constexpr int fc_min_blocks() {
+  return (sizeof(T) == 4 && TN == 32 && NT <= 3) ? 3 : 1;
+}
+
 template <typename T, int LAYOUT, int TN, int NT>
-__global__ void __launch_bounds__(kFcThreads)
+__global__ void __launch_bounds__(kFcThreads, (fc_min_blocks<T, TN, NT>()))
 fctp_kernel(const T* __restrict__ op0, const T* __restrict__ op1, const T* __restrict__ op2, int64_t dim0,
             int64_t dim1, int64_t dim2, const T* __restrict__ w, T* __restrict__ res, int64_t dim_res, int64_t n,
             const FcRes* __restrict__ rtab, const FcTerm* __restrict__ terms, const FcEnt* __restrict__ ents,
@@ -271,16 +299,15 @@ fctp_kernel(const T* __restrict__ op0, const T* __restrict__ op1, const T* __res
   T* Ps = reinterpret_cast<T*>(fc_smem);
   for (int t = R.term_begin; t < R.term_end; ++t) {
     const FcTerm Tm = terms[t];
-    T* Qs = Ps + R.ts * (Tm.p_d * (Tm.p_m + kFcPad));
     const T* P = Tm.p_op == 0 ? op0 : (Tm.p_op == 1 ? op1 : op2);
     const T* Q = Tm.q_op == 0 ? op0 : (Tm.q_op == 1 ? op1 : op2);
     const int64_t pdim = Tm.p_op == 0 ? dim0 : (Tm.p_op == 1 ? dim1 : dim2);
     const int64_t qdim = Tm.q_op == 0 ? dim0 : (Tm.q_op == 1 ? dim1 : dim2);
     __syncthreads();  // the previous term's LDS reads are done
     fc_stage<T, LAYOUT>(P, pdim, Tm.p_off, Tm.p_d, Tm.p_m, s0, ts, n, Ps, tid);
-    fc_stage<T, LAYOUT>(Q, qdim, Tm.q_off, Tm.q_d, Tm.q_m, s0, ts, n, Qs, tid);
-    // (fc_term's first barrier publishes the staged blocks)
-    fc_term<T, TN, NT>(Tm, ents, w, Ps, Qs, Bs, R.m, c0, sl, kc, rv, has0, has1, tid, lane, acc);
+    // (fc_term's first barrier publishes the staged block)
+    fc_term<T, LAYOUT, TN, NT>(Tm, ents, w, Ps, Q + s0 * qdim, qdim, Bs, R.m, c0, sl, kc, rv, has0, has1, tid,
+                               lane, acc);
   }
 
   // epilogue: rows (sample, component), columns c0 + ..
@@ -317,7 +344,8 @@ __device__ __forceinline__ void fc_dw_tile(const FcDwPath& P, const FcEnt* __res
   using M = Mfma<T>;
   constexpr int kNT = kFcDwCols / 16;
   const int pcs = P.p_m + kFcPad, qcs = P.q_m + kFcPad, gcs = P.g_m + kFcPad;
-  const int pss = P.p_d * pcs, qss = P.q_d * qcs, gss = P.g_d * gcs;
+  const int pss = fc_sample_stride(P.p_d, P.p_m), qss = fc_sample_stride(P.q_d, P.q_m),
+            gss = fc_sample_stride(P.g_d, P.g_m);
   int pa[NT], qb[NT];
   T cf[NT];
 #pragma unroll
@@ -398,10 +426,9 @@ fctp_dw_kernel(const T* __restrict__ x1, const T* __restrict__ x2, const T* __re
   const int tid = threadIdx.x, lane = tid % 64, wave = tid / 64;
   const int u0 = ut * kFcDwU + 2 * wave, v0 = vt * kFcDwV, c0 = ct * kFcDwCols;
   const int col = c0 + lane % 16;
-  const int pcs = P.p_m + kFcPad, qcs = P.q_m + kFcPad;
   T* Ps = reinterpret_cast<T*>(fc_smem);
-  T* Qs = Ps + P.ts * (P.p_d * pcs);
-  T* Gs = Qs + P.ts * (P.q_d * qcs);
+  T* Qs = Ps + P.ts * fc_sample_stride(P.p_d, P.p_m);
+  T* Gs = Qs + P.ts * fc_sample_stride(P.q_d, P.q_m);
   const T* Pg = P.p_op == 0 ? x1 : x2;
   const T* Qg = P.q_op == 0 ? x1 : x2;
   const int64_t pdim = P.p_op == 0 ? dim1 : dim2, qdim = P.q_op == 0 ? dim1 : dim2;
