@@ -66,6 +66,13 @@ CASES = [
     ("16x0e+16x1o+16x2e", "0e+1o+2e", "16x0e+16x1o+16x2e", 300),
     ("64x0e+48x1o", "8x0e+8x1o", "80x0e+40x1o", 70),
     ("2x0e+1x1o", "1x0e", "2x0e+1x1o+2x2e", 5),
+    # every compiled coupling-count class (entries per component, rounded to
+    # 1, 2, 3, 4, 6, 8): the launch runs the largest class among its terms
+    ("4x0e+3x1o", "2x0e", "3x0e+2x1o", 91),          # forward 1, dx1 1, dx2 3
+    ("3x1o", "2x1o", "2x1e", 77),                    # 1 x 1 -> 1: 2 everywhere
+    ("3x1o", "2x2e", "2x1o", 65),                    # forward 4, dx1 4, dx2 3
+    ("2x2e", "3x2e", "2x2e", 50),                    # 6 everywhere
+    ("2x2e", "2x2e", "2x4e", 45),                    # forward 6, dx1 8, dx2 8
 ]
 
 
