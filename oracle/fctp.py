@@ -146,3 +146,40 @@ class FullyConnectedTP:
                 c = np.abs(c)
             out[r] = self.alpha[o] * np.einsum("abk,na,nb,nk->", c, a[i][:, :, u], b[j][:, :, v], gb[o][:, :, w])
         return out
+
+    def conv(self, x1, x2, w, src, dst, n_nodes, layout="mul_ir", reduce="sum", absolute=False):
+        """The fully connected product as a graph convolution (the
+        convolution layer of the cuequivariance-torch skill document, "Other
+        operations and layers": source features, edge harmonics and one
+        weight row per edge from the edge MLP, summed or averaged into the
+        destinations):
+
+            out[n] = s_n sum over edges e with dst[e] = n of fwd(x1[src[e]], x2[e]; w[e]),
+
+        s_n = 1, or 1 / (number of such edges) with reduce="mean" (rows
+        without edges are zero).  x1 [n_src, dim_in1]; x2 [n_edges, dim_in2];
+        w [n_edges, weight_numel] or [1, weight_numel] (shared).  Returns
+        float64 [n_nodes, dim_out]."""
+        x1, x2, w = (np.asarray(a, dtype=np.float64) for a in (x1, x2, w))
+        if absolute:
+            x1, x2, w = np.abs(x1), np.abs(x2), np.abs(w)
+        src = np.asarray(src, dtype=np.int64)
+        dst = np.asarray(dst, dtype=np.int64)
+        a = split_blocks(x1, self.in1, layout)
+        b = split_blocks(x2, self.in2, layout)
+        ob = [np.zeros((n_nodes, 2 * l + 1, m)) for m, l, _ in self.out]
+        for p, (i, j, o, off) in enumerate(self.paths):
+            m1, m2, m3 = self.in1[i][0], self.in2[j][0], self.out[o][0]
+            c = real_cg(self.in1[i][1], self.in2[j][1], self.out[o][1])
+            if absolute:
+                c = np.abs(c)
+            We = w[:, off:off + m1 * m2 * m3].reshape(-1, m1, m2, m3)
+            msg = self.alpha[o] * np.einsum("abk,eau,ebv,euvw->ekw", c, a[i][src], b[j], We, optimize=True)
+            np.add.at(ob[o], dst, msg)
+        if reduce == "mean":
+            deg = np.bincount(dst, minlength=n_nodes)[:n_nodes].astype(np.float64)
+            inv = np.where(deg > 0, 1.0 / np.maximum(deg, 1.0), 0.0)
+            ob = [t * inv[:, None, None] for t in ob]
+        elif reduce != "sum":
+            raise ValueError("reduce is 'sum' or 'mean'")
+        return join_blocks(ob, layout)

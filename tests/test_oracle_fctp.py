@@ -200,3 +200,61 @@ def test_dw_entries_match_vjp():
         assert np.allclose(f.dw_entries(x1, x2, g, flat, layout=lay), dw[0], atol=1e-12)
         assert np.allclose(f.dw_entries(x1, x2, g, flat, layout=lay, absolute=True),
                            f.vjp(x1, x2, w, g, layout=lay, absolute=True)[2][0], atol=1e-12)
+
+
+def _graph(rng, n_src, n_nodes, n_edges):
+    dst = np.sort(rng.integers(0, n_nodes, n_edges))
+    src = rng.integers(0, n_src, n_edges)
+    return src, dst
+
+
+@pytest.mark.parametrize("lay", ["mul_ir", "ir_mul"])
+def test_conv_edge_by_edge(lay):
+    """The convolution form against a loop over edges that evaluates the
+    batch product of one edge with that edge's weight row and adds it into
+    its destination; rows without edges stay zero."""
+    f = fctp.FullyConnectedTP("3x0e+2x1o", "0e+1o+2e", "2x0e+3x1o+1x2e")
+    rng = np.random.default_rng(9)
+    src, dst = _graph(rng, 7, 6, 15)
+    dst[dst == 4] = 5                     # node 4 has no edges
+    x1 = rng.normal(size=(7, f.dim_in1))
+    x2 = rng.normal(size=(15, f.dim_in2))
+    w = rng.normal(size=(15, f.weight_numel))
+    want = np.zeros((6, f.dim_out))
+    for e in range(15):
+        want[dst[e]] += f.fwd(x1[src[e]:src[e] + 1], x2[e:e + 1], w[e:e + 1], layout=lay)[0]
+    got = f.conv(x1, x2, w, src, dst, 6, layout=lay)
+    assert np.allclose(got, want, atol=1e-12)
+    assert np.count_nonzero(got[4]) == 0
+    # one shared row = the same row on every edge
+    assert np.allclose(f.conv(x1, x2, w[:1], src, dst, 6, layout=lay),
+                       f.conv(x1, x2, np.repeat(w[:1], 15, axis=0), src, dst, 6, layout=lay), atol=1e-12)
+
+
+def test_conv_identity_graph_is_batch_product():
+    f = fctp.FullyConnectedTP("2x0e+2x1o", "1x0e+1x1o", "2x0e+2x1o")
+    rng = np.random.default_rng(10)
+    x1 = rng.normal(size=(8, f.dim_in1))
+    x2 = rng.normal(size=(8, f.dim_in2))
+    w = rng.normal(size=(1, f.weight_numel))
+    idx = np.arange(8)
+    assert np.allclose(f.conv(x1, x2, w, idx, idx, 8), f.fwd(x1, x2, w), atol=1e-13)
+
+
+def test_conv_mean_and_equivariance():
+    f = fctp.FullyConnectedTP("3x0e+2x1o", "0e+1o", "2x0e+2x1o+1x1e")
+    rng = np.random.default_rng(11)
+    src, dst = _graph(rng, 5, 4, 12)
+    x1 = rng.normal(size=(5, f.dim_in1))
+    x2 = rng.normal(size=(12, f.dim_in2))
+    w = rng.normal(size=(12, f.weight_numel))
+    s = f.conv(x1, x2, w, src, dst, 4)
+    m = f.conv(x1, x2, w, src, dst, 4, reduce="mean")
+    deg = np.bincount(dst, minlength=4)
+    for n in range(4):
+        assert np.allclose(m[n], s[n] / max(deg[n], 1), atol=1e-13)
+    aa = np.array([0.3, 0.5, -0.4])
+    D1 = wigner.wigner_d_irreps(f.in1, aa, parity=-1)
+    D2 = wigner.wigner_d_irreps(f.in2, aa, parity=-1)
+    Do = wigner.wigner_d_irreps(f.out, aa, parity=-1)
+    assert np.allclose(f.conv(x1 @ D1.T, x2 @ D2.T, w, src, dst, 4), s @ Do.T, atol=1e-11)
