@@ -288,6 +288,8 @@ def main():
         note("linear layers timed")
         result["fctp"] = fc_product(torch, sp, workloads, dev, args)
         note("fully connected product timed")
+        result["fctp_conv"] = fc_conv(torch, sp, workloads, dev, args)
+        note("fully connected convolution timed")
 
     if args.copy_calibration:
         a = torch.empty(1 << 28, dtype=torch.float32, device=dev)   # 1 GiB
@@ -493,6 +495,39 @@ def fc_product(torch, sp, workloads, dev, args):
                                               "unit": "TFLOP/s", "frac": tfb / FP32_MFMA_PEAK_TFLOPS,
                                               "algorithmic_flops": 2.0 * bwd_macs * wl.n}}}
         del x1, x2, w, g, out, ws
+    return res
+
+
+def fc_conv(torch, sp, workloads, dev, args):
+    """The fully connected product as a convolution with one weight row per
+    edge on the 20k-node / 600k-edge graph (16x0e+16x1o features, l <= 2
+    harmonics), both layouts.  Algorithmic bytes: every operand read or
+    written once: per edge the weight row, the harmonics and the two
+    indices; per node the x row and the output row."""
+    import numpy as np
+
+    from oracle import fctp as ofc   # sizes only
+    wl = workloads.WORKLOADS[9]
+    f = ofc.FullyConnectedTP(wl.irreps_in1, wl.irreps_sh, wl.irreps_out)
+    inp = workloads.fcconv_inputs(wl, f.weight_numel)
+    to = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    x, sh, w, src, dst = (to(inp[k]) for k in ("x", "sh", "w", "src", "dst"))
+    N, E = inp["n_nodes"], inp["dst"].shape[0]
+    del inp
+    nbytes = E * (f.weight_numel + f.dim_in2) * 4 + 2 * E * 4 + N * (f.dim_in1 + f.dim_out) * 4
+    res = {"workload": wl.name, "nodes": N, "edges": E, "algorithmic_bytes": nbytes}
+    for lay in wl.layouts:
+        h = sp.fctp_create(wl.irreps_in1, wl.irreps_sh, wl.irreps_out, layout=lay, dtype=wl.dtype)
+        out = torch.empty((N, h.dim_out), dtype=torch.float32, device=dev)
+        wall, per = time_launches(torch, lambda: sp.fctp_conv_fwd(h, x, sh, w, src, dst, N, out=out), args.steps,
+                                  args.warmup)
+        kms = sum(per) / len(per)
+        gbps = nbytes / (kms * 1e-3) / 1e9
+        res[lay] = {"ms_per_call": kms, "edges_per_s": E / (wall / args.steps), "kernel": "fcconv_kernel",
+                    "roofline": {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                                 "frac": gbps / HBM_PEAK_GBPS}}
+        del out
+    del x, sh, w, src, dst
     return res
 
 

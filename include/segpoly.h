@@ -402,10 +402,10 @@ int linear_destroy(linear_handle h);
  * alpha_o = 1 / sqrt(sum over the paths into o of mul1 mul2) (0 for an
  * output block no path reaches: its rows are zero).  Weights: one segment
  * per path of mul1 * mul2 * mul3 values, (u, v, w) row-major, shared by all
- * samples ([1, WEIGHT_NUMEL]).  flags: SEGPOLY_VALIDATE accepted (nothing
- * to validate: no indices).  E_UNSUPPORTED for l > 6, more than 32 blocks on
- * a side, more than 64 paths, or blocks too wide for one workgroup's LDS.
- * Touches no GPU.
+ * samples ([1, WEIGHT_NUMEL]).  flags: SEGPOLY_VALIDATE (index checks of
+ * fctp_conv_fwd), SEGPOLY_REDUCE_MEAN (fctp_conv_fwd averages instead of
+ * summing).  E_UNSUPPORTED for l > 6, more than 32 blocks on a side, more
+ * than 64 paths, or blocks too wide for one workgroup's LDS.  Touches no GPU.
  */
 int fctp_create(const char* irreps_in1, const char* irreps_in2, const char* irreps_out, int layout, int dtype,
                 unsigned flags, fctp_handle* out);
@@ -440,6 +440,30 @@ int fctp_bwd_workspace(fctp_handle h, int64_t n, size_t* bytes);
  */
 int fctp_bwd(fctp_handle h, const void* x1, const void* x2, const void* w, const void* grad_out, int64_t n,
              void* grad_x1, void* grad_x2, void* grad_w, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * fctp_conv_fwd: the product as a graph convolution with per-edge weights
+ * ("cuequivariance-torch" skill document, "Other operations and layers":
+ * FullyConnectedTensorProductConv, whose edge MLP gives one weight row per
+ * edge; the MLP itself is the caller's):
+ *   out[n] = s_n sum over edges e with dst[e] = n of fctp(x[src[e]], sh[e]; w[e]),
+ * s_n = 1, or 1 / (number of edges into n) with SEGPOLY_REDUCE_MEAN; rows
+ * without edges are zero.
+ *   x    [n_src, DIM_IN1] device, layout of the handle.
+ *   sh   [n_edges, DIM_IN2] device: input 2 must have one channel per block
+ *        (the edge harmonics; E_UNSUPPORTED otherwise), so its layout is moot.
+ *   w    [w_rows, WEIGHT_NUMEL] device, w_rows = n_edges (per edge) or 1
+ *        (shared by every edge).
+ *   src, dst [n_edges] device, int32 or int64 per idx_dtype; dst sorted
+ *        ascending (the precondition of tp_conv_fwd; VALIDATE checks it and
+ *        the ranges); an edge whose source is out of range contributes
+ *        nothing.
+ *   out  [n_nodes, DIM_OUT] device, fully overwritten.
+ * E_UNSUPPORTED also for input-1 blocks of more than 64 channels.
+ */
+int fctp_conv_fwd(fctp_handle h, const void* x, int64_t n_src, const void* sh, const void* w, int64_t w_rows,
+                  const void* src, const void* dst, int idx_dtype, int64_t n_edges, int64_t n_nodes, void* out,
+                  void* stream);
 
 /* fctp_destroy: free the handle (NULL is a no-op). */
 int fctp_destroy(fctp_handle h);

@@ -34,7 +34,7 @@ EXPORTS = ("tp_create", "tp_query", "tp_irreps_out", "tp_path_info", "tp_path_cg
            "tp_conv_fwd", "tp_conv_fwd_vec", "tp_conv_bwd_workspace", "tp_conv_bwd", "tp_destroy", "symcon_create", "symcon_query", "symcon_coupling_info",
            "symcon_coupling_dense", "symcon_fwd", "symcon_bwd_workspace", "symcon_bwd", "symcon_destroy", "linear_create", "linear_query", "linear_fwd",
            "linear_bwd_workspace", "linear_bwd", "linear_destroy", "fctp_create", "fctp_query", "fctp_path_info",
-           "fctp_fwd", "fctp_bwd_workspace", "fctp_bwd", "fctp_destroy", "sh_fwd", "sh_bwd", "segpoly_real_cg",
+           "fctp_fwd", "fctp_bwd_workspace", "fctp_bwd", "fctp_conv_fwd", "fctp_destroy", "sh_fwd", "sh_bwd", "segpoly_real_cg",
            "segpoly_last_error", "segpoly_version")
 
 
@@ -101,6 +101,7 @@ def _load():
         "fctp_fwd": [vp, vp, vp, vp, i64, vp, vp],
         "fctp_bwd_workspace": [vp, i64, ctypes.POINTER(ctypes.c_size_t)],
         "fctp_bwd": [vp, vp, vp, vp, vp, i64, vp, vp, vp, vp, ctypes.c_size_t, vp],
+        "fctp_conv_fwd": [vp, vp, i64, vp, vp, i64, vp, vp, c_int, i64, i64, vp, vp],
         "fctp_destroy": [vp],
         "sh_fwd": [c_int, c_int, c_int, vp, i64, vp, vp],
         "sh_bwd": [c_int, c_int, c_int, vp, vp, i64, vp, vp],
@@ -573,11 +574,16 @@ class FctpHandle:
             self._h = None
 
 
-def fctp_create(irreps_in1, irreps_in2, irreps_out, layout="mul_ir", dtype="f32", validate=False):
-    """Fully connected (uvw) tensor product with shared weights."""
+def fctp_create(irreps_in1, irreps_in2, irreps_out, layout="mul_ir", dtype="f32", validate=False, reduce="sum"):
+    """Fully connected (uvw) tensor product (batch form with shared weights;
+    convolution form with per-edge or shared weights, ``reduce`` "sum" or
+    "mean")."""
+    if reduce not in ("sum", "mean"):
+        raise ValueError("reduce is 'sum' or 'mean'")
     raw = ctypes.c_void_p()
+    flags = (VALIDATE if validate else 0) | (REDUCE_MEAN if reduce == "mean" else 0)
     _check(lib.fctp_create(irreps_in1.encode(), irreps_in2.encode(), irreps_out.encode(), _LAYOUTS[layout],
-                           _DTYPES[dtype], VALIDATE if validate else 0, ctypes.byref(raw)))
+                           _DTYPES[dtype], flags, ctypes.byref(raw)))
     return FctpHandle(raw, layout, dtype)
 
 
@@ -633,6 +639,34 @@ def fctp_bwd(h, x1, x2, w, grad_out, need=(True, True, True), workspace=None):
     _check(lib.fctp_bwd(h._h, _ptr(x1), _ptr(x2), _ptr(w), _ptr(grad_out), n, _ptr(g1), _ptr(g2), _ptr(gw),
                         _ptr(workspace), wbytes, _stream_ptr(x1.device)))
     return g1, g2, gw
+
+
+def fctp_conv_fwd(h, x, sh, w, src, dst, n_nodes, out=None):
+    """Convolution form: out [n_nodes, dim_out] = sum (or mean) over the
+    edges into each node of the product of x[src[e]] and sh[e] with weight
+    row w[e] (w [n_edges, weight_numel]) or the shared row (w [1, ...])."""
+    import torch
+    t = _torch_dtype(h.dtype)
+    for name, a in (("x", x), ("sh", sh), ("w", w)):
+        if a.dtype != t or not a.is_cuda or not a.is_contiguous() or a.dim() != 2:
+            raise ValueError(f"{name} must be a contiguous 2-d {t} device tensor")
+    n_edges = sh.shape[0]
+    if x.shape[1] != h.dim_in1 or sh.shape[1] != h.dim_in2 or w.shape[1] != h.weight_numel:
+        raise ValueError("operand widths do not match the descriptor")
+    if w.shape[0] not in (1, n_edges):
+        raise ValueError("weights are [n_edges, weight_numel] or [1, weight_numel]")
+    for name, a in (("src", src), ("dst", dst)):
+        if a.shape != (n_edges,) or not a.is_cuda or not a.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous [n_edges] device tensor")
+    if src.dtype != dst.dtype:
+        raise ValueError("src and dst must have the same dtype")
+    if out is None:
+        out = torch.empty((n_nodes, h.dim_out), dtype=t, device=x.device)
+    elif out.shape != (n_nodes, h.dim_out) or out.dtype != t or not out.is_contiguous():
+        raise ValueError("out has the wrong shape or dtype")
+    _check(lib.fctp_conv_fwd(h._h, _ptr(x), x.shape[0], _ptr(sh), _ptr(w), w.shape[0], _ptr(src), _ptr(dst),
+                             _index_dtype(src), n_edges, n_nodes, _ptr(out), _stream_ptr(x.device)))
+    return out
 
 
 # ---------------------------------------------------------------- spherical harmonics

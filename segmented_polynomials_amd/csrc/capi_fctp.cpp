@@ -15,6 +15,7 @@
 
 #include "capi_util.hpp"
 #include "cg.hpp"
+#include "fcconv_tables.hpp"
 #include "fctp_tables.hpp"
 #include "irreps.hpp"
 #include "launch.hpp"
@@ -95,6 +96,19 @@ struct segpoly_fctp {
   int dw_nt = 1;                  // entry class of the weight-gradient launch
   size_t dw_lds = 0, dw_off = 0, ent_off = 0;
   std::vector<FcEnt> ents;
+  // the graph convolution form (per-edge weights); conv_error is why it is
+  // unavailable for this descriptor ("" if available)
+  std::string conv_error;
+  std::vector<FcvBlock> cv_blocks;
+  std::vector<FcvPath> cv_paths;
+  std::vector<FcvQK> cv_qks;
+  std::vector<FcvEnt> cv_ents;
+  std::vector<FcvTile> cv_tiles;
+  std::vector<FcvQ> cv_qs;
+  std::vector<FcvChunk> cv_chunks;
+  int cv_ncomp = 0, cv_max_nqk = 0, cv_lane_bits = 0;
+  size_t cv_lds = 0;
+  size_t cv_off[7] = {0, 0, 0, 0, 0, 0, 0};  // blocks, paths, qks, ents, tiles, qs, chunks within the blob
   std::vector<unsigned char> blob;
   std::map<int, DeviceBuffer> dev;
   std::mutex mu;
@@ -255,6 +269,95 @@ int build_dw(segpoly_fctp* h) {
   return SEGPOLY_OK;
 }
 
+// Tables of the convolution form: input 2 must be the edge harmonics (one
+// channel per block), input-1 blocks at most 64 channels.
+void build_conv(segpoly_fctp* h) {
+  for (const auto& b : h->in2)
+    if (b.mul != 1) {
+      h->conv_error = "the convolution form needs one channel per input-2 block (edge harmonics)";
+      return;
+    }
+  int mmax = 1;
+  for (const auto& b : h->in1) mmax = std::max(mmax, b.mul);
+  if (mmax > 64) {
+    h->conv_error = "the convolution form supports at most 64 channels per input-1 block";
+    return;
+  }
+  int comp = 0;
+  for (size_t i = 0; i < h->in1.size(); ++i) {
+    const Irrep& b = h->in1[i];
+    h->cv_blocks.push_back({h->off1[i], 2 * b.l + 1, b.mul, comp});
+    comp += 2 * b.l + 1;
+  }
+  h->cv_ncomp = comp;
+  int nwmax = 1;
+  for (size_t o = 0; o < h->out.size(); ++o) {
+    const Irrep& ob = h->out[o];
+    const int d3 = 2 * ob.l + 1;
+    if (ob.mul == 0) continue;
+    const int path_begin = static_cast<int>(h->cv_paths.size());
+    const int qk_begin = static_cast<int>(h->cv_qks.size());
+    int nqk = 0;
+    for (const auto& pa : h->paths) {
+      if (pa.o != static_cast<int>(o)) continue;
+      const Irrep &a = h->in1[pa.i], &b = h->in2[pa.j];
+      const int d1 = 2 * a.l + 1, d2 = 2 * b.l + 1;
+      h->cv_paths.push_back({pa.w_off, a.mul, nqk});
+      const std::vector<double>& C = real_cg(a.l, b.l, ob.l);
+      for (int k = 0; k < d3; ++k) {
+        FcvQK q{static_cast<int>(h->cv_ents.size()), 0};
+        for (int ia = 0; ia < d1; ++ia)
+          for (int ib = 0; ib < d2; ++ib) {
+            const double c = C[(static_cast<size_t>(ia) * d2 + ib) * d3 + k];
+            if (std::fabs(c) < 1e-13) continue;
+            h->cv_ents.push_back({h->cv_blocks[pa.i].comp + ia, static_cast<int>(h->off2[pa.j]) + ib,
+                                  h->alpha[o] * c});
+          }
+        q.ent_end = static_cast<int>(h->cv_ents.size());
+        h->cv_qks.push_back(q);
+      }
+      nqk += d3;
+    }
+    const int path_end = static_cast<int>(h->cv_paths.size());
+    h->cv_max_nqk = std::max(h->cv_max_nqk, nqk);
+    // full 16-channel chunks of every path, and the remaining channels one by one
+    const int chunk_begin = static_cast<int>(h->cv_chunks.size());
+    const int q_begin = static_cast<int>(h->cv_qs.size());
+    for (int pi = path_begin; pi < path_end; ++pi) {
+      const FcvPath& P = h->cv_paths[pi];
+      int u = 0;
+      for (; u + kFcvChunkU <= P.m1; u += kFcvChunkU)
+        h->cv_chunks.push_back({P.w_off + static_cast<int64_t>(u) * ob.mul, P.qk, u});
+      for (; u < P.m1; ++u) h->cv_qs.push_back({P.w_off + static_cast<int64_t>(u) * ob.mul, P.qk, u});
+    }
+    const int n_chunks = static_cast<int>(h->cv_chunks.size()) - chunk_begin;
+    const int nq = static_cast<int>(h->cv_qs.size()) - q_begin;
+    for (int w0 = 0; w0 < ob.mul; w0 += 64) {
+      FcvTile t{};
+      t.out_off = h->offo[o];
+      t.d = d3, t.m = ob.mul, t.w0 = w0, t.nw = std::min(64, ob.mul - w0);
+      t.path_begin = path_begin, t.path_end = path_end;
+      t.qk_begin = qk_begin, t.nqk = nqk;
+      t.q_begin = q_begin, t.nq = nq;
+      t.chunk_begin = chunk_begin, t.n_chunks = n_chunks;
+      nwmax = std::max(nwmax, t.nw);
+      h->cv_tiles.push_back(t);
+    }
+  }
+  int lanes = 1;
+  while (lanes < std::max(mmax, nwmax)) lanes <<= 1;
+  int bits = 0;
+  while ((1 << bits) < lanes) ++bits;
+  h->cv_lane_bits = bits;
+  const size_t S = 64 >> bits;
+  h->cv_lds = S * (static_cast<size_t>(h->cv_ncomp) * lanes + 1 + static_cast<size_t>(h->dim2) + 1 +
+                   static_cast<size_t>(h->cv_max_nqk) * lanes + 1) * elt(h->dtype);
+  if (h->cv_lds > 64 * 1024) {
+    h->conv_error = "the convolution form's per-edge rows exceed the LDS of one wave";
+    return;
+  }
+}
+
 template <typename V>
 size_t append(std::vector<unsigned char>& blob, const std::vector<V>& v) {
   const size_t off = (blob.size() + 255) & ~size_t(255);
@@ -338,7 +441,7 @@ int fctp_create(const char* irreps_in1, const char* irreps_in2, const char* irre
   if (!irreps_in1 || !irreps_in2 || !irreps_out) return fail(SEGPOLY_E_INVALID, "null irreps string");
   if (layout != SEGPOLY_MUL_IR && layout != SEGPOLY_IR_MUL) return fail(SEGPOLY_E_INVALID, "bad layout");
   if (dtype != SEGPOLY_F32 && dtype != SEGPOLY_F64) return fail(SEGPOLY_E_INVALID, "bad dtype");
-  if (flags & ~SEGPOLY_VALIDATE) return fail(SEGPOLY_E_INVALID, "unknown flag bits");
+  if (flags & ~(SEGPOLY_VALIDATE | SEGPOLY_REDUCE_MEAN)) return fail(SEGPOLY_E_INVALID, "unknown flag bits");
   segpoly_fctp* h = nullptr;
   try {
     h = new segpoly_fctp();
@@ -394,6 +497,7 @@ int fctp_create(const char* irreps_in1, const char* irreps_in2, const char* irre
   try {
     for (int w = 0; w < 3 && rc == SEGPOLY_OK; ++w) rc = build_pass(h, w);
     if (rc == SEGPOLY_OK) rc = build_dw(h);
+    if (rc == SEGPOLY_OK) build_conv(h);
     if (rc == SEGPOLY_OK) {
       for (int w = 0; w < 3; ++w) {
         h->pass[w].res_off = append(h->blob, h->pass[w].res);
@@ -401,6 +505,13 @@ int fctp_create(const char* irreps_in1, const char* irreps_in2, const char* irre
       }
       h->dw_off = append(h->blob, h->dw);
       h->ent_off = append(h->blob, h->ents);
+      h->cv_off[0] = append(h->blob, h->cv_blocks);
+      h->cv_off[1] = append(h->blob, h->cv_paths);
+      h->cv_off[2] = append(h->blob, h->cv_qks);
+      h->cv_off[3] = append(h->blob, h->cv_ents);
+      h->cv_off[4] = append(h->blob, h->cv_tiles);
+      h->cv_off[5] = append(h->blob, h->cv_qs);
+      h->cv_off[6] = append(h->blob, h->cv_chunks);
     }
   } catch (const std::bad_alloc&) {
     rc = fail(SEGPOLY_E_OOM, "out of host memory");
@@ -506,6 +617,54 @@ int fctp_bwd(fctp_handle h, const void* x1, const void* x2, const void* w, const
     const int rc = launch_fctp_dw(a, t);
     if (rc) return fail(SEGPOLY_E_HIP, std::string("fctp dw launch: ") + hipGetErrorString(static_cast<hipError_t>(rc)));
   }
+  return ok();
+}
+
+int fctp_conv_fwd(fctp_handle h, const void* x, int64_t n_src, const void* sh, const void* w, int64_t w_rows,
+                  const void* src, const void* dst, int idx_dtype, int64_t n_edges, int64_t n_nodes, void* out,
+                  void* stream) {
+  if (!h) return fail(SEGPOLY_E_INVALID, "null handle");
+  if (!h->conv_error.empty()) return fail(SEGPOLY_E_UNSUPPORTED, h->conv_error);
+  if (n_src < 0 || n_edges < 0 || n_nodes < 0) return fail(SEGPOLY_E_INVALID, "negative size");
+  if (idx_dtype != SEGPOLY_I32 && idx_dtype != SEGPOLY_I64) return fail(SEGPOLY_E_INVALID, "bad index dtype");
+  if (w_rows != 1 && w_rows != n_edges) return fail(SEGPOLY_E_INVALID, "w_rows must be 1 (shared) or n_edges");
+  if (n_nodes == 0) return ok();
+  if (!out) return fail(SEGPOLY_E_INVALID, "null output");
+  if (n_edges > 0 && (!src || !dst || (h->dim2 > 0 && !sh) || (h->numel > 0 && !w) || (n_src > 0 && !x)))
+    return fail(SEGPOLY_E_INVALID, "null buffer");
+  if (n_nodes > kMaxGridX) return fail(SEGPOLY_E_UNSUPPORTED, "too many destination rows for one launch");
+  if (h->flags & SEGPOLY_VALIDATE) {
+    const int st = idx_dtype == SEGPOLY_I32 ? check_indices<int32_t>(src, dst, n_edges, n_src, n_nodes, stream)
+                                            : check_indices<int64_t>(src, dst, n_edges, n_src, n_nodes, stream);
+    if (st) return st;
+  }
+  int st = SEGPOLY_OK;
+  const unsigned char* db = device_blob(h, &st);
+  if (!db) return st;
+  FcvArgs a{};
+  a.x = x, a.sh = sh, a.w = w, a.src = src, a.dst = dst;
+  a.n_src = n_src, a.n_edges = n_edges, a.n_nodes = n_nodes;
+  a.dim1 = h->dim1, a.dim2 = h->dim2, a.dimo = h->dimo;
+  a.w_stride = w_rows == 1 && n_edges != 1 ? 0 : h->numel;
+  a.out = out;
+  a.mean = (h->flags & SEGPOLY_REDUCE_MEAN) ? 1 : 0;
+  a.blocks = reinterpret_cast<const FcvBlock*>(db + h->cv_off[0]);
+  a.paths = reinterpret_cast<const FcvPath*>(db + h->cv_off[1]);
+  a.qks = reinterpret_cast<const FcvQK*>(db + h->cv_off[2]);
+  a.ents = reinterpret_cast<const FcvEnt*>(db + h->cv_off[3]);
+  a.tiles = reinterpret_cast<const FcvTile*>(db + h->cv_off[4]);
+  a.qs = reinterpret_cast<const FcvQ*>(db + h->cv_off[5]);
+  a.chunks = reinterpret_cast<const FcvChunk*>(db + h->cv_off[6]);
+  a.n_blocks = static_cast<int>(h->cv_blocks.size());
+  a.n_tiles = static_cast<int>(h->cv_tiles.size());
+  a.ncomp = h->cv_ncomp;
+  a.max_nqk = h->cv_max_nqk;
+  a.lane_bits = h->cv_lane_bits;
+  a.lds_bytes = h->cv_lds;
+  a.dtype = h->dtype, a.layout = h->layout, a.idx = idx_dtype;
+  a.stream = stream;
+  const int rc = launch_fcconv(a);
+  if (rc) return fail(SEGPOLY_E_HIP, std::string("fctp conv launch: ") + hipGetErrorString(static_cast<hipError_t>(rc)));
   return ok();
 }
 

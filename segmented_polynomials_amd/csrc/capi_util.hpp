@@ -2,9 +2,11 @@
 #pragma once
 #include <hip/hip_runtime_api.h>
 
+#include <cstdint>
 #include <map>
 #include <mutex>
 #include <string>
+#include <vector>
 
 #include "segpoly.h"
 
@@ -66,6 +68,26 @@ inline void free_all(std::map<int, DeviceBuffer>& cache) {
   }
   if (have) (void)hipSetDevice(cur);
   cache.clear();
+}
+
+// Host-side index checks of the VALIDATE flag (synchronises the stream).
+template <typename Index>
+inline int check_indices(const void* dsrc, const void* ddst, int64_t n_edges, int64_t n_src, int64_t n_nodes,
+                  void* stream) {
+  std::vector<Index> s(n_edges), d(n_edges);
+  hipError_t e = hipStreamSynchronize(static_cast<hipStream_t>(stream));
+  if (e == hipSuccess && n_edges) e = hipMemcpy(s.data(), dsrc, n_edges * sizeof(Index), hipMemcpyDeviceToHost);
+  if (e == hipSuccess && n_edges) e = hipMemcpy(d.data(), ddst, n_edges * sizeof(Index), hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return fail(SEGPOLY_E_HIP, std::string("validate copy: ") + hipGetErrorString(e));
+  for (int64_t i = 0; i < n_edges; ++i) {
+    if (s[i] < 0 || static_cast<int64_t>(s[i]) >= n_src)
+      return fail(SEGPOLY_E_RANGE, "src[" + std::to_string(i) + "] = " + std::to_string(s[i]) + " outside [0, n_src)");
+    if (d[i] < 0 || static_cast<int64_t>(d[i]) >= n_nodes)
+      return fail(SEGPOLY_E_RANGE, "dst[" + std::to_string(i) + "] = " + std::to_string(d[i]) + " outside [0, n_nodes)");
+    if (i && d[i] < d[i - 1])
+      return fail(SEGPOLY_E_UNSORTED, "dst is not sorted ascending at edge " + std::to_string(i));
+  }
+  return ok();
 }
 
 constexpr int64_t kMaxGridX = 2147483647;

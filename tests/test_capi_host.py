@@ -319,6 +319,19 @@ def test_fctp_errors_and_workspace():
     assert b(h._h, p, p, None, p, 5000, p, None, None, None, 0, None) == sp.E_INVALID     # dx1 needs w
     assert b(h._h, None, None, None, None, 0, None, None, None, None, 0, None) == sp.OK
     assert sp.lib.fctp_destroy(None) == sp.OK
+    # the convolution form: input 2 with one channel per block, w_rows 1 or n_edges
+    cv = sp.lib.fctp_conv_fwd
+    assert cv(h._h, p, 4, p, p, 1, p, p, 0, 3, 2, p, None) == sp.E_UNSUPPORTED        # 32x0e+32x1o as input 2
+    hc = sp.fctp_create("16x0e+16x1o", "0e+1o+2e", "16x0e+16x1o", reduce="mean")
+    assert cv(hc._h, p, 4, p, p, 2, p, p, 0, 3, 2, p, None) == sp.E_INVALID           # w_rows
+    assert cv(hc._h, p, 4, p, p, 3, p, p, 5, 3, 2, p, None) == sp.E_INVALID           # index dtype
+    assert cv(hc._h, p, 4, p, p, 3, None, p, 0, 3, 2, p, None) == sp.E_INVALID        # null src
+    assert cv(hc._h, p, 4, p, p, 3, p, p, 0, 3, 2, None, None) == sp.E_INVALID        # null out
+    assert cv(hc._h, p, -4, p, p, 3, p, p, 0, 3, 2, p, None) == sp.E_INVALID
+    assert cv(hc._h, None, 0, None, None, 1, None, None, 0, 0, 0, None, None) == sp.OK  # nothing to do
+    wide = sp.fctp_create("80x0e", "0e", "8x0e")
+    assert cv(wide._h, p, 4, p, p, 1, p, p, 0, 3, 2, p, None) == sp.E_UNSUPPORTED     # > 64 channels
+    assert c(b"2x0e", b"2x0e", b"2x0e", 0, 0, 8 | 16, ctypes.byref(raw)) == sp.E_INVALID  # unknown flag
 
 
 def test_sh_argument_errors():

@@ -1,0 +1,163 @@
+"""GPU parity of the fully connected product as a graph convolution with
+per-edge weights (fctp_conv_fwd), called through the C ABI, against the
+float64 oracle on the same seeded inputs.  Tolerance: scaled error
+(oracle.metrics) <= 1e-5 in float32, <= 1e-12 in float64."""
+
+import numpy as np
+import pytest
+
+import workloads
+from oracle import fctp as ofc
+from oracle import layout as ol
+from tests._gpu import announce, check_scaled, dev, need_gpu
+
+pytestmark = pytest.mark.gpu
+
+
+def _sp():
+    need_gpu()
+    import segmented_polynomials_amd as sp
+    return sp
+
+
+def _td(dtype):
+    import torch
+    return torch.float32 if dtype == "f32" else torch.float64
+
+
+def _graph(rng, n_nodes, max_degree, n_src):
+    deg = rng.integers(0, max_degree + 1, size=n_nodes)
+    deg[rng.random(n_nodes) < 0.2] = 0          # isolated destinations
+    dst = np.repeat(np.arange(n_nodes), deg)
+    src = rng.integers(0, n_src, size=dst.shape[0])
+    return src, dst
+
+
+def _case_inputs(f, n_nodes, max_degree, n_src, dtype, seed, shared=False):
+    rng = np.random.default_rng(seed)
+    dt = np.float32 if dtype == "f32" else np.float64
+    src, dst = _graph(rng, n_nodes, max_degree, n_src)
+    E = dst.shape[0]
+    x = rng.standard_normal((n_src, f.dim_in1)).astype(dt)
+    sh = rng.standard_normal((E, f.dim_in2)).astype(dt)
+    w = rng.standard_normal((1 if shared else E, f.weight_numel)).astype(dt)
+    return x, sh, w, src, dst
+
+
+def _run(sp, h, x, sh, w, src, dst, n_nodes, dtype, idx="int32"):
+    import torch
+    td = _td(dtype)
+    it = torch.int32 if idx == "int32" else torch.int64
+    out = sp.fctp_conv_fwd(h, dev(x, td), dev(sh, td), dev(w, td), dev(src).to(it), dev(dst).to(it), n_nodes)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+CASES = [
+    # (in1, sh, out, n_nodes, max in-degree, n_src): the workload's irreps
+    # (4 edges per wave), odd multiplicities (8 edges per wave), 64 input
+    # channels and an 80-channel output block (two tiles), l = 2 features
+    ("16x0e+16x1o", "0e+1o+2e", "16x0e+16x1o", 150, 12, 170),
+    ("5x0e+3x1o+2x2e", "0e+1o+2e", "4x0e+3x1o+2x1e+1x2e", 90, 9, 60),
+    ("64x0e+40x1o", "0e+1o", "80x0e+24x1o", 40, 7, 45),
+    ("8x0e+8x1o+8x2e", "0e+1o+2e", "8x0e+8x1o+8x2e+4x2o", 60, 10, 60),
+]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f64"])
+@pytest.mark.parametrize("lay", ["mul_ir", "ir_mul"])
+@pytest.mark.parametrize("case", range(len(CASES)))
+def test_parity(case, lay, dtype):
+    sp = _sp()
+    in1, in2, out, n_nodes, deg, n_src = CASES[case]
+    f = ofc.FullyConnectedTP(in1, in2, out)
+    h = sp.fctp_create(in1, in2, out, layout=lay, dtype=dtype)
+    x, sh, w, src, dst = _case_inputs(f, n_nodes, deg, n_src, dtype, 300 + case)
+    idx = "int32" if (case + (lay == "ir_mul")) % 2 == 0 else "int64"
+    announce(f"fcconv case {case} {in1} x {in2} -> {out} E={dst.shape[0]} {lay} {dtype} {idx}")
+    got = _run(sp, h, x, sh, w, src, dst, n_nodes, dtype, idx)
+    check_scaled(got, f.conv(x, sh, w, src, dst, n_nodes, layout=lay),
+                 f.conv(x, sh, w, src, dst, n_nodes, layout=lay, absolute=True), dtype, f"fcconv case {case}")
+    deg_n = np.bincount(dst, minlength=n_nodes)
+    assert np.count_nonzero(got[deg_n == 0]) == 0
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f64"])
+def test_shared_weights_and_mean(dtype):
+    sp = _sp()
+    in1, in2, out, n_nodes, deg, n_src = CASES[1]
+    f = ofc.FullyConnectedTP(in1, in2, out)
+    x, sh, w, src, dst = _case_inputs(f, n_nodes, deg, n_src, dtype, 310, shared=True)
+    announce(f"fcconv shared weights {dtype}")
+    h = sp.fctp_create(in1, in2, out, dtype=dtype)
+    got = _run(sp, h, x, sh, w, src, dst, n_nodes, dtype)
+    check_scaled(got, f.conv(x, sh, w, src, dst, n_nodes), f.conv(x, sh, w, src, dst, n_nodes, absolute=True),
+                 dtype, "shared")
+    announce(f"fcconv reduce=mean {dtype}")
+    hm = sp.fctp_create(in1, in2, out, dtype=dtype, reduce="mean")
+    x, sh, w, src, dst = _case_inputs(f, n_nodes, deg, n_src, dtype, 311)
+    got = _run(sp, hm, x, sh, w, src, dst, n_nodes, dtype)
+    check_scaled(got, f.conv(x, sh, w, src, dst, n_nodes, reduce="mean"),
+                 f.conv(x, sh, w, src, dst, n_nodes, reduce="mean", absolute=True), dtype, "mean")
+
+
+def test_layouts_agree_and_empty_graph():
+    import torch
+    sp = _sp()
+    in1, in2, out, n_nodes, deg, n_src = CASES[3]
+    f = ofc.FullyConnectedTP(in1, in2, out)
+    x, sh, w, src, dst = _case_inputs(f, n_nodes, deg, n_src, "f64", 312)
+    announce("fcconv layouts agree")
+    a = _run(sp, sp.fctp_create(in1, in2, out, layout="mul_ir", dtype="f64"), x, sh, w, src, dst, n_nodes, "f64")
+    b = _run(sp, sp.fctp_create(in1, in2, out, layout="ir_mul", dtype="f64"),
+             ol.transpose(x, f.in1, "mul_ir", "ir_mul"), sh, w, src, dst, n_nodes, "f64")
+    assert np.allclose(ol.transpose(b, f.out, "ir_mul", "mul_ir"), a, atol=1e-12)
+    announce("fcconv empty graph")
+    h = sp.fctp_create(in1, in2, out, dtype="f32")
+    e = np.zeros(0, dtype=np.int32)
+    got = _run(sp, h, x.astype(np.float32), sh[:0].astype(np.float32), w[:1].astype(np.float32), e, e, 7, "f32")
+    assert got.shape == (7, f.dim_out) and np.count_nonzero(got) == 0
+    del torch
+
+
+def test_page_example_so3_two_edges():
+    """The skill document's "0 + 1" product of two feature rows with the
+    harmonics of its two vectors, both edges into one destination."""
+    from oracle import sh as osh
+    sp = _sp()
+    f = ofc.FullyConnectedTP("0 + 1", "0 + 1", "0 + 1")
+    h = sp.fctp_create("0 + 1", "0 + 1", "0 + 1", dtype="f64")
+    rng = np.random.default_rng(0)
+    x = rng.standard_normal((2, 4))
+    vecs = np.array([[0.3, -0.7, 1.1], [1.2, 0.4, -0.2]])
+    sh = osh.real_sh([0, 1], vecs, normalize=False)
+    w = rng.standard_normal((2, 5))
+    src, dst = np.array([0, 1]), np.array([0, 0])
+    announce("fcconv page example")
+    got = _run(sp, h, x, sh, w, src, dst, 1, "f64")
+    want = f.fwd(x[:1], sh[:1], w[:1]) + f.fwd(x[1:], sh[1:], w[1:])
+    check_scaled(got, want, f.conv(x, sh, w, src, dst, 1, absolute=True), "f64", "page example")
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("lay", ["mul_ir", "ir_mul"])
+def test_full_size_workload_sampled(lay):
+    """The 600k-edge workload in the launch configuration the benchmark
+    times; sampled destination rows against the oracle on their edges."""
+    import torch
+    sp = _sp()
+    wl = workloads.WORKLOADS[9]
+    f = ofc.FullyConnectedTP(wl.irreps_in1, wl.irreps_sh, wl.irreps_out)
+    h = sp.fctp_create(wl.irreps_in1, wl.irreps_sh, wl.irreps_out, layout=lay, dtype=wl.dtype)
+    inp = workloads.fcconv_inputs(wl, f.weight_numel)
+    N = inp["n_nodes"]
+    announce(f"fcconv full size E={inp['dst'].shape[0]} {lay}")
+    got = _run(sp, h, inp["x"], inp["sh"], inp["w"], inp["src"], inp["dst"], N, wl.dtype)
+    nodes = np.unique(np.concatenate([np.arange(6), N - 1 - np.arange(6),
+                                      np.random.default_rng(7).integers(0, N, 40)]))
+    sel = np.isin(inp["dst"], nodes)
+    dsel = np.searchsorted(nodes, inp["dst"][sel])
+    args = (inp["x"], inp["sh"][sel], inp["w"][sel], inp["src"][sel], dsel, len(nodes))
+    check_scaled(got[nodes], f.conv(*args, layout=lay), f.conv(*args, layout=lay, absolute=True), wl.dtype,
+                 "full size rows")
+    del torch

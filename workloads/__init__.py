@@ -83,6 +83,20 @@ class FCWorkload:
     n: int
 
 
+@dataclass(frozen=True)
+class FCConvWorkload:
+    number: int
+    name: str
+    irreps_in1: str
+    irreps_sh: str
+    irreps_out: str
+    layouts: tuple
+    dtype: str
+    n_nodes: int
+    degree: int
+    sh_ls: tuple
+
+
 # the output irreps of the 600k-edge convolution (13 blocks, 5,504 values per
 # node), written out: the linear layer that follows the convolution mixes
 # them back to 128 channels per type
@@ -115,6 +129,11 @@ WORKLOADS = {
     # 12a's exercise 1, one row per node of a 100k-node batch
     8: FCWorkload(8, "fctp_uvw_32x0e+32x1o_100k", "32x0e+32x1o", "32x0e+32x1o", "32x0e+32x1o",
                   ("mul_ir", "ir_mul"), "f32", n=100000),
+    # the fully connected product as a convolution with one weight row per
+    # edge (the skill document's FullyConnectedTensorProductConv), 16-channel
+    # scalar + vector features and l <= 2 harmonics on the 20k-node graph
+    9: FCConvWorkload(9, "fctp_conv_20k_nodes_600k_edges", "16x0e+16x1o", "0e+1o+2e", "16x0e+16x1o",
+                      ("mul_ir", "ir_mul"), "f32", n_nodes=20000, degree=30, sh_ls=(0, 1, 2)),
 }
 
 
@@ -359,3 +378,22 @@ def fc_inputs(wl, weight_numel, n=None, seed=None):
     x2 = _normal(rng, (n, _irreps_dim(wl.irreps_in2)), wl.dtype).astype(dt, copy=False)
     w = _normal(rng, (1, weight_numel), wl.dtype).astype(dt, copy=False)
     return dict(x1=x1, x2=x2, w=w)
+
+
+def fcconv_inputs(wl, weight_numel, n_nodes=None, degree=None, graph=None, seed=None):
+    """Inputs of the fully connected convolution workload: the regular graph
+    (or the ragged one), harmonics of the edge vectors, x N(0,1), one weight
+    row per edge N(0,1) (the product's 1/sqrt(fan-in) keeps outputs at unit
+    scale).  Returns dict(x, sh, w, src, dst (int32), n_nodes)."""
+    rng = np.random.default_rng(1000 + wl.number if seed is None else seed)
+    dt = _np_dtype(wl.dtype)
+    nn = wl.n_nodes if n_nodes is None else n_nodes
+    dg = wl.degree if degree is None else degree
+    if graph == "ragged":
+        src, dst, vec = ragged_graph(rng, nn, dg)
+    else:
+        src, dst, vec = regular_graph(rng, nn, dg)
+    sh = edge_harmonics(vec, wl.sh_ls).astype(dt)
+    x = _normal(rng, (nn, _irreps_dim(wl.irreps_in1)), wl.dtype).astype(dt, copy=False)
+    w = _normal(rng, (sh.shape[0], weight_numel), wl.dtype).astype(dt, copy=False)
+    return dict(x=x, sh=sh, w=w, src=src.astype(np.int32), dst=dst.astype(np.int32), n_nodes=nn)
