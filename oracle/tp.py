@@ -27,6 +27,13 @@ Per edge e and path p:
 
 C_p is :func:`oracle.cg.real_cg`.  Without indices (batch mode) src and dst
 are the identity.
+
+Merged output (``merge=True``; the e3nn instruction list the pages print has
+one output block per instruction, and several instructions may write one
+irrep): a reading of the pages, not a printed example.  The paths of one
+output type sum into a single block of that type, in the same type order;
+all paths of a type must then have the same multiplicity.  Weights and path
+order are unchanged.
 """
 
 import numpy as np
@@ -39,7 +46,7 @@ from .layout import split_blocks, join_blocks
 class ChannelwiseTP:
     """Descriptor of one channelwise tensor product."""
 
-    def __init__(self, irreps_in1, irreps_in2, irreps_out):
+    def __init__(self, irreps_in1, irreps_in2, irreps_out, merge=False):
         self.in1 = ir.parse(irreps_in1)
         self.in2 = ir.parse(irreps_in2)
         for mul, _, _ in self.in2:
@@ -60,11 +67,35 @@ class ChannelwiseTP:
         self.weight_numel = sum(self.in1[i][0] for i, _, _, _ in paths)
         self.dim_in1 = ir.dim(self.in1)
         self.dim_in2 = ir.dim(self.in2)
-        self.dim_out = ir.dim(self.out)
+        self.merge = merge
+        self.path_out = list(range(len(paths)))   # output block of each path
+        self.out_blocks = list(self.out)          # the output row's blocks
+        if merge:
+            types, self.out_blocks = [], []
+            for p, (mul, lo, po) in enumerate(self.out):
+                if (lo, po) not in types:
+                    types.append((lo, po))
+                    self.out_blocks.append((mul, lo, po))
+                t = types.index((lo, po))
+                if self.out_blocks[t][0] != mul:
+                    raise ValueError("merged paths of one type need one multiplicity")
+                self.path_out[p] = t
+        self.dim_out = ir.dim(self.out_blocks)
 
     @property
     def irreps_out(self):
-        return ir.to_str(self.out)
+        return ir.to_str(self.out_blocks)
+
+    def _merge_parts(self, parts):
+        """Per-path output blocks -> the row's blocks (sums per type when
+        merged)."""
+        if not self.merge:
+            return parts
+        out = [None] * len(self.out_blocks)
+        for p, part in enumerate(parts):
+            t = self.path_out[p]
+            out[t] = part if out[t] is None else out[t] + part
+        return out
 
     @property
     def num_paths(self):
@@ -150,7 +181,7 @@ class ChannelwiseTP:
             out_parts = [b * inv[:, None, None] for b in out_parts]
         elif reduce != "sum":
             raise ValueError("reduce is 'sum' or 'mean'")
-        return join_blocks(out_parts, layout)
+        return join_blocks(self._merge_parts(out_parts), layout)
 
     def conv_vjp(self, x, sh, w, src, dst, n_nodes, g, layout="mul_ir", shared_weights=False,
                  absolute=False, reduce="sum"):
@@ -188,7 +219,8 @@ class ChannelwiseTP:
             raise ValueError("reduce is 'sum' or 'mean'")
         x1 = split_blocks(x, self.in1, layout)          # per block [n_src, 2l+1, mul]
         x2 = split_blocks(sh, self.in2, "ir_mul")       # per block [n_edges, 2l+1, 1]
-        gb = split_blocks(g, self.out, layout)          # per path [n_nodes, 2lo+1, mul]
+        gb = split_blocks(g, self.out_blocks, layout)   # per output block [n_nodes, 2lo+1, mul]
+        gb = [gb[self.path_out[p]] for p in range(len(self.paths))]   # per path
         dx1 = [np.zeros_like(b) for b in x1]
         dsh = np.zeros_like(sh)
         dw = np.zeros((n_edges, self.weight_numel))

@@ -195,3 +195,40 @@ def test_mean_reduction():
     assert np.isclose(np.sum(g * d.conv(vx, sh, w, src, dst, 5, reduce="mean")), np.sum(dx * vx), rtol=1e-12)
     vw = rng.normal(size=w.shape)
     assert np.isclose(np.sum(g * d.conv(x, sh, vw, src, dst, 5, reduce="mean")), np.sum(dw * vw), rtol=1e-12)
+
+
+def test_merged_output_sums_paths_of_a_type():
+    """merge=True: the output row has one block per type, the sum of the
+    unmerged path blocks of that type; with one path per type nothing
+    changes; the VJP keeps the adjoint identities; mixed multiplicities
+    within a type are rejected."""
+    ins, sh_ir, outs = "6x0e+6x1o", "0e+1o+2e", "0e+1o+2e"
+    u = tp.ChannelwiseTP(ins, sh_ir, outs)
+    m = tp.ChannelwiseTP(ins, sh_ir, outs, merge=True)
+    assert m.irreps_out == "6x0e+6x1o+6x2e" and m.weight_numel == u.weight_numel
+    rng = np.random.default_rng(20)
+    src = rng.integers(0, 5, 14)
+    dst = np.sort(rng.integers(0, 4, 14))
+    x = rng.normal(size=(5, u.dim_in1))
+    sh = rng.normal(size=(14, u.dim_in2))
+    w = rng.normal(size=(14, u.weight_numel))
+    for lay in ("mul_ir", "ir_mul"):
+        yu = layout.split_blocks(u.conv(x, sh, w, src, dst, 4, layout=lay), u.out, lay)
+        ym = layout.split_blocks(m.conv(x, sh, w, src, dst, 4, layout=lay), m.out_blocks, lay)
+        for t, (mul, lo, po) in enumerate(m.out_blocks):
+            want = sum(yu[p] for p, (_, l2, p2) in enumerate(u.out) if (l2, p2) == (lo, po))
+            assert np.allclose(ym[t], want, atol=1e-12)
+        g = rng.normal(size=(4, m.dim_out))
+        dx, dsh, dw = m.conv_vjp(x, sh, w, src, dst, 4, g, layout=lay)
+        vx, vs, vw = rng.normal(size=x.shape), rng.normal(size=sh.shape), rng.normal(size=w.shape)
+        assert np.isclose(np.sum(g * m.conv(vx, sh, w, src, dst, 4, layout=lay)), np.sum(dx * vx), rtol=1e-11)
+        assert np.isclose(np.sum(g * m.conv(x, vs, w, src, dst, 4, layout=lay)), np.sum(dsh * vs), rtol=1e-11)
+        assert np.isclose(np.sum(g * m.conv(x, sh, vw, src, dst, 4, layout=lay)), np.sum(dw * vw), rtol=1e-11)
+    one = tp.ChannelwiseTP("4x1o", "0e", "1o", merge=True)
+    ref = tp.ChannelwiseTP("4x1o", "0e", "1o")
+    xx = rng.normal(size=(3, 12))
+    ss = rng.normal(size=(3, 1))
+    ww = rng.normal(size=(3, 4))
+    assert np.allclose(one.conv(xx, ss, ww), ref.conv(xx, ss, ww), atol=1e-13)
+    with pytest.raises(ValueError):
+        tp.ChannelwiseTP("4x0e+3x0e", "0e", "0e", merge=True)
