@@ -76,6 +76,11 @@ extern "C" {
                                      (rows without edges stay zero); the convolution layer's reduce="mean"
                                      of the "cuequivariance-torch" skill document, "Other operations and
                                      layers".  The backward takes the same flag from the handle. */
+#define SEGPOLY_MERGE_PATHS 16u   /* tp_create: the paths of one output type sum into a single block of that
+                                     type (e3nn-style instructions writing one irrep; a reading, the pages
+                                     print no merged example); output blocks in type order, all paths of a
+                                     type must have the same multiplicity (E_UNSUPPORTED otherwise); weights
+                                     and path order unchanged.  tp_irreps_out reports the merged irreps. */
 
 /* query keys */
 #define SEGPOLY_Q_DIM_IN1 0

@@ -22,7 +22,7 @@ E_INVALID, E_PARSE, E_UNSUPPORTED, E_UNSORTED, E_HIP, E_OOM, E_RANGE = -1, -2, -
 MUL_IR, IR_MUL = 0, 1
 F32, F64 = 0, 1
 I32, I64 = 0, 1
-SHARED_WEIGHTS, VALIDATE, FORCE_GENERIC, REDUCE_MEAN = 1, 2, 4, 8
+SHARED_WEIGHTS, VALIDATE, FORCE_GENERIC, REDUCE_MEAN, MERGE_PATHS = 1, 2, 4, 8, 16
 (Q_DIM_IN1, Q_DIM_IN2, Q_DIM_OUT, Q_WEIGHT_NUMEL, Q_NUM_PATHS, Q_CG_NNZ, Q_SPECIALIZED, Q_MUL,
  Q_DIM_IN, Q_NUM_COUPLINGS, Q_NUM_TERMS, Q_NUM_ELEMENTS, Q_NUM_MONOMIALS) = range(13)
 
@@ -143,9 +143,10 @@ def _str(fn, h, cap=1 << 16):
     return buf.value.decode()
 
 
-def _flags(shared_weights=False, validate=False, force_generic=False, reduce_mean=False):
+def _flags(shared_weights=False, validate=False, force_generic=False, reduce_mean=False, merge=False):
     return (SHARED_WEIGHTS if shared_weights else 0) | (VALIDATE if validate else 0) | \
-        (FORCE_GENERIC if force_generic else 0) | (REDUCE_MEAN if reduce_mean else 0)
+        (FORCE_GENERIC if force_generic else 0) | (REDUCE_MEAN if reduce_mean else 0) | \
+        (MERGE_PATHS if merge else 0)
 
 
 def _stream_ptr(device):
@@ -205,12 +206,14 @@ class TPHandle:
 
 
 def tp_create(irreps_in1, irreps_in2, irreps_out, layout="mul_ir", dtype="f32", shared_weights=False,
-              validate=False, force_generic=False, reduce="sum"):
+              validate=False, force_generic=False, reduce="sum", merge=False):
+    """Channelwise product / convolution handle; ``merge`` sums the paths of
+    one output type into one block."""
     if reduce not in ("sum", "mean"):
         raise ValueError("reduce is 'sum' or 'mean'")
     raw = ctypes.c_void_p()
     _check(lib.tp_create(irreps_in1.encode(), irreps_in2.encode(), irreps_out.encode(), _LAYOUTS[layout],
-                         _DTYPES[dtype], _flags(shared_weights, validate, force_generic, reduce == "mean"),
+                         _DTYPES[dtype], _flags(shared_weights, validate, force_generic, reduce == "mean", merge),
                          ctypes.byref(raw)))
     return TPHandle(raw, layout, dtype, shared_weights)
 

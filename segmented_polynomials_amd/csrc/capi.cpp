@@ -149,12 +149,13 @@ int tp_create(const char* in1, const char* in2, const char* outs, int layout, in
   if (!in1 || !in2 || !outs) return fail(SEGPOLY_E_INVALID, "null irreps string");
   if (layout != SEGPOLY_MUL_IR && layout != SEGPOLY_IR_MUL) return fail(SEGPOLY_E_INVALID, "bad layout");
   if (dtype != SEGPOLY_F32 && dtype != SEGPOLY_F64) return fail(SEGPOLY_E_INVALID, "bad dtype");
-  if (flags & ~(SEGPOLY_SHARED_WEIGHTS | SEGPOLY_VALIDATE | SEGPOLY_FORCE_GENERIC | SEGPOLY_REDUCE_MEAN))
+  if (flags & ~(SEGPOLY_SHARED_WEIGHTS | SEGPOLY_VALIDATE | SEGPOLY_FORCE_GENERIC | SEGPOLY_REDUCE_MEAN |
+                SEGPOLY_MERGE_PATHS))
     return fail(SEGPOLY_E_INVALID, "unknown flag bits");
   segpoly_tp* h = nullptr;
   try {
     h = new segpoly_tp();
-    h->d = build_tp(in1, in2, outs);
+    h->d = build_tp(in1, in2, outs, (flags & SEGPOLY_MERGE_PATHS) != 0);
   } catch (const ParseError& e) {
     delete h;
     return fail(SEGPOLY_E_PARSE, e.what());
@@ -179,8 +180,7 @@ int tp_create(const char* in1, const char* in2, const char* outs, int layout, in
         break;
       }
   }
-  // generic tables
-  int kc = 0;
+  // generic tables (merged paths share their output components)
   for (const auto& p : h->d.paths) {
     GPath g{};
     g.l1 = p.l1;
@@ -189,8 +189,7 @@ int tp_create(const char* in1, const char* in2, const char* outs, int layout, in
     g.nz_begin = static_cast<int>(h->gnz.size());
     for (const auto& z : p.nz) h->gnz.push_back({z.i, z.j, z.k, 0, z.c});
     g.nz_end = static_cast<int>(h->gnz.size());
-    g.kcomp = kc;
-    kc += 2 * p.lo + 1;
+    g.kcomp = p.kcomp;
     g.off1 = p.off1;
     g.off2 = p.off2;
     g.offo = p.offo;

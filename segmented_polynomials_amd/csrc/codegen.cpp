@@ -289,7 +289,11 @@ void emit_tp(const std::string& name, unsigned dtypes, const TPDescriptor& d, st
       in_blocks.push_back({comp, 2 * r.l + 1});
       comp += 2 * r.l + 1;
     }
-    for (const auto& p : d.paths) out_blocks.push_back({p.kcomp, 2 * p.lo + 1});
+    for (const auto& p : d.paths) {  // one block per distinct output slot (merged paths share one)
+      bool seen = false;
+      for (const auto& b : out_blocks) seen = seen || b.first == p.kcomp;
+      if (!seen) out_blocks.push_back({p.kcomp, 2 * p.lo + 1});
+    }
   }
   emit_row_io(os, "load_xs", "NX", in_blocks, d.nx, true);
   emit_row_io(os, "store_xs", "NX", in_blocks, d.nx, false);
@@ -597,10 +601,10 @@ int main(int argc, char** argv) {
       const unsigned dt = dtype_mask(h[2]);
       const std::string path = outdir + "/" + kind + "_" + name + ".hip";
       std::ofstream os(path);
-      if (kind == "tp") {
-        TPDescriptor d = build_tp(parts[1], parts[2], parts[3]);
+      if (kind == "tp" || kind == "tpm") {  // tpm: merged output blocks
+        TPDescriptor d = build_tp(parts[1], parts[2], parts[3], kind == "tpm");
         emit_tp(name, dt, d, os);
-        regs.push_back({kind, name, d.key, dt});
+        regs.push_back({"tp", name, d.key, dt});
       } else if (kind == "symcon") {
         std::vector<int> deg;
         for (auto& t : split(parts[3], ',')) deg.push_back(std::stoi(t));

@@ -15,8 +15,9 @@ int64_t TPDescriptor::cg_nnz() const {
   return n;
 }
 
-TPDescriptor build_tp(const std::string& s1, const std::string& s2, const std::string& so) {
+TPDescriptor build_tp(const std::string& s1, const std::string& s2, const std::string& so, bool merge) {
   TPDescriptor d;
+  d.merged = merge;
   d.in1 = parse_irreps(s1);
   d.in2 = parse_irreps(s2);
   std::vector<Irrep> filt = parse_irreps(so);
@@ -74,13 +75,28 @@ TPDescriptor build_tp(const std::string& s1, const std::string& s2, const std::s
   });
   int64_t oo = 0, wo = 0;
   int kc = 0;
-  for (auto& p : paths) {
-    p.offo = oo;
+  std::vector<int> type_first;  // merged: the first path of each output type
+  for (size_t pi = 0; pi < paths.size(); ++pi) {
+    TPPath& p = paths[pi];
     p.woff = wo;
-    p.kcomp = kc;
-    oo += static_cast<int64_t>(p.mul) * (2 * p.lo + 1);
     wo += p.mul;
-    kc += 2 * p.lo + 1;
+    int same = -1;
+    if (merge)
+      for (int f : type_first)
+        if (paths[f].lo == p.lo && paths[f].po == p.po) same = f;
+    if (same >= 0) {  // one block per type: share the first path's block
+      if (paths[same].mul != p.mul)
+        throw std::invalid_argument("merged paths of one output type need one multiplicity");
+      p.offo = paths[same].offo;
+      p.kcomp = paths[same].kcomp;
+    } else {
+      p.offo = oo;
+      p.kcomp = kc;
+      oo += static_cast<int64_t>(p.mul) * (2 * p.lo + 1);
+      kc += 2 * p.lo + 1;
+      type_first.push_back(static_cast<int>(pi));
+      d.out.push_back({p.mul, p.lo, p.po});
+    }
     const auto& cg = real_cg(p.l1, p.l2, p.lo);
     const int d1 = 2 * p.l1 + 1, d2 = 2 * p.l2 + 1, d3 = 2 * p.lo + 1;
     for (int k = 0; k < d3; ++k)
@@ -89,7 +105,6 @@ TPDescriptor build_tp(const std::string& s1, const std::string& s2, const std::s
           double v = cg[(static_cast<size_t>(i) * d2 + j) * d3 + k];
           if (v != 0.0) p.nz.push_back({i, j, k, v});
         }
-    d.out.push_back({p.mul, p.lo, p.po});
   }
   d.dimo = oo;
   d.numel = wo;
@@ -109,6 +124,7 @@ TPDescriptor build_tp(const std::string& s1, const std::string& s2, const std::s
   key += "|";
   for (const auto& p : d.paths)
     key += std::to_string(p.b1) + "." + std::to_string(p.b2) + "." + std::to_string(p.lo) + ",";
+  if (merge) key += "|merged";
   d.key = key;
   return d;
 }

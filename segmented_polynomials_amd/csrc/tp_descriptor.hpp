@@ -45,14 +45,17 @@ struct TPDescriptor {
   int mul = 0;               // that multiplicity (if uniform)
   int nx = 0;                // components per channel of input 1 (sum 2l+1)
   int nk = 0;                // components per channel of the output
+  bool merged = false;       // paths of one output type share one output block
   std::string key;           // structure key (independent of multiplicity)
   int64_t cg_nnz() const;
 };
 
 // Throws ParseError on bad strings, std::invalid_argument on unsupported
 // input (input-2 multiplicity other than 1, l above the supported maximum).
+// merge: the paths of one output type sum into one block of that type (all
+// of them must have the same multiplicity); output blocks in type order.
 TPDescriptor build_tp(const std::string& irreps_in1, const std::string& irreps_in2,
-                      const std::string& irreps_out);
+                      const std::string& irreps_out, bool merge = false);
 
 constexpr int kMaxL = 8;
 

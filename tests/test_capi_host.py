@@ -334,6 +334,16 @@ def test_fctp_errors_and_workspace():
     assert c(b"2x0e", b"2x0e", b"2x0e", 0, 0, 8 | 16, ctypes.byref(raw)) == sp.E_INVALID  # unknown flag
 
 
+def test_merged_descriptor():
+    h = sp.tp_create("32x0e+32x1o", "0e+1o+2e", "0e+1o+2e", merge=True)
+    o = otp.ChannelwiseTP("32x0e+32x1o", "0e+1o+2e", "0e+1o+2e", merge=True)
+    assert h.irreps_out == o.irreps_out and h.dim_out == o.dim_out and h.weight_numel == o.weight_numel
+    assert h.specialized and h.num_paths == o.num_paths
+    raw = ctypes.c_void_p()
+    assert sp.lib.tp_create(b"4x0e+3x0e", b"0e", b"0e", 0, 0, sp.MERGE_PATHS, ctypes.byref(raw)) == sp.E_UNSUPPORTED
+    assert sp.lib.tp_create(b"4x0e", b"0e", b"0e", 0, 0, 32, ctypes.byref(raw)) == sp.E_INVALID
+
+
 def test_sh_argument_errors():
     p = ctypes.c_void_p(16)
     assert sp.lib.sh_fwd(7, 1, 0, p, 4, p, None) == sp.E_UNSUPPORTED
