@@ -99,9 +99,14 @@ class FullyConnectedTP:
             ob[o] += self.alpha[o] * np.einsum("abk,nau,nbv,uvw->nkw", c, a[i], b[j], W, optimize=True)
         return join_blocks(ob, layout)
 
-    def vjp(self, x1, x2, w, g, layout="mul_ir", absolute=False):
+    def vjp(self, x1, x2, w, g, layout="mul_ir", absolute=False, edge_weights=None):
         """Vector-Jacobian product of :meth:`fwd` for g = dL/d(out): returns
-        (dx1, dx2, dw); the output is linear in each of x1, x2 and w."""
+        (dx1, dx2, dw); the output is linear in each of x1, x2 and w.  With
+        ``edge_weights`` [n, weight_numel] (one row per sample, w unused) dw
+        is per sample, [n, weight_numel]."""
+        per = edge_weights is not None
+        if per:
+            w = edge_weights
         x1, x2, w, g = (np.asarray(a, dtype=np.float64) for a in (x1, x2, w, g))
         if absolute:
             x1, x2, w, g = np.abs(x1), np.abs(x2), np.abs(w), np.abs(g)
@@ -115,8 +120,16 @@ class FullyConnectedTP:
             c = real_cg(self.in1[i][1], self.in2[j][1], self.out[o][1])
             if absolute:
                 c = np.abs(c)
-            W = self._segment(w, p)
             al = self.alpha[o]
+            m1, m2, m3 = self.in1[i][0], self.in2[j][0], self.out[o][0]
+            if per:
+                W = w[:, off:off + m1 * m2 * m3].reshape(-1, m1, m2, m3)
+                da[i] += al * np.einsum("abk,nbv,nuvw,nkw->nau", c, b[j], W, gb[o], optimize=True)
+                db[j] += al * np.einsum("abk,nau,nuvw,nkw->nbv", c, a[i], W, gb[o], optimize=True)
+                dW = al * np.einsum("abk,nau,nbv,nkw->nuvw", c, a[i], b[j], gb[o], optimize=True)
+                dw[:, off:off + m1 * m2 * m3] = dW.reshape(dW.shape[0], -1)
+                continue
+            W = self._segment(w, p)
             da[i] += al * np.einsum("abk,nbv,uvw,nkw->nau", c, b[j], W, gb[o], optimize=True)
             db[j] += al * np.einsum("abk,nau,uvw,nkw->nbv", c, a[i], W, gb[o], optimize=True)
             dW = al * np.einsum("abk,nau,nbv,nkw->uvw", c, a[i], b[j], gb[o], optimize=True)
@@ -183,3 +196,25 @@ class FullyConnectedTP:
         elif reduce != "sum":
             raise ValueError("reduce is 'sum' or 'mean'")
         return join_blocks(ob, layout)
+
+    def conv_vjp(self, x1, x2, w, src, dst, n_nodes, g, layout="mul_ir", reduce="sum", absolute=False):
+        """Vector-Jacobian product of :meth:`conv` with one weight row per
+        edge, for g = dL/d(out) [n_nodes, dim_out]: returns (dx1 [n_src,
+        dim_in1], dx2 [n_edges, dim_in2], dw [n_edges, weight_numel]).  Per
+        edge e (source s, destination n, G = g[n] scaled by 1/deg(n) with
+        reduce="mean") it is the batch VJP of the edge's product; dx1 sums
+        the edges that read each source."""
+        x1, x2, w, g = (np.asarray(a, dtype=np.float64) for a in (x1, x2, w, g))
+        src = np.asarray(src, dtype=np.int64)
+        dst = np.asarray(dst, dtype=np.int64)
+        if reduce == "mean":
+            deg = np.bincount(dst, minlength=n_nodes)[:n_nodes].astype(np.float64)
+            g = g * np.where(deg > 0, 1.0 / np.maximum(deg, 1.0), 0.0)[:, None]
+        elif reduce != "sum":
+            raise ValueError("reduce is 'sum' or 'mean'")
+        if w.shape[0] == 1 and x2.shape[0] != 1:
+            raise ValueError("the convolution VJP takes one weight row per edge")
+        d1, d2, dw = self.vjp(x1[src], x2, None, g[dst], layout=layout, absolute=absolute, edge_weights=w)
+        dx1 = np.zeros_like(x1)
+        np.add.at(dx1, src, d1)
+        return dx1, d2, dw

@@ -258,3 +258,29 @@ def test_conv_mean_and_equivariance():
     D2 = wigner.wigner_d_irreps(f.in2, aa, parity=-1)
     Do = wigner.wigner_d_irreps(f.out, aa, parity=-1)
     assert np.allclose(f.conv(x1 @ D1.T, x2 @ D2.T, w, src, dst, 4), s @ Do.T, atol=1e-11)
+
+
+@pytest.mark.parametrize("reduce", ["sum", "mean"])
+def test_conv_vjp_adjoint_identities(reduce):
+    f = fctp.FullyConnectedTP("3x0e+2x1o", "0e+1o+2e", "2x0e+3x1o+1x2e")
+    rng = np.random.default_rng(12)
+    src, dst = _graph(rng, 6, 5, 14)
+    dst[dst == 2] = 3                       # node 2 without edges
+    x1 = rng.normal(size=(6, f.dim_in1))
+    x2 = rng.normal(size=(14, f.dim_in2))
+    w = rng.normal(size=(14, f.weight_numel))
+    g = rng.normal(size=(5, f.dim_out))
+    for lay in ("mul_ir", "ir_mul"):
+        dx1, dx2, dw = f.conv_vjp(x1, x2, w, src, dst, 5, g, layout=lay, reduce=reduce)
+        v1, v2, vw = rng.normal(size=x1.shape), rng.normal(size=x2.shape), rng.normal(size=w.shape)
+        F = lambda a, b, c: f.conv(a, b, c, src, dst, 5, layout=lay, reduce=reduce)
+        assert np.isclose(np.sum(g * F(v1, x2, w)), np.sum(dx1 * v1), rtol=1e-11)
+        assert np.isclose(np.sum(g * F(x1, v2, w)), np.sum(dx2 * v2), rtol=1e-11)
+        assert np.isclose(np.sum(g * F(x1, x2, vw)), np.sum(dw * vw), rtol=1e-11)
+    # sources no edge reads get zero; absolute mode bounds every gradient
+    unread = np.setdiff1d(np.arange(6), src)
+    assert np.count_nonzero(dx1[unread]) == 0
+    a1, a2, aw = f.conv_vjp(x1, x2, w, src, dst, 5, g, reduce=reduce, absolute=True)
+    r1, r2, rw = f.conv_vjp(x1, x2, w, src, dst, 5, g, reduce=reduce)
+    for r, a in ((r1, a1), (r2, a2), (rw, aw)):
+        assert np.all(np.abs(r) <= a + 1e-12)
