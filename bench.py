@@ -526,7 +526,23 @@ def fc_conv(torch, sp, workloads, dev, args):
         res[lay] = {"ms_per_call": kms, "edges_per_s": E / (wall / args.steps), "kernel": "fcconv_kernel",
                     "roofline": {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                                  "frac": gbps / HBM_PEAK_GBPS}}
-        del out
+        # backward: per edge the weight row read and its gradient written, the
+        # harmonics and their gradient, the source message written and read
+        # back; per node the output-gradient row; per source x and dx
+        g = torch.from_numpy(workloads.output_gradient(N, h.dim_out, wl.dtype, seed=2009)).to(dev)
+        perm = torch.argsort(src, stable=True).to(src.dtype)
+        ws = torch.empty(max(1, sp.fctp_conv_bwd_workspace(h, E)), dtype=torch.uint8, device=dev)
+        wallb, perb = time_launches(torch, lambda: sp.fctp_conv_bwd(h, x, sh, w, g, src, dst, perm, N, workspace=ws),
+                                    args.steps, args.warmup)
+        kb = sum(perb) / len(perb)
+        bbytes = (E * (2 * f.weight_numel + 2 * f.dim_in2 + 2 * f.dim_in1) * 4 + 3 * E * 4 +
+                  N * f.dim_out * 4 + 2 * N * f.dim_in1 * 4)
+        res[lay]["backward"] = {"ms_per_call": kb, "kernels": ["fcconv_bwd_edge_kernel", "fcconv_bwd_src_kernel"],
+                                "roofline": {"bound": "hbm", "achieved": bbytes / (kb * 1e-3) / 1e9,
+                                             "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                                             "frac": bbytes / (kb * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+                                             "algorithmic_bytes": bbytes}}
+        del out, g, perm, ws
     del x, sh, w, src, dst
     return res
 

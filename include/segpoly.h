@@ -470,6 +470,31 @@ int fctp_conv_fwd(fctp_handle h, const void* x, int64_t n_src, const void* sh, c
                   const void* src, const void* dst, int idx_dtype, int64_t n_edges, int64_t n_nodes, void* out,
                   void* stream);
 
+/* fctp_conv_bwd_workspace: bytes of workspace fctp_conv_bwd needs for
+ * n_edges edges (the per-edge source messages, [n_edges, DIM_IN1]). */
+int fctp_conv_bwd_workspace(fctp_handle h, int64_t n_edges, size_t* bytes);
+
+/*
+ * fctp_conv_bwd: vector-Jacobian product of fctp_conv_fwd with one weight
+ * row per edge (w_rows == n_edges; one shared row gives E_UNSUPPORTED), for
+ * grad_out = dL/d(out) [n_nodes, DIM_OUT] device (divided by each row's edge
+ * count with SEGPOLY_REDUCE_MEAN, as the forward):
+ *   grad_w  [n_edges, WEIGHT_NUMEL]: per edge, dW_e[p][u, w] = sum_k y[p, k, u] G[o, k, w]
+ *   grad_sh [n_edges, DIM_IN2]:      per edge
+ *   grad_x  [n_src, DIM_IN1]:        summed over the edges that read each source,
+ * all fully overwritten (zero for sources no edge reads and for edges whose
+ * destination lies outside [0, n_nodes)).  src_perm [n_edges] (same index
+ * dtype) lists the edges ordered by source (a stable argsort of src:
+ * structure of the batch, like the sorted dst); VALIDATE checks it and the
+ * indices.  The source sums run in src_perm order: deterministic.
+ * `workspace` holds fctp_conv_bwd_workspace(n_edges) bytes.  Other
+ * arguments as fctp_conv_fwd.
+ */
+int fctp_conv_bwd(fctp_handle h, const void* x, int64_t n_src, const void* sh, const void* w, int64_t w_rows,
+                  const void* src, const void* dst, const void* src_perm, int idx_dtype, int64_t n_edges,
+                  int64_t n_nodes, const void* grad_out, void* grad_x, void* grad_sh, void* grad_w, void* workspace,
+                  size_t workspace_bytes, void* stream);
+
 /* fctp_destroy: free the handle (NULL is a no-op). */
 int fctp_destroy(fctp_handle h);
 

@@ -34,7 +34,7 @@ EXPORTS = ("tp_create", "tp_query", "tp_irreps_out", "tp_path_info", "tp_path_cg
            "tp_conv_fwd", "tp_conv_fwd_vec", "tp_conv_bwd_workspace", "tp_conv_bwd", "tp_destroy", "symcon_create", "symcon_query", "symcon_coupling_info",
            "symcon_coupling_dense", "symcon_fwd", "symcon_bwd_workspace", "symcon_bwd", "symcon_destroy", "linear_create", "linear_query", "linear_fwd",
            "linear_bwd_workspace", "linear_bwd", "linear_destroy", "fctp_create", "fctp_query", "fctp_path_info",
-           "fctp_fwd", "fctp_bwd_workspace", "fctp_bwd", "fctp_conv_fwd", "fctp_destroy", "sh_fwd", "sh_bwd", "segpoly_real_cg",
+           "fctp_fwd", "fctp_bwd_workspace", "fctp_bwd", "fctp_conv_fwd", "fctp_conv_bwd_workspace", "fctp_conv_bwd", "fctp_destroy", "sh_fwd", "sh_bwd", "segpoly_real_cg",
            "segpoly_last_error", "segpoly_version")
 
 
@@ -102,6 +102,9 @@ def _load():
         "fctp_bwd_workspace": [vp, i64, ctypes.POINTER(ctypes.c_size_t)],
         "fctp_bwd": [vp, vp, vp, vp, vp, i64, vp, vp, vp, vp, ctypes.c_size_t, vp],
         "fctp_conv_fwd": [vp, vp, i64, vp, vp, i64, vp, vp, c_int, i64, i64, vp, vp],
+        "fctp_conv_bwd_workspace": [vp, i64, ctypes.POINTER(ctypes.c_size_t)],
+        "fctp_conv_bwd": [vp, vp, i64, vp, vp, i64, vp, vp, vp, c_int, i64, i64, vp, vp, vp, vp, vp,
+                          ctypes.c_size_t, vp],
         "fctp_destroy": [vp],
         "sh_fwd": [c_int, c_int, c_int, vp, i64, vp, vp],
         "sh_bwd": [c_int, c_int, c_int, vp, vp, i64, vp, vp],
@@ -670,6 +673,35 @@ def fctp_conv_fwd(h, x, sh, w, src, dst, n_nodes, out=None):
     _check(lib.fctp_conv_fwd(h._h, _ptr(x), x.shape[0], _ptr(sh), _ptr(w), w.shape[0], _ptr(src), _ptr(dst),
                              _index_dtype(src), n_edges, n_nodes, _ptr(out), _stream_ptr(x.device)))
     return out
+
+
+def fctp_conv_bwd_workspace(h, n_edges):
+    v = ctypes.c_size_t()
+    _check(lib.fctp_conv_bwd_workspace(h._h, n_edges, ctypes.byref(v)))
+    return v.value
+
+
+def fctp_conv_bwd(h, x, sh, w, grad_out, src, dst, src_perm, n_nodes=None, workspace=None):
+    """(grad_x, grad_sh, grad_w) of ``fctp_conv_fwd`` with one weight row per
+    edge; ``src_perm`` orders the edges by source (stable argsort of src)."""
+    import torch
+    n_edges = sh.shape[0]
+    n_nodes = grad_out.shape[0] if n_nodes is None else n_nodes
+    if w.shape[0] != n_edges:
+        raise ValueError("the backward takes one weight row per edge")
+    for name, a in (("src", src), ("dst", dst), ("src_perm", src_perm)):
+        if a.shape != (n_edges,) or a.dtype != src.dtype or not a.is_cuda or not a.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous [n_edges] device tensor of src's dtype")
+    if grad_out.shape != (n_nodes, h.dim_out) or not grad_out.is_contiguous():
+        raise ValueError("grad_out has the wrong shape")
+    gx, gs, gw = torch.empty_like(x), torch.empty_like(sh), torch.empty_like(w)
+    if workspace is None:
+        workspace = torch.empty(max(1, fctp_conv_bwd_workspace(h, n_edges)), dtype=torch.uint8, device=x.device)
+    wbytes = workspace.numel() * workspace.element_size()
+    _check(lib.fctp_conv_bwd(h._h, _ptr(x), x.shape[0], _ptr(sh), _ptr(w), w.shape[0], _ptr(src), _ptr(dst),
+                             _ptr(src_perm), _index_dtype(src), n_edges, n_nodes, _ptr(grad_out), _ptr(gx), _ptr(gs),
+                             _ptr(gw), _ptr(workspace), wbytes, _stream_ptr(x.device)))
+    return gx, gs, gw
 
 
 # ---------------------------------------------------------------- spherical harmonics

@@ -36,26 +36,6 @@ int copy_str(const std::string& s, char* buf, size_t cap) {
   return ok();
 }
 
-// VALIDATE for the backward: perm is a permutation of the edges with
-// src[perm[.]] ascending.
-template <typename Index>
-int check_perm(const void* dsrc, const void* dperm, int64_t n_edges, void* stream) {
-  std::vector<Index> s(n_edges), p(n_edges);
-  hipError_t e = hipStreamSynchronize(static_cast<hipStream_t>(stream));
-  if (e == hipSuccess && n_edges) e = hipMemcpy(s.data(), dsrc, n_edges * sizeof(Index), hipMemcpyDeviceToHost);
-  if (e == hipSuccess && n_edges) e = hipMemcpy(p.data(), dperm, n_edges * sizeof(Index), hipMemcpyDeviceToHost);
-  if (e != hipSuccess) return fail(SEGPOLY_E_HIP, std::string("validate copy: ") + hipGetErrorString(e));
-  std::vector<char> seen(n_edges, 0);
-  for (int64_t i = 0; i < n_edges; ++i) {
-    const int64_t q = static_cast<int64_t>(p[i]);
-    if (q < 0 || q >= n_edges || seen[q])
-      return fail(SEGPOLY_E_RANGE, "src_perm is not a permutation of the edges (entry " + std::to_string(i) + ")");
-    seen[q] = 1;
-    if (i && s[q] < s[p[i - 1]])
-      return fail(SEGPOLY_E_UNSORTED, "src[src_perm[.]] is not ascending at entry " + std::to_string(i));
-  }
-  return ok();
-}
 
 // VALIDATE for the symmetric-contraction backward: perm is a permutation
 // of the atoms with species[perm[.]] ascending.

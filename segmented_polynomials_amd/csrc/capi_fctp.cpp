@@ -106,9 +106,12 @@ struct segpoly_fctp {
   std::vector<FcvTile> cv_tiles;
   std::vector<FcvQ> cv_qs;
   std::vector<FcvChunk> cv_chunks;
+  std::vector<FcvBPath> cv_bpaths;    // backward: every path with its global rows
+  std::string conv_bwd_error;         // why the backward is unavailable ("" if available)
+  size_t cv_bwd_lds = 0;
   int cv_ncomp = 0, cv_max_nqk = 0, cv_lane_bits = 0;
   size_t cv_lds = 0;
-  size_t cv_off[7] = {0, 0, 0, 0, 0, 0, 0};  // blocks, paths, qks, ents, tiles, qs, chunks within the blob
+  size_t cv_off[8] = {0, 0, 0, 0, 0, 0, 0, 0};  // blocks, paths, qks, ents, tiles, qs, chunks, bpaths in the blob
   std::vector<unsigned char> blob;
   std::map<int, DeviceBuffer> dev;
   std::mutex mu;
@@ -332,6 +335,10 @@ void build_conv(segpoly_fctp* h) {
     }
     const int n_chunks = static_cast<int>(h->cv_chunks.size()) - chunk_begin;
     const int nq = static_cast<int>(h->cv_qs.size()) - q_begin;
+    for (int pi = path_begin; pi < path_end; ++pi) {
+      const FcvPath& P = h->cv_paths[pi];
+      h->cv_bpaths.push_back({P.w_off, h->offo[o], P.m1, ob.mul, d3, qk_begin + P.qk});
+    }
     for (int w0 = 0; w0 < ob.mul; w0 += 64) {
       FcvTile t{};
       t.out_off = h->offo[o];
@@ -356,6 +363,11 @@ void build_conv(segpoly_fctp* h) {
     h->conv_error = "the convolution form's per-edge rows exceed the LDS of one wave";
     return;
   }
+  const size_t nrows = h->cv_qks.size();
+  h->cv_bwd_lds = (S * (2 * (static_cast<size_t>(h->cv_ncomp) * lanes + 1) + static_cast<size_t>(h->dim2) + 1 +
+                        2 * (nrows * lanes + 1) + static_cast<size_t>(h->dim2) * lanes + 1) +
+                   static_cast<size_t>(h->dimo)) * elt(h->dtype);
+  if (h->cv_bwd_lds > 64 * 1024) h->conv_bwd_error = "the convolution backward's per-edge rows exceed the LDS of one wave";
 }
 
 template <typename V>
@@ -512,6 +524,7 @@ int fctp_create(const char* irreps_in1, const char* irreps_in2, const char* irre
       h->cv_off[4] = append(h->blob, h->cv_tiles);
       h->cv_off[5] = append(h->blob, h->cv_qs);
       h->cv_off[6] = append(h->blob, h->cv_chunks);
+      h->cv_off[7] = append(h->blob, h->cv_bpaths);
     }
   } catch (const std::bad_alloc&) {
     rc = fail(SEGPOLY_E_OOM, "out of host memory");
@@ -665,6 +678,73 @@ int fctp_conv_fwd(fctp_handle h, const void* x, int64_t n_src, const void* sh, c
   a.stream = stream;
   const int rc = launch_fcconv(a);
   if (rc) return fail(SEGPOLY_E_HIP, std::string("fctp conv launch: ") + hipGetErrorString(static_cast<hipError_t>(rc)));
+  return ok();
+}
+
+int fctp_conv_bwd_workspace(fctp_handle h, int64_t n_edges, size_t* bytes) {
+  if (!h || !bytes) return fail(SEGPOLY_E_INVALID, "null argument");
+  if (n_edges < 0) return fail(SEGPOLY_E_INVALID, "negative edge count");
+  *bytes = static_cast<size_t>(round_up_256(n_edges * h->dim1 * static_cast<int64_t>(elt(h->dtype))));
+  return ok();
+}
+
+int fctp_conv_bwd(fctp_handle h, const void* x, int64_t n_src, const void* sh, const void* w, int64_t w_rows,
+                  const void* src, const void* dst, const void* src_perm, int idx_dtype, int64_t n_edges,
+                  int64_t n_nodes, const void* grad_out, void* grad_x, void* grad_sh, void* grad_w, void* workspace,
+                  size_t workspace_bytes, void* stream) {
+  if (!h) return fail(SEGPOLY_E_INVALID, "null handle");
+  if (!h->conv_error.empty()) return fail(SEGPOLY_E_UNSUPPORTED, h->conv_error);
+  if (!h->conv_bwd_error.empty()) return fail(SEGPOLY_E_UNSUPPORTED, h->conv_bwd_error);
+  if (n_src < 0 || n_edges < 0 || n_nodes < 0) return fail(SEGPOLY_E_INVALID, "negative size");
+  if (idx_dtype != SEGPOLY_I32 && idx_dtype != SEGPOLY_I64) return fail(SEGPOLY_E_INVALID, "bad index dtype");
+  if (w_rows != n_edges)
+    return fail(n_edges > 1 && w_rows == 1 ? SEGPOLY_E_UNSUPPORTED : SEGPOLY_E_INVALID,
+                "the convolution backward takes one weight row per edge (w_rows == n_edges)");
+  size_t need = 0;
+  fctp_conv_bwd_workspace(h, n_edges, &need);
+  if (workspace_bytes < need) return fail(SEGPOLY_E_INVALID, "workspace too small: need " + std::to_string(need) + " bytes");
+  if ((n_src > 0 && !grad_x) || (n_edges > 0 && (!grad_sh || !grad_w)))
+    return fail(SEGPOLY_E_INVALID, "null gradient buffer");
+  if (n_edges > 0 && (!src || !dst || !src_perm || !workspace || (h->dim2 > 0 && !sh) || (h->numel > 0 && !w) ||
+                      (n_src > 0 && !x) || (n_nodes > 0 && h->dimo > 0 && !grad_out)))
+    return fail(SEGPOLY_E_INVALID, "null buffer");
+  if (n_nodes > kMaxGridX || n_src > kMaxGridX) return fail(SEGPOLY_E_UNSUPPORTED, "too many rows for one launch");
+  if (n_edges == 0) {  // dx = 0
+    const int rc = launch_fill_zero(grad_x, n_src * h->dim1, h->dtype, stream);
+    if (rc) return fail(SEGPOLY_E_HIP, std::string("fill: ") + hipGetErrorString(static_cast<hipError_t>(rc)));
+    return ok();
+  }
+  if (h->flags & SEGPOLY_VALIDATE) {
+    int st = idx_dtype == SEGPOLY_I32 ? check_indices<int32_t>(src, dst, n_edges, n_src, n_nodes, stream)
+                                      : check_indices<int64_t>(src, dst, n_edges, n_src, n_nodes, stream);
+    if (st) return st;
+    st = idx_dtype == SEGPOLY_I32 ? check_perm<int32_t>(src, src_perm, n_edges, stream)
+                                  : check_perm<int64_t>(src, src_perm, n_edges, stream);
+    if (st) return st;
+  }
+  int st = SEGPOLY_OK;
+  const unsigned char* db = device_blob(h, &st);
+  if (!db) return st;
+  FcvBwdArgs a{};
+  a.x = x, a.sh = sh, a.w = w, a.g = grad_out, a.src = src, a.dst = dst, a.perm = src_perm;
+  a.n_src = n_src, a.n_edges = n_edges, a.n_nodes = n_nodes;
+  a.dim1 = h->dim1, a.dim2 = h->dim2, a.dimo = h->dimo, a.numel = h->numel;
+  a.mean = (h->flags & SEGPOLY_REDUCE_MEAN) ? 1 : 0;
+  a.dx = grad_x, a.dsh = grad_sh, a.dw = grad_w, a.msg = workspace;
+  a.blocks = reinterpret_cast<const FcvBlock*>(db + h->cv_off[0]);
+  a.qks = reinterpret_cast<const FcvQK*>(db + h->cv_off[2]);
+  a.ents = reinterpret_cast<const FcvEnt*>(db + h->cv_off[3]);
+  a.bpaths = reinterpret_cast<const FcvBPath*>(db + h->cv_off[7]);
+  a.n_blocks = static_cast<int>(h->cv_blocks.size());
+  a.n_bpaths = static_cast<int>(h->cv_bpaths.size());
+  a.nrows = static_cast<int>(h->cv_qks.size());
+  a.ncomp = h->cv_ncomp;
+  a.lane_bits = h->cv_lane_bits;
+  a.lds_bytes = h->cv_bwd_lds;
+  a.dtype = h->dtype, a.layout = h->layout, a.idx = idx_dtype;
+  a.stream = stream;
+  const int rc = launch_fcconv_bwd(a);
+  if (rc) return fail(SEGPOLY_E_HIP, std::string("fctp conv backward launch: ") + hipGetErrorString(static_cast<hipError_t>(rc)));
   return ok();
 }
 

@@ -63,6 +63,42 @@ struct FcvTile {
   int q_begin, nq;                 // the remaining (path, u) weight elements
 };
 
+// Backward: every path with its rows in the global list of coupled rows
+// (the tiles' rows, output block by block).
+struct FcvBPath {
+  int64_t w_off;                   // weight segment [m1][m3]
+  int64_t g_off;                   // output block offset in a row of the output gradient
+  int m1, m3, d3;
+  int row;                         // first of its d3 rows
+};
+
+struct FcvBwdArgs {
+  const void* x;
+  const void* sh;
+  const void* w;
+  const void* g;
+  const void* src;
+  const void* dst;
+  const void* perm;                // edges ordered by source (stable argsort of src)
+  int64_t n_src, n_edges, n_nodes;
+  int64_t dim1, dim2, dimo, numel;
+  int mean;
+  void* dx;
+  void* dsh;
+  void* dw;
+  void* msg;                       // workspace: per-edge source messages [n_edges][dim1]
+  const FcvBlock* blocks;          // device tables
+  const FcvQK* qks;
+  const FcvEnt* ents;
+  const FcvBPath* bpaths;
+  int n_blocks, n_bpaths, nrows, ncomp, lane_bits;
+  size_t lds_bytes;
+  int dtype, layout, idx;
+  void* stream;
+};
+
+int launch_fcconv_bwd(const FcvBwdArgs& a);
+
 struct FcvArgs {
   const void* x;
   const void* sh;

@@ -1,0 +1,229 @@
+// Backward (vector-Jacobian product) of the fully connected convolution
+// with per-edge weights.  With G = dL/d(out)[dst_e] (divided by the in-degree
+// for reduce="mean") and, per path p = (i, j, o) of edge e,
+//   y[p, k, u] = alpha_o sum_(a, b) C[a, b, k] x[src_e, i, a, u] sh[e, j, b]   (the forward's rows)
+//   z[p, k, u] = sum_w W_e[p][u, w] G[o, k, w]
+// the gradients are
+//   dW_e[p][u, w]     = sum_k y[p, k, u] G[o, k, w]
+//   dsh[e, j, b]     += alpha_o sum_(a, k, u) C[a, b, k] x[src_e, i, a, u] z[p, k, u]
+//   msg_e[i, a, u]   += alpha_o sum_(b, k) C[a, b, k] sh[e, j, b] z[p, k, u]
+//   dx[s]             = sum over the edges e with src_e = s of msg_e.
+// fcconv_bwd_edge_kernel: one wave per destination, the forward's lane
+// slots (S edges at once, lane (slot, c)); dW and dsh are written per edge
+// (each edge belongs to one destination), the messages go to the workspace.
+// Edges whose destination lies outside [0, n_nodes) get zero gradients
+// (written by the first and the last destination's wave).
+// fcconv_bwd_src_kernel: one wave per source sums its edges' messages in
+// the order of the caller's source permutation (deterministic, no atomics).
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "../fcconv_tables.hpp"
+#include "../launch.hpp"
+#include "common.hpp"
+#include "tp_conv_bwd.hpp"
+#include "tp_conv_spec.hpp"
+
+namespace segpoly {
+namespace kern {
+
+__device__ __forceinline__ void fcb_wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+template <typename T, typename Index, int LAYOUT>
+__global__ void __launch_bounds__(64)
+fcconv_bwd_edge_kernel(const T* __restrict__ x, const T* __restrict__ sh, const T* __restrict__ w,
+                       const T* __restrict__ g, const Index* __restrict__ src, const Index* __restrict__ dst,
+                       int64_t n_src, int64_t n_edges, int64_t n_nodes, int64_t dim1, int64_t dim2, int64_t dimo,
+                       int64_t numel, int mean, T* __restrict__ dsh, T* __restrict__ dw, T* __restrict__ msg,
+                       const FcvBlock* __restrict__ blocks, const FcvQK* __restrict__ qks,
+                       const FcvEnt* __restrict__ ents, const FcvBPath* __restrict__ bpaths, int n_blocks,
+                       int n_bpaths, int nrows, int ncomp, int lane_bits) {
+  extern __shared__ __align__(16) unsigned char fcb_smem[];
+  T* lds = reinterpret_cast<T*>(fcb_smem);
+  const int64_t node = blockIdx.x;
+  const int lane = threadIdx.x;
+  const int M = 1 << lane_bits;
+  const int S = 64 >> lane_bits;
+  const int slot = lane >> lane_bits, c = lane & (M - 1);
+  // per-slot regions, strides padded by one: x, harmonics, y rows, z rows,
+  // messages, harmonic-gradient partials; then the node's gradient row
+  const int XS = ncomp * M + 1, SH = static_cast<int>(dim2) + 1, YS = nrows * M + 1, HS = static_cast<int>(dim2) * M + 1;
+  const int per_slot = 2 * XS + SH + 2 * YS + HS;
+  T* base = lds + slot * per_slot;
+  T* xs = base;
+  T* ms = xs + XS;
+  T* shs = ms + XS;
+  T* ys = shs + SH;
+  T* zs = ys + YS;
+  T* hp = zs + YS;
+  T* Gs = lds + S * per_slot;
+
+  int64_t e0, e1;
+  edge_range(dst, n_edges, 0, node, e0, e1);
+
+  // edges of no destination: zero gradients and messages
+  auto zero_edges = [&](int64_t a, int64_t b) {
+    for (int64_t e = a; e < b; ++e) {
+      for (int64_t i = lane; i < numel; i += 64) dw[e * numel + i] = T(0);
+      for (int64_t i = lane; i < dim2; i += 64) dsh[e * dim2 + i] = T(0);
+      for (int64_t i = lane; i < dim1; i += 64) msg[e * dim1 + i] = T(0);
+    }
+  };
+  if (node == 0) zero_edges(0, e0);
+  if (node == n_nodes - 1) zero_edges(e1, n_edges);
+
+  const T scale = (mean && e1 > e0) ? T(1) / static_cast<T>(e1 - e0) : T(1);
+  for (int64_t i = lane; i < dimo; i += 64) Gs[i] = scale * g[node * dimo + i];
+  fcb_wave_sync();
+  // G[o, k, w] of a path's output block in the row's layout
+  auto gidx = [&](const FcvBPath& P, int k, int wc) -> int64_t {
+    return P.g_off + (LAYOUT == kIrMul ? static_cast<int64_t>(k) * P.m3 + wc : static_cast<int64_t>(wc) * P.d3 + k);
+  };
+
+  for (int64_t eb = e0; eb < e1; eb += S) {
+    const int64_t e = eb + slot;
+    const bool valid = e < e1;
+    const int64_t s = valid ? static_cast<int64_t>(src[e]) : int64_t(-1);
+    const bool ok = s >= 0 && s < n_src;
+    // stage x[src] (zero for an out-of-range source) and the harmonics
+    for (int bi = 0; bi < n_blocks; ++bi) {
+      const FcvBlock B = blocks[bi];
+      const bool on = ok && c < B.m;
+      for (int a = 0; a < B.d; ++a) {
+        const int64_t off = LAYOUT == kIrMul ? B.off + static_cast<int64_t>(a) * B.m + c : B.off + static_cast<int64_t>(c) * B.d + a;
+        xs[(B.comp + a) * M + c] = on ? x[s * dim1 + off] : T(0);
+        ms[(B.comp + a) * M + c] = T(0);
+      }
+    }
+    for (int b = c; b < dim2; b += M) shs[b] = valid ? sh[e * dim2 + b] : T(0);
+    for (int b = 0; b < dim2; ++b) hp[b * M + c] = T(0);
+    fcb_wave_sync();
+    // coupled rows y (lane = input channel)
+    for (int r = 0; r < nrows; ++r) {
+      const FcvQK Q = qks[r];
+      T t = T(0);
+      for (int en = Q.ent_begin; en < Q.ent_end; ++en) {
+        const FcvEnt E = ents[en];
+        t = fmadd(static_cast<T>(E.c) * shs[E.b], xs[E.a * M + c], t);
+      }
+      ys[r * M + c] = t;
+    }
+    // z rows (lane = input channel u): z[p, k, u] = sum_w W[u, w] G[o, k, w]
+    for (int pi = 0; pi < n_bpaths; ++pi) {
+      const FcvBPath P = bpaths[pi];
+      const T* wr = w + e * numel + P.w_off + static_cast<int64_t>(c) * P.m3;
+      const bool on = valid && c < P.m1;
+      for (int k = 0; k < P.d3; ++k) {
+        T t = T(0);
+        if (on)
+          for (int wc = 0; wc < P.m3; ++wc) t = fmadd(wr[wc], Gs[gidx(P, k, wc)], t);
+        zs[(P.row + k) * M + c] = t;
+      }
+    }
+    fcb_wave_sync();
+    // dW (lane = output channel w): sum_k y[p, k, u] G[o, k, w]
+    if (valid)
+      for (int pi = 0; pi < n_bpaths; ++pi) {
+        const FcvBPath P = bpaths[pi];
+        for (int wc = c; wc < P.m3; wc += M) {
+          T* dwr = dw + e * numel + P.w_off + wc;
+          for (int u = 0; u < P.m1; ++u) {
+            T t = T(0);
+            for (int k = 0; k < P.d3; ++k) t = fmadd(ys[(P.row + k) * M + u], Gs[gidx(P, k, wc)], t);
+            dwr[static_cast<int64_t>(u) * P.m3] = t;
+          }
+        }
+      }
+    // messages and harmonic-gradient partials (lane = input channel)
+    for (int r = 0; r < nrows; ++r) {
+      const FcvQK Q = qks[r];
+      const T zv = zs[r * M + c];
+      for (int en = Q.ent_begin; en < Q.ent_end; ++en) {
+        const FcvEnt E = ents[en];
+        const T cz = static_cast<T>(E.c) * zv;
+        ms[E.a * M + c] = fmadd(cz, shs[E.b], ms[E.a * M + c]);
+        hp[E.b * M + c] = fmadd(cz, xs[E.a * M + c], hp[E.b * M + c]);
+      }
+    }
+    if (valid) {
+      for (int bi = 0; bi < n_blocks; ++bi) {
+        const FcvBlock B = blocks[bi];
+        if (c < B.m)
+          for (int a = 0; a < B.d; ++a) {
+            const int64_t off = LAYOUT == kIrMul ? B.off + static_cast<int64_t>(a) * B.m + c : B.off + static_cast<int64_t>(c) * B.d + a;
+            msg[e * dim1 + off] = ms[(B.comp + a) * M + c];
+          }
+      }
+    }
+    // dsh[e, b] = sum over the slot's lanes of hp[b]
+    for (int b = 0; b < dim2; ++b) {
+      T v = hp[b * M + c];
+      for (int dd = 1; dd < M; dd <<= 1) v += __shfl_xor(v, dd);
+      if (valid && c == 0) dsh[e * dim2 + b] = v;
+    }
+    fcb_wave_sync();
+  }
+}
+
+// dx[s] = sum of the messages of the edges that read s, in permutation order.
+template <typename T, typename Index>
+__global__ void __launch_bounds__(64)
+fcconv_bwd_src_kernel(const Index* __restrict__ src, const Index* __restrict__ perm, const T* __restrict__ msg,
+                      int64_t n_edges, int64_t dim1, T* __restrict__ dx) {
+  const int64_t s = blockIdx.x;
+  const int lane = threadIdx.x;
+  const int64_t i0 = lower_bound_perm(src, perm, n_edges, 0, n_edges, s);
+  const int64_t i1 = lower_bound_perm(src, perm, n_edges, i0, n_edges, s + 1);
+  for (int64_t j = lane; j < dim1; j += 64) {
+    T acc = T(0);
+    for (int64_t i = i0; i < i1; ++i) {
+      const int64_t e = static_cast<int64_t>(perm[i]);
+      if (e < 0 || e >= n_edges) continue;  // only an invalid permutation gets here
+      acc += msg[e * dim1 + j];
+    }
+    dx[s * dim1 + j] = acc;
+  }
+}
+
+template <typename T, typename Index, int LAYOUT>
+int fcconv_bwd_launch(const FcvBwdArgs& a) {
+  const hipStream_t st = static_cast<hipStream_t>(a.stream);
+  if (a.n_nodes > 0 && a.n_edges > 0)
+    hipLaunchKernelGGL((fcconv_bwd_edge_kernel<T, Index, LAYOUT>), dim3(static_cast<unsigned>(a.n_nodes)), dim3(64),
+                       a.lds_bytes, st, static_cast<const T*>(a.x), static_cast<const T*>(a.sh),
+                       static_cast<const T*>(a.w), static_cast<const T*>(a.g), static_cast<const Index*>(a.src),
+                       static_cast<const Index*>(a.dst), a.n_src, a.n_edges, a.n_nodes, a.dim1, a.dim2, a.dimo,
+                       a.numel, a.mean, static_cast<T*>(a.dsh), static_cast<T*>(a.dw), static_cast<T*>(a.msg),
+                       a.blocks, a.qks, a.ents, a.bpaths, a.n_blocks, a.n_bpaths, a.nrows, a.ncomp, a.lane_bits);
+  else if (a.n_edges > 0) {  // no destinations: every edge lies outside the output
+    fill_zero(static_cast<T*>(a.dw), a.n_edges * a.numel, st);
+    fill_zero(static_cast<T*>(a.dsh), a.n_edges * a.dim2, st);
+    fill_zero(static_cast<T*>(a.msg), a.n_edges * a.dim1, st);
+  }
+  int rc = static_cast<int>(hipGetLastError());
+  if (rc || a.n_src == 0) return rc;
+  hipLaunchKernelGGL((fcconv_bwd_src_kernel<T, Index>), dim3(static_cast<unsigned>(a.n_src)), dim3(64), 0, st,
+                     static_cast<const Index*>(a.src), static_cast<const Index*>(a.perm),
+                     static_cast<const T*>(a.msg), a.n_edges, a.dim1, static_cast<T*>(a.dx));
+  return static_cast<int>(hipGetLastError());
+}
+
+template <typename T>
+int fcconv_bwd_dispatch(const FcvBwdArgs& a) {
+  if (a.idx == kI64)
+    return a.layout == kMulIr ? fcconv_bwd_launch<T, int64_t, kMulIr>(a) : fcconv_bwd_launch<T, int64_t, kIrMul>(a);
+  return a.layout == kMulIr ? fcconv_bwd_launch<T, int32_t, kMulIr>(a) : fcconv_bwd_launch<T, int32_t, kIrMul>(a);
+}
+
+}  // namespace kern
+
+int launch_fcconv_bwd(const FcvBwdArgs& a) {
+  return a.dtype == kF32 ? kern::fcconv_bwd_dispatch<float>(a) : kern::fcconv_bwd_dispatch<double>(a);
+}
+
+}  // namespace segpoly

@@ -1,6 +1,6 @@
 """GPU parity of the fully connected product as a graph convolution with
-per-edge weights (fctp_conv_fwd), called through the C ABI, against the
-float64 oracle on the same seeded inputs.  Tolerance: scaled error
+per-edge weights (fctp_conv_fwd, and its backward fctp_conv_bwd), called
+through the C ABI, against the float64 oracle on the same seeded inputs.  Tolerance: scaled error
 (oracle.metrics) <= 1e-5 in float32, <= 1e-12 in float64."""
 
 import numpy as np
@@ -161,3 +161,60 @@ def test_full_size_workload_sampled(lay):
     check_scaled(got[nodes], f.conv(*args, layout=lay), f.conv(*args, layout=lay, absolute=True), wl.dtype,
                  "full size rows")
     del torch
+
+
+def _bwd(sp, h, x, sh, w, g, src, dst, n_nodes, dtype, idx="int32"):
+    import torch
+    td = _td(dtype)
+    it = torch.int32 if idx == "int32" else torch.int64
+    perm = np.argsort(src, kind="stable")
+    out = sp.fctp_conv_bwd(h, dev(x, td), dev(sh, td), dev(w, td), dev(g, td), dev(src).to(it), dev(dst).to(it),
+                           dev(perm).to(it), n_nodes=n_nodes)
+    torch.cuda.synchronize()
+    return [t.cpu().numpy() for t in out]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f64"])
+@pytest.mark.parametrize("lay", ["mul_ir", "ir_mul"])
+@pytest.mark.parametrize("case", range(len(CASES)))
+def test_backward_parity(case, lay, dtype):
+    sp = _sp()
+    in1, in2, out, n_nodes, deg, n_src = CASES[case]
+    f = ofc.FullyConnectedTP(in1, in2, out)
+    h = sp.fctp_create(in1, in2, out, layout=lay, dtype=dtype)
+    x, sh, w, src, dst = _case_inputs(f, n_nodes, deg, n_src, dtype, 320 + case)
+    g = np.random.default_rng(330 + case).standard_normal((n_nodes, f.dim_out)).astype(x.dtype)
+    idx = "int64" if (case + (lay == "ir_mul")) % 2 == 0 else "int32"
+    announce(f"fcconv backward case {case} E={dst.shape[0]} {lay} {dtype} {idx}")
+    got = _bwd(sp, h, x, sh, w, g, src, dst, n_nodes, dtype, idx)
+    ref = f.conv_vjp(x, sh, w, src, dst, n_nodes, g, layout=lay)
+    scale = f.conv_vjp(x, sh, w, src, dst, n_nodes, g, layout=lay, absolute=True)
+    for name, a, b, c in zip(("dx", "dsh", "dw"), got, ref, scale):
+        check_scaled(a, b, c, dtype, f"fcconv backward case {case} {name}")
+
+
+def test_backward_mean_and_outside_edges():
+    """reduce="mean" scales the output gradient by 1/in-degree; edges whose
+    destination is past the last row get zero gradients."""
+    sp = _sp()
+    in1, in2, out, n_nodes, deg, n_src = CASES[1]
+    f = ofc.FullyConnectedTP(in1, in2, out)
+    hm = sp.fctp_create(in1, in2, out, dtype="f64", reduce="mean")
+    x, sh, w, src, dst = _case_inputs(f, n_nodes, deg, n_src, "f64", 340)
+    g = np.random.default_rng(341).standard_normal((n_nodes, f.dim_out))
+    announce("fcconv backward mean")
+    got = _bwd(sp, hm, x, sh, w, g, src, dst, n_nodes, "f64")
+    ref = f.conv_vjp(x, sh, w, src, dst, n_nodes, g, reduce="mean")
+    scale = f.conv_vjp(x, sh, w, src, dst, n_nodes, g, reduce="mean", absolute=True)
+    for name, a, b, c in zip(("dx", "dsh", "dw"), got, ref, scale):
+        check_scaled(a, b, c, "f64", f"mean {name}")
+    # the output holds only the first 30 destinations: later edges lie outside
+    announce("fcconv backward edges outside the output")
+    h = sp.fctp_create(in1, in2, out, dtype="f64")
+    keep = 30
+    got = _bwd(sp, h, x, sh, w, g[:keep], src, dst, keep, "f64")
+    inside = dst < keep
+    ref = f.conv_vjp(x, sh[inside], w[inside], src[inside], dst[inside], keep, g[:keep])
+    assert np.allclose(got[0], ref[0], atol=1e-12)
+    assert np.allclose(got[1][inside], ref[1], atol=1e-12) and np.count_nonzero(got[1][~inside]) == 0
+    assert np.allclose(got[2][inside], ref[2], atol=1e-12) and np.count_nonzero(got[2][~inside]) == 0
