@@ -34,6 +34,73 @@ __device__ __forceinline__ void fcb_wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// One path of one edge, for an output block of D components:
+//   z[row + k, u] = sum_w W[u, w] G[k, w]     (lane = input channel u, the
+//                                            weight row read once, 16 channels at a time)
+//   dW[u, w]      = sum_k y[row + k, u] G[k, w] (lane = output channel w, G[., w] in registers)
+template <typename T, int LAYOUT, int D>
+__device__ __forceinline__ void fcb_path(const FcvBPath& P, const T* __restrict__ w, int64_t e, int64_t numel,
+                                         bool valid, int M, int c, const T* Gs, const T* ys, T* zs,
+                                         T* __restrict__ dw) {
+  auto gi = [&](int k, int wc) -> int {
+    return static_cast<int>(P.g_off) + (LAYOUT == kIrMul ? k * P.m3 + wc : wc * D + k);
+  };
+  {  // every lane stores its z rows (zero past mul1: the message phase reads them all)
+    T z[D];
+#pragma unroll
+    for (int k = 0; k < D; ++k) z[k] = T(0);
+    if (valid && c < P.m1) {
+      const T* wr = w + e * numel + P.w_off + static_cast<int64_t>(c) * P.m3;
+      int w0 = 0;
+      // 16-byte vector loads where the row is aligned (it is whenever m3
+      // is a multiple of 16 / sizeof(T) channels), else plain loads
+      const bool vec = (reinterpret_cast<uintptr_t>(wr) % 16) == 0 && (P.m3 * sizeof(T)) % 16 == 0;
+      for (; w0 + 16 <= P.m3; w0 += 16) {
+        T wv[16];
+        if (vec) {
+          constexpr int kV = 16 / sizeof(T);
+          typedef T vec_t __attribute__((ext_vector_type(kV)));
+#pragma unroll
+          for (int i = 0; i < 16; i += kV) {
+            const vec_t v = *reinterpret_cast<const vec_t*>(wr + w0 + i);
+#pragma unroll
+            for (int j = 0; j < kV; ++j) wv[i + j] = v[j];
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) wv[i] = wr[w0 + i];
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+#pragma unroll
+          for (int k = 0; k < D; ++k) z[k] = fmadd(wv[i], Gs[gi(k, w0 + i)], z[k]);
+      }
+      for (; w0 < P.m3; ++w0) {
+        const T wv = wr[w0];
+#pragma unroll
+        for (int k = 0; k < D; ++k) z[k] = fmadd(wv, Gs[gi(k, w0)], z[k]);
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < D; ++k) zs[(P.row + k) * M + c] = z[k];
+  }
+  if (valid)
+    for (int wc = c; wc < P.m3; wc += M) {
+      T gk[D];
+#pragma unroll
+      for (int k = 0; k < D; ++k) gk[k] = Gs[gi(k, wc)];
+      T* dwr = dw + e * numel + P.w_off + wc;
+      const T* yr = ys + P.row * M;
+#pragma unroll 4
+      for (int u = 0; u < P.m1; ++u) {
+        T t = T(0);
+#pragma unroll
+        for (int k = 0; k < D; ++k) t = fmadd(yr[k * M + u], gk[k], t);
+        dwr[static_cast<int64_t>(u) * P.m3] = t;
+      }
+    }
+}
+
 template <typename T, typename Index, int LAYOUT>
 __global__ void __launch_bounds__(64)
 fcconv_bwd_edge_kernel(const T* __restrict__ x, const T* __restrict__ sh, const T* __restrict__ w,
@@ -80,10 +147,6 @@ fcconv_bwd_edge_kernel(const T* __restrict__ x, const T* __restrict__ sh, const 
   const T scale = (mean && e1 > e0) ? T(1) / static_cast<T>(e1 - e0) : T(1);
   for (int64_t i = lane; i < dimo; i += 64) Gs[i] = scale * g[node * dimo + i];
   fcb_wave_sync();
-  // G[o, k, w] of a path's output block in the row's layout
-  auto gidx = [&](const FcvBPath& P, int k, int wc) -> int64_t {
-    return P.g_off + (LAYOUT == kIrMul ? static_cast<int64_t>(k) * P.m3 + wc : static_cast<int64_t>(wc) * P.d3 + k);
-  };
 
   for (int64_t eb = e0; eb < e1; eb += S) {
     const int64_t e = eb + slot;
@@ -113,32 +176,20 @@ fcconv_bwd_edge_kernel(const T* __restrict__ x, const T* __restrict__ sh, const 
       }
       ys[r * M + c] = t;
     }
-    // z rows (lane = input channel u): z[p, k, u] = sum_w W[u, w] G[o, k, w]
+    fcb_wave_sync();
+    // per path: z rows (lane = input channel) and dW (lane = output channel)
     for (int pi = 0; pi < n_bpaths; ++pi) {
       const FcvBPath P = bpaths[pi];
-      const T* wr = w + e * numel + P.w_off + static_cast<int64_t>(c) * P.m3;
-      const bool on = valid && c < P.m1;
-      for (int k = 0; k < P.d3; ++k) {
-        T t = T(0);
-        if (on)
-          for (int wc = 0; wc < P.m3; ++wc) t = fmadd(wr[wc], Gs[gidx(P, k, wc)], t);
-        zs[(P.row + k) * M + c] = t;
+      switch (P.d3) {
+        case 1: fcb_path<T, LAYOUT, 1>(P, w, e, numel, valid, M, c, Gs, ys, zs, dw); break;
+        case 3: fcb_path<T, LAYOUT, 3>(P, w, e, numel, valid, M, c, Gs, ys, zs, dw); break;
+        case 5: fcb_path<T, LAYOUT, 5>(P, w, e, numel, valid, M, c, Gs, ys, zs, dw); break;
+        case 7: fcb_path<T, LAYOUT, 7>(P, w, e, numel, valid, M, c, Gs, ys, zs, dw); break;
+        case 9: fcb_path<T, LAYOUT, 9>(P, w, e, numel, valid, M, c, Gs, ys, zs, dw); break;
+        case 11: fcb_path<T, LAYOUT, 11>(P, w, e, numel, valid, M, c, Gs, ys, zs, dw); break;
+        default: fcb_path<T, LAYOUT, 13>(P, w, e, numel, valid, M, c, Gs, ys, zs, dw); break;
       }
     }
-    fcb_wave_sync();
-    // dW (lane = output channel w): sum_k y[p, k, u] G[o, k, w]
-    if (valid)
-      for (int pi = 0; pi < n_bpaths; ++pi) {
-        const FcvBPath P = bpaths[pi];
-        for (int wc = c; wc < P.m3; wc += M) {
-          T* dwr = dw + e * numel + P.w_off + wc;
-          for (int u = 0; u < P.m1; ++u) {
-            T t = T(0);
-            for (int k = 0; k < P.d3; ++k) t = fmadd(ys[(P.row + k) * M + u], Gs[gidx(P, k, wc)], t);
-            dwr[static_cast<int64_t>(u) * P.m3] = t;
-          }
-        }
-      }
     // messages and harmonic-gradient partials (lane = input channel)
     for (int r = 0; r < nrows; ++r) {
       const FcvQK Q = qks[r];
