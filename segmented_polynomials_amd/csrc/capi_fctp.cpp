@@ -259,7 +259,7 @@ int build_dw(segpoly_fctp* h) {
     }
     const size_t per = (static_cast<size_t>(fc_sample_stride(q.p_d, q.p_m)) + fc_sample_stride(q.q_d, q.q_m) +
                         fc_sample_stride(q.g_d, q.g_m)) * elt(h->dtype);
-    int ts = static_cast<int>(std::min<size_t>(64, kLdsLimit / per)) & ~3;
+    int ts = static_cast<int>(std::min<size_t>(kFcDwSamples, kLdsLimit / per)) & ~3;
     if (ts < 4) return fail(SEGPOLY_E_UNSUPPORTED, "operand blocks too wide for the weight-gradient kernel");
     q.ts = ts;
     h->dw_nt = std::max(h->dw_nt, fc_t_class(q.T));

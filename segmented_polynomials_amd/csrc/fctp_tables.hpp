@@ -28,6 +28,8 @@ constexpr int kFcMaxRes = 32;    // result blocks per pass
 constexpr int kFcRowsMax = 128;  // rows (sample, component) per tile
 constexpr int kFcPad = 1;        // LDS padding of each staged channel row
 constexpr int kFcDwChunk = 1024; // samples per weight-gradient partial sum
+constexpr int kFcDwSamples = 16; // samples a weight-gradient workgroup stages at a time (few: several
+                                 // workgroups then share a CU and hide each other's staging loads)
 
 // LDS stride of one staged sample ([component][channel + kFcPad]), rounded up
 // to 16 mod 32 elements: the four samples one MFMA step reads (lane / 16)
