@@ -218,3 +218,46 @@ def test_backward_mean_and_outside_edges():
     assert np.allclose(got[0], ref[0], atol=1e-12)
     assert np.allclose(got[1][inside], ref[1], atol=1e-12) and np.count_nonzero(got[1][~inside]) == 0
     assert np.allclose(got[2][inside], ref[2], atol=1e-12) and np.count_nonzero(got[2][~inside]) == 0
+
+
+def test_out_of_range_source_and_validate():
+    """Without VALIDATE an edge whose source index is out of range
+    contributes nothing (forward) and gets zero dW and dsh (backward), like
+    the edge left out; with VALIDATE the forward and backward report
+    unsorted destinations, out-of-range indices and a bad permutation."""
+    import torch
+    sp = _sp()
+    in1, in2, out, n_nodes, deg, n_src = CASES[1]
+    f = ofc.FullyConnectedTP(in1, in2, out)
+    x, sh, w, src, dst = _case_inputs(f, n_nodes, deg, n_src, "f64", 350)
+    bad = src.copy()
+    bad[::7] = n_src + 3                       # every 7th edge reads past the table
+    keep = bad < n_src
+    h = sp.fctp_create(in1, in2, out, dtype="f64")
+    announce("fcconv out-of-range sources")
+    got = _run(sp, h, x, sh, w, bad, dst, n_nodes, "f64")
+    want = f.conv(x, sh[keep], w[keep], src[keep], dst[keep], n_nodes)
+    assert np.allclose(got, want, atol=1e-12)
+    g = np.random.default_rng(351).standard_normal((n_nodes, f.dim_out))
+    gx, gs, gw = _bwd(sp, h, x, sh, w, g, bad, dst, n_nodes, "f64")
+    rx, rs, rw = f.conv_vjp(x, sh[keep], w[keep], src[keep], dst[keep], n_nodes, g)
+    assert np.allclose(gx, rx, atol=1e-12)
+    assert np.allclose(gs[keep], rs, atol=1e-12) and np.count_nonzero(gs[~keep]) == 0
+    assert np.allclose(gw[keep], rw, atol=1e-12) and np.count_nonzero(gw[~keep]) == 0
+    announce("fcconv VALIDATE")
+    hv = sp.fctp_create(in1, in2, out, dtype="f64", validate=True)
+    td = torch.float64
+    X, S, W, G = dev(x, td), dev(sh, td), dev(w, td), dev(g, td)
+    with pytest.raises(sp.SegpolyError) as ei:
+        sp.fctp_conv_fwd(hv, X, S, W, dev(bad), dev(dst), n_nodes)
+    assert ei.value.code == sp.E_RANGE
+    with pytest.raises(sp.SegpolyError) as ei:
+        sp.fctp_conv_fwd(hv, X, S, W, dev(src), dev(dst[::-1].copy()), n_nodes)
+    assert ei.value.code == sp.E_UNSORTED
+    perm = np.argsort(src, kind="stable")
+    with pytest.raises(sp.SegpolyError) as ei:
+        sp.fctp_conv_bwd(hv, X, S, W, G, dev(src), dev(dst), dev(perm[::-1].copy()), n_nodes)
+    assert ei.value.code == sp.E_UNSORTED
+    ok = sp.fctp_conv_bwd(hv, X, S, W, G, dev(src), dev(dst), dev(perm), n_nodes)
+    torch.cuda.synchronize()
+    assert np.allclose(ok[2].cpu().numpy(), f.conv_vjp(x, sh, w, src, dst, n_nodes, g)[2], atol=1e-12)
