@@ -498,6 +498,38 @@ int fctp_conv_bwd(fctp_handle h, const void* x, int64_t n_src, const void* sh, c
 /* fctp_destroy: free the handle (NULL is a no-op). */
 int fctp_destroy(fctp_handle h);
 
+/* ---------------------------------------------------- edge embedding assembly */
+
+/*
+ * edge_scalars_fwd: the edge MLP input of the convolution layer with its
+ * optional per-node scalars ("cuequivariance-torch" skill document, "Other
+ * operations and layers": FullyConnectedTensorProductConv's src_scalars and
+ * dst_scalars go with the edge embedding into the edge MLP):
+ *   out[e] = [edge_emb[e], src_scalars[src[e]], dst_scalars[dst[e]]]
+ *   edge_emb [n_edges, d_emb], src_scalars [n_src, d_src], dst_scalars
+ *   [n_dst, d_dst], out [n_edges, d_emb + d_src + d_dst], device, dtype per
+ *   `dtype`; d_src = 0 or d_dst = 0 leaves that part out (its pointers may
+ *   then be NULL).  src, dst [n_edges] int32/int64.  An index out of range
+ *   gives a zero slice.  out is fully overwritten.
+ */
+int edge_scalars_fwd(int dtype, const void* edge_emb, int64_t d_emb, const void* src_scalars, int64_t d_src,
+                     const void* dst_scalars, int64_t d_dst, const void* src, const void* dst, int idx_dtype,
+                     int64_t n_edges, int64_t n_src, int64_t n_dst, void* out, void* stream);
+
+/*
+ * edge_scalars_bwd: its vector-Jacobian product for grad_out [n_edges,
+ * d_emb + d_src + d_dst]: grad_emb [n_edges, d_emb] (the slice), grad_src
+ * [n_src, d_src] (sum over the edges reading each source, in src_perm order:
+ * a stable argsort of src), grad_dst [n_dst, d_dst] (sum over each
+ * destination's edges: dst sorted ascending, the convolution's
+ * precondition).  Fully overwritten (zero rows for unread sources and
+ * destinations without edges); deterministic.
+ */
+int edge_scalars_bwd(int dtype, const void* grad_out, int64_t d_emb, int64_t d_src, int64_t d_dst, const void* src,
+                     const void* dst, const void* src_perm, int idx_dtype, int64_t n_edges, int64_t n_src,
+                     int64_t n_dst, void* grad_emb, void* grad_src, void* grad_dst, void* stream);
+
+
 /* ------------------------------------------------------- spherical harmonics */
 
 /*

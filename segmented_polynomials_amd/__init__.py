@@ -34,7 +34,7 @@ EXPORTS = ("tp_create", "tp_query", "tp_irreps_out", "tp_path_info", "tp_path_cg
            "tp_conv_fwd", "tp_conv_fwd_vec", "tp_conv_bwd_workspace", "tp_conv_bwd", "tp_destroy", "symcon_create", "symcon_query", "symcon_coupling_info",
            "symcon_coupling_dense", "symcon_fwd", "symcon_bwd_workspace", "symcon_bwd", "symcon_destroy", "linear_create", "linear_query", "linear_fwd",
            "linear_bwd_workspace", "linear_bwd", "linear_destroy", "fctp_create", "fctp_query", "fctp_path_info",
-           "fctp_fwd", "fctp_bwd_workspace", "fctp_bwd", "fctp_conv_fwd", "fctp_conv_bwd_workspace", "fctp_conv_bwd", "fctp_destroy", "sh_fwd", "sh_bwd", "segpoly_real_cg",
+           "fctp_fwd", "fctp_bwd_workspace", "fctp_bwd", "fctp_conv_fwd", "fctp_conv_bwd_workspace", "fctp_conv_bwd", "fctp_destroy", "edge_scalars_fwd", "edge_scalars_bwd", "sh_fwd", "sh_bwd", "segpoly_real_cg",
            "segpoly_last_error", "segpoly_version")
 
 
@@ -106,6 +106,8 @@ def _load():
         "fctp_conv_bwd": [vp, vp, i64, vp, vp, i64, vp, vp, vp, c_int, i64, i64, vp, vp, vp, vp, vp,
                           ctypes.c_size_t, vp],
         "fctp_destroy": [vp],
+        "edge_scalars_fwd": [c_int, vp, i64, vp, i64, vp, i64, vp, vp, c_int, i64, i64, i64, vp, vp],
+        "edge_scalars_bwd": [c_int, vp, i64, i64, i64, vp, vp, vp, c_int, i64, i64, i64, vp, vp, vp, vp],
         "sh_fwd": [c_int, c_int, c_int, vp, i64, vp, vp],
         "sh_bwd": [c_int, c_int, c_int, vp, vp, i64, vp, vp],
         "segpoly_real_cg": [c_int, c_int, c_int, pd],
@@ -702,6 +704,51 @@ def fctp_conv_bwd(h, x, sh, w, grad_out, src, dst, src_perm, n_nodes=None, works
                              _ptr(src_perm), _index_dtype(src), n_edges, n_nodes, _ptr(grad_out), _ptr(gx), _ptr(gs),
                              _ptr(gw), _ptr(workspace), wbytes, _stream_ptr(x.device)))
     return gx, gs, gw
+
+
+# ---------------------------------------------------------------- edge embedding assembly
+
+def _dt_of(t):
+    import torch
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.float64:
+        return F64
+    raise ValueError("float32 or float64 tensors only")
+
+
+def edge_scalars_fwd(edge_emb, src, dst, src_scalars=None, dst_scalars=None, out=None):
+    """[edge_emb[e], src_scalars[src[e]], dst_scalars[dst[e]]] per edge (the
+    convolution layer's edge MLP input)."""
+    import torch
+    n_edges, d_emb = edge_emb.shape
+    d_src = 0 if src_scalars is None else src_scalars.shape[1]
+    d_dst = 0 if dst_scalars is None else dst_scalars.shape[1]
+    n_src = 0 if src_scalars is None else src_scalars.shape[0]
+    n_dst = 0 if dst_scalars is None else dst_scalars.shape[0]
+    for a in (edge_emb, src_scalars, dst_scalars):
+        if a is not None and (a.dtype != edge_emb.dtype or not a.is_cuda or not a.is_contiguous()):
+            raise ValueError("operands must be contiguous device tensors of one dtype")
+    if out is None:
+        out = torch.empty((n_edges, d_emb + d_src + d_dst), dtype=edge_emb.dtype, device=edge_emb.device)
+    _check(lib.edge_scalars_fwd(_dt_of(edge_emb), _ptr(edge_emb), d_emb, _ptr(src_scalars), d_src, _ptr(dst_scalars),
+                                d_dst, _ptr(src), _ptr(dst), _index_dtype(src), n_edges, n_src, n_dst, _ptr(out),
+                                _stream_ptr(edge_emb.device)))
+    return out
+
+
+def edge_scalars_bwd(grad_out, d_emb, d_src, d_dst, src, dst, src_perm, n_src, n_dst):
+    """(grad_emb, grad_src or None, grad_dst or None) of ``edge_scalars_fwd``."""
+    import torch
+    n_edges = grad_out.shape[0]
+    kw = dict(dtype=grad_out.dtype, device=grad_out.device)
+    ge = torch.empty((n_edges, d_emb), **kw)
+    gs = torch.empty((n_src, d_src), **kw) if d_src else None
+    gd = torch.empty((n_dst, d_dst), **kw) if d_dst else None
+    _check(lib.edge_scalars_bwd(_dt_of(grad_out), _ptr(grad_out), d_emb, d_src, d_dst, _ptr(src), _ptr(dst),
+                                _ptr(src_perm), _index_dtype(src), n_edges, n_src, n_dst, _ptr(ge), _ptr(gs), _ptr(gd),
+                                _stream_ptr(grad_out.device)))
+    return ge, gs, gd
 
 
 # ---------------------------------------------------------------- spherical harmonics

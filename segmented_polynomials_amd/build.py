@@ -63,12 +63,12 @@ def build(verbose=False, jobs=None):
 
     # 2. compile
     jobs_list = []
-    for s in HOST_SOURCES + ["capi.cpp", "capi_linear.cpp", "capi_sh.cpp", "capi_fctp.cpp"]:
+    for s in HOST_SOURCES + ["capi.cpp", "capi_linear.cpp", "capi_sh.cpp", "capi_fctp.cpp", "capi_edge.cpp"]:
         jobs_list.append(["g++", *HOST_FLAGS, *inc, "-c", os.path.join(CSRC, s),
                           "-o", os.path.join(obj, s + ".o")])
     jobs_list.append(["g++", *HOST_FLAGS, *inc, "-c", os.path.join(gen, "registry.cpp"),
                       "-o", os.path.join(obj, "registry.cpp.o")])
-    kernels = [os.path.join(CSRC, "kernels", k) for k in ("generic.hip", "linear.hip", "sh.hip", "fctp_f32.hip", "fctp_f64.hip", "fcconv.hip", "fcconv_bwd.hip")]
+    kernels = [os.path.join(CSRC, "kernels", k) for k in ("generic.hip", "linear.hip", "sh.hip", "fctp_f32.hip", "fctp_f64.hip", "fcconv.hip", "fcconv_bwd.hip", "edge_scalars.hip")]
     for h in kernels + gen_hip:
         jobs_list.append([hipcc, *HIP_FLAGS, *inc, "-c", h,
                           "-o", os.path.join(obj, os.path.basename(h) + ".o")])

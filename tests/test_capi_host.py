@@ -351,6 +351,18 @@ def test_merged_descriptor():
     assert sp.lib.tp_create(b"4x0e", b"0e", b"0e", 0, 0, 32, ctypes.byref(raw)) == sp.E_INVALID
 
 
+def test_edge_scalars_argument_errors():
+    p = ctypes.c_void_p(16)
+    f, b = sp.lib.edge_scalars_fwd, sp.lib.edge_scalars_bwd
+    assert f(3, p, 4, p, 2, p, 2, p, p, 0, 5, 3, 3, p, None) == sp.E_INVALID          # dtype
+    assert f(0, p, 4, p, 2, p, 2, p, p, 7, 5, 3, 3, p, None) == sp.E_INVALID          # index dtype
+    assert f(0, p, 4, p, 2, p, 2, p, p, 0, -5, 3, 3, p, None) == sp.E_INVALID         # negative
+    assert f(0, p, 4, None, 2, p, 2, p, p, 0, 5, 3, 3, p, None) == sp.E_INVALID       # src scalars
+    assert f(0, p, 4, None, 0, None, 0, None, None, 0, 0, 0, 0, None, None) == sp.OK  # nothing to do
+    assert b(0, p, 4, 2, 2, p, p, None, 0, 5, 3, 3, p, p, p, None) == sp.E_INVALID    # no src_perm
+    assert b(0, p, 4, 2, 2, p, p, p, 0, 5, 3, 3, p, None, p, None) == sp.E_INVALID    # no grad_src
+
+
 def test_sh_argument_errors():
     p = ctypes.c_void_p(16)
     assert sp.lib.sh_fwd(7, 1, 0, p, 4, p, None) == sp.E_UNSUPPORTED
