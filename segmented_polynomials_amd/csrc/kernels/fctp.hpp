@@ -33,6 +33,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <type_traits>
 
 #include "../fctp_tables.hpp"
 #include "../launch.hpp"
@@ -42,6 +43,9 @@ namespace segpoly {
 namespace kern {
 
 constexpr int kFcThreads = 256;
+// s_waitcnt immediate that waits for every outstanding vector memory load
+// (vmcnt 0) and leaves the export and LDS counters alone (gfx9 encoding).
+constexpr unsigned kWaitVmcnt0 = 0x0F70;
 constexpr int kFcTK = 32;  // K rows per staged weight chunk (8 MFMA steps)
 
 // B rows of TN + 16 elements: the four K rows one MFMA
@@ -182,68 +186,94 @@ __device__ __forceinline__ void fc_term(const FcTerm& Tm, const FcEnt* __restric
     wb[i] = (kk_of(i) < win && c0 + cc_of(i) < m_res) ? Tm.w_off + kk_of(i) * Tm.s_q + (c0 + cc_of(i)) * Tm.s_r
                                                        : int64_t(-1);
   T rb[kBPer];
+  // Branch-free: an element outside the window loads the segment's first
+  // weight (a guarded load would split the chunk loop into branches), and
+  // put() zeroes it; the select sits at put() so that nothing waits for the
+  // prefetch before the steps have run.
   auto fetch = [&](int u, int vc) {
     const int64_t off = u * Tm.s_p + static_cast<int64_t>(vc) * win * Tm.s_q;
 #pragma unroll
-    for (int i = 0; i < kBPer; ++i)
-      rb[i] = (wb[i] >= 0 && vc * win + kk_of(i) < Tm.q_m) ? w[wb[i] + off] : T(0);
+    for (int i = 0; i < kBPer; ++i) {
+      const bool ok = wb[i] >= 0 && vc * win + kk_of(i) < Tm.q_m;
+      rb[i] = w[ok ? wb[i] + off : Tm.w_off];
+    }
   };
-  auto put = [&](int buf) {
+  auto put = [&](int buf, int vc) {
 #pragma unroll
-    for (int i = 0; i < kBPer; ++i) Bs[buf][kk_of(i)][cc_of(i)] = rb[i];
+    for (int i = 0; i < kBPer; ++i) {
+      const bool ok = wb[i] >= 0 && vc * win + kk_of(i) < Tm.q_m;
+      Bs[buf][kk_of(i)][cc_of(i)] = ok ? rb[i] : T(0);
+    }
   };
 
-  auto step = [&](int buf, int s, const T (&y)[2][NT]) {
-    T b[kNT];
+  auto load_b = [&](int buf, int s, T (&b)[kNT]) {
 #pragma unroll
     for (int j = 0; j < kNT; ++j) b[j] = Bs[buf][4 * s + lane / 16][j * 16 + lane % 16];
-    T a[2];
+  };
+  // One MFMA step for the wave's row tiles: RT = 2 (both) or 1 (the second
+  // starts past the tile's rows); chosen once per chunk, so the steps run
+  // as straight-line code.
+  auto step = [&](auto rt_count, int s, const T (&b)[kNT], const T (&y)[2][NT]) {
+    constexpr int RT = decltype(rt_count)::value;
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt) {
+    for (int rt = 0; rt < RT; ++rt) {
       T t = y[rt][0] * qreg[rt][0][s];
 #pragma unroll
       for (int e = 1; e < NT; ++e) t += y[rt][e] * qreg[rt][e][s];
-      a[rt] = t;
-    }
-    if (has0) {
 #pragma unroll
-      for (int j = 0; j < kNT; ++j) acc[0][j] = M::mma(a[0], b[j], acc[0][j]);
+      for (int j = 0; j < kNT; ++j) acc[rt][j] = M::mma(t, b[j], acc[rt][j]);
     }
-    if (has1) {
+  };
+  auto chunk = [&](auto rt_count, int buf, const T (&y)[2][NT]) {
+    if (steps == VS) {
+      // the whole chunk's B values first: one LDS wait per chunk
+      T b[VS][kNT];
 #pragma unroll
-      for (int j = 0; j < kNT; ++j) acc[1][j] = M::mma(a[1], b[j], acc[1][j]);
+      for (int s = 0; s < VS; ++s) load_b(buf, s, b[s]);
+      __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of the steps
+#pragma unroll
+      for (int s = 0; s < VS; ++s) step(rt_count, s, b[s], y);
+    } else {
+      for (int s = 0; s < steps; ++s) {
+        T b[kNT];
+        load_b(buf, s, b);
+        step(rt_count, s, b, y);
+      }
     }
   };
 
+  // Windows outer, P channels inner.  The Q window's loads are waited for
+  // explicitly before the channel loop, so the loop's only outstanding
+  // global loads are the weight prefetch, which the steps never wait for.
   fetch(0, 0);
-  put(0);
-  load_q(0, win);
-  __syncthreads();
-  int u = 0, vc = 0;
-  for (int ch = 0; ch < nch; ++ch) {
-    int un = u + 1, vcn = vc;
-    if (un == Tm.p_m) {
-      un = 0;
-      ++vcn;
-    }
-    if (ch + 1 < nch) fetch(un, vcn);
-    const int buf = ch & 1;
-    T y[2][NT];
-#pragma unroll
-    for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-      for (int e = 0; e < NT; ++e) y[rt][e] = cf[rt][e] * Ps[po[rt][e] + u];
-    if (steps == VS) {
-#pragma unroll
-      for (int s = 0; s < VS; ++s) step(buf, s, y);
-    } else {
-      for (int s = 0; s < steps; ++s) step(buf, s, y);
-    }
-    if (ch + 1 < nch) put(buf ^ 1);
+  put(0, 0);
+  int ch = 0;
+  for (int vc = 0; vc < nvc; ++vc) {
+    load_q(vc, win);
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __syncthreads();
-    if (vcn != vc && ch + 1 < nch) load_q(vcn, win);
-    u = un;
-    vc = vcn;
+    for (int u = 0; u < Tm.p_m; ++u, ++ch) {
+      const bool more = ch + 1 < nch;
+      if (more) {
+        if (u + 1 < Tm.p_m)
+          fetch(u + 1, vc);
+        else
+          fetch(0, vc + 1);
+      }
+      __builtin_amdgcn_sched_barrier(0);  // issue the prefetch before the steps
+      const int buf = ch & 1;
+      T y[2][NT];
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+        for (int e = 0; e < NT; ++e) y[rt][e] = cf[rt][e] * Ps[po[rt][e] + u];
+      if (has1)
+        chunk(std::integral_constant<int, 2>{}, buf, y);
+      else if (has0)
+        chunk(std::integral_constant<int, 1>{}, buf, y);
+      if (more) put(buf ^ 1, u + 1 < Tm.p_m ? vc : vc + 1);
+      __syncthreads();
+    }
   }
 }
 
@@ -279,7 +309,9 @@ fctp_kernel(const T* __restrict__ op0, const T* __restrict__ op1, const T* __res
   const int c0 = tcol * TN;
 
   const int tid = threadIdx.x, lane = tid % 64, wave = tid / 64;
-  const bool has0 = wave * 16 < rows, has1 = (wave + 4) * 16 < rows;  // wave-uniform
+  // wave-uniform (readfirstlane tells the compiler so: scalar branches)
+  const bool has0 = __builtin_amdgcn_readfirstlane(wave * 16 < rows ? 1 : 0) != 0;
+  const bool has1 = __builtin_amdgcn_readfirstlane((wave + 4) * 16 < rows ? 1 : 0) != 0;
   int sl[2], kc[2];
   bool rv[2];
 #pragma unroll
