@@ -111,6 +111,43 @@ def time_launches(torch, fn, steps, warmup):
     return wall, per
 
 
+def pattern_ceiling(torch, wl, h, x, sh, w, src, out, N, E, args):
+    """Time the traffic replay of the conv on the large graph (same loads and
+    stores as the fused kernel, trivial arithmetic): weight rows alone, with
+    the output rows (plain and non-temporal stores), and the full traffic
+    with the gathered source rows and harmonics.  None when the probe
+    library is missing or the graph is not the uniform-degree one."""
+    import ctypes
+    path = os.path.join(ROOT, "segmented_polynomials_amd", "libsegpoly_bench.so")
+    if not os.path.exists(path) or E != N * wl.degree:
+        note("pattern ceiling skipped (probe library missing or non-uniform degree)")
+        return None
+    lib = ctypes.CDLL(path)
+    fn = lib.segpoly_bench_traffic_replay
+    fn.restype = ctypes.c_int
+    fn.argtypes = [ctypes.c_int, ctypes.c_int] + [ctypes.c_void_p] * 5 + [ctypes.c_int64, ctypes.c_int64,
+                                                                          ctypes.c_int] + [ctypes.c_int64] * 4 + [
+        ctypes.c_void_p]
+
+    def run(mode, nt):
+        stream = torch.cuda.current_stream().cuda_stream
+        rc = fn(mode, nt, w.data_ptr(), x.data_ptr(), sh.data_ptr(), src.data_ptr(), out.data_ptr(), N,
+                x.shape[0], wl.degree, h.weight_numel, h.dim_in1, h.dim_in2, h.dim_out, stream)
+        if rc != 0:
+            raise RuntimeError(f"traffic replay failed ({rc})")
+
+    res = {"what": "the conv's loads and stores with trivial arithmetic, one wave per destination node"}
+    steps = max(5, args.steps // 2)
+    for key, mode, nt in (("weights_ms", 0, 0), ("weights_out_ms", 1, 0), ("weights_out_nt_ms", 1, 1),
+                          ("full_ms", 2, 0), ("full_nt_ms", 2, 1)):
+        _, per = time_launches(torch, lambda: run(mode, nt), steps, 2)
+        res[key] = sum(per) / len(per)
+    bytes_w = E * h.weight_numel * 4
+    res["weights_GBps"] = bytes_w / (res["weights_ms"] * 1e-3) / 1e9
+    note("pattern ceiling timed")
+    return res
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -226,6 +263,13 @@ def main():
                                   "GBps": copy_gbps, "frac_of_peak": copy_gbps / HBM_PEAK_GBPS}
         result["roofline"]["frac_of_copy"] = achieved_gbps / copy_gbps
         del wc
+
+        # ceiling of the access pattern itself: the kernel's loads and stores
+        # replayed with trivial arithmetic (libsegpoly_bench.so)
+        rep = pattern_ceiling(torch, wl, h, x, sh, w, src, out, N, E, args)
+        if rep is not None:
+            result["pattern_ceiling"] = rep
+            result["roofline"]["frac_of_pattern_ceiling"] = rep["full_ms"] / avg_kernel_ms
 
     if not args.no_extras or args.with_backward:
         del out

@@ -23,6 +23,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libsegpoly.so")
+BENCH_LIB = os.path.join(PKG, "libsegpoly_bench.so")
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 
 HOST_SOURCES = ["irreps.cpp", "cg.cpp", "tp_descriptor.cpp", "symcon_descriptor.cpp"]
@@ -81,6 +82,16 @@ def build(verbose=False, jobs=None):
     _run([hipcc, "-shared", "-fPIC", "--offload-arch=gfx950", *objs, "-o", tmp,
           f"-L{ROCM}/lib", "-lamdhip64"], verbose)
     os.replace(tmp, LIB)
+
+    # 4. the benchmark's traffic-replay probe: a library of its own, loaded
+    # only by bench.py (the method's library does not contain it)
+    probe_obj = os.path.join(BUILD, "traffic_replay.o")
+    _run([hipcc, *HIP_FLAGS, *inc, "-c", os.path.join(CSRC, "bench", "traffic_replay.hip"), "-o", probe_obj],
+         verbose)
+    tmp = BENCH_LIB + ".tmp"
+    _run([hipcc, "-shared", "-fPIC", "--offload-arch=gfx950", probe_obj, "-o", tmp, f"-L{ROCM}/lib",
+          "-lamdhip64"], verbose)
+    os.replace(tmp, BENCH_LIB)
     return LIB
 
 
