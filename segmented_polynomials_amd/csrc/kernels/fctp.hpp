@@ -57,16 +57,20 @@ struct FcB {
 
 // Stage `ns` samples (rows s0 ..) of one operand block into LDS as
 // [sample (fc_sample_stride)][component][channel + kFcPad]; samples at or
-// past n read as zero.
-template <typename T, int LAYOUT>
+// past n read as zero.  Row s0 must be < n.  Each thread issues its loads
+// in batches of BATCH before writing any of them (a load followed by its
+// own select and LDS write keeps one load in flight), with out-of-range
+// rows reading row s0 and zeroed at the write.  The product kernel stages
+// with batches of 8; the weight-gradient kernel, which relies on many
+// small workgroups per CU to hide its staging, with 1 (more registers
+// would cost it workgroups).
+template <typename T, int LAYOUT, int BATCH>
 __device__ __forceinline__ void fc_stage(const T* __restrict__ src, int64_t sdim, int64_t boff, int bd, int bm,
                                          int64_t s0, int ns, int64_t n, T* dst, int tid) {
   const int blk = bd * bm;
   const int cstride = bm + kFcPad, sstride = fc_sample_stride(bd, bm);
-  if (blk <= kFcThreads) {
-    const int spp = kFcThreads / blk;  // samples per pass
-    const int sp = tid / blk, rem = tid - sp * blk;
-    if (sp >= spp) return;
+  // samples s0 + s for s = sfirst, sfirst + sstep, ... < ns of element rem
+  auto column = [&](int rem, int sfirst, int sstep) {
     int a, u;
     if (LAYOUT == kIrMul) {
       a = rem / bm;
@@ -76,26 +80,27 @@ __device__ __forceinline__ void fc_stage(const T* __restrict__ src, int64_t sdim
       a = rem - u * bd;
     }
     const int li = a * cstride + u;
-    for (int s = sp; s < ns; s += spp) {
-      const int64_t row = s0 + s;
-      dst[s * sstride + li] = row < n ? src[row * sdim + boff + rem] : T(0);
+    const T* col = src + boff + rem;
+    for (int s = sfirst; s < ns; s += sstep * BATCH) {
+      T v[BATCH];
+#pragma unroll
+      for (int k = 0; k < BATCH; ++k) {
+        const int64_t row = s0 + s + k * sstep;
+        v[k] = col[(row < n ? row : s0) * sdim];
+      }
+#pragma unroll
+      for (int k = 0; k < BATCH; ++k) {
+        const int sk = s + k * sstep;
+        if (sk < ns) dst[sk * sstride + li] = s0 + sk < n ? v[k] : T(0);
+      }
     }
+  };
+  if (blk <= kFcThreads) {
+    const int spp = kFcThreads / blk;  // samples per pass
+    const int sp = tid / blk;
+    if (sp < spp) column(tid - sp * blk, sp, spp);
   } else {
-    for (int rem = tid; rem < blk; rem += kFcThreads) {
-      int a, u;
-      if (LAYOUT == kIrMul) {
-        a = rem / bm;
-        u = rem - a * bm;
-      } else {
-        u = rem / bd;
-        a = rem - u * bd;
-      }
-      const int li = a * cstride + u;
-      for (int s = 0; s < ns; ++s) {
-        const int64_t row = s0 + s;
-        dst[s * sstride + li] = row < n ? src[row * sdim + boff + rem] : T(0);
-      }
-    }
+    for (int rem = tid; rem < blk; rem += kFcThreads) column(rem, 0, 1);
   }
 }
 
@@ -128,37 +133,49 @@ __device__ __forceinline__ void fc_term(const FcTerm& Tm, const FcEnt* __restric
 
   // entries of this lane's rows: P offset in LDS (without the channel) and
   // coefficient (zero for padding and rows past the tile)
+  // (all entries read before any is used, and padding entries read the
+  // row's first entry and are zeroed, so the reads are not serialised)
   int po[2][NT];
+  int64_t qo[2][NT];  // Q offset of the entry's component, without the channel
   T cf[2][NT];
+  FcEnt E[2][NT];
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+    for (int e = 0; e < NT; ++e) E[rt][e] = ents[Tm.ent + kc[rt] * Tm.T + (e < Tm.T ? e : 0)];
 #pragma unroll
   for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
     for (int e = 0; e < NT; ++e) {
-      po[rt][e] = 0;
-      cf[rt][e] = T(0);
-      if (e < Tm.T) {
-        const FcEnt E = ents[Tm.ent + kc[rt] * Tm.T + e];
-        po[rt][e] = sl[rt] * pss + E.pa * pcs;
-        cf[rt][e] = rv[rt] ? static_cast<T>(E.c) : T(0);
-      }
+      const bool on = e < Tm.T;
+      po[rt][e] = on ? sl[rt] * pss + E[rt][e].pa * pcs : 0;
+      cf[rt][e] = on && rv[rt] ? static_cast<T>(E[rt][e].c) : T(0);
+      const int qb = on ? E[rt][e].qb : 0;
+      qo[rt][e] = sl[rt] * qdim + Tm.q_off + (LAYOUT == kIrMul ? qb * Tm.q_m : qb);
     }
 
-  // the Q window (re-reading the entries' Q components: this runs once per
-  // window, not per chunk)
+  // the Q window: every load issued before any is zeroed (channels past q_m
+  // read channel 0)
   T qreg[2][NT][VS];
   auto load_q = [&](int vc, int win) {
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-      for (int e = 0; e < NT; ++e) {
-        const int qb = e < Tm.T ? ents[Tm.ent + kc[rt] * Tm.T + e].qb : 0;
-        const T* qp = Qt + sl[rt] * qdim + Tm.q_off + (LAYOUT == kIrMul ? qb * Tm.q_m : qb);
+      for (int e = 0; e < NT; ++e)
 #pragma unroll
         for (int s = 0; s < VS; ++s) {
           const int v = vc * win + 4 * s + lane / 16;
-          qreg[rt][e][s] = (4 * s < win && v < Tm.q_m) ? qp[v * qvs] : T(0);
+          qreg[rt][e][s] = Qt[qo[rt][e] + static_cast<int64_t>(4 * s < win && v < Tm.q_m ? v : 0) * qvs];
         }
-      }
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+      for (int e = 0; e < NT; ++e)
+#pragma unroll
+        for (int s = 0; s < VS; ++s) {
+          const int v = vc * win + 4 * s + lane / 16;
+          if (!(4 * s < win && v < Tm.q_m)) qreg[rt][e][s] = T(0);
+        }
   };
 
   // window of the Q channels: VK, or q_m rounded up to 4 if smaller
@@ -336,7 +353,7 @@ fctp_kernel(const T* __restrict__ op0, const T* __restrict__ op1, const T* __res
     const int64_t pdim = Tm.p_op == 0 ? dim0 : (Tm.p_op == 1 ? dim1 : dim2);
     const int64_t qdim = Tm.q_op == 0 ? dim0 : (Tm.q_op == 1 ? dim1 : dim2);
     __syncthreads();  // the previous term's LDS reads are done
-    fc_stage<T, LAYOUT>(P, pdim, Tm.p_off, Tm.p_d, Tm.p_m, s0, ts, n, Ps, tid);
+    fc_stage<T, LAYOUT, 8>(P, pdim, Tm.p_off, Tm.p_d, Tm.p_m, s0, ts, n, Ps, tid);
     // (fc_term's first barrier publishes the staged block)
     fc_term<T, LAYOUT, TN, NT>(Tm, ents, w, Ps, Q + s0 * qdim, qdim, Bs, R.m, c0, sl, kc, rv, has0, has1, tid,
                                lane, acc);
@@ -476,9 +493,9 @@ fctp_dw_kernel(const T* __restrict__ x1, const T* __restrict__ x2, const T* __re
     const int ns = static_cast<int>(n_end - sb < P.ts ? n_end - sb : P.ts);
     const int nsp = (ns + 3) & ~3;  // staged samples (zero rows up to a multiple of 4)
     __syncthreads();
-    fc_stage<T, LAYOUT>(Pg, pdim, P.p_off, P.p_d, P.p_m, sb, nsp, n_end, Ps, tid);
-    fc_stage<T, LAYOUT>(Qg, qdim, P.q_off, P.q_d, P.q_m, sb, nsp, n_end, Qs, tid);
-    fc_stage<T, LAYOUT>(g, dimo, P.g_off, P.g_d, P.g_m, sb, nsp, n_end, Gs, tid);
+    fc_stage<T, LAYOUT, 1>(Pg, pdim, P.p_off, P.p_d, P.p_m, sb, nsp, n_end, Ps, tid);
+    fc_stage<T, LAYOUT, 1>(Qg, qdim, P.q_off, P.q_d, P.q_m, sb, nsp, n_end, Qs, tid);
+    fc_stage<T, LAYOUT, 1>(g, dimo, P.g_off, P.g_d, P.g_m, sb, nsp, n_end, Gs, tid);
     __syncthreads();
     if (!wave_any) continue;
     for (int k = 0; k < P.g_d; ++k) {
