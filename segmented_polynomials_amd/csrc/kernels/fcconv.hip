@@ -56,22 +56,32 @@ __device__ __forceinline__ void fcv_run(const T* __restrict__ x, const T* __rest
   constexpr int kB = sizeof(T) == 4 ? kFcvBatch : kFcvBatch / 2;  // chunks held in registers
   const bool wlane = c < tile.nw;
   auto source = [&](int64_t e) -> int64_t { return e < e1 ? static_cast<int64_t>(src[e]) : int64_t(-1); };
+  // A batch of weight chunks b0 .. b0 + kB - 1, branch-free: every load is
+  // issued before any is used (a guarded load per element made each chunk
+  // wait for the previous one).  A chunk past the tile's last re-reads its
+  // last chunk and is never used; a lane past the tile's channels reads
+  // channel 0; a slot past the edge range reads the range's first edge.
+  // Lanes whose edge has no valid source skip the mixing (their weights
+  // are not used at all).
+  T wr[kB][kFcvChunkU];
+  auto fetch_w = [&](int b0, const T* wl) {
+    int64_t off[kB];
+#pragma unroll
+    for (int i = 0; i < kB; ++i) off[i] = tc[b0 + i < tile.n_chunks ? b0 + i : tile.n_chunks - 1].off;
+#pragma unroll
+    for (int i = 0; i < kB; ++i)
+#pragma unroll
+      for (int uu = 0; uu < kFcvChunkU; ++uu) wr[i][uu] = wl[off[i] + uu * tile.m];
+  };
   int64_t s_next = source(e0 + slot);
   for (int64_t eb = e0; eb < e1; eb += S) {
     const int64_t e = eb + slot;
     const int64_t s = s_next;
     const bool ok = s >= 0 && s < n_src;
     const bool wok = ok && wlane;
-    const T* wrow = w + e * w_stride + tile.w0 + c;
+    const T* wl = w + (e < e1 ? e : e0) * w_stride + tile.w0 + (wlane ? c : 0);
     // the first batch of weight chunks, issued before anything waits on memory
-    T wr[kB][kFcvChunkU];
-#pragma unroll
-    for (int i = 0; i < kB; ++i)
-      if (i < tile.n_chunks) {
-        const int64_t off = tc[i].off;
-#pragma unroll
-        for (int uu = 0; uu < kFcvChunkU; ++uu) wr[i][uu] = wok ? wrow[off + uu * tile.m] : T(0);
-      }
+    if (tile.n_chunks > 0) fetch_w(0, wl);
     s_next = source(eb + S + slot);
     // stage the slot's edge: x[src] (all input-1 blocks) and the harmonics
     for (int bi = 0; bi < n_blocks; ++bi) {
@@ -97,32 +107,28 @@ __device__ __forceinline__ void fcv_run(const T* __restrict__ x, const T* __rest
     wave_sync();
     // mixing, lane = output channel: acc[k] += W[u, w] y[qk + k, u]
     for (int b0 = 0; b0 < tile.n_chunks; b0 += kB) {
-      if (b0 > 0) {
+      if (b0 > 0) fetch_w(b0, wl);
+      if (wok) {
 #pragma unroll
         for (int i = 0; i < kB; ++i)
           if (b0 + i < tile.n_chunks) {
-            const int64_t off = tc[b0 + i].off;
+            const FcvChunk C = tc[b0 + i];
+            const T* yq = ys + C.qk * M + C.u0;
 #pragma unroll
-            for (int uu = 0; uu < kFcvChunkU; ++uu) wr[i][uu] = wok ? wrow[off + uu * tile.m] : T(0);
+            for (int uu = 0; uu < kFcvChunkU; ++uu)
+#pragma unroll
+              for (int k = 0; k < D; ++k) acc[k] = fmadd(wr[i][uu], yq[k * M + uu], acc[k]);
           }
       }
-#pragma unroll
-      for (int i = 0; i < kB; ++i)
-        if (b0 + i < tile.n_chunks) {
-          const FcvChunk C = tc[b0 + i];
-          const T* yq = ys + C.qk * M + C.u0;
-#pragma unroll
-          for (int uu = 0; uu < kFcvChunkU; ++uu)
-#pragma unroll
-            for (int k = 0; k < D; ++k) acc[k] = fmadd(wr[i][uu], yq[k * M + uu], acc[k]);
-        }
     }
     for (int q = 0; q < tile.nq; ++q) {  // channels past the last full chunk
       const FcvQ Q = tq[q];
-      const T wv = wok ? wrow[Q.off] : T(0);
+      const T wv = wl[Q.off];
       const T* yq = ys + Q.qk * M + Q.u;
+      if (wok) {
 #pragma unroll
-      for (int k = 0; k < D; ++k) acc[k] = fmadd(wv, yq[k * M], acc[k]);
+        for (int k = 0; k < D; ++k) acc[k] = fmadd(wv, yq[k * M], acc[k]);
+      }
     }
     wave_sync();
   }
@@ -147,11 +153,12 @@ __device__ __forceinline__ void fcv_store(T (&acc)[D], const FcvTile& tile, T* _
   }
 }
 
-// The float mul_ir kernel is held to four waves per SIMD (its register
-// allocation otherwise allows three; measured 0.86 -> 0.79 ms on the
-// 600k-edge graph); the others keep the compiler's choice.
+// The float kernels are held to four waves per SIMD (their register
+// allocation otherwise allows three; a few registers spill, and on the
+// 600k-edge graph the four waves still win: 0.79 -> 0.76 ms mul_ir,
+// 0.76 -> 0.72 ms ir_mul); double keeps the compiler's choice.
 template <typename T, typename Index, int LAYOUT>
-__global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(sizeof(T) == 4 && LAYOUT == kMulIr ? 4 : 1)))
+__global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(sizeof(T) == 4 ? 4 : 1)))
 fcconv_kernel(const T* __restrict__ x, const T* __restrict__ sh, const T* __restrict__ w,
               const Index* __restrict__ src, const Index* __restrict__ dst, int64_t n_src, int64_t n_edges,
               int64_t dim1, int64_t dim2, int64_t dimo, int64_t w_stride, int mean, T* __restrict__ out,
