@@ -372,3 +372,26 @@ def test_sh_argument_errors():
     assert sp.lib.sh_fwd(3, 1, 0, None, 4, p, None) == sp.E_INVALID
     assert sp.lib.sh_bwd(3, 1, 0, p, None, 4, p, None) == sp.E_INVALID
     assert sp.lib.sh_fwd(3, 1, 0, None, 0, None, None) == sp.OK
+
+
+def test_bench_traffic_replay_rejects_other_shapes_before_any_gpu_call():
+    """The benchmark's traffic-replay probe (its own library, loaded only by
+    bench.py) replays the large graph's shape alone; anything else, and
+    missing buffers, are refused before a launch."""
+    path = os.path.join(os.path.dirname(sp.__file__), "libsegpoly_bench.so")
+    if not os.path.exists(path):
+        pytest.skip("probe library not built")
+    lib = ctypes.CDLL(path)
+    fn = lib.segpoly_bench_traffic_replay
+    fn.restype = ctypes.c_int
+    fn.argtypes = [ctypes.c_int, ctypes.c_int] + [ctypes.c_void_p] * 5 + [ctypes.c_int64, ctypes.c_int64,
+                                                                          ctypes.c_int] + [ctypes.c_int64] * 4 + [
+        ctypes.c_void_p]
+    p = ctypes.c_void_p(16)
+    shape = (1664, 1152, 16, 5504)
+    assert fn(0, 0, p, p, p, p, p, 10, 10, 30, 1663, 1152, 16, 5504, None) == -1   # weights per edge
+    assert fn(0, 0, p, p, p, p, p, 10, 10, 30, 1664, 1152, 9, 5504, None) == -1    # harmonics
+    assert fn(2, 0, p, None, p, p, p, 10, 10, 30, *shape, None) == -1              # gather without x
+    assert fn(0, 0, p, p, p, p, p, 0, 10, 30, *shape, None) == -1                  # no nodes
+    assert fn(0, 0, p, p, p, p, p, 10, 10, 0, *shape, None) == -1                  # no edges per node
+    assert fn(7, 0, p, p, p, p, p, 10, 10, 30, *shape, None) == -1                 # mode
