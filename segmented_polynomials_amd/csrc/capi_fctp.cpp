@@ -27,6 +27,8 @@ using namespace segpoly;
 namespace {
 
 constexpr size_t kLdsLimit = 52 * 1024;  // per workgroup (three workgroups fit a CU's 160 KB)
+// The float 32-column product kernels run four workgroups per CU.
+size_t product_lds_limit(int dtype, int tn) { return dtype == SEGPOLY_F32 && tn == 32 ? 40 * 1024 : kLdsLimit; }
 constexpr int kMaxL = 6;
 
 // A term without a parity letter is an SO(3) irrep (parity 0: the parity
@@ -175,7 +177,7 @@ int build_pass(segpoly_fctp* h, int which) {
   int mmax = 1;
   for (const auto& b : rb) mmax = std::max(mmax, b.mul);
   P.tn = tn_for(mmax);
-  const size_t budget = kLdsLimit - static_b_bytes(P.tn, h->dtype);
+  const size_t budget = product_lds_limit(h->dtype, P.tn) - static_b_bytes(P.tn, h->dtype);
   for (size_t r = 0; r < rb.size(); ++r) {
     FcRes R{};
     R.off = roff[r];
