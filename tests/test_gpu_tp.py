@@ -100,6 +100,35 @@ def test_ragged_graph_and_ragged_channel_tiles(mul, layout):
     assert np.count_nonzero(got[iso]) == 0
 
 
+@pytest.mark.parametrize("mul", [32, 16, 12, 5])
+@pytest.mark.parametrize("layout", ["mul_ir", "ir_mul"])
+def test_small_multiplicities(mul, layout):
+    """Multiplicities of at most 32 (most lanes of the wave idle): ragged
+    in-degrees 0..40 with isolated destinations, channel counts that are not
+    powers of two (12 and 5), int64 indices for one case, and bitwise
+    repeatable results."""
+    sp = _sp()
+    import torch
+    wl = workloads.WORKLOADS[2]
+    in1 = f"{mul}x0e+{mul}x1o"
+    o = otp.ChannelwiseTP(in1, wl.irreps_in2, wl.irreps_out)
+    h = sp.tp_create(in1, wl.irreps_in2, wl.irreps_out, layout=layout)
+    assert h.specialized
+    wl4 = workloads.WORKLOADS[4]
+    wl2 = workloads.TPWorkload(**{**wl4.__dict__, "irreps_in1": in1, "irreps_in2": wl.irreps_in2,
+                                  "irreps_out": wl.irreps_out, "sh_ls": wl.sh_ls})
+    inp = workloads.tp_inputs(wl2, o.weight_fan_in(), n_nodes=157, degree=40, graph="ragged", seed=300 + mul)
+    announce(f"tp small multiplicity mul={mul} {layout}")
+    it = torch.int64 if mul == 12 else torch.int32
+    got = _run(sp, h, inp, idx_dtype=it)
+    again = _run(sp, h, inp, idx_dtype=it)
+    assert np.array_equal(got, again)
+    ref, scale = _oracle(o, inp, layout)
+    check_scaled(got, ref, scale, "f32", f"small multiplicity mul={mul} {layout}")
+    iso = np.bincount(inp["dst"], minlength=157) == 0
+    assert iso.any() and np.count_nonzero(got[iso]) == 0
+
+
 @pytest.mark.parametrize("case", [
     ("3x0e+5x1o+2x2e+4x3o", "0e+1o+2e", "0e+1o+1e+2e+3o+3e", "mul_ir"),   # non-uniform muls
     ("64x0e+64x1o+64x2e", "0e+1o+2e+3o", "0e+0o+1e+1o+2e+2o", "ir_mul"),   # registered, forced generic
