@@ -25,7 +25,8 @@ constexpr int fc_t_class(int t) { return t <= 1 ? 1 : t <= 2 ? 2 : t <= 3 ? 3 : 
 
 constexpr int kFcMaxT = 8;       // coupling entries per (term, result component)
 constexpr int kFcMaxRes = 32;    // result blocks per pass
-constexpr int kFcRowsMax = 128;  // rows (sample, component) per tile
+constexpr int kFcRT = 2;         // 16-row MFMA tiles per wave (4 waves per workgroup)
+constexpr int kFcRowsMax = 64 * kFcRT;  // rows (sample, component) per tile
 constexpr int kFcPad = 1;        // LDS padding of each staged channel row
 constexpr int kFcDwChunk = 1024; // samples per weight-gradient partial sum
 constexpr int kFcDwSamples = 16; // samples a weight-gradient workgroup stages at a time (few: several

@@ -117,9 +117,9 @@ __device__ __forceinline__ void fc_stage(const T* __restrict__ src, int64_t sdim
 template <typename T, int LAYOUT, int TN, int NT>
 __device__ __forceinline__ void fc_term(const FcTerm& Tm, const FcEnt* __restrict__ ents, const T* __restrict__ w,
                                         const T* Ps, const T* __restrict__ Qt, int64_t qdim,
-                                        T (*Bs)[kFcTK][FcB<TN>::stride], int m_res, int c0, const int (&sl)[2],
-                                        const int (&kc)[2], const bool (&rv)[2], bool has0, bool has1, int tid,
-                                        int lane, typename Mfma<T>::acc_t (&acc)[2][TN / 16]) {
+                                        T (*Bs)[kFcTK][FcB<TN>::stride], int m_res, int c0, const int (&sl)[kFcRT],
+                                        const int (&kc)[kFcRT], const bool (&rv)[kFcRT], int nrt, int tid,
+                                        int lane, typename Mfma<T>::acc_t (&acc)[kFcRT][TN / 16]) {
   using M = Mfma<T>;
   constexpr int kNT = TN / 16;
   constexpr int VS = NT <= 4 ? 8 : 4;       // MFMA steps per chunk
@@ -135,16 +135,16 @@ __device__ __forceinline__ void fc_term(const FcTerm& Tm, const FcEnt* __restric
   // coefficient (zero for padding and rows past the tile)
   // (all entries read before any is used, and padding entries read the
   // row's first entry and are zeroed, so the reads are not serialised)
-  int po[2][NT];
-  int64_t qo[2][NT];  // Q offset of the entry's component, without the channel
-  T cf[2][NT];
-  FcEnt E[2][NT];
+  int po[kFcRT][NT];
+  int64_t qo[kFcRT][NT];  // Q offset of the entry's component, without the channel
+  T cf[kFcRT][NT];
+  FcEnt E[kFcRT][NT];
 #pragma unroll
-  for (int rt = 0; rt < 2; ++rt)
+  for (int rt = 0; rt < kFcRT; ++rt)
 #pragma unroll
     for (int e = 0; e < NT; ++e) E[rt][e] = ents[Tm.ent + kc[rt] * Tm.T + (e < Tm.T ? e : 0)];
 #pragma unroll
-  for (int rt = 0; rt < 2; ++rt)
+  for (int rt = 0; rt < kFcRT; ++rt)
 #pragma unroll
     for (int e = 0; e < NT; ++e) {
       const bool on = e < Tm.T;
@@ -156,10 +156,10 @@ __device__ __forceinline__ void fc_term(const FcTerm& Tm, const FcEnt* __restric
 
   // the Q window: every load issued before any is zeroed (channels past q_m
   // read channel 0)
-  T qreg[2][NT][VS];
+  T qreg[kFcRT][NT][VS];
   auto load_q = [&](int vc, int win) {
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt)
+    for (int rt = 0; rt < kFcRT; ++rt)
 #pragma unroll
       for (int e = 0; e < NT; ++e)
 #pragma unroll
@@ -168,7 +168,7 @@ __device__ __forceinline__ void fc_term(const FcTerm& Tm, const FcEnt* __restric
           qreg[rt][e][s] = Qt[qo[rt][e] + static_cast<int64_t>(4 * s < win && v < Tm.q_m ? v : 0) * qvs];
         }
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt)
+    for (int rt = 0; rt < kFcRT; ++rt)
 #pragma unroll
       for (int e = 0; e < NT; ++e)
 #pragma unroll
@@ -230,7 +230,7 @@ __device__ __forceinline__ void fc_term(const FcTerm& Tm, const FcEnt* __restric
   // One MFMA step for the wave's row tiles: RT = 2 (both) or 1 (the second
   // starts past the tile's rows); chosen once per chunk, so the steps run
   // as straight-line code.
-  auto step = [&](auto rt_count, int s, const T (&b)[kNT], const T (&y)[2][NT]) {
+  auto step = [&](auto rt_count, int s, const T (&b)[kNT], const T (&y)[kFcRT][NT]) {
     constexpr int RT = decltype(rt_count)::value;
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
@@ -241,7 +241,7 @@ __device__ __forceinline__ void fc_term(const FcTerm& Tm, const FcEnt* __restric
       for (int j = 0; j < kNT; ++j) acc[rt][j] = M::mma(t, b[j], acc[rt][j]);
     }
   };
-  auto chunk = [&](auto rt_count, int buf, const T (&y)[2][NT]) {
+  auto chunk = [&](auto rt_count, int buf, const T (&y)[kFcRT][NT]) {
     if (steps == VS) {
       // the whole chunk's B values first: one LDS wait per chunk
       T b[VS][kNT];
@@ -279,14 +279,14 @@ __device__ __forceinline__ void fc_term(const FcTerm& Tm, const FcEnt* __restric
       }
       __builtin_amdgcn_sched_barrier(0);  // issue the prefetch before the steps
       const int buf = ch & 1;
-      T y[2][NT];
+      T y[kFcRT][NT];
 #pragma unroll
-      for (int rt = 0; rt < 2; ++rt)
+      for (int rt = 0; rt < kFcRT; ++rt)
 #pragma unroll
         for (int e = 0; e < NT; ++e) y[rt][e] = cf[rt][e] * Ps[po[rt][e] + u];
-      if (has1)
-        chunk(std::integral_constant<int, 2>{}, buf, y);
-      else if (has0)
+      if (kFcRT == 2 && nrt == 2)
+        chunk(std::integral_constant<int, kFcRT>{}, buf, y);
+      else if (nrt >= 1)
         chunk(std::integral_constant<int, 1>{}, buf, y);
       if (more) put(buf ^ 1, u + 1 < Tm.p_m ? vc : vc + 1);
       __syncthreads();
@@ -328,22 +328,25 @@ fctp_kernel(const T* __restrict__ op0, const T* __restrict__ op1, const T* __res
   const int c0 = tcol * TN;
 
   const int tid = threadIdx.x, lane = tid % 64, wave = tid / 64;
-  // wave-uniform (readfirstlane tells the compiler so: scalar branches)
-  const bool has0 = __builtin_amdgcn_readfirstlane(wave * 16 < rows ? 1 : 0) != 0;
-  const bool has1 = __builtin_amdgcn_readfirstlane((wave + 4) * 16 < rows ? 1 : 0) != 0;
-  int sl[2], kc[2];
-  bool rv[2];
+  // row tiles of this wave that hold rows (wave-uniform; readfirstlane
+  // tells the compiler so: scalar branches)
+  int nrt = 0;
 #pragma unroll
-  for (int rt = 0; rt < 2; ++rt) {
+  for (int rt = 0; rt < kFcRT; ++rt) nrt += (wave + 4 * rt) * 16 < rows ? 1 : 0;
+  nrt = __builtin_amdgcn_readfirstlane(nrt);
+  int sl[kFcRT], kc[kFcRT];
+  bool rv[kFcRT];
+#pragma unroll
+  for (int rt = 0; rt < kFcRT; ++rt) {
     const int row = (wave + 4 * rt) * 16 + lane % 16;
     rv[rt] = row < rows;
     sl[rt] = rv[rt] ? row / d : 0;
     kc[rt] = rv[rt] ? row - sl[rt] * d : 0;
   }
 
-  typename M::acc_t acc[2][kNT];
+  typename M::acc_t acc[kFcRT][kNT];
 #pragma unroll
-  for (int rt = 0; rt < 2; ++rt)
+  for (int rt = 0; rt < kFcRT; ++rt)
 #pragma unroll
     for (int j = 0; j < kNT; ++j) acc[rt][j] = typename M::acc_t{0, 0, 0, 0};
 
@@ -357,14 +360,14 @@ fctp_kernel(const T* __restrict__ op0, const T* __restrict__ op1, const T* __res
     __syncthreads();  // the previous term's LDS reads are done
     fc_stage<T, LAYOUT, 8>(P, pdim, Tm.p_off, Tm.p_d, Tm.p_m, s0, ts, n, Ps, tid);
     // (fc_term's first barrier publishes the staged block)
-    fc_term<T, LAYOUT, TN, NT>(Tm, ents, w, Ps, Q + s0 * qdim, qdim, Bs, R.m, c0, sl, kc, rv, has0, has1, tid,
+    fc_term<T, LAYOUT, TN, NT>(Tm, ents, w, Ps, Q + s0 * qdim, qdim, Bs, R.m, c0, sl, kc, rv, nrt, tid,
                                lane, acc);
   }
 
   // epilogue: rows (sample, component), columns c0 + ..
 #pragma unroll
-  for (int rt = 0; rt < 2; ++rt) {
-    if (!(rt == 0 ? has0 : has1)) continue;
+  for (int rt = 0; rt < kFcRT; ++rt) {
+    if (rt >= nrt) continue;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int row = (wave + 4 * rt) * 16 + M::row(lane, q);
