@@ -74,6 +74,7 @@ struct FcPass {
   std::vector<FcTerm> terms;
   int tn = 32;
   int nt = 1;                        // entry class of the launch
+  bool lds_direct = false;           // every term suits LDS-direct weight chunks (weight alignment aside)
   size_t lds = 0;
   int64_t dim_res = 0;
   size_t res_off = 0, term_off = 0;  // within the device blob
@@ -235,6 +236,15 @@ int build_pass(segpoly_fctp* h, int which) {
     P.lds = std::max(P.lds, static_cast<size_t>(R.ts) * per_sample);
     P.res.push_back(R);
   }
+  // LDS-direct weight chunks: float, 32-column tiles, result blocks of whole
+  // column tiles, and every term with the result channel the contiguous
+  // weight index, whole 32-channel windows of Q, rows of a multiple of four
+  // elements, at most four couplings per component (32-row chunks)
+  P.lds_direct = h->dtype == SEGPOLY_F32 && P.tn == 32 && P.nt <= 4 && !P.terms.empty();
+  for (const auto& R : P.res)
+    if (R.m % 32) P.lds_direct = false;
+  for (const auto& t : P.terms)
+    if (t.s_r != 1 || t.q_m % 32 || t.w_off % 4 || t.s_q % 4 || t.s_p % 4) P.lds_direct = false;
   return SEGPOLY_OK;
 }
 
@@ -430,6 +440,7 @@ int run_pass(segpoly_fctp* h, const unsigned char* db, int which, const void* x1
   a.ents = reinterpret_cast<const FcEnt*>(db + h->ent_off);
   a.tn = P.tn;
   a.nt = P.nt;
+  a.lds_direct = P.lds_direct && reinterpret_cast<uintptr_t>(w) % 16 == 0;
   a.lds_bytes = P.lds;
   a.dtype = h->dtype;
   a.layout = h->layout;

@@ -116,6 +116,7 @@ struct FcArgs {
   const FcEnt* ents;
   int tn;                   // column tile width: 32 or 64
   int nt;                   // entry class (fc_t_class)
+  int lds_direct;           // weight chunks copied straight into LDS (see fc_term)
   size_t lds_bytes;
   int dtype, layout;
   void* stream;
@@ -133,6 +134,7 @@ struct FcDwArgs {
   const FcDwPath* paths;    // device
   const FcEnt* ents;
   int nt;                   // entry class (fc_t_class)
+  int lds_direct;           // weight chunks copied straight into LDS (see fc_term)
   size_t lds_bytes;
   int dtype, layout;
   void* stream;

@@ -114,10 +114,11 @@ __device__ __forceinline__ void fc_stage(const T* __restrict__ src, int64_t sdim
 // staged in LDS.  The weight rows of the next chunk are fetched into
 // registers while the current chunk multiplies, then written to the other
 // LDS buffer.
-template <typename T, int LAYOUT, int TN, int NT>
+template <typename T, int LAYOUT, int TN, int NT, bool DMA>
 __device__ __forceinline__ void fc_term(const FcTerm& Tm, const FcEnt* __restrict__ ents, const T* __restrict__ w,
                                         const T* Ps, const T* __restrict__ Qt, int64_t qdim,
-                                        T (*Bs)[kFcTK][FcB<TN>::stride], int m_res, int c0, const int (&sl)[kFcRT],
+                                        T (*B0)[FcB<TN>::stride], T (*B1)[FcB<TN>::stride], int m_res, int c0,
+                                        const int (&sl)[kFcRT],
                                         const int (&kc)[kFcRT], const bool (&rv)[kFcRT], int nrt, int tid,
                                         int lane, typename Mfma<T>::acc_t (&acc)[kFcRT][TN / 16]) {
   using M = Mfma<T>;
@@ -216,16 +217,18 @@ __device__ __forceinline__ void fc_term(const FcTerm& Tm, const FcEnt* __restric
     }
   };
   auto put = [&](int buf, int vc) {
+    T (*B)[FcB<TN>::stride] = buf ? B1 : B0;
 #pragma unroll
     for (int i = 0; i < kBPer; ++i) {
       const bool ok = wb[i] >= 0 && vc * win + kk_of(i) < Tm.q_m;
-      Bs[buf][kk_of(i)][cc_of(i)] = ok ? rb[i] : T(0);
+      B[kk_of(i)][cc_of(i)] = ok ? rb[i] : T(0);
     }
   };
 
-  auto load_b = [&](int buf, int s, T (&b)[kNT]) {
+  // B values of step s from a chunk buffer with rows of `rs` elements
+  auto load_b = [&](const T* base, int rs, int s, T (&b)[kNT]) {
 #pragma unroll
-    for (int j = 0; j < kNT; ++j) b[j] = Bs[buf][4 * s + lane / 16][j * 16 + lane % 16];
+    for (int j = 0; j < kNT; ++j) b[j] = base[(4 * s + lane / 16) * rs + j * 16 + lane % 16];
   };
   // One MFMA step for the wave's row tiles: RT = 2 (both) or 1 (the second
   // starts past the tile's rows); chosen once per chunk, so the steps run
@@ -241,23 +244,80 @@ __device__ __forceinline__ void fc_term(const FcTerm& Tm, const FcEnt* __restric
       for (int j = 0; j < kNT; ++j) acc[rt][j] = M::mma(t, b[j], acc[rt][j]);
     }
   };
-  auto chunk = [&](auto rt_count, int buf, const T (&y)[kFcRT][NT]) {
+  auto chunk = [&](auto rt_count, const T* base, int rs, const T (&y)[kFcRT][NT]) {
     if (steps == VS) {
       // the whole chunk's B values first: one LDS wait per chunk
       T b[VS][kNT];
 #pragma unroll
-      for (int s = 0; s < VS; ++s) load_b(buf, s, b[s]);
+      for (int s = 0; s < VS; ++s) load_b(base, rs, s, b[s]);
       __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of the steps
 #pragma unroll
       for (int s = 0; s < VS; ++s) step(rt_count, s, b[s], y);
     } else {
       for (int s = 0; s < steps; ++s) {
         T b[kNT];
-        load_b(buf, s, b);
+        load_b(base, rs, s, b);
         step(rt_count, s, b, y);
       }
     }
   };
+  auto chunk_rows = [&](const T* base, int rs, int u) {
+    T y[kFcRT][NT];
+#pragma unroll
+    for (int rt = 0; rt < kFcRT; ++rt)
+#pragma unroll
+      for (int e = 0; e < NT; ++e) y[rt][e] = cf[rt][e] * Ps[po[rt][e] + u];
+    if (kFcRT == 2 && nrt == 2)
+      chunk(std::integral_constant<int, kFcRT>{}, base, rs, y);
+    else if (nrt >= 1)
+      chunk(std::integral_constant<int, 1>{}, base, rs, y);
+  };
+
+  // DMA: LDS-direct weight chunks (the host launches this form only for
+  // float, 32 columns, the result channel the contiguous weight index, full
+  // windows and column tiles, 16-byte aligned rows): wave k copies rows
+  // 8k .. 8k + 7 of the next chunk with one 16-byte-per-lane load straight
+  // into LDS (rows of 32, no registers, no LDS write), into the buffer the
+  // current chunk does not read; the two buffers are separate arrays, so
+  // the reads of one never wait for the copy into the other.  Each wave
+  // waits for its own copy before the chunk's barrier.
+  if constexpr (DMA) {
+    static_assert(sizeof(T) == 4 && TN == 32 && VK == 32, "LDS-direct chunks are float rows of 32");
+    {
+      const int wv = __builtin_amdgcn_readfirstlane(tid / 64);
+      T* D0 = &B0[0][0];
+      T* D1 = &B1[0][0];
+      auto copy = [&](T* dst, int c) {
+        const int vc = c / Tm.p_m, u = c - vc * Tm.p_m;
+        const int kk = 8 * wv + lane / 8, cc = 4 * (lane % 8);
+        const T* gp = w + Tm.w_off + static_cast<int64_t>(u) * Tm.s_p +
+                      static_cast<int64_t>(vc * win + kk) * Tm.s_q + c0 + cc;
+        // (address-space casts: global source, LDS destination)
+        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(gp),
+                                         (__attribute__((address_space(3))) void*)(dst + 8 * wv * TN), 16, 0, 0);
+      };
+      auto body = [&](int c, const T* cur, T* nxt) {
+        const int vc = c / Tm.p_m, u = c - vc * Tm.p_m;
+        if (c + 1 < nch) copy(nxt, c + 1);
+        chunk_rows(cur, TN, u);
+        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+        __syncthreads();
+        if (c + 1 < nch && (c + 1) / Tm.p_m != vc) {
+          load_q((c + 1) / Tm.p_m, win);
+          __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+        }
+      };
+      copy(D0, 0);
+      load_q(0, win);
+      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+      __syncthreads();
+      for (int c = 0; c < nch; c += 2) {
+        body(c, D0, D1);
+        if (c + 1 < nch) body(c + 1, D1, D0);
+      }
+      return;
+    }
+  }
 
   // Windows outer, P channels inner.  The Q window's loads are waited for
   // explicitly before the channel loop, so the loop's only outstanding
@@ -279,15 +339,7 @@ __device__ __forceinline__ void fc_term(const FcTerm& Tm, const FcEnt* __restric
       }
       __builtin_amdgcn_sched_barrier(0);  // issue the prefetch before the steps
       const int buf = ch & 1;
-      T y[kFcRT][NT];
-#pragma unroll
-      for (int rt = 0; rt < kFcRT; ++rt)
-#pragma unroll
-        for (int e = 0; e < NT; ++e) y[rt][e] = cf[rt][e] * Ps[po[rt][e] + u];
-      if (kFcRT == 2 && nrt == 2)
-        chunk(std::integral_constant<int, kFcRT>{}, buf, y);
-      else if (nrt >= 1)
-        chunk(std::integral_constant<int, 1>{}, buf, y);
+      chunk_rows(&(buf ? B1 : B0)[0][0], FcB<TN>::stride, u);
       if (more) put(buf ^ 1, u + 1 < Tm.p_m ? vc : vc + 1);
       __syncthreads();
     }
@@ -304,7 +356,7 @@ constexpr int fc_min_blocks() {
   return (sizeof(T) == 4 && TN == 32 && NT <= 3) ? 4 : 1;
 }
 
-template <typename T, int LAYOUT, int TN, int NT>
+template <typename T, int LAYOUT, int TN, int NT, bool DMA>
 __global__ void __launch_bounds__(kFcThreads, (fc_min_blocks<T, TN, NT>()))
 fctp_kernel(const T* __restrict__ op0, const T* __restrict__ op1, const T* __restrict__ op2, int64_t dim0,
             int64_t dim1, int64_t dim2, const T* __restrict__ w, T* __restrict__ res, int64_t dim_res, int64_t n,
@@ -313,7 +365,8 @@ fctp_kernel(const T* __restrict__ op0, const T* __restrict__ op1, const T* __res
   using M = Mfma<T>;
   constexpr int kNT = TN / 16;
   extern __shared__ __align__(16) unsigned char fc_smem[];
-  __shared__ T Bs[2][kFcTK][FcB<TN>::stride];
+  __shared__ T Bs0[kFcTK][FcB<TN>::stride];
+  __shared__ T Bs1[kFcTK][FcB<TN>::stride];
 
   const int bid = blockIdx.x;
   int r = 0;
@@ -360,7 +413,7 @@ fctp_kernel(const T* __restrict__ op0, const T* __restrict__ op1, const T* __res
     __syncthreads();  // the previous term's LDS reads are done
     fc_stage<T, LAYOUT, 8>(P, pdim, Tm.p_off, Tm.p_d, Tm.p_m, s0, ts, n, Ps, tid);
     // (fc_term's first barrier publishes the staged block)
-    fc_term<T, LAYOUT, TN, NT>(Tm, ents, w, Ps, Q + s0 * qdim, qdim, Bs, R.m, c0, sl, kc, rv, nrt, tid,
+    fc_term<T, LAYOUT, TN, NT, DMA>(Tm, ents, w, Ps, Q + s0 * qdim, qdim, Bs0, Bs1, R.m, c0, sl, kc, rv, nrt, tid,
                                lane, acc);
   }
 
@@ -541,11 +594,11 @@ fctp_dw_fold_kernel(const T* __restrict__ part, int chunks, int64_t numel, T* __
   }
 }
 
-template <typename T, int LAYOUT, int TN, int NT>
+template <typename T, int LAYOUT, int TN, int NT, bool DMA = false>
 int fctp_launch_k(const FcArgs& a, const FcTiles& t) {
   const int total = t.tile_begin[t.n_res];
   if (total == 0) return 0;
-  hipLaunchKernelGGL((fctp_kernel<T, LAYOUT, TN, NT>), dim3(static_cast<unsigned>(total)), dim3(kFcThreads),
+  hipLaunchKernelGGL((fctp_kernel<T, LAYOUT, TN, NT, DMA>), dim3(static_cast<unsigned>(total)), dim3(kFcThreads),
                      a.lds_bytes, static_cast<hipStream_t>(a.stream), static_cast<const T*>(a.op[0]),
                      static_cast<const T*>(a.op[1]), static_cast<const T*>(a.op[2]), a.dim[0], a.dim[1], a.dim[2],
                      static_cast<const T*>(a.w), static_cast<T*>(a.res), a.dim_res, a.n, a.res_tab, a.terms, a.ents,
@@ -555,6 +608,17 @@ int fctp_launch_k(const FcArgs& a, const FcTiles& t) {
 
 template <typename T, int LAYOUT, int TN>
 int fctp_launch_tn(const FcArgs& a, const FcTiles& t) {
+  if constexpr (sizeof(T) == 4 && TN == 32) {
+    if (a.lds_direct) {  // (the host checked the pass's terms and the weight alignment)
+      switch (a.nt) {
+        case 1: return fctp_launch_k<T, LAYOUT, TN, 1, true>(a, t);
+        case 2: return fctp_launch_k<T, LAYOUT, TN, 2, true>(a, t);
+        case 3: return fctp_launch_k<T, LAYOUT, TN, 3, true>(a, t);
+        case 4: return fctp_launch_k<T, LAYOUT, TN, 4, true>(a, t);
+        default: break;
+      }
+    }
+  }
   switch (a.nt) {
     case 1: return fctp_launch_k<T, LAYOUT, TN, 1>(a, t);
     case 2: return fctp_launch_k<T, LAYOUT, TN, 2>(a, t);
