@@ -591,6 +591,49 @@ def fc_conv(torch, sp, workloads, dev, args):
     return res
 
 
+def eager_per_path(torch, h, wl, t, N, E, dev):
+    """Context for the fusion: the same convolution as plain PyTorch-ROCm
+    operations, one gather, contraction and index_add_ per path (the
+    launch-per-path form the fused kernel replaces), on the same GPU and
+    inputs; ir_mul blocks, coefficients read from the descriptor."""
+    import numpy as np
+
+    from oracle import irreps as oir   # sizes only: block offsets
+
+    def offsets(irreps):
+        o, r = 0, []
+        for mul, l, _ in oir.parse(irreps):
+            r.append(o)
+            o += mul * (2 * l + 1)
+        return r
+    assert h.layout == "ir_mul"
+    off1, off2 = offsets(wl.irreps_in1), offsets(wl.irreps_in2)
+    paths = []
+    for p in range(h.num_paths):
+        i = h.path_info(p)
+        d1, d2, d3 = 2 * i["l1"] + 1, 2 * i["l2"] + 1, 2 * i["lo"] + 1
+        C = torch.from_numpy(h.path_cg(p).astype(np.float32)).to(dev)
+        paths.append((off1[i["in1_block"]], off2[i["in2_block"]], i["out_offset"], i["weight_offset"],
+                      i["mul"], d1, d2, d3, C))
+    x, sh, w, src, dst = t["x"], t["sh"], t["w"], t["src"].long(), t["dst"].long()
+    out = torch.zeros((N, h.dim_out), dtype=x.dtype, device=dev)
+
+    def run():
+        out.zero_()
+        for o1, o2, oo, wo, mul, d1, d2, d3, C in paths:
+            xb = x[:, o1:o1 + d1 * mul].index_select(0, src).view(E, d1, mul)
+            m = torch.einsum("abk,eau,eb->eku", C, xb, sh[:, o2:o2 + d2]) * w[:, wo:wo + mul].view(E, 1, mul)
+            out[:, oo:oo + d3 * mul].index_add_(0, dst, m.reshape(E, d3 * mul))
+    run()
+    torch.cuda.synchronize()
+    diff = float((out - t["out"]).abs().max()) / max(float(t["out"].abs().max()), 1e-30)
+    steps = 20
+    wall, per = time_launches(torch, run, steps, 3)
+    return {"what": "one gather, contraction and index_add_ per path in PyTorch (fp32), same inputs",
+            "paths": len(paths), "us_per_call": wall * 1e6 / steps,
+            "max_rel_diff_to_fused": diff}
+
+
 def other_workloads(torch, sp, workloads, dev, args):
     """The smaller workloads: microseconds per call (eager, and replayed from
     a HIP graph for the launch-bound molecular batch) and edges/s; the
@@ -627,6 +670,7 @@ def other_workloads(torch, sp, workloads, dev, args):
             b = E * (h.weight_numel + h.dim_in2 + 2) * 4 + N * (h.dim_in1 + h.dim_out) * 4
             rec["cold_input_sets"] = len(sets)
             rec["hbm_GBps_algorithmic"] = b / (sum(per) / len(per) * 1e-3) / 1e9
+            rec["eager_per_path"] = eager_per_path(torch, h, wl, sets[0], N, E, dev)
         if n == 2:
             # HIP graph replay of 20 calls (the path has no memset or host work)
             t = sets[0]
