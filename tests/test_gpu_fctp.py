@@ -151,6 +151,32 @@ def test_empty_and_single_sample():
     assert np.count_nonzero(gw.cpu().numpy()) == 0
 
 
+def test_weight_alignment_selects_the_staging():
+    """Weights that are not 16-byte aligned take the register-staged path
+    instead of the LDS-direct one (whose copies need aligned rows); both
+    must give the oracle's result."""
+    import torch
+    sp = _sp()
+    in1, in2, out, n = CASES[0]
+    f = ofc.FullyConnectedTP(in1, in2, out)
+    h = sp.fctp_create(in1, in2, out, dtype="f32")
+    x1, x2, w, g = _inputs(f, n, "f32", 13)
+    X1, X2 = dev(x1, torch.float32), dev(x2, torch.float32)
+    announce("fctp weights aligned and misaligned")
+    buf = torch.empty(f.weight_numel + 1, dtype=torch.float32, device="cuda")
+    Wm = buf[1:].view(1, f.weight_numel)
+    Wm.copy_(dev(w, torch.float32))
+    assert Wm.data_ptr() % 16 != 0
+    Wa = dev(w, torch.float32)
+    assert Wa.data_ptr() % 16 == 0
+    ref = f.fwd(x1, x2, w)
+    scale = f.fwd(x1, x2, w, absolute=True)
+    for W, what in ((Wa, "aligned"), (Wm, "misaligned")):
+        got = sp.fctp_fwd(h, X1, X2, W)
+        torch.cuda.synchronize()
+        check_scaled(got.cpu().numpy(), ref, scale, "f32", f"weights {what}")
+
+
 def test_deterministic():
     import torch
     sp = _sp()
