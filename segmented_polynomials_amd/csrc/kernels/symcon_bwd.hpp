@@ -25,7 +25,10 @@
 //     and accumulates dw in registers; at the end it writes the chunk's
 //     partial dw row.  Chunks of out-of-range elements write zero dx.
 //     Measured on 50k atoms (10 elements, 128 channels): chunks of 8 atoms
-//     beat 16 and 32 (more waves), and the prefetch gains 8 %;
+//     beat 16 and 32 (more waves), and the prefetch gains 8 %.  It runs as
+//     two launches, WHICH = 1 (dw partials) and WHICH = 2 (dx), each of
+//     which holds fewer values than the fused pass (two or three waves per
+//     SIMD instead of one: 0.61 -> 0.51 ms, the rows read twice);
 //  3. fold kernel: dw[e] = sum of its chunks' partial rows in a fixed order
 //     (zero for an element without atoms).
 #pragma once
@@ -92,7 +95,7 @@ symcon_table_kernel(const Index* __restrict__ species, const Index* __restrict__
   }
 }
 
-template <class S, typename T, typename Index, int LAYOUT>
+template <class S, typename T, typename Index, int LAYOUT, int WHICH>
 __global__ void __launch_bounds__(kWave)
 symcon_bwd_kernel(const T* __restrict__ x, const Index* __restrict__ perm, const T* __restrict__ w,
                   const T* __restrict__ g, int64_t n_atoms, int ne, int mul, const int64_t* __restrict__ table,
@@ -147,17 +150,18 @@ symcon_bwd_kernel(const T* __restrict__ x, const Index* __restrict__ perm, const
         load(a_next);
       }
       if (ok(a)) {
-        S::template bwd_w<T>(v, go, dw);
-        S::template bwd_x<T>(v, go, wv, dv);
+        if constexpr ((WHICH & 1) != 0) S::template bwd_w<T>(v, go, dw);
+        if constexpr ((WHICH & 2) != 0) S::template bwd_x<T>(v, go, wv, dv);
       }
     } else {
       if (i + 1 < i1) a_next = atom(i + 1);
 #pragma unroll
       for (int m = 0; m < S::NV; ++m) dv[m] = T(0);
     }
-    if (active && ok(a)) S::template store_v<T, LAYOUT>(dx + a * dim_in, mul, u, dv);
+    if constexpr ((WHICH & 2) != 0)
+      if (active && ok(a)) S::template store_v<T, LAYOUT>(dx + a * dim_in, mul, u, dv);
   }
-  if (valid && active) {
+  if ((WHICH & 1) != 0 && valid && active) {
     T* prow = part + t * numel;
 #pragma unroll
     for (int s = 0; s < S::NS; ++s) prow[s * mul + u] = dw[s];
@@ -211,7 +215,13 @@ int symcon_bwd_launch(const SymconBwdArgs& a) {
   const int64_t chunks = symcon_bwd_max_chunks(a.n_atoms, ne);
   const unsigned tiles = static_cast<unsigned>((a.mul + kWave - 1) / kWave);
   if (a.n_atoms > 0) {
-    hipLaunchKernelGGL((symcon_bwd_kernel<S, T, Index, LAYOUT>), dim3(static_cast<unsigned>(chunks), tiles),
+    hipLaunchKernelGGL((symcon_bwd_kernel<S, T, Index, LAYOUT, 1>), dim3(static_cast<unsigned>(chunks), tiles),
+                       dim3(kWave), 0, st, static_cast<const T*>(a.x), static_cast<const Index*>(a.perm),
+                       static_cast<const T*>(a.w), static_cast<const T*>(a.g), a.n_atoms, ne, a.mul, table,
+                       static_cast<T*>(a.dx), part);
+    rc = static_cast<int>(hipGetLastError());
+    if (rc) return rc;
+    hipLaunchKernelGGL((symcon_bwd_kernel<S, T, Index, LAYOUT, 2>), dim3(static_cast<unsigned>(chunks), tiles),
                        dim3(kWave), 0, st, static_cast<const T*>(a.x), static_cast<const Index*>(a.perm),
                        static_cast<const T*>(a.w), static_cast<const T*>(a.g), a.n_atoms, ne, a.mul, table,
                        static_cast<T*>(a.dx), part);
