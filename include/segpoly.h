@@ -430,16 +430,18 @@ int fctp_path_info(fctp_handle h, int p, int64_t* info4);
  */
 int fctp_fwd(fctp_handle h, const void* x1, const void* x2, const void* w, int64_t n, void* out, void* stream);
 
-/* fctp_bwd_workspace: bytes of workspace fctp_bwd needs for the weight
- * gradient of n samples (per-chunk partial sums). */
+/* fctp_bwd_workspace: bytes of workspace fctp_bwd needs for n samples:
+ * the weight gradient's per-chunk partial sums and two transposed copies of
+ * the weights that the input gradients read (0 for n = 0). */
 int fctp_bwd_workspace(fctp_handle h, int64_t n, size_t* bytes);
 
 /*
  * fctp_bwd: vector-Jacobian product of fctp_fwd for g = dL/d(out):
  *   grad_x1 [n, DIM_IN1], grad_x2 [n, DIM_IN2], grad_w [1, WEIGHT_NUMEL],
- * each fully overwritten, or NULL (not computed).  grad_w needs
- * `workspace` of fctp_bwd_workspace(n) bytes; it sums fixed chunks of 1024
- * samples and then the chunks in order (deterministic).  Inputs a requested
+ * each fully overwritten, or NULL (not computed).  Any requested gradient
+ * needs `workspace` of fctp_bwd_workspace(n) bytes (overwritten); grad_w
+ * sums fixed chunks of 1024 samples and then the chunks in order
+ * (deterministic).  Inputs a requested
  * gradient does not read may be NULL (grad_x1 reads x2, g, w; grad_x2 reads
  * x1, g, w; grad_w reads x1, x2, g).
  */

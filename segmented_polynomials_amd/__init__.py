@@ -641,7 +641,7 @@ def fctp_bwd(h, x1, x2, w, grad_out, need=(True, True, True), workspace=None):
     g1 = torch.empty_like(x1) if need[0] else None
     g2 = torch.empty_like(x2) if need[1] else None
     gw = torch.empty_like(w) if need[2] else None
-    if need[2] and workspace is None:
+    if any(need) and workspace is None:
         workspace = torch.empty(max(1, fctp_bwd_workspace(h, n)), dtype=torch.uint8, device=x1.device)
     wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib.fctp_bwd(h._h, _ptr(x1), _ptr(x2), _ptr(w), _ptr(grad_out), n, _ptr(g1), _ptr(g2), _ptr(gw),

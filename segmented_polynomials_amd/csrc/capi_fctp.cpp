@@ -97,7 +97,8 @@ struct segpoly_fctp {
   FcPass pass[3];                 // forward, input-1 gradient, input-2 gradient
   std::vector<FcDwPath> dw;
   int dw_nt = 1;                  // entry class of the weight-gradient launch
-  size_t dw_lds = 0, dw_off = 0, ent_off = 0;
+  size_t dw_lds = 0, dw_off = 0, ent_off = 0, tr_off = 0;
+  std::vector<FcTrPath> tr_paths;     // segments of the weight transposition
   std::vector<FcEnt> ents;
   // the graph convolution form (per-edge weights); conv_error is why it is
   // unavailable for this descriptor ("" if available)
@@ -199,16 +200,16 @@ int build_pass(segpoly_fctp* h, int which) {
         t.p_d = d1, t.p_m = a.mul, t.p_off = h->off1[pa.i];
         t.q_d = d2, t.q_m = b.mul, t.q_off = h->off2[pa.j];
         t.s_p = m2 * m3, t.s_q = m3, t.s_r = 1;
-      } else if (which == 1) {  // P = x2 (b, v), Q = g (k, w), result (a, u)
+      } else if (which == 1) {  // P = x2 (b, v), Q = g (k, w), result (a, u); weights W1[v][w][u]
         t.p_op = 1, t.q_op = 2;
         t.p_d = d2, t.p_m = b.mul, t.p_off = h->off2[pa.j];
         t.q_d = d3, t.q_m = o.mul, t.q_off = h->offo[pa.o];
-        t.s_p = m3, t.s_q = 1, t.s_r = m2 * m3;
-      } else {  // P = x1 (a, u), Q = g (k, w), result (b, v)
+        t.s_p = m3 * m1, t.s_q = m1, t.s_r = 1;
+      } else {  // P = x1 (a, u), Q = g (k, w), result (b, v); weights W2[u][w][v]
         t.p_op = 0, t.q_op = 2;
         t.p_d = d1, t.p_m = a.mul, t.p_off = h->off1[pa.i];
         t.q_d = d3, t.q_m = o.mul, t.q_off = h->offo[pa.o];
-        t.s_p = m2 * m3, t.s_q = 1, t.s_r = m3;
+        t.s_p = m3 * m2, t.s_q = m2, t.s_r = 1;
       }
       if (static_cast<int64_t>(t.p_m) * t.q_m >= (1ll << 31))
         return fail(SEGPOLY_E_UNSUPPORTED, "multiplicities too large (mul1 * mul2 must stay below 2^31)");
@@ -455,6 +456,16 @@ size_t dw_workspace(const segpoly_fctp* h, int64_t n) {
   return static_cast<size_t>(round_up_256(chunks * h->numel * static_cast<int64_t>(elt(h->dtype))));
 }
 
+// bytes of one transposed weight copy (the input-gradient passes read two)
+size_t tr_bytes(const segpoly_fctp* h) {
+  return static_cast<size_t>(round_up_256(h->numel * static_cast<int64_t>(elt(h->dtype))));
+}
+
+// workspace of fctp_bwd: [dW partials][W1][W2]
+size_t bwd_workspace(const segpoly_fctp* h, int64_t n) {
+  return n > 0 && h->numel > 0 ? dw_workspace(h, n) + 2 * tr_bytes(h) : 0;
+}
+
 }  // namespace
 
 extern "C" {
@@ -513,6 +524,7 @@ int fctp_create(const char* irreps_in1, const char* irreps_in2, const char* irre
         const Irrep &a = h->in1[i], &b = h->in2[j], &c = h->out[o];
         if (c.l < std::abs(a.l - b.l) || c.l > a.l + b.l || c.p != a.p * b.p) continue;
         h->paths.push_back({static_cast<int>(i), static_cast<int>(j), static_cast<int>(o), woff});
+        h->tr_paths.push_back({woff, a.mul, b.mul, c.mul});
         woff += static_cast<int64_t>(a.mul) * b.mul * c.mul;
         fan[o] += static_cast<int64_t>(a.mul) * b.mul;
       }
@@ -529,6 +541,7 @@ int fctp_create(const char* irreps_in1, const char* irreps_in2, const char* irre
         h->pass[w].term_off = append(h->blob, h->pass[w].terms);
       }
       h->dw_off = append(h->blob, h->dw);
+      h->tr_off = append(h->blob, h->tr_paths);
       h->ent_off = append(h->blob, h->ents);
       h->cv_off[0] = append(h->blob, h->cv_blocks);
       h->cv_off[1] = append(h->blob, h->cv_paths);
@@ -589,7 +602,7 @@ int fctp_fwd(fctp_handle h, const void* x1, const void* x2, const void* w, int64
 int fctp_bwd_workspace(fctp_handle h, int64_t n, size_t* bytes) {
   if (!h || !bytes) return fail(SEGPOLY_E_INVALID, "null argument");
   if (n < 0) return fail(SEGPOLY_E_INVALID, "negative sample count");
-  *bytes = dw_workspace(h, n);
+  *bytes = bwd_workspace(h, n);
   return ok();
 }
 
@@ -597,9 +610,10 @@ int fctp_bwd(fctp_handle h, const void* x1, const void* x2, const void* w, const
              void* grad_x1, void* grad_x2, void* grad_w, void* workspace, size_t workspace_bytes, void* stream) {
   if (!h) return fail(SEGPOLY_E_INVALID, "null handle");
   if (n < 0) return fail(SEGPOLY_E_INVALID, "negative sample count");
-  if (grad_w && h->numel > 0 && workspace_bytes < dw_workspace(h, n))
-    return fail(SEGPOLY_E_INVALID, "workspace too small: need " + std::to_string(dw_workspace(h, n)) + " bytes");
-  if (grad_w && h->numel > 0 && n > 0 && !workspace) return fail(SEGPOLY_E_INVALID, "null workspace");
+  const bool any = grad_x1 || grad_x2 || grad_w;
+  if (any && workspace_bytes < bwd_workspace(h, n))
+    return fail(SEGPOLY_E_INVALID, "workspace too small: need " + std::to_string(bwd_workspace(h, n)) + " bytes");
+  if (any && bwd_workspace(h, n) > 0 && !workspace) return fail(SEGPOLY_E_INVALID, "null workspace");
   if (n > 0) {
     if ((h->dimo > 0 && !grad_out) || (h->dim1 > 0 && !x1 && (grad_x2 || grad_w)) ||
         (h->dim2 > 0 && !x2 && (grad_x1 || grad_w)) || (h->numel > 0 && !w && (grad_x1 || grad_x2)))
@@ -615,12 +629,27 @@ int fctp_bwd(fctp_handle h, const void* x1, const void* x2, const void* w, const
   int st = SEGPOLY_OK;
   const unsigned char* db = device_blob(h, &st);
   if (!db) return st;
+  if ((grad_x1 || grad_x2) && h->numel > 0) {  // the transposed weights both input gradients read
+    unsigned char* ws = static_cast<unsigned char*>(workspace) + dw_workspace(h, n);
+    FcTrArgs a{};
+    a.w = w;
+    a.w1 = ws;
+    a.w2 = ws + tr_bytes(h);
+    a.paths = reinterpret_cast<const FcTrPath*>(db + h->tr_off);
+    a.n_paths = static_cast<int>(h->tr_paths.size());
+    a.numel = h->numel;
+    a.dtype = h->dtype;
+    a.stream = stream;
+    const int rc = launch_fctp_transpose(a);
+    if (rc) return fail(SEGPOLY_E_HIP, std::string("fctp transpose: ") + hipGetErrorString(static_cast<hipError_t>(rc)));
+  }
+  const unsigned char* w1 = static_cast<const unsigned char*>(workspace) + dw_workspace(h, n);
   if (grad_x1) {
-    const int rc = run_pass(h, db, 1, x1, x2, grad_out, w, n, grad_x1, stream);
+    const int rc = run_pass(h, db, 1, x1, x2, grad_out, h->numel > 0 ? w1 : w, n, grad_x1, stream);
     if (rc) return rc;
   }
   if (grad_x2) {
-    const int rc = run_pass(h, db, 2, x1, x2, grad_out, w, n, grad_x2, stream);
+    const int rc = run_pass(h, db, 2, x1, x2, grad_out, h->numel > 0 ? w1 + tr_bytes(h) : w, n, grad_x2, stream);
     if (rc) return rc;
   }
   if (grad_w && h->numel > 0) {

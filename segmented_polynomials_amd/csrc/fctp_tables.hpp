@@ -134,11 +134,37 @@ struct FcDwArgs {
   const FcDwPath* paths;    // device
   const FcEnt* ents;
   int nt;                   // entry class (fc_t_class)
-  int lds_direct;           // weight chunks copied straight into LDS (see fc_term)
   size_t lds_bytes;
   int dtype, layout;
   void* stream;
 };
+
+// The input-gradient passes read the weights transposed, so that their
+// result channel is the contiguous weight index (the form whose chunks go
+// straight into LDS): per path W[u][v][w] -> W1[v][w][u] (for dx1) and
+// W2[u][w][v] (for dx2), at the same segment offsets.
+struct FcTrPath {
+  int64_t w_off;
+  int m1, m2, m3;
+};
+
+struct FcTrArgs {
+  const void* w;
+  void* w1;
+  void* w2;
+  const FcTrPath* paths;    // device, in segment order
+  int n_paths;
+  int64_t numel;
+  int dtype;
+  void* stream;
+};
+
+int launch_fctp_transpose_f32(const FcTrArgs& a);
+int launch_fctp_transpose_f64(const FcTrArgs& a);
+
+inline int launch_fctp_transpose(const FcTrArgs& a) {
+  return a.dtype == kF32 ? launch_fctp_transpose_f32(a) : launch_fctp_transpose_f64(a);
+}
 
 int launch_fctp_f32(const FcArgs& a, const FcTiles& t);
 int launch_fctp_f64(const FcArgs& a, const FcTiles& t);

@@ -594,6 +594,42 @@ fctp_dw_fold_kernel(const T* __restrict__ part, int chunks, int64_t numel, T* __
   }
 }
 
+// W[u][v][w] -> W1[v][w][u], W2[u][w][v] per path segment (one thread per
+// weight; the segment of weight i is the last path whose offset is <= i).
+template <typename T>
+__global__ void __launch_bounds__(256)
+fctp_transpose_kernel(const T* __restrict__ w, T* __restrict__ w1, T* __restrict__ w2,
+                      const FcTrPath* __restrict__ paths, int n_paths, int64_t numel) {
+  for (int64_t i = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; i < numel;
+       i += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    int lo = 0, hi = n_paths - 1;
+    while (lo < hi) {  // last path with w_off <= i
+      const int mid = (lo + hi + 1) / 2;
+      if (paths[mid].w_off <= i)
+        lo = mid;
+      else
+        hi = mid - 1;
+    }
+    const FcTrPath P = paths[lo];
+    const int64_t r = i - P.w_off;
+    const int64_t c = r % P.m3, t = r / P.m3;
+    const int64_t v = t % P.m2, u = t / P.m2;
+    const T x = w[i];
+    w1[P.w_off + (v * P.m3 + c) * P.m1 + u] = x;
+    w2[P.w_off + (u * P.m3 + c) * P.m2 + v] = x;
+  }
+}
+
+template <typename T>
+int fctp_transpose_launch(const FcTrArgs& a) {
+  if (a.numel == 0 || a.n_paths == 0) return 0;
+  const int64_t blocks = (a.numel + 255) / 256;
+  hipLaunchKernelGGL((fctp_transpose_kernel<T>), dim3(static_cast<unsigned>(blocks < 4096 ? blocks : 4096)),
+                     dim3(256), 0, static_cast<hipStream_t>(a.stream), static_cast<const T*>(a.w),
+                     static_cast<T*>(a.w1), static_cast<T*>(a.w2), a.paths, a.n_paths, a.numel);
+  return static_cast<int>(hipGetLastError());
+}
+
 template <typename T, int LAYOUT, int TN, int NT, bool DMA = false>
 int fctp_launch_k(const FcArgs& a, const FcTiles& t) {
   const int total = t.tile_begin[t.n_res];

@@ -14,4 +14,6 @@ int launch_fctp_dw_f32(const FcDwArgs& a, const FcDwTiles& t) {
   return a.layout == kMulIr ? fctp_dw_launch<float, kMulIr>(a, t) : fctp_dw_launch<float, kIrMul>(a, t);
 }
 
+int launch_fctp_transpose_f32(const FcTrArgs& a) { return kern::fctp_transpose_launch<float>(a); }
+
 }  // namespace segpoly

@@ -14,4 +14,6 @@ int launch_fctp_dw_f64(const FcDwArgs& a, const FcDwTiles& t) {
   return a.layout == kMulIr ? fctp_dw_launch<double, kMulIr>(a, t) : fctp_dw_launch<double, kIrMul>(a, t);
 }
 
+int launch_fctp_transpose_f64(const FcTrArgs& a) { return kern::fctp_transpose_launch<double>(a); }
+
 }  // namespace segpoly

@@ -309,14 +309,17 @@ def test_fctp_errors_and_workspace():
     assert sp.lib.fctp_fwd(h._h, p, p, p, 3, None, None) == sp.E_INVALID
     assert sp.lib.fctp_fwd(h._h, None, None, None, 0, None, None) == sp.OK
     assert sp.lib.fctp_fwd(None, p, p, p, 3, p, None) == sp.E_INVALID
-    # weight gradient workspace: one partial row of weight_numel per chunk of 1024 samples
+    # backward workspace: one partial row of weight_numel per chunk of 1024
+    # samples (weight gradient) and two transposed weight copies (input gradients)
     assert sp.fctp_bwd_workspace(h, 0) == 0
-    assert sp.fctp_bwd_workspace(h, 1) == 131072 * 4
-    assert sp.fctp_bwd_workspace(h, 2049) == 3 * 131072 * 4
+    assert sp.fctp_bwd_workspace(h, 1) == (1 + 2) * 131072 * 4
+    assert sp.fctp_bwd_workspace(h, 2049) == (3 + 2) * 131072 * 4
     b = sp.lib.fctp_bwd
     assert b(h._h, p, p, p, p, 5000, None, None, p, p, 8, None) == sp.E_INVALID          # workspace small
     assert b(h._h, p, p, p, p, 5000, None, None, p, None, 1 << 30, None) == sp.E_INVALID  # null workspace
-    assert b(h._h, p, p, None, p, 5000, p, None, None, None, 0, None) == sp.E_INVALID     # dx1 needs w
+    assert b(h._h, p, p, None, p, 5000, p, None, None, None, 0, None) == sp.E_INVALID     # dx1: no workspace
+    big = 1 << 30
+    assert b(h._h, p, p, None, p, 5000, p, None, None, p, big, None) == sp.E_INVALID      # dx1 needs w
     assert b(h._h, None, None, None, None, 0, None, None, None, None, 0, None) == sp.OK
     assert sp.lib.fctp_destroy(None) == sp.OK
     # the convolution form: input 2 with one channel per block, w_rows 1 or n_edges
