@@ -97,6 +97,7 @@ struct segpoly_fctp {
   FcPass pass[3];                 // forward, input-1 gradient, input-2 gradient
   std::vector<FcDwPath> dw;
   int dw_nt = 1;                  // entry class of the weight-gradient launch
+  bool dw_dma = false;            // weight-gradient staging straight into LDS
   size_t dw_lds = 0, dw_off = 0, ent_off = 0, tr_off = 0;
   std::vector<FcTrPath> tr_paths;     // segments of the weight transposition
   std::vector<FcEnt> ents;
@@ -282,6 +283,24 @@ int build_dw(segpoly_fctp* h) {
     h->dw_lds = std::max(h->dw_lds, static_cast<size_t>(ts) * per);
     h->dw.push_back(q);
   }
+  // Float launches stage through the LDS-direct buffers when every staged
+  // sample fits the per-lane copies and four samples of the three blocks
+  // fit one buffer.
+  bool dma = h->dtype == SEGPOLY_F32;
+  for (const auto& q : h->dw) {
+    const int ps = fc_sample_stride(q.p_d, q.p_m), qs = fc_sample_stride(q.q_d, q.q_m),
+              gs = fc_sample_stride(q.g_d, q.g_m);
+    dma = dma && std::max({ps, qs, gs}) <= 64 * kFcDwDmaJ && kFcDwDmaElems / (ps + qs + gs) >= 4;
+  }
+  if (dma) {
+    for (auto& q : h->dw) {
+      const int per = fc_sample_stride(q.p_d, q.p_m) + fc_sample_stride(q.q_d, q.q_m) +
+                      fc_sample_stride(q.g_d, q.g_m);
+      q.ts = std::min(kFcDwSamples, kFcDwDmaElems / per) & ~3;
+    }
+    h->dw_lds = 0;
+  }
+  h->dw_dma = dma;
   return SEGPOLY_OK;
 }
 
@@ -666,6 +685,7 @@ int fctp_bwd(fctp_handle h, const void* x1, const void* x2, const void* w, const
     a.ents = reinterpret_cast<const FcEnt*>(db + h->ent_off);
     a.nt = h->dw_nt;
     a.lds_bytes = h->dw_lds;
+    a.dma = h->dw_dma ? 1 : 0;
     a.dtype = h->dtype;
     a.layout = h->layout;
     a.stream = stream;

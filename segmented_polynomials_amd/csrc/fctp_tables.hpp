@@ -91,6 +91,13 @@ struct FcDwPath {
   int col_tiles;            // tiles of kFcDwCols columns w
 };
 
+// Float weight-gradient staging straight into LDS: two static buffers of
+// kFcDwDmaElems floats per workgroup (the group being multiplied and the
+// next), and at most kFcDwDmaJ dword copies per lane for one staged sample
+// of a block (sample strides up to 64 kFcDwDmaJ floats).
+constexpr int kFcDwDmaElems = 4096;
+constexpr int kFcDwDmaJ = 2;
+
 constexpr int kFcDwU = 8;        // P channels per weight-gradient tile (2 per wave)
 constexpr int kFcDwV = 32;       // Q channels per weight-gradient tile
 constexpr int kFcDwCols = 32;    // output channels per weight-gradient tile
@@ -135,6 +142,7 @@ struct FcDwArgs {
   const FcEnt* ents;
   int nt;                   // entry class (fc_t_class)
   size_t lds_bytes;
+  int dma;                  // stage through the static LDS-direct buffers (float only)
   int dtype, layout;
   void* stream;
 };

@@ -467,19 +467,17 @@ __device__ __forceinline__ void fc_dw_tile(const FcDwPath& P, const FcEnt* __res
       cf[e] = static_cast<T>(E.c);
     }
   }
-  // this lane's channels (clamped reads; invalid ones contribute zero)
-  bool pok[2], qok[2];
-  int pu[2], qv[2];
+  // This lane's channels, clamped into the staged rows.  A channel p or q
+  // past the block only feeds rows of the result, and a column w past it
+  // only columns, that are never written, so the values need no zeroing.
+  int pu[2], qv[2], gc[kNT];
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
-    pok[i] = u0 + i < P.p_m;
-    pu[i] = pok[i] ? u0 + i : 0;
-    qok[i] = v0 + 16 * i + lane % 16 < P.q_m;
-    qv[i] = qok[i] ? v0 + 16 * i + lane % 16 : 0;
+    pu[i] = u0 + i < P.p_m ? u0 + i : 0;
+    qv[i] = v0 + 16 * i + lane % 16 < P.q_m ? v0 + 16 * i + lane % 16 : 0;
   }
-  bool gok[kNT];
 #pragma unroll
-  for (int j = 0; j < kNT; ++j) gok[j] = col + 16 * j < P.g_m;
+  for (int j = 0; j < kNT; ++j) gc[j] = k * gcs + (col + 16 * j < P.g_m ? col + 16 * j : 0);
   for (int s4 = 0; s4 < nsp; s4 += 4) {
     const int s = s4 + lane / 16;
     T y[2][NT], z[2][NT];
@@ -487,13 +485,13 @@ __device__ __forceinline__ void fc_dw_tile(const FcDwPath& P, const FcEnt* __res
     for (int e = 0; e < NT; ++e) {
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
-        y[i][e] = pok[i] ? cf[e] * Ps[s * pss + pa[e] + pu[i]] : T(0);
-        z[i][e] = qok[i] ? Qs[s * qss + qb[e] + qv[i]] : T(0);
+        y[i][e] = cf[e] * Ps[s * pss + pa[e] + pu[i]];
+        z[i][e] = Qs[s * qss + qb[e] + qv[i]];
       }
     }
     T b[kNT];
 #pragma unroll
-    for (int j = 0; j < kNT; ++j) b[j] = gok[j] ? Gs[s * gss + k * gcs + col + 16 * j] : T(0);
+    for (int j = 0; j < kNT; ++j) b[j] = Gs[s * gss + gc[j]];
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -507,8 +505,58 @@ __device__ __forceinline__ void fc_dw_tile(const FcDwPath& P, const FcEnt* __res
   }
 }
 
-template <typename T, int LAYOUT, int NT>
-__global__ void __launch_bounds__(kFcThreads)
+// Weight-gradient staging straight into LDS (float): a lane's slots of
+// one staged sample of a block are r = 64 j + lane (j < kFcDwDmaJ), at
+// component r / (m + kFcPad) and channel r % (m + kFcPad); off[j] is the
+// element's offset in the block, 0 for pad slots (which are never read)
+// and -1 past the sample's stride (the lane copies nothing).
+template <int LAYOUT>
+__device__ __forceinline__ void fc_dw_dma_lanes(int bd, int bm, int lane, int (&off)[kFcDwDmaJ]) {
+  const int cstride = bm + kFcPad, sstride = fc_sample_stride(bd, bm);
+#pragma unroll
+  for (int j = 0; j < kFcDwDmaJ; ++j) {
+    const int r = 64 * j + lane;
+    const int a = r / cstride, u = r - a * cstride;
+    const int e = LAYOUT == kIrMul ? a * bm + u : u * bd + a;
+    off[j] = r >= sstride ? -1 : (a < bd && u < bm ? e : 0);
+  }
+}
+
+// Copy samples sb + s (s = wave, wave + 4, ... < nsp) of one block to
+// dst + s sstride with one dword global_load_lds per slot group; samples
+// at or past the chunk end are written as zeros.
+__device__ __forceinline__ void fc_dw_dma_issue(const float* __restrict__ src, int64_t sdim, int64_t boff,
+                                                int sstride, const int (&off)[kFcDwDmaJ], int64_t sb, int nsp,
+                                                int64_t n_end, float* dst, int wave, int lane) {
+  for (int s = wave; s < nsp; s += 4) {
+    float* d = dst + s * sstride;
+    if (sb + s < n_end) {
+      const float* g = src + (sb + s) * sdim + boff;
+#pragma unroll
+      for (int j = 0; j < kFcDwDmaJ; ++j)
+        if (off[j] >= 0)
+          __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(g + off[j]),
+                                           (__attribute__((address_space(3))) void*)(d + 64 * j), 4, 0, 0);
+    } else {
+#pragma unroll
+      for (int j = 0; j < kFcDwDmaJ; ++j)
+        if (off[j] >= 0) d[64 * j + lane] = 0.0f;
+    }
+  }
+}
+
+// Five weight-gradient workgroups per CU for the float kernels of up to
+// three couplings per component that stage through registers (they hide
+// each other's staging loads; four couplings would spill); four for those
+// that stage straight into LDS, so that nothing spills (a scratch reload
+// waits for every outstanding load, the copies of the next group too).
+template <typename T, int NT, bool DMA>
+constexpr int fc_dw_min_blocks() {
+  return (sizeof(T) == 4 && NT <= 3) ? (DMA ? 4 : 5) : 1;
+}
+
+template <typename T, int LAYOUT, int NT, bool DMA>
+__global__ void __launch_bounds__(kFcThreads, (fc_dw_min_blocks<T, NT, DMA>()))
 fctp_dw_kernel(const T* __restrict__ x1, const T* __restrict__ x2, const T* __restrict__ g, int64_t dim1,
                int64_t dim2, int64_t dimo, T* __restrict__ part, int64_t numel, int64_t n,
                const FcDwPath* __restrict__ paths, const FcEnt* __restrict__ ents, FcDwTiles tiles) {
@@ -547,6 +595,46 @@ fctp_dw_kernel(const T* __restrict__ x1, const T* __restrict__ x2, const T* __re
 #pragma unroll
     for (int j = 0; j < kNT; ++j) acc[r][j] = typename M::acc_t{0, 0, 0, 0};
 
+  if constexpr (DMA) {
+    // Double-buffered: the next group of samples is copied into the other
+    // static buffer while this one multiplies (two distinct LDS objects, so
+    // reads of one never wait for copies into the other).
+    __shared__ __align__(16) float Sb0[kFcDwDmaElems];
+    __shared__ __align__(16) float Sb1[kFcDwDmaElems];
+    const int wv = __builtin_amdgcn_readfirstlane(wave);
+    const int pss = fc_sample_stride(P.p_d, P.p_m), qss = fc_sample_stride(P.q_d, P.q_m),
+              gss = fc_sample_stride(P.g_d, P.g_m);
+    const int qbase = P.ts * pss, gbase = qbase + P.ts * qss;
+    int offp[kFcDwDmaJ], offq[kFcDwDmaJ], offg[kFcDwDmaJ];
+    fc_dw_dma_lanes<LAYOUT>(P.p_d, P.p_m, lane, offp);
+    fc_dw_dma_lanes<LAYOUT>(P.q_d, P.q_m, lane, offq);
+    fc_dw_dma_lanes<LAYOUT>(P.g_d, P.g_m, lane, offg);
+    auto group = [&](int64_t sb) {
+      const int ns = static_cast<int>(n_end - sb < P.ts ? n_end - sb : P.ts);
+      return (ns + 3) & ~3;  // staged samples (zero rows up to a multiple of 4)
+    };
+    auto issue = [&](int64_t sb, float* buf) {
+      const int nsp = group(sb);
+      fc_dw_dma_issue(Pg, pdim, P.p_off, pss, offp, sb, nsp, n_end, buf, wv, lane);
+      fc_dw_dma_issue(Qg, qdim, P.q_off, qss, offq, sb, nsp, n_end, buf + qbase, wv, lane);
+      fc_dw_dma_issue(g, dimo, P.g_off, gss, offg, sb, nsp, n_end, buf + gbase, wv, lane);
+    };
+    auto step = [&](int64_t sb, const float* cur, float* nxt) {
+      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+      __syncthreads();  // cur has landed; nxt is no longer read
+      if (sb + P.ts < n_end) issue(sb + P.ts, nxt);
+      if (wave_any) {
+        const int nsp = group(sb);
+        for (int k = 0; k < P.g_d; ++k)
+          fc_dw_tile<T, NT>(P, ents, cur, cur + qbase, cur + gbase, nsp, k, u0, v0, col, lane, acc);
+      }
+    };
+    issue(n_begin, Sb0);
+    for (int64_t sb = n_begin; sb < n_end; sb += 2 * P.ts) {
+      step(sb, Sb0, Sb1);
+      if (sb + P.ts < n_end) step(sb + P.ts, Sb1, Sb0);
+    }
+  } else {
   for (int64_t sb = n_begin; sb < n_end; sb += P.ts) {
     const int ns = static_cast<int>(n_end - sb < P.ts ? n_end - sb : P.ts);
     const int nsp = (ns + 3) & ~3;  // staged samples (zero rows up to a multiple of 4)
@@ -559,6 +647,7 @@ fctp_dw_kernel(const T* __restrict__ x1, const T* __restrict__ x2, const T* __re
     for (int k = 0; k < P.g_d; ++k) {
       fc_dw_tile<T, NT>(P, ents, Ps, Qs, Gs, nsp, k, u0, v0, col, lane, acc);
     }
+  }
   }
   if (!wave_any) return;
   // accumulator j of row tile (i, h): rows = the 16 q of half h for channel
@@ -670,15 +759,23 @@ int fctp_launch(const FcArgs& a, const FcTiles& t) {
   return a.tn == 32 ? fctp_launch_tn<T, LAYOUT, 32>(a, t) : fctp_launch_tn<T, LAYOUT, 64>(a, t);
 }
 
-template <typename T, int LAYOUT, int NT>
-int fctp_dw_launch_k(const FcDwArgs& a, const FcDwTiles& t) {
+template <typename T, int LAYOUT, int NT, bool DMA>
+int fctp_dw_launch_d(const FcDwArgs& a, const FcDwTiles& t) {
   const int total = t.tile_begin[t.n_paths];
   if (total == 0) return 0;
-  hipLaunchKernelGGL((fctp_dw_kernel<T, LAYOUT, NT>), dim3(static_cast<unsigned>(total)), dim3(kFcThreads),
+  hipLaunchKernelGGL((fctp_dw_kernel<T, LAYOUT, NT, DMA>), dim3(static_cast<unsigned>(total)), dim3(kFcThreads),
                      a.lds_bytes, static_cast<hipStream_t>(a.stream), static_cast<const T*>(a.x1),
                      static_cast<const T*>(a.x2), static_cast<const T*>(a.g), a.dim1, a.dim2, a.dimo,
                      static_cast<T*>(a.part), a.numel, a.n, a.paths, a.ents, t);
   return static_cast<int>(hipGetLastError());
+}
+
+template <typename T, int LAYOUT, int NT>
+int fctp_dw_launch_k(const FcDwArgs& a, const FcDwTiles& t) {
+  if constexpr (std::is_same_v<T, float>) {
+    if (a.dma) return fctp_dw_launch_d<T, LAYOUT, NT, true>(a, t);
+  }
+  return fctp_dw_launch_d<T, LAYOUT, NT, false>(a, t);
 }
 
 template <typename T, int LAYOUT>
