@@ -283,6 +283,10 @@ int build_dw(segpoly_fctp* h) {
     h->dw_lds = std::max(h->dw_lds, static_cast<size_t>(ts) * per);
     h->dw.push_back(q);
   }
+  // Paths whose output block has more components dispatch first: their
+  // workgroups do proportionally more work, and starting them early keeps
+  // the launch's tail short.
+  std::stable_sort(h->dw.begin(), h->dw.end(), [](const FcDwPath& x, const FcDwPath& y) { return x.g_d > y.g_d; });
   // Float launches stage through the LDS-direct buffers when every staged
   // sample fits the per-lane copies and four samples of the three blocks
   // fit one buffer.
