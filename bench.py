@@ -480,17 +480,18 @@ def linear_layers(torch, sp, workloads, dev, args):
                           "frac": tf / FP32_MFMA_PEAK_TFLOPS, "algorithmic_flops": flops},
              "hbm": {"achieved": nbytes / (kms * 1e-3) / 1e9, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "algorithmic_bytes": nbytes}}
-        if cls is None:
-            g = torch.from_numpy(workloads.output_gradient(wl.n, h.dim_out, "f32", seed=66)).to(dev)
-            ws = torch.empty(max(1, sp.linear_bwd_workspace(h, wl.n)), dtype=torch.uint8, device=dev)
-            fb = lambda: sp.linear_bwd(h, x, w, g, workspace=ws)
-            wallb, perb = time_launches(torch, fb, args.steps, args.warmup)
-            kb = sum(perb) / len(perb)
-            tfb = 2 * flops / (kb * 1e-3) / 1e12
-            r["backward"] = {"ms_per_call": kb, "roofline": {"bound": "mfma", "achieved": tfb,
-                                                            "peak": FP32_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
-                                                            "frac": tfb / FP32_MFMA_PEAK_TFLOPS}}
-            del g, ws
+        # backward: dx and dW (one weight row per class with classes)
+        nc = 0 if cls is None else w.shape[0]
+        g = torch.from_numpy(workloads.output_gradient(wl.n, h.dim_out, "f32", seed=66)).to(dev)
+        ws = torch.empty(max(1, sp.linear_bwd_workspace(h, wl.n, nc)), dtype=torch.uint8, device=dev)
+        fb = lambda: sp.linear_bwd(h, x, w, g, classes=cls, num_classes=nc or None, workspace=ws)
+        wallb, perb = time_launches(torch, fb, args.steps, args.warmup)
+        kb = sum(perb) / len(perb)
+        tfb = 2 * flops / (kb * 1e-3) / 1e12
+        r["backward"] = {"ms_per_call": kb, "roofline": {"bound": "mfma", "achieved": tfb,
+                                                        "peak": FP32_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                                                        "frac": tfb / FP32_MFMA_PEAK_TFLOPS}}
+        del g, ws
         res[wl.name] = r
         del x, w, out, cls
     return res

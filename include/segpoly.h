@@ -369,18 +369,25 @@ int linear_fwd(linear_handle h, const void* x, const void* w, const void* classe
                int64_t n, void* out, void* stream);
 
 /* linear_bwd_workspace: bytes of workspace linear_bwd needs for the weight
- * gradient of n samples (per-chunk partial sums). */
-int linear_bwd_workspace(linear_handle h, int64_t n, size_t* bytes);
+ * gradient of n samples: per-chunk partial sums, for each of num_classes
+ * weight rows with class-indexed weights (then also two int32 per row
+ * chunk: the classes it holds); num_classes = 0 for shared weights. */
+int linear_bwd_workspace(linear_handle h, int64_t n, int num_classes, size_t* bytes);
 
 /*
  * linear_bwd: vector-Jacobian product of linear_fwd for g = dL/d(out):
  *   grad_x[n, i, m, u] = alpha_t sum over pairs (i, o) of sum_v W_io[u, v] g[n, o, m, v]
  *   grad_w[W_io][u, v] = alpha_t sum over samples n and components m of x[n, i, m, u] g[n, o, m, v]
- * grad_x [n, DIM_IN] is fully overwritten.  grad_w [1, WEIGHT_NUMEL] may be
- * NULL (not computed; x and the workspace are then not used); with
- * `classes` it must be NULL (E_UNSUPPORTED otherwise).  The weight gradient
- * sums fixed chunks of 2048 rows and then the chunks in order:
- * deterministic.  Other arguments as linear_fwd.
+ * grad_x [n, DIM_IN] is fully overwritten.  grad_w [1, WEIGHT_NUMEL], or
+ * [num_classes, WEIGHT_NUMEL] with `classes` (row c sums over the samples
+ * of class c; samples of a class outside [0, num_classes) add nothing),
+ * fully overwritten, may be NULL (not computed; x and the workspace are
+ * then not used).  The weight gradient sums fixed chunks of 2048 rows and
+ * then the chunks in order: deterministic.  With classes each chunk makes
+ * one pass per class between its lowest and highest class (sorted classes:
+ * one or two passes; at most 65535 classes, E_UNSUPPORTED beyond).  The
+ * workspace holds linear_bwd_workspace(n, classes ? num_classes : 0)
+ * bytes.  Other arguments as linear_fwd.
  */
 int linear_bwd(linear_handle h, const void* x, const void* w, const void* grad_out, const void* classes,
                int idx_dtype, int num_classes, int64_t n, void* grad_x, void* grad_w, void* workspace,

@@ -92,7 +92,7 @@ def _load():
         "linear_create": [ctypes.c_char_p, ctypes.c_char_p, c_int, c_int, c_uint, ctypes.POINTER(vp)],
         "linear_query": [vp, c_int, p64],
         "linear_fwd": [vp, vp, vp, vp, c_int, c_int, i64, vp, vp],
-        "linear_bwd_workspace": [vp, i64, ctypes.POINTER(ctypes.c_size_t)],
+        "linear_bwd_workspace": [vp, i64, ctypes.c_int, ctypes.POINTER(ctypes.c_size_t)],
         "linear_bwd": [vp, vp, vp, vp, vp, c_int, c_int, i64, vp, vp, vp, ctypes.c_size_t, vp],
         "linear_destroy": [vp],
         "fctp_create": [ctypes.c_char_p, ctypes.c_char_p, ctypes.c_char_p, c_int, c_int, c_uint, ctypes.POINTER(vp)],
@@ -528,15 +528,16 @@ def linear_fwd(h, x, w, classes=None, num_classes=None, out=None):
     return out
 
 
-def linear_bwd_workspace(h, n):
+def linear_bwd_workspace(h, n, num_classes=0):
     v = ctypes.c_size_t()
-    _check(lib.linear_bwd_workspace(h._h, n, ctypes.byref(v)))
+    _check(lib.linear_bwd_workspace(h._h, n, num_classes, ctypes.byref(v)))
     return v.value
 
 
 def linear_bwd(h, x, w, grad_out, classes=None, num_classes=None, need_dw=True, workspace=None):
     """Gradients (grad_x, grad_w or None) of ``linear_fwd`` for ``grad_out``
-    [n, dim_out]; the weight gradient needs shared weights."""
+    [n, dim_out]; grad_w is shaped like w (one row per class with
+    ``classes``)."""
     import torch
     t, n, idx, nc = _lin_common(h, x, w, classes, num_classes)
     if grad_out.shape != (n, h.dim_out) or grad_out.dtype != t or not grad_out.is_contiguous():
@@ -544,7 +545,8 @@ def linear_bwd(h, x, w, grad_out, classes=None, num_classes=None, need_dw=True, 
     gx = torch.empty_like(x)
     gw = torch.empty_like(w) if need_dw else None
     if need_dw and workspace is None:
-        workspace = torch.empty(max(1, linear_bwd_workspace(h, n)), dtype=torch.uint8, device=x.device)
+        workspace = torch.empty(max(1, linear_bwd_workspace(h, n, nc if classes is not None else 0)),
+                                dtype=torch.uint8, device=x.device)
     wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib.linear_bwd(h._h, _ptr(x), _ptr(w), _ptr(grad_out), _ptr(classes), idx, nc, n, _ptr(gx), _ptr(gw),
                           _ptr(workspace), wbytes, _stream_ptr(x.device)))

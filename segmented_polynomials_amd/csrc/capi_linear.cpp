@@ -62,8 +62,8 @@ void fill_tiles(LinTable& t, const std::vector<Irrep>& blocks, int64_t n) {
   t.total_tiles = static_cast<int>(acc);
 }
 
-int64_t fill_dw_tiles(LinDwTable& t, int64_t n) {
-  int64_t tiles = 0, part = 0;
+int64_t fill_dw_tiles(LinDwTable& t, int64_t n, int64_t* n_chunks = nullptr) {
+  int64_t tiles = 0, part = 0, chunks = 0;
   for (int p = 0; p < t.n_pairs; ++p) {
     LinDwPair& P = t.pairs[p];
     const int64_t rows = n * P.d;
@@ -72,11 +72,26 @@ int64_t fill_dw_tiles(LinDwTable& t, int64_t n) {
     P.v_tiles = (P.mul_out + kLinTN - 1) / kLinTN;
     P.tile_begin = static_cast<int>(tiles);
     P.part_off = part;
+    P.range_off = chunks;
     tiles += static_cast<int64_t>(P.chunks) * P.u_tiles * P.v_tiles;
     part += static_cast<int64_t>(P.chunks) * P.mul_in * P.mul_out;
+    chunks += P.chunks;
   }
   t.total_tiles = static_cast<int>(tiles);
-  return part;  // elements of partials
+  if (n_chunks) *n_chunks = chunks;
+  return part;  // elements of partials (of one class)
+}
+
+// Workspace of the weight gradient: the partials of every class, then two
+// int32 (first and last class present) per row chunk with classes.
+size_t dw_workspace_bytes(const segpoly_linear* h, int64_t n, int num_classes) {
+  LinDwTable t = h->dw;
+  int64_t chunks = 0;
+  const int64_t part = fill_dw_tiles(t, n, &chunks);
+  if (part == 0) return 0;
+  const size_t elt = h->dtype == SEGPOLY_F32 ? 4 : 8;
+  if (num_classes <= 0) return static_cast<size_t>(part) * elt;
+  return static_cast<size_t>(part) * num_classes * elt + static_cast<size_t>(chunks) * 2 * sizeof(int32_t);
 }
 
 bool tiles_fit(int64_t n, const segpoly_linear* h) {
@@ -256,12 +271,10 @@ int linear_fwd(linear_handle h, const void* x, const void* w, const void* classe
   return ok();
 }
 
-int linear_bwd_workspace(linear_handle h, int64_t n, size_t* bytes) {
+int linear_bwd_workspace(linear_handle h, int64_t n, int num_classes, size_t* bytes) {
   if (!h || !bytes) return fail(SEGPOLY_E_INVALID, "null argument");
-  if (n < 0) return fail(SEGPOLY_E_INVALID, "negative size");
-  LinDwTable t = h->dw;
-  const int64_t part = fill_dw_tiles(t, n);
-  *bytes = static_cast<size_t>(part) * (h->dtype == SEGPOLY_F32 ? 4 : 8);
+  if (n < 0 || num_classes < 0) return fail(SEGPOLY_E_INVALID, "negative size");
+  *bytes = dw_workspace_bytes(h, n, num_classes);
   return ok();
 }
 
@@ -272,15 +285,15 @@ int linear_bwd(linear_handle h, const void* x, const void* w, const void* grad_o
   if (n < 0) return fail(SEGPOLY_E_INVALID, "negative size");
   if (idx_dtype != SEGPOLY_I32 && idx_dtype != SEGPOLY_I64) return fail(SEGPOLY_E_INVALID, "bad index dtype");
   if (classes && num_classes < 1) return fail(SEGPOLY_E_INVALID, "num_classes must be >= 1 with classes");
-  if (classes && grad_w)
-    return fail(SEGPOLY_E_UNSUPPORTED, "the weight gradient of class-indexed weights is not supported");
+  if (classes && grad_w && num_classes > 65535)
+    return fail(SEGPOLY_E_UNSUPPORTED, "more than 65535 classes for the weight gradient");
   if (!tiles_fit(n, h)) return fail(SEGPOLY_E_UNSUPPORTED, "too many rows for one launch");
   if (n > 0 && (!grad_x || !grad_out || (h->numel > 0 && !w) || (grad_w && h->dim_in > 0 && !x)))
     return fail(SEGPOLY_E_INVALID, "null pointer");
   LinDwTable dt = h->dw;
   const int64_t part = fill_dw_tiles(dt, n);
-  if (grad_w && part > 0 &&
-      (!workspace || workspace_bytes < static_cast<size_t>(part) * (h->dtype == SEGPOLY_F32 ? 4 : 8)))
+  const size_t need = dw_workspace_bytes(h, n, classes ? num_classes : 0);
+  if (grad_w && need > 0 && (!workspace || workspace_bytes < need))
     return fail(SEGPOLY_E_INVALID, "workspace missing or smaller than linear_bwd_workspace()");
   if (classes && (h->flags & SEGPOLY_VALIDATE) && n > 0) {
     int st = idx_dtype == SEGPOLY_I32 ? check_classes<int32_t>(classes, n, num_classes, stream)
@@ -309,19 +322,24 @@ int linear_bwd(linear_handle h, const void* x, const void* w, const void* grad_o
     rc = launch_linear(a, t, true);
   }
   if (rc == 0 && grad_w && h->numel > 0) {
+    const int nc = classes ? num_classes : 1;
     if (n == 0) {
-      rc = launch_fill_zero(grad_w, h->numel, h->dtype, stream);
+      rc = launch_fill_zero(grad_w, h->numel * nc, h->dtype, stream);
     } else {
       LinearDwArgs d{};
       d.x = x;
       d.g = grad_out;
+      d.cls = classes;
       d.dw = grad_w;
       d.workspace = workspace;
       d.n = n;
       d.dim_in = h->dim_in;
       d.dim_out = h->dim_out;
       d.numel = h->numel;
+      d.part = part;
+      d.num_classes = nc;
       d.dtype = h->dtype;
+      d.idx = idx_dtype;
       d.layout = h->layout;
       d.stream = stream;
       rc = launch_linear_dw(d, dt);

@@ -214,10 +214,17 @@ linear_kernel(const T* __restrict__ x, const T* __restrict__ w, const Index* __r
 // Weight gradient of one pair, one (64 u x 128 v) tile and one chunk of
 // kLinDwRows rows: part[chunk][u][v] = sum over the chunk's rows (n, m) of
 // x[n, i, m, u] g[n, o, m, v] (A = x^T staged as [u][row], B = g as [row][v]).
-template <typename T, int LAYOUT>
+// With class-indexed weights (CLS) the workgroup first finds the lowest and
+// highest class among the chunk's samples (recorded in `ranges` by the
+// chunk's first tile) and makes one pass per class in that range, rows of
+// other classes (and classes outside [0, num_classes)) masked to zero:
+// part[c][chunk][u][v], part_class elements apart.  Sorted classes give one
+// or two passes per chunk; any order is correct.
+template <typename T, int LAYOUT, bool CLS, typename Index>
 __global__ void __launch_bounds__(kLinThreads)
 linear_dw_kernel(const T* __restrict__ x, const T* __restrict__ g, T* __restrict__ part, int64_t n, int64_t dim_in,
-                 int64_t dim_out, LinDwTable tab) {
+                 int64_t dim_out, LinDwTable tab, const Index* __restrict__ cls, int num_classes,
+                 int64_t part_class, int* __restrict__ ranges) {
   using M = Mfma<T>;
   __shared__ T As[kLinTM][kLinTK + kLinPadA];   // [u][row]
   __shared__ T Bs[kLinTK][kLinTN + kLinPadB];   // [row][v]
@@ -241,17 +248,55 @@ linear_dw_kernel(const T* __restrict__ x, const T* __restrict__ g, T* __restrict
   constexpr int kBStep = kLinThreads / kLinTN;   // rows of B per pass (2)
   const int uu_a = tid % kLinTM, rk_a = tid / kLinTM;
   const int vv_b = tid % kLinTN, rk_b = tid / kLinTN;
-  int a_n = (r_begin + rk_a) / d, a_m = (r_begin + rk_a) - a_n * d;
-  int b_n = (r_begin + rk_b) / d, b_m = (r_begin + rk_b) - b_n * d;
+  int c_lo = 0, c_hi = 0;
+  if constexpr (CLS) {
+    const int s_begin = r_begin / d, s_end = (r_end - 1) / d + 1;
+    int lo = num_classes, hi = -1;
+    for (int sm = s_begin + tid; sm < s_end; sm += kLinThreads) {
+      const int64_t c = static_cast<int64_t>(cls[sm]);
+      if (c >= 0 && c < num_classes) {
+        lo = static_cast<int>(c) < lo ? static_cast<int>(c) : lo;
+        hi = static_cast<int>(c) > hi ? static_cast<int>(c) : hi;
+      }
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      const int l2 = __shfl_xor(lo, o), h2 = __shfl_xor(hi, o);
+      lo = l2 < lo ? l2 : lo;
+      hi = h2 > hi ? h2 : hi;
+    }
+    __shared__ int red[2][kLinThreads / 64];
+    if (lane == 0) {
+      red[0][wave] = lo;
+      red[1][wave] = hi;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < kLinThreads / 64; ++k) {
+      lo = red[0][k] < lo ? red[0][k] : lo;
+      hi = red[1][k] > hi ? red[1][k] : hi;
+    }
+    c_lo = lo;
+    c_hi = hi;
+    if (t == 0 && tid == 0) {
+      ranges[2 * (P.range_off + chunk)] = lo;
+      ranges[2 * (P.range_off + chunk) + 1] = hi;
+    }
+  }
   const int step_n = kLinTK / d, step_m = kLinTK - step_n * d;      // divmod(kLinTK, d)
   const int sa_n = kAStep / d, sa_m = kAStep - sa_n * d;            // divmod(kAStep, d)
   const int sb_n = kBStep / d, sb_m = kBStep - sb_n * d;            // divmod(kBStep, d)
+  const int u = u0 + uu_a, v = v0 + vv_b;
+  for (int cc = c_lo; cc <= c_hi; ++cc) {
+  int a_n = (r_begin + rk_a) / d, a_m = (r_begin + rk_a) - a_n * d;
+  int b_n = (r_begin + rk_b) / d, b_m = (r_begin + rk_b) - b_n * d;
+  // rows of another class than cc contribute nothing
+  auto in_class = [&](int nn) { return !CLS || static_cast<int64_t>(cls[nn]) == cc; };
   typename M::acc_t acc[kMT][kNT];
 #pragma unroll
   for (int a = 0; a < kMT; ++a)
 #pragma unroll
     for (int b = 0; b < kNT; ++b) acc[a][b] = typename M::acc_t{0, 0, 0, 0};
-  const int u = u0 + uu_a, v = v0 + vv_b;
   // the next chunk of rows is loaded into registers while the current one
   // is multiplied
   T ra[kLinTK / kAStep], rb[kLinTK / kBStep];
@@ -261,7 +306,7 @@ linear_dw_kernel(const T* __restrict__ x, const T* __restrict__ g, T* __restrict
     for (int e = 0; e < kLinTK / kAStep; ++e) {
       const int row = k0 + rk_a + e * kAStep;
       T val = T(0);
-      if (row < r_end && u < P.mul_in) {
+      if (row < r_end && u < P.mul_in && in_class(nn)) {
         const int64_t off = LAYOUT == kIrMul ? P.x_off + static_cast<int64_t>(m) * P.mul_in + u
                                              : P.x_off + static_cast<int64_t>(u) * d + m;
         val = x[static_cast<int64_t>(nn) * dim_in + off];
@@ -280,7 +325,7 @@ linear_dw_kernel(const T* __restrict__ x, const T* __restrict__ g, T* __restrict
     for (int e = 0; e < kLinTK / kBStep; ++e) {
       const int row = k0 + rk_b + e * kBStep;
       T val = T(0);
-      if (row < r_end && v < P.mul_out) {
+      if (row < r_end && v < P.mul_out && in_class(nn)) {
         const int64_t off = LAYOUT == kIrMul ? P.g_off + static_cast<int64_t>(m) * P.mul_out + v
                                              : P.g_off + static_cast<int64_t>(v) * d + m;
         val = g[static_cast<int64_t>(nn) * dim_out + off];
@@ -332,7 +377,7 @@ linear_dw_kernel(const T* __restrict__ x, const T* __restrict__ g, T* __restrict
         for (int j = 0; j < kNT; ++j) acc[i][j] = M::mma(a[i], b[j], acc[i][j]);
     }
   }
-  T* prow = part + P.part_off + static_cast<int64_t>(chunk) * P.mul_in * P.mul_out;
+  T* prow = part + (CLS ? cc * part_class : 0) + P.part_off + static_cast<int64_t>(chunk) * P.mul_in * P.mul_out;
 #pragma unroll
   for (int i = 0; i < kMT; ++i)
 #pragma unroll
@@ -343,36 +388,56 @@ linear_dw_kernel(const T* __restrict__ x, const T* __restrict__ g, T* __restrict
         const int vo = v0 + wc * (kLinTN / 2) + j * 16 + lane % 16;
         if (uo < P.mul_in && vo < P.mul_out) prow[static_cast<int64_t>(uo) * P.mul_out + vo] = acc[i][j][q];
       }
+  }
 }
 
-// dw[w_off + e] = alpha * sum over the pair's chunks (in order) of part[chunk][e].
-template <typename T>
+// dw[c][w_off + e] = alpha * sum over the pair's chunks (in order) of
+// part[c][chunk][e]; with classes (CLS, class c = blockIdx.z) only the
+// chunks whose class range holds c have written that partial.
+template <typename T, bool CLS>
 __global__ void __launch_bounds__(256)
-linear_dw_fold_kernel(const T* __restrict__ part, LinDwTable tab, T* __restrict__ dw) {
-  const int pi = blockIdx.y;
+linear_dw_fold_kernel(const T* __restrict__ part, LinDwTable tab, T* __restrict__ dw, int64_t part_class,
+                      int64_t numel, const int* __restrict__ ranges) {
+  const int pi = blockIdx.y, c = blockIdx.z;
   const LinDwPair P = tab.pairs[pi];
   const int64_t sz = static_cast<int64_t>(P.mul_in) * P.mul_out;
+  const T* pc = part + c * part_class + P.part_off;
   for (int64_t e = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; e < sz;
        e += static_cast<int64_t>(gridDim.x) * blockDim.x) {
     T acc = T(0);
-    for (int c = 0; c < P.chunks; ++c) acc += part[P.part_off + c * sz + e];
-    dw[P.w_off + e] = static_cast<T>(P.alpha) * acc;
+    for (int k = 0; k < P.chunks; ++k) {
+      if constexpr (CLS) {
+        const int lo = ranges[2 * (P.range_off + k)], hi = ranges[2 * (P.range_off + k) + 1];
+        if (c < lo || c > hi) continue;
+      }
+      acc += pc[k * sz + e];
+    }
+    dw[c * numel + P.w_off + e] = static_cast<T>(P.alpha) * acc;
   }
+}
+
+template <typename T, int LAYOUT, bool CLS, typename Index>
+int linear_dw_launch_c(const LinearDwArgs& a, const LinDwTable& tab) {
+  const hipStream_t st = static_cast<hipStream_t>(a.stream);
+  T* part = static_cast<T*>(a.workspace);
+  const int nc = CLS ? a.num_classes : 1;
+  int* ranges = CLS ? reinterpret_cast<int*>(part + a.part * nc) : nullptr;
+  if (tab.total_tiles > 0)
+    hipLaunchKernelGGL((linear_dw_kernel<T, LAYOUT, CLS, Index>), dim3(static_cast<unsigned>(tab.total_tiles)),
+                       dim3(kLinThreads), 0, st, static_cast<const T*>(a.x), static_cast<const T*>(a.g), part, a.n,
+                       a.dim_in, a.dim_out, tab, static_cast<const Index*>(a.cls), nc, a.part, ranges);
+  int rc = static_cast<int>(hipGetLastError());
+  if (rc || tab.n_pairs == 0) return rc;
+  hipLaunchKernelGGL((linear_dw_fold_kernel<T, CLS>), dim3(64, static_cast<unsigned>(tab.n_pairs), nc), dim3(256), 0,
+                     st, static_cast<const T*>(part), tab, static_cast<T*>(a.dw), a.part, a.numel, ranges);
+  return static_cast<int>(hipGetLastError());
 }
 
 template <typename T, int LAYOUT>
 int linear_dw_launch(const LinearDwArgs& a, const LinDwTable& tab) {
-  const hipStream_t st = static_cast<hipStream_t>(a.stream);
-  T* part = static_cast<T*>(a.workspace);
-  if (tab.total_tiles > 0)
-    hipLaunchKernelGGL((linear_dw_kernel<T, LAYOUT>), dim3(static_cast<unsigned>(tab.total_tiles)), dim3(kLinThreads),
-                       0, st, static_cast<const T*>(a.x), static_cast<const T*>(a.g), part, a.n, a.dim_in, a.dim_out,
-                       tab);
-  int rc = static_cast<int>(hipGetLastError());
-  if (rc || tab.n_pairs == 0) return rc;
-  hipLaunchKernelGGL((linear_dw_fold_kernel<T>), dim3(64, static_cast<unsigned>(tab.n_pairs)), dim3(256), 0, st,
-                     static_cast<const T*>(part), tab, static_cast<T*>(a.dw));
-  return static_cast<int>(hipGetLastError());
+  if (!a.cls) return linear_dw_launch_c<T, LAYOUT, false, int32_t>(a, tab);
+  return a.idx == kI32 ? linear_dw_launch_c<T, LAYOUT, true, int32_t>(a, tab)
+                       : linear_dw_launch_c<T, LAYOUT, true, int64_t>(a, tab);
 }
 
 template <typename T, typename Index, int LAYOUT, bool TRANSW>

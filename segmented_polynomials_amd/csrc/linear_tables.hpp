@@ -46,6 +46,7 @@ struct LinDwPair {
   int mul_in, mul_out, d;
   int chunks;            // row chunks of this pair
   int64_t part_off;      // first element of its partials in the workspace
+  int64_t range_off;     // first chunk of its class ranges (class-indexed weights)
   int tile_begin;        // first workgroup
   int u_tiles, v_tiles;  // tiles of mul_in x mul_out
   double alpha;
@@ -72,12 +73,15 @@ struct LinearArgs {
 };
 
 struct LinearDwArgs {
-  const void* x;  // [n, dim_in] forward input
-  const void* g;  // [n, dim_out] output gradient
-  void* dw;       // [numel]
-  void* workspace;
+  const void* x;    // [n, dim_in] forward input
+  const void* g;    // [n, dim_out] output gradient
+  const void* cls;  // [n] class of each sample, or null (shared weights)
+  void* dw;         // [num_classes, numel]
+  void* workspace;  // partials [num_classes][part], then the chunks' class ranges
   int64_t n, dim_in, dim_out, numel;
-  int dtype, layout;
+  int64_t part;     // partial elements of one class (fill_dw_tiles)
+  int num_classes;  // 1 without classes
+  int dtype, idx, layout;
   void* stream;
 };
 

@@ -275,8 +275,14 @@ def test_linear_descriptor_and_errors():
     assert f(h._h, p, p, None, 0, 1, 2, None, None) == sp.E_INVALID    # null out
     assert f(h._h, None, None, None, 0, 1, 0, None, None) == sp.OK     # nothing to do
     b = sp.lib.linear_bwd
-    assert b(h._h, p, p, p, p, 0, 2, 2, p, p, p, 1 << 30, None) == sp.E_UNSUPPORTED   # dw with classes
+    assert b(h._h, p, p, p, p, 0, 70000, 2, p, p, p, 1 << 30, None) == sp.E_UNSUPPORTED  # dw, too many classes
     assert b(h._h, p, p, p, None, 0, 1, 2, p, p, p, 8, None) == sp.E_INVALID          # workspace small
+    assert b(h._h, p, p, p, p, 0, 3, 2, p, p, p, 8, None) == sp.E_INVALID             # same with classes
+    # class-indexed weight gradient: one set of partials per class and two
+    # int32 class bounds per row chunk
+    w0, w3 = sp.linear_bwd_workspace(h, 5000, 0), sp.linear_bwd_workspace(h, 5000, 3)
+    assert w0 > 0 and w3 > 3 * w0 and (w3 - 3 * w0) % 8 == 0
+    assert sp.linear_bwd_workspace(h, 0, 3) == 0
 
 
 @pytest.mark.parametrize("a,b,c", [("0 + 1", "0 + 1", "0 + 1"), ("32x0e+32x1o", "32x0e+32x1o", "32x0e+32x1o"),

@@ -115,32 +115,39 @@ def test_ragged_tiles(layout):
     check_scaled(gw, rw, sw, "f32", "ragged dw")
 
 
+@pytest.mark.parametrize("n", [400, 3000])
 @pytest.mark.parametrize("order", ["sorted", "unsorted"])
-def test_class_indexed(order):
+def test_class_indexed(order, n):
     """Species-indexed weights: sorted classes (the pages' contract) and an
     unsorted order (still exact), an out-of-range class (zero row, zero
-    dx), int64 indices for the unsorted case."""
+    dx, no weight-gradient contribution), int64 indices for the unsorted
+    case; 3000 samples span several row chunks of the weight gradient."""
     sp = _sp()
     wl = workloads.WORKLOADS[7]
     o = olin.Linear(wl.irreps_in, wl.irreps_out)
     h = sp.linear_create(wl.irreps_in, wl.irreps_out, layout="ir_mul")
-    inp = workloads.linear_inputs(wl, o.weight_numel, n=400)
+    inp = workloads.linear_inputs(wl, o.weight_numel, n=n)
     cls = inp["classes"].copy()
     if order == "unsorted":
         cls = np.random.default_rng(3).permutation(cls).astype(np.int64)
     cls[5] = wl.num_classes          # out of range
-    g = workloads.output_gradient(400, o.dim_out, "f32", seed=71)
-    announce(f"linear class-indexed {order}")
+    g = workloads.output_gradient(n, o.dim_out, "f32", seed=71)
+    announce(f"linear class-indexed {order} n={n}")
     got = _fwd(sp, h, inp["x"], inp["w"], cls)
     check_scaled(got, o.fwd(inp["x"], inp["w"], indices=cls), o.fwd(inp["x"], inp["w"], indices=cls, absolute=True),
                  "f32", f"class-indexed fwd {order}")
     assert np.count_nonzero(got[5]) == 0
     gx, gw = _bwd(sp, h, inp["x"], inp["w"], g, cls, need_dw=False)
     assert gw is None
-    rx, _ = o.vjp(inp["x"], inp["w"], g, indices=cls)
-    sx, _ = o.vjp(inp["x"], inp["w"], g, indices=cls, absolute=True)
+    rx, rw = o.vjp(inp["x"], inp["w"], g, indices=cls)
+    sx, sw = o.vjp(inp["x"], inp["w"], g, indices=cls, absolute=True)
     check_scaled(gx, rx, sx, "f32", f"class-indexed dx {order}")
     assert np.count_nonzero(gx[5]) == 0
+    # weight gradient: one row per class, each summing its own samples
+    gx2, gw = _bwd(sp, h, inp["x"], inp["w"], g, cls)
+    assert gw.shape == inp["w"].shape
+    assert np.array_equal(gx2, gx)
+    check_scaled(gw, rw, sw, "f32", f"class-indexed dw {order}")
 
 
 def test_float64_backward_and_determinism():
