@@ -179,7 +179,10 @@ int tp_conv_fwd(tp_handle h, const void* x, int64_t n_src, const void* sh, const
  * one source message per edge (n_edges * DIM_IN1 elements of the handle's
  * dtype, indexed mode only), rounded up to 256 bytes, plus, when the
  * multiplicity exceeds 64, ceil(mul / 64) * n_edges * DIM_IN2 elements of
- * per-tile harmonic-gradient partials.  0 means no workspace is needed.
+ * per-tile harmonic-gradient partials; with SEGPOLY_SHARED_WEIGHTS then,
+ * each part 256-byte aligned, n_edges * WEIGHT_NUMEL per-edge weight
+ * gradients and ceil(n_edges / 1024) * WEIGHT_NUMEL partial sums of them.
+ * 0 means no workspace is needed.
  */
 int tp_conv_bwd_workspace(tp_handle h, int64_t n_edges, int batch, size_t* bytes);
 
@@ -201,8 +204,7 @@ int tp_conv_bwd_workspace(tp_handle h, int64_t n_edges, int batch, size_t* bytes
  * source or destination lies outside its range get zero gradients and add
  * nothing to grad_x (for an out-of-range source: given finite sh and
  * grad_out, since its x and w enter as zeros).
- *   x, sh, w, src, dst, idx_dtype, n_src, n_edges, n_nodes: as tp_conv_fwd
- *              (per-edge weights only).
+ *   x, sh, w, src, dst, idx_dtype, n_src, n_edges, n_nodes: as tp_conv_fwd.
  *   src_perm   [n_edges] device, idx_dtype: the edge ids ordered by src
  *              ascending (a stable argsort of src: the order within one
  *              source is the order in which its messages are summed, so a
@@ -211,14 +213,17 @@ int tp_conv_bwd_workspace(tp_handle h, int64_t n_edges, int batch, size_t* bytes
  *              in batch mode.
  *   grad_out   [n_nodes, DIM_OUT] device, layout of the handle.
  *   grad_x     [n_src, DIM_IN1] device.  grad_sh [n_edges, DIM_IN2] device.
- *   grad_w     [n_edges, WEIGHT_NUMEL] device.
+ *   grad_w     [n_edges, WEIGHT_NUMEL] device; with SEGPOLY_SHARED_WEIGHTS
+ *              [1, WEIGHT_NUMEL], the sum over the edges of their
+ *              per-edge gradients (written to the workspace, summed in
+ *              fixed chunks of 1024 edges, then the chunks in order).
  *   workspace  device, at least tp_conv_bwd_workspace() bytes, 256-byte
  *              aligned; may be NULL when that size is 0.  Its contents on
  *              entry do not matter.
  * Two to three launches on `stream`, no atomics: results are deterministic
- * (bitwise, for fixed inputs and src_perm).  Fails closed with
- * E_UNSUPPORTED for shared weights and for a descriptor without a
- * specialised kernel.  Sizes: n_nodes, n_src < 2^31.
+ * (bitwise, for fixed inputs and src_perm); two more with shared weights.
+ * Fails closed with E_UNSUPPORTED for a descriptor without a specialised
+ * kernel.  Sizes: n_nodes, n_src < 2^31.
  */
 int tp_conv_bwd(tp_handle h, const void* x, int64_t n_src, const void* sh, const void* w, const void* src,
                 const void* dst, const void* src_perm, int idx_dtype, int64_t n_edges, int64_t n_nodes,

@@ -323,8 +323,9 @@ def tp_conv_bwd(h, x, sh, w, grad_out, src=None, dst=None, src_perm=None, n_node
         if a.dtype != t or not a.is_cuda or not a.is_contiguous():
             raise ValueError(f"{name} must be a contiguous {t} device tensor")
     n_src, n_edges = x.shape[0], sh.shape[0]
-    if x.shape[1] != h.dim_in1 or sh.shape[1] != h.dim_in2 or w.shape != (n_edges, h.weight_numel):
-        raise ValueError("operand widths do not match the descriptor")
+    w_rows = 1 if h.shared_weights else n_edges
+    if x.shape[1] != h.dim_in1 or sh.shape[1] != h.dim_in2 or w.shape != (w_rows, h.weight_numel):
+        raise ValueError("operand widths do not match the descriptor (weights: one row per edge, or one when shared)")
     if not (src is None) == (dst is None) == (src_perm is None):
         raise ValueError("give src, dst and src_perm, or none of them")
     idx = I32

@@ -343,16 +343,31 @@ extern "C" {
 // Messages [n_edges][DIM_IN1] (indexed mode), then 256-byte aligned the
 // harmonic-gradient partials [tiles][n_edges][DIM_IN2] when one wave of
 // single channels does not cover the multiplicity (tiles = ceil(mul / 64),
-// the most any launch uses).
-int tp_conv_bwd_workspace(tp_handle h, int64_t n_edges, int batch, size_t* bytes) {
-  if (!h || !bytes) return fail(SEGPOLY_E_INVALID, "null argument");
-  if (n_edges < 0) return fail(SEGPOLY_E_INVALID, "negative size");
+// the most any launch uses); with shared weights then, 256-byte aligned,
+// the per-edge weight-gradient rows [n_edges][numel] and, again aligned,
+// their partial sums [ceil(n_edges / kTpDwChunk)][numel].
+// `dw_off` receives the offset of the per-edge rows.
+static size_t tp_bwd_ws(const segpoly_tp* h, int64_t n_edges, bool batch, int64_t* dw_off) {
   const size_t esz = h->dtype == SEGPOLY_F32 ? 4 : 8;
   const size_t e = static_cast<size_t>(n_edges);
   const size_t msg = static_cast<size_t>(round_up_256(static_cast<int64_t>(batch ? 0 : e * h->d.dim1 * esz)));
   const int mul = h->d.uniform_mul ? h->d.mul : 0;
   const size_t tiles = static_cast<size_t>((mul + 63) / 64);
-  *bytes = msg + (tiles > 1 ? tiles * e * static_cast<size_t>(h->d.dim2) * esz : 0);
+  size_t bytes = msg + (tiles > 1 ? tiles * e * static_cast<size_t>(h->d.dim2) * esz : 0);
+  if ((h->flags & SEGPOLY_SHARED_WEIGHTS) && n_edges > 0) {
+    bytes = static_cast<size_t>(round_up_256(static_cast<int64_t>(bytes)));
+    if (dw_off) *dw_off = static_cast<int64_t>(bytes);
+    const size_t numel = static_cast<size_t>(h->d.numel);
+    const size_t chunks = (e + kTpDwChunk - 1) / kTpDwChunk;
+    bytes += static_cast<size_t>(round_up_256(static_cast<int64_t>(e * numel * esz))) + chunks * numel * esz;
+  }
+  return bytes;
+}
+
+int tp_conv_bwd_workspace(tp_handle h, int64_t n_edges, int batch, size_t* bytes) {
+  if (!h || !bytes) return fail(SEGPOLY_E_INVALID, "null argument");
+  if (n_edges < 0) return fail(SEGPOLY_E_INVALID, "negative size");
+  *bytes = tp_bwd_ws(h, n_edges, batch != 0, nullptr);
   return ok();
 }
 
@@ -366,8 +381,7 @@ int tp_conv_bwd(tp_handle h, const void* x, int64_t n_src, const void* sh, const
   if ((src == nullptr) != (dst == nullptr) || (src == nullptr) != (src_perm == nullptr))
     return fail(SEGPOLY_E_INVALID, "src, dst and src_perm must all be given or all be NULL");
   const auto& d = h->d;
-  if (h->flags & SEGPOLY_SHARED_WEIGHTS)
-    return fail(SEGPOLY_E_UNSUPPORTED, "backward with shared weights is not supported");
+  const bool shared = (h->flags & SEGPOLY_SHARED_WEIGHTS) != 0;
   if (!h->spec || !h->spec->launch_bwd)
     return fail(SEGPOLY_E_UNSUPPORTED, "backward needs a specialised kernel for this descriptor");
   const bool batch = src == nullptr && n_edges > 0;
@@ -375,6 +389,8 @@ int tp_conv_bwd(tp_handle h, const void* x, int64_t n_src, const void* sh, const
     return fail(SEGPOLY_E_INVALID, "batch mode needs n_edges == n_nodes <= n_src");
   if (n_nodes > kMaxGrid || n_src > kMaxGrid) return fail(SEGPOLY_E_UNSUPPORTED, "n_nodes and n_src must be below 2^31");
   if (n_src > 0 && !grad_x) return fail(SEGPOLY_E_INVALID, "null grad_x");
+  if (shared && !grad_w && d.numel > 0) return fail(SEGPOLY_E_INVALID, "null grad_w");
+  int64_t dw_off = 0;
   if (n_edges > 0) {
     if (!grad_w || (!grad_sh && d.dim2 > 0)) return fail(SEGPOLY_E_INVALID, "null grad_sh or grad_w");
     if (n_nodes > 0) {
@@ -383,8 +399,7 @@ int tp_conv_bwd(tp_handle h, const void* x, int64_t n_src, const void* sh, const
       if (!x && n_src > 0) return fail(SEGPOLY_E_INVALID, "null x");
       if (!grad_out) return fail(SEGPOLY_E_INVALID, "null grad_out");
     }
-    size_t need = 0;
-    tp_conv_bwd_workspace(h, n_edges, batch ? 1 : 0, &need);
+    const size_t need = tp_bwd_ws(h, n_edges, batch, &dw_off);
     if (need && (!workspace || workspace_bytes < need))
       return fail(SEGPOLY_E_INVALID, "workspace missing or smaller than tp_conv_bwd_workspace()");
   }
@@ -396,7 +411,7 @@ int tp_conv_bwd(tp_handle h, const void* x, int64_t n_src, const void* sh, const
                                     : check_perm<int64_t>(src, src_perm, n_edges, stream);
     if (st != SEGPOLY_OK) return st;
   }
-  if (n_src == 0 && n_edges == 0) return ok();
+  if (n_src == 0 && n_edges == 0 && !(shared && d.numel > 0)) return ok();
   TPBwdArgs a{};
   a.x = x;
   a.sh = sh;
@@ -415,6 +430,8 @@ int tp_conv_bwd(tp_handle h, const void* x, int64_t n_src, const void* sh, const
   a.mul = d.mul;
   a.batch = batch ? 1 : 0;
   a.mean = (h->flags & SEGPOLY_REDUCE_MEAN) ? 1 : 0;
+  a.shared_w = shared ? 1 : 0;
+  a.dw_ws_off = dw_off;
   a.dtype = h->dtype;
   a.idx = idx_dtype;
   a.layout = h->layout;

@@ -86,7 +86,8 @@ struct Pow2Ceil<1> {
 // PF: keep the next edge's operands in flight (two channels per lane; with
 // one the extra registers cost more occupancy than the overlap gains).
 // `dsh_out` is dsh [n_edges][D2] with one tile, else part [tiles][n_edges][D2].
-template <class S, typename T, typename Index, int LAYOUT, int CPL>
+// SHW: one weight row shared by every edge (dw rows still per edge).
+template <class S, typename T, typename Index, int LAYOUT, int CPL, bool SHW>
 __global__ void __launch_bounds__(kWave)
 tp_bwd_edge_kernel(const T* __restrict__ x, const T* __restrict__ sh, const T* __restrict__ w,
                    const Index* __restrict__ src, const Index* __restrict__ dst, const T* __restrict__ g,
@@ -145,7 +146,7 @@ tp_bwd_edge_kernel(const T* __restrict__ x, const T* __restrict__ sh, const T* _
   auto load = [&](int64_t e, int64_t s, T (&xv)[CPL][S::NX], T (&wv)[CPL][S::NP], T (&shv)[S::D2]) {
     const int64_t sc = (s >= 0 && s < n_src) ? s : 0;
     S::template load_xs<T, LAYOUT, CPL>(x + sc * dim1, mul, ubl, xv);
-    const T* wrow = w + e * numel + ubl;
+    const T* wrow = w + (SHW ? 0 : e * numel) + ubl;
 #pragma unroll
     for (int p = 0; p < S::NP; ++p) {
       if constexpr (CPL == 2) {
@@ -292,6 +293,20 @@ fold_partials_kernel(const T* __restrict__ part, int tiles, int64_t n, T* __rest
   }
 }
 
+// Shared weights: part[c][j] = sum of dwe[e][j] over the edges e of chunk
+// c (kTpDwChunk edges, in order); one thread per column j.
+template <typename T>
+__global__ void __launch_bounds__(256)
+dw_edge_sum_kernel(const T* __restrict__ dwe, int64_t n_edges, int64_t numel, T* __restrict__ part) {
+  const int64_t j = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x;
+  if (j >= numel) return;
+  const int64_t e0 = blockIdx.y * kTpDwChunk;
+  const int64_t e1 = e0 + kTpDwChunk < n_edges ? e0 + kTpDwChunk : n_edges;
+  T v = T(0);
+  for (int64_t e = e0; e < e1; ++e) v += dwe[e * numel + j];
+  part[blockIdx.y * numel + j] = v;
+}
+
 template <typename T>
 __global__ void __launch_bounds__(256) fill_zero_kernel(T* __restrict__ p, int64_t n) {
   for (int64_t i = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; i < n;
@@ -317,27 +332,52 @@ int tp_bwd_launch(const TPBwdArgs& a) {
   const int tiles = (a.mul + kWave * CPL - 1) / (kWave * CPL);
   T* const dx = static_cast<T*>(a.dx);
   T* const dsh = static_cast<T*>(a.dsh);
-  if (a.n_edges == 0) {  // nothing reaches the output: dx is zero
+  const int64_t numel = static_cast<int64_t>(a.mul) * S::NP;
+  if (a.n_edges == 0) {  // nothing reaches the output: dx (and a shared dw) is zero
     fill_zero(dx, a.n_src * dim1, st);
+    if (a.shared_w) fill_zero(static_cast<T*>(a.dw), numel, st);
     return static_cast<int>(hipGetLastError());
   }
   if (a.n_nodes == 0) {  // every edge has a destination outside the output
     fill_zero(dx, a.n_src * dim1, st);
-    fill_zero(static_cast<T*>(a.dw), a.n_edges * static_cast<int64_t>(a.mul) * S::NP, st);
+    fill_zero(static_cast<T*>(a.dw), a.shared_w ? numel : a.n_edges * numel, st);
     fill_zero(dsh, a.n_edges * S::D2, st);
     return static_cast<int>(hipGetLastError());
   }
   unsigned char* ws = static_cast<unsigned char*>(a.workspace);
+  // shared weights: per-edge gradient rows in the workspace, summed below
+  T* const dwe = a.shared_w ? reinterpret_cast<T*>(ws + a.dw_ws_off) : static_cast<T*>(a.dw);
   T* const msg = a.batch ? dx : reinterpret_cast<T*>(ws);
   T* const part =
       tiles > 1 ? reinterpret_cast<T*>(ws + (a.batch ? 0 : round_up_256(a.n_edges * dim1 * static_cast<int64_t>(sizeof(T))))) : dsh;
-  hipLaunchKernelGGL((tp_bwd_edge_kernel<S, T, Index, LAYOUT, CPL>),
-                     dim3(static_cast<unsigned>(a.n_nodes), static_cast<unsigned>(tiles)), dim3(kWave), 0, st,
-                     static_cast<const T*>(a.x), static_cast<const T*>(a.sh), static_cast<const T*>(a.w),
-                     static_cast<const Index*>(a.src), static_cast<const Index*>(a.dst), static_cast<const T*>(a.g),
-                     a.n_src, a.n_edges, a.n_nodes, a.mul, a.batch, a.mean, static_cast<T*>(a.dw), part, msg);
+  const dim3 grid(static_cast<unsigned>(a.n_nodes), static_cast<unsigned>(tiles));
+  if (a.shared_w)
+    hipLaunchKernelGGL((tp_bwd_edge_kernel<S, T, Index, LAYOUT, CPL, true>), grid, dim3(kWave), 0, st,
+                       static_cast<const T*>(a.x), static_cast<const T*>(a.sh), static_cast<const T*>(a.w),
+                       static_cast<const Index*>(a.src), static_cast<const Index*>(a.dst),
+                       static_cast<const T*>(a.g), a.n_src, a.n_edges, a.n_nodes, a.mul, a.batch, a.mean, dwe, part,
+                       msg);
+  else
+    hipLaunchKernelGGL((tp_bwd_edge_kernel<S, T, Index, LAYOUT, CPL, false>), grid, dim3(kWave), 0, st,
+                       static_cast<const T*>(a.x), static_cast<const T*>(a.sh), static_cast<const T*>(a.w),
+                       static_cast<const Index*>(a.src), static_cast<const Index*>(a.dst),
+                       static_cast<const T*>(a.g), a.n_src, a.n_edges, a.n_nodes, a.mul, a.batch, a.mean, dwe, part,
+                       msg);
   int rc = static_cast<int>(hipGetLastError());
   if (rc) return rc;
+  if (a.shared_w) {
+    const int64_t chunks = (a.n_edges + kTpDwChunk - 1) / kTpDwChunk;
+    T* const dpart = reinterpret_cast<T*>(ws + a.dw_ws_off +
+                                          round_up_256(a.n_edges * numel * static_cast<int64_t>(sizeof(T))));
+    hipLaunchKernelGGL((dw_edge_sum_kernel<T>), dim3(static_cast<unsigned>((numel + 255) / 256),
+                                                     static_cast<unsigned>(chunks)),
+                       dim3(256), 0, st, dwe, a.n_edges, numel, dpart);
+    const int64_t blocks = (numel + 255) / 256;
+    hipLaunchKernelGGL((fold_partials_kernel<T>), dim3(static_cast<unsigned>(blocks < 4096 ? blocks : 4096)),
+                       dim3(256), 0, st, dpart, static_cast<int>(chunks), numel, static_cast<T*>(a.dw));
+    rc = static_cast<int>(hipGetLastError());
+    if (rc) return rc;
+  }
   if (tiles > 1) {
     const int64_t n = a.n_edges * S::D2;
     const int64_t blocks = (n + 255) / 256;

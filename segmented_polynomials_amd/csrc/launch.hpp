@@ -41,12 +41,14 @@ struct TPBwdArgs {
   const void* g;      // [n_nodes, dim_out] gradient of the output
   void* dx;           // [n_src, dim1]
   void* dsh;          // [n_edges, dim2]
-  void* dw;           // [n_edges, numel]
-  void* workspace;    // [n_edges, dim1] per-edge source messages (unused in batch mode)
+  void* dw;           // [n_edges, numel], or [1, numel] with shared weights
+  void* workspace;    // [n_edges, dim1] per-edge source messages (unused in batch mode), ...
   int64_t n_src, n_edges, n_nodes;
   int mul;
   int batch;
   int mean;           // 1: the forward divided each row by its number of edges
+  int shared_w;       // 1: w is one row shared by every edge (dw sums over the edges)
+  int64_t dw_ws_off;  // shared weights: byte offset of the per-edge dw rows in the workspace
   int dtype, idx, layout;
   void* stream;
 };
@@ -106,6 +108,8 @@ int launch_sh(const ShArgs& a);
 // Workspace layouts of the backward calls, shared by the C ABI (sizes) and
 // the launchers (offsets).
 inline int64_t round_up_256(int64_t n) { return (n + 255) / 256 * 256; }
+// Edges per partial sum of a shared weight gradient (then the partials in order).
+constexpr int64_t kTpDwChunk = 1024;
 
 // Symmetric contraction: a segment table of 2 * (E + 3) int64, then one
 // partial weight-gradient row per chunk of kSymconBwdChunk atoms (each

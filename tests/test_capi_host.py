@@ -220,9 +220,15 @@ def test_backward_argument_errors_fail_before_any_gpu_call():
     assert f(h._h, p, 1, p, p, p, p, p, 0, 1, 1, p, p, p, p, p, 8, None) == sp.E_INVALID       # workspace small
     assert f(h._h, p, 1, p, p, p, p, p, 0, 1, 1, p, p, p, p, None, big, None) == sp.E_INVALID  # no workspace
     assert f(h._h, p, 1, p, p, None, None, None, 0, 2, 2, p, p, p, p, None, 0, None) == sp.E_INVALID  # batch
-    # shared weights and generic descriptors fail closed
+    # shared weights: the workspace adds the per-edge weight gradients and
+    # one partial sum per 1024 edges; generic descriptors fail closed
     hs = sp.tp_create("32x0e+32x1o", "0e+1o", "0e+1o", shared_weights=True)
-    assert f(hs._h, p, 1, p, p, p, p, p, 0, 1, 1, p, p, p, p, p, big, None) == sp.E_UNSUPPORTED
+    assert sp.tp_conv_bwd_workspace(hs, 1000) == 1000 * hs.dim_in1 * 4 + 1000 * hs.weight_numel * 4 \
+        + hs.weight_numel * 4
+    assert sp.tp_conv_bwd_workspace(hs, 2049) == (2049 * hs.dim_in1 * 4 + 255) // 256 * 256 \
+        + (2049 * hs.weight_numel * 4 + 255) // 256 * 256 + 3 * hs.weight_numel * 4
+    assert f(hs._h, p, 1, p, p, p, p, p, 0, 1, 1, p, p, p, p, p, 8, None) == sp.E_INVALID       # workspace small
+    assert f(hs._h, p, 1, p, p, p, p, p, 0, 1, 1, p, p, p, None, p, big, None) == sp.E_INVALID  # grad_w
     hg = sp.tp_create("32x0e+32x1o", "0e+1o", "0e+1o", force_generic=True)
     assert f(hg._h, p, 1, p, p, p, p, p, 0, 1, 1, p, p, p, p, p, big, None) == sp.E_UNSUPPORTED
     # nothing to do: succeeds without touching a device

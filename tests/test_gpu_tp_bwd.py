@@ -225,3 +225,37 @@ def test_mean_reduction_backward():
     ref = o.conv_vjp(*args, layout="ir_mul", reduce="mean")
     scale = o.conv_vjp(*args, layout="ir_mul", absolute=True, reduce="mean")
     _check_all(got, ref, scale, "f32", "mean reduction")
+
+
+@pytest.mark.parametrize("layout,dtype", [("mul_ir", "f32"), ("ir_mul", "f32"), ("mul_ir", "f64")])
+def test_shared_weights_backward(layout, dtype):
+    """One weight row shared by every edge: grad_w [1, numel] sums the
+    per-edge gradients (2,700 edges: three partial sums of 1,024 edges, the
+    last ragged); no edges gives a zero row."""
+    sp = _sp()
+    import torch
+    wl = workloads.WORKLOADS[4]
+    o = otp.ChannelwiseTP(wl.irreps_in1, wl.irreps_in2, wl.irreps_out)
+    wlt = workloads.TPWorkload(**{**wl.__dict__, "dtype": dtype})
+    inp = workloads.tp_inputs(wlt, o.weight_fan_in(), n_nodes=300, degree=9, seed=91)
+    inp = dict(inp, w=np.ascontiguousarray(inp["w"][:1]))
+    g = workloads.output_gradient(300, o.dim_out, dtype, seed=92)
+    h = sp.tp_create(wl.irreps_in1, wl.irreps_in2, wl.irreps_out, layout=layout, dtype=dtype, shared_weights=True)
+    announce(f"tp bwd shared weights {layout} {dtype} n_edges={len(inp['src'])}")
+    got = _bwd(sp, h, inp, g)
+    assert got[2].shape == (1, o.weight_numel)
+    args = (inp["x"], inp["sh"], inp["w"], inp["src"], inp["dst"], inp["n_nodes"], g)
+    ref = o.conv_vjp(*args, layout=layout, shared_weights=True)
+    scale = o.conv_vjp(*args, layout=layout, absolute=True, shared_weights=True)
+    _check_all(got, ref, scale, dtype, f"shared weights {layout} {dtype}")
+    if dtype == "f32" and layout == "mul_ir":
+        td = torch.float32
+        x = torch.randn(4, h.dim_in1, device="cuda")
+        e = torch.empty(0, dtype=torch.int32, device="cuda")
+        announce("tp bwd shared weights, no edges")
+        dx, dsh, dw = sp.tp_conv_bwd(h, x, torch.empty(0, h.dim_in2, device="cuda"),
+                                     torch.randn(1, h.weight_numel, device="cuda", dtype=td),
+                                     torch.randn(6, h.dim_out, device="cuda"), e, e, e, n_nodes=6,
+                                     grad_w=torch.full((1, h.weight_numel), 7.0, device="cuda"))
+        torch.cuda.synchronize()
+        assert torch.count_nonzero(dx).item() == 0 and torch.count_nonzero(dw).item() == 0
