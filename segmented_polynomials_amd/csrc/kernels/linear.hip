@@ -249,16 +249,19 @@ linear_dw_kernel(const T* __restrict__ x, const T* __restrict__ g, T* __restrict
   const int uu_a = tid % kLinTM, rk_a = tid / kLinTM;
   const int vv_b = tid % kLinTN, rk_b = tid / kLinTN;
   int c_lo = 0, c_hi = 0;
+  bool sorted = false;
+  const int s_begin = r_begin / d, s_end = (r_end - 1) / d + 1;  // the chunk's samples
   if constexpr (CLS) {
-    const int s_begin = r_begin / d, s_end = (r_end - 1) / d + 1;
-    int lo = num_classes, hi = -1;
+    int lo = num_classes, hi = -1, unsorted = 0;
     for (int sm = s_begin + tid; sm < s_end; sm += kLinThreads) {
       const int64_t c = static_cast<int64_t>(cls[sm]);
+      if (sm + 1 < s_end && c > static_cast<int64_t>(cls[sm + 1])) unsorted = 1;
       if (c >= 0 && c < num_classes) {
         lo = static_cast<int>(c) < lo ? static_cast<int>(c) : lo;
         hi = static_cast<int>(c) > hi ? static_cast<int>(c) : hi;
       }
     }
+    sorted = __syncthreads_or(unsorted) == 0;
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) {
       const int l2 = __shfl_xor(lo, o), h2 = __shfl_xor(hi, o);
@@ -288,10 +291,32 @@ linear_dw_kernel(const T* __restrict__ x, const T* __restrict__ g, T* __restrict
   const int sb_n = kBStep / d, sb_m = kBStep - sb_n * d;            // divmod(kBStep, d)
   const int u = u0 + uu_a, v = v0 + vv_b;
   for (int cc = c_lo; cc <= c_hi; ++cc) {
-  int a_n = (r_begin + rk_a) / d, a_m = (r_begin + rk_a) - a_n * d;
-  int b_n = (r_begin + rk_b) / d, b_m = (r_begin + rk_b) - b_n * d;
+  // rows [kb, ke) of the pass; when the chunk's classes are sorted, class
+  // cc is one run of samples (found by binary search) and the pass covers
+  // exactly its rows, else every row of the chunk with the others masked
+  int kb = r_begin, ke = r_end;
+  bool mask = CLS;
+  if constexpr (CLS) {
+    if (sorted) {
+      auto first_at_least = [&](int64_t c) {  // first sample of the chunk with class >= c
+        int lo = s_begin, hi = s_end;
+        while (lo < hi) {
+          const int mid = (lo + hi) / 2;
+          if (static_cast<int64_t>(cls[mid]) < c) lo = mid + 1;
+          else hi = mid;
+        }
+        return lo;
+      };
+      const int sa = first_at_least(cc), sb = first_at_least(static_cast<int64_t>(cc) + 1);
+      kb = sa * d > r_begin ? sa * d : r_begin;
+      ke = sb * d < r_end ? sb * d : r_end;
+      mask = false;
+    }
+  }
+  int a_n = (kb + rk_a) / d, a_m = (kb + rk_a) - a_n * d;
+  int b_n = (kb + rk_b) / d, b_m = (kb + rk_b) - b_n * d;
   // rows of another class than cc contribute nothing
-  auto in_class = [&](int nn) { return !CLS || static_cast<int64_t>(cls[nn]) == cc; };
+  auto in_class = [&](int nn) { return !mask || static_cast<int64_t>(cls[nn]) == cc; };
   typename M::acc_t acc[kMT][kNT];
 #pragma unroll
   for (int a = 0; a < kMT; ++a)
@@ -306,7 +331,7 @@ linear_dw_kernel(const T* __restrict__ x, const T* __restrict__ g, T* __restrict
     for (int e = 0; e < kLinTK / kAStep; ++e) {
       const int row = k0 + rk_a + e * kAStep;
       T val = T(0);
-      if (row < r_end && u < P.mul_in && in_class(nn)) {
+      if (row < ke && u < P.mul_in && in_class(nn)) {
         const int64_t off = LAYOUT == kIrMul ? P.x_off + static_cast<int64_t>(m) * P.mul_in + u
                                              : P.x_off + static_cast<int64_t>(u) * d + m;
         val = x[static_cast<int64_t>(nn) * dim_in + off];
@@ -325,7 +350,7 @@ linear_dw_kernel(const T* __restrict__ x, const T* __restrict__ g, T* __restrict
     for (int e = 0; e < kLinTK / kBStep; ++e) {
       const int row = k0 + rk_b + e * kBStep;
       T val = T(0);
-      if (row < r_end && v < P.mul_out && in_class(nn)) {
+      if (row < ke && v < P.mul_out && in_class(nn)) {
         const int64_t off = LAYOUT == kIrMul ? P.g_off + static_cast<int64_t>(m) * P.mul_out + v
                                              : P.g_off + static_cast<int64_t>(v) * d + m;
         val = g[static_cast<int64_t>(nn) * dim_out + off];
@@ -352,9 +377,9 @@ linear_dw_kernel(const T* __restrict__ x, const T* __restrict__ g, T* __restrict
       ++b_n;
     }
   };
-  int k0 = r_begin;
-  if (k0 < r_end) fetch(k0);
-  while (k0 < r_end) {
+  int k0 = kb;
+  if (k0 < ke) fetch(k0);
+  while (k0 < ke) {
     __syncthreads();
 #pragma unroll
     for (int e = 0; e < kLinTK / kAStep; ++e) As[uu_a][rk_a + e * kAStep] = ra[e];
@@ -362,7 +387,7 @@ linear_dw_kernel(const T* __restrict__ x, const T* __restrict__ g, T* __restrict
     for (int e = 0; e < kLinTK / kBStep; ++e) Bs[rk_b + e * kBStep][vv_b] = rb[e];
     __syncthreads();
     k0 += kLinTK;
-    if (k0 < r_end) fetch(k0);
+    if (k0 < ke) fetch(k0);
 #pragma unroll
     for (int s = 0; s < kLinTK / 4; ++s) {
       const int kq = s * 4 + lane / 16;
