@@ -485,15 +485,23 @@ int fctp_conv_fwd(fctp_handle h, const void* x, int64_t n_src, const void* sh, c
                   void* stream);
 
 /* fctp_conv_bwd_workspace: bytes of workspace fctp_conv_bwd needs for
- * n_edges edges (the per-edge source messages, [n_edges, DIM_IN1]). */
-int fctp_conv_bwd_workspace(fctp_handle h, int64_t n_edges, size_t* bytes);
+ * n_edges edges and w_rows weight rows (n_edges, or 1 shared): the
+ * per-edge source messages [n_edges, DIM_IN1], rounded up to 256 bytes;
+ * with a shared row (and n_edges != 1) then the per-edge weight gradients
+ * [n_edges, WEIGHT_NUMEL], rounded up to 256 bytes, and
+ * ceil(n_edges / 1024) * WEIGHT_NUMEL partial sums.  Elements of the
+ * handle's dtype. */
+int fctp_conv_bwd_workspace(fctp_handle h, int64_t n_edges, int64_t w_rows, size_t* bytes);
 
 /*
  * fctp_conv_bwd: vector-Jacobian product of fctp_conv_fwd with one weight
- * row per edge (w_rows == n_edges; one shared row gives E_UNSUPPORTED), for
- * grad_out = dL/d(out) [n_nodes, DIM_OUT] device (divided by each row's edge
- * count with SEGPOLY_REDUCE_MEAN, as the forward):
- *   grad_w  [n_edges, WEIGHT_NUMEL]: per edge, dW_e[p][u, w] = sum_k y[p, k, u] G[o, k, w]
+ * row per edge (w_rows == n_edges) or one row shared by every edge
+ * (w_rows == 1), for grad_out = dL/d(out) [n_nodes, DIM_OUT] device
+ * (divided by each row's edge count with SEGPOLY_REDUCE_MEAN, as the
+ * forward):
+ *   grad_w  [w_rows, WEIGHT_NUMEL]: per edge, dW_e[p][u, w] = sum_k y[p, k, u] G[o, k, w];
+ *           a shared row gets the sum over the edges (per-edge rows in the
+ *           workspace, summed in chunks of 1024 edges, then in order)
  *   grad_sh [n_edges, DIM_IN2]:      per edge
  *   grad_x  [n_src, DIM_IN1]:        summed over the edges that read each source,
  * all fully overwritten (zero for sources no edge reads and for edges whose
@@ -501,7 +509,7 @@ int fctp_conv_bwd_workspace(fctp_handle h, int64_t n_edges, size_t* bytes);
  * dtype) lists the edges ordered by source (a stable argsort of src:
  * structure of the batch, like the sorted dst); VALIDATE checks it and the
  * indices.  The source sums run in src_perm order: deterministic.
- * `workspace` holds fctp_conv_bwd_workspace(n_edges) bytes.  Other
+ * `workspace` holds fctp_conv_bwd_workspace(n_edges, w_rows) bytes.  Other
  * arguments as fctp_conv_fwd.
  */
 int fctp_conv_bwd(fctp_handle h, const void* x, int64_t n_src, const void* sh, const void* w, int64_t w_rows,

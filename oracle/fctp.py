@@ -198,12 +198,14 @@ class FullyConnectedTP:
         return join_blocks(ob, layout)
 
     def conv_vjp(self, x1, x2, w, src, dst, n_nodes, g, layout="mul_ir", reduce="sum", absolute=False):
-        """Vector-Jacobian product of :meth:`conv` with one weight row per
-        edge, for g = dL/d(out) [n_nodes, dim_out]: returns (dx1 [n_src,
-        dim_in1], dx2 [n_edges, dim_in2], dw [n_edges, weight_numel]).  Per
-        edge e (source s, destination n, G = g[n] scaled by 1/deg(n) with
-        reduce="mean") it is the batch VJP of the edge's product; dx1 sums
-        the edges that read each source."""
+        """Vector-Jacobian product of :meth:`conv` for g = dL/d(out)
+        [n_nodes, dim_out]: returns (dx1 [n_src, dim_in1], dx2 [n_edges,
+        dim_in2], dw shaped like w).  Per edge e (source s, destination n,
+        G = g[n] scaled by 1/deg(n) with reduce="mean") it is the batch VJP of
+        the edge's product; dx1 sums the edges that read each source.  One
+        shared weight row [1, weight_numel] enters every edge, so its
+        gradient is the sum of the per-edge gradients (chain rule through
+        the broadcast)."""
         x1, x2, w, g = (np.asarray(a, dtype=np.float64) for a in (x1, x2, w, g))
         src = np.asarray(src, dtype=np.int64)
         dst = np.asarray(dst, dtype=np.int64)
@@ -212,9 +214,11 @@ class FullyConnectedTP:
             g = g * np.where(deg > 0, 1.0 / np.maximum(deg, 1.0), 0.0)[:, None]
         elif reduce != "sum":
             raise ValueError("reduce is 'sum' or 'mean'")
-        if w.shape[0] == 1 and x2.shape[0] != 1:
-            raise ValueError("the convolution VJP takes one weight row per edge")
-        d1, d2, dw = self.vjp(x1[src], x2, None, g[dst], layout=layout, absolute=absolute, edge_weights=w)
+        shared = w.shape[0] == 1 and x2.shape[0] != 1
+        we = np.broadcast_to(w, (x2.shape[0], w.shape[1])) if shared else w
+        d1, d2, dw = self.vjp(x1[src], x2, None, g[dst], layout=layout, absolute=absolute, edge_weights=we)
         dx1 = np.zeros_like(x1)
         np.add.at(dx1, src, d1)
+        if shared:
+            dw = dw.sum(axis=0, keepdims=True)
         return dx1, d2, dw

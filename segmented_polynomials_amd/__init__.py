@@ -102,7 +102,7 @@ def _load():
         "fctp_bwd_workspace": [vp, i64, ctypes.POINTER(ctypes.c_size_t)],
         "fctp_bwd": [vp, vp, vp, vp, vp, i64, vp, vp, vp, vp, ctypes.c_size_t, vp],
         "fctp_conv_fwd": [vp, vp, i64, vp, vp, i64, vp, vp, c_int, i64, i64, vp, vp],
-        "fctp_conv_bwd_workspace": [vp, i64, ctypes.POINTER(ctypes.c_size_t)],
+        "fctp_conv_bwd_workspace": [vp, i64, i64, ctypes.POINTER(ctypes.c_size_t)],
         "fctp_conv_bwd": [vp, vp, i64, vp, vp, i64, vp, vp, vp, c_int, i64, i64, vp, vp, vp, vp, vp,
                           ctypes.c_size_t, vp],
         "fctp_destroy": [vp],
@@ -680,20 +680,21 @@ def fctp_conv_fwd(h, x, sh, w, src, dst, n_nodes, out=None):
     return out
 
 
-def fctp_conv_bwd_workspace(h, n_edges):
+def fctp_conv_bwd_workspace(h, n_edges, w_rows=None):
     v = ctypes.c_size_t()
-    _check(lib.fctp_conv_bwd_workspace(h._h, n_edges, ctypes.byref(v)))
+    _check(lib.fctp_conv_bwd_workspace(h._h, n_edges, n_edges if w_rows is None else w_rows, ctypes.byref(v)))
     return v.value
 
 
 def fctp_conv_bwd(h, x, sh, w, grad_out, src, dst, src_perm, n_nodes=None, workspace=None):
     """(grad_x, grad_sh, grad_w) of ``fctp_conv_fwd`` with one weight row per
-    edge; ``src_perm`` orders the edges by source (stable argsort of src)."""
+    edge or one shared row (grad_w shaped like w); ``src_perm`` orders the
+    edges by source (stable argsort of src)."""
     import torch
     n_edges = sh.shape[0]
     n_nodes = grad_out.shape[0] if n_nodes is None else n_nodes
-    if w.shape[0] != n_edges:
-        raise ValueError("the backward takes one weight row per edge")
+    if w.shape[0] not in (1, n_edges):
+        raise ValueError("weights: one row per edge, or one shared row")
     for name, a in (("src", src), ("dst", dst), ("src_perm", src_perm)):
         if a.shape != (n_edges,) or a.dtype != src.dtype or not a.is_cuda or not a.is_contiguous():
             raise ValueError(f"{name} must be a contiguous [n_edges] device tensor of src's dtype")
@@ -701,7 +702,8 @@ def fctp_conv_bwd(h, x, sh, w, grad_out, src, dst, src_perm, n_nodes=None, works
         raise ValueError("grad_out has the wrong shape")
     gx, gs, gw = torch.empty_like(x), torch.empty_like(sh), torch.empty_like(w)
     if workspace is None:
-        workspace = torch.empty(max(1, fctp_conv_bwd_workspace(h, n_edges)), dtype=torch.uint8, device=x.device)
+        workspace = torch.empty(max(1, fctp_conv_bwd_workspace(h, n_edges, w.shape[0])), dtype=torch.uint8,
+                                device=x.device)
     wbytes = workspace.numel() * workspace.element_size()
     _check(lib.fctp_conv_bwd(h._h, _ptr(x), x.shape[0], _ptr(sh), _ptr(w), w.shape[0], _ptr(src), _ptr(dst),
                              _ptr(src_perm), _index_dtype(src), n_edges, n_nodes, _ptr(grad_out), _ptr(gx), _ptr(gs),

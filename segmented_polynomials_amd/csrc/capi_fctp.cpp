@@ -747,10 +747,25 @@ int fctp_conv_fwd(fctp_handle h, const void* x, int64_t n_src, const void* sh, c
   return ok();
 }
 
-int fctp_conv_bwd_workspace(fctp_handle h, int64_t n_edges, size_t* bytes) {
+// Per-edge messages [n_edges][dim1]; with one shared weight row then,
+// 256-byte aligned, the per-edge weight gradients [n_edges][numel] and,
+// aligned again, their partial sums [ceil(n_edges / kTpDwChunk)][numel].
+static size_t fcv_bwd_ws(const segpoly_fctp* h, int64_t n_edges, bool shared, int64_t* dw_off) {
+  const int64_t esz = static_cast<int64_t>(elt(h->dtype));
+  int64_t b = round_up_256(n_edges * h->dim1 * esz);
+  if (shared && n_edges > 0 && h->numel > 0) {
+    if (dw_off) *dw_off = b;
+    const int64_t chunks = (n_edges + kTpDwChunk - 1) / kTpDwChunk;
+    b += round_up_256(n_edges * h->numel * esz) + chunks * h->numel * esz;
+  }
+  return static_cast<size_t>(b);
+}
+
+int fctp_conv_bwd_workspace(fctp_handle h, int64_t n_edges, int64_t w_rows, size_t* bytes) {
   if (!h || !bytes) return fail(SEGPOLY_E_INVALID, "null argument");
   if (n_edges < 0) return fail(SEGPOLY_E_INVALID, "negative edge count");
-  *bytes = static_cast<size_t>(round_up_256(n_edges * h->dim1 * static_cast<int64_t>(elt(h->dtype))));
+  if (w_rows != 1 && w_rows != n_edges) return fail(SEGPOLY_E_INVALID, "w_rows must be 1 (shared) or n_edges");
+  *bytes = fcv_bwd_ws(h, n_edges, w_rows == 1 && n_edges != 1, nullptr);
   return ok();
 }
 
@@ -763,20 +778,20 @@ int fctp_conv_bwd(fctp_handle h, const void* x, int64_t n_src, const void* sh, c
   if (!h->conv_bwd_error.empty()) return fail(SEGPOLY_E_UNSUPPORTED, h->conv_bwd_error);
   if (n_src < 0 || n_edges < 0 || n_nodes < 0) return fail(SEGPOLY_E_INVALID, "negative size");
   if (idx_dtype != SEGPOLY_I32 && idx_dtype != SEGPOLY_I64) return fail(SEGPOLY_E_INVALID, "bad index dtype");
-  if (w_rows != n_edges)
-    return fail(n_edges > 1 && w_rows == 1 ? SEGPOLY_E_UNSUPPORTED : SEGPOLY_E_INVALID,
-                "the convolution backward takes one weight row per edge (w_rows == n_edges)");
-  size_t need = 0;
-  fctp_conv_bwd_workspace(h, n_edges, &need);
+  if (w_rows != 1 && w_rows != n_edges) return fail(SEGPOLY_E_INVALID, "w_rows must be 1 (shared) or n_edges");
+  const bool shared = w_rows == 1 && n_edges != 1;
+  int64_t dw_off = 0;
+  const size_t need = fcv_bwd_ws(h, n_edges, shared, &dw_off);
   if (workspace_bytes < need) return fail(SEGPOLY_E_INVALID, "workspace too small: need " + std::to_string(need) + " bytes");
-  if ((n_src > 0 && !grad_x) || (n_edges > 0 && (!grad_sh || !grad_w)))
+  if ((n_src > 0 && !grad_x) || (n_edges > 0 && (!grad_sh || !grad_w)) || (shared && h->numel > 0 && !grad_w))
     return fail(SEGPOLY_E_INVALID, "null gradient buffer");
   if (n_edges > 0 && (!src || !dst || !src_perm || !workspace || (h->dim2 > 0 && !sh) || (h->numel > 0 && !w) ||
                       (n_src > 0 && !x) || (n_nodes > 0 && h->dimo > 0 && !grad_out)))
     return fail(SEGPOLY_E_INVALID, "null buffer");
   if (n_nodes > kMaxGridX || n_src > kMaxGridX) return fail(SEGPOLY_E_UNSUPPORTED, "too many rows for one launch");
-  if (n_edges == 0) {  // dx = 0
-    const int rc = launch_fill_zero(grad_x, n_src * h->dim1, h->dtype, stream);
+  if (n_edges == 0) {  // dx = 0 (and a shared weight gradient)
+    int rc = launch_fill_zero(grad_x, n_src * h->dim1, h->dtype, stream);
+    if (!rc && shared) rc = launch_fill_zero(grad_w, h->numel, h->dtype, stream);
     if (rc) return fail(SEGPOLY_E_HIP, std::string("fill: ") + hipGetErrorString(static_cast<hipError_t>(rc)));
     return ok();
   }
@@ -797,6 +812,8 @@ int fctp_conv_bwd(fctp_handle h, const void* x, int64_t n_src, const void* sh, c
   a.dim1 = h->dim1, a.dim2 = h->dim2, a.dimo = h->dimo, a.numel = h->numel;
   a.mean = (h->flags & SEGPOLY_REDUCE_MEAN) ? 1 : 0;
   a.dx = grad_x, a.dsh = grad_sh, a.dw = grad_w, a.msg = workspace;
+  a.shared_w = shared ? 1 : 0;
+  a.dw_ws_off = dw_off;
   a.blocks = reinterpret_cast<const FcvBlock*>(db + h->cv_off[0]);
   a.qks = reinterpret_cast<const FcvQK*>(db + h->cv_off[2]);
   a.ents = reinterpret_cast<const FcvEnt*>(db + h->cv_off[3]);

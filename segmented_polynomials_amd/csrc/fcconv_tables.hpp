@@ -87,6 +87,8 @@ struct FcvBwdArgs {
   void* dsh;
   void* dw;
   void* msg;                       // workspace: per-edge source messages [n_edges][dim1]
+  int shared_w;                    // one weight row for every edge: dw [1, numel] sums over the edges
+  int64_t dw_ws_off;               // shared: byte offset of the per-edge dw rows in the workspace
   const FcvBlock* blocks;          // device tables
   const FcvQK* qks;
   const FcvEnt* ents;

@@ -38,7 +38,7 @@ __device__ __forceinline__ void fcb_wave_sync() {
 //   z[row + k, u] = sum_w W[u, w] G[k, w]     (lane = input channel u, the
 //                                            weight row read once, 16 channels at a time)
 //   dW[u, w]      = sum_k y[row + k, u] G[k, w] (lane = output channel w, G[., w] in registers)
-template <typename T, int LAYOUT, int D>
+template <typename T, int LAYOUT, int D, bool SHW>
 __device__ __forceinline__ void fcb_path(const FcvBPath& P, const T* __restrict__ w, int64_t e, int64_t numel,
                                          bool valid, int M, int c, const T* Gs, const T* ys, T* zs,
                                          T* __restrict__ dw) {
@@ -50,7 +50,7 @@ __device__ __forceinline__ void fcb_path(const FcvBPath& P, const T* __restrict_
 #pragma unroll
     for (int k = 0; k < D; ++k) z[k] = T(0);
     if (valid && c < P.m1) {
-      const T* wr = w + e * numel + P.w_off + static_cast<int64_t>(c) * P.m3;
+      const T* wr = w + (SHW ? 0 : e * numel) + P.w_off + static_cast<int64_t>(c) * P.m3;
       int w0 = 0;
       // 16-byte vector loads where the row is aligned (it is whenever m3
       // is a multiple of 16 / sizeof(T) channels), else plain loads
@@ -101,7 +101,8 @@ __device__ __forceinline__ void fcb_path(const FcvBPath& P, const T* __restrict_
     }
 }
 
-template <typename T, typename Index, int LAYOUT>
+// SHW: one weight row shared by every edge (the dw rows stay per edge).
+template <typename T, typename Index, int LAYOUT, bool SHW>
 __global__ void __launch_bounds__(64)
 fcconv_bwd_edge_kernel(const T* __restrict__ x, const T* __restrict__ sh, const T* __restrict__ w,
                        const T* __restrict__ g, const Index* __restrict__ src, const Index* __restrict__ dst,
@@ -181,13 +182,13 @@ fcconv_bwd_edge_kernel(const T* __restrict__ x, const T* __restrict__ sh, const 
     for (int pi = 0; pi < n_bpaths; ++pi) {
       const FcvBPath P = bpaths[pi];
       switch (P.d3) {
-        case 1: fcb_path<T, LAYOUT, 1>(P, w, e, numel, valid, M, c, Gs, ys, zs, dw); break;
-        case 3: fcb_path<T, LAYOUT, 3>(P, w, e, numel, valid, M, c, Gs, ys, zs, dw); break;
-        case 5: fcb_path<T, LAYOUT, 5>(P, w, e, numel, valid, M, c, Gs, ys, zs, dw); break;
-        case 7: fcb_path<T, LAYOUT, 7>(P, w, e, numel, valid, M, c, Gs, ys, zs, dw); break;
-        case 9: fcb_path<T, LAYOUT, 9>(P, w, e, numel, valid, M, c, Gs, ys, zs, dw); break;
-        case 11: fcb_path<T, LAYOUT, 11>(P, w, e, numel, valid, M, c, Gs, ys, zs, dw); break;
-        default: fcb_path<T, LAYOUT, 13>(P, w, e, numel, valid, M, c, Gs, ys, zs, dw); break;
+        case 1: fcb_path<T, LAYOUT, 1, SHW>(P, w, e, numel, valid, M, c, Gs, ys, zs, dw); break;
+        case 3: fcb_path<T, LAYOUT, 3, SHW>(P, w, e, numel, valid, M, c, Gs, ys, zs, dw); break;
+        case 5: fcb_path<T, LAYOUT, 5, SHW>(P, w, e, numel, valid, M, c, Gs, ys, zs, dw); break;
+        case 7: fcb_path<T, LAYOUT, 7, SHW>(P, w, e, numel, valid, M, c, Gs, ys, zs, dw); break;
+        case 9: fcb_path<T, LAYOUT, 9, SHW>(P, w, e, numel, valid, M, c, Gs, ys, zs, dw); break;
+        case 11: fcb_path<T, LAYOUT, 11, SHW>(P, w, e, numel, valid, M, c, Gs, ys, zs, dw); break;
+        default: fcb_path<T, LAYOUT, 13, SHW>(P, w, e, numel, valid, M, c, Gs, ys, zs, dw); break;
       }
     }
     // messages and harmonic-gradient partials (lane = input channel)
@@ -241,23 +242,49 @@ fcconv_bwd_src_kernel(const Index* __restrict__ src, const Index* __restrict__ p
   }
 }
 
+template <typename T, typename Index, int LAYOUT, bool SHW>
+void fcconv_bwd_edges(const FcvBwdArgs& a, T* dwe, hipStream_t st) {
+  hipLaunchKernelGGL((fcconv_bwd_edge_kernel<T, Index, LAYOUT, SHW>), dim3(static_cast<unsigned>(a.n_nodes)), dim3(64),
+                     a.lds_bytes, st, static_cast<const T*>(a.x), static_cast<const T*>(a.sh),
+                     static_cast<const T*>(a.w), static_cast<const T*>(a.g), static_cast<const Index*>(a.src),
+                     static_cast<const Index*>(a.dst), a.n_src, a.n_edges, a.n_nodes, a.dim1, a.dim2, a.dimo,
+                     a.numel, a.mean, static_cast<T*>(a.dsh), dwe, static_cast<T*>(a.msg), a.blocks, a.qks, a.ents,
+                     a.bpaths, a.n_blocks, a.n_bpaths, a.nrows, a.ncomp, a.lane_bits);
+}
+
 template <typename T, typename Index, int LAYOUT>
 int fcconv_bwd_launch(const FcvBwdArgs& a) {
   const hipStream_t st = static_cast<hipStream_t>(a.stream);
-  if (a.n_nodes > 0 && a.n_edges > 0)
-    hipLaunchKernelGGL((fcconv_bwd_edge_kernel<T, Index, LAYOUT>), dim3(static_cast<unsigned>(a.n_nodes)), dim3(64),
-                       a.lds_bytes, st, static_cast<const T*>(a.x), static_cast<const T*>(a.sh),
-                       static_cast<const T*>(a.w), static_cast<const T*>(a.g), static_cast<const Index*>(a.src),
-                       static_cast<const Index*>(a.dst), a.n_src, a.n_edges, a.n_nodes, a.dim1, a.dim2, a.dimo,
-                       a.numel, a.mean, static_cast<T*>(a.dsh), static_cast<T*>(a.dw), static_cast<T*>(a.msg),
-                       a.blocks, a.qks, a.ents, a.bpaths, a.n_blocks, a.n_bpaths, a.nrows, a.ncomp, a.lane_bits);
-  else if (a.n_edges > 0) {  // no destinations: every edge lies outside the output
-    fill_zero(static_cast<T*>(a.dw), a.n_edges * a.numel, st);
+  // shared weights: per-edge gradient rows in the workspace, summed below
+  T* const dwe = a.shared_w ? reinterpret_cast<T*>(static_cast<unsigned char*>(a.msg) + a.dw_ws_off)
+                            : static_cast<T*>(a.dw);
+  if (a.n_nodes > 0 && a.n_edges > 0) {
+    if (a.shared_w)
+      fcconv_bwd_edges<T, Index, LAYOUT, true>(a, dwe, st);
+    else
+      fcconv_bwd_edges<T, Index, LAYOUT, false>(a, dwe, st);
+  } else if (a.n_edges > 0) {  // no destinations: every edge lies outside the output
+    fill_zero(static_cast<T*>(a.dw), a.shared_w ? a.numel : a.n_edges * a.numel, st);
     fill_zero(static_cast<T*>(a.dsh), a.n_edges * a.dim2, st);
     fill_zero(static_cast<T*>(a.msg), a.n_edges * a.dim1, st);
   }
   int rc = static_cast<int>(hipGetLastError());
-  if (rc || a.n_src == 0) return rc;
+  if (rc) return rc;
+  if (a.shared_w && a.n_nodes > 0 && a.n_edges > 0 && a.numel > 0) {
+    const int64_t chunks = (a.n_edges + kTpDwChunk - 1) / kTpDwChunk;
+    T* const dpart = reinterpret_cast<T*>(reinterpret_cast<unsigned char*>(dwe) +
+                                          round_up_256(a.n_edges * a.numel * static_cast<int64_t>(sizeof(T))));
+    hipLaunchKernelGGL((dw_edge_sum_kernel<T>), dim3(static_cast<unsigned>((a.numel + 255) / 256),
+                                                     static_cast<unsigned>(chunks)),
+                       dim3(256), 0, st, static_cast<const T*>(dwe), a.n_edges, a.numel, dpart);
+    const int64_t blocks = (a.numel + 255) / 256;
+    hipLaunchKernelGGL((fold_partials_kernel<T>), dim3(static_cast<unsigned>(blocks < 4096 ? blocks : 4096)),
+                       dim3(256), 0, st, static_cast<const T*>(dpart), static_cast<int>(chunks), a.numel,
+                       static_cast<T*>(a.dw));
+    rc = static_cast<int>(hipGetLastError());
+    if (rc) return rc;
+  }
+  if (a.n_src == 0) return rc;
   hipLaunchKernelGGL((fcconv_bwd_src_kernel<T, Index>), dim3(static_cast<unsigned>(a.n_src)), dim3(64), 0, st,
                      static_cast<const Index*>(a.src), static_cast<const Index*>(a.perm),
                      static_cast<const T*>(a.msg), a.n_edges, a.dim1, static_cast<T*>(a.dx));

@@ -347,10 +347,15 @@ def test_fctp_errors_and_workspace():
     wide = sp.fctp_create("80x0e", "0e", "8x0e")
     assert cv(wide._h, p, 4, p, p, 1, p, p, 0, 3, 2, p, None) == sp.E_UNSUPPORTED     # > 64 channels
     assert c(b"2x0e", b"2x0e", b"2x0e", 0, 0, 8 | 16, ctypes.byref(raw)) == sp.E_INVALID  # unknown flag
-    # its backward: per-edge weights only, workspace of the per-edge messages
+    # its backward: workspace of the per-edge messages, plus per-edge weight
+    # gradients and their partial sums per 1024 edges with one shared row
     bw = sp.lib.fctp_conv_bwd
     assert sp.fctp_conv_bwd_workspace(hc, 1000) == 1000 * hc.dim_in1 * 4
-    assert bw(hc._h, p, 4, p, p, 1, p, p, p, 0, 3, 2, p, p, p, p, p, 1 << 30, None) == sp.E_UNSUPPORTED  # shared
+    assert sp.fctp_conv_bwd_workspace(hc, 1000, 1) == 1000 * hc.dim_in1 * 4 \
+        + (1000 * hc.weight_numel * 4 + 255) // 256 * 256 + hc.weight_numel * 4
+    assert sp.fctp_conv_bwd_workspace(hc, 1, 1) == (hc.dim_in1 * 4 + 255) // 256 * 256  # one edge: its own row
+    assert bw(hc._h, p, 4, p, p, 2, p, p, p, 0, 3, 2, p, p, p, p, p, 1 << 30, None) == sp.E_INVALID      # w_rows
+    assert bw(hc._h, p, 4, p, p, 1, p, p, p, 0, 3, 2, p, p, p, p, p, 8, None) == sp.E_INVALID            # shared: workspace
     assert bw(hc._h, p, 4, p, p, 3, p, p, p, 0, 3, 2, p, p, p, p, p, 8, None) == sp.E_INVALID            # workspace
     assert bw(hc._h, p, 4, p, p, 3, p, p, None, 0, 3, 2, p, p, p, p, p, 1 << 30, None) == sp.E_INVALID   # no perm
     assert bw(hc._h, p, 4, p, p, 3, p, p, p, 0, 3, 2, p, p, None, p, p, 1 << 30, None) == sp.E_INVALID   # no dsh

@@ -193,6 +193,28 @@ def test_backward_parity(case, lay, dtype):
         check_scaled(a, b, c, dtype, f"fcconv backward case {case} {name}")
 
 
+@pytest.mark.parametrize("dtype", ["f32", "f64"])
+def test_backward_shared_weights(dtype):
+    """One weight row for every edge: grad_w [1, numel] is the sum of the
+    per-edge gradients (summed in chunks of 1024 edges, then in order);
+    dx and dsh as with that row repeated per edge."""
+    sp = _sp()
+    in1, in2, out = CASES[1][:3]
+    f = ofc.FullyConnectedTP(in1, in2, out)
+    h = sp.fctp_create(in1, in2, out, layout="ir_mul", dtype=dtype)
+    n_nodes = 900
+    x, sh, w, src, dst = _case_inputs(f, n_nodes, 8, 700, dtype, 360, shared=True)
+    assert w.shape[0] == 1 and dst.shape[0] > 2048
+    g = np.random.default_rng(361).standard_normal((n_nodes, f.dim_out)).astype(x.dtype)
+    announce(f"fcconv backward shared weights E={dst.shape[0]} {dtype}")
+    got = _bwd(sp, h, x, sh, w, g, src, dst, n_nodes, dtype)
+    assert got[2].shape == w.shape
+    ref = f.conv_vjp(x, sh, w, src, dst, n_nodes, g, layout="ir_mul")
+    scale = f.conv_vjp(x, sh, w, src, dst, n_nodes, g, layout="ir_mul", absolute=True)
+    for name, a, b, c in zip(("dx", "dsh", "dw"), got, ref, scale):
+        check_scaled(a, b, c, dtype, f"fcconv backward shared weights {name}")
+
+
 def test_backward_mean_and_outside_edges():
     """reduce="mean" scales the output gradient by 1/in-degree; edges whose
     destination is past the last row get zero gradients."""

@@ -277,6 +277,13 @@ def test_conv_vjp_adjoint_identities(reduce):
         assert np.isclose(np.sum(g * F(v1, x2, w)), np.sum(dx1 * v1), rtol=1e-11)
         assert np.isclose(np.sum(g * F(x1, v2, w)), np.sum(dx2 * v2), rtol=1e-11)
         assert np.isclose(np.sum(g * F(x1, x2, vw)), np.sum(dw * vw), rtol=1e-11)
+        # one shared weight row: the forward is still linear in it
+        ws = rng.normal(size=(1, f.weight_numel))
+        _, s2, sw = f.conv_vjp(x1, x2, ws, src, dst, 5, g, layout=lay, reduce=reduce)
+        vs = rng.normal(size=ws.shape)
+        assert sw.shape == ws.shape
+        assert np.isclose(np.sum(g * F(x1, x2, vs)), np.sum(sw * vs), rtol=1e-11)
+        assert np.isclose(np.sum(g * F(x1, v2, ws)), np.sum(s2 * v2), rtol=1e-11)
     # sources no edge reads get zero; absolute mode bounds every gradient
     unread = np.setdiff1d(np.arange(6), src)
     assert np.count_nonzero(dx1[unread]) == 0
