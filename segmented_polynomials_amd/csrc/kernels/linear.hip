@@ -251,11 +251,14 @@ linear_dw_kernel(const T* __restrict__ x, const T* __restrict__ g, T* __restrict
   int c_lo = 0, c_hi = 0;
   bool sorted = false;
   const int s_begin = r_begin / d, s_end = (r_end - 1) / d + 1;  // the chunk's samples
+  // the chunk's classes in LDS for the masked passes (-1: outside [0, num_classes))
+  __shared__ int cls_s[CLS ? kLinDwRows : 1];
   if constexpr (CLS) {
     int lo = num_classes, hi = -1, unsorted = 0;
     for (int sm = s_begin + tid; sm < s_end; sm += kLinThreads) {
       const int64_t c = static_cast<int64_t>(cls[sm]);
       if (sm + 1 < s_end && c > static_cast<int64_t>(cls[sm + 1])) unsorted = 1;
+      cls_s[sm - s_begin] = c >= 0 && c < num_classes ? static_cast<int>(c) : -1;
       if (c >= 0 && c < num_classes) {
         lo = static_cast<int>(c) < lo ? static_cast<int>(c) : lo;
         hi = static_cast<int>(c) > hi ? static_cast<int>(c) : hi;
@@ -316,7 +319,7 @@ linear_dw_kernel(const T* __restrict__ x, const T* __restrict__ g, T* __restrict
   int a_n = (kb + rk_a) / d, a_m = (kb + rk_a) - a_n * d;
   int b_n = (kb + rk_b) / d, b_m = (kb + rk_b) - b_n * d;
   // rows of another class than cc contribute nothing
-  auto in_class = [&](int nn) { return !mask || static_cast<int64_t>(cls[nn]) == cc; };
+  auto in_class = [&](int nn) { return !mask || cls_s[nn - s_begin] == cc; };
   typename M::acc_t acc[kMT][kNT];
 #pragma unroll
   for (int a = 0; a < kMT; ++a)
