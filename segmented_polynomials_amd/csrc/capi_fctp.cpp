@@ -217,7 +217,7 @@ int build_pass(segpoly_fctp* h, int which) {
       t.ent = static_cast<int>(h->ents.size());
       const int which_idx = which == 0 ? 2 : (which == 1 ? 0 : 1);
       t.T = add_entries(h->ents, real_cg(a.l, b.l, o.l), d1, d2, d3, which_idx, h->alpha[pa.o]);
-      if (t.T < 0) return fail(SEGPOLY_E_UNSUPPORTED, "more than 8 couplings per component in one path");
+      if (t.T < 0) return fail(SEGPOLY_E_UNSUPPORTED, "more than 16 couplings per component in one path");
       if (t.p_m > t.q_m) {  // Q, held in registers along K, is the side with more channels
         std::swap(t.p_op, t.q_op);
         std::swap(t.p_d, t.q_d);
@@ -262,7 +262,7 @@ int build_dw(segpoly_fctp* h) {
     q.s_p = static_cast<int64_t>(b.mul) * o.mul, q.s_q = o.mul;
     q.ent = static_cast<int>(h->ents.size());
     q.T = add_entries(h->ents, real_cg(a.l, b.l, o.l), d1, d2, d3, 2, h->alpha[pa.o]);
-    if (q.T < 0) return fail(SEGPOLY_E_UNSUPPORTED, "more than 8 couplings per component in one path");
+    if (q.T < 0) return fail(SEGPOLY_E_UNSUPPORTED, "more than 16 couplings per component in one path");
     if (q.p_m > q.q_m) {  // Q, the 32-channel side of a tile, has more channels
       std::swap(q.p_op, q.q_op);
       std::swap(q.p_d, q.q_d);

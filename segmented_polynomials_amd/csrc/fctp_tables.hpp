@@ -21,9 +21,11 @@ namespace segpoly {
 // Entries per (term, result component) rounded up to a compiled class: a
 // launch runs one class, the largest among its terms (smaller terms are
 // zero-padded).
-constexpr int fc_t_class(int t) { return t <= 1 ? 1 : t <= 2 ? 2 : t <= 3 ? 3 : t <= 4 ? 4 : t <= 6 ? 6 : 8; }
+constexpr int fc_t_class(int t) {
+  return t <= 1 ? 1 : t <= 2 ? 2 : t <= 3 ? 3 : t <= 4 ? 4 : t <= 6 ? 6 : t <= 8 ? 8 : 16;
+}
 
-constexpr int kFcMaxT = 8;       // coupling entries per (term, result component)
+constexpr int kFcMaxT = 16;      // coupling entries per (term, result component): every l <= 6
 constexpr int kFcMaxRes = 32;    // result blocks per pass
 constexpr int kFcRT = 2;         // 16-row MFMA tiles per wave (4 waves per workgroup)
 constexpr int kFcRowsMax = 64 * kFcRT;  // rows (sample, component) per tile

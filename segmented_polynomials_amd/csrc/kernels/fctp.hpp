@@ -750,7 +750,8 @@ int fctp_launch_tn(const FcArgs& a, const FcTiles& t) {
     case 3: return fctp_launch_k<T, LAYOUT, TN, 3>(a, t);
     case 4: return fctp_launch_k<T, LAYOUT, TN, 4>(a, t);
     case 6: return fctp_launch_k<T, LAYOUT, TN, 6>(a, t);
-    default: return fctp_launch_k<T, LAYOUT, TN, 8>(a, t);
+    case 8: return fctp_launch_k<T, LAYOUT, TN, 8>(a, t);
+    default: return fctp_launch_k<T, LAYOUT, TN, 16>(a, t);
   }
 }
 
@@ -787,7 +788,8 @@ int fctp_dw_launch(const FcDwArgs& a, const FcDwTiles& t) {
     case 3: rc = fctp_dw_launch_k<T, LAYOUT, 3>(a, t); break;
     case 4: rc = fctp_dw_launch_k<T, LAYOUT, 4>(a, t); break;
     case 6: rc = fctp_dw_launch_k<T, LAYOUT, 6>(a, t); break;
-    default: rc = fctp_dw_launch_k<T, LAYOUT, 8>(a, t); break;
+    case 8: rc = fctp_dw_launch_k<T, LAYOUT, 8>(a, t); break;
+    default: rc = fctp_dw_launch_k<T, LAYOUT, 16>(a, t); break;
   }
   if (rc || a.numel == 0) return rc;
   const int64_t blocks = (a.numel + 255) / 256;

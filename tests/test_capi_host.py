@@ -310,8 +310,9 @@ def test_fctp_errors_and_workspace():
     assert c(b"2x0q", b"2x0e", b"2x0e", 0, 0, 0, ctypes.byref(raw)) == sp.E_PARSE
     assert c(b"0 + 1", b"0e", b"0e", 0, 0, 0, ctypes.byref(raw)) == sp.E_PARSE           # SO(3) with O(3)
     assert c(b"1x7o", b"1x0e", b"1x7o", 0, 0, 0, ctypes.byref(raw)) == sp.E_UNSUPPORTED  # l > 6
-    # 3 x 3 -> 3 couples up to 10 component pairs per component: beyond 8
-    assert c(b"2x3o", b"1x3o", b"2x2e", 0, 0, 0, ctypes.byref(raw)) == sp.E_UNSUPPORTED
+    # 3 x 3 -> 2 couples up to 10 component pairs per component (the 16-entry class)
+    assert c(b"2x3o", b"1x3o", b"2x2e", 0, 0, 0, ctypes.byref(raw)) == sp.OK
+    assert sp.lib.fctp_destroy(raw) == sp.OK
     h = sp.fctp_create("32x0e+32x1o", "32x0e+32x1o", "32x0e+32x1o")
     info = (ctypes.c_int64 * 4)()
     assert sp.lib.fctp_path_info(h._h, 4, info) == sp.E_INVALID

@@ -73,6 +73,8 @@ CASES = [
     ("3x1o", "2x2e", "2x1o", 65),                    # forward 4, dx1 4, dx2 3
     ("2x2e", "3x2e", "2x2e", 50),                    # 6 everywhere
     ("2x2e", "2x2e", "2x4e", 45),                    # forward 6, dx1 8, dx2 8
+    ("2x3o", "1x3o", "2x1e+2x2e", 40),               # 3 x 3: up to 10 entries (class 16)
+    ("1x4e", "2x4e", "1x3e+1x4e", 30),               # 4 x 4: up to 14 entries (class 16)
 ]
 
 
