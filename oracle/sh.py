@@ -59,6 +59,48 @@ def real_sh_l(l, vecs, normalize=True):
     return out
 
 
+def _abs_terms_poly(l, x, y, z, r2):
+    """The polynomial of :func:`real_sh_l_abs` at (x, y, z) with r2 standing
+    for x^2 + y^2 + z^2 (or 1 on the sphere): every coefficient replaced by
+    its absolute value, evaluated without taking absolute values of the
+    variables (so it can be differentiated)."""
+    out = np.empty(np.shape(x) + (2 * l + 1,))
+    for m in range(-l, l + 1):
+        a = abs(m)
+        n = math.sqrt((2 * l + 1) * math.factorial(l - a) / math.factorial(l + a))
+        coef = np.zeros(l + 1)
+        coef[l] = 1.0
+        pw = npleg.leg2poly(npleg.legder(coef, a) if a > 0 else coef)   # power series of P_l^(a)
+        # l - a - k is even wherever c_k != 0 (P_l^(a) has the parity of l - a)
+        zpart = sum(abs(c) * z ** k * r2 ** ((l - a - k) // 2) for k, c in enumerate(pw) if c != 0)
+        parity = 0 if m >= 0 else 1                                       # Re: even j, Im: odd j
+        xy = sum(math.comb(a, j) * x ** (a - j) * y ** j for j in range(parity, a + 1, 2)) if a else 1.0
+        out[..., l + m] = (math.sqrt(2.0) if m != 0 else 1.0) * n * zpart * xy
+    return out
+
+
+def real_sh_l_abs(l, vecs, normalize=True):
+    """Sum of the absolute values of the terms of :func:`real_sh_l`, the
+    forward-error scale of the parity gate.
+
+    Each harmonic is written as N P_l^(m)(z) times Re or Im of (x + i y)^m;
+    expanding P_l^(m) as a power series in z and (x + i y)^m by the binomial
+    theorem gives one monomial x^(m-j) y^j z^k per pair (j, k), so the sum of
+    the absolute terms is N (sum_k |c_k| |z|^k) (sum_j binom(m, j) |x|^(m-j) |y|^j)
+    over the j of the real (even) or imaginary (odd) part.  Without
+    normalisation the homogeneous form carries r^(l-m-k) beside each z^k."""
+    v = np.asarray(vecs, dtype=np.float64)
+    r = np.linalg.norm(v, axis=-1)
+    u = np.abs(v if not normalize else v / r[..., None])
+    r2 = r * r if not normalize else np.ones_like(r)
+    return _abs_terms_poly(l, u[..., 0], u[..., 1], u[..., 2], r2)
+
+
+def real_sh_abs(ls, vecs, normalize=True):
+    """Concatenation of :func:`real_sh_l_abs` for each l in ``ls``."""
+    return np.concatenate([real_sh_l_abs(l, vecs, normalize) for l in ls], axis=-1)
+
+
 def real_sh(ls, vecs, normalize=True):
     """Concatenation of :func:`real_sh_l` for each l in ``ls`` (the layout
     of an ``0e + 1o + 2e + ...`` operand with multiplicity one)."""
@@ -70,15 +112,15 @@ def real_sh_vjp(ls, vecs, g, normalize=True):
     the columns of ``real_sh(ls, vecs)``, return dL/d(vecs) [..., 3].
 
     Without normalisation every column is a homogeneous polynomial of degree
-    l in (x, y, z), so its derivative along an axis at t = 0 of
-    Y(v + t e_a) is the derivative of a polynomial in t of degree l, which
-    the five-point quotient (8 (f(h) - f(-h)) - (f(2h) - f(-2h))) / (12 h)
-    gives exactly for l <= 4 (up to rounding).  With normalisation Y depends
-    on u = v / |v| only, and the chain rule gives
-    dY/dv = (I - u u^T) / |v| * grad P(u), P the polynomial of the
-    unnormalised harmonics (its radial part drops out)."""
-    if max(ls) > 4:
-        raise ValueError("the exact difference quotient covers l <= 4")
+    l in (x, y, z), so along an axis t -> Y(v + t e_a) is a polynomial in t of
+    degree l, whose derivative at t = 0 the seven-point central quotient
+    (45 (f(h) - f(-h)) - 9 (f(2h) - f(-2h)) + (f(3h) - f(-3h))) / (60 h)
+    gives exactly for degree <= 6 (its error term is the seventh derivative),
+    up to rounding.  With normalisation Y depends on u = v / |v| only, and the
+    chain rule gives dY/dv = (I - u u^T) / |v| * grad P(u), P the polynomial
+    of the unnormalised harmonics (its radial part drops out)."""
+    if max(ls) > 6:
+        raise ValueError("the exact seven-point quotient covers l <= 6")
     v = np.asarray(vecs, dtype=np.float64)
     g = np.asarray(g, dtype=np.float64)
     r = np.linalg.norm(v, axis=-1, keepdims=True)
@@ -89,10 +131,42 @@ def real_sh_vjp(ls, vecs, g, normalize=True):
         e = np.zeros(3)
         e[a] = 1.0
         f = lambda t: np.sum(g * real_sh(ls, base + t * e, normalize=False), axis=-1)
-        grad[..., a] = (8 * (f(h[..., 0:1] * 1) - f(-h[..., 0:1] * 1)) - (f(2 * h[..., 0:1]) - f(-2 * h[..., 0:1]))) \
-            / (12 * h[..., 0])
+        d1, d2, d3 = (f(k * h) - f(-k * h) for k in (1, 2, 3))
+        grad[..., a] = (45 * d1 - 9 * d2 + d3) / (60 * h[..., 0])
     if not normalize:
         return grad
     u = base
     radial = np.sum(u * grad, axis=-1, keepdims=True)
     return (grad - u * radial) / r
+
+
+def real_sh_vjp_abs(ls, vecs, g, normalize=True):
+    """Forward-error scale of :func:`real_sh_vjp`: the same product with |g|
+    and the gradient of the absolute-term polynomial of
+    :func:`real_sh_l_abs` at (|x|, |y|, |z|) (each monomial of dY/dv_a
+    enters with its absolute value), then, with normalisation, the sums of
+    absolute terms of the tangential projection (|grad| + |u| (|u| . |grad|)) / |v|.
+    Same seven-point quotient as :func:`real_sh_vjp` (exact, degree <= 6)."""
+    if max(ls) > 6:
+        raise ValueError("the exact seven-point quotient covers l <= 6")
+    v = np.asarray(vecs, dtype=np.float64)
+    g = np.abs(np.asarray(g, dtype=np.float64))
+    r = np.linalg.norm(v, axis=-1, keepdims=True)
+    base = np.abs(v / r if normalize else v)
+    h = 0.5 * np.maximum(base.max(axis=-1, keepdims=True), 1e-3)
+    grad = np.zeros(v.shape[:-1] + (3,))
+    for a in range(3):
+        e = np.zeros(3)
+        e[a] = 1.0
+
+        def f(t):
+            p = base + t * e
+            r2 = np.sum(p * p, axis=-1)
+            return np.sum(g * np.concatenate([_abs_terms_poly(l, p[..., 0], p[..., 1], p[..., 2], r2)
+                                               for l in ls], axis=-1), axis=-1)
+        d1, d2, d3 = (f(k * h) - f(-k * h) for k in (1, 2, 3))
+        grad[..., a] = (45 * d1 - 9 * d2 + d3) / (60 * h[..., 0])
+    if not normalize:
+        return grad
+    radial = np.sum(base * grad, axis=-1, keepdims=True)
+    return (grad + base * radial) / r
