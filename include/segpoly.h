@@ -123,7 +123,8 @@ typedef struct segpoly_fctp* fctp_handle;
  * output type (l, natural parity (-1)^l first); the weight row holds one
  * segment of mul channels per path in that order.  Coefficients: real-basis
  * Clebsch-Gordan tensors scaled so that sum_ij C_ijk C_ijk' = delta_kk'.
- * Errors: E_PARSE (string), E_UNSUPPORTED (in2 multiplicity != 1, l > 8),
+ * Errors: E_PARSE (string), E_UNSUPPORTED (in2 multiplicity != 1, or a
+ * block with l > 6 in any of the three strings, so no path reaches l > 6),
  * E_INVALID (null out, bad enum).  Touches no GPU.
  */
 int tp_create(const char* irreps_in1, const char* irreps_in2, const char* irreps_out, int layout,
@@ -577,7 +578,8 @@ int sh_bwd(int lmax, int normalize, int dtype, const void* vec, const void* grad
            void* stream);
 
 /* segpoly_real_cg: the real coupling tensor of l1 x l2 -> l3 (the same
- * coefficients the paths use), row-major [2l1+1][2l2+1][2l3+1]. */
+ * coefficients the paths use), row-major [2l1+1][2l2+1][2l3+1]; zeros when
+ * the triangle rule fails.  l1, l2, l3 in [0, 6] (E_UNSUPPORTED otherwise). */
 int segpoly_real_cg(int l1, int l2, int l3, double* out);
 
 /* Message of the last failure on the calling thread ("" if none). */

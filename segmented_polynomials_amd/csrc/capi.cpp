@@ -113,7 +113,7 @@ const char* segpoly_version(void) { return "segpoly 0.1.0 (gfx950)"; }
 
 int segpoly_real_cg(int l1, int l2, int l3, double* out) {
   if (!out) return fail(SEGPOLY_E_INVALID, "null output");
-  if (l1 < 0 || l2 < 0 || l3 < 0 || l1 > kMaxL || l2 > kMaxL || l3 > 2 * kMaxL)
+  if (l1 < 0 || l2 < 0 || l3 < 0 || l1 > kMaxL || l2 > kMaxL || l3 > kMaxL)
     return fail(SEGPOLY_E_UNSUPPORTED, "l outside the supported range");
   const auto& t = real_cg(l1, l2, l3);
   std::memcpy(out, t.data(), t.size() * sizeof(double));

@@ -21,6 +21,8 @@ TPDescriptor build_tp(const std::string& s1, const std::string& s2, const std::s
   d.in1 = parse_irreps(s1);
   d.in2 = parse_irreps(s2);
   std::vector<Irrep> filt = parse_irreps(so);
+  for (const auto& r : filt)
+    if (r.l > kMaxL) throw std::invalid_argument("output filter has l above the supported maximum");
   for (const auto& r : d.in2)
     if (r.mul != 1) throw std::invalid_argument("input 2 must have multiplicity 1 per block");
   for (const auto& r : d.in1)

@@ -51,12 +51,16 @@ struct TPDescriptor {
 };
 
 // Throws ParseError on bad strings, std::invalid_argument on unsupported
-// input (input-2 multiplicity other than 1, l above the supported maximum).
+// input (input-2 multiplicity other than 1, an l above kMaxL in any of the
+// three strings, so that no path couples to an output above kMaxL).
 // merge: the paths of one output type sum into one block of that type (all
 // of them must have the same multiplicity); output blocks in type order.
 TPDescriptor build_tp(const std::string& irreps_in1, const std::string& irreps_in2,
                       const std::string& irreps_out, bool merge = false);
 
-constexpr int kMaxL = 8;
+// Largest l of any block (inputs and output filter).  Every coupling tensor
+// the builder can produce (l1, l2, lo <= 6) is compared entry by entry with
+// the oracle's exact-arithmetic construction on the host.
+constexpr int kMaxL = 6;
 
 }  // namespace segpoly

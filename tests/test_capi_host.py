@@ -33,13 +33,20 @@ def test_exports_every_declared_symbol():
     assert "gfx950" in sp.version()
 
 
-@pytest.mark.parametrize("l1,l2", [(a, b) for a in range(5) for b in range(5)])
+@pytest.mark.parametrize("l1,l2", [(a, b) for a in range(7) for b in range(7)])
 def test_real_cg_matches_oracle(l1, l2):
-    for l3 in range(abs(l1 - l2), l1 + l2 + 1):
+    """Every coupling the library can build (l1, l2, l3 <= 6) against the
+    oracle's exact-arithmetic tensor, entry by entry and in its zero pattern;
+    l3 outside the triangle gives zeros, l above 6 fails closed."""
+    for l3 in range(0, 7):
         a = sp.real_cg(l1, l2, l3)
         b = ocg.real_cg(l1, l2, l3)
         assert np.abs(a - b).max() <= 2e-16 * max(1, np.abs(b).max()), (l1, l2, l3)
         assert np.array_equal(a != 0, b != 0)
+    out = np.zeros(15 * 15 * 15)
+    buf = out.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+    assert sp.lib.segpoly_real_cg(l1, l2, 7, buf) == sp.E_UNSUPPORTED
+    assert sp.lib.segpoly_real_cg(7, l2, l1, buf) == sp.E_UNSUPPORTED
 
 
 def _compare_tp(in1, in2, filt, layout="mul_ir"):
@@ -78,13 +85,13 @@ def test_page_descriptor():
     assert h.irreps_out == "32x0e+32x0e+32x1o+32x1o"
 
 
-_irrep = st.tuples(st.integers(1, 5), st.integers(0, 3), st.sampled_from("eo"))
+_irrep = st.tuples(st.integers(1, 5), st.integers(0, 6), st.sampled_from("eo"))
 
 
 @settings(max_examples=60, deadline=None)
-@given(st.lists(_irrep, min_size=1, max_size=4), st.lists(st.tuples(st.integers(0, 3), st.sampled_from("eo")),
+@given(st.lists(_irrep, min_size=1, max_size=4), st.lists(st.tuples(st.integers(0, 6), st.sampled_from("eo")),
                                                           min_size=1, max_size=4),
-       st.lists(st.tuples(st.integers(0, 4), st.sampled_from("eo")), min_size=1, max_size=6))
+       st.lists(st.tuples(st.integers(0, 6), st.sampled_from("eo")), min_size=1, max_size=6))
 def test_fuzz_tp_descriptor(b1, b2, bo):
     in1 = "+".join(f"{m}x{l}{p}" for m, l, p in b1)
     in2 = "+".join(f"{l}{p}" for l, p in b2)
@@ -141,6 +148,13 @@ def test_create_errors():
     assert _raw_create(b"3x", b"0e", b"0e", 0, 0, 0)[0] == sp.E_PARSE
     assert _raw_create(b"4x0e", b"2x1o", b"1o", 0, 0, 0)[0] == sp.E_UNSUPPORTED
     assert _raw_create(b"4x9e", b"0e", b"9e", 0, 0, 0)[0] == sp.E_UNSUPPORTED
+    # the envelope is l <= 6 on every side: 6 builds, 7 anywhere fails closed
+    rc, raw = _raw_create(b"4x6e", b"0e+6e", b"0e+6e", 0, 0, 0)
+    assert rc == sp.OK
+    sp.lib.tp_destroy(raw)
+    assert _raw_create(b"4x7o", b"0e", b"7o", 0, 0, 0)[0] == sp.E_UNSUPPORTED
+    assert _raw_create(b"4x3o", b"4e", b"7o", 0, 0, 0)[0] == sp.E_UNSUPPORTED
+    assert _raw_create(b"4x3o", b"7o", b"4e", 0, 0, 0)[0] == sp.E_UNSUPPORTED
     assert _raw_create(b"4x0e", b"0e", b"0e", 7, 0, 0)[0] == sp.E_INVALID
     assert _raw_create(b"4x0e", b"0e", b"0e", 0, 5, 0)[0] == sp.E_INVALID
     assert _raw_create(b"4x0e", b"0e", b"0e", 0, 0, 64)[0] == sp.E_INVALID

@@ -155,6 +155,37 @@ def test_generic_kernel(case):
     check_scaled(got, ref, scale, "f32", f"generic {in1}")
 
 
+@pytest.mark.parametrize("case", [
+    ("5x5o+3x6e", "0e+1o+2e", "4e+4o+5e+5o+6e+6o", "mul_ir", "f32"),
+    ("2x6o+3x4e", "6e+5o", "0e+1o+2e+3o+4e+5o+6e+0o+1e+2o+3e+4o+5e+6o", "ir_mul", "f32"),
+    ("3x6e+2x5o", "6e+4e", "0e+2e+4e+6e+1o+3o+5o", "ir_mul", "f64"),
+    ("3x6e+2x5o", "6e+4e", "0e+2e+4e+6e+1o+3o+5o", "mul_ir", "f64"),
+])
+def test_generic_kernel_high_l(case):
+    """Inputs and outputs up to l = 6, the top of the descriptor envelope:
+    every coupling with l1, l2 in 4..6 runs through the table-driven kernel
+    (the second operand is any per-edge block, here N(0,1) values)."""
+    sp = _sp()
+    import torch
+    in1, in2, filt, layout, dtype = case
+    o = otp.ChannelwiseTP(in1, in2, filt)
+    h = sp.tp_create(in1, in2, filt, layout=layout, dtype=dtype)
+    assert h.kernel_name == "tp_conv_generic"
+    rng = np.random.default_rng(31)
+    n_src, n_dst, n_e = 23, 41, 260
+    src = rng.integers(0, n_src, n_e).astype(np.int64)
+    dst = np.sort(rng.integers(0, n_dst, n_e)).astype(np.int64)
+    npd = np.float32 if dtype == "f32" else np.float64
+    inp = dict(x=rng.standard_normal((n_src, o.dim_in1)).astype(npd).astype(np.float64),
+               sh=rng.standard_normal((n_e, o.dim_in2)).astype(npd).astype(np.float64),
+               w=rng.standard_normal((n_e, o.weight_numel)).astype(npd).astype(np.float64),
+               src=src, dst=dst, n_nodes=n_dst)
+    announce(f"tp generic high l {in1} x {in2} {layout} {dtype}")
+    got = _run(sp, h, inp, idx_dtype=torch.int64)
+    ref, scale = _oracle(o, inp, layout)
+    check_scaled(got, ref, scale, dtype, f"generic high l {in1} {layout} {dtype}")
+
+
 def test_float64_specialized_and_generic():
     sp = _sp()
     wl = workloads.WORKLOADS[3]
