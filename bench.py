@@ -27,6 +27,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0            # MI355X HBM3E, published
 FP32_VALU_PEAK_TFLOPS = 78.6      # 256 CU x 4 SIMD x 16 lanes x 2 flop x 2.4 GHz (no packed FP32)
+FP32_PUBLISHED_TFLOPS = 157.3     # MI355X published FP32 vector figure (with packed FP32)
 FP32_MFMA_PEAK_TFLOPS = 157.3     # MI355X dense FP32 matrix, published
 METRIC = "edges/sec + achieved HBM GB/s (fraction of peak) for fused equivariant TP-conv"
 
@@ -273,7 +274,12 @@ def main():
 
     if not args.no_extras or args.with_backward:
         del out
-        result["tp_conv_bwd"] = backward(torch, sp, workloads, h, x, sh, w, src, dst, N, E, args)
+        other = "mul_ir" if layout == "ir_mul" else "ir_mul"
+        hs = [h] if args.no_extras else [h, sp.tp_create(wl.irreps_in1, wl.irreps_in2, wl.irreps_out, layout=other)]
+        bw = backward(torch, sp, workloads, hs, x, sh, w, src, dst, N, E, args)
+        result["tp_conv_bwd"] = bw[layout]
+        if len(hs) > 1:
+            result[f"tp_conv_bwd_{other}"] = bw[other]
 
     if not args.no_extras:
         import gc
@@ -306,7 +312,10 @@ def main():
             "hbm": {"achieved": s_bytes / (k3 * 1e-3) / 1e9, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                     "frac": s_bytes / (k3 * 1e-3) / 1e9 / HBM_PEAK_GBPS, "algorithmic_bytes": s_bytes},
             "alu": {"achieved": s_flops / (k3 * 1e-3) / 1e12, "peak": FP32_VALU_PEAK_TFLOPS, "unit": "TFLOP/s",
-                    "frac": s_flops / (k3 * 1e-3) / 1e12 / FP32_VALU_PEAK_TFLOPS, "algorithmic_flops": s_flops},
+                    "frac": s_flops / (k3 * 1e-3) / 1e12 / FP32_VALU_PEAK_TFLOPS, "algorithmic_flops": s_flops,
+                    "peak_kind": "derived: 256 CU x 4 SIMD x 16 lanes x 2 flop (FMA) x 2.4 GHz, packed FP32 "
+                                 "not used; the published FP32 vector figure (157.3) counts packed FP32",
+                    "frac_of_published_fp32": s_flops / (k3 * 1e-3) / 1e12 / FP32_PUBLISHED_TFLOPS},
         }
         # backward of the symmetric contraction on the same atoms
         sg = torch.from_numpy(workloads.output_gradient(s5.n_atoms, hs.dim_out, "f32", seed=59)).to(dev)
@@ -361,6 +370,9 @@ def main():
         note("oracle timed on one core")
         result["cpu_baseline_parallel"] = parallel_oracle(wl, base_inp, layout)
         note("oracle timed on all cores")
+        if not args.no_extras:
+            result["cpu_baseline_by_config"] = oracle_by_config(workloads)
+            note("oracle timed on the other configurations")
 
     print(json.dumps(result), flush=True)
 
@@ -370,9 +382,41 @@ def _oracle_warm(_):
     so that every worker takes one of these tasks."""
     import threadpoolctl  # noqa: F401
 
+    import oracle.symcon  # noqa: F401
     import oracle.tp  # noqa: F401
     time.sleep(0.5)
     return os.getpid()
+
+
+_SYMCON_CACHE = {}
+
+
+def _symcon_object(irreps):
+    from oracle import symcon as osym
+    if irreps not in _SYMCON_CACHE:
+        _SYMCON_CACHE[irreps] = osym.SymmetricContraction(*irreps)
+    return _SYMCON_CACHE[irreps]
+
+
+def _symcon_prepare(irreps):
+    """Build the oracle's contraction in a worker before the timed run (its
+    basis construction is set-up, not evaluation), then wait so that every
+    worker takes one of these tasks."""
+    _symcon_object(irreps)
+    time.sleep(0.5)
+    return os.getpid()
+
+
+def _symcon_chunk(a):
+    """One worker of the parallel symmetric-contraction oracle run."""
+    from threadpoolctl import threadpool_limits
+
+    irreps, x, species, w, layout = a
+    so = _symcon_object(irreps)
+    with threadpool_limits(1):
+        t0 = time.perf_counter()
+        so.eval(x, species, w, layout=layout)
+        return time.perf_counter() - t0
 
 
 def _oracle_chunk(a):
@@ -422,30 +466,130 @@ def parallel_oracle(wl, inp, layout):
                       f"over {workers} processes of one thread each, {wall:.1f} s"}
 
 
-def backward(torch, sp, workloads, h, x, sh, w, src, dst, N, E, args):
-    """Vector-Jacobian product on the same graph: both kernels per call.
-    Bytes: the operands and gradients once each (x, g and dx per node; w,
-    sh, dw, dsh and the three index arrays per edge) plus the per-edge
-    source messages written by the first kernel and read by the second."""
-    g = torch.from_numpy(workloads.output_gradient(N, h.dim_out, "f32", seed=74)).to(x.device)
+def _tp_dst_chunks(wl, inp, layout, parts):
+    """Split a dst-sorted graph into `parts` destination ranges; each chunk
+    carries only the source rows its edges read (renumbered)."""
+    import numpy as np
+    n, dst = inp["n_nodes"], inp["dst"]
+    bounds = np.linspace(0, n, parts + 1).astype(int)
+    chunks = []
+    for a, b in zip(bounds[:-1], bounds[1:]):
+        e0, e1 = int(np.searchsorted(dst, a)), int(np.searchsorted(dst, b))
+        rows, src_local = np.unique(inp["src"][e0:e1], return_inverse=True)
+        chunks.append(((wl.irreps_in1, wl.irreps_in2, wl.irreps_out), inp["x"][rows], inp["sh"][e0:e1],
+                       inp["w"][e0:e1], src_local.astype(np.int64), dst[e0:e1], int(a), int(b), layout))
+    return chunks
+
+
+def oracle_by_config(workloads):
+    """The oracle as it stands on the other configurations (float64 NumPy):
+    one core (median of three runs for the batch and the molecules, one run
+    for the 2k-node graph, a bounded sample of the 50k-atom contraction), and
+    the same work split over the host cores (at most 16 processes of one
+    thread each, by destination range or atom range; worker start-up not
+    timed).  Context only: the oracle is the correctness reference."""
+    import concurrent.futures as cf
+    import multiprocessing as mp
+
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    from oracle import symcon as osym, tp as otp
+    workers = max(1, min(16, os.cpu_count() or 1))
+    ex = cf.ProcessPoolExecutor(max_workers=workers, mp_context=mp.get_context("spawn"))
+    res = {"host_cpu": _cpu_model(), "host_nproc": os.cpu_count()}
+    try:
+        list(ex.map(_oracle_warm, range(workers), timeout=120))
+        for n in (1, 2, 3):
+            wl = workloads.WORKLOADS[n]
+            o = otp.ChannelwiseTP(wl.irreps_in1, wl.irreps_in2, wl.irreps_out)
+            inp = workloads.tp_inputs(wl, o.weight_fan_in())
+            lay = wl.layouts[0]
+            E = inp["sh"].shape[0]
+            runs = 3 if n in (1, 2) else 1
+            times = []
+            with threadpool_limits(1):
+                for _ in range(runs):
+                    t0 = time.perf_counter()
+                    o.conv(inp["x"], inp["sh"], inp["w"], inp["src"], inp["dst"], inp["n_nodes"], layout=lay)
+                    times.append(time.perf_counter() - t0)
+            dt = sorted(times)[len(times) // 2]
+            rec = {"workload": wl.name, "edges": E,
+                   "one_core": {"s": dt, "value": E / dt, "unit": "edges/s", "cores": 1,
+                                "sample": f"whole workload, {'median of 3 runs' if runs == 3 else 'one run'}"}}
+            if inp["src"] is not None:
+                chunks = _tp_dst_chunks(wl, inp, lay, workers)
+                t0 = time.perf_counter()
+                list(ex.map(_oracle_chunk, chunks, timeout=300))
+                wall = time.perf_counter() - t0
+                rec["all_cores"] = {"s": wall, "value": E / wall, "unit": "edges/s", "cores": workers,
+                                    "sample": f"whole workload split by destination range over {workers} processes"}
+            res[wl.name] = rec
+            note(f"oracle timed on {wl.name}")
+        s5 = workloads.WORKLOADS[5]
+        so = osym.SymmetricContraction(s5.irreps_in, s5.irreps_out)
+        per_worker, one = 500, 1000
+        si = workloads.symcon_inputs(s5, so.weight_fan_in(), n_atoms=max(one, workers * per_worker))
+        with threadpool_limits(1):
+            t0 = time.perf_counter()
+            so.eval(si["x"][:one], si["species"][:one], si["w"], layout="ir_mul")
+            dt = time.perf_counter() - t0
+        rec = {"workload": s5.name,
+               "one_core": {"s": dt, "value": one / dt, "unit": "atoms/s", "cores": 1,
+                            "sample": f"first {one} of the {s5.n_atoms} atoms, ir_mul"}}
+        list(ex.map(_symcon_prepare, [(s5.irreps_in, s5.irreps_out)] * workers, timeout=300))
+        chunks = [((s5.irreps_in, s5.irreps_out), si["x"][k * per_worker:(k + 1) * per_worker],
+                   si["species"][k * per_worker:(k + 1) * per_worker], si["w"], "ir_mul") for k in range(workers)]
+        t0 = time.perf_counter()
+        list(ex.map(_symcon_chunk, chunks, timeout=300))
+        wall = time.perf_counter() - t0
+        rec["all_cores"] = {"s": wall, "value": workers * per_worker / wall, "unit": "atoms/s", "cores": workers,
+                            "sample": f"first {workers * per_worker} atoms, {per_worker} per process"}
+        res[s5.name] = rec
+    except Exception as err:   # a worker that cannot start must not cost the bench line
+        ex.shutdown(wait=False, cancel_futures=True)
+        res["error"] = f"{type(err).__name__}: {err}"
+        return res
+    ex.shutdown()
+    return res
+
+
+def backward(torch, sp, workloads, hs, x, sh, w, src, dst, N, E, args):
+    """Vector-Jacobian product on the same graph, both kernels per call, for
+    each handle of ``hs`` (one per layout).  The roofline counts the
+    operands and gradients once each (x, g and dx per node; w, sh, dw, dsh
+    and the three index arrays per edge).  The per-edge source messages that
+    the first kernel writes and the second reads back are this design's own
+    workspace round trip, not algorithmic bytes: they are reported beside
+    the roofline as overhead, with the counter traffic over the operands."""
+    g = torch.from_numpy(workloads.output_gradient(N, hs[0].dim_out, "f32", seed=74)).to(x.device)
     perm = torch.argsort(src, stable=True).to(src.dtype)
     gx, gsh, gw = torch.empty_like(x), torch.empty_like(sh), torch.empty_like(w)
-    ws = torch.empty(sp.tp_conv_bwd_workspace(h, E), dtype=torch.uint8, device=x.device)
-    fb = lambda: sp.tp_conv_bwd(h, x, sh, w, g, src, dst, perm, n_nodes=N, workspace=ws,
-                                grad_x=gx, grad_sh=gsh, grad_w=gw)
-    wall, per = time_launches(torch, fb, args.steps, args.warmup)
-    kms = sum(per) / len(per)
-    operands = (2 * E * h.weight_numel * 4 + 2 * E * h.dim_in2 * 4 + 3 * E * 4 +
-                2 * N * h.dim_in1 * 4 + N * h.dim_out * 4)
-    messages = 2 * E * h.dim_in1 * 4
-    gbps = (operands + messages) / (kms * 1e-3) / 1e9
-    r = {"edges_per_s": E / (wall / args.steps), "ms_per_call": kms,
-         "algorithmic_bytes": {"operands": operands, "messages": messages},
-         "hbm": {"achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": gbps / HBM_PEAK_GBPS,
-                 "traffic": stored_traffic(h.layout, "bwd")},
-         "kernels": ["tp_bwd_edge_kernel", "tp_bwd_src_kernel"]}
+    ws = torch.empty(sp.tp_conv_bwd_workspace(hs[0], E), dtype=torch.uint8, device=x.device)
+    res = {}
+    for h in hs:
+        fb = lambda: sp.tp_conv_bwd(h, x, sh, w, g, src, dst, perm, n_nodes=N, workspace=ws,
+                                    grad_x=gx, grad_sh=gsh, grad_w=gw)
+        wall, per = time_launches(torch, fb, args.steps, args.warmup)
+        kms = sum(per) / len(per)
+        operands = (2 * E * h.weight_numel * 4 + 2 * E * h.dim_in2 * 4 + 3 * E * 4 +
+                    2 * N * h.dim_in1 * 4 + N * h.dim_out * 4)
+        messages = 2 * E * h.dim_in1 * 4
+        gbps = operands / (kms * 1e-3) / 1e9
+        traffic = stored_traffic(h.layout, "bwd")
+        res[h.layout] = {
+            "edges_per_s": E / (wall / args.steps), "ms_per_call": kms,
+            "hbm": {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                    "frac": gbps / HBM_PEAK_GBPS, "algorithmic_bytes": operands, "traffic": traffic,
+                    "traffic_over_algorithmic": None if traffic is None else traffic / operands},
+            "design_overhead": {"what": "per-edge source messages written by the edge kernel and read back by "
+                                        "the source kernel (workspace round trip, not counted above)",
+                                "bytes": messages,
+                                "GBps_with_overhead": (operands + messages) / (kms * 1e-3) / 1e9},
+            "kernels": ["tp_bwd_edge_kernel", "tp_bwd_src_kernel"]}
+        note(f"backward {h.layout} timed")
     del g, perm, gx, gsh, gw, ws
-    return r
+    return res
 
 
 def linear_layers(torch, sp, workloads, dev, args):
@@ -572,21 +716,26 @@ def fc_conv(torch, sp, workloads, dev, args):
                     "roofline": {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                                  "frac": gbps / HBM_PEAK_GBPS}}
         # backward: per edge the weight row read and its gradient written, the
-        # harmonics and their gradient, the source message written and read
-        # back; per node the output-gradient row; per source x and dx
+        # harmonics and their gradient and three indices; per node the
+        # output-gradient row; per source x and dx (the source message written
+        # and read back is reported apart, as the design's overhead)
         g = torch.from_numpy(workloads.output_gradient(N, h.dim_out, wl.dtype, seed=2009)).to(dev)
         perm = torch.argsort(src, stable=True).to(src.dtype)
         ws = torch.empty(max(1, sp.fctp_conv_bwd_workspace(h, E)), dtype=torch.uint8, device=dev)
         wallb, perb = time_launches(torch, lambda: sp.fctp_conv_bwd(h, x, sh, w, g, src, dst, perm, N, workspace=ws),
                                     args.steps, args.warmup)
         kb = sum(perb) / len(perb)
-        bbytes = (E * (2 * f.weight_numel + 2 * f.dim_in2 + 2 * f.dim_in1) * 4 + 3 * E * 4 +
+        bbytes = (E * (2 * f.weight_numel + 2 * f.dim_in2) * 4 + 3 * E * 4 +
                   N * f.dim_out * 4 + 2 * N * f.dim_in1 * 4)
+        msg = 2 * E * f.dim_in1 * 4
         res[lay]["backward"] = {"ms_per_call": kb, "kernels": ["fcconv_bwd_edge_kernel", "fcconv_bwd_src_kernel"],
                                 "roofline": {"bound": "hbm", "achieved": bbytes / (kb * 1e-3) / 1e9,
                                              "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                                              "frac": bbytes / (kb * 1e-3) / 1e9 / HBM_PEAK_GBPS,
-                                             "algorithmic_bytes": bbytes}}
+                                             "algorithmic_bytes": bbytes},
+                                "design_overhead": {"what": "per-edge source messages (workspace round trip, "
+                                                            "not counted above)", "bytes": msg,
+                                                    "GBps_with_overhead": (bbytes + msg) / (kb * 1e-3) / 1e9}}
         del out, g, perm, ws
     del x, sh, w, src, dst
     return res
