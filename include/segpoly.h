@@ -333,6 +333,29 @@ int symcon_bwd(symcon_handle h, const void* x, const void* species, const void* 
                const void* w, const void* grad_out, int64_t n_atoms, void* grad_x, void* grad_w, void* workspace,
                size_t workspace_bytes, void* stream);
 
+/*
+ * symcon_bwd_noalloc: symcon_bwd for callers that cannot allocate device
+ * memory on the compute path (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc).  Same arguments, kernels and
+ * results as symcon_bwd, without the workspace: it uses a fixed device array
+ * of SEGPOLY_NOALLOC_SCRATCH_BYTES inside this library instead (one copy per
+ * device, held from the library's first use on that device until the
+ * process ends).  The call itself allocates nothing, device or host.
+ *   Errors: E_UNSUPPORTED when symcon_bwd_workspace(h, n_atoms) exceeds
+ *   SEGPOLY_NOALLOC_SCRATCH_BYTES (checked before any launch; 128 MiB holds
+ *   50,000 atoms of 128 channels with 3,712 weights per element) or when the
+ *   handle has SEGPOLY_VALIDATE (its index check copies into host buffers);
+ *   otherwise as symcon_bwd.
+ * Every call on one device shares that device's array and leaves its own
+ * contents there (nothing in it needs to start at zero): calls that overlap
+ * on one device (different streams, or threads without ordering) race and
+ * must not be issued; calls ordered on one stream are safe.
+ */
+#define SEGPOLY_NOALLOC_SCRATCH_BYTES (128ull * 1024ull * 1024ull)
+int symcon_bwd_noalloc(symcon_handle h, const void* x, const void* species, const void* species_perm, int idx_dtype,
+                       const void* w, const void* grad_out, int64_t n_atoms, void* grad_x, void* grad_w,
+                       void* stream);
+
 int symcon_destroy(symcon_handle h);
 
 /* ------------------------------------------------------------------ misc */

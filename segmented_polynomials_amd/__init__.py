@@ -32,7 +32,7 @@ _DTYPES = {"f32": F32, "f64": F64}
 # every symbol include/segpoly.h declares
 EXPORTS = ("tp_create", "tp_query", "tp_irreps_out", "tp_path_info", "tp_path_cg", "tp_kernel_name",
            "tp_conv_fwd", "tp_conv_fwd_vec", "tp_conv_bwd_workspace", "tp_conv_bwd", "tp_destroy", "symcon_create", "symcon_query", "symcon_coupling_info",
-           "symcon_coupling_dense", "symcon_fwd", "symcon_bwd_workspace", "symcon_bwd", "symcon_destroy", "linear_create", "linear_query", "linear_fwd",
+           "symcon_coupling_dense", "symcon_fwd", "symcon_bwd_workspace", "symcon_bwd", "symcon_bwd_noalloc", "symcon_destroy", "linear_create", "linear_query", "linear_fwd",
            "linear_bwd_workspace", "linear_bwd", "linear_destroy", "fctp_create", "fctp_query", "fctp_path_info",
            "fctp_fwd", "fctp_bwd_workspace", "fctp_bwd", "fctp_conv_fwd", "fctp_conv_bwd_workspace", "fctp_conv_bwd", "fctp_destroy", "edge_scalars_fwd", "edge_scalars_bwd", "sh_fwd", "sh_bwd", "segpoly_real_cg",
            "segpoly_last_error", "segpoly_version")
@@ -88,6 +88,7 @@ def _load():
         "symcon_fwd": [vp, vp, vp, c_int, vp, i64, vp, vp],
         "symcon_bwd_workspace": [vp, i64, ctypes.POINTER(ctypes.c_size_t)],
         "symcon_bwd": [vp, vp, vp, vp, c_int, vp, vp, i64, vp, vp, vp, ctypes.c_size_t, vp],
+        "symcon_bwd_noalloc": [vp, vp, vp, vp, c_int, vp, vp, i64, vp, vp, vp],
         "symcon_destroy": [vp],
         "linear_create": [ctypes.c_char_p, ctypes.c_char_p, c_int, c_int, c_uint, ctypes.POINTER(vp)],
         "linear_query": [vp, c_int, p64],
@@ -460,6 +461,33 @@ def symcon_bwd(h, x, species, w, grad_out, species_perm, workspace=None, grad_x=
     wbytes = workspace.numel() * workspace.element_size()
     _check(lib.symcon_bwd(h._h, _ptr(x), _ptr(species), _ptr(species_perm), _index_dtype(species), _ptr(w),
                           _ptr(grad_out), n, _ptr(gx), _ptr(gw), _ptr(workspace), wbytes, _stream_ptr(x.device)))
+    return gx, gw
+
+
+NOALLOC_SCRATCH_BYTES = 128 * 1024 * 1024   # SEGPOLY_NOALLOC_SCRATCH_BYTES
+
+
+def symcon_bwd_noalloc(h, x, species, w, grad_out, species_perm, grad_x=None, grad_w=None):
+    """``symcon_bwd`` through the allocation-free entry point (its workspace
+    is the library's fixed device scratch).  The gradients are allocated
+    here if not given (the C call itself allocates nothing)."""
+    import torch
+    t = _torch_dtype(h.dtype)
+    for name, a in (("x", x), ("w", w), ("grad_out", grad_out)):
+        if a.dtype != t or not a.is_cuda or not a.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous {t} device tensor")
+    n = x.shape[0]
+    if x.shape[1] != h.dim_in or grad_out.shape != (n, h.dim_out) or w.shape != (h.num_elements, h.weight_numel):
+        raise ValueError("operand shapes do not match the descriptor")
+    for name, a in (("species", species), ("species_perm", species_perm)):
+        if a.shape != (n,) or a.dtype != species.dtype or not a.is_cuda or not a.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous [n_atoms] device tensor of one integer dtype")
+    gx = torch.empty_like(x) if grad_x is None else grad_x
+    gw = torch.empty_like(w) if grad_w is None else grad_w
+    if gx.shape != x.shape or gw.shape != w.shape or gx.dtype != t or gw.dtype != t:
+        raise ValueError("gradient buffers have the wrong shape or dtype")
+    _check(lib.symcon_bwd_noalloc(h._h, _ptr(x), _ptr(species), _ptr(species_perm), _index_dtype(species), _ptr(w),
+                                  _ptr(grad_out), n, _ptr(gx), _ptr(gw), _stream_ptr(x.device)))
     return gx, gw
 
 

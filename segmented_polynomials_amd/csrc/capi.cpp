@@ -105,6 +105,11 @@ int tp_conv_fwd_impl(tp_handle h, const void* x, int64_t n_src, const void* sh, 
                      int64_t n_nodes, void* out, void* stream);
 }  // namespace
 
+namespace segpoly {
+// the creation flags of a handle (for the allocation-free backward in noalloc.hip)
+unsigned symcon_handle_flags(symcon_handle h) { return h ? h->flags : 0u; }
+}  // namespace segpoly
+
 extern "C" {
 
 const char* segpoly_last_error(void) { return g_last_error.c_str(); }
