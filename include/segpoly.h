@@ -180,10 +180,11 @@ int tp_conv_fwd(tp_handle h, const void* x, int64_t n_src, const void* sh, const
  * one source message per edge (n_edges * DIM_IN1 elements of the handle's
  * dtype, indexed mode only), rounded up to 256 bytes, plus, when the
  * multiplicity exceeds 64, ceil(mul / 64) * n_edges * DIM_IN2 elements of
- * per-tile harmonic-gradient partials; with SEGPOLY_SHARED_WEIGHTS then,
- * each part 256-byte aligned, n_edges * WEIGHT_NUMEL per-edge weight
- * gradients and ceil(n_edges / 1024) * WEIGHT_NUMEL partial sums of them.
- * 0 means no workspace is needed.
+ * per-tile harmonic-gradient partials; in indexed mode then, 256-byte
+ * aligned, n_edges int32 (the sources in src_perm order); with
+ * SEGPOLY_SHARED_WEIGHTS then, each part 256-byte aligned, n_edges *
+ * WEIGHT_NUMEL per-edge weight gradients and ceil(n_edges / 1024) *
+ * WEIGHT_NUMEL partial sums of them.  0 means no workspace is needed.
  */
 int tp_conv_bwd_workspace(tp_handle h, int64_t n_edges, int batch, size_t* bytes);
 
@@ -221,7 +222,7 @@ int tp_conv_bwd_workspace(tp_handle h, int64_t n_edges, int batch, size_t* bytes
  *   workspace  device, at least tp_conv_bwd_workspace() bytes, 256-byte
  *              aligned; may be NULL when that size is 0.  Its contents on
  *              entry do not matter.
- * Two to three launches on `stream`, no atomics: results are deterministic
+ * Two to four launches on `stream`, no atomics: results are deterministic
  * (bitwise, for fixed inputs and src_perm); two more with shared weights.
  * Fails closed with E_UNSUPPORTED for a descriptor without a specialised
  * kernel.  Sizes: n_nodes, n_src < 2^31.

@@ -348,17 +348,24 @@ extern "C" {
 // Messages [n_edges][DIM_IN1] (indexed mode), then 256-byte aligned the
 // harmonic-gradient partials [tiles][n_edges][DIM_IN2] when one wave of
 // single channels does not cover the multiplicity (tiles = ceil(mul / 64),
-// the most any launch uses); with shared weights then, 256-byte aligned,
-// the per-edge weight-gradient rows [n_edges][numel] and, again aligned,
-// their partial sums [ceil(n_edges / kTpDwChunk)][numel].
-// `dw_off` receives the offset of the per-edge rows.
-static size_t tp_bwd_ws(const segpoly_tp* h, int64_t n_edges, bool batch, int64_t* dw_off) {
+// the most any launch uses); in indexed mode then, 256-byte aligned, the
+// sources in src_perm order [n_edges] int32; with shared weights then,
+// 256-byte aligned, the per-edge weight-gradient rows [n_edges][numel] and,
+// again aligned, their partial sums [ceil(n_edges / kTpDwChunk)][numel].
+// `dw_off` and `keys_off` receive the offsets of the per-edge rows and keys.
+static size_t tp_bwd_ws(const segpoly_tp* h, int64_t n_edges, bool batch, int64_t* dw_off,
+                        int64_t* keys_off = nullptr) {
   const size_t esz = h->dtype == SEGPOLY_F32 ? 4 : 8;
   const size_t e = static_cast<size_t>(n_edges);
   const size_t msg = static_cast<size_t>(round_up_256(static_cast<int64_t>(batch ? 0 : e * h->d.dim1 * esz)));
   const int mul = h->d.uniform_mul ? h->d.mul : 0;
   const size_t tiles = static_cast<size_t>((mul + 63) / 64);
   size_t bytes = msg + (tiles > 1 ? tiles * e * static_cast<size_t>(h->d.dim2) * esz : 0);
+  if (!batch && n_edges > 0) {
+    bytes = static_cast<size_t>(round_up_256(static_cast<int64_t>(bytes)));
+    if (keys_off) *keys_off = static_cast<int64_t>(bytes);
+    bytes += e * sizeof(int32_t);
+  }
   if ((h->flags & SEGPOLY_SHARED_WEIGHTS) && n_edges > 0) {
     bytes = static_cast<size_t>(round_up_256(static_cast<int64_t>(bytes)));
     if (dw_off) *dw_off = static_cast<int64_t>(bytes);
@@ -395,7 +402,7 @@ int tp_conv_bwd(tp_handle h, const void* x, int64_t n_src, const void* sh, const
   if (n_nodes > kMaxGrid || n_src > kMaxGrid) return fail(SEGPOLY_E_UNSUPPORTED, "n_nodes and n_src must be below 2^31");
   if (n_src > 0 && !grad_x) return fail(SEGPOLY_E_INVALID, "null grad_x");
   if (shared && !grad_w && d.numel > 0) return fail(SEGPOLY_E_INVALID, "null grad_w");
-  int64_t dw_off = 0;
+  int64_t dw_off = 0, keys_off = 0;
   if (n_edges > 0) {
     if (!grad_w || (!grad_sh && d.dim2 > 0)) return fail(SEGPOLY_E_INVALID, "null grad_sh or grad_w");
     if (n_nodes > 0) {
@@ -404,7 +411,7 @@ int tp_conv_bwd(tp_handle h, const void* x, int64_t n_src, const void* sh, const
       if (!x && n_src > 0) return fail(SEGPOLY_E_INVALID, "null x");
       if (!grad_out) return fail(SEGPOLY_E_INVALID, "null grad_out");
     }
-    const size_t need = tp_bwd_ws(h, n_edges, batch, &dw_off);
+    const size_t need = tp_bwd_ws(h, n_edges, batch, &dw_off, &keys_off);
     if (need && (!workspace || workspace_bytes < need))
       return fail(SEGPOLY_E_INVALID, "workspace missing or smaller than tp_conv_bwd_workspace()");
   }
@@ -437,6 +444,7 @@ int tp_conv_bwd(tp_handle h, const void* x, int64_t n_src, const void* sh, const
   a.mean = (h->flags & SEGPOLY_REDUCE_MEAN) ? 1 : 0;
   a.shared_w = shared ? 1 : 0;
   a.dw_ws_off = dw_off;
+  a.keys_ws_off = keys_off;
   a.dtype = h->dtype;
   a.idx = idx_dtype;
   a.layout = h->layout;

@@ -295,6 +295,12 @@ void emit_tp(const std::string& name, unsigned dtypes, const TPDescriptor& d, st
       if (!seen) out_blocks.push_back({p.kcomp, 2 * p.lo + 1});
     }
   }
+  // input-1 blocks (2l + 1 components each, in row order): the backward
+  // stages mul_ir message rows block by block
+  os << "  static constexpr int NXB = " << in_blocks.size() << ";\n";
+  os << "  __host__ __device__ static constexpr int xblock_dim(int b) {\n    constexpr int d[NXB] = {";
+  for (size_t b = 0; b < in_blocks.size(); ++b) os << (b ? ", " : "") << in_blocks[b].second;
+  os << "};\n    return d[b];\n  }\n\n";
   emit_row_io(os, "load_xs", "NX", in_blocks, d.nx, true);
   emit_row_io(os, "store_xs", "NX", in_blocks, d.nx, false);
   emit_row_io(os, "load_gs", "NK", out_blocks, d.nk, true);

@@ -83,6 +83,54 @@ struct Pow2Ceil<1> {
   static constexpr int value = 1;
 };
 
+// Message rows go out through LDS.  In mul_ir a lane's channels lie 2l + 1
+// values apart within each block, so every direct store instruction writes
+// a part of many cache lines, and with the non-temporal hint lines left the
+// cache partly written (1.27x the message bytes on the 600k-edge graph).
+// The tile's row is assembled in LDS (`stage`, kWave * CPL * NX values,
+// 16-byte aligned) in the handle's layout with the tile width as the
+// multiplicity; each slice that is contiguous in both places (a block in
+// mul_ir, a component in ir_mul) is then written with 16-byte non-temporal
+// stores.  (ir_mul rows are written directly: a lane's channel pair is
+// contiguous there, and its stores assemble whole lines in L2.)
+using raw16_t = unsigned int __attribute__((ext_vector_type(4)));
+
+template <typename T>
+__device__ __forceinline__ void copy_slice_nt(T* __restrict__ gp, const T* __restrict__ sp, int len) {
+  constexpr int V = 16 / static_cast<int>(sizeof(T));
+  const int lane = threadIdx.x % kWave;
+  // sp is 16-byte aligned; gp may not be (then element by element)
+  const int nv = (reinterpret_cast<uintptr_t>(gp) % 16) == 0 ? len / V : 0;
+  for (int q = lane; q < nv; q += kWave)
+    __builtin_nontemporal_store(*reinterpret_cast<const raw16_t*>(sp + q * V), reinterpret_cast<raw16_t*>(gp + q * V));
+  for (int q = nv * V + lane; q < len; q += kWave) st1<T, true>(gp + q, sp[q]);
+}
+
+template <class S, typename T, int LAYOUT, int CPL>
+__device__ __forceinline__ void store_msg_staged(T* __restrict__ grow, T* __restrict__ stage, int mul, int tile0,
+                                                 const T (&v)[CPL][S::NX]) {
+  constexpr int TW = kWave * CPL;
+  const int lane = threadIdx.x % kWave;
+  S::template store_xs<T, LAYOUT, CPL, false>(stage, TW, lane * CPL, v);
+  __syncthreads();
+  const int act = mul - tile0 < TW ? mul - tile0 : TW;
+  if constexpr (LAYOUT == kMulIr) {
+    int comp = 0;
+#pragma unroll
+    for (int b = 0; b < S::NXB; ++b) {
+      const int d = S::xblock_dim(b);
+      copy_slice_nt(grow + static_cast<int64_t>(comp) * mul + static_cast<int64_t>(tile0) * d, stage + comp * TW,
+                    act * d);
+      comp += d;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < S::NX; ++i)
+      copy_slice_nt(grow + static_cast<int64_t>(i) * mul + tile0, stage + i * TW, act);
+  }
+  __syncthreads();
+}
+
 // PF: keep the next edge's operands in flight (two channels per lane; with
 // one the extra registers cost more occupancy than the overlap gains).
 // `dsh_out` is dsh [n_edges][D2] with one tile, else part [tiles][n_edges][D2].
@@ -103,11 +151,18 @@ tp_bwd_edge_kernel(const T* __restrict__ x, const T* __restrict__ sh, const T* _
   const int64_t numel = static_cast<int64_t>(mul) * S::NP;
   const int64_t dim1 = static_cast<int64_t>(mul) * S::NX;
   T* const hrow = dsh_out + static_cast<int64_t>(blockIdx.y) * n_edges * S::D2;
+  __shared__ __align__(16) T stage[LAYOUT == kMulIr ? kWave * CPL * S::NX : 1];
+  const int tile0 = blockIdx.y * (kWave * CPL);
 
   int64_t e0, e1;
   edge_range(dst, n_edges, batch, node, e0, e1);
 
   auto zero_edge = [&](int64_t e) {
+    T z[CPL][S::NX];
+#pragma unroll
+    for (int c = 0; c < CPL; ++c)
+#pragma unroll
+      for (int i = 0; i < S::NX; ++i) z[c][i] = T(0);
     if (active) {
 #pragma unroll
       for (int p = 0; p < S::NP; ++p) {
@@ -116,13 +171,10 @@ tp_bwd_edge_kernel(const T* __restrict__ x, const T* __restrict__ sh, const T* _
         else
           st1<T, true>(dw + e * numel + p * mul + ub, T(0));
       }
-      T z[CPL][S::NX];
-#pragma unroll
-      for (int c = 0; c < CPL; ++c)
-#pragma unroll
-        for (int i = 0; i < S::NX; ++i) z[c][i] = T(0);
-      S::template store_xs<T, LAYOUT, CPL, true>(msg + e * dim1, mul, ub, z);
+      if constexpr (LAYOUT != kMulIr) S::template store_xs<T, LAYOUT, CPL, true>(msg + e * dim1, mul, ub, z);
     }
+    // the staged store needs the whole wave
+    if constexpr (LAYOUT == kMulIr) store_msg_staged<S, T, LAYOUT, CPL>(msg + e * dim1, stage, mul, tile0, z);
     if (lane < S::D2) hrow[e * S::D2 + lane] = T(0);
   };
   if (!batch) {
@@ -220,8 +272,9 @@ tp_bwd_edge_kernel(const T* __restrict__ x, const T* __restrict__ sh, const T* _
         else
           st1<T, true>(dw + e * numel + p * mul + ub, dwv[0][p]);
       }
-      S::template store_xs<T, LAYOUT, CPL, true>(msg + e * dim1, mul, ub, mxv);
+      if constexpr (LAYOUT != kMulIr) S::template store_xs<T, LAYOUT, CPL, true>(msg + e * dim1, mul, ub, mxv);
     }
+    if constexpr (LAYOUT == kMulIr) store_msg_staged<S, T, LAYOUT, CPL>(msg + e * dim1, stage, mul, tile0, mxv);
     const T tot = wave_sum_many<T, DP>(hsh);
     constexpr int stride = kWave / DP;
     if (lane % stride == 0 && lane / stride < S::D2) hrow[e * S::D2 + lane / stride] = tot;
@@ -230,7 +283,8 @@ tp_bwd_edge_kernel(const T* __restrict__ x, const T* __restrict__ sh, const T* _
 
 // First i in [lo, hi) with src[perm[i]] >= key (src[perm[.]] ascending),
 // by the same wave-cooperative search as the forward.  perm entries outside
-// [0, n_edges) compare as +infinity.
+// [0, n_edges) compare as +infinity.  (The source sums of the other
+// backward kernels; this one searches the contiguous keys below.)
 template <typename Index>
 __device__ __forceinline__ int64_t lower_bound_perm(const Index* __restrict__ src, const Index* __restrict__ perm,
                                                     int64_t n_edges, int64_t lo, int64_t hi, int64_t key) {
@@ -251,9 +305,32 @@ __device__ __forceinline__ int64_t lower_bound_perm(const Index* __restrict__ sr
   return lo + __popcll(__ballot(below(lo + lane)));
 }
 
+// keys[i] = src[perm[i]] clamped to [-1, n_src] (an entry of perm outside
+// [0, n_edges) counts as n_src): the sources in sorted order as one
+// contiguous int32 array, so that the source kernel's range searches probe
+// 2.4 MB that stays in L2 on the 600k-edge graph instead of following
+// perm into src at every probe (0.44 GB of L2-miss probes before).
+template <typename Index>
+__global__ void __launch_bounds__(256)
+tp_bwd_keys_kernel(const Index* __restrict__ src, const Index* __restrict__ perm, int64_t n_edges, int64_t n_src,
+                   int32_t* __restrict__ keys) {
+  for (int64_t i = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; i < n_edges;
+       i += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    const int64_t e = static_cast<int64_t>(perm[i]);
+    int64_t k = n_src;
+    if (e >= 0 && e < n_edges) {
+      const int64_t s = static_cast<int64_t>(src[e]);
+      k = s < 0 ? -1 : (s > n_src ? n_src : s);
+    }
+    keys[i] = static_cast<int32_t>(k);
+  }
+}
+
+constexpr int kSrcBatch = 4;
+
 template <class S, typename T, typename Index, int LAYOUT, int CPL>
 __global__ void __launch_bounds__(kWave)
-tp_bwd_src_kernel(const Index* __restrict__ src, const Index* __restrict__ perm, const T* __restrict__ msg,
+tp_bwd_src_kernel(const int32_t* __restrict__ keys, const Index* __restrict__ perm, const T* __restrict__ msg,
                   int64_t n_edges, int mul, T* __restrict__ dx) {
   const int64_t s = blockIdx.x;
   const int lane = threadIdx.x % kWave;
@@ -261,22 +338,37 @@ tp_bwd_src_kernel(const Index* __restrict__ src, const Index* __restrict__ perm,
   const bool active = ub < mul;
   const int ubl = active ? ub : 0;
   const int64_t dim1 = static_cast<int64_t>(mul) * S::NX;
-  const int64_t i0 = lower_bound_perm(src, perm, n_edges, 0, n_edges, s);
-  const int64_t i1 = lower_bound_perm(src, perm, n_edges, i0, n_edges, s + 1);
+  // keys ascend (src_perm sorts the sources): the same wave-cooperative
+  // search as the forward's destination ranges
+  const int64_t i0 = lower_bound_wave(keys, 0, n_edges, s);
+  const int64_t i1 = lower_bound_wave(keys, i0, n_edges, s + 1);
   T acc[CPL][S::NX];
 #pragma unroll
   for (int c = 0; c < CPL; ++c)
 #pragma unroll
     for (int i = 0; i < S::NX; ++i) acc[c][i] = T(0);
-  for (int64_t i = i0; i < i1; ++i) {
-    const int64_t e = static_cast<int64_t>(perm[i]);
-    if (e < 0 || e >= n_edges) continue;  // only an invalid perm gets here
-    T m[CPL][S::NX];
-    S::template load_xs<T, LAYOUT, CPL>(msg + e * dim1, mul, ubl, m);
+  // kSrcBatch edge ids, then their message rows, are loaded before any is
+  // summed (several rows in flight per wave); the sum stays in perm order
+  constexpr int B = kSrcBatch;
+  for (int64_t i = i0; i < i1; i += B) {
+    int64_t eb[B];
 #pragma unroll
-    for (int c = 0; c < CPL; ++c)
+    for (int b = 0; b < B; ++b) {
+      const int64_t e = i + b < i1 ? static_cast<int64_t>(perm[i + b]) : -1;
+      eb[b] = (e >= 0 && e < n_edges) ? e : -1;  // out of range only for an invalid perm
+    }
+    T m[B][CPL][S::NX];
 #pragma unroll
-      for (int k = 0; k < S::NX; ++k) acc[c][k] += m[c][k];
+    for (int b = 0; b < B; ++b)
+      S::template load_xs<T, LAYOUT, CPL>(msg + (eb[b] >= 0 ? eb[b] : 0) * dim1, mul, ubl, m[b]);
+#pragma unroll
+    for (int b = 0; b < B; ++b)
+      if (eb[b] >= 0) {
+#pragma unroll
+        for (int c = 0; c < CPL; ++c)
+#pragma unroll
+          for (int k = 0; k < S::NX; ++k) acc[c][k] += m[b][c][k];
+      }
   }
   if (active) S::template store_xs<T, LAYOUT, CPL>(dx + s * dim1, mul, ub, acc);
 }
@@ -324,7 +416,9 @@ void fill_zero(T* p, int64_t n, hipStream_t st) {
 
 // Workspace layout: messages [n_edges][dim1] (not in batch mode), then,
 // 256-byte aligned, the harmonic-gradient partials [tiles][n_edges][D2]
-// (several tiles only).  Sizes in tp_bwd_workspace_bytes.
+// (several tiles only), then (not in batch mode) the sorted source keys
+// [n_edges] int32 at keys_ws_off, then the shared-weight rows at dw_ws_off.
+// Sizes and offsets come from the C ABI (tp_bwd_ws in capi.cpp).
 template <class S, typename T, typename Index, int LAYOUT, int CPL>
 int tp_bwd_launch(const TPBwdArgs& a) {
   const hipStream_t st = static_cast<hipStream_t>(a.stream);
@@ -387,10 +481,15 @@ int tp_bwd_launch(const TPBwdArgs& a) {
   if (a.batch) {  // rows beyond the batch receive nothing
     fill_zero(dx + a.n_edges * dim1, (a.n_src - a.n_edges) * dim1, st);
   } else if (a.n_src > 0) {
+    int32_t* const keys = reinterpret_cast<int32_t*>(ws + a.keys_ws_off);
+    const int64_t blocks = (a.n_edges + 255) / 256;
+    hipLaunchKernelGGL((tp_bwd_keys_kernel<Index>), dim3(static_cast<unsigned>(blocks < 4096 ? blocks : 4096)),
+                       dim3(256), 0, st, static_cast<const Index*>(a.src), static_cast<const Index*>(a.perm),
+                       a.n_edges, a.n_src, keys);
     hipLaunchKernelGGL((tp_bwd_src_kernel<S, T, Index, LAYOUT, CPL>),
                        dim3(static_cast<unsigned>(a.n_src), static_cast<unsigned>(tiles)), dim3(kWave), 0, st,
-                       static_cast<const Index*>(a.src), static_cast<const Index*>(a.perm),
-                       static_cast<const T*>(a.workspace), a.n_edges, a.mul, dx);
+                       keys, static_cast<const Index*>(a.perm), static_cast<const T*>(a.workspace), a.n_edges,
+                       a.mul, dx);
   }
   return static_cast<int>(hipGetLastError());
 }
@@ -400,8 +499,11 @@ int tp_bwd_launch(const TPBwdArgs& a) {
 template <class S, typename T, typename Index, int LAYOUT>
 int tp_bwd_dispatch_cpl(const TPBwdArgs& a) {
   const size_t pa = 2 * sizeof(T);
+  // with shared weights the per-edge dw rows (paired stores) sit in the
+  // workspace, in batch mode too; a.dw is then written by the fold only
+  const void* dwe = a.shared_w ? static_cast<const unsigned char*>(a.workspace) + a.dw_ws_off : a.dw;
   if (a.mul > kWave && a.mul % 2 == 0 && aligned(a.x, pa) && aligned(a.w, pa) && aligned(a.g, pa) &&
-      aligned(a.dw, pa) && aligned(a.dx, pa) && (a.batch || aligned(a.workspace, pa)))
+      aligned(dwe, pa) && aligned(a.dx, pa) && ((a.batch && !a.shared_w) || aligned(a.workspace, pa)))
     return tp_bwd_launch<S, T, Index, LAYOUT, 2>(a);
   return tp_bwd_launch<S, T, Index, LAYOUT, 1>(a);
 }

@@ -49,6 +49,7 @@ struct TPBwdArgs {
   int mean;           // 1: the forward divided each row by its number of edges
   int shared_w;       // 1: w is one row shared by every edge (dw sums over the edges)
   int64_t dw_ws_off;  // shared weights: byte offset of the per-edge dw rows in the workspace
+  int64_t keys_ws_off;  // indexed mode: byte offset of the sorted source keys [n_edges] int32
   int dtype, idx, layout;
   void* stream;
 };

@@ -96,6 +96,14 @@ def test_fuzz_tp_descriptor(b1, b2, bo):
     in1 = "+".join(f"{m}x{l}{p}" for m, l, p in b1)
     in2 = "+".join(f"{l}{p}" for l, p in b2)
     filt = "+".join(f"{l}{p}" for l, p in bo)
+    o = otp.ChannelwiseTP(in1, in2, filt)
+    if sum(2 * lo + 1 for _, _, lo, _ in o.paths) * 64 * 4 > 64 * 1024:
+        # more output components per channel than the table-driven kernel
+        # holds in LDS (and no generated kernel): fails closed
+        with pytest.raises(sp.SegpolyError) as err:
+            sp.tp_create(in1, in2, filt)
+        assert err.value.code == sp.E_UNSUPPORTED
+        return
     _compare_tp(in1, in2, filt)
 
 
@@ -210,8 +218,10 @@ def test_backward_argument_errors_fail_before_any_gpu_call():
     h = sp.tp_create("32x0e+32x1o", "0e+1o", "0e+1o")
     assert h.specialized
     n = ctypes.c_size_t()
+    r256 = lambda b: (b + 255) // 256 * 256
+    # indexed mode: messages, then the int32 sources in src_perm order
     assert sp.lib.tp_conv_bwd_workspace(h._h, 10, 0, ctypes.byref(n)) == sp.OK
-    assert n.value == (10 * h.dim_in1 * 4 + 255) // 256 * 256
+    assert n.value == r256(10 * h.dim_in1 * 4) + 10 * 4
     assert sp.lib.tp_conv_bwd_workspace(h._h, 10, 1, ctypes.byref(n)) == sp.OK and n.value == 0
     assert sp.lib.tp_conv_bwd_workspace(h._h, -1, 0, ctypes.byref(n)) == sp.E_INVALID
     # multiplicity 200: four tiles of harmonic-gradient partials
@@ -219,7 +229,7 @@ def test_backward_argument_errors_fail_before_any_gpu_call():
     assert sp.lib.tp_conv_bwd_workspace(h2._h, 7, 1, ctypes.byref(n)) == sp.OK
     assert n.value == 4 * 7 * h2.dim_in2 * 4
     assert sp.lib.tp_conv_bwd_workspace(h2._h, 7, 0, ctypes.byref(n)) == sp.OK
-    assert n.value == (7 * h2.dim_in1 * 4 + 255) // 256 * 256 + 4 * 7 * h2.dim_in2 * 4
+    assert n.value == r256(r256(7 * h2.dim_in1 * 4) + 4 * 7 * h2.dim_in2 * 4) + 7 * 4
     f = sp.lib.tp_conv_bwd
     p = ctypes.c_void_p(16)   # never dereferenced: every call below fails validation
     big = 1 << 40
@@ -237,10 +247,12 @@ def test_backward_argument_errors_fail_before_any_gpu_call():
     # shared weights: the workspace adds the per-edge weight gradients and
     # one partial sum per 1024 edges; generic descriptors fail closed
     hs = sp.tp_create("32x0e+32x1o", "0e+1o", "0e+1o", shared_weights=True)
-    assert sp.tp_conv_bwd_workspace(hs, 1000) == 1000 * hs.dim_in1 * 4 + 1000 * hs.weight_numel * 4 \
-        + hs.weight_numel * 4
-    assert sp.tp_conv_bwd_workspace(hs, 2049) == (2049 * hs.dim_in1 * 4 + 255) // 256 * 256 \
-        + (2049 * hs.weight_numel * 4 + 255) // 256 * 256 + 3 * hs.weight_numel * 4
+    assert sp.tp_conv_bwd_workspace(hs, 1000) == r256(1000 * hs.dim_in1 * 4 + 1000 * 4) \
+        + 1000 * hs.weight_numel * 4 + hs.weight_numel * 4
+    assert sp.tp_conv_bwd_workspace(hs, 2049) == r256(r256(2049 * hs.dim_in1 * 4) + 2049 * 4) \
+        + r256(2049 * hs.weight_numel * 4) + 3 * hs.weight_numel * 4
+    # batch mode with shared weights: no messages and no keys
+    assert sp.tp_conv_bwd_workspace(hs, 1000, batch=True) == 1000 * hs.weight_numel * 4 + hs.weight_numel * 4
     assert f(hs._h, p, 1, p, p, p, p, p, 0, 1, 1, p, p, p, p, p, 8, None) == sp.E_INVALID       # workspace small
     assert f(hs._h, p, 1, p, p, p, p, p, 0, 1, 1, p, p, p, None, p, big, None) == sp.E_INVALID  # grad_w
     hg = sp.tp_create("32x0e+32x1o", "0e+1o", "0e+1o", force_generic=True)
