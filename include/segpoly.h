@@ -220,8 +220,8 @@ int tp_conv_bwd_workspace(tp_handle h, int64_t n_edges, int batch, size_t* bytes
  *              per-edge gradients (written to the workspace, summed in
  *              fixed chunks of 1024 edges, then the chunks in order).
  *   workspace  device, at least tp_conv_bwd_workspace() bytes, 256-byte
- *              aligned; may be NULL when that size is 0.  Its contents on
- *              entry do not matter.
+ *              aligned (E_INVALID otherwise); may be NULL when that size
+ *              is 0.  Its contents on entry do not matter.
  * Two to four launches on `stream`, no atomics: results are deterministic
  * (bitwise, for fixed inputs and src_perm); two more with shared weights.
  * Fails closed with E_UNSUPPORTED for a descriptor without a specialised
@@ -326,7 +326,8 @@ int symcon_bwd_workspace(symcon_handle h, int64_t n_atoms, size_t* bytes);
  *   grad_x      [n_atoms, DIM_IN] device, fully overwritten.
  *   grad_w      [num_elements, WEIGHT_NUMEL] device, fully overwritten.
  *   workspace   device, at least symcon_bwd_workspace() bytes, 256-byte
- *               aligned; its contents on entry do not matter.
+ *               aligned (E_INVALID otherwise); its contents on entry do not
+ *               matter.
  * Three launches on `stream`, no atomics.  Fails closed with E_UNSUPPORTED
  * for a descriptor without a specialised kernel.  Sizes: n_atoms < 2^31.
  */

@@ -414,6 +414,8 @@ int tp_conv_bwd(tp_handle h, const void* x, int64_t n_src, const void* sh, const
     const size_t need = tp_bwd_ws(h, n_edges, batch, &dw_off, &keys_off);
     if (need && (!workspace || workspace_bytes < need))
       return fail(SEGPOLY_E_INVALID, "workspace missing or smaller than tp_conv_bwd_workspace()");
+    if (need && reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
+      return fail(SEGPOLY_E_INVALID, "workspace must be 256-byte aligned");
   }
   if ((h->flags & SEGPOLY_VALIDATE) && !batch) {
     int st = idx_dtype == SEGPOLY_I32 ? check_indices<int32_t>(src, dst, n_edges, n_src, n_nodes, stream)
@@ -641,6 +643,8 @@ int symcon_bwd(symcon_handle h, const void* x, const void* species, const void* 
   symcon_bwd_workspace(h, n_atoms, &need);
   if (!workspace || workspace_bytes < need)
     return fail(SEGPOLY_E_INVALID, "workspace missing or smaller than symcon_bwd_workspace()");
+  if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
+    return fail(SEGPOLY_E_INVALID, "workspace must be 256-byte aligned");
   if ((h->flags & SEGPOLY_VALIDATE) && n_atoms > 0) {
     int st = idx_dtype == SEGPOLY_I32 ? check_species<int32_t>(species, n_atoms, h->num_elements, stream)
                                       : check_species<int64_t>(species, n_atoms, h->num_elements, stream);

@@ -254,6 +254,13 @@ def test_backward_argument_errors_fail_before_any_gpu_call():
     # batch mode with shared weights: no messages and no keys
     assert sp.tp_conv_bwd_workspace(hs, 1000, batch=True) == 1000 * hs.weight_numel * 4 + hs.weight_numel * 4
     assert f(hs._h, p, 1, p, p, p, p, p, 0, 1, 1, p, p, p, p, p, 8, None) == sp.E_INVALID       # workspace small
+    # a workspace off the 256-byte alignment fails closed (its shared-weight
+    # rows take paired stores), in indexed and in batch mode
+    odd = ctypes.c_void_p(256 + 4)
+    assert f(hs._h, p, 1, p, p, p, p, p, 0, 1, 1, p, p, p, p, odd, big, None) == sp.E_INVALID
+    assert b"aligned" in sp.lib.segpoly_last_error()
+    assert f(hs._h, p, 2, p, p, None, None, None, 0, 2, 2, p, p, p, p, odd, big, None) == sp.E_INVALID
+    assert b"aligned" in sp.lib.segpoly_last_error()
     assert f(hs._h, p, 1, p, p, p, p, p, 0, 1, 1, p, p, p, None, p, big, None) == sp.E_INVALID  # grad_w
     hg = sp.tp_create("32x0e+32x1o", "0e+1o", "0e+1o", force_generic=True)
     assert f(hg._h, p, 1, p, p, p, p, p, 0, 1, 1, p, p, p, p, p, big, None) == sp.E_UNSUPPORTED
@@ -280,6 +287,9 @@ def test_symcon_backward_argument_errors_fail_before_any_gpu_call():
     assert f(s._h, p, p, None, 0, p, p, 3, p, p, p, big, None) == sp.E_INVALID    # no perm
     assert f(s._h, p, p, p, 0, p, p, 3, p, None, p, big, None) == sp.E_INVALID    # no grad_w
     assert f(s._h, p, p, p, 0, p, p, 3, p, p, p, 16, None) == sp.E_INVALID        # workspace small
+    odd = ctypes.c_void_p(512 + 8)
+    assert f(s._h, p, p, p, 0, p, p, 3, p, p, odd, big, None) == sp.E_INVALID      # workspace misaligned
+    assert b"aligned" in sp.lib.segpoly_last_error()
     assert f(s._h, p, p, p, 0, p, p, 1 << 31, p, p, p, big, None) == sp.E_UNSUPPORTED
     sg = sp.symcon_create("32x0e+32x1o", "32x0e", 3, 4, force_generic=True)
     assert f(sg._h, p, p, p, 0, p, p, 3, p, p, p, big, None) == sp.E_UNSUPPORTED
