@@ -13,6 +13,7 @@
 #include "capi_util.hpp"
 #include "cg.hpp"
 #include "generic_tables.hpp"
+#include "linear_tables.hpp"
 #include "launch.hpp"
 #include "segpoly.h"
 #include "symcon_descriptor.hpp"
@@ -303,7 +304,9 @@ int tp_conv_fwd_impl(tp_handle h, const void* x, int64_t n_src, const void* sh, 
   a.dst = dst;
   a.out = out;
   a.n_src = n_src;
-  a.n_edges = n_edges;
+  // without source rows no edge contributes (and x may be NULL): every
+  // output row is zero, as with no edges
+  a.n_edges = (!batch && n_src == 0) ? 0 : n_edges;
   a.n_nodes = n_nodes;
   a.w_stride = (h->flags & SEGPOLY_SHARED_WEIGHTS) ? 0 : d.numel;
   a.mul = d.uniform_mul ? d.mul : 0;
@@ -426,6 +429,15 @@ int tp_conv_bwd(tp_handle h, const void* x, int64_t n_src, const void* sh, const
     if (st != SEGPOLY_OK) return st;
   }
   if (n_src == 0 && n_edges == 0 && !(shared && d.numel > 0)) return ok();
+  if (!batch && n_src == 0 && n_edges > 0) {
+    // no edge has a source row (x may be NULL): nothing reached the output,
+    // so every weight and harmonics gradient is zero
+    int rc = launch_fill_zero(grad_w, shared ? d.numel : n_edges * d.numel, h->dtype, stream);
+    if (rc == 0 && d.dim2 > 0) rc = launch_fill_zero(grad_sh, n_edges * d.dim2, h->dtype, stream);
+    if (rc != 0)
+      return fail(SEGPOLY_E_HIP, std::string("kernel launch failed: ") + hipGetErrorString(static_cast<hipError_t>(rc)));
+    return ok();
+  }
   TPBwdArgs a{};
   a.x = x;
   a.sh = sh;

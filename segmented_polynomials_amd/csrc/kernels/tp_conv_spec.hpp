@@ -66,6 +66,20 @@ __device__ __forceinline__ int64_t lower_bound_wave(const Index* __restrict__ ds
   return lo + __popcll(__ballot(below));
 }
 
+// lower_bound_wave from a position known to be at or below the answer,
+// trying the 64 positions after it first: a node's edges usually end within
+// 64 of where they start, and then one round of probes finds the end.
+template <typename Index>
+__device__ __forceinline__ int64_t lower_bound_wave_near(const Index* __restrict__ dst, int64_t lo, int64_t hi,
+                                                         int64_t key) {
+  const int lane = threadIdx.x % kWave;
+  const int64_t idx = lo + lane;
+  const bool below = idx < hi && static_cast<int64_t>(dst[idx]) < key;
+  const int c = __popcll(__ballot(below));
+  if (c < kWave || lo + kWave >= hi) return lo + c;  // the first position not below key is lo + c
+  return lower_bound_wave(dst, lo + kWave, hi, key);
+}
+
 // Edge range of `node` (batch mode: edge e is node e).
 template <typename Index>
 __device__ __forceinline__ void edge_range(const Index* __restrict__ dst, int64_t n_edges, int batch, int64_t node,
@@ -75,7 +89,7 @@ __device__ __forceinline__ void edge_range(const Index* __restrict__ dst, int64_
     e1 = node + 1;
   } else {
     e0 = lower_bound_wave(dst, 0, n_edges, node);
-    e1 = lower_bound_wave(dst, e0, n_edges, node + 1);
+    e1 = lower_bound_wave_near(dst, e0, n_edges, node + 1);
   }
 }
 
@@ -182,6 +196,120 @@ tp_conv_kernel(const T* __restrict__ x, const T* __restrict__ sh, const T* __res
     S::template store_s<T, LAYOUT, CPL, NTS>(out + node * (static_cast<int64_t>(mul) * S::NK), mul, ub, acc);
 }
 
+// Small multiplicities (mul <= GW <= 32) with a graph: one workgroup of
+// kSplitThreads lanes per destination node, split into EG = kSplitThreads /
+// GW groups of GW lanes (lane = channel).  Group g takes the node's edges
+// e0 + g, e0 + g + EG, ..., two at a time with the operands of both loaded
+// before either is computed, so a node's chain of dependent loads is 2 EG
+// times shorter than with one wave walking all of it (the molecular batch
+// has about 15 edges per node, and 64 lanes per wave would leave half
+// idle).  The groups' sums are added in group order through LDS and written
+// once: deterministic, no atomics.
+//
+// Measured on the molecular batch and dropped: a range search seeded with
+// node * n_edges / n_nodes (its first probes are node-specific cache lines,
+// where the whole-range search shares its first rounds across nodes), and
+// finding the range end edge by edge from dst instead of searching it.
+constexpr int kSplitThreads = 256;
+
+template <class S, typename T, typename Index, int LAYOUT, int GW, bool SHV = false>
+__global__ void __launch_bounds__(kSplitThreads)
+tp_conv_split_kernel(const T* __restrict__ x, const T* __restrict__ sh, const T* __restrict__ w,
+                     const Index* __restrict__ src, const Index* __restrict__ dst, int64_t n_src, int64_t n_edges,
+                     int64_t w_stride, int mul, int mean, T* __restrict__ out, const T* __restrict__ vec = nullptr,
+                     int sh_normalize = 0, ShConsts shk = {}) {
+  constexpr int EG = kSplitThreads / GW;
+  __shared__ T red[EG][S::NK][GW];
+  const int64_t node = blockIdx.x;
+  const int g = threadIdx.x / GW;
+  const int ul = threadIdx.x % GW;
+  const bool active = ul < mul;
+  const int ub = active ? ul : 0;
+  int64_t e0, e1;
+  edge_range(dst, n_edges, 0, node, e0, e1);  // every wave finds the same range
+  const int64_t dim1 = static_cast<int64_t>(mul) * S::NX;
+
+  T acc[1][S::NK];
+#pragma unroll
+  for (int k = 0; k < S::NK; ++k) acc[0][k] = T(0);
+  auto load_edge = [&](int64_t e, T (&wv)[1][S::NP], T (&shv)[S::D2]) {
+    const T* wrow = w + e * w_stride + ub;
+#pragma unroll
+    for (int p = 0; p < S::NP; ++p) wv[0][p] = __builtin_nontemporal_load(wrow + p * mul);
+    if constexpr (SHV) {
+      const T* vr = vec + e * 3;
+      sh_eval<T, sh_lmax_of(S::D2)>(vr[0], vr[1], vr[2], sh_normalize != 0, shk, shv);
+    } else {
+      const T* shrow = sh + e * S::D2;
+#pragma unroll
+      for (int j = 0; j < S::D2; ++j) shv[j] = shrow[j];
+    }
+  };
+  auto mask = [](bool keep, T (&xv)[1][S::NX], T (&wv)[1][S::NP], T (&shv)[S::D2]) {
+#pragma unroll
+    for (int i = 0; i < S::NX; ++i) xv[0][i] = keep ? xv[0][i] : T(0);
+#pragma unroll
+    for (int p = 0; p < S::NP; ++p) wv[0][p] = keep ? wv[0][p] : T(0);
+#pragma unroll
+    for (int j = 0; j < S::D2; ++j) shv[j] = keep ? shv[j] : T(0);
+  };
+  for (int64_t e = e0 + g; e < e1; e += 2 * EG) {
+    const bool has_f = e + EG < e1;
+    const int64_t f = has_f ? e + EG : e;  // clamped: every load below is unconditional
+    const int64_t se = static_cast<int64_t>(src[e]), sfl = static_cast<int64_t>(src[f]);
+    T we[1][S::NP], she[S::D2], wf[1][S::NP], shf[S::D2], xe[1][S::NX], xf[1][S::NX];
+    load_edge(e, we, she);
+    load_edge(f, wf, shf);
+    S::template load_xs<T, LAYOUT, 1>(x + ((se >= 0 && se < n_src) ? se : 0) * dim1, mul, ub, xe);
+    S::template load_xs<T, LAYOUT, 1>(x + ((sfl >= 0 && sfl < n_src) ? sfl : 0) * dim1, mul, ub, xf);
+    // a missing second edge, or an out-of-range source, adds exact zeros: its
+    // operands are zeroed by selects rather than skipped by a branch (behind
+    // a branch the compiler issues the loads one after another)
+    mask(se >= 0 && se < n_src, xe, we, she);
+    mask(has_f && sfl >= 0 && sfl < n_src, xf, wf, shf);
+    S::template edge<T, 1>(xe, she, we, acc);
+    S::template edge<T, 1>(xf, shf, wf, acc);
+  }
+#pragma unroll
+  for (int k = 0; k < S::NK; ++k) red[g][k][ul] = acc[0][k];
+  __syncthreads();
+  if (threadIdx.x < GW && active) {
+    const T scale = (mean && e1 > e0) ? T(1) / static_cast<T>(e1 - e0) : T(1);
+    T v[1][S::NK];
+#pragma unroll
+    for (int k = 0; k < S::NK; ++k) {
+      T t = red[0][k][ul];
+#pragma unroll
+      for (int q = 1; q < EG; ++q) t += red[q][k][ul];
+      v[0][k] = mean ? t * scale : t;
+    }
+    S::template store_s<T, LAYOUT, 1, false>(out + node * (static_cast<int64_t>(mul) * S::NK), mul, ul, v);
+  }
+}
+
+template <class S, typename T, typename Index, int LAYOUT, int GW>
+int tp_conv_split_launch(const TPArgs& a) {
+  const dim3 grid(static_cast<unsigned>(a.n_nodes));
+  if (a.vec) {
+    constexpr bool is_sh = (sh_lmax_of(S::D2) + 1) * (sh_lmax_of(S::D2) + 1) == S::D2 && sh_lmax_of(S::D2) <= kShMaxL;
+    if constexpr (is_sh) {
+      hipLaunchKernelGGL((tp_conv_split_kernel<S, T, Index, LAYOUT, GW, true>), grid, dim3(kSplitThreads), 0,
+                         static_cast<hipStream_t>(a.stream), static_cast<const T*>(a.x), nullptr,
+                         static_cast<const T*>(a.w), static_cast<const Index*>(a.src),
+                         static_cast<const Index*>(a.dst), a.n_src, a.n_edges, a.w_stride, a.mul, a.mean,
+                         static_cast<T*>(a.out), static_cast<const T*>(a.vec), a.sh_normalize, *a.sh_consts);
+      return static_cast<int>(hipGetLastError());
+    } else {
+      return -2;  // operand 2 is not a harmonics set
+    }
+  }
+  hipLaunchKernelGGL((tp_conv_split_kernel<S, T, Index, LAYOUT, GW>), grid, dim3(kSplitThreads), 0,
+                     static_cast<hipStream_t>(a.stream), static_cast<const T*>(a.x), static_cast<const T*>(a.sh),
+                     static_cast<const T*>(a.w), static_cast<const Index*>(a.src), static_cast<const Index*>(a.dst),
+                     a.n_src, a.n_edges, a.w_stride, a.mul, a.mean, static_cast<T*>(a.out));
+  return static_cast<int>(hipGetLastError());
+}
+
 template <class S, typename T, typename Index, int LAYOUT, int CPL, bool NTS = false>
 int tp_conv_launch(const TPArgs& a) {
   const int per_tile = kWave * CPL;
@@ -213,6 +341,14 @@ inline bool aligned(const void* p, size_t n) { return (reinterpret_cast<uintptr_
 // single channels and the pair accesses are aligned; one otherwise.
 template <class S, typename T, typename Index, int LAYOUT>
 int tp_conv_dispatch_cpl(const TPArgs& a) {
+  // graphs with at most 32 channels: the destination-split kernel (its LDS
+  // reduction buffer is kSplitThreads * NK values)
+  if constexpr (kSplitThreads * S::NK * sizeof(T) <= 64 * 1024) {
+    if (!a.batch && a.mul <= 32) {
+      if (a.mul <= 16) return tp_conv_split_launch<S, T, Index, LAYOUT, 16>(a);
+      return tp_conv_split_launch<S, T, Index, LAYOUT, 32>(a);
+    }
+  }
   const size_t pa = 2 * sizeof(T);
   if (a.mul > kWave && a.mul % 2 == 0 && aligned(a.x, pa) && aligned(a.w, pa) && aligned(a.out, pa))
     return tp_conv_launch<S, T, Index, LAYOUT, 2>(a);

@@ -327,3 +327,32 @@ def test_mean_reduction(force_generic):
     check_scaled(got, ref, scale, "f32", f"mean generic={force_generic}")
     iso = np.bincount(inp["dst"], minlength=120) == 0
     assert iso.any() and np.count_nonzero(got[iso]) == 0
+
+
+@pytest.mark.parametrize("mul", [32, 128])
+def test_no_source_rows(mul):
+    """n_src = 0 with edges: no edge has a source row, so the forward is zero
+    and the backward gives zero weight and harmonics gradients (x holds no
+    rows; the kernels must not read it).  Both kernels of the forward (the
+    destination-split one for mul <= 32 and the wave-per-node one)."""
+    sp = _sp()
+    import torch
+    in1, in2, filt = f"{mul}x0e+{mul}x1o", "0e+1o+2e", "0e+1o+2e"
+    o = otp.ChannelwiseTP(in1, in2, filt)
+    h = sp.tp_create(in1, in2, filt)
+    rng = np.random.default_rng(41)
+    n_e, n_dst = 50, 7
+    dst = np.sort(rng.integers(0, n_dst, n_e)).astype(np.int32)
+    src = rng.integers(0, 5, n_e).astype(np.int32)
+    x = torch.zeros((0, o.dim_in1), dtype=torch.float32, device="cuda")
+    sh = dev(rng.standard_normal((n_e, o.dim_in2), dtype=np.float32))
+    w = dev(rng.standard_normal((n_e, o.weight_numel), dtype=np.float32))
+    announce(f"tp no source rows mul={mul}")
+    out = sp.tp_conv_fwd(h, x, sh, w, dev(src), dev(dst), n_nodes=n_dst)
+    g = dev(rng.standard_normal((n_dst, o.dim_out), dtype=np.float32))
+    perm = dev(np.argsort(src, kind="stable").astype(np.int32))
+    gx, gsh, gw = sp.tp_conv_bwd(h, x, sh, w, g, dev(src), dev(dst), perm, n_nodes=n_dst)
+    torch.cuda.synchronize()
+    assert out.shape == (n_dst, o.dim_out) and torch.count_nonzero(out) == 0
+    assert gx.shape == (0, o.dim_in1)
+    assert torch.count_nonzero(gsh) == 0 and torch.count_nonzero(gw) == 0
