@@ -448,7 +448,10 @@ int linear_destroy(linear_handle h);
  * samples ([1, WEIGHT_NUMEL]).  flags: SEGPOLY_VALIDATE (index checks of
  * fctp_conv_fwd), SEGPOLY_REDUCE_MEAN (fctp_conv_fwd averages instead of
  * summing).  E_UNSUPPORTED for l > 6, more than 32 blocks on a side, more
- * than 64 paths, or blocks too wide for one workgroup's LDS.  Touches no GPU.
+ * than 64 paths, blocks too wide for one workgroup's LDS, or a path whose
+ * coupling has more than 16 non-zero entries along one index of any of its
+ * three axes (within l <= 6 only couplings with two of l1, l2, l3 at 5 or 6,
+ * e.g. 5 x 1 -> 5 with 18).  Touches no GPU.
  */
 int fctp_create(const char* irreps_in1, const char* irreps_in2, const char* irreps_out, int layout, int dtype,
                 unsigned flags, fctp_handle* out);

@@ -230,6 +230,71 @@ class SymmetricContraction:
             return res
         return back(dv_all, self.inp), dw
 
+    def eval_plain(self, x, species, w, layout="ir_mul"):
+        """The definition written out, for small cases: per atom a and
+        channel u, with v the components of x[a, :, u] (all input blocks in
+        order), out[a, L:M, u] = sum over the weight segments (nu, L, k) of
+        w[species_a, seg, u] * (U^k contracted with v in each of its nu input
+        slots)[M], each contraction one dense np.einsum.  Loops over atoms
+        and channels; no batching, gathering or scattering.  Same result as
+        :meth:`eval` up to rounding."""
+        x = np.asarray(x, dtype=np.float64)
+        w = np.asarray(w, dtype=np.float64)
+        comps = np.concatenate(split_blocks(x, self.inp, layout), axis=1)     # [A, n, mul]
+        outs = [np.zeros((x.shape[0], 2 * L + 1, self.mul)) for _, L, _ in self.out]
+        for a in range(x.shape[0]):
+            s = int(species[a])
+            if not 0 <= s < w.shape[0]:
+                continue
+            for u in range(self.mul):
+                v = comps[a, :, u]
+                for s_idx, (nu, ob, k) in enumerate(self.segments):
+                    U = self.basis[(nu, ob)][k]
+                    if nu == 1:
+                        t = np.einsum("iM,i->M", U, v)
+                    elif nu == 2:
+                        t = np.einsum("ijM,i,j->M", U, v, v)
+                    else:
+                        t = np.einsum("ijkM,i,j,k->M", U, v, v, v)
+                    outs[ob][a, :, u] += w[s, s_idx * self.mul + u] * t
+        return join_blocks(outs, layout)
+
+    def eval_vjp_plain(self, x, species, w, g, layout="ir_mul"):
+        """:meth:`eval_vjp` written out the same way: per atom and channel,
+        dw gets g . (U contracted with v) and dv gets, for each input slot,
+        w g . (U contracted with v in the other slots), one dense np.einsum
+        each (the product rule with no use of U being symmetric)."""
+        x = np.asarray(x, dtype=np.float64)
+        w = np.asarray(w, dtype=np.float64)
+        comps = np.concatenate(split_blocks(x, self.inp, layout), axis=1)
+        gs = split_blocks(np.asarray(g, dtype=np.float64), self.out, layout)   # each [A, 2L+1, mul]
+        dv = np.zeros_like(comps)
+        dw = np.zeros_like(w)
+        for a in range(x.shape[0]):
+            s = int(species[a])
+            if not 0 <= s < w.shape[0]:
+                continue
+            for u in range(self.mul):
+                v = comps[a, :, u]
+                for s_idx, (nu, ob, k) in enumerate(self.segments):
+                    U = self.basis[(nu, ob)][k]
+                    gm = gs[ob][a, :, u]
+                    col = s_idx * self.mul + u
+                    if nu == 1:
+                        dw[s, col] += np.einsum("iM,i,M->", U, v, gm)
+                        dv[a, :, u] += w[s, col] * np.einsum("iM,M->i", U, gm)
+                    elif nu == 2:
+                        dw[s, col] += np.einsum("ijM,i,j,M->", U, v, v, gm)
+                        dv[a, :, u] += w[s, col] * (np.einsum("ijM,j,M->i", U, v, gm)
+                                                    + np.einsum("ijM,i,M->j", U, v, gm))
+                    else:
+                        dw[s, col] += np.einsum("ijkM,i,j,k,M->", U, v, v, v, gm)
+                        dv[a, :, u] += w[s, col] * (np.einsum("ijkM,j,k,M->i", U, v, v, gm)
+                                                    + np.einsum("ijkM,i,k,M->j", U, v, v, gm)
+                                                    + np.einsum("ijkM,i,j,M->k", U, v, v, gm))
+        blocks = np.split(dv, np.cumsum([2 * l + 1 for _, l, _ in self.inp])[:-1], axis=1)
+        return join_blocks(blocks, layout), dw
+
     def eval(self, x, species, w, layout="ir_mul", absolute=False):
         """x [n_atoms, dim_in] in ``layout``; species [n_atoms] integers;
         w [num_elements, weight_numel].  Returns float64 [n_atoms, dim_out].

@@ -452,3 +452,28 @@ def test_bench_traffic_replay_rejects_other_shapes_before_any_gpu_call():
     assert fn(0, 0, p, p, p, p, p, 0, 10, 30, *shape, None) == -1                  # no nodes
     assert fn(0, 0, p, p, p, p, p, 10, 10, 0, *shape, None) == -1                  # no edges per node
     assert fn(7, 0, p, p, p, p, p, 10, 10, 30, *shape, None) == -1                 # mode
+
+
+def test_fctp_coupling_entry_limit_matches_oracle():
+    """The fully connected product compiles coupling classes of up to 16
+    non-zero entries per component (along each of the three axes: output,
+    and the two input gradients).  Every SO(3) coupling with l1, l2, l3 <= 6
+    builds exactly when the oracle's tensor stays within that, and fails
+    closed (E_UNSUPPORTED) otherwise, e.g. 5 x 1 -> 5 (18 entries)."""
+    for l1 in range(7):
+        for l2 in range(7):
+            for l3 in range(abs(l1 - l2), min(l1 + l2, 6) + 1):
+                nz = np.abs(ocg.real_cg(l1, l2, l3)) > 1e-13
+                most = max(nz.sum(axis=(1, 2)).max(), nz.sum(axis=(0, 2)).max(), nz.sum(axis=(0, 1)).max())
+                raw = ctypes.c_void_p()
+                rc = sp.lib.fctp_create(f"1x{l1}".encode(), f"1x{l2}".encode(), f"1x{l3}".encode(), 0, 0, 0,
+                                        ctypes.byref(raw))
+                if most > 16:
+                    assert rc == sp.E_UNSUPPORTED, (l1, l2, l3, most)
+                    assert b"couplings per component" in sp.lib.segpoly_last_error()
+                else:
+                    assert rc == sp.OK, (l1, l2, l3, sp.lib.segpoly_last_error())
+                    sp.lib.fctp_destroy(raw)
+    with pytest.raises(sp.SegpolyError) as err:
+        sp.fctp_create("1x5o", "1x1o", "1x5e")
+    assert err.value.code == sp.E_UNSUPPORTED
