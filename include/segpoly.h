@@ -152,7 +152,13 @@ int tp_kernel_name(tp_handle h, char* buf, size_t cap);
 /*
  * tp_conv_fwd: out[n] = sum over edges e with dst[e] == n of the product
  * of x[src[e]], sh[e] and w[e] through every path; rows with no edge are
- * written as zeros.  `out` is fully overwritten.
+ * written as zeros.  `out` is fully overwritten.  The product is the
+ * channelwise descriptor of e3nn-course Lesson 12a, section 21.4 (one fused
+ * kernel over every path, sections 21.1 and 21.6); the gather by source and
+ * the sum into destinations (repeated receivers add, receivers without edges
+ * stay zero, the destination count given explicitly) are those of the
+ * cuequivariance-torch skill document, "SegmentedPolynomial: gather and
+ * scatter".
  *   x       [n_src, DIM_IN1] device, layout of the handle.
  *   sh      [n_edges, DIM_IN2] device.
  *   w       [n_edges, WEIGHT_NUMEL] device, or [1, WEIGHT_NUMEL] with
@@ -254,7 +260,12 @@ int tp_destroy(tp_handle h);
 /* ------------------------------------------------------------------ symcon */
 
 /*
- * symcon_create: symmetric contraction of degrees 1..max_degree (1..3).
+ * symcon_create: symmetric contraction of degrees 1..max_degree (1..3):
+ * the MACE-style polynomial of e3nn-course Lesson 12a, section 21.4.1 (its
+ * degree-1..3 descriptors evaluated in one launch), with the element-indexed
+ * weights of the cuequivariance-torch skill document, "Other operations and
+ * layers" (SymmetricContraction: uniform multiplicities, one weight row per
+ * element).
  *   irreps_in, irreps_out  every block with the same multiplicity.
  *   num_elements           number of species (rows of the weight table).
  * Coupling basis per (degree nu, output block): candidates are the
@@ -284,7 +295,9 @@ int symcon_coupling_dense(symcon_handle h, int c, double* out);
 
 /*
  * symcon_fwd: out[a] = sum over degrees and couplings of
- * w[species[a], segment] * coupling(x[a], ..., x[a]) per channel.
+ * w[species[a], segment] * coupling(x[a], ..., x[a]) per channel (Lesson
+ * 12a, section 21.4.1; the call sc(x, element_indices) of the skill
+ * document, "Other operations and layers").
  *   x        [n_atoms, DIM_IN] device, layout of the handle.
  *   species  [n_atoms] device, int32 or int64 per idx_dtype; an element
  *            outside [0, num_elements) gives a zero row (E_RANGE with
