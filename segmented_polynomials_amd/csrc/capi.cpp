@@ -81,7 +81,8 @@ struct segpoly_tp {
   std::string kernel_name;
   std::vector<GPath> gpaths;
   std::vector<GNz> gnz;
-  std::vector<unsigned char> blob;  // gpaths then gnz, uploaded once per device
+  std::vector<GIn> gin;
+  std::vector<unsigned char> blob;  // gpaths, gnz, then gin, uploaded once per device
   int max_mul = 0;
   std::mutex mu;
   std::map<int, DeviceBuffer> dev;
@@ -101,6 +102,44 @@ struct segpoly_symcon {
 };
 
 namespace {
+// Device view of a handle's uploaded tables (gpaths, gnz, gin in one blob).
+GenericTPInfo generic_tp_info(const segpoly_tp* h, void* dp) {
+  const size_t bp = h->gpaths.size() * sizeof(GPath), bz = h->gnz.size() * sizeof(GNz);
+  unsigned char* base = static_cast<unsigned char*>(dp);
+  GenericTPInfo g{};
+  g.paths = reinterpret_cast<const GPath*>(base);
+  g.nz = reinterpret_cast<const GNz*>(base + bp);
+  g.in = reinterpret_cast<const GIn*>(base + bp + bz);
+  g.np = static_cast<int>(h->gpaths.size());
+  g.nk = h->d.nk;
+  g.max_mul = h->max_mul;
+  g.n_in = static_cast<int>(h->gin.size());
+  g.nx = h->d.nx;
+  g.dim1 = h->d.dim1;
+  g.dim2 = h->d.dim2;
+  g.dimo = h->d.dimo;
+  g.numel = h->d.numel;
+  return g;
+}
+
+// Device view of a symmetric contraction's uploaded tables (terms, input
+// blocks, output blocks in one blob).
+GenericSymconInfo generic_symcon_info(const segpoly_symcon* h, void* dp) {
+  const size_t bt = h->gterms.size() * sizeof(GTerm), bi = h->gin.size() * sizeof(GBlock);
+  unsigned char* base = static_cast<unsigned char*>(dp);
+  GenericSymconInfo g{};
+  g.terms = reinterpret_cast<const GTerm*>(base);
+  g.in_blocks = reinterpret_cast<const GBlock*>(base + bt);
+  g.out_blocks = reinterpret_cast<const GBlock*>(base + bt + bi);
+  g.n_terms = static_cast<int>(h->gterms.size());
+  g.n_in_blocks = static_cast<int>(h->gin.size());
+  g.n_out_blocks = static_cast<int>(h->gout.size());
+  g.nv = h->d.n;
+  g.no = h->d.nout;
+  g.numel = h->d.numel;
+  return g;
+}
+
 int tp_conv_fwd_impl(tp_handle h, const void* x, int64_t n_src, const void* sh, const void* vec, int normalize,
                      const void* w, const void* src, const void* dst, int idx_dtype, int64_t n_edges,
                      int64_t n_nodes, void* out, void* stream);
@@ -176,6 +215,7 @@ int tp_create(const char* in1, const char* in2, const char* outs, int layout, in
     for (const auto& z : p.nz) h->gnz.push_back({z.i, z.j, z.k, 0, z.c});
     g.nz_end = static_cast<int>(h->gnz.size());
     g.kcomp = p.kcomp;
+    g.xcomp = p.xcomp;
     g.off1 = p.off1;
     g.off2 = p.off2;
     g.offo = p.offo;
@@ -183,11 +223,23 @@ int tp_create(const char* in1, const char* in2, const char* outs, int layout, in
     h->gpaths.push_back(g);
     h->max_mul = std::max(h->max_mul, p.mul);
   }
+  {  // input-1 blocks (the table-driven backward writes dx block by block)
+    int64_t off = 0;
+    int comp = 0;
+    for (const auto& r : h->d.in1) {
+      h->gin.push_back({r.l, comp, r.mul, 0, off});
+      off += static_cast<int64_t>(r.mul) * (2 * r.l + 1);
+      comp += 2 * r.l + 1;
+      h->max_mul = std::max(h->max_mul, r.mul);
+    }
+  }
   {
-    const size_t bp = h->gpaths.size() * sizeof(GPath), bz = h->gnz.size() * sizeof(GNz);
-    h->blob.resize(bp + bz);
+    const size_t bp = h->gpaths.size() * sizeof(GPath), bz = h->gnz.size() * sizeof(GNz),
+                 bi = h->gin.size() * sizeof(GIn);
+    h->blob.resize(bp + bz + bi);
     if (bp) std::memcpy(h->blob.data(), h->gpaths.data(), bp);
     if (bz) std::memcpy(h->blob.data() + bp, h->gnz.data(), bz);
+    if (bi) std::memcpy(h->blob.data() + bp + bz, h->gin.data(), bi);
   }
   const size_t esz = dtype == SEGPOLY_F32 ? 4 : 8;
   if (!h->spec && static_cast<size_t>(h->d.nk) * 64 * esz > kGenericLdsLimit) {
@@ -324,20 +376,10 @@ int tp_conv_fwd_impl(tp_handle h, const void* x, int64_t n_src, const void* sh, 
     rc = h->spec->launch(a);
     if (rc == -2) return fail(SEGPOLY_E_UNSUPPORTED, "input 2 of this descriptor is not a harmonics set");
   } else {
-    const size_t bp = h->gpaths.size() * sizeof(GPath);
     int st = SEGPOLY_OK;
     void* dp = upload(h->dev, h->mu, h->blob.data(), h->blob.size(), &st);
     if (!dp) return st;
-    GenericTPInfo g{};
-    g.paths = static_cast<const GPath*>(dp);
-    g.nz = reinterpret_cast<const GNz*>(static_cast<unsigned char*>(dp) + bp);
-    g.np = static_cast<int>(h->gpaths.size());
-    g.nk = d.nk;
-    g.max_mul = h->max_mul;
-    g.dim1 = d.dim1;
-    g.dim2 = d.dim2;
-    g.dimo = d.dimo;
-    rc = launch_tp_generic(a, g);
+    rc = launch_tp_generic(a, generic_tp_info(h, dp));
   }
   if (rc != 0)
     return fail(SEGPOLY_E_HIP, std::string("kernel launch failed: ") + hipGetErrorString(static_cast<hipError_t>(rc)));
@@ -360,6 +402,13 @@ static size_t tp_bwd_ws(const segpoly_tp* h, int64_t n_edges, bool batch, int64_
                         int64_t* keys_off = nullptr) {
   const size_t esz = h->dtype == SEGPOLY_F32 ? 4 : 8;
   const size_t e = static_cast<size_t>(n_edges);
+  if (!h->spec) {  // table-driven backward: only the shared-weight rows and their chunk sums
+    if (dw_off) *dw_off = 0;
+    if (!(h->flags & SEGPOLY_SHARED_WEIGHTS) || n_edges == 0) return 0;
+    const size_t numel = static_cast<size_t>(h->d.numel);
+    const size_t chunks = (e + kTpDwChunk - 1) / kTpDwChunk;
+    return static_cast<size_t>(round_up_256(static_cast<int64_t>(e * numel * esz))) + chunks * numel * esz;
+  }
   const size_t msg = static_cast<size_t>(round_up_256(static_cast<int64_t>(batch ? 0 : e * h->d.dim1 * esz)));
   const int mul = h->d.uniform_mul ? h->d.mul : 0;
   const size_t tiles = static_cast<size_t>((mul + 63) / 64);
@@ -397,8 +446,10 @@ int tp_conv_bwd(tp_handle h, const void* x, int64_t n_src, const void* sh, const
     return fail(SEGPOLY_E_INVALID, "src, dst and src_perm must all be given or all be NULL");
   const auto& d = h->d;
   const bool shared = (h->flags & SEGPOLY_SHARED_WEIGHTS) != 0;
-  if (!h->spec || !h->spec->launch_bwd)
+  if (h->spec && !h->spec->launch_bwd)
     return fail(SEGPOLY_E_UNSUPPORTED, "backward needs a specialised kernel for this descriptor");
+  if (!h->spec && tp_generic_bwd_lds(d.nx, d.dim2, h->dtype) > kGenericLdsLimit)
+    return fail(SEGPOLY_E_UNSUPPORTED, "too many input-1 or input-2 components per channel for the generic backward");
   const bool batch = src == nullptr && n_edges > 0;
   if (batch && (n_edges != n_nodes || n_src < n_edges))
     return fail(SEGPOLY_E_INVALID, "batch mode needs n_edges == n_nodes <= n_src");
@@ -463,7 +514,15 @@ int tp_conv_bwd(tp_handle h, const void* x, int64_t n_src, const void* sh, const
   a.idx = idx_dtype;
   a.layout = h->layout;
   a.stream = stream;
-  const int rc = h->spec->launch_bwd(a);
+  int rc;
+  if (h->spec) {
+    rc = h->spec->launch_bwd(a);
+  } else {
+    int st = SEGPOLY_OK;
+    void* dp = upload(h->dev, h->mu, h->blob.data(), h->blob.size(), &st);
+    if (!dp) return st;
+    rc = launch_tp_generic_bwd(a, generic_tp_info(h, dp));
+  }
   if (rc != 0)
     return fail(SEGPOLY_E_HIP, std::string("kernel launch failed: ") + hipGetErrorString(static_cast<hipError_t>(rc)));
   return ok();
@@ -607,22 +666,10 @@ int symcon_fwd(symcon_handle h, const void* x, const void* species, int idx_dtyp
   if (h->spec) {
     rc = h->spec->launch(a);
   } else {
-    const size_t bt = h->gterms.size() * sizeof(GTerm), bi = h->gin.size() * sizeof(GBlock);
     int st = SEGPOLY_OK;
     void* dp = upload(h->dev, h->mu, h->blob.data(), h->blob.size(), &st);
     if (!dp) return st;
-    unsigned char* base = static_cast<unsigned char*>(dp);
-    GenericSymconInfo g{};
-    g.terms = reinterpret_cast<const GTerm*>(base);
-    g.in_blocks = reinterpret_cast<const GBlock*>(base + bt);
-    g.out_blocks = reinterpret_cast<const GBlock*>(base + bt + bi);
-    g.n_terms = static_cast<int>(h->gterms.size());
-    g.n_in_blocks = static_cast<int>(h->gin.size());
-    g.n_out_blocks = static_cast<int>(h->gout.size());
-    g.nv = h->d.n;
-    g.no = h->d.nout;
-    g.numel = h->d.numel;
-    rc = launch_symcon_generic(a, g);
+    rc = launch_symcon_generic(a, generic_symcon_info(h, dp));
   }
   if (rc != 0)
     return fail(SEGPOLY_E_HIP, std::string("kernel launch failed: ") + hipGetErrorString(static_cast<hipError_t>(rc)));
@@ -632,6 +679,10 @@ int symcon_fwd(symcon_handle h, const void* x, const void* species, int idx_dtyp
 int symcon_bwd_workspace(symcon_handle h, int64_t n_atoms, size_t* bytes) {
   if (!h || !bytes) return fail(SEGPOLY_E_INVALID, "null argument");
   if (n_atoms < 0) return fail(SEGPOLY_E_INVALID, "negative size");
+  if (!h->spec) {  // the table-driven backward needs no workspace
+    *bytes = 0;
+    return ok();
+  }
   const size_t esz = h->dtype == SEGPOLY_F32 ? 4 : 8;
   const size_t table = static_cast<size_t>(symcon_bwd_table_bytes(h->num_elements));
   const size_t chunks = static_cast<size_t>(symcon_bwd_max_chunks(n_atoms, h->num_elements));
@@ -645,17 +696,20 @@ int symcon_bwd(symcon_handle h, const void* x, const void* species, const void* 
   if (!h) return fail(SEGPOLY_E_INVALID, "null handle");
   if (n_atoms < 0) return fail(SEGPOLY_E_INVALID, "negative size");
   if (idx_dtype != SEGPOLY_I32 && idx_dtype != SEGPOLY_I64) return fail(SEGPOLY_E_INVALID, "bad index dtype");
-  if (!h->spec || !h->spec->launch_bwd)
+  if (h->spec && !h->spec->launch_bwd)
     return fail(SEGPOLY_E_UNSUPPORTED, "backward needs a specialised kernel for this descriptor");
+  const int nseg = static_cast<int>(h->d.couplings.size());
+  if (!h->spec && symcon_generic_bwd_lds(h->d.n, h->d.nout, nseg, h->dtype) > kGenericLdsLimit)
+    return fail(SEGPOLY_E_UNSUPPORTED, "too many components or couplings per channel for the generic backward");
   if (n_atoms > kMaxGrid) return fail(SEGPOLY_E_UNSUPPORTED, "n_atoms must be below 2^31");
   if (!grad_w) return fail(SEGPOLY_E_INVALID, "null grad_w");
   if (n_atoms > 0 && (!x || !species || !species_perm || !w || !grad_out || !grad_x))
     return fail(SEGPOLY_E_INVALID, "null pointer");
   size_t need = 0;
   symcon_bwd_workspace(h, n_atoms, &need);
-  if (!workspace || workspace_bytes < need)
+  if (need && (!workspace || workspace_bytes < need))
     return fail(SEGPOLY_E_INVALID, "workspace missing or smaller than symcon_bwd_workspace()");
-  if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
+  if (need && reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
     return fail(SEGPOLY_E_INVALID, "workspace must be 256-byte aligned");
   if ((h->flags & SEGPOLY_VALIDATE) && n_atoms > 0) {
     int st = idx_dtype == SEGPOLY_I32 ? check_species<int32_t>(species, n_atoms, h->num_elements, stream)
@@ -681,7 +735,15 @@ int symcon_bwd(symcon_handle h, const void* x, const void* species, const void* 
   a.idx = idx_dtype;
   a.layout = h->layout;
   a.stream = stream;
-  const int rc = h->spec->launch_bwd(a);
+  int rc;
+  if (h->spec) {
+    rc = h->spec->launch_bwd(a);
+  } else {
+    int st = SEGPOLY_OK;
+    void* dp = upload(h->dev, h->mu, h->blob.data(), h->blob.size(), &st);
+    if (!dp) return st;
+    rc = launch_symcon_generic_bwd(a, generic_symcon_info(h, dp));
+  }
   if (rc != 0)
     return fail(SEGPOLY_E_HIP, std::string("kernel launch failed: ") + hipGetErrorString(static_cast<hipError_t>(rc)));
   return ok();

@@ -1,6 +1,7 @@
 // Device-side tables of the table-driven kernels (plain structs, uploaded
 // once per device by the C ABI).
 #pragma once
+#include <cstddef>
 #include <cstdint>
 
 #include "launch.hpp"
@@ -8,8 +9,14 @@
 namespace segpoly {
 
 struct GPath {
-  int l1, lo, mul, nz_begin, nz_end, kcomp, pad0, pad1;
+  int l1, lo, mul, nz_begin, nz_end, kcomp, xcomp, pad1;
   int64_t off1, off2, offo, woff;
+};
+
+// an input-1 block of the tensor product (for the backward's dx rows)
+struct GIn {
+  int l, comp, mul, pad;
+  int64_t off;
 };
 
 struct GNz {
@@ -29,8 +36,9 @@ struct GBlock {
 struct GenericTPInfo {
   const GPath* paths;
   const GNz* nz;
-  int np, nk, max_mul;
-  int64_t dim1, dim2, dimo;
+  const GIn* in;      // input-1 blocks (backward only)
+  int np, nk, max_mul, n_in, nx;
+  int64_t dim1, dim2, dimo, numel;
 };
 
 struct GenericSymconInfo {
@@ -43,5 +51,12 @@ struct GenericSymconInfo {
 
 int launch_tp_generic(const TPArgs& a, const GenericTPInfo& g);
 int launch_symcon_generic(const SymconArgs& a, const GenericSymconInfo& g);
+// backward of the table-driven products (no workspace but the shared-weight
+// rows and their chunk sums, laid out as for the generated kernels)
+int launch_tp_generic_bwd(const TPBwdArgs& a, const GenericTPInfo& g);
+int launch_symcon_generic_bwd(const SymconBwdArgs& a, const GenericSymconInfo& g);
+// LDS the table-driven backward kernels need (bytes), for the C ABI's checks
+size_t tp_generic_bwd_lds(int nx, int64_t dim2, int dtype);
+size_t symcon_generic_bwd_lds(int nv, int no, int nseg, int dtype);
 
 }  // namespace segpoly

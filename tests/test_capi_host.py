@@ -262,8 +262,17 @@ def test_backward_argument_errors_fail_before_any_gpu_call():
     assert f(hs._h, p, 2, p, p, None, None, None, 0, 2, 2, p, p, p, p, odd, big, None) == sp.E_INVALID
     assert b"aligned" in sp.lib.segpoly_last_error()
     assert f(hs._h, p, 1, p, p, p, p, p, 0, 1, 1, p, p, p, None, p, big, None) == sp.E_INVALID  # grad_w
+    # table-driven descriptors: no workspace, except the shared-weight rows
     hg = sp.tp_create("32x0e+32x1o", "0e+1o", "0e+1o", force_generic=True)
-    assert f(hg._h, p, 1, p, p, p, p, p, 0, 1, 1, p, p, p, p, p, big, None) == sp.E_UNSUPPORTED
+    assert sp.tp_conv_bwd_workspace(hg, 1000) == 0
+    hgs = sp.tp_create("32x0e+32x1o", "0e+1o", "0e+1o", force_generic=True, shared_weights=True)
+    assert sp.tp_conv_bwd_workspace(hgs, 2049) == r256(2049 * hgs.weight_numel * 4) + 3 * hgs.weight_numel * 4
+    assert f(hgs._h, p, 1, p, p, p, p, p, 0, 1, 1, p, p, p, p, None, 0, None) == sp.E_INVALID  # no workspace
+    # more input components per channel than the table-driven backward holds
+    # in LDS (float64: 128 components of 64 lanes)
+    hbig = sp.tp_create("+".join(["2x6e"] * 10), "1o", "5o", dtype="f64")   # 130 input components
+    assert not hbig.specialized
+    assert f(hbig._h, p, 1, p, p, p, p, p, 0, 1, 1, p, p, p, p, p, big, None) == sp.E_UNSUPPORTED
     # nothing to do: succeeds without touching a device
     assert f(h._h, None, 0, None, None, None, None, None, 0, 0, 0, None, None, None, None, None, 0,
              None) == sp.OK
@@ -292,7 +301,8 @@ def test_symcon_backward_argument_errors_fail_before_any_gpu_call():
     assert b"aligned" in sp.lib.segpoly_last_error()
     assert f(s._h, p, p, p, 0, p, p, 1 << 31, p, p, p, big, None) == sp.E_UNSUPPORTED
     sg = sp.symcon_create("32x0e+32x1o", "32x0e", 3, 4, force_generic=True)
-    assert f(sg._h, p, p, p, 0, p, p, 3, p, p, p, big, None) == sp.E_UNSUPPORTED
+    assert sp.symcon_bwd_workspace(sg, 100) == 0   # the table-driven backward needs none
+    assert f(sg._h, p, p, p, 0, p, p, 3, p, None, None, 0, None) == sp.E_INVALID  # no grad_w
 
 
 def test_linear_descriptor_and_errors():
