@@ -116,12 +116,16 @@ def test_ragged_tiles(layout):
 
 
 @pytest.mark.parametrize("n", [400, 3000])
-@pytest.mark.parametrize("order", ["sorted", "unsorted"])
+@pytest.mark.parametrize("order", ["sorted", "sorted_out_of_range_ends", "unsorted"])
 def test_class_indexed(order, n):
     """Species-indexed weights: sorted classes (the pages' contract) and an
-    unsorted order (still exact), an out-of-range class (zero row, zero
-    dx, no weight-gradient contribution), int64 indices for the unsorted
-    case; 3000 samples span several row chunks of the weight gradient."""
+    unsorted order (still exact), out-of-range classes (zero row, zero dx,
+    no weight-gradient contribution), int64 indices for the unsorted case;
+    3000 samples span several row chunks of the weight gradient.  "sorted"
+    puts an out-of-range class inside the first chunk (which then takes the
+    masked pass); "sorted_out_of_range_ends" keeps the order sorted with
+    leading -1 and trailing num_classes, so every chunk takes the
+    binary-searched pass over its classes' runs, including the end chunks."""
     sp = _sp()
     wl = workloads.WORKLOADS[7]
     o = olin.Linear(wl.irreps_in, wl.irreps_out)
@@ -130,24 +134,70 @@ def test_class_indexed(order, n):
     cls = inp["classes"].copy()
     if order == "unsorted":
         cls = np.random.default_rng(3).permutation(cls).astype(np.int64)
-    cls[5] = wl.num_classes          # out of range
+    if order == "sorted_out_of_range_ends":
+        cls[:3] = -1
+        cls[-4:] = wl.num_classes
+        assert np.all(np.diff(cls) >= 0)
+        oob = np.r_[0:3, n - 4:n]
+    else:
+        cls[5] = wl.num_classes      # out of range
+        oob = np.array([5])
     g = workloads.output_gradient(n, o.dim_out, "f32", seed=71)
     announce(f"linear class-indexed {order} n={n}")
     got = _fwd(sp, h, inp["x"], inp["w"], cls)
     check_scaled(got, o.fwd(inp["x"], inp["w"], indices=cls), o.fwd(inp["x"], inp["w"], indices=cls, absolute=True),
                  "f32", f"class-indexed fwd {order}")
-    assert np.count_nonzero(got[5]) == 0
+    assert np.count_nonzero(got[oob]) == 0
     gx, gw = _bwd(sp, h, inp["x"], inp["w"], g, cls, need_dw=False)
     assert gw is None
     rx, rw = o.vjp(inp["x"], inp["w"], g, indices=cls)
     sx, sw = o.vjp(inp["x"], inp["w"], g, indices=cls, absolute=True)
     check_scaled(gx, rx, sx, "f32", f"class-indexed dx {order}")
-    assert np.count_nonzero(gx[5]) == 0
+    assert np.count_nonzero(gx[oob]) == 0
     # weight gradient: one row per class, each summing its own samples
     gx2, gw = _bwd(sp, h, inp["x"], inp["w"], g, cls)
     assert gw.shape == inp["w"].shape
     assert np.array_equal(gx2, gx)
     check_scaled(gw, rw, sw, "f32", f"class-indexed dw {order}")
+
+
+@pytest.mark.parametrize("layout", ["ir_mul", "mul_ir"])
+def test_class_indexed_full_size(layout):
+    """The species layer at the shape the benchmark times: 50,000 atoms,
+    10 sorted classes (about 25 weight-gradient row chunks), in the same
+    launch configuration.  Forward and dx on 256 sampled rows (the oracle on
+    those rows); for the weight gradient a second call whose output gradient
+    is zero except on 1,024 sampled rows spread over every chunk, so the
+    oracle on those rows alone gives all of dw (the oracle over all 50,000
+    rows takes minutes)."""
+    sp = _sp()
+    wl = workloads.WORKLOADS[7]
+    o = olin.Linear(wl.irreps_in, wl.irreps_out)
+    h = sp.linear_create(wl.irreps_in, wl.irreps_out, layout=layout)
+    inp = workloads.linear_inputs(wl, o.weight_numel)
+    n = wl.n
+    cls = inp["classes"]
+    assert n == 50000 and np.all(np.diff(cls) >= 0) and len(np.unique(cls)) == wl.num_classes
+    g = workloads.output_gradient(n, o.dim_out, "f32", seed=72)
+    announce(f"linear class-indexed full size {layout} n={n}")
+    got = _fwd(sp, h, inp["x"], inp["w"], cls)
+    gx, gw = _bwd(sp, h, inp["x"], inp["w"], g, cls)
+    rows = np.sort(np.random.default_rng(73).choice(n, 256, replace=False))
+    xs, cs, gs = inp["x"][rows], cls[rows], g[rows]
+    check_scaled(got[rows], o.fwd(xs, inp["w"], layout=layout, indices=cs),
+                 o.fwd(xs, inp["w"], layout=layout, indices=cs, absolute=True), "f32", f"full-size fwd {layout}")
+    (rx, _), (sx, _) = (o.vjp(xs, inp["w"], gs, layout=layout, indices=cs),
+                        o.vjp(xs, inp["w"], gs, layout=layout, indices=cs, absolute=True))
+    check_scaled(gx[rows], rx, sx, "f32", f"full-size dx {layout}")
+    assert gw.shape == inp["w"].shape and np.all(np.isfinite(gw))
+    keep = np.sort(np.random.default_rng(74).choice(n, 1024, replace=False))
+    gm = np.zeros_like(g)
+    gm[keep] = g[keep]
+    _, gw2 = _bwd(sp, h, inp["x"], inp["w"], gm, cls)
+    xk, ck, gk = inp["x"][keep], cls[keep], g[keep]
+    (_, rw), (_, sw) = (o.vjp(xk, inp["w"], gk, layout=layout, indices=ck),
+                        o.vjp(xk, inp["w"], gk, layout=layout, indices=ck, absolute=True))
+    check_scaled(gw2, rw, sw, "f32", f"full-size dw {layout}")
 
 
 def test_float64_backward_and_determinism():
