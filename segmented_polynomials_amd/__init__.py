@@ -15,7 +15,9 @@ import os
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libsegpoly.so")
+# SEGPOLY_LIB selects another build of the same library (the sanitizer
+# build of build_sanitize.py); by default the one built next to this file
+LIB_PATH = os.environ.get("SEGPOLY_LIB") or os.path.join(_HERE, "libsegpoly.so")
 
 OK = 0
 E_INVALID, E_PARSE, E_UNSUPPORTED, E_UNSORTED, E_HIP, E_OOM, E_RANGE = -1, -2, -3, -4, -5, -6, -7
