@@ -389,7 +389,8 @@ int symcon_destroy(symcon_handle h);
  * t); an output block whose type no input has is zero.  Weight segments:
  * pairs in the order i, then o, each mul_i x mul_o with v fastest
  * (WEIGHT_NUMEL in total).  flags: SEGPOLY_VALIDATE only.  E_UNSUPPORTED
- * beyond 32 blocks on a side or 32 pairs.  Touches no GPU.
+ * beyond 32 blocks on a side or 32 pairs, DIM_IN or DIM_OUT above 65536 or
+ * WEIGHT_NUMEL above 2^27.  Touches no GPU.
  */
 int linear_create(const char* irreps_in, const char* irreps_out, int layout, int dtype, unsigned flags,
                   linear_handle* out);

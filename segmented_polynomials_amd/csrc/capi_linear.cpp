@@ -156,6 +156,10 @@ int linear_create(const char* irreps_in, const char* irreps_out, int layout, int
         h->numel += static_cast<int64_t>(h->in[i].mul) * h->out[o].mul;
       }
   }
+  if (h->dim_in > kLinMaxDim || h->dim_out > kLinMaxDim || h->numel > kLinMaxNumel) {
+    delete h;
+    return fail(SEGPOLY_E_UNSUPPORTED, "rows wider than 65536 elements or more than 2^27 weights");
+  }
   const int n_pairs = static_cast<int>(woff.size());
   if (h->out.size() > static_cast<size_t>(kLinMaxOut) || h->in.size() > static_cast<size_t>(kLinMaxOut) ||
       n_pairs > kLinMaxPairs / 2) {

@@ -1,0 +1,40 @@
+// Loads through a buffer resource (gfx9 raw buffer, stride 0): the hardware
+// checks each offset against the resource's byte count and an offset at or
+// past it reads zero without touching memory.  A masked operand element is
+// then one select on a 32-bit offset before the load instead of a branch or
+// a select on the loaded value, and the loads of a staging pass can all be in
+// flight together.
+#pragma once
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace segpoly {
+namespace kern {
+
+// word 3 of a gfx9 buffer resource: 32-bit data format, no swizzle
+constexpr int kBufWord3 = 0x00020000;
+// an offset no resource reaches (byte counts are kept below it)
+constexpr uint32_t kBufMasked = 0x80000000u;
+constexpr int64_t kBufMaxBytes = 0x7fffffff;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, int64_t bytes) {
+  const int n = static_cast<int>(bytes < kBufMaxBytes ? bytes : kBufMaxBytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, n, kBufWord3);
+}
+
+template <typename T>
+__device__ __forceinline__ T buf_load(__amdgpu_buffer_rsrc_t r, uint32_t byte_off);
+
+template <>
+__device__ __forceinline__ float buf_load<float>(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, byte_off, 0, 0));
+}
+
+template <>
+__device__ __forceinline__ double buf_load<double>(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+  return __builtin_bit_cast(double, __builtin_amdgcn_raw_buffer_load_b64(r, byte_off, 0, 0));
+}
+
+}  // namespace kern
+}  // namespace segpoly

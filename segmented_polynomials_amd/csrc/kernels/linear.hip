@@ -12,9 +12,9 @@
 // kernel computes the backward's dx = alpha G W^T (TRANSW: the weight
 // segment is read transposed).
 //
-// Tiling: a workgroup of 4 waves owns a 64 x 128 tile of one output block's
-// GEMM; the K loop stages 64 x 32 of A (rows of x) and 32 x 128 of B (the
-// weight segment) in LDS; each wave computes 32 x 64 with eight
+// Tiling: a workgroup of 4 waves owns a 128 x 128 tile of one output block's
+// GEMM; the K loop stages 128 x 32 of A (rows of x) and 32 x 128 of B (the
+// weight segment) in LDS; each wave computes 64 x 64 with sixteen
 // v_mfma_*_16x16x4 per 4 k.  Class-indexed weights (one row of weights per
 // sample picked by an index, sorted in practice): the tile runs one masked
 // pass per class present among its rows (rows of other classes read as
@@ -25,6 +25,7 @@
 
 #include "../launch.hpp"
 #include "../linear_tables.hpp"
+#include "bufload.hpp"
 #include "mfma.hpp"
 
 namespace segpoly {
@@ -69,9 +70,12 @@ linear_kernel(const T* __restrict__ x, const T* __restrict__ w, const Index* __r
   const int wr = wave / 2, wc = wave % 2;  // wave tile: rows 32 wr.., cols 64 wc..
 
   // the A rows this thread stages: r = e * 8 + tid / 32, channel tid % 32
-  // (decomposed once: sample base address, component, class)
+  // (decomposed once: element offset from the tile's first sample s0,
+  // component, class).  Offsets stay below 2^31 bytes: a tile spans at most
+  // kLinTM + 1 samples and the host bounds dim_in.
   const int kk_a = tid % kLinTK;
-  int64_t a_base[kARows];
+  const int s0 = row0 / d;
+  int a_rel[kARows];
   int a_m[kARows];
   bool a_ok[kARows];
   int a_cls[CLASSES ? kARows : 1];
@@ -79,14 +83,16 @@ linear_kernel(const T* __restrict__ x, const T* __restrict__ w, const Index* __r
   for (int e = 0; e < kARows; ++e) {
     const int row = row0 + e * (kLinThreads / kLinTK) + tid / kLinTK;
     a_ok[e] = row < R;
-    const int nn = a_ok[e] ? row / d : 0;
+    const int nn = a_ok[e] ? row / d : s0;
     a_m[e] = a_ok[e] ? row - nn * d : 0;
-    a_base[e] = static_cast<int64_t>(nn) * dim_in;
+    a_rel[e] = (nn - s0) * static_cast<int>(dim_in);
     if constexpr (CLASSES) {
       const int64_t c = a_ok[e] ? static_cast<int64_t>(cls[nn]) : -1;
       a_cls[e] = (c >= 0 && c < num_classes) ? static_cast<int>(c) : -1;
     }
   }
+  const __amdgpu_buffer_rsrc_t x_rsrc =
+      buf_rsrc(x + static_cast<int64_t>(s0) * dim_in, (n - s0) * dim_in * static_cast<int64_t>(sizeof(T)));
 
   // classes present among the tile's rows
   int cmin = 0, cmax = 0;
@@ -105,8 +111,8 @@ linear_kernel(const T* __restrict__ x, const T* __restrict__ w, const Index* __r
         }
     }
     __syncthreads();
-    cmin = cls_range[0];
-    cmax = cls_range[1];
+    cmin = __builtin_amdgcn_readfirstlane(cls_range[0]);
+    cmax = __builtin_amdgcn_readfirstlane(cls_range[1]);
   }
 
   typename M::acc_t acc[kMT][kNT];
@@ -119,34 +125,35 @@ linear_kernel(const T* __restrict__ x, const T* __restrict__ w, const Index* __r
   // kLinTK channels); the next chunk's global loads are issued into
   // registers before the current chunk's MFMAs, so their latency hides
   // behind the matrix work.
+  // Staging loads go through buffer resources: a masked element (a row past
+  // the end or of another class, a channel past the block's K, a column past
+  // its N) gets an offset beyond the resource and reads zero, so no load
+  // waits on a branch or a select of its value.
   T ra[kARows], rb[kBElems];
   auto fetch = [&](int c, int p, int k0) {
     const LinPair P = tab.pairs[p];
-    const T* wc_base = CLASSES ? w + static_cast<int64_t>(c) * numel : w;
+    const __amdgpu_buffer_rsrc_t w_rsrc =
+        buf_rsrc(CLASSES ? w + static_cast<int64_t>(c) * numel : w, numel * static_cast<int64_t>(sizeof(T)));
     const int u = k0 + kk_a;
+    const bool u_in = u < P.k_ext;
+    const int in_off = static_cast<int>(P.in_off), k_ext = P.k_ext;
 #pragma unroll
     for (int e = 0; e < kARows; ++e) {
-      bool take = a_ok[e] && u < P.k_ext;
+      bool take = a_ok[e] && u_in;
       if constexpr (CLASSES) take = take && a_cls[e] == c;
-      T v = T(0);
-      if (take) {
-        const int64_t off = LAYOUT == kIrMul ? P.in_off + static_cast<int64_t>(a_m[e]) * P.k_ext + u
-                                             : P.in_off + static_cast<int64_t>(u) * d + a_m[e];
-        v = x[a_base[e] + off];
-      }
-      ra[e] = v;
+      const int off = a_rel[e] + in_off + (LAYOUT == kIrMul ? a_m[e] * k_ext + u : u * d + a_m[e]);
+      ra[e] = buf_load<T>(x_rsrc, take ? static_cast<uint32_t>(off) * sizeof(T) : kBufMasked);
     }
+    const int w_off = static_cast<int>(P.w_off), n_ext = O.n_ext;
 #pragma unroll
     for (int e = 0; e < kBElems; ++e) {
       const int idx = e * kLinThreads + tid;
       const int kk = TRANSW ? idx % kLinTK : idx / kLinTN;
       const int cc = TRANSW ? idx / kLinTK : idx % kLinTN;
       const int uu = k0 + kk, v = col0 + cc;
-      T val = T(0);
-      if (uu < P.k_ext && v < O.n_ext)
-        val = TRANSW ? wc_base[P.w_off + static_cast<int64_t>(v) * P.k_ext + uu]
-                     : wc_base[P.w_off + static_cast<int64_t>(uu) * O.n_ext + v];
-      rb[e] = val;
+      const bool in = uu < k_ext && v < n_ext;
+      const int off = w_off + (TRANSW ? v * k_ext + uu : uu * n_ext + v);
+      rb[e] = buf_load<T>(w_rsrc, in ? static_cast<uint32_t>(off) * sizeof(T) : kBufMasked);
     }
   };
   // advance (c, p, k0) to the next chunk; false at the end
@@ -293,6 +300,15 @@ linear_dw_kernel(const T* __restrict__ x, const T* __restrict__ g, T* __restrict
   const int sa_n = kAStep / d, sa_m = kAStep - sa_n * d;            // divmod(kAStep, d)
   const int sb_n = kBStep / d, sb_m = kBStep - sb_n * d;            // divmod(kBStep, d)
   const int u = u0 + uu_a, v = v0 + vv_b;
+  const bool u_in = u < P.mul_in, v_in = v < P.mul_out;
+  const int x_off = static_cast<int>(P.x_off), g_off = static_cast<int>(P.g_off);
+  // the chunk's rows through buffer resources based at its first sample:
+  // 32-bit offsets, as a chunk spans at most kLinDwRows samples and the host
+  // bounds dim_in and dim_out
+  const __amdgpu_buffer_rsrc_t x_rsrc = buf_rsrc(x + static_cast<int64_t>(s_begin) * dim_in,
+                                                 (n - s_begin) * dim_in * static_cast<int64_t>(sizeof(T)));
+  const __amdgpu_buffer_rsrc_t g_rsrc = buf_rsrc(g + static_cast<int64_t>(s_begin) * dim_out,
+                                                 (n - s_begin) * dim_out * static_cast<int64_t>(sizeof(T)));
   for (int cc = c_lo; cc <= c_hi; ++cc) {
   // rows [kb, ke) of the pass; when the chunk's classes are sorted, class
   // cc is one run of samples (found by binary search) and the pass covers
@@ -318,28 +334,29 @@ linear_dw_kernel(const T* __restrict__ x, const T* __restrict__ g, T* __restrict
   }
   int a_n = (kb + rk_a) / d, a_m = (kb + rk_a) - a_n * d;
   int b_n = (kb + rk_b) / d, b_m = (kb + rk_b) - b_n * d;
-  // rows of another class than cc contribute nothing
-  auto in_class = [&](int nn) { return !mask || cls_s[nn - s_begin] == cc; };
+  // rows of another class than cc contribute nothing (the index is clamped
+  // so that the read stays in cls_s for rows past the pass)
+  auto in_class = [&](int nn) {
+    const int i = nn - s_begin < kLinDwRows - 1 ? nn - s_begin : kLinDwRows - 1;
+    return !mask || cls_s[i] == cc;
+  };
   typename M::acc_t acc[kMT][kNT];
 #pragma unroll
   for (int a = 0; a < kMT; ++a)
 #pragma unroll
     for (int b = 0; b < kNT; ++b) acc[a][b] = typename M::acc_t{0, 0, 0, 0};
   // the next chunk of rows is loaded into registers while the current one
-  // is multiplied
+  // is multiplied; masked elements read zero through the buffer range check
   T ra[kLinTK / kAStep], rb[kLinTK / kBStep];
   auto fetch = [&](int k0) {
     int nn = a_n, m = a_m;
 #pragma unroll
     for (int e = 0; e < kLinTK / kAStep; ++e) {
       const int row = k0 + rk_a + e * kAStep;
-      T val = T(0);
-      if (row < ke && u < P.mul_in && in_class(nn)) {
-        const int64_t off = LAYOUT == kIrMul ? P.x_off + static_cast<int64_t>(m) * P.mul_in + u
-                                             : P.x_off + static_cast<int64_t>(u) * d + m;
-        val = x[static_cast<int64_t>(nn) * dim_in + off];
-      }
-      ra[e] = val;
+      const bool take = row < ke && u_in && in_class(nn);
+      const int off = (nn - s_begin) * static_cast<int>(dim_in) + x_off +
+                      (LAYOUT == kIrMul ? m * P.mul_in + u : u * d + m);
+      ra[e] = buf_load<T>(x_rsrc, take ? static_cast<uint32_t>(off) * sizeof(T) : kBufMasked);
       nn += sa_n;
       m += sa_m;
       if (m >= d) {
@@ -352,13 +369,10 @@ linear_dw_kernel(const T* __restrict__ x, const T* __restrict__ g, T* __restrict
 #pragma unroll
     for (int e = 0; e < kLinTK / kBStep; ++e) {
       const int row = k0 + rk_b + e * kBStep;
-      T val = T(0);
-      if (row < ke && v < P.mul_out && in_class(nn)) {
-        const int64_t off = LAYOUT == kIrMul ? P.g_off + static_cast<int64_t>(m) * P.mul_out + v
-                                             : P.g_off + static_cast<int64_t>(v) * d + m;
-        val = g[static_cast<int64_t>(nn) * dim_out + off];
-      }
-      rb[e] = val;
+      const bool take = row < ke && v_in && in_class(nn);
+      const int off = (nn - s_begin) * static_cast<int>(dim_out) + g_off +
+                      (LAYOUT == kIrMul ? m * P.mul_out + v : v * d + m);
+      rb[e] = buf_load<T>(g_rsrc, take ? static_cast<uint32_t>(off) * sizeof(T) : kBufMasked);
       nn += sb_n;
       m += sb_m;
       if (m >= d) {

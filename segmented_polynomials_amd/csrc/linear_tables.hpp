@@ -32,6 +32,14 @@ constexpr int kLinTileCols = 128;
 constexpr int kLinMaxOut = 32;
 constexpr int kLinMaxPairs = 64;
 
+// The kernels address operands through buffer resources with 32-bit byte
+// offsets from a tile's (or a row chunk's) first sample.  A row chunk of the
+// weight gradient spans at most kLinDwRows (2048) samples, so rows of at most
+// 2^16 elements of 8 bytes keep every offset below 2^30 bytes; a class's
+// weight row of at most 2^27 elements likewise.
+constexpr int64_t kLinMaxDim = int64_t(1) << 16;
+constexpr int64_t kLinMaxNumel = int64_t(1) << 27;
+
 struct LinTable {
   int n_out;
   int total_tiles;

@@ -320,6 +320,13 @@ def test_linear_descriptor_and_errors():
     assert sp.lib.linear_create(b"3x0e", b"3x0e", 0, 0, 1, ctypes.byref(raw)) == sp.E_INVALID   # flag
     big = "+".join(["1x0e"] * 40)
     assert sp.lib.linear_create(big.encode(), b"1x0e", 0, 0, 0, ctypes.byref(raw)) == sp.E_UNSUPPORTED
+    # rows up to 65536 elements and 2^27 weights (32-bit operand offsets)
+    wide = sp.linear_create("65536x0e", "1x0e")
+    assert wide.dim_in == 65536
+    assert sp.lib.linear_create(b"65537x0e", b"1x0e", 0, 0, 0, ctypes.byref(raw)) == sp.E_UNSUPPORTED
+    assert sp.lib.linear_create(b"1x0e", b"21846x1o", 0, 0, 0, ctypes.byref(raw)) == sp.E_UNSUPPORTED
+    assert sp.lib.linear_create(b"12000x0e", b"12000x0e", 0, 0, 0, ctypes.byref(raw)) == sp.E_UNSUPPORTED
+    assert b"65536" in sp.lib.segpoly_last_error()
     p = ctypes.c_void_p(16)
     f = sp.lib.linear_fwd
     assert f(h._h, p, p, None, 0, 1, -1, p, None) == sp.E_INVALID
