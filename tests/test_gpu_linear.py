@@ -200,6 +200,44 @@ def test_class_indexed_full_size(layout):
     check_scaled(gw2, rw, sw, "f32", f"full-size dw {layout}")
 
 
+@pytest.mark.parametrize("layout", ["ir_mul", "mul_ir"])
+@pytest.mark.parametrize("classes", [False, True])
+def test_many_tiles_per_workgroup(layout, classes):
+    """More tiles than the device holds workgroups at once (2,800 tiles
+    of 128 rows), an output block no input type feeds (zero tiles), and
+    with classes: a sorted half and an unsorted half, out-of-range classes,
+    and a run of 400 samples with no valid class (tiles with no pass,
+    stored as zeros)."""
+    sp = _sp()
+    import torch
+    ins, outs = "32x0e+16x1o+8x1o", "40x0e+24x1o+8x2e"
+    o = olin.Linear(ins, outs)
+    h = sp.linear_create(ins, outs, layout=layout)
+    n, nc = 40000, 7
+    rng = np.random.default_rng(75)
+    x = rng.standard_normal((n, o.dim_in), dtype=np.float32)
+    w = rng.standard_normal((nc if classes else 1, o.weight_numel), dtype=np.float32)
+    cls = None
+    if classes:
+        cls = rng.integers(-1, nc + 1, n).astype(np.int32)
+        cls[:20000] = np.sort(cls[:20000])
+        cls[25000:25400] = -1
+    announce(f"linear many tiles {layout} classes={classes}")
+    out = sp.linear_fwd(h, dev(x), dev(w), classes=None if cls is None else dev(cls),
+                        num_classes=nc if classes else None)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    rows = np.sort(np.concatenate([rng.choice(n, 600, replace=False), np.arange(24990, 25010), [0, n - 1]]))
+    kw = {} if cls is None else {"indices": cls[rows]}
+    check_scaled(got[rows], o.fwd(x[rows], w, layout=layout, **kw), o.fwd(x[rows], w, layout=layout, absolute=True, **kw),
+                 "f32", f"many tiles {layout} classes={classes}")
+    if classes:
+        bad = (cls < 0) | (cls >= nc)
+        assert np.count_nonzero(got[bad]) == 0
+    # the 2e block (the last 8 x 5 columns in either layout) has no input of its type
+    assert np.count_nonzero(got[:, o.dim_out - 40:]) == 0
+
+
 def test_float64_backward_and_determinism():
     sp = _sp()
     ins, outs = "16x0e+8x1o+8x1o", "12x0e+20x1o"

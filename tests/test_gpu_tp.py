@@ -218,6 +218,47 @@ def test_shared_weights_and_source_count():
     check_scaled(got, ref, scale, "f32", "shared weights")
 
 
+@pytest.mark.parametrize("idx", ["int32", "int64"])
+def test_split_kernel_range_search(idx):
+    """The destination-split kernel (multiplicity 32) on a graph of 78,000
+    edges (four rounds of the 64-ary range search), with hub nodes of
+    in-degree 300 and 700 (range ends past the 64 entries the end search
+    probes first, and many edges per lane group), isolated nodes, the first
+    and last node with edges, and out-of-range sources spread over the
+    graph and inside a hub's range (they add nothing); int32 and int64
+    indices."""
+    sp = _sp()
+    import torch
+    in1, in2, filt = "32x0e+32x1o", "0e+1o+2e", "0e+1o+2e"
+    o = otp.ChannelwiseTP(in1, in2, filt)
+    h = sp.tp_create(in1, in2, filt, layout="mul_ir")
+    rng = np.random.default_rng(42)
+    n = 3000
+    deg = rng.integers(0, 51, n)
+    deg[rng.random(n) < 0.1] = 0
+    deg[[0, n - 1]] = [5, 9]
+    deg[[1000, 2500]] = [300, 700]
+    dst = np.repeat(np.arange(n), deg)
+    e = dst.shape[0]
+    src = rng.integers(0, n, e)
+    hub = np.flatnonzero(dst == 2500)
+    bad = np.concatenate([rng.choice(e, 40, replace=False), hub[[3, 400, 650]]])
+    src[bad] = n + 7
+    inp = dict(x=rng.standard_normal((n, o.dim_in1), dtype=np.float32),
+               sh=rng.standard_normal((e, o.dim_in2), dtype=np.float32),
+               w=rng.standard_normal((e, o.weight_numel), dtype=np.float32),
+               src=src, dst=dst, n_nodes=n)
+    assert e > 65536
+    announce(f"tp split-kernel range search {idx} edges={e}")
+    got = _run(sp, h, inp, idx_dtype=getattr(torch, idx))
+    ok = src < n
+    sub = dict(inp, sh=inp["sh"][ok], w=inp["w"][ok], src=src[ok], dst=dst[ok])
+    nodes = np.unique(np.concatenate([rng.choice(n, 300, replace=False), [0, 1, 1000, 2500, n - 2, n - 1]]))
+    ref, scale = _oracle(o, sub, "mul_ir", nodes=nodes)
+    check_scaled(got[nodes], ref, scale, "f32", f"split search {idx}")
+    assert np.count_nonzero(got[deg == 0]) == 0
+
+
 def test_no_edges_gives_zero_rows():
     sp = _sp()
     import torch
