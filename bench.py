@@ -641,9 +641,36 @@ def linear_layers(torch, sp, workloads, dev, args):
                                                         "peak": FP32_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                                                         "frac": tfb / FP32_MFMA_PEAK_TFLOPS}}
         del g, ws
+        r["library_gemm_reference"] = library_gemm_reference(torch, dev, args, wl, blocks_in, blocks_out, flops)
         res[wl.name] = r
         del x, w, out, cls
     return res
+
+
+def library_gemm_reference(torch, dev, args, wl, blocks_in, blocks_out, flops):
+    """What the vendor BLAS (torch.mm on ROCm: hipBLASLt / rocBLAS, float32,
+    no reduced-precision modes) reaches on the same dense products: one
+    [n (2l+1), K] x [K, mul_out] GEMM per output block, K = the input
+    channels of its type, with one shared weight matrix.  A measuring stick
+    for the hand-written kernels on these tall, short-K shapes, never part
+    of the layer's path (and for the species-indexed layer a lower bound of
+    its work: it ignores the per-class weights)."""
+    torch.backends.cuda.matmul.allow_tf32 = False
+    mats = []
+    for mo, lo, po in blocks_out:
+        k = sum(mi for mi, li, pi in blocks_in if (li, pi) == (lo, po))
+        if k == 0:
+            continue
+        m = wl.n * (2 * lo + 1)
+        mats.append((torch.randn(m, k, device=dev), torch.randn(k, mo, device=dev), torch.empty(m, mo, device=dev)))
+    f = lambda: [torch.mm(a, b, out=c) for a, b, c in mats]
+    wall, per = time_launches(torch, f, args.steps, args.warmup)
+    ms = sum(per) / len(per)
+    tf = flops / (ms * 1e-3) / 1e12
+    del mats
+    return {"ms_per_call": ms, "shapes": "one GEMM per output block, shared weights",
+            "roofline": {"bound": "mfma", "achieved": tf, "peak": FP32_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": tf / FP32_MFMA_PEAK_TFLOPS}}
 
 
 def fc_product(torch, sp, workloads, dev, args):
