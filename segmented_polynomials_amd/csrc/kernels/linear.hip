@@ -50,8 +50,12 @@ linear_kernel(const T* __restrict__ x, const T* __restrict__ w, const Index* __r
               LinTable tab) {
   using M = Mfma<T>;
   __shared__ T As[kLinTM][kLinTK + kLinPadA];
-  __shared__ T Bs[kLinTK][kLinTN + kLinPadB];
-  __shared__ int cls_range[2];
+  // B as [k][column]; with TRANSW as [column][k]: the transposed segment is
+  // read k-contiguous, and writing it k-major into [k][column] rows of 144
+  // put 8 lanes of a wave on each bank
+  constexpr int kBRows = TRANSW ? kLinTN : kLinTK, kBCols = TRANSW ? kLinTK + kLinPadA : kLinTN + kLinPadB;
+  __shared__ T Bs[kBRows][kBCols];
+  __shared__ int cls_range[kLinThreads / 64][2];
 
   // which output block and tile
   const int bid = blockIdx.x;
@@ -94,27 +98,6 @@ linear_kernel(const T* __restrict__ x, const T* __restrict__ w, const Index* __r
   const __amdgpu_buffer_rsrc_t x_rsrc =
       buf_rsrc(x + static_cast<int64_t>(s0) * dim_in, (n - s0) * dim_in * static_cast<int64_t>(sizeof(T)));
 
-  // classes present among the tile's rows
-  int cmin = 0, cmax = 0;
-  if constexpr (CLASSES) {
-    if (tid == 0) {
-      cls_range[0] = num_classes;
-      cls_range[1] = -1;
-    }
-    __syncthreads();
-    if (kk_a == 0) {
-#pragma unroll
-      for (int e = 0; e < kARows; ++e)
-        if (a_cls[e] >= 0) {
-          atomicMin(&cls_range[0], a_cls[e]);
-          atomicMax(&cls_range[1], a_cls[e]);
-        }
-    }
-    __syncthreads();
-    cmin = __builtin_amdgcn_readfirstlane(cls_range[0]);
-    cmax = __builtin_amdgcn_readfirstlane(cls_range[1]);
-  }
-
   typename M::acc_t acc[kMT][kNT];
 #pragma unroll
   for (int a = 0; a < kMT; ++a)
@@ -126,9 +109,11 @@ linear_kernel(const T* __restrict__ x, const T* __restrict__ w, const Index* __r
   // registers before the current chunk's MFMAs, so their latency hides
   // behind the matrix work.
   // Staging loads go through buffer resources: a masked element (a row past
-  // the end or of another class, a channel past the block's K, a column past
-  // its N) gets an offset beyond the resource and reads zero, so no load
-  // waits on a branch or a select of its value.
+  // the end, a channel past the block's K, a column past its N) gets an
+  // offset beyond the resource and reads zero, so no load waits on a branch
+  // or a select of its value.  The class mask is applied when the chunk is
+  // written to LDS: the loads of a tile's first chunk then wait for no class
+  // of its rows, only for the (scalar) class of its first sample.
   T ra[kARows], rb[kBElems];
   auto fetch = [&](int c, int p, int k0) {
     const LinPair P = tab.pairs[p];
@@ -139,8 +124,7 @@ linear_kernel(const T* __restrict__ x, const T* __restrict__ w, const Index* __r
     const int in_off = static_cast<int>(P.in_off), k_ext = P.k_ext;
 #pragma unroll
     for (int e = 0; e < kARows; ++e) {
-      bool take = a_ok[e] && u_in;
-      if constexpr (CLASSES) take = take && a_cls[e] == c;
+      const bool take = a_ok[e] && u_in;
       const int off = a_rel[e] + in_off + (LAYOUT == kIrMul ? a_m[e] * k_ext + u : u * d + a_m[e]);
       ra[e] = buf_load<T>(x_rsrc, take ? static_cast<uint32_t>(off) * sizeof(T) : kBufMasked);
     }
@@ -156,28 +140,85 @@ linear_kernel(const T* __restrict__ x, const T* __restrict__ w, const Index* __r
       rb[e] = buf_load<T>(w_rsrc, in ? static_cast<uint32_t>(off) * sizeof(T) : kBufMasked);
     }
   };
-  // advance (c, p, k0) to the next chunk; false at the end
+
+  // Classes: the tile makes one pass per class between the lowest (cmin)
+  // and highest (cmax) class among its rows, starting with the class of its
+  // first sample (`first`) when that is in range, so that the first chunk's
+  // loads go out before the class range is known.
+  int cmin = 0, cmax = 0, first = 0;
+  int c = 0, p = O.pair_begin, k0 = 0;
+  bool have = O.pair_begin < O.pair_end;
+  if constexpr (CLASSES) {
+    const int64_t c0 = static_cast<int64_t>(cls[s0]);
+    first = (c0 >= 0 && c0 < num_classes) ? static_cast<int>(c0) : -1;
+    if (have && first >= 0) fetch(first, p, k0);
+    // range over the wave's rows, then over the four waves through LDS
+    int lo = num_classes, hi = -1;
+#pragma unroll
+    for (int e = 0; e < kARows; ++e)
+      if (a_cls[e] >= 0) {
+        lo = a_cls[e] < lo ? a_cls[e] : lo;
+        hi = a_cls[e] > hi ? a_cls[e] : hi;
+      }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      const int l2 = __shfl_xor(lo, o), h2 = __shfl_xor(hi, o);
+      lo = l2 < lo ? l2 : lo;
+      hi = h2 > hi ? h2 : hi;
+    }
+    if (lane == 0) {
+      cls_range[wave][0] = lo;
+      cls_range[wave][1] = hi;
+    }
+    __syncthreads();
+    cmin = num_classes;
+    cmax = -1;
+#pragma unroll
+    for (int q = 0; q < kLinThreads / 64; ++q) {
+      cmin = cls_range[q][0] < cmin ? cls_range[q][0] : cmin;
+      cmax = cls_range[q][1] > cmax ? cls_range[q][1] : cmax;
+    }
+    cmin = __builtin_amdgcn_readfirstlane(cmin);
+    cmax = __builtin_amdgcn_readfirstlane(cmax);
+    if (first < 0) {
+      first = cmin;
+      have = have && cmin <= cmax;
+      if (have) fetch(first, p, k0);
+    }
+    c = first;
+  } else {
+    if (have) fetch(c, p, k0);
+  }
+  // advance (c, p, k0) to the next chunk; false at the end.  After the
+  // first class the passes run from cmin up, skipping `first`.
   auto next = [&](int& c, int& p, int& k0) -> bool {
     k0 += kLinTK;
     if (k0 < tab.pairs[p].k_ext) return true;
     k0 = 0;
     if (++p < O.pair_end) return true;
     p = O.pair_begin;
-    return ++c <= cmax;
+    if constexpr (!CLASSES) return false;
+    c = c == first ? cmin : c + 1;
+    if (c == first) ++c;
+    return c <= cmax;
   };
-  int c = cmin, p = O.pair_begin, k0 = 0;
-  bool have = c <= cmax && O.pair_begin < O.pair_end;
-  if (have) fetch(c, p, k0);
   while (have) {
     __syncthreads();  // the previous chunk's operands are no longer read
 #pragma unroll
-    for (int e = 0; e < kARows; ++e) As[e * (kLinThreads / kLinTK) + tid / kLinTK][kk_a] = ra[e];
+    for (int e = 0; e < kARows; ++e) {
+      bool keep = true;
+      if constexpr (CLASSES) keep = a_cls[e] == c;
+      As[e * (kLinThreads / kLinTK) + tid / kLinTK][kk_a] = keep ? ra[e] : T(0);
+    }
 #pragma unroll
     for (int e = 0; e < kBElems; ++e) {
       const int idx = e * kLinThreads + tid;
       const int kk = TRANSW ? idx % kLinTK : idx / kLinTN;
       const int cc = TRANSW ? idx / kLinTK : idx % kLinTN;
-      Bs[kk][cc] = rb[e];
+      if constexpr (TRANSW)
+        Bs[cc][kk] = rb[e];
+      else
+        Bs[kk][cc] = rb[e];
     }
     __syncthreads();
     have = next(c, p, k0);
@@ -189,7 +230,10 @@ linear_kernel(const T* __restrict__ x, const T* __restrict__ w, const Index* __r
 #pragma unroll
       for (int i = 0; i < kMT; ++i) a[i] = As[wr * (kLinTM / 2) + i * 16 + lane % 16][kq];
 #pragma unroll
-      for (int j = 0; j < kNT; ++j) b[j] = Bs[kq][wc * (kLinTN / 2) + j * 16 + lane % 16];
+      for (int j = 0; j < kNT; ++j) {
+        const int col = wc * (kLinTN / 2) + j * 16 + lane % 16;
+        b[j] = TRANSW ? Bs[col][kq] : Bs[kq][col];
+      }
 #pragma unroll
       for (int i = 0; i < kMT; ++i)
 #pragma unroll
