@@ -273,16 +273,22 @@ tp_conv_split_kernel(const T* __restrict__ x, const T* __restrict__ sh, const T*
 #pragma unroll
   for (int k = 0; k < S::NK; ++k) red[g][k][ul] = acc[0][k];
   __syncthreads();
+  // the group sums, in group order, by the whole workgroup: thread (g, ul)
+  // adds up components k = g, g + EG, ... of channel ul into red[0][k][ul]
+  // (one thread per (k, ul), so the in-place write meets no other reader),
+  // instead of the first GW lanes doing all NK * EG reads in turn
+  for (int k = g; k < S::NK; k += EG) {
+    T t = red[0][k][ul];
+#pragma unroll
+    for (int q = 1; q < EG; ++q) t += red[q][k][ul];
+    red[0][k][ul] = t;
+  }
+  __syncthreads();
   if (threadIdx.x < GW && active) {
     const T scale = (mean && e1 > e0) ? T(1) / static_cast<T>(e1 - e0) : T(1);
     T v[1][S::NK];
 #pragma unroll
-    for (int k = 0; k < S::NK; ++k) {
-      T t = red[0][k][ul];
-#pragma unroll
-      for (int q = 1; q < EG; ++q) t += red[q][k][ul];
-      v[0][k] = mean ? t * scale : t;
-    }
+    for (int k = 0; k < S::NK; ++k) v[0][k] = mean ? red[0][k][ul] * scale : red[0][k][ul];
     S::template store_s<T, LAYOUT, 1, false>(out + node * (static_cast<int64_t>(mul) * S::NK), mul, ul, v);
   }
 }
