@@ -521,7 +521,9 @@ int fctp_bwd(fctp_handle h, const void* x1, const void* x2, const void* w, const
  *        the ranges); an edge whose source is out of range contributes
  *        nothing.
  *   out  [n_nodes, DIM_OUT] device, fully overwritten.
- * E_UNSUPPORTED also for input-1 blocks of more than 64 channels.
+ * Input-1 blocks of more than 64 channels are taken 64 channels at a time;
+ * E_UNSUPPORTED when one edge's staged rows (x components times channels,
+ * the harmonics, the coupled rows) exceed the 64 KB of LDS of one wave.
  */
 int fctp_conv_fwd(fctp_handle h, const void* x, int64_t n_src, const void* sh, const void* w, int64_t w_rows,
                   const void* src, const void* dst, int idx_dtype, int64_t n_edges, int64_t n_nodes, void* out,

@@ -109,14 +109,15 @@ struct segpoly_fctp {
   std::vector<FcvQK> cv_qks;
   std::vector<FcvEnt> cv_ents;
   std::vector<FcvTile> cv_tiles;
+  std::vector<FcvUT> cv_uts;
   std::vector<FcvQ> cv_qs;
   std::vector<FcvChunk> cv_chunks;
   std::vector<FcvBPath> cv_bpaths;    // backward: every path with its global rows
   std::string conv_bwd_error;         // why the backward is unavailable ("" if available)
   size_t cv_bwd_lds = 0;
-  int cv_ncomp = 0, cv_max_nqk = 0, cv_lane_bits = 0;
+  int cv_ncomp = 0, cv_max_nqk = 0, cv_lane_bits = 0, cv_n_ut = 1;
   size_t cv_lds = 0;
-  size_t cv_off[8] = {0, 0, 0, 0, 0, 0, 0, 0};  // blocks, paths, qks, ents, tiles, qs, chunks, bpaths in the blob
+  size_t cv_off[9] = {0, 0, 0, 0, 0, 0, 0, 0, 0};  // blocks, paths, qks, ents, tiles, qs, chunks, bpaths, uts in the blob
   std::vector<unsigned char> blob;
   std::map<int, DeviceBuffer> dev;
   std::mutex mu;
@@ -309,7 +310,8 @@ int build_dw(segpoly_fctp* h) {
 }
 
 // Tables of the convolution form: input 2 must be the edge harmonics (one
-// channel per block), input-1 blocks at most 64 channels.
+// channel per block).  Input-1 blocks of more than 64 channels are taken
+// 64 channels (one u tile) at a time.
 void build_conv(segpoly_fctp* h) {
   for (const auto& b : h->in2)
     if (b.mul != 1) {
@@ -318,10 +320,8 @@ void build_conv(segpoly_fctp* h) {
     }
   int mmax = 1;
   for (const auto& b : h->in1) mmax = std::max(mmax, b.mul);
-  if (mmax > 64) {
-    h->conv_error = "the convolution form supports at most 64 channels per input-1 block";
-    return;
-  }
+  const int n_ut = (mmax + kFcvUTile - 1) / kFcvUTile;
+  h->cv_n_ut = n_ut;
   int comp = 0;
   for (size_t i = 0; i < h->in1.size(); ++i) {
     const Irrep& b = h->in1[i];
@@ -359,18 +359,24 @@ void build_conv(segpoly_fctp* h) {
     }
     const int path_end = static_cast<int>(h->cv_paths.size());
     h->cv_max_nqk = std::max(h->cv_max_nqk, nqk);
-    // full 16-channel chunks of every path, and the remaining channels one by one
-    const int chunk_begin = static_cast<int>(h->cv_chunks.size());
-    const int q_begin = static_cast<int>(h->cv_qs.size());
-    for (int pi = path_begin; pi < path_end; ++pi) {
-      const FcvPath& P = h->cv_paths[pi];
-      int u = 0;
-      for (; u + kFcvChunkU <= P.m1; u += kFcvChunkU)
-        h->cv_chunks.push_back({P.w_off + static_cast<int64_t>(u) * ob.mul, P.qk, u});
-      for (; u < P.m1; ++u) h->cv_qs.push_back({P.w_off + static_cast<int64_t>(u) * ob.mul, P.qk, u});
+    // per u tile: the full 16-channel chunks of every path inside it, then
+    // the remaining channels one by one (u tiles start at multiples of 64,
+    // so chunks never straddle two)
+    const int ut_begin = static_cast<int>(h->cv_uts.size());
+    for (int ut = 0; ut < n_ut; ++ut) {
+      FcvUT U{static_cast<int>(h->cv_chunks.size()), 0, static_cast<int>(h->cv_qs.size()), 0};
+      for (int pi = path_begin; pi < path_end; ++pi) {
+        const FcvPath& P = h->cv_paths[pi];
+        const int lo = ut * kFcvUTile, hi = std::min(P.m1, lo + kFcvUTile);
+        int u = lo;
+        for (; u + kFcvChunkU <= hi; u += kFcvChunkU)
+          h->cv_chunks.push_back({P.w_off + static_cast<int64_t>(u) * ob.mul, P.qk, u});
+        for (; u < hi; ++u) h->cv_qs.push_back({P.w_off + static_cast<int64_t>(u) * ob.mul, P.qk, u});
+      }
+      U.n_chunks = static_cast<int>(h->cv_chunks.size()) - U.chunk_begin;
+      U.nq = static_cast<int>(h->cv_qs.size()) - U.q_begin;
+      h->cv_uts.push_back(U);
     }
-    const int n_chunks = static_cast<int>(h->cv_chunks.size()) - chunk_begin;
-    const int nq = static_cast<int>(h->cv_qs.size()) - q_begin;
     for (int pi = path_begin; pi < path_end; ++pi) {
       const FcvPath& P = h->cv_paths[pi];
       h->cv_bpaths.push_back({P.w_off, h->offo[o], P.m1, ob.mul, d3, qk_begin + P.qk});
@@ -381,14 +387,13 @@ void build_conv(segpoly_fctp* h) {
       t.d = d3, t.m = ob.mul, t.w0 = w0, t.nw = std::min(64, ob.mul - w0);
       t.path_begin = path_begin, t.path_end = path_end;
       t.qk_begin = qk_begin, t.nqk = nqk;
-      t.q_begin = q_begin, t.nq = nq;
-      t.chunk_begin = chunk_begin, t.n_chunks = n_chunks;
+      t.ut_begin = ut_begin;
       nwmax = std::max(nwmax, t.nw);
       h->cv_tiles.push_back(t);
     }
   }
   int lanes = 1;
-  while (lanes < std::max(mmax, nwmax)) lanes <<= 1;
+  while (lanes < std::max(std::min(mmax, kFcvUTile), nwmax)) lanes <<= 1;
   int bits = 0;
   while ((1 << bits) < lanes) ++bits;
   h->cv_lane_bits = bits;
@@ -574,6 +579,7 @@ int fctp_create(const char* irreps_in1, const char* irreps_in2, const char* irre
       h->cv_off[5] = append(h->blob, h->cv_qs);
       h->cv_off[6] = append(h->blob, h->cv_chunks);
       h->cv_off[7] = append(h->blob, h->cv_bpaths);
+      h->cv_off[8] = append(h->blob, h->cv_uts);
     }
   } catch (const std::bad_alloc&) {
     rc = fail(SEGPOLY_E_OOM, "out of host memory");
@@ -739,6 +745,8 @@ int fctp_conv_fwd(fctp_handle h, const void* x, int64_t n_src, const void* sh, c
   a.ncomp = h->cv_ncomp;
   a.max_nqk = h->cv_max_nqk;
   a.lane_bits = h->cv_lane_bits;
+  a.uts = reinterpret_cast<const FcvUT*>(db + h->cv_off[8]);
+  a.n_ut = h->cv_n_ut;
   a.lds_bytes = h->cv_lds;
   a.dtype = h->dtype, a.layout = h->layout, a.idx = idx_dtype;
   a.stream = stream;
@@ -823,6 +831,7 @@ int fctp_conv_bwd(fctp_handle h, const void* x, int64_t n_src, const void* sh, c
   a.nrows = static_cast<int>(h->cv_qks.size());
   a.ncomp = h->cv_ncomp;
   a.lane_bits = h->cv_lane_bits;
+  a.n_ut = h->cv_n_ut;
   a.lds_bytes = h->cv_bwd_lds;
   a.dtype = h->dtype, a.layout = h->layout, a.idx = idx_dtype;
   a.stream = stream;

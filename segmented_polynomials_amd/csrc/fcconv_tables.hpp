@@ -54,13 +54,24 @@ struct FcvChunk {
 constexpr int kFcvChunkU = 16;     // channels per chunk
 constexpr int kFcvBatch = 4;       // chunks whose weights a lane holds in registers at a time (half in double)
 
+// Input-1 channels are taken 64 at a time when a block has more than 64
+// (a "u tile"; one u tile otherwise): the weight elements of one output
+// block and one u tile, the full 16-channel chunks of its paths that lie in
+// the u tile and then the remaining (path, u) elements one by one.
+constexpr int kFcvUTile = 64;
+
+struct FcvUT {
+  int chunk_begin, n_chunks;       // full 16-channel chunks
+  int q_begin, nq;                 // the remaining (path, u) weight elements
+};
+
 struct FcvTile {
   int64_t out_off;                 // block offset in an output row
   int d, m, w0, nw;                // components, channels, channel range of the tile
   int path_begin, path_end;        // paths into the block
   int qk_begin, nqk;               // qk rows of the tile
-  int chunk_begin, n_chunks;       // full 16-channel chunks of its paths
-  int q_begin, nq;                 // the remaining (path, u) weight elements
+  int ut_begin;                    // its u tiles' weight elements (n_ut entries of FcvUT)
+  int pad;
 };
 
 // Backward: every path with its rows in the global list of coupled rows
@@ -94,6 +105,7 @@ struct FcvBwdArgs {
   const FcvEnt* ents;
   const FcvBPath* bpaths;
   int n_blocks, n_bpaths, nrows, ncomp, lane_bits;
+  int n_ut;                        // u tiles of kFcvUTile input channels (1 when no block has more)
   size_t lds_bytes;
   int dtype, layout, idx;
   void* stream;
@@ -117,9 +129,11 @@ struct FcvArgs {
   const FcvQK* qks;
   const FcvEnt* ents;
   const FcvTile* tiles;
+  const FcvUT* uts;
   const FcvQ* qs;
   const FcvChunk* chunks;
   int n_blocks, n_tiles;
+  int n_ut;                        // u tiles of kFcvUTile input channels (1 when no block has more)
   int ncomp;                       // staged x components per edge (sum of 2l + 1)
   int max_nqk;                     // qk rows of the largest tile
   int lane_bits;                   // log2 of the lanes per edge (channels rounded up to a power of two)

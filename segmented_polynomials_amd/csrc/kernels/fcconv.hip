@@ -44,30 +44,33 @@ __device__ __forceinline__ void wave_sync() {
 
 // The edge loop of one (destination, tile) for an output block of D
 // components (compile-time, so the component loops carry no run-time
-// guards).
+// guards).  With more than 64 input-1 channels each edge is taken one u tile
+// (64 channels, one edge per wave) at a time: stage that tile of x[src],
+// form its coupled rows, mix its weight elements.
 template <typename T, typename Index, int LAYOUT, int D>
 __device__ __forceinline__ void fcv_run(const T* __restrict__ x, const T* __restrict__ sh, const T* __restrict__ w,
                                         const Index* __restrict__ src, int64_t n_src, int64_t e0, int64_t e1,
                                         int64_t dim1, int64_t dim2, int64_t w_stride, const FcvTile& tile,
                                         const FcvBlock* __restrict__ blocks, const FcvQK* __restrict__ qks,
-                                        const FcvEnt* __restrict__ ents, const FcvQ* __restrict__ tq,
-                                        const FcvChunk* __restrict__ tc, int n_blocks, int M, int S, int slot, int c,
-                                        T* xs, T* shs, T* ys, T (&acc)[D]) {
+                                        const FcvEnt* __restrict__ ents, const FcvQ* __restrict__ qs,
+                                        const FcvChunk* __restrict__ chunks, const FcvUT* __restrict__ uts, int n_ut,
+                                        int n_blocks, int M, int S, int slot, int c, T* xs, T* shs, T* ys,
+                                        T (&acc)[D]) {
   constexpr int kB = sizeof(T) == 4 ? kFcvBatch : kFcvBatch / 2;  // chunks held in registers
   const bool wlane = c < tile.nw;
   auto source = [&](int64_t e) -> int64_t { return e < e1 ? static_cast<int64_t>(src[e]) : int64_t(-1); };
-  // A batch of weight chunks b0 .. b0 + kB - 1, branch-free: every load is
-  // issued before any is used (a guarded load per element made each chunk
-  // wait for the previous one).  A chunk past the tile's last re-reads its
-  // last chunk and is never used; a lane past the tile's channels reads
-  // channel 0; a slot past the edge range reads the range's first edge.
-  // Lanes whose edge has no valid source skip the mixing (their weights
-  // are not used at all).
+  // A batch of weight chunks b0 .. b0 + kB - 1 of u tile U, branch-free:
+  // every load is issued before any is used (a guarded load per element
+  // made each chunk wait for the previous one).  A chunk past the u tile's
+  // last re-reads its last chunk and is never used; a lane past the tile's
+  // channels reads channel 0; a slot past the edge range reads the range's
+  // first edge.  Lanes whose edge has no valid source skip the mixing
+  // (their weights are not used at all).
   T wr[kB][kFcvChunkU];
-  auto fetch_w = [&](int b0, const T* wl) {
+  auto fetch_w = [&](const FcvChunk* tc, int n_chunks, int b0, const T* wl) {
     int64_t off[kB];
 #pragma unroll
-    for (int i = 0; i < kB; ++i) off[i] = tc[b0 + i < tile.n_chunks ? b0 + i : tile.n_chunks - 1].off;
+    for (int i = 0; i < kB; ++i) off[i] = tc[b0 + i < n_chunks ? b0 + i : n_chunks - 1].off;
 #pragma unroll
     for (int i = 0; i < kB; ++i)
 #pragma unroll
@@ -80,57 +83,65 @@ __device__ __forceinline__ void fcv_run(const T* __restrict__ x, const T* __rest
     const bool ok = s >= 0 && s < n_src;
     const bool wok = ok && wlane;
     const T* wl = w + (e < e1 ? e : e0) * w_stride + tile.w0 + (wlane ? c : 0);
-    // the first batch of weight chunks, issued before anything waits on memory
-    if (tile.n_chunks > 0) fetch_w(0, wl);
     s_next = source(eb + S + slot);
-    // stage the slot's edge: x[src] (all input-1 blocks) and the harmonics
-    for (int bi = 0; bi < n_blocks; ++bi) {
-      const FcvBlock B = blocks[bi];
-      const bool on = ok && c < B.m;
-      for (int a = 0; a < B.d; ++a) {
-        const int64_t off = LAYOUT == kIrMul ? B.off + static_cast<int64_t>(a) * B.m + c : B.off + static_cast<int64_t>(c) * B.d + a;
-        xs[(B.comp + a) * M + c] = on ? x[s * dim1 + off] : T(0);
-      }
-    }
     for (int b = c; b < dim2; b += M) shs[b] = ok ? sh[e * dim2 + b] : T(0);
-    wave_sync();
-    // coupled rows, lane = input channel
-    for (int r = 0; r < tile.nqk; ++r) {
-      const FcvQK Q = qks[tile.qk_begin + r];
-      T t = T(0);
-      for (int en = Q.ent_begin; en < Q.ent_end; ++en) {
-        const FcvEnt E = ents[en];
-        t = fmadd(static_cast<T>(E.c) * shs[E.b], xs[E.a * M + c], t);
+    for (int ut = 0; ut < n_ut; ++ut) {
+      const FcvUT U = uts[tile.ut_begin + ut];
+      const FcvChunk* tc = chunks + U.chunk_begin;
+      const FcvQ* tq = qs + U.q_begin;
+      const int ub = ut * kFcvUTile;  // first channel of the u tile (0 with one u tile)
+      const int u = ub + c;           // this lane's input channel
+      // the first batch of weight chunks, issued before anything waits on memory
+      if (U.n_chunks > 0) fetch_w(tc, U.n_chunks, 0, wl);
+      // stage the slot's edge: x[src] (all input-1 blocks, this u tile)
+      for (int bi = 0; bi < n_blocks; ++bi) {
+        const FcvBlock B = blocks[bi];
+        const bool on = ok && u < B.m;
+        for (int a = 0; a < B.d; ++a) {
+          const int64_t off = LAYOUT == kIrMul ? B.off + static_cast<int64_t>(a) * B.m + u
+                                               : B.off + static_cast<int64_t>(u) * B.d + a;
+          xs[(B.comp + a) * M + c] = on ? x[s * dim1 + off] : T(0);
+        }
       }
-      ys[r * M + c] = t;
-    }
-    wave_sync();
-    // mixing, lane = output channel: acc[k] += W[u, w] y[qk + k, u]
-    for (int b0 = 0; b0 < tile.n_chunks; b0 += kB) {
-      if (b0 > 0) fetch_w(b0, wl);
-      if (wok) {
-#pragma unroll
-        for (int i = 0; i < kB; ++i)
-          if (b0 + i < tile.n_chunks) {
-            const FcvChunk C = tc[b0 + i];
-            const T* yq = ys + C.qk * M + C.u0;
-#pragma unroll
-            for (int uu = 0; uu < kFcvChunkU; ++uu)
-#pragma unroll
-              for (int k = 0; k < D; ++k) acc[k] = fmadd(wr[i][uu], yq[k * M + uu], acc[k]);
-          }
+      wave_sync();
+      // coupled rows, lane = input channel
+      for (int r = 0; r < tile.nqk; ++r) {
+        const FcvQK Q = qks[tile.qk_begin + r];
+        T t = T(0);
+        for (int en = Q.ent_begin; en < Q.ent_end; ++en) {
+          const FcvEnt E = ents[en];
+          t = fmadd(static_cast<T>(E.c) * shs[E.b], xs[E.a * M + c], t);
+        }
+        ys[r * M + c] = t;
       }
-    }
-    for (int q = 0; q < tile.nq; ++q) {  // channels past the last full chunk
-      const FcvQ Q = tq[q];
-      const T wv = wl[Q.off];
-      const T* yq = ys + Q.qk * M + Q.u;
-      if (wok) {
+      wave_sync();
+      // mixing, lane = output channel: acc[k] += W[u, w] y[qk + k, u]
+      for (int b0 = 0; b0 < U.n_chunks; b0 += kB) {
+        if (b0 > 0) fetch_w(tc, U.n_chunks, b0, wl);
+        if (wok) {
 #pragma unroll
-        for (int k = 0; k < D; ++k) acc[k] = fmadd(wv, yq[k * M], acc[k]);
+          for (int i = 0; i < kB; ++i)
+            if (b0 + i < U.n_chunks) {
+              const FcvChunk C = tc[b0 + i];
+              const T* yq = ys + C.qk * M + (C.u0 - ub);
+#pragma unroll
+              for (int uu = 0; uu < kFcvChunkU; ++uu)
+#pragma unroll
+                for (int k = 0; k < D; ++k) acc[k] = fmadd(wr[i][uu], yq[k * M + uu], acc[k]);
+            }
+        }
       }
+      for (int q = 0; q < U.nq; ++q) {  // channels past the last full chunk
+        const FcvQ Q = tq[q];
+        const T wv = wl[Q.off];
+        const T* yq = ys + Q.qk * M + (Q.u - ub);
+        if (wok) {
+#pragma unroll
+          for (int k = 0; k < D; ++k) acc[k] = fmadd(wv, yq[k * M], acc[k]);
+        }
+      }
+      wave_sync();
     }
-    wave_sync();
   }
 }
 
@@ -164,7 +175,7 @@ fcconv_kernel(const T* __restrict__ x, const T* __restrict__ sh, const T* __rest
               int64_t dim1, int64_t dim2, int64_t dimo, int64_t w_stride, int mean, T* __restrict__ out,
               const FcvBlock* __restrict__ blocks, const FcvQK* __restrict__ qks, const FcvEnt* __restrict__ ents,
               const FcvTile* __restrict__ tiles, const FcvQ* __restrict__ qs, const FcvChunk* __restrict__ chunks,
-              int n_blocks, int ncomp, int max_nqk, int lane_bits) {
+              const FcvUT* __restrict__ uts, int n_ut, int n_blocks, int ncomp, int max_nqk, int lane_bits) {
   extern __shared__ __align__(16) unsigned char fcv_smem[];
   T* lds = reinterpret_cast<T*>(fcv_smem);
   const int64_t node = blockIdx.x;
@@ -178,8 +189,6 @@ fcconv_kernel(const T* __restrict__ x, const T* __restrict__ sh, const T* __rest
   T* xs = lds + slot * XS;
   T* shs = lds + S * XS + slot * SH;
   T* ys = lds + S * (XS + SH) + slot * YS;
-  const FcvQ* tq = qs + tile.q_begin;
-  const FcvChunk* tc = chunks + tile.chunk_begin;
 
   int64_t e0, e1;
   edge_range(dst, n_edges, 0, node, e0, e1);
@@ -189,8 +198,8 @@ fcconv_kernel(const T* __restrict__ x, const T* __restrict__ sh, const T* __rest
   case DD: {                                                                                                    \
     T acc[DD];                                                                                                  \
     for (int k = 0; k < DD; ++k) acc[k] = T(0);                                                                 \
-    fcv_run<T, Index, LAYOUT, DD>(x, sh, w, src, n_src, e0, e1, dim1, dim2, w_stride, tile, blocks, qks, ents, tq, \
-                                  tc, n_blocks, M, S, slot, c, xs, shs, ys, acc);                                \
+    fcv_run<T, Index, LAYOUT, DD>(x, sh, w, src, n_src, e0, e1, dim1, dim2, w_stride, tile, blocks, qks, ents, qs, \
+                                  chunks, uts, n_ut, n_blocks, M, S, slot, c, xs, shs, ys, acc);                 \
     fcv_store<T, LAYOUT, DD>(acc, tile, out, node, dimo, M, slot, c, scale);                                    \
     break;                                                                                                      \
   }
@@ -215,7 +224,8 @@ int fcconv_launch(const FcvArgs& a) {
                      static_cast<hipStream_t>(a.stream), static_cast<const T*>(a.x), static_cast<const T*>(a.sh),
                      static_cast<const T*>(a.w), static_cast<const Index*>(a.src), static_cast<const Index*>(a.dst),
                      a.n_src, a.n_edges, a.dim1, a.dim2, a.dimo, a.w_stride, a.mean, static_cast<T*>(a.out),
-                     a.blocks, a.qks, a.ents, a.tiles, a.qs, a.chunks, a.n_blocks, a.ncomp, a.max_nqk, a.lane_bits);
+                     a.blocks, a.qks, a.ents, a.tiles, a.qs, a.chunks, a.uts, a.n_ut, a.n_blocks, a.ncomp, a.max_nqk,
+                     a.lane_bits);
   return static_cast<int>(hipGetLastError());
 }
 

@@ -34,14 +34,16 @@ __device__ __forceinline__ void fcb_wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// One path of one edge, for an output block of D components:
+// One path of one edge and one u tile (input channels ub .. ub + M - 1), for
+// an output block of D components:
 //   z[row + k, u] = sum_w W[u, w] G[k, w]     (lane = input channel u, the
 //                                            weight row read once, 16 channels at a time)
 //   dW[u, w]      = sum_k y[row + k, u] G[k, w] (lane = output channel w, G[., w] in registers)
-template <typename T, int LAYOUT, int D, bool SHW>
+template <typename T, int LAYOUT, int D, bool SHW, bool WIDE>
 __device__ __forceinline__ void fcb_path(const FcvBPath& P, const T* __restrict__ w, int64_t e, int64_t numel,
-                                         bool valid, int M, int c, const T* Gs, const T* ys, T* zs,
+                                         bool valid, int M, int c, int ub_, const T* Gs, const T* ys, T* zs,
                                          T* __restrict__ dw) {
+  const int ub = WIDE ? ub_ : 0;  // one u tile: every channel of the path is a lane
   auto gi = [&](int k, int wc) -> int {
     return static_cast<int>(P.g_off) + (LAYOUT == kIrMul ? k * P.m3 + wc : wc * D + k);
   };
@@ -49,8 +51,8 @@ __device__ __forceinline__ void fcb_path(const FcvBPath& P, const T* __restrict_
     T z[D];
 #pragma unroll
     for (int k = 0; k < D; ++k) z[k] = T(0);
-    if (valid && c < P.m1) {
-      const T* wr = w + (SHW ? 0 : e * numel) + P.w_off + static_cast<int64_t>(c) * P.m3;
+    if (valid && ub + c < P.m1) {
+      const T* wr = w + (SHW ? 0 : e * numel) + P.w_off + static_cast<int64_t>(ub + c) * P.m3;
       int w0 = 0;
       // 16-byte vector loads where the row is aligned (it is whenever m3
       // is a multiple of 16 / sizeof(T) channels), else plain loads
@@ -90,9 +92,10 @@ __device__ __forceinline__ void fcb_path(const FcvBPath& P, const T* __restrict_
 #pragma unroll
       for (int k = 0; k < D; ++k) gk[k] = Gs[gi(k, wc)];
       T* dwr = dw + e * numel + P.w_off + wc;
-      const T* yr = ys + P.row * M;
+      const T* yr = ys + P.row * M - ub;
+      const int u1 = WIDE && ub + M < P.m1 ? ub + M : P.m1;
 #pragma unroll 4
-      for (int u = 0; u < P.m1; ++u) {
+      for (int u = ub; u < u1; ++u) {
         T t = T(0);
 #pragma unroll
         for (int k = 0; k < D; ++k) t = fmadd(yr[k * M + u], gk[k], t);
@@ -102,7 +105,10 @@ __device__ __forceinline__ void fcb_path(const FcvBPath& P, const T* __restrict_
 }
 
 // SHW: one weight row shared by every edge (the dw rows stay per edge).
-template <typename T, typename Index, int LAYOUT, bool SHW>
+// WIDE: input-1 blocks of more than 64 channels, taken a u tile at a time
+// (a separate instance: the u-tile loop costs the one-tile case registers,
+// 167 -> 237 VGPRs for float ir_mul, and a wave per SIMD).
+template <typename T, typename Index, int LAYOUT, bool SHW, bool WIDE>
 __global__ void __launch_bounds__(64)
 fcconv_bwd_edge_kernel(const T* __restrict__ x, const T* __restrict__ sh, const T* __restrict__ w,
                        const T* __restrict__ g, const Index* __restrict__ src, const Index* __restrict__ dst,
@@ -110,7 +116,7 @@ fcconv_bwd_edge_kernel(const T* __restrict__ x, const T* __restrict__ sh, const 
                        int64_t numel, int mean, T* __restrict__ dsh, T* __restrict__ dw, T* __restrict__ msg,
                        const FcvBlock* __restrict__ blocks, const FcvQK* __restrict__ qks,
                        const FcvEnt* __restrict__ ents, const FcvBPath* __restrict__ bpaths, int n_blocks,
-                       int n_bpaths, int nrows, int ncomp, int lane_bits) {
+                       int n_bpaths, int nrows, int ncomp, int lane_bits, int n_ut) {
   extern __shared__ __align__(16) unsigned char fcb_smem[];
   T* lds = reinterpret_cast<T*>(fcb_smem);
   const int64_t node = blockIdx.x;
@@ -154,65 +160,77 @@ fcconv_bwd_edge_kernel(const T* __restrict__ x, const T* __restrict__ sh, const 
     const bool valid = e < e1;
     const int64_t s = valid ? static_cast<int64_t>(src[e]) : int64_t(-1);
     const bool ok = s >= 0 && s < n_src;
-    // stage x[src] (zero for an out-of-range source) and the harmonics
-    for (int bi = 0; bi < n_blocks; ++bi) {
-      const FcvBlock B = blocks[bi];
-      const bool on = ok && c < B.m;
-      for (int a = 0; a < B.d; ++a) {
-        const int64_t off = LAYOUT == kIrMul ? B.off + static_cast<int64_t>(a) * B.m + c : B.off + static_cast<int64_t>(c) * B.d + a;
-        xs[(B.comp + a) * M + c] = on ? x[s * dim1 + off] : T(0);
-        ms[(B.comp + a) * M + c] = T(0);
-      }
-    }
-    for (int b = c; b < dim2; b += M) shs[b] = valid ? sh[e * dim2 + b] : T(0);
-    for (int b = 0; b < dim2; ++b) hp[b * M + c] = T(0);
-    fcb_wave_sync();
-    // coupled rows y (lane = input channel)
-    for (int r = 0; r < nrows; ++r) {
-      const FcvQK Q = qks[r];
-      T t = T(0);
-      for (int en = Q.ent_begin; en < Q.ent_end; ++en) {
-        const FcvEnt E = ents[en];
-        t = fmadd(static_cast<T>(E.c) * shs[E.b], xs[E.a * M + c], t);
-      }
-      ys[r * M + c] = t;
-    }
-    fcb_wave_sync();
-    // per path: z rows (lane = input channel) and dW (lane = output channel)
-    for (int pi = 0; pi < n_bpaths; ++pi) {
-      const FcvBPath P = bpaths[pi];
-      switch (P.d3) {
-        case 1: fcb_path<T, LAYOUT, 1, SHW>(P, w, e, numel, valid, M, c, Gs, ys, zs, dw); break;
-        case 3: fcb_path<T, LAYOUT, 3, SHW>(P, w, e, numel, valid, M, c, Gs, ys, zs, dw); break;
-        case 5: fcb_path<T, LAYOUT, 5, SHW>(P, w, e, numel, valid, M, c, Gs, ys, zs, dw); break;
-        case 7: fcb_path<T, LAYOUT, 7, SHW>(P, w, e, numel, valid, M, c, Gs, ys, zs, dw); break;
-        case 9: fcb_path<T, LAYOUT, 9, SHW>(P, w, e, numel, valid, M, c, Gs, ys, zs, dw); break;
-        case 11: fcb_path<T, LAYOUT, 11, SHW>(P, w, e, numel, valid, M, c, Gs, ys, zs, dw); break;
-        default: fcb_path<T, LAYOUT, 13, SHW>(P, w, e, numel, valid, M, c, Gs, ys, zs, dw); break;
-      }
-    }
-    // messages and harmonic-gradient partials (lane = input channel)
-    for (int r = 0; r < nrows; ++r) {
-      const FcvQK Q = qks[r];
-      const T zv = zs[r * M + c];
-      for (int en = Q.ent_begin; en < Q.ent_end; ++en) {
-        const FcvEnt E = ents[en];
-        const T cz = static_cast<T>(E.c) * zv;
-        ms[E.a * M + c] = fmadd(cz, shs[E.b], ms[E.a * M + c]);
-        hp[E.b * M + c] = fmadd(cz, xs[E.a * M + c], hp[E.b * M + c]);
-      }
-    }
-    if (valid) {
+    // one u tile (input channels ub .. ub + M - 1) at a time; one tile when
+    // no block has more than 64 channels
+    const int nut = WIDE ? n_ut : 1;
+    for (int ut = 0; ut < nut; ++ut) {
+      const int ub = ut * kFcvUTile;
+      const int u = ub + c;  // this lane's input channel
+      // stage x[src] (zero for an out-of-range source)
       for (int bi = 0; bi < n_blocks; ++bi) {
         const FcvBlock B = blocks[bi];
-        if (c < B.m)
-          for (int a = 0; a < B.d; ++a) {
-            const int64_t off = LAYOUT == kIrMul ? B.off + static_cast<int64_t>(a) * B.m + c : B.off + static_cast<int64_t>(c) * B.d + a;
-            msg[e * dim1 + off] = ms[(B.comp + a) * M + c];
-          }
+        const bool on = ok && u < B.m;
+        for (int a = 0; a < B.d; ++a) {
+          const int64_t off = LAYOUT == kIrMul ? B.off + static_cast<int64_t>(a) * B.m + u
+                                               : B.off + static_cast<int64_t>(u) * B.d + a;
+          xs[(B.comp + a) * M + c] = on ? x[s * dim1 + off] : T(0);
+          ms[(B.comp + a) * M + c] = T(0);
+        }
       }
+      if (ut == 0) {  // the harmonics, and the harmonic-gradient partials every u tile adds to
+        for (int b = c; b < dim2; b += M) shs[b] = valid ? sh[e * dim2 + b] : T(0);
+        for (int b = 0; b < dim2; ++b) hp[b * M + c] = T(0);
+      }
+      fcb_wave_sync();
+      // coupled rows y (lane = input channel)
+      for (int r = 0; r < nrows; ++r) {
+        const FcvQK Q = qks[r];
+        T t = T(0);
+        for (int en = Q.ent_begin; en < Q.ent_end; ++en) {
+          const FcvEnt E = ents[en];
+          t = fmadd(static_cast<T>(E.c) * shs[E.b], xs[E.a * M + c], t);
+        }
+        ys[r * M + c] = t;
+      }
+      fcb_wave_sync();
+      // per path: z rows (lane = input channel) and dW (lane = output channel)
+      for (int pi = 0; pi < n_bpaths; ++pi) {
+        const FcvBPath P = bpaths[pi];
+        switch (P.d3) {
+          case 1: fcb_path<T, LAYOUT, 1, SHW, WIDE>(P, w, e, numel, valid, M, c, ub, Gs, ys, zs, dw); break;
+          case 3: fcb_path<T, LAYOUT, 3, SHW, WIDE>(P, w, e, numel, valid, M, c, ub, Gs, ys, zs, dw); break;
+          case 5: fcb_path<T, LAYOUT, 5, SHW, WIDE>(P, w, e, numel, valid, M, c, ub, Gs, ys, zs, dw); break;
+          case 7: fcb_path<T, LAYOUT, 7, SHW, WIDE>(P, w, e, numel, valid, M, c, ub, Gs, ys, zs, dw); break;
+          case 9: fcb_path<T, LAYOUT, 9, SHW, WIDE>(P, w, e, numel, valid, M, c, ub, Gs, ys, zs, dw); break;
+          case 11: fcb_path<T, LAYOUT, 11, SHW, WIDE>(P, w, e, numel, valid, M, c, ub, Gs, ys, zs, dw); break;
+          default: fcb_path<T, LAYOUT, 13, SHW, WIDE>(P, w, e, numel, valid, M, c, ub, Gs, ys, zs, dw); break;
+        }
+      }
+      // messages and harmonic-gradient partials (lane = input channel)
+      for (int r = 0; r < nrows; ++r) {
+        const FcvQK Q = qks[r];
+        const T zv = zs[r * M + c];
+        for (int en = Q.ent_begin; en < Q.ent_end; ++en) {
+          const FcvEnt E = ents[en];
+          const T cz = static_cast<T>(E.c) * zv;
+          ms[E.a * M + c] = fmadd(cz, shs[E.b], ms[E.a * M + c]);
+          hp[E.b * M + c] = fmadd(cz, xs[E.a * M + c], hp[E.b * M + c]);
+        }
+      }
+      if (valid) {
+        for (int bi = 0; bi < n_blocks; ++bi) {
+          const FcvBlock B = blocks[bi];
+          if (u < B.m)
+            for (int a = 0; a < B.d; ++a) {
+              const int64_t off = LAYOUT == kIrMul ? B.off + static_cast<int64_t>(a) * B.m + u
+                                                   : B.off + static_cast<int64_t>(u) * B.d + a;
+              msg[e * dim1 + off] = ms[(B.comp + a) * M + c];
+            }
+        }
+      }
+      fcb_wave_sync();
     }
-    // dsh[e, b] = sum over the slot's lanes of hp[b]
+    // dsh[e, b] = sum over the slot's lanes of hp[b] (every u tile added in)
     for (int b = 0; b < dim2; ++b) {
       T v = hp[b * M + c];
       for (int dd = 1; dd < M; dd <<= 1) v += __shfl_xor(v, dd);
@@ -244,12 +262,21 @@ fcconv_bwd_src_kernel(const Index* __restrict__ src, const Index* __restrict__ p
 
 template <typename T, typename Index, int LAYOUT, bool SHW>
 void fcconv_bwd_edges(const FcvBwdArgs& a, T* dwe, hipStream_t st) {
-  hipLaunchKernelGGL((fcconv_bwd_edge_kernel<T, Index, LAYOUT, SHW>), dim3(static_cast<unsigned>(a.n_nodes)), dim3(64),
+  if (a.n_ut > 1) {
+    hipLaunchKernelGGL((fcconv_bwd_edge_kernel<T, Index, LAYOUT, SHW, true>), dim3(static_cast<unsigned>(a.n_nodes)),
+                       dim3(64), a.lds_bytes, st, static_cast<const T*>(a.x), static_cast<const T*>(a.sh),
+                       static_cast<const T*>(a.w), static_cast<const T*>(a.g), static_cast<const Index*>(a.src),
+                       static_cast<const Index*>(a.dst), a.n_src, a.n_edges, a.n_nodes, a.dim1, a.dim2, a.dimo,
+                       a.numel, a.mean, static_cast<T*>(a.dsh), dwe, static_cast<T*>(a.msg), a.blocks, a.qks,
+                       a.ents, a.bpaths, a.n_blocks, a.n_bpaths, a.nrows, a.ncomp, a.lane_bits, a.n_ut);
+    return;
+  }
+  hipLaunchKernelGGL((fcconv_bwd_edge_kernel<T, Index, LAYOUT, SHW, false>), dim3(static_cast<unsigned>(a.n_nodes)), dim3(64),
                      a.lds_bytes, st, static_cast<const T*>(a.x), static_cast<const T*>(a.sh),
                      static_cast<const T*>(a.w), static_cast<const T*>(a.g), static_cast<const Index*>(a.src),
                      static_cast<const Index*>(a.dst), a.n_src, a.n_edges, a.n_nodes, a.dim1, a.dim2, a.dimo,
                      a.numel, a.mean, static_cast<T*>(a.dsh), dwe, static_cast<T*>(a.msg), a.blocks, a.qks, a.ents,
-                     a.bpaths, a.n_blocks, a.n_bpaths, a.nrows, a.ncomp, a.lane_bits);
+                     a.bpaths, a.n_blocks, a.n_bpaths, a.nrows, a.ncomp, a.lane_bits, a.n_ut);
 }
 
 template <typename T, typename Index, int LAYOUT>

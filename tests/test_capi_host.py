@@ -398,8 +398,8 @@ def test_fctp_errors_and_workspace():
     assert cv(hc._h, p, 4, p, p, 3, p, p, 0, 3, 2, None, None) == sp.E_INVALID        # null out
     assert cv(hc._h, p, -4, p, p, 3, p, p, 0, 3, 2, p, None) == sp.E_INVALID
     assert cv(hc._h, None, 0, None, None, 1, None, None, 0, 0, 0, None, None) == sp.OK  # nothing to do
-    wide = sp.fctp_create("80x0e", "0e", "8x0e")
-    assert cv(wide._h, p, 4, p, p, 1, p, p, 0, 3, 2, p, None) == sp.E_UNSUPPORTED     # > 64 channels
+    wide = sp.fctp_create("80x0e", "0e", "8x0e")                                     # > 64 channels:
+    assert cv(wide._h, p, 4, p, p, 1, p, p, 0, 3, 2, None, None) == sp.E_INVALID     # accepted (null out)
     assert c(b"2x0e", b"2x0e", b"2x0e", 0, 0, 8 | 16, ctypes.byref(raw)) == sp.E_INVALID  # unknown flag
     # its backward: workspace of the per-edge messages, plus per-edge weight
     # gradients and their partial sums per 1024 edges with one shared row

@@ -61,6 +61,10 @@ CASES = [
     ("5x0e+3x1o+2x2e", "0e+1o+2e", "4x0e+3x1o+2x1e+1x2e", 90, 9, 60),
     ("64x0e+40x1o", "0e+1o", "80x0e+24x1o", 40, 7, 45),
     ("8x0e+8x1o+8x2e", "0e+1o+2e", "8x0e+8x1o+8x2e+4x2o", 60, 10, 60),
+    # more than 64 input channels (two u tiles of 64: full chunks in both,
+    # and 100 / 70 channels: chunks then single channels in the second)
+    ("128x0e+80x1o", "0e+1o", "24x0e+16x1o", 30, 6, 35),
+    ("100x0e+70x1o+3x2e", "0e+1o+2e", "12x0e+8x1o+4x2e", 25, 5, 30),
 ]
 
 
