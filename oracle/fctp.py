@@ -82,19 +82,28 @@ class FullyConnectedTP:
         return w[0, off:off + m1 * m2 * m3].reshape(m1, m2, m3)
 
     def fwd(self, x1, x2, w, layout="mul_ir", absolute=False):
-        """x1 [n, dim_in1], x2 [n, dim_in2] in ``layout``; w [1, weight_numel].
-        Returns float64 [n, dim_out].  ``absolute`` takes |x1|, |x2|, |w|, |C|."""
+        """x1 [n, dim_in1], x2 [n, dim_in2] in ``layout``; w [1, weight_numel]
+        (shared), or [n, weight_numel] with n > 1: one row per sample (the
+        skill document's external weights with shared_weights=False,
+        "distinct weights per item", "Layouts and weights").  Returns float64
+        [n, dim_out].  ``absolute`` takes |x1|, |x2|, |w|, |C|."""
         x1, x2, w = (np.asarray(a, dtype=np.float64) for a in (x1, x2, w))
         if absolute:
             x1, x2, w = np.abs(x1), np.abs(x2), np.abs(w)
         a = split_blocks(x1, self.in1, layout)
         b = split_blocks(x2, self.in2, layout)
         n = x1.shape[0]
+        per = n > 1 and w.shape[0] == n
         ob = [np.zeros((n, 2 * l + 1, m)) for m, l, _ in self.out]
-        for p, (i, j, o, _) in enumerate(self.paths):
+        for p, (i, j, o, off) in enumerate(self.paths):
             c = real_cg(self.in1[i][1], self.in2[j][1], self.out[o][1])
             if absolute:
                 c = np.abs(c)
+            if per:
+                m1, m2, m3 = self.in1[i][0], self.in2[j][0], self.out[o][0]
+                W = w[:, off:off + m1 * m2 * m3].reshape(n, m1, m2, m3)
+                ob[o] += self.alpha[o] * np.einsum("abk,nau,nbv,nuvw->nkw", c, a[i], b[j], W, optimize=True)
+                continue
             W = self._segment(w, p)
             ob[o] += self.alpha[o] * np.einsum("abk,nau,nbv,uvw->nkw", c, a[i], b[j], W, optimize=True)
         return join_blocks(ob, layout)

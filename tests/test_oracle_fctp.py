@@ -291,3 +291,36 @@ def test_conv_vjp_adjoint_identities(reduce):
     r1, r2, rw = f.conv_vjp(x1, x2, w, src, dst, 5, g, reduce=reduce)
     for r, a in ((r1, a1), (r2, a2), (rw, aw)):
         assert np.all(np.abs(r) <= a + 1e-12)
+
+
+@pytest.mark.parametrize("lay", ["mul_ir", "ir_mul"])
+def test_per_sample_weights(lay):
+    """One weight row per sample: each sample is the shared-row product with
+    its own row (sample by sample), the same as the convolution form on the
+    identity graph; a per-sample weight matrix with equal rows is the shared
+    product; the product is linear in the rows, and the VJP's per-sample dw
+    (vjp with edge_weights) is its adjoint."""
+    f = fctp.FullyConnectedTP("3x0e+2x1o", "2x0e+1x1o", "2x0e+3x1o+1x1e")
+    rng = np.random.default_rng(21)
+    n = 6
+    x1 = rng.normal(size=(n, f.dim_in1))
+    x2 = rng.normal(size=(n, f.dim_in2))
+    w = rng.normal(size=(n, f.weight_numel))
+    got = f.fwd(x1, x2, w, layout=lay)
+    for s in range(n):
+        assert np.allclose(got[s], f.fwd(x1[s:s + 1], x2[s:s + 1], w[s:s + 1], layout=lay)[0], atol=1e-12)
+    idx = np.arange(n)
+    assert np.allclose(got, f.conv(x1, x2, w, idx, idx, n, layout=lay), atol=1e-12)
+    assert np.allclose(f.fwd(x1, x2, np.repeat(w[:1], n, axis=0), layout=lay), f.fwd(x1, x2, w[:1], layout=lay),
+                       atol=1e-12)
+    g = rng.normal(size=(n, f.dim_out))
+    dx1, dx2, dw = f.vjp(x1, x2, None, g, layout=lay, edge_weights=w)
+    assert dw.shape == w.shape
+    v = rng.normal(size=w.shape)
+    assert np.isclose(np.sum(g * f.fwd(x1, x2, v, layout=lay)), np.sum(dw * v), rtol=1e-11)
+    v1 = rng.normal(size=x1.shape)
+    assert np.isclose(np.sum(g * f.fwd(v1, x2, w, layout=lay)), np.sum(dx1 * v1), rtol=1e-11)
+    v2 = rng.normal(size=x2.shape)
+    assert np.isclose(np.sum(g * f.fwd(x1, v2, w, layout=lay)), np.sum(dx2 * v2), rtol=1e-11)
+    assert np.all(np.abs(got) <= f.fwd(x1, x2, w, layout=lay, absolute=True) + 1e-12)
+
