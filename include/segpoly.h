@@ -504,6 +504,36 @@ int fctp_bwd(fctp_handle h, const void* x1, const void* x2, const void* w, const
              void* grad_x1, void* grad_x2, void* grad_w, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * fctp_fwd_per_sample: the product with one weight row per sample (external
+ * per-item weights: "cuequivariance-torch" skill document, "Layouts and
+ * weights", shared_weights=False with a [batch, weight_numel] operand):
+ *   out[s] = fctp(x1[s], x2[s]; w[s]) for s < n.
+ *   x1 [n, DIM_IN1], x2 [n, DIM_IN2], w [n, WEIGHT_NUMEL], out [n, DIM_OUT]:
+ *   device, row-major, layout and dtype of the handle; out fully overwritten.
+ * Each weight row is read once (the product streams the weights).  No
+ * workspace.  E_UNSUPPORTED when one sample's staged rows (x1, x2 and 64
+ * coupled values per output component) exceed 64 KB of LDS, when a weight
+ * row is 2 GiB or more, or n exceeds one launch's grid.
+ */
+int fctp_fwd_per_sample(fctp_handle h, const void* x1, const void* x2, const void* w, int64_t n, void* out,
+                        void* stream);
+
+/*
+ * fctp_bwd_per_sample: vector-Jacobian product of fctp_fwd_per_sample for
+ * g = dL/d(out) [n, DIM_OUT]:
+ *   grad_x1 [n, DIM_IN1], grad_x2 [n, DIM_IN2], grad_w [n, WEIGHT_NUMEL]
+ * (one gradient row per sample, no sum over the samples), each fully
+ * overwritten, or NULL (not computed).  Every sum is taken in a fixed order
+ * (deterministic).  No workspace.  Inputs a requested gradient does not
+ * read may be NULL (grad_x1 reads x2, g, w; grad_x2 reads x1, g, w; grad_w
+ * reads x1, x2, g).  E_UNSUPPORTED as fctp_fwd_per_sample, the LDS holding
+ * also the two input-gradient rows and 64 weight-contracted values per
+ * output component.
+ */
+int fctp_bwd_per_sample(fctp_handle h, const void* x1, const void* x2, const void* w, const void* grad_out,
+                        int64_t n, void* grad_x1, void* grad_x2, void* grad_w, void* stream);
+
+/*
  * fctp_conv_fwd: the product as a graph convolution with per-edge weights
  * ("cuequivariance-torch" skill document, "Other operations and layers":
  * FullyConnectedTensorProductConv, whose edge MLP gives one weight row per

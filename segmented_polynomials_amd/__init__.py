@@ -36,7 +36,7 @@ EXPORTS = ("tp_create", "tp_query", "tp_irreps_out", "tp_path_info", "tp_path_cg
            "tp_conv_fwd", "tp_conv_fwd_vec", "tp_conv_bwd_workspace", "tp_conv_bwd", "tp_destroy", "symcon_create", "symcon_query", "symcon_coupling_info",
            "symcon_coupling_dense", "symcon_fwd", "symcon_bwd_workspace", "symcon_bwd", "symcon_bwd_noalloc", "symcon_destroy", "linear_create", "linear_query", "linear_fwd",
            "linear_bwd_workspace", "linear_bwd", "linear_destroy", "fctp_create", "fctp_query", "fctp_path_info",
-           "fctp_fwd", "fctp_bwd_workspace", "fctp_bwd", "fctp_conv_fwd", "fctp_conv_bwd_workspace", "fctp_conv_bwd", "fctp_destroy", "edge_scalars_fwd", "edge_scalars_bwd", "sh_fwd", "sh_bwd", "segpoly_real_cg",
+           "fctp_fwd", "fctp_bwd_workspace", "fctp_bwd", "fctp_fwd_per_sample", "fctp_bwd_per_sample", "fctp_conv_fwd", "fctp_conv_bwd_workspace", "fctp_conv_bwd", "fctp_destroy", "edge_scalars_fwd", "edge_scalars_bwd", "sh_fwd", "sh_bwd", "segpoly_real_cg",
            "segpoly_last_error", "segpoly_version")
 
 
@@ -104,6 +104,8 @@ def _load():
         "fctp_fwd": [vp, vp, vp, vp, i64, vp, vp],
         "fctp_bwd_workspace": [vp, i64, ctypes.POINTER(ctypes.c_size_t)],
         "fctp_bwd": [vp, vp, vp, vp, vp, i64, vp, vp, vp, vp, ctypes.c_size_t, vp],
+        "fctp_fwd_per_sample": [vp, vp, vp, vp, i64, vp, vp],
+        "fctp_bwd_per_sample": [vp, vp, vp, vp, vp, i64, vp, vp, vp, vp],
         "fctp_conv_fwd": [vp, vp, i64, vp, vp, i64, vp, vp, c_int, i64, i64, vp, vp],
         "fctp_conv_bwd_workspace": [vp, i64, i64, ctypes.POINTER(ctypes.c_size_t)],
         "fctp_conv_bwd": [vp, vp, i64, vp, vp, i64, vp, vp, vp, c_int, i64, i64, vp, vp, vp, vp, vp,
@@ -628,37 +630,79 @@ def fctp_create(irreps_in1, irreps_in2, irreps_out, layout="mul_ir", dtype="f32"
     return FctpHandle(raw, layout, dtype)
 
 
-def _fc_check(h, **tensors):
+def _fc_check(h, per_sample=None, **tensors):
+    """Checks the operands; returns (dtype, n, per_sample).  Weights are one
+    shared row [1, weight_numel] or one row per sample [n, weight_numel]
+    (n > 1); ``per_sample`` True or False insists on one of the two."""
     t = _torch_dtype(h.dtype)
     n = None
     widths = {"x1": h.dim_in1, "x2": h.dim_in2, "grad_out": h.dim_out}
+    w = None
     for name, a in tensors.items():
         if a is None:
             continue
         if a.dtype != t or not a.is_cuda or not a.is_contiguous() or a.dim() != 2:
             raise ValueError(f"{name} must be a contiguous 2-d {t} device tensor")
         if name == "w":
-            if a.shape != (1, h.weight_numel):
-                raise ValueError("weights are one shared row [1, weight_numel]")
+            w = a
             continue
         if a.shape[1] != widths[name]:
             raise ValueError(f"{name} width does not match the descriptor")
         if n is not None and a.shape[0] != n:
             raise ValueError("operands have different sample counts")
         n = a.shape[0]
-    return t, n
+    per = bool(per_sample)
+    if w is not None:
+        if w.shape[1] != h.weight_numel:
+            raise ValueError("weight width does not match the descriptor")
+        if per_sample is None:
+            per = w.shape[0] != 1
+        if per and n is not None and w.shape[0] != n:
+            raise ValueError("per-sample weights need one row per sample [n, weight_numel]")
+        if not per and w.shape[0] != 1:
+            raise ValueError("shared weights are one row [1, weight_numel]")
+    return t, n, per
 
 
 def fctp_fwd(h, x1, x2, w, out=None):
-    """out [n, dim_out] for x1 [n, dim_in1], x2 [n, dim_in2], w [1, weight_numel]."""
+    """out [n, dim_out] for x1 [n, dim_in1], x2 [n, dim_in2] and w: one
+    shared row [1, weight_numel] (matrix-core kernels), or one row per sample
+    [n, weight_numel] with n > 1 (the per-sample kernel)."""
     import torch
-    t, n = _fc_check(h, x1=x1, x2=x2, w=w)
+    t, n, per = _fc_check(h, x1=x1, x2=x2, w=w)
     if out is None:
         out = torch.empty((n, h.dim_out), dtype=t, device=x1.device)
     elif out.shape != (n, h.dim_out) or out.dtype != t or not out.is_contiguous():
         raise ValueError("out has the wrong shape or dtype")
-    _check(lib.fctp_fwd(h._h, _ptr(x1), _ptr(x2), _ptr(w), n, _ptr(out), _stream_ptr(x1.device)))
+    fn = lib.fctp_fwd_per_sample if per else lib.fctp_fwd
+    _check(fn(h._h, _ptr(x1), _ptr(x2), _ptr(w), n, _ptr(out), _stream_ptr(x1.device)))
     return out
+
+
+def fctp_fwd_per_sample(h, x1, x2, w, out=None):
+    """out [n, dim_out] for x1 [n, dim_in1], x2 [n, dim_in2] and one weight
+    row per sample, w [n, weight_numel] (any n, 1 included)."""
+    import torch
+    t, n, _ = _fc_check(h, per_sample=True, x1=x1, x2=x2, w=w)
+    if out is None:
+        out = torch.empty((n, h.dim_out), dtype=t, device=x1.device)
+    elif out.shape != (n, h.dim_out) or out.dtype != t or not out.is_contiguous():
+        raise ValueError("out has the wrong shape or dtype")
+    _check(lib.fctp_fwd_per_sample(h._h, _ptr(x1), _ptr(x2), _ptr(w), n, _ptr(out), _stream_ptr(x1.device)))
+    return out
+
+
+def fctp_bwd_per_sample(h, x1, x2, w, grad_out, need=(True, True, True)):
+    """(grad_x1, grad_x2, grad_w) of ``fctp_fwd_per_sample``, grad_w
+    [n, weight_numel]; each None where ``need`` is False."""
+    import torch
+    _, n, _ = _fc_check(h, per_sample=True, x1=x1, x2=x2, w=w, grad_out=grad_out)
+    g1 = torch.empty_like(x1) if need[0] else None
+    g2 = torch.empty_like(x2) if need[1] else None
+    gw = torch.empty_like(w) if need[2] else None
+    _check(lib.fctp_bwd_per_sample(h._h, _ptr(x1), _ptr(x2), _ptr(w), _ptr(grad_out), n, _ptr(g1), _ptr(g2),
+                                   _ptr(gw), _stream_ptr(x1.device)))
+    return g1, g2, gw
 
 
 def fctp_bwd_workspace(h, n):
@@ -668,9 +712,13 @@ def fctp_bwd_workspace(h, n):
 
 
 def fctp_bwd(h, x1, x2, w, grad_out, need=(True, True, True), workspace=None):
-    """(grad_x1, grad_x2, grad_w), each None where ``need`` is False."""
+    """(grad_x1, grad_x2, grad_w), each None where ``need`` is False; with
+    per-sample weights [n, weight_numel] (n > 1) grad_w has one row per
+    sample and the per-sample kernel runs (no workspace)."""
     import torch
-    _, n = _fc_check(h, x1=x1, x2=x2, w=w, grad_out=grad_out)
+    _, n, per = _fc_check(h, x1=x1, x2=x2, w=w, grad_out=grad_out)
+    if per:
+        return fctp_bwd_per_sample(h, x1, x2, w, grad_out, need)
     g1 = torch.empty_like(x1) if need[0] else None
     g2 = torch.empty_like(x2) if need[1] else None
     gw = torch.empty_like(w) if need[2] else None

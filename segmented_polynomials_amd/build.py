@@ -69,7 +69,7 @@ def build(verbose=False, jobs=None):
                           "-o", os.path.join(obj, s + ".o")])
     jobs_list.append(["g++", *HOST_FLAGS, *inc, "-c", os.path.join(gen, "registry.cpp"),
                       "-o", os.path.join(obj, "registry.cpp.o")])
-    kernels = [os.path.join(CSRC, "kernels", k) for k in ("generic.hip", "linear.hip", "sh.hip", "fctp_f32.hip", "fctp_f64.hip", "fcconv.hip", "fcconv_bwd.hip", "edge_scalars.hip")]
+    kernels = [os.path.join(CSRC, "kernels", k) for k in ("generic.hip", "linear.hip", "sh.hip", "fctp_f32.hip", "fctp_f64.hip", "fcconv.hip", "fcconv_bwd.hip", "fctp_ps.hip", "edge_scalars.hip")]
     kernels.append(os.path.join(CSRC, "noalloc.hip"))
     for h in kernels + gen_hip:
         jobs_list.append([hipcc, *HIP_FLAGS, *inc, "-c", h,

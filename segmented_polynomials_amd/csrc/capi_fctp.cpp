@@ -16,6 +16,7 @@
 #include "capi_util.hpp"
 #include "cg.hpp"
 #include "fcconv_tables.hpp"
+#include "fctp_ps_tables.hpp"
 #include "fctp_tables.hpp"
 #include "irreps.hpp"
 #include "launch.hpp"
@@ -118,6 +119,13 @@ struct segpoly_fctp {
   int cv_ncomp = 0, cv_max_nqk = 0, cv_lane_bits = 0, cv_n_ut = 1;
   size_t cv_lds = 0;
   size_t cv_off[9] = {0, 0, 0, 0, 0, 0, 0, 0, 0};  // blocks, paths, qks, ents, tiles, qs, chunks, bpaths, uts in the blob
+  // one weight row per sample: tiles, paths, entry lists, entries
+  std::vector<PsTile> ps_tiles;
+  std::vector<PsPath> ps_paths;
+  std::vector<PsList> ps_lists;
+  std::vector<PsEnt> ps_ents;
+  int ps_max_d = 1;
+  size_t ps_off[4] = {0, 0, 0, 0};
   std::vector<unsigned char> blob;
   std::map<int, DeviceBuffer> dev;
   std::mutex mu;
@@ -411,6 +419,61 @@ void build_conv(segpoly_fctp* h) {
   if (h->cv_bwd_lds > 64 * 1024) h->conv_bwd_error = "the convolution backward's per-edge rows exceed the LDS of one wave";
 }
 
+// Tables of the per-sample form: paths grouped by output block, each with
+// its coupling entries listed three ways (by output, input-1 and input-2
+// component); tiles of up to 64 output channels.
+void build_ps(segpoly_fctp* h) {
+  for (size_t o = 0; o < h->out.size(); ++o) {
+    const Irrep& ob = h->out[o];
+    const int d3 = 2 * ob.l + 1;
+    const int path_begin = static_cast<int>(h->ps_paths.size());
+    for (const auto& pa : h->paths) {
+      if (pa.o != static_cast<int>(o)) continue;
+      const Irrep &a = h->in1[pa.i], &b = h->in2[pa.j];
+      const int d1 = 2 * a.l + 1, d2 = 2 * b.l + 1;
+      const std::vector<double>& C = real_cg(a.l, b.l, ob.l);
+      std::vector<PsEnt> nz;
+      for (int ia = 0; ia < d1; ++ia)
+        for (int ib = 0; ib < d2; ++ib)
+          for (int k = 0; k < d3; ++k) {
+            const double c = C[(static_cast<size_t>(ia) * d2 + ib) * d3 + k];
+            if (std::fabs(c) >= 1e-13) nz.push_back({ia, ib, k, 0, h->alpha[o] * c});
+          }
+      PsPath P{};
+      P.woff = pa.w_off;
+      P.off1 = static_cast<int>(h->off1[pa.i]);
+      P.off2 = static_cast<int>(h->off2[pa.j]);
+      P.m1 = a.mul, P.m2 = b.mul, P.d1 = d1, P.d2 = d2;
+      // which = 0: by output component, 1: by input-1, 2: by input-2
+      auto lists = [&](int which, int count) {
+        const int first = static_cast<int>(h->ps_lists.size());
+        for (int q = 0; q < count; ++q) {
+          PsList L{static_cast<int>(h->ps_ents.size()), 0};
+          for (const PsEnt& e : nz)
+            if ((which == 0 ? e.k : which == 1 ? e.a : e.b) == q) h->ps_ents.push_back(e);
+          L.end = static_cast<int>(h->ps_ents.size());
+          h->ps_lists.push_back(L);
+        }
+        return first;
+      };
+      P.k_list = lists(0, d3);
+      P.a_list = lists(1, d1);
+      P.b_list = lists(2, d2);
+      h->ps_paths.push_back(P);
+    }
+    const int path_end = static_cast<int>(h->ps_paths.size());
+    for (int w0 = 0; w0 < ob.mul; w0 += 64) {
+      PsTile t{};
+      t.offo = static_cast<int>(h->offo[o]);
+      t.d3 = d3, t.m3 = ob.mul, t.w0 = w0, t.nw = std::min(64, ob.mul - w0);
+      t.path_begin = path_begin, t.path_end = path_end;
+      while ((1 << t.lane_bits) < t.nw) ++t.lane_bits;
+      h->ps_max_d = std::max(h->ps_max_d, d3);
+      h->ps_tiles.push_back(t);
+    }
+  }
+}
+
 template <typename V>
 size_t append(std::vector<unsigned char>& blob, const std::vector<V>& v) {
   const size_t off = (blob.size() + 255) & ~size_t(255);
@@ -563,6 +626,7 @@ int fctp_create(const char* irreps_in1, const char* irreps_in2, const char* irre
     for (int w = 0; w < 3 && rc == SEGPOLY_OK; ++w) rc = build_pass(h, w);
     if (rc == SEGPOLY_OK) rc = build_dw(h);
     if (rc == SEGPOLY_OK) build_conv(h);
+    if (rc == SEGPOLY_OK) build_ps(h);
     if (rc == SEGPOLY_OK) {
       for (int w = 0; w < 3; ++w) {
         h->pass[w].res_off = append(h->blob, h->pass[w].res);
@@ -580,6 +644,10 @@ int fctp_create(const char* irreps_in1, const char* irreps_in2, const char* irre
       h->cv_off[6] = append(h->blob, h->cv_chunks);
       h->cv_off[7] = append(h->blob, h->cv_bpaths);
       h->cv_off[8] = append(h->blob, h->cv_uts);
+      h->ps_off[0] = append(h->blob, h->ps_tiles);
+      h->ps_off[1] = append(h->blob, h->ps_paths);
+      h->ps_off[2] = append(h->blob, h->ps_lists);
+      h->ps_off[3] = append(h->blob, h->ps_ents);
     }
   } catch (const std::bad_alloc&) {
     rc = fail(SEGPOLY_E_OOM, "out of host memory");
@@ -702,6 +770,78 @@ int fctp_bwd(fctp_handle h, const void* x1, const void* x2, const void* w, const
     const int rc = launch_fctp_dw(a, t);
     if (rc) return fail(SEGPOLY_E_HIP, std::string("fctp dw launch: ") + hipGetErrorString(static_cast<hipError_t>(rc)));
   }
+  return ok();
+}
+
+}  // extern "C"
+
+namespace {
+
+// Shared checks and arguments of the per-sample entry points; 0 or an error.
+int ps_args(segpoly_fctp* h, int64_t n, bool bwd, FcPsArgs& a, const unsigned char** db) {
+  const size_t e = elt(h->dtype);
+  a.lds_bytes = bwd ? ps_lds_bwd(h->dim1, h->dim2, h->ps_max_d, e) : ps_lds_fwd(h->dim1, h->dim2, h->ps_max_d, e);
+  if (a.lds_bytes > static_cast<size_t>(kPsLdsLimit))
+    return fail(SEGPOLY_E_UNSUPPORTED, "one sample's staged rows exceed 64 KB of LDS");
+  if (h->numel * static_cast<int64_t>(e) > 0x7fffffff)
+    return fail(SEGPOLY_E_UNSUPPORTED, "a weight row of 2 GiB or more");
+  if (n > kMaxGridX || (!bwd && h->ps_tiles.size() > 65535))
+    return fail(SEGPOLY_E_UNSUPPORTED, "too many samples or tiles for one launch");
+  int st = SEGPOLY_OK;
+  *db = device_blob(h, &st);
+  if (!*db) return st;
+  a.n = n;
+  a.dim1 = h->dim1, a.dim2 = h->dim2, a.dimo = h->dimo, a.numel = h->numel;
+  a.tiles = reinterpret_cast<const PsTile*>(*db + h->ps_off[0]);
+  a.paths = reinterpret_cast<const PsPath*>(*db + h->ps_off[1]);
+  a.lists = reinterpret_cast<const PsList*>(*db + h->ps_off[2]);
+  a.ents = reinterpret_cast<const PsEnt*>(*db + h->ps_off[3]);
+  a.n_tiles = static_cast<int>(h->ps_tiles.size());
+  a.max_d = h->ps_max_d;
+  a.dtype = h->dtype;
+  a.layout = h->layout;
+  return SEGPOLY_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fctp_fwd_per_sample(fctp_handle h, const void* x1, const void* x2, const void* w, int64_t n, void* out,
+                        void* stream) {
+  if (!h) return fail(SEGPOLY_E_INVALID, "null handle");
+  if (n < 0) return fail(SEGPOLY_E_INVALID, "negative sample count");
+  if (n == 0) return ok();
+  if (!out || (h->numel > 0 && !w) || (h->dim1 > 0 && !x1) || (h->dim2 > 0 && !x2))
+    return fail(SEGPOLY_E_INVALID, "null buffer");
+  FcPsArgs a{};
+  const unsigned char* db = nullptr;
+  int rc = ps_args(h, n, false, a, &db);
+  if (rc) return rc;
+  a.x1 = x1, a.x2 = x2, a.w = w, a.out = out;
+  a.stream = stream;
+  rc = launch_fctp_ps_fwd(a);
+  if (rc) return fail(SEGPOLY_E_HIP, std::string("fctp per-sample launch: ") + hipGetErrorString(static_cast<hipError_t>(rc)));
+  return ok();
+}
+
+int fctp_bwd_per_sample(fctp_handle h, const void* x1, const void* x2, const void* w, const void* grad_out,
+                        int64_t n, void* grad_x1, void* grad_x2, void* grad_w, void* stream) {
+  if (!h) return fail(SEGPOLY_E_INVALID, "null handle");
+  if (n < 0) return fail(SEGPOLY_E_INVALID, "negative sample count");
+  if (n == 0 || !(grad_x1 || grad_x2 || grad_w)) return ok();
+  if ((h->dimo > 0 && !grad_out) || (h->dim1 > 0 && !x1 && (grad_x2 || grad_w)) ||
+      (h->dim2 > 0 && !x2 && (grad_x1 || grad_w)) || (h->numel > 0 && !w && (grad_x1 || grad_x2)))
+    return fail(SEGPOLY_E_INVALID, "null buffer");
+  FcPsArgs a{};
+  const unsigned char* db = nullptr;
+  int rc = ps_args(h, n, true, a, &db);
+  if (rc) return rc;
+  a.x1 = x1, a.x2 = x2, a.w = w, a.g = grad_out;
+  a.dx1 = grad_x1, a.dx2 = grad_x2, a.dw = h->numel > 0 ? grad_w : nullptr;
+  a.stream = stream;
+  rc = launch_fctp_ps_bwd(a);
+  if (rc) return fail(SEGPOLY_E_HIP, std::string("fctp per-sample backward launch: ") + hipGetErrorString(static_cast<hipError_t>(rc)));
   return ok();
 }
 

@@ -387,6 +387,22 @@ def test_fctp_errors_and_workspace():
     big = 1 << 30
     assert b(h._h, p, p, None, p, 5000, p, None, None, p, big, None) == sp.E_INVALID      # dx1 needs w
     assert b(h._h, None, None, None, None, 0, None, None, None, None, 0, None) == sp.OK
+    # one weight row per sample: no workspace
+    pf, pb = sp.lib.fctp_fwd_per_sample, sp.lib.fctp_bwd_per_sample
+    assert pf(h._h, p, p, p, -1, p, None) == sp.E_INVALID
+    assert pf(h._h, p, p, p, 3, None, None) == sp.E_INVALID
+    assert pf(h._h, p, p, None, 3, p, None) == sp.E_INVALID
+    assert pf(h._h, None, None, None, 0, None, None) == sp.OK
+    assert pf(None, p, p, p, 3, p, None) == sp.E_INVALID
+    assert pb(h._h, p, p, p, None, 3, p, None, None, None) == sp.E_INVALID      # no output gradient
+    assert pb(h._h, p, p, None, p, 3, p, None, None, None) == sp.E_INVALID      # dx1 needs w
+    assert pb(h._h, None, p, p, p, 3, None, None, p, None) == sp.E_INVALID      # dw needs x1
+    assert pb(h._h, p, p, p, p, 3, None, None, None, None) == sp.OK             # nothing requested
+    assert pb(h._h, p, p, p, p, -2, p, p, p, None) == sp.E_INVALID
+    many = "+".join(["1000x0e"] * 5)
+    wide = sp.fctp_create(many, many, "1x0e")   # the backward stages 2 (5000 + 5000) floats
+    assert pb(wide._h, p, p, p, p, 3, p, None, None, None) == sp.E_UNSUPPORTED
+    assert b"64 KB" in sp.lib.segpoly_last_error()
     assert sp.lib.fctp_destroy(None) == sp.OK
     # the convolution form: input 2 with one channel per block, w_rows 1 or n_edges
     cv = sp.lib.fctp_conv_fwd
