@@ -348,6 +348,8 @@ def main():
         note("fully connected product timed")
         result["fctp_conv"] = fc_conv(torch, sp, workloads, dev, args)
         note("fully connected convolution timed")
+        result["fctp_per_sample"] = fc_per_sample(torch, sp, workloads, dev, args)
+        note("fully connected product with per-sample weights timed")
 
     if args.copy_calibration:
         a = torch.empty(1 << 28, dtype=torch.float32, device=dev)   # 1 GiB
@@ -770,6 +772,52 @@ def fc_conv(torch, sp, workloads, dev, args):
                                                     "GBps_with_overhead": (bbytes + msg) / (kb * 1e-3) / 1e9}}
         del out, g, perm, ws
     del x, sh, w, src, dst
+    return res
+
+
+def fc_per_sample(torch, sp, workloads, dev, args):
+    """The fully connected product with one weight row per sample (20k
+    samples of 16x0e+16x1o x 8x0e+8x1o -> 16x0e+16x1o, 8,192 weights per
+    sample), both layouts.  Algorithmic bytes: every operand read or written
+    once; per sample forward the weight row, x1, x2 and the output row;
+    backward the weight row, x1, x2 and the output gradient read, the
+    weight-gradient row and both input gradients written."""
+    import numpy as np
+
+    from oracle import fctp as ofc   # sizes only
+    wl = workloads.WORKLOADS[10]
+    f = ofc.FullyConnectedTP(wl.irreps_in1, wl.irreps_in2, wl.irreps_out)
+    inp = workloads.fc_inputs(wl, f.weight_numel)
+    to = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    x1, x2, w = (to(inp[k]) for k in ("x1", "x2", "w"))
+    del inp
+    g = to(workloads.output_gradient(wl.n, f.dim_out, wl.dtype, seed=2010))
+    n = wl.n
+    fbytes = n * (f.weight_numel + f.dim_in1 + f.dim_in2 + f.dim_out) * 4
+    bbytes = n * (2 * f.weight_numel + 2 * f.dim_in1 + 2 * f.dim_in2 + f.dim_out) * 4
+    res = {"workload": wl.name, "samples": n, "weights_per_sample": f.weight_numel,
+           "algorithmic_bytes": {"forward": fbytes, "backward": bbytes}}
+    out = torch.empty((n, f.dim_out), dtype=torch.float32, device=dev)
+    g1, g2, gw = torch.empty_like(x1), torch.empty_like(x2), torch.empty_like(w)
+    for lay in wl.layouts:
+        h = sp.fctp_create(wl.irreps_in1, wl.irreps_in2, wl.irreps_out, layout=lay, dtype=wl.dtype)
+        st = sp._stream_ptr(x1.device)
+        fwd = lambda: sp._check(sp.lib.fctp_fwd_per_sample(h._h, sp._ptr(x1), sp._ptr(x2), sp._ptr(w), n,
+                                                           sp._ptr(out), st))
+        wall, per = time_launches(torch, fwd, args.steps, args.warmup)
+        kms = sum(per) / len(per)
+        bwd = lambda: sp._check(sp.lib.fctp_bwd_per_sample(h._h, sp._ptr(x1), sp._ptr(x2), sp._ptr(w), sp._ptr(g),
+                                                           n, sp._ptr(g1), sp._ptr(g2), sp._ptr(gw), st))
+        wallb, perb = time_launches(torch, bwd, args.steps, args.warmup)
+        kb = sum(perb) / len(perb)
+        fg, bg = fbytes / (kms * 1e-3) / 1e9, bbytes / (kb * 1e-3) / 1e9
+        res[lay] = {"ms_per_call": kms, "samples_per_s": n / (wall / args.steps), "kernel": "fctp_ps_fwd_kernel",
+                    "roofline": {"bound": "hbm", "achieved": fg, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                                 "frac": fg / HBM_PEAK_GBPS},
+                    "backward": {"ms_per_call": kb, "kernel": "fctp_ps_bwd_kernel",
+                                 "roofline": {"bound": "hbm", "achieved": bg, "peak": HBM_PEAK_GBPS,
+                                              "unit": "GB/s", "frac": bg / HBM_PEAK_GBPS}}}
+    del x1, x2, w, g, out, g1, g2, gw
     return res
 
 

@@ -839,6 +839,12 @@ int fctp_bwd_per_sample(fctp_handle h, const void* x1, const void* x2, const voi
   if (rc) return rc;
   a.x1 = x1, a.x2 = x2, a.w = w, a.g = grad_out;
   a.dx1 = grad_x1, a.dx2 = grad_x2, a.dw = h->numel > 0 ? grad_w : nullptr;
+  // 16-byte pieces of the weight rows: every output multiplicity (so every
+  // row, segment and tile start) a multiple of 16 bytes, and aligned buffers
+  const int64_t vw = 16 / static_cast<int64_t>(elt(h->dtype));
+  bool vec = reinterpret_cast<uintptr_t>(w) % 16 == 0 && reinterpret_cast<uintptr_t>(a.dw) % 16 == 0;
+  for (const auto& b : h->out) vec = vec && b.mul % vw == 0;
+  a.vec = vec ? 1 : 0;
   a.stream = stream;
   rc = launch_fctp_ps_bwd(a);
   if (rc) return fail(SEGPOLY_E_HIP, std::string("fctp per-sample backward launch: ") + hipGetErrorString(static_cast<hipError_t>(rc)));

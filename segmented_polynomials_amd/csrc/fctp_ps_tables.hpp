@@ -60,14 +60,16 @@ struct FcPsArgs {
   const PsList* lists;
   const PsEnt* ents;
   int n_tiles, max_d;
+  int vec;                       // backward: weight rows read and written in 16-byte pieces (aligned rows)
   size_t lds_bytes;
   int dtype, layout;
   void* stream;
 };
 
-// LDS of one workgroup (one wave): the sample's two input rows, one chunk of
-// coupled values (forward, and the weight gradient), and in the backward the
-// per-chunk weight-contracted values and the two input-gradient rows.
+// LDS of one workgroup (one wave): the sample's two input rows and one chunk
+// of coupled values (forward); in the backward the two input rows, the two
+// input-gradient rows, the tile's output gradient (64 channels per output
+// component) and one chunk of weight-contracted values.
 inline size_t ps_lds_fwd(int64_t dim1, int64_t dim2, int max_d, size_t elt) {
   return static_cast<size_t>(dim1 + dim2 + static_cast<int64_t>(kPsChunk) * max_d) * elt;
 }

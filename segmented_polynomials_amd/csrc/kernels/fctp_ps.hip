@@ -17,12 +17,15 @@
 // S consecutive weight rows of M channels) and accumulates acc[k] += W A[k].
 // The slots are summed with cross-lane shuffles at the end of the tile.
 //
-// Backward: one wave per sample, all tiles in turn, with the input-gradient
-// rows accumulated in LDS.  Per chunk: the weight gradient
-// dW_s[p][u, v, w] = sum_k A[k, u, v] g[s, o, k, w] is written once; the
-// weight-contracted output gradient R[k, u, v] = sum_w W_s[p][u, v, w] g[s, o, k, w]
-// is summed over the M lanes of a slot and kept in LDS; then the lanes each
-// own input-gradient elements of the chunk (pairs (a, u), then (b, v)) and add
+// Backward: one wave per sample, all tiles in turn, with the tile's output
+// gradient g[s, o, ., w] and the input-gradient rows in LDS.  Lane q owns
+// pair q of a chunk: it forms A[., u, v] in registers and walks the weight
+// row W_s[p][u, v, .] of its tile (16-byte loads where the rows are aligned),
+// writing the weight gradient dW_s[p][u, v, w] = sum_k A[k, u, v] g[s, o, k, w]
+// once and summing the weight-contracted output gradient
+// R[k, u, v] = sum_w W_s[p][u, v, w] g[s, o, k, w] in registers, no
+// cross-lane traffic.  Then the lanes each own input-gradient elements of
+// the chunk (pairs (a, u), then (b, v)) and add
 //   dx1[a, u] += sum_v sum_(b, k) C[a, b, k] x2[b, v] R[k, u, v],
 //   dx2[b, v] += sum_u sum_(a, k) C[a, b, k] x1[a, u] R[k, u, v]
 // (alpha_o folded into C), so no two lanes write one element and every sum
@@ -192,13 +195,12 @@ __device__ __forceinline__ void ps_dx(const PsPath& P, int c0, int nuv, int lane
       const int vb = max(0, c0 - u * m2), ve = min(m2, c1 - u * m2);
       const PsList L = lists[P.a_list + a];
       T acc = T(0);
-      for (int v = vb; v < ve; ++v) {
-        const T* rr = Rs + (u * m2 + v - c0) * D;
-        const T* r2 = xs2 + P.off2 + (LAYOUT == kIrMul ? v : v * d2);
-        for (int e = L.begin; e < L.end; ++e) {
-          const PsEnt E = ents[e];
-          acc = fmadd(static_cast<T>(E.c) * r2[E.b * sb], rr[E.k], acc);
-        }
+      for (int e = L.begin; e < L.end; ++e) {
+        const PsEnt E = ents[e];
+        const T ce = static_cast<T>(E.c);
+        const T* r2 = xs2 + P.off2 + E.b * sb;
+        for (int v = vb; v < ve; ++v)
+          acc = fmadd(ce * r2[LAYOUT == kIrMul ? v : v * d2], Rs[(u * m2 + v - c0) * D + E.k], acc);
       }
       dx1a[P.off1 + ps_idx<LAYOUT>(a, u, d1, m1)] += acc;
     }
@@ -213,93 +215,166 @@ __device__ __forceinline__ void ps_dx(const PsPath& P, int c0, int nuv, int lane
       const int ue = c1 - 1 >= v ? (c1 - 1 - v) / m2 : -1;
       const PsList L = lists[P.b_list + b];
       T acc = T(0);
-      for (int u = ub; u <= ue; ++u) {
-        const T* rr = Rs + (u * m2 + v - c0) * D;
-        const T* r1 = xs1 + P.off1 + (LAYOUT == kIrMul ? u : u * d1);
-        for (int e = L.begin; e < L.end; ++e) {
-          const PsEnt E = ents[e];
-          acc = fmadd(static_cast<T>(E.c) * r1[E.a * sa], rr[E.k], acc);
-        }
+      for (int e = L.begin; e < L.end; ++e) {
+        const PsEnt E = ents[e];
+        const T ce = static_cast<T>(E.c);
+        const T* r1 = xs1 + P.off1 + E.a * sa;
+        for (int u = ub; u <= ue; ++u)
+          acc = fmadd(ce * r1[LAYOUT == kIrMul ? u : u * d1], Rs[(u * m2 + v - c0) * D + E.k], acc);
       }
       dx2a[P.off2 + ps_idx<LAYOUT>(b, v, d2, m2)] += acc;
     }
   }
 }
 
+// A[k, u, v] of pair j of path P in registers (zero if !ok).
 template <typename T, int LAYOUT, int D>
-__device__ __forceinline__ void ps_bwd_tile(__amdgpu_buffer_rsrc_t wr, const T* __restrict__ grow,
-                                            T* __restrict__ dwrow, const T* xs1, const T* xs2, T* As, T* Rs,
+__device__ __forceinline__ void ps_coupled_regs(const PsPath& P, int j, bool ok, const T* xs1, const T* xs2,
+                                                const PsList* __restrict__ lists, const PsEnt* __restrict__ ents,
+                                                T (&A)[D]) {
+  const int u = ok ? j / P.m2 : 0;
+  const int v = ok ? j - u * P.m2 : 0;
+  const int sa = LAYOUT == kIrMul ? P.m1 : 1;
+  const int sb = LAYOUT == kIrMul ? P.m2 : 1;
+  const T* r1 = xs1 + P.off1 + (LAYOUT == kIrMul ? u : u * P.d1);
+  const T* r2 = xs2 + P.off2 + (LAYOUT == kIrMul ? v : v * P.d2);
+#pragma unroll
+  for (int k = 0; k < D; ++k) {
+    const PsList L = lists[P.k_list + k];
+    T s = T(0);
+    for (int e = L.begin; e < L.end; ++e) {
+      const PsEnt E = ents[e];
+      s = fmadd(static_cast<T>(E.c) * r1[E.a * sa], r2[E.b * sb], s);
+    }
+    A[k] = ok ? s : T(0);
+  }
+}
+
+// Elements of a weight row a lane handles at a time: four 16-byte pieces.
+template <typename T>
+constexpr int ps_piece() {
+  return 64 / static_cast<int>(sizeof(T));
+}
+
+// The first `cnt` (uniform) elements of a piece at byte offset `off` of a
+// row, zero past them or when !ok.  VEC: 16-byte loads (the offset and cnt
+// are multiples of 16 bytes).
+template <typename T, bool VEC>
+__device__ __forceinline__ void ps_load_piece(__amdgpu_buffer_rsrc_t r, uint32_t off, bool ok, int cnt,
+                                              T (&v)[ps_piece<T>()]) {
+  constexpr int PW = ps_piece<T>();
+  if constexpr (VEC) {
+    constexpr int VW = 16 / static_cast<int>(sizeof(T));
+#pragma unroll
+    for (int q = 0; q < PW / VW; ++q) {
+      const uint32_t o = ok && q * VW < cnt ? off + 16u * q : kBufMasked;
+      const auto raw = __builtin_amdgcn_raw_buffer_load_b128(r, o, 0, 0);
+      const auto t = __builtin_bit_cast(T __attribute__((ext_vector_type(VW))), raw);
+#pragma unroll
+      for (int e = 0; e < VW; ++e) v[q * VW + e] = t[e];
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < PW; ++e)
+      v[e] = buf_load<T>(r, ok && e < cnt ? off + static_cast<uint32_t>(e * sizeof(T)) : kBufMasked);
+  }
+}
+
+// Stores of the same elements (a masked offset drops the store).
+template <typename T, bool VEC>
+__device__ __forceinline__ void ps_store_piece(__amdgpu_buffer_rsrc_t r, uint32_t off, bool ok, int cnt,
+                                               const T (&v)[ps_piece<T>()]) {
+  constexpr int PW = ps_piece<T>();
+  if constexpr (VEC) {
+    constexpr int VW = 16 / static_cast<int>(sizeof(T));
+#pragma unroll
+    for (int q = 0; q < PW / VW; ++q) {
+      if (q * VW >= cnt) break;
+      T __attribute__((ext_vector_type(VW))) t;
+#pragma unroll
+      for (int e = 0; e < VW; ++e) t[e] = v[q * VW + e];
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned, t), r,
+                                             ok ? off + 16u * q : kBufMasked, 0, 0);
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < PW; ++e) {
+      if (e >= cnt) break;
+      const uint32_t o = ok ? off + static_cast<uint32_t>(e * sizeof(T)) : kBufMasked;
+      if constexpr (sizeof(T) == 4)
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, v[e]), r, o, 0, 0);
+      else
+        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(__attribute__((ext_vector_type(2))) unsigned, v[e]),
+                                              r, o, 0, 0);
+    }
+  }
+}
+
+template <typename T, int LAYOUT, int D, bool VEC>
+__device__ __forceinline__ void ps_bwd_tile(__amdgpu_buffer_rsrc_t wr, __amdgpu_buffer_rsrc_t dwr, bool want_dw,
+                                            const T* __restrict__ grow, const T* xs1, const T* xs2, T* gsl, T* Rs,
                                             T* dx1a, T* dx2a, bool want1, bool want2, const PsTile& t,
                                             const PsPath* __restrict__ paths, const PsList* __restrict__ lists,
                                             const PsEnt* __restrict__ ents, int lane) {
-  constexpr int B = ps_batch<T>();
-  const int M = 1 << t.lane_bits, S = 64 >> t.lane_bits;
-  const int slot = lane >> t.lane_bits, c = lane & (M - 1);
-  const bool wlane = c < t.nw;
-  const int w = t.w0 + c;
-  const bool want_dw = dwrow != nullptr;
+  constexpr int PW = ps_piece<T>();
   const bool want_dx = want1 || want2;
-  T gk[D];
-#pragma unroll
-  for (int k = 0; k < D; ++k) gk[k] = wlane ? grow[t.offo + ps_idx<LAYOUT>(k, w, D, t.m3)] : T(0);
+  // the tile's output gradient: gsl[k * 64 + c] = g[s, o, k, w0 + c]
+  for (int i = lane; i < D * t.nw; i += 64) {
+    const int k = i / t.nw, c = i - k * t.nw;
+    gsl[k * 64 + c] = grow[t.offo + ps_idx<LAYOUT>(k, t.w0 + c, D, t.m3)];
+  }
+  ps_wave_sync();
   for (int p = t.path_begin; p < t.path_end; ++p) {
     const PsPath P = paths[p];
     const int nuv = P.m1 * P.m2;
     for (int c0 = 0; c0 < nuv; c0 += kPsChunk) {
-      if (want_dw) ps_coupled<T, LAYOUT, D>(P, c0, nuv, lane, xs1, xs2, As, lists, ents);
-      ps_wave_sync();
-      const int n_in = min(kPsChunk, nuv - c0);
-      const int steps = (n_in + S - 1) / S;
-      for (int s0 = 0; s0 < steps; s0 += B) {
-        T wv[B];
-        if (want_dx) {
+      const int j = c0 + lane;
+      const bool ok = j < nuv;
+      T A[D];
+      if (want_dw) ps_coupled_regs<T, LAYOUT, D>(P, j, ok, xs1, xs2, lists, ents, A);
+      T R[D];
 #pragma unroll
-          for (int q = 0; q < B; ++q) {
-            const int j = (s0 + q) * S + slot;
-            const bool ok = wlane && j < n_in;
-            const uint32_t off = ok ? static_cast<uint32_t>((P.woff + static_cast<int64_t>(c0 + j) * t.m3 + w) *
-                                                            sizeof(T))
-                                    : kBufMasked;
-            wv[q] = s0 + q < steps ? buf_load<T>(wr, off) : T(0);
-          }
-        }
+      for (int k = 0; k < D; ++k) R[k] = T(0);
+      const int64_t row = P.woff + static_cast<int64_t>(ok ? j : 0) * t.m3 + t.w0;
+      for (int wc = 0; wc < t.nw; wc += PW) {
+        const int cnt = min(PW, t.nw - wc);
+        const uint32_t off = static_cast<uint32_t>((row + wc) * static_cast<int64_t>(sizeof(T)));
+        T wv[PW], dv[PW];
+        if (want_dx) ps_load_piece<T, VEC>(wr, off, ok, cnt, wv);
 #pragma unroll
-        for (int q = 0; q < B; ++q) {
-          if (s0 + q >= steps) break;
-          const int j = (s0 + q) * S + slot;
-          const bool valid = j < n_in;
-          if (want_dw && valid && wlane) {
-            const T* a = As + j * D;
-            T d = T(0);
+        for (int e = 0; e < PW; ++e) {
+          dv[e] = T(0);
+          if (e < cnt) {
+            T gk[D];
 #pragma unroll
-            for (int k = 0; k < D; ++k) d = fmadd(a[k], gk[k], d);
-            dwrow[P.woff + static_cast<int64_t>(c0 + j) * t.m3 + w] = d;
-          }
-          if (want_dx) {
-            T r[D];
+            for (int k = 0; k < D; ++k) gk[k] = gsl[k * 64 + wc + e];
+            if (want_dx) {
 #pragma unroll
-            for (int k = 0; k < D; ++k) r[k] = wv[q] * gk[k];
-            for (int off = 1; off < M; off <<= 1) {
-#pragma unroll
-              for (int k = 0; k < D; ++k) r[k] += __shfl_xor(r[k], off, 64);
+              for (int k = 0; k < D; ++k) R[k] = fmadd(wv[e], gk[k], R[k]);
             }
-            if (valid && c == 0) {
+            if (want_dw) {
+              T d = T(0);
 #pragma unroll
-              for (int k = 0; k < D; ++k) Rs[j * D + k] = r[k];
+              for (int k = 0; k < D; ++k) d = fmadd(A[k], gk[k], d);
+              dv[e] = d;
             }
           }
         }
+        if (want_dw) ps_store_piece<T, VEC>(dwr, off, ok, cnt, dv);
       }
-      ps_wave_sync();
       if (want_dx) {
+#pragma unroll
+        for (int k = 0; k < D; ++k) Rs[lane * D + k] = R[k];
+        ps_wave_sync();
         ps_dx<T, LAYOUT, D>(P, c0, nuv, lane, xs1, xs2, Rs, dx1a, dx2a, want1, want2, lists, ents);
         ps_wave_sync();
       }
     }
   }
+  ps_wave_sync();  // the next tile rewrites gsl
 }
 
-template <typename T, int LAYOUT>
+template <typename T, int LAYOUT, bool VEC>
 __global__ __launch_bounds__(64) void fctp_ps_bwd_kernel(const T* __restrict__ x1, const T* __restrict__ x2,
                                                          const T* __restrict__ w, const T* __restrict__ g,
                                                          T* __restrict__ dx1, T* __restrict__ dx2,
@@ -314,8 +389,8 @@ __global__ __launch_bounds__(64) void fctp_ps_bwd_kernel(const T* __restrict__ x
   T* xs2 = xs1 + dim1;
   T* dx1a = xs2 + dim2;
   T* dx2a = dx1a + dim1;
-  T* As = dx2a + dim2;
-  T* Rs = As + kPsChunk * max_d;
+  T* gsl = dx2a + dim2;
+  T* Rs = gsl + kPsChunk * max_d;
   const int64_t s = blockIdx.x;
   const int lane = threadIdx.x;
   const bool want1 = dx1 != nullptr, want2 = dx2 != nullptr;
@@ -329,15 +404,17 @@ __global__ __launch_bounds__(64) void fctp_ps_bwd_kernel(const T* __restrict__ x
     dx2a[i] = T(0);
   }
   ps_wave_sync();
-  const __amdgpu_buffer_rsrc_t wr = buf_rsrc(w ? w + s * numel : w, w ? numel * static_cast<int64_t>(sizeof(T)) : 0);
+  const int64_t rb = numel * static_cast<int64_t>(sizeof(T));
+  const __amdgpu_buffer_rsrc_t wr = buf_rsrc(w ? w + s * numel : w, w ? rb : 0);
+  const __amdgpu_buffer_rsrc_t dwr = buf_rsrc(dw ? dw + s * numel : dw, dw ? rb : 0);
   const T* grow = g + s * dimo;
-  T* dwrow = dw ? dw + s * numel : nullptr;
+  const bool want_dw = dw != nullptr;
   for (int ti = 0; ti < n_tiles; ++ti) {
     const PsTile t = tiles[ti];
 #define SEGPOLY_PS_BWD_CASE(DD)                                                                                  \
   case DD:                                                                                                       \
-    ps_bwd_tile<T, LAYOUT, DD>(wr, grow, dwrow, xs1, xs2, As, Rs, dx1a, dx2a, want1, want2, t, paths, lists,     \
-                               ents, lane);                                                                      \
+    ps_bwd_tile<T, LAYOUT, DD, VEC>(wr, dwr, want_dw, grow, xs1, xs2, gsl, Rs, dx1a, dx2a, want1, want2, t,      \
+                                    paths, lists, ents, lane);                                                   \
     break;
     switch (t.d3) {
       SEGPOLY_PS_BWD_CASE(1)
@@ -368,9 +445,9 @@ int ps_fwd_launch(const FcPsArgs& a) {
   return static_cast<int>(hipGetLastError());
 }
 
-template <typename T, int LAYOUT>
+template <typename T, int LAYOUT, bool VEC>
 int ps_bwd_launch(const FcPsArgs& a) {
-  hipLaunchKernelGGL((fctp_ps_bwd_kernel<T, LAYOUT>), dim3(static_cast<unsigned>(a.n)), dim3(64), a.lds_bytes,
+  hipLaunchKernelGGL((fctp_ps_bwd_kernel<T, LAYOUT, VEC>), dim3(static_cast<unsigned>(a.n)), dim3(64), a.lds_bytes,
                      static_cast<hipStream_t>(a.stream), static_cast<const T*>(a.x1), static_cast<const T*>(a.x2),
                      static_cast<const T*>(a.w), static_cast<const T*>(a.g), static_cast<T*>(a.dx1),
                      static_cast<T*>(a.dx2), static_cast<T*>(a.dw), a.dim1, a.dim2, a.dimo, a.numel, a.tiles,
@@ -385,7 +462,8 @@ int ps_fwd_dispatch(const FcPsArgs& a) {
 
 template <typename T>
 int ps_bwd_dispatch(const FcPsArgs& a) {
-  return a.layout == kIrMul ? ps_bwd_launch<T, kIrMul>(a) : ps_bwd_launch<T, kMulIr>(a);
+  if (a.vec) return a.layout == kIrMul ? ps_bwd_launch<T, kIrMul, true>(a) : ps_bwd_launch<T, kMulIr, true>(a);
+  return a.layout == kIrMul ? ps_bwd_launch<T, kIrMul, false>(a) : ps_bwd_launch<T, kMulIr, false>(a);
 }
 
 }  // namespace

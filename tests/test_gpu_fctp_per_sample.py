@@ -152,25 +152,30 @@ def test_empty_and_errors():
         sp.fctp_fwd(h, x1, x2, torch.zeros((2, f.weight_numel), device="cuda"))
 
 
-def test_many_samples_sampled():
-    """A larger batch (4096 samples, the per-sample shape used for timing):
-    sampled rows against the oracle one by one."""
+def test_full_size_workload_sampled():
+    """The timed per-sample workload at full size (20k samples, 8,192
+    weights each), in the launch configuration the benchmark times:
+    sampled rows against the oracle one by one, both layouts."""
     sp = _sp()
     import torch
-    i1, i2, io = "16x0e+16x1o", "8x0e+8x1o", "16x0e+16x1o"
-    f = ofc.FullyConnectedTP(i1, i2, io)
-    h = sp.fctp_create(i1, i2, io, dtype="f32")
-    n = 4096
-    x1, x2, w, g = _inputs(f, n, "f32", seed=77)
+    import workloads
+    wl = workloads.WORKLOADS[10]
+    f = ofc.FullyConnectedTP(wl.irreps_in1, wl.irreps_in2, wl.irreps_out)
+    inp = workloads.fc_inputs(wl, f.weight_numel)
+    x1, x2, w = inp["x1"], inp["x2"], inp["w"]
+    g = workloads.output_gradient(wl.n, f.dim_out, wl.dtype, seed=2010)
     X1, X2, W, G = dev(x1), dev(x2), dev(w), dev(g)
-    announce("fctp per-sample 4096 samples")
-    out = sp.fctp_fwd_per_sample(h, X1, X2, W).cpu().numpy()
-    g1, g2, gw = (t.cpu().numpy() for t in sp.fctp_bwd_per_sample(h, X1, X2, W, G))
-    rows = np.random.default_rng(3).choice(n, 24, replace=False)
-    rows = np.concatenate([rows, [0, n - 1]])
-    s = (x1[rows], x2[rows], w[rows])
-    check_scaled(out[rows], f.fwd(*s), f.fwd(*s, absolute=True), "f32", "fwd rows")
-    r = f.vjp(*s[:2], None, g[rows], edge_weights=s[2])
-    a = f.vjp(*s[:2], None, g[rows], absolute=True, edge_weights=s[2])
-    for got, ref, sc, name in zip((g1, g2, gw), r, a, ("dx1", "dx2", "dw")):
-        check_scaled(got[rows], ref, sc, "f32", f"{name} rows")
+    rows = np.concatenate([np.random.default_rng(3).choice(wl.n, 24, replace=False), [0, wl.n - 1]])
+    for lay in wl.layouts:
+        h = sp.fctp_create(wl.irreps_in1, wl.irreps_in2, wl.irreps_out, layout=lay, dtype=wl.dtype)
+        announce(f"fctp per-sample full size {wl.name} {lay}")
+        out = sp.fctp_fwd(h, X1, X2, W).cpu().numpy()
+        g1, g2, gw = (t.cpu().numpy() for t in sp.fctp_bwd(h, X1, X2, W, G))
+        torch.cuda.synchronize()
+        s = (x1[rows], x2[rows], w[rows])
+        check_scaled(out[rows], f.fwd(*s, layout=lay), f.fwd(*s, layout=lay, absolute=True), "f32",
+                     f"{lay} fwd rows")
+        r = f.vjp(*s[:2], None, g[rows], layout=lay, edge_weights=s[2])
+        a = f.vjp(*s[:2], None, g[rows], layout=lay, absolute=True, edge_weights=s[2])
+        for got, ref, sc, name in zip((g1, g2, gw), r, a, ("dx1", "dx2", "dw")):
+            check_scaled(got[rows], ref, sc, "f32", f"{lay} {name} rows")

@@ -81,6 +81,7 @@ class FCWorkload:
     layouts: tuple
     dtype: str
     n: int
+    per_sample: bool = False  # one weight row per sample [n, numel] (else one shared row)
 
 
 @dataclass(frozen=True)
@@ -134,6 +135,12 @@ WORKLOADS = {
     # scalar + vector features and l <= 2 harmonics on the 20k-node graph
     9: FCConvWorkload(9, "fctp_conv_20k_nodes_600k_edges", "16x0e+16x1o", "0e+1o+2e", "16x0e+16x1o",
                       ("mul_ir", "ir_mul"), "f32", n_nodes=20000, degree=30, sh_ls=(0, 1, 2)),
+    # the fully connected product with external weights, one row per sample
+    # (the skill document's shared_weights=False), 16-channel scalar + vector
+    # features times 8-channel scalar + vector attributes over a 20k batch:
+    # 8,192 weights (32 KB) per sample
+    10: FCWorkload(10, "fctp_per_sample_16x0e+16x1o_x_8x0e+8x1o_20k", "16x0e+16x1o", "8x0e+8x1o",
+                   "16x0e+16x1o", ("mul_ir", "ir_mul"), "f32", n=20000, per_sample=True),
 }
 
 
@@ -369,14 +376,15 @@ def linear_inputs(wl, weight_numel, n=None, seed=None):
 
 def fc_inputs(wl, weight_numel, n=None, seed=None):
     """Inputs of a fully connected product workload: x1 [n, dim_in1] and
-    x2 [n, dim_in2] N(0,1), shared weights [1, weight_numel] N(0,1) (the
+    x2 [n, dim_in2] N(0,1), weights N(0,1), one shared row [1, weight_numel]
+    or, for a per-sample workload, one row per sample [n, weight_numel] (the
     product's own 1/sqrt(fan-in) keeps outputs at unit scale)."""
     rng = np.random.default_rng(1000 + wl.number if seed is None else seed)
     dt = _np_dtype(wl.dtype)
     n = wl.n if n is None else n
     x1 = _normal(rng, (n, _irreps_dim(wl.irreps_in1)), wl.dtype).astype(dt, copy=False)
     x2 = _normal(rng, (n, _irreps_dim(wl.irreps_in2)), wl.dtype).astype(dt, copy=False)
-    w = _normal(rng, (1, weight_numel), wl.dtype).astype(dt, copy=False)
+    w = _normal(rng, (n if wl.per_sample else 1, weight_numel), wl.dtype).astype(dt, copy=False)
     return dict(x1=x1, x2=x2, w=w)
 
 
