@@ -129,7 +129,7 @@ __device__ __forceinline__ void ps_fwd_tile(__amdgpu_buffer_rsrc_t wr, const T* 
   }
 }
 
-template <typename T, int LAYOUT>
+template <typename T, int LAYOUT, int DMAX>
 __global__ __launch_bounds__(64) void fctp_ps_fwd_kernel(const T* __restrict__ x1, const T* __restrict__ x2,
                                                          const T* __restrict__ w, T* __restrict__ out, int64_t dim1,
                                                          int64_t dim2, int64_t dimo, int64_t numel,
@@ -152,7 +152,7 @@ __global__ __launch_bounds__(64) void fctp_ps_fwd_kernel(const T* __restrict__ x
   const int slot = lane >> t.lane_bits, c = lane & (M - 1);
   T* orow = out + s * dimo + t.offo;
 #define SEGPOLY_PS_FWD_CASE(DD)                                                                  \
-  case DD: {                                                                                     \
+  case DD: if constexpr (DD <= DMAX) {                                                           \
     T acc[DD];                                                                                   \
     _Pragma("unroll") for (int k = 0; k < DD; ++k) acc[k] = T(0);                                \
     ps_fwd_tile<T, LAYOUT, DD>(wr, xs1, xs2, As, t, paths, lists, ents, lane, slot, c, S, acc);  \
@@ -162,8 +162,8 @@ __global__ __launch_bounds__(64) void fctp_ps_fwd_kernel(const T* __restrict__ x
     if (slot == 0 && c < t.nw) {                                                                 \
       _Pragma("unroll") for (int k = 0; k < DD; ++k) orow[ps_idx<LAYOUT>(k, t.w0 + c, DD, t.m3)] = acc[k]; \
     }                                                                                            \
-    break;                                                                                       \
-  }
+  }                                                                                              \
+  break;
   switch (t.d3) {
     SEGPOLY_PS_FWD_CASE(1)
     SEGPOLY_PS_FWD_CASE(3)
@@ -374,7 +374,7 @@ __device__ __forceinline__ void ps_bwd_tile(__amdgpu_buffer_rsrc_t wr, __amdgpu_
   ps_wave_sync();  // the next tile rewrites gsl
 }
 
-template <typename T, int LAYOUT, bool VEC>
+template <typename T, int LAYOUT, bool VEC, int DMAX>
 __global__ __launch_bounds__(64) void fctp_ps_bwd_kernel(const T* __restrict__ x1, const T* __restrict__ x2,
                                                          const T* __restrict__ w, const T* __restrict__ g,
                                                          T* __restrict__ dx1, T* __restrict__ dx2,
@@ -413,6 +413,7 @@ __global__ __launch_bounds__(64) void fctp_ps_bwd_kernel(const T* __restrict__ x
     const PsTile t = tiles[ti];
 #define SEGPOLY_PS_BWD_CASE(DD)                                                                                  \
   case DD:                                                                                                       \
+    if constexpr (DD <= DMAX)                                                                                    \
     ps_bwd_tile<T, LAYOUT, DD, VEC>(wr, dwr, want_dw, grow, xs1, xs2, gsl, Rs, dx1a, dx2a, want1, want2, t,      \
                                     paths, lists, ents, lane);                                                   \
     break;
@@ -435,19 +436,21 @@ __global__ __launch_bounds__(64) void fctp_ps_bwd_kernel(const T* __restrict__ x
     for (int64_t i = lane; i < dim2; i += 64) dx2[s * dim2 + i] = dx2a[i];
 }
 
-template <typename T, int LAYOUT>
+// The kernels are compiled for output blocks up to DMAX components (3, 7 or
+// 13): registers are allocated for the largest block a kernel handles.
+template <typename T, int LAYOUT, int DMAX>
 int ps_fwd_launch(const FcPsArgs& a) {
   const dim3 grid(static_cast<unsigned>(a.n), static_cast<unsigned>(a.n_tiles));
-  hipLaunchKernelGGL((fctp_ps_fwd_kernel<T, LAYOUT>), grid, dim3(64), a.lds_bytes, static_cast<hipStream_t>(a.stream),
+  hipLaunchKernelGGL((fctp_ps_fwd_kernel<T, LAYOUT, DMAX>), grid, dim3(64), a.lds_bytes, static_cast<hipStream_t>(a.stream),
                      static_cast<const T*>(a.x1), static_cast<const T*>(a.x2), static_cast<const T*>(a.w),
                      static_cast<T*>(a.out), a.dim1, a.dim2, a.dimo, a.numel, a.tiles, a.paths, a.lists, a.ents,
                      a.max_d);
   return static_cast<int>(hipGetLastError());
 }
 
-template <typename T, int LAYOUT, bool VEC>
+template <typename T, int LAYOUT, bool VEC, int DMAX>
 int ps_bwd_launch(const FcPsArgs& a) {
-  hipLaunchKernelGGL((fctp_ps_bwd_kernel<T, LAYOUT, VEC>), dim3(static_cast<unsigned>(a.n)), dim3(64), a.lds_bytes,
+  hipLaunchKernelGGL((fctp_ps_bwd_kernel<T, LAYOUT, VEC, DMAX>), dim3(static_cast<unsigned>(a.n)), dim3(64), a.lds_bytes,
                      static_cast<hipStream_t>(a.stream), static_cast<const T*>(a.x1), static_cast<const T*>(a.x2),
                      static_cast<const T*>(a.w), static_cast<const T*>(a.g), static_cast<T*>(a.dx1),
                      static_cast<T*>(a.dx2), static_cast<T*>(a.dw), a.dim1, a.dim2, a.dimo, a.numel, a.tiles,
@@ -455,15 +458,30 @@ int ps_bwd_launch(const FcPsArgs& a) {
   return static_cast<int>(hipGetLastError());
 }
 
+template <typename T, int DMAX>
+int ps_fwd_dispatch(const FcPsArgs& a) {
+  return a.layout == kIrMul ? ps_fwd_launch<T, kIrMul, DMAX>(a) : ps_fwd_launch<T, kMulIr, DMAX>(a);
+}
+
 template <typename T>
 int ps_fwd_dispatch(const FcPsArgs& a) {
-  return a.layout == kIrMul ? ps_fwd_launch<T, kIrMul>(a) : ps_fwd_launch<T, kMulIr>(a);
+  if (a.max_d <= 3) return ps_fwd_dispatch<T, 3>(a);
+  if (a.max_d <= 7) return ps_fwd_dispatch<T, 7>(a);
+  return ps_fwd_dispatch<T, kPsMaxD>(a);
+}
+
+template <typename T, int DMAX>
+int ps_bwd_dispatch(const FcPsArgs& a) {
+  if (a.vec)
+    return a.layout == kIrMul ? ps_bwd_launch<T, kIrMul, true, DMAX>(a) : ps_bwd_launch<T, kMulIr, true, DMAX>(a);
+  return a.layout == kIrMul ? ps_bwd_launch<T, kIrMul, false, DMAX>(a) : ps_bwd_launch<T, kMulIr, false, DMAX>(a);
 }
 
 template <typename T>
 int ps_bwd_dispatch(const FcPsArgs& a) {
-  if (a.vec) return a.layout == kIrMul ? ps_bwd_launch<T, kIrMul, true>(a) : ps_bwd_launch<T, kMulIr, true>(a);
-  return a.layout == kIrMul ? ps_bwd_launch<T, kIrMul, false>(a) : ps_bwd_launch<T, kMulIr, false>(a);
+  if (a.max_d <= 3) return ps_bwd_dispatch<T, 3>(a);
+  if (a.max_d <= 7) return ps_bwd_dispatch<T, 7>(a);
+  return ps_bwd_dispatch<T, kPsMaxD>(a);
 }
 
 }  // namespace
