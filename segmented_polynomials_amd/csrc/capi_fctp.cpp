@@ -430,6 +430,7 @@ void build_ps(segpoly_fctp* h) {
     for (const auto& pa : h->paths) {
       if (pa.o != static_cast<int>(o)) continue;
       const Irrep &a = h->in1[pa.i], &b = h->in2[pa.j];
+      if (a.mul == 0 || b.mul == 0) continue;  // no (u, v) pairs, no weights
       const int d1 = 2 * a.l + 1, d2 = 2 * b.l + 1;
       const std::vector<double>& C = real_cg(a.l, b.l, ob.l);
       std::vector<PsEnt> nz;
