@@ -208,8 +208,10 @@ tp_conv_kernel(const T* __restrict__ x, const T* __restrict__ sh, const T* __res
 //
 // Measured on the molecular batch and dropped: a range search seeded with
 // node * n_edges / n_nodes (its first probes are node-specific cache lines,
-// where the whole-range search shares its first rounds across nodes), and
-// finding the range end edge by edge from dst instead of searching it.
+// where the whole-range search shares its first rounds across nodes),
+// finding the range end edge by edge from dst instead of searching it, and
+// a search by all four waves together (256 probes per round through LDS
+// counts and barriers: two dependent loads instead of four, 9.8 -> 10.1 us).
 constexpr int kSplitThreads = 256;
 
 template <class S, typename T, typename Index, int LAYOUT, int GW, bool SHV = false>
