@@ -259,6 +259,26 @@ def main():
                                       "two_call_ms": sum(pers) / len(pers) + avg_kernel_ms}
         del shbuf
 
+        # one GPU's share of an eight-way destination split: the first eighth
+        # of the destinations with their edges (dst-sorted: one contiguous
+        # edge range) and the whole source table, as each GPU would run it
+        # after the all-gather of x; algorithmic bytes count the source rows
+        # its edges read once each
+        n8 = N // 8
+        e8 = int((dst < n8).sum().item())
+        out8 = out[:n8]
+        f8 = lambda: sp.tp_conv_fwd(h, x, sh[:e8], w[:e8], src[:e8], dst[:e8], n_nodes=n8, out=out8)
+        wall8, per8 = time_launches(torch, f8, args.steps, args.warmup)
+        k8 = sum(per8) / len(per8)
+        rows8 = int(torch.unique(src[:e8]).numel())
+        b8 = e8 * (h.weight_numel + h.dim_in2 + 2) * 4 + rows8 * h.dim_in1 * 4 + n8 * h.dim_out * 4
+        result["shard_one_of_eight"] = {"what": "destinations [0, N/8) and their edges, whole source table",
+                                        "nodes": n8, "edges": e8, "source_rows_read": rows8, "kernel_ms": k8,
+                                        "edges_per_s": e8 / (wall8 / args.steps),
+                                        "hbm_GBps_algorithmic": b8 / (k8 * 1e-3) / 1e9,
+                                        "hbm_fraction_of_peak": b8 / (k8 * 1e-3) / 1e9 / HBM_PEAK_GBPS}
+        note("one-eighth shard timed")
+
         # practical ceiling: a plain device copy of the weight tensor (4 GB read + 4 GB written)
         wc = torch.empty_like(w)
         cwall, cper = time_launches(torch, lambda: wc.copy_(w), max(5, args.steps // 4), 2)
