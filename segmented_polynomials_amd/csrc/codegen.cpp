@@ -340,64 +340,96 @@ void emit_symcon(const std::string& name, unsigned dtypes, const SymconDescripto
   std::map<std::tuple<int, int, int>, std::vector<std::tuple<int, int, double>>> mono;
   for (int s = 0; s < ns; ++s)
     for (const auto& t : d.couplings[s].terms) mono[{t.m[0], t.m[1], t.m[2]}].push_back({s, t.M, t.c});
-  std::set<std::pair<int, int>> used_acc;
+  // Forward, per atom and channel, with the degree-3 terms factored by
+  // their first (smallest) component index a:
+  //   o[og] += v[a] * sum over segments s into og of wv[s] * T_{s,M,a},
+  //   T_{s,M,a} = sum over the terms (a, b, c) of (s, M) of c * q_bc,
+  // q_bc = v[b] v[c] formed once, before its first use (a ascending).  Per
+  // atom-channel this takes one multiply per distinct pair, one operation per
+  // term and one per (s, M, a) and per (og, a) group, against one multiply
+  // per distinct monomial plus one operation per term plus one per segment
+  // when every monomial is formed and each segment's sum is weighted at the
+  // end (the l <= 3 -> l <= 1 contraction: 854 against 1,089 operations).
+  // Degrees 1 and 2: o[og] += wv[s] * (sum of c * v[a] or c * q_ab).
   std::ostringstream body;
-  auto accum = [&](const std::string& m, const std::vector<std::tuple<int, int, double>>& terms) {
-    for (const auto& [s, M, c] : terms) {
-      const std::string a = "a" + std::to_string(s) + "_" + std::to_string(M);
-      if (!used_acc.count({s, M})) {
-        used_acc.insert({s, M});
-        body << "    T " << a << " = " << lit(c) << " * " << m << ";\n";
+  {
+    std::set<std::pair<int, int>> have_q;
+    std::set<int> started;
+    auto q = [&](int b, int c) {
+      const std::string nm = "q" + std::to_string(b) + "_" + std::to_string(c);
+      if (!have_q.count({b, c})) {
+        have_q.insert({b, c});
+        body << "    const T " << nm << " = v[" << b << "] * v[" << c << "];\n";
+      }
+      return nm;
+    };
+    auto acc_o = [&](int og, const std::string& f, const std::string& t) {
+      if (started.count(og)) {
+        body << "    o[" << og << "] = fmadd(" << f << ", " << t << ", o[" << og << "]);\n";
       } else {
-        body << "    " << a << " = fmadd(" << lit(c) << ", " << m << ", " << a << ");\n";
+        started.insert(og);
+        body << "    o[" << og << "] = " << f << " * " << t << ";\n";
       }
-    }
-  };
-  // degree 1
-  for (int a = 0; a < n; ++a) {
-    auto it = mono.find({a, -1, -1});
-    if (it != mono.end()) accum("v[" + std::to_string(a) + "]", it->second);
-  }
-  // degrees 2 and 3, grouped by the sorted prefix (a, b)
-  for (int a = 0; a < n; ++a)
-    for (int b = a; b < n; ++b) {
-      bool need = mono.count({a, b, -1}) > 0;
-      for (int c = b; c < n && !need; ++c) need = mono.count({a, b, c}) > 0;
-      if (!need) continue;
-      const std::string p = "p" + std::to_string(a) + "_" + std::to_string(b);
-      body << "    const T " << p << " = v[" << a << "] * v[" << b << "];\n";
-      auto it = mono.find({a, b, -1});
-      if (it != mono.end()) accum(p, it->second);
-      for (int c = b; c < n; ++c) {
-        auto jt = mono.find({a, b, c});
-        if (jt == mono.end()) continue;
-        const std::string m = "m" + std::to_string(a) + "_" + std::to_string(b) + "_" + std::to_string(c);
-        body << "    const T " << m << " = " << p << " * v[" << c << "];\n";
-        accum(m, jt->second);
-      }
-    }
-  // outputs
-  for (size_t ob = 0; ob < d.out.size(); ++ob) {
-    const int dL = 2 * d.out[ob].l + 1;
-    for (int M = 0; M < dL; ++M) {
-      const int og = d.out_comp[ob] + M;
-      bool first = true;
-      for (int s = 0; s < ns; ++s) {
-        if (d.couplings[s].ob != static_cast<int>(ob) || !used_acc.count({s, M})) continue;
-        const std::string a = "a" + std::to_string(s) + "_" + std::to_string(M);
-        if (first)
-          body << "    o[" << og << "] = wv[" << s << "] * " << a << ";\n";
+    };
+    auto og_of = [&](int sg, int M) { return d.out_comp[d.couplings[sg].ob] + M; };
+    // degrees 1 and 2, per (segment, component)
+    std::map<std::pair<int, int>, std::vector<std::tuple<double, int, int>>> low;
+    // degree 3: a -> (og, segment) -> [(c, b, cc)]
+    std::map<int, std::map<std::pair<int, int>, std::vector<std::tuple<double, int, int>>>> hi3;
+    for (int sg = 0; sg < ns; ++sg)
+      for (const auto& t : d.couplings[sg].terms) {
+        if (t.m[2] >= 0)
+          hi3[t.m[0]][{og_of(sg, t.M), sg}].push_back({t.c, t.m[1], t.m[2]});
         else
-          body << "    o[" << og << "] = fmadd(wv[" << s << "], " << a << ", o[" << og << "]);\n";
+          low[{sg, t.M}].push_back({t.c, t.m[0], t.m[1]});
+      }
+    for (const auto& [key, lst] : low) {
+      const std::string tn = "t" + std::to_string(key.first) + "_" + std::to_string(key.second);
+      bool first = true;
+      for (const auto& [c, a, b] : lst) {
+        const std::string x = b < 0 ? "v[" + std::to_string(a) + "]" : q(a, b);
+        if (first)
+          body << "    T " << tn << " = " << lit(c) << " * " << x << ";\n";
+        else
+          body << "    " << tn << " = fmadd(" << lit(c) << ", " << x << ", " << tn << ");\n";
         first = false;
       }
-      if (first) body << "    o[" << og << "] = T(0);\n";
+      acc_o(og_of(key.first, key.second), "wv[" + std::to_string(key.first) + "]", tn);
     }
+    for (const auto& [a, groups] : hi3) {
+      std::map<int, std::vector<int>> segs_of_og;  // og -> segments, in order
+      for (const auto& [key, lst] : groups) segs_of_og[key.first].push_back(key.second);
+      for (const auto& [og, segs] : segs_of_og) {
+        const std::string un = "u" + std::to_string(a) + "_" + std::to_string(og);
+        bool first_u = true;
+        for (int sg : segs) {
+          const auto& lst = groups.at({og, sg});
+          const std::string tn = "r" + std::to_string(a) + "_" + std::to_string(og) + "_" + std::to_string(sg);
+          bool first = true;
+          for (const auto& [c, b, cc] : lst) {
+            const std::string x = q(b, cc);
+            if (first)
+              body << "    T " << tn << " = " << lit(c) << " * " << x << ";\n";
+            else
+              body << "    " << tn << " = fmadd(" << lit(c) << ", " << x << ", " << tn << ");\n";
+            first = false;
+          }
+          if (first_u)
+            body << "    T " << un << " = wv[" << sg << "] * " << tn << ";\n";
+          else
+            body << "    " << un << " = fmadd(wv[" << sg << "], " << tn << ", " << un << ");\n";
+          first_u = false;
+        }
+        acc_o(og, "v[" + std::to_string(a) + "]", un);
+      }
+    }
+    for (int og = 0; og < d.nout; ++og)
+      if (!started.count(og)) body << "    o[" << og << "] = T(0);\n";
   }
 
   // backward, per atom and channel, in two functions (fewer live registers):
-  // bwd_w: the forward accumulators a_{s,M} (same code as above), then
-  //    dw[s] += g[M] a_{s,M};
+  // bwd_w: dw[s] += sum over M of g[M] a_{s,M}, a_{s,M} the segment sums of
+  //    the forward, evaluated in the forward's factored form (as above);
   // bwd_x: gw_{s,M} = w[s] g[M]; per monomial B = sum of c gw over its terms;
   //    dx by the product rule, grouped by the sorted prefix (a, b):
   //    S_ab = B_ab + sum_c B_abc v[c], dx[c] += B_abc v[a] v[b],
@@ -405,43 +437,74 @@ void emit_symcon(const std::string& name, unsigned dtypes, const SymconDescripto
   std::ostringstream bwd;
   std::string bwd_w, bwd_x;
   {
-    std::set<std::pair<int, int>> used1;
-    auto acc1 = [&](const std::string& m, const std::vector<std::tuple<int, int, double>>& terms) {
-      for (const auto& [sg, M, c] : terms) {
-        const std::string a = "a" + std::to_string(sg) + "_" + std::to_string(M);
-        if (!used1.count({sg, M})) {
-          used1.insert({sg, M});
-          bwd << "      T " << a << " = " << lit(c) << " * " << m << ";\n";
-        } else {
-          bwd << "      " << a << " = fmadd(" << lit(c) << ", " << m << ", " << a << ");\n";
-        }
+    std::set<std::pair<int, int>> used1;  // (segment, component) pairs with terms
+    for (int sg = 0; sg < ns; ++sg)
+      for (const auto& t : d.couplings[sg].terms) used1.insert({sg, t.M});
+    auto og_of = [&](int sg, int M) { return d.out_comp[d.couplings[sg].ob] + M; };
+    // bwd_w, factored like the forward, with the output gradient in the
+    // place of the weights: dw[s] += g[og] * (degree-1 and -2 sums), and
+    // per first index a, dw[s] += v[a] * sum over M of g[og] * T_{s,M,a}
+    std::set<std::pair<int, int>> have_q;
+    auto q = [&](int b, int c) {
+      const std::string nm = "q" + std::to_string(b) + "_" + std::to_string(c);
+      if (!have_q.count({b, c})) {
+        have_q.insert({b, c});
+        bwd << "      const T " << nm << " = v[" << b << "] * v[" << c << "];\n";
       }
+      return nm;
     };
-    bwd << "    {\n";
-    for (int a = 0; a < n; ++a) {
-      auto it = mono.find({a, -1, -1});
-      if (it != mono.end()) acc1("v[" + std::to_string(a) + "]", it->second);
-    }
-    for (int a = 0; a < n; ++a)
-      for (int b = a; b < n; ++b) {
-        bool need = mono.count({a, b, -1}) > 0;
-        for (int c = b; c < n && !need; ++c) need = mono.count({a, b, c}) > 0;
-        if (!need) continue;
-        const std::string p = "p" + std::to_string(a) + "_" + std::to_string(b);
-        bwd << "      const T " << p << " = v[" << a << "] * v[" << b << "];\n";
-        auto it = mono.find({a, b, -1});
-        if (it != mono.end()) acc1(p, it->second);
-        for (int c = b; c < n; ++c) {
-          auto jt = mono.find({a, b, c});
-          if (jt == mono.end()) continue;
-          const std::string m = "m" + std::to_string(a) + "_" + std::to_string(b) + "_" + std::to_string(c);
-          bwd << "      const T " << m << " = " << p << " * v[" << c << "];\n";
-          acc1(m, jt->second);
-        }
+    std::map<std::pair<int, int>, std::vector<std::tuple<double, int, int>>> low;
+    // a -> (segment, M) -> [(c, b, cc)]
+    std::map<int, std::map<std::pair<int, int>, std::vector<std::tuple<double, int, int>>>> hi3;
+    for (int sg = 0; sg < ns; ++sg)
+      for (const auto& t : d.couplings[sg].terms) {
+        if (t.m[2] >= 0)
+          hi3[t.m[0]][{sg, t.M}].push_back({t.c, t.m[1], t.m[2]});
+        else
+          low[{sg, t.M}].push_back({t.c, t.m[0], t.m[1]});
       }
-    for (const auto& [sg, M] : used1) {
-      const int og = d.out_comp[d.couplings[sg].ob] + M;
-      bwd << "      dw[" << sg << "] = fmadd(g[" << og << "], a" << sg << "_" << M << ", dw[" << sg << "]);\n";
+    bwd << "    {\n";
+    for (const auto& [key, lst] : low) {
+      const std::string tn = "t" + std::to_string(key.first) + "_" + std::to_string(key.second);
+      bool first = true;
+      for (const auto& [c, a, b] : lst) {
+        const std::string x = b < 0 ? "v[" + std::to_string(a) + "]" : q(a, b);
+        if (first)
+          bwd << "      T " << tn << " = " << lit(c) << " * " << x << ";\n";
+        else
+          bwd << "      " << tn << " = fmadd(" << lit(c) << ", " << x << ", " << tn << ");\n";
+        first = false;
+      }
+      bwd << "      dw[" << key.first << "] = fmadd(g[" << og_of(key.first, key.second) << "], " << tn << ", dw["
+          << key.first << "]);\n";
+    }
+    for (const auto& [a, groups] : hi3) {
+      std::map<int, std::vector<int>> comps_of_seg;  // segment -> components, in order
+      for (const auto& [key, lst] : groups) comps_of_seg[key.first].push_back(key.second);
+      for (const auto& [sg, comps] : comps_of_seg) {
+        const std::string un = "u" + std::to_string(a) + "_" + std::to_string(sg);
+        bool first_u = true;
+        for (int M : comps) {
+          const auto& lst = groups.at({sg, M});
+          const std::string tn = "r" + std::to_string(a) + "_" + std::to_string(sg) + "_" + std::to_string(M);
+          bool first = true;
+          for (const auto& [c, b, cc] : lst) {
+            const std::string x = q(b, cc);
+            if (first)
+              bwd << "      T " << tn << " = " << lit(c) << " * " << x << ";\n";
+            else
+              bwd << "      " << tn << " = fmadd(" << lit(c) << ", " << x << ", " << tn << ");\n";
+            first = false;
+          }
+          const std::string gg = "g[" + std::to_string(og_of(sg, M)) + "]";
+          if (first_u)
+            bwd << "      T " << un << " = " << gg << " * " << tn << ";\n";
+          else
+            bwd << "      " << un << " = fmadd(" << gg << ", " << tn << ", " << un << ");\n";
+          first_u = false;
+        }
+        bwd << "      dw[" << sg << "] = fmadd(v[" << a << "], " << un << ", dw[" << sg << "]);\n";
+      }
     }
     bwd << "    }\n";
     bwd_w = bwd.str();
