@@ -571,7 +571,12 @@ int symcon_create(const char* s_in, const char* s_out, int max_degree, int num_e
   h->flags = flags;
   h->num_elements = num_elements;
   const unsigned bit = dtype == SEGPOLY_F32 ? 1u : 2u;
-  if (!(flags & SEGPOLY_FORCE_GENERIC))
+  // the specialised forward addresses one atom's rows (x, w, out) through
+  // 32-bit buffer offsets: rows below 2 GiB
+  const int64_t widest = std::max<int64_t>({static_cast<int64_t>(h->d.n), static_cast<int64_t>(h->d.nout),
+                                            static_cast<int64_t>(h->d.couplings.size())});
+  const bool rows_fit = static_cast<int64_t>(h->d.mul) * widest * (dtype == SEGPOLY_F32 ? 4 : 8) <= 0x7fffffff;
+  if (!(flags & SEGPOLY_FORCE_GENERIC) && rows_fit)
     for (int i = 0; i < kNumSymconSpecs; ++i)
       if ((kSymconSpecs[i].dtypes & bit) && h->d.key == kSymconSpecs[i].key) {
         h->spec = &kSymconSpecs[i];

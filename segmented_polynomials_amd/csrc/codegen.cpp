@@ -581,6 +581,22 @@ void emit_symcon(const std::string& name, unsigned dtypes, const SymconDescripto
     os << "      }\n";
   }
   os << "    }\n  }\n\n";
+  // the same load through a buffer resource based at the row: the lane's
+  // offset is one register per block width, the component offsets are
+  // wave-uniform (scalar) operands, so no per-load address arithmetic
+  os << "  template <typename T, int LAYOUT>\n  __device__ __forceinline__ static void load_v_b(__amdgpu_buffer_rsrc_t r, int mul, int u, T* v) {\n";
+  os << "    constexpr uint32_t E = sizeof(T);\n    const uint32_t m = static_cast<uint32_t>(mul);\n";
+  os << "    if constexpr (LAYOUT == kIrMul) {\n      const uint32_t vo = static_cast<uint32_t>(u) * E;\n";
+  for (int m = 0; m < n; ++m) os << "      v[" << m << "] = buf_load_s<T>(r, vo, " << m << "u * m * E);\n";
+  os << "    } else {\n";
+  for (size_t b = 0; b < d.in.size(); ++b) {
+    const int dl = 2 * d.in[b].l + 1, comp = d.in_comp[b];
+    os << "      {\n        const uint32_t vo = static_cast<uint32_t>(u) * " << dl << "u * E;\n";
+    for (int i = 0; i < dl; ++i)
+      os << "        v[" << comp + i << "] = buf_load_s<T>(r, vo, (" << comp << "u * m + " << i << "u) * E);\n";
+    os << "      }\n";
+  }
+  os << "    }\n  }\n\n";
   // gradient-row load (output layout) and input-gradient store (input layout)
   os << "  template <typename T, int LAYOUT>\n  __device__ __forceinline__ static void load_o(const T* __restrict__ row, int mul, int u, T* o) {\n";
   os << "    if constexpr (LAYOUT == kIrMul) {\n";
@@ -615,6 +631,19 @@ void emit_symcon(const std::string& name, unsigned dtypes, const SymconDescripto
   os << "  template <typename T>\n  __device__ __forceinline__ static void eval(const T* v, const T* wv, T* o) {\n";
   os << body.str();
   os << "  }\n\n";
+  os << "  template <typename T, int LAYOUT>\n  __device__ __forceinline__ static void store_b(__amdgpu_buffer_rsrc_t r, int mul, int u, const T* o) {\n";
+  os << "    constexpr uint32_t E = sizeof(T);\n    const uint32_t m = static_cast<uint32_t>(mul);\n";
+  os << "    if constexpr (LAYOUT == kIrMul) {\n      const uint32_t vo = static_cast<uint32_t>(u) * E;\n";
+  for (int k = 0; k < d.nout; ++k) os << "      buf_store_s<T>(r, vo, " << k << "u * m * E, o[" << k << "]);\n";
+  os << "    } else {\n";
+  for (size_t b = 0; b < d.out.size(); ++b) {
+    const int dl = 2 * d.out[b].l + 1, comp = d.out_comp[b];
+    os << "      {\n        const uint32_t vo = static_cast<uint32_t>(u) * " << dl << "u * E;\n";
+    for (int i = 0; i < dl; ++i)
+      os << "        buf_store_s<T>(r, vo, (" << comp << "u * m + " << i << "u) * E, o[" << comp + i << "]);\n";
+    os << "      }\n";
+  }
+  os << "    }\n  }\n\n";
   os << "  template <typename T, int LAYOUT>\n  __device__ __forceinline__ static void store(T* __restrict__ row, int mul, int u, const T* o) {\n";
   os << "    if constexpr (LAYOUT == kIrMul) {\n";
   for (int k = 0; k < d.nout; ++k) os << "      row[" << k << " * mul + u] = o[" << k << "];\n";

@@ -36,5 +36,37 @@ __device__ __forceinline__ double buf_load<double>(__amdgpu_buffer_rsrc_t r, uin
   return __builtin_bit_cast(double, __builtin_amdgcn_raw_buffer_load_b64(r, byte_off, 0, 0));
 }
 
+// Loads and stores with a lane offset `voff` and a wave-uniform offset
+// `soff` (a scalar operand of the instruction): an element of component c
+// of a channel-major row is (u, c * mul), with u per lane and c * mul the
+// same for every lane.  A store at an offset past the range is dropped.
+template <typename T>
+__device__ __forceinline__ T buf_load_s(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff);
+
+template <>
+__device__ __forceinline__ float buf_load_s<float>(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
+}
+
+template <>
+__device__ __forceinline__ double buf_load_s<double>(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(double, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0));
+}
+
+template <typename T>
+__device__ __forceinline__ void buf_store_s(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, T v);
+
+template <>
+__device__ __forceinline__ void buf_store_s<float>(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, float v) {
+  __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, v), r, voff, soff, 0);
+}
+
+template <>
+__device__ __forceinline__ void buf_store_s<double>(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff,
+                                                    double v) {
+  __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(__attribute__((ext_vector_type(2))) unsigned, v), r,
+                                        voff, soff, 0);
+}
+
 }  // namespace kern
 }  // namespace segpoly

@@ -24,6 +24,7 @@
 #include <cstdint>
 
 #include "../launch.hpp"
+#include "bufload.hpp"
 #include "common.hpp"
 
 namespace segpoly {
@@ -40,9 +41,14 @@ symcon_spec_kernel(const T* __restrict__ x, const Index* __restrict__ species,
   const int tile0 = blockIdx.y * (kSymconWave * CPL);
   const int64_t sp = static_cast<int64_t>(species[atom]);
   const bool valid = sp >= 0 && sp < num_elements;  // out-of-range element: zero row
-  const T* xrow = x + atom * (static_cast<int64_t>(mul) * S::NV);
-  const T* wrow = w + (valid ? sp : 0) * (static_cast<int64_t>(mul) * S::NS);
-  T* orow = out + atom * (static_cast<int64_t>(mul) * S::NO);
+  // the atom's rows as buffer resources: per element the lane's offset is a
+  // register and the component's offset a scalar, so the loads and stores
+  // need no per-element address arithmetic (rows stay below 2 GiB: the
+  // host uses this kernel only then)
+  const int64_t m = mul;
+  const __amdgpu_buffer_rsrc_t xr = buf_rsrc(x + atom * (m * S::NV), m * S::NV * sizeof(T));
+  const __amdgpu_buffer_rsrc_t wr = buf_rsrc(w + (valid ? sp : 0) * (m * S::NS), m * S::NS * sizeof(T));
+  const __amdgpu_buffer_rsrc_t orr = buf_rsrc(out + atom * (m * S::NO), m * S::NO * sizeof(T));
 #pragma unroll
   for (int c = 0; c < CPL; ++c) {
     const int u = tile0 + c * kSymconWave + lane;
@@ -51,15 +57,16 @@ symcon_spec_kernel(const T* __restrict__ x, const Index* __restrict__ species,
       if (valid) {
         T v[S::NV];
         T wv[S::NS];
-        S::template load_v<T, LAYOUT>(xrow, mul, u, v);
+        S::template load_v_b<T, LAYOUT>(xr, mul, u, v);
 #pragma unroll
-        for (int s = 0; s < S::NS; ++s) wv[s] = wrow[s * mul + u];
+        for (int s = 0; s < S::NS; ++s)
+          wv[s] = buf_load_s<T>(wr, static_cast<uint32_t>(u) * sizeof(T), static_cast<uint32_t>(s * mul) * sizeof(T));
         S::template eval<T>(v, wv, o);
       } else {
 #pragma unroll
         for (int k = 0; k < S::NO; ++k) o[k] = T(0);
       }
-      S::template store<T, LAYOUT>(orow, mul, u, o);
+      S::template store_b<T, LAYOUT>(orr, mul, u, o);
     }
   }
 }
