@@ -581,6 +581,39 @@ void emit_symcon(const std::string& name, unsigned dtypes, const SymconDescripto
     os << "      }\n";
   }
   os << "    }\n  }\n\n";
+  // buffer-resource forms of the row accesses: load_v_b (input row),
+  // load_o_b (output-gradient row), store_v_b (input-gradient row), store_b
+  // (output row)
+  auto emit_buf = [&](const char* fname, bool store, const char* arr, const std::vector<Irrep>& blocks,
+                      const std::vector<int>& comps, int count) {
+    os << "  template <typename T, int LAYOUT>\n  __device__ __forceinline__ static void " << fname
+       << "(__amdgpu_buffer_rsrc_t r, int mul, int u, " << (store ? "const T* " : "T* ") << arr << ") {\n";
+    os << "    constexpr uint32_t E = sizeof(T);\n    const uint32_t m = static_cast<uint32_t>(mul);\n";
+    os << "    if constexpr (LAYOUT == kIrMul) {\n      const uint32_t vo = static_cast<uint32_t>(u) * E;\n";
+    for (int k = 0; k < count; ++k) {
+      if (store)
+        os << "      buf_store_s<T>(r, vo, " << k << "u * m * E, " << arr << "[" << k << "]);\n";
+      else
+        os << "      " << arr << "[" << k << "] = buf_load_s<T>(r, vo, " << k << "u * m * E);\n";
+    }
+    os << "    } else {\n";
+    for (size_t b = 0; b < blocks.size(); ++b) {
+      const int dl = 2 * blocks[b].l + 1, comp = comps[b];
+      os << "      {\n        const uint32_t vo = static_cast<uint32_t>(u) * " << dl << "u * E;\n";
+      for (int i = 0; i < dl; ++i) {
+        if (store)
+          os << "        buf_store_s<T>(r, vo, (" << comp << "u * m + " << i << "u) * E, " << arr << "[" << comp + i
+             << "]);\n";
+        else
+          os << "        " << arr << "[" << comp + i << "] = buf_load_s<T>(r, vo, (" << comp << "u * m + " << i
+             << "u) * E);\n";
+      }
+      os << "      }\n";
+    }
+    os << "    }\n  }\n\n";
+  };
+  emit_buf("load_o_b", false, "o", d.out, d.out_comp, d.nout);
+  emit_buf("store_v_b", true, "v", d.in, d.in_comp, n);
   // the same load through a buffer resource based at the row: the lane's
   // offset is one register per block width, the component offsets are
   // wave-uniform (scalar) operands, so no per-load address arithmetic

@@ -37,6 +37,7 @@
 #include <cstdint>
 
 #include "../launch.hpp"
+#include "bufload.hpp"
 #include "common.hpp"
 #include "tp_conv_spec.hpp"
 
@@ -129,10 +130,22 @@ symcon_bwd_kernel(const T* __restrict__ x, const Index* __restrict__ perm, const
   auto atom = [&](int64_t i) -> int64_t { return static_cast<int64_t>(perm[i]); };
   auto ok = [&](int64_t a) { return a >= 0 && a < n_atoms; };  // false only for an invalid perm
   T vn[S::NV], gn[S::NO];
+  // ir_mul rows through buffer resources (lane offset in a register,
+  // component offsets as scalar operands: no per-element address
+  // arithmetic); mul_ir rows hold a channel's components of a block
+  // contiguously, so plain pointers need one address per block and the
+  // block's elements load as one vector
   auto load = [&](int64_t a) {
     const int64_t ac = ok(a) ? a : 0;
-    S::template load_v<T, LAYOUT>(x + ac * dim_in, mul, ul, vn);
-    S::template load_o<T, LAYOUT>(g + ac * dim_out, mul, ul, gn);
+    if constexpr (LAYOUT == kIrMul) {
+      S::template load_v_b<T, LAYOUT>(buf_rsrc(x + ac * dim_in, dim_in * static_cast<int64_t>(sizeof(T))), mul, ul,
+                                      vn);
+      S::template load_o_b<T, LAYOUT>(buf_rsrc(g + ac * dim_out, dim_out * static_cast<int64_t>(sizeof(T))), mul,
+                                      ul, gn);
+    } else {
+      S::template load_v<T, LAYOUT>(x + ac * dim_in, mul, ul, vn);
+      S::template load_o<T, LAYOUT>(g + ac * dim_out, mul, ul, gn);
+    }
   };
   int64_t a_next = i0 < i1 ? atom(i0) : 0;
   if (valid && i0 < i1) load(a_next);
@@ -159,7 +172,13 @@ symcon_bwd_kernel(const T* __restrict__ x, const Index* __restrict__ perm, const
       for (int m = 0; m < S::NV; ++m) dv[m] = T(0);
     }
     if constexpr ((WHICH & 2) != 0)
-      if (active && ok(a)) S::template store_v<T, LAYOUT>(dx + a * dim_in, mul, u, dv);
+      if (active && ok(a)) {
+        if constexpr (LAYOUT == kIrMul)
+          S::template store_v_b<T, LAYOUT>(buf_rsrc(dx + a * dim_in, dim_in * static_cast<int64_t>(sizeof(T))), mul,
+                                           u, dv);
+        else
+          S::template store_v<T, LAYOUT>(dx + a * dim_in, mul, u, dv);
+      }
   }
   if ((WHICH & 1) != 0 && valid && active) {
     T* prow = part + t * numel;

@@ -42,13 +42,17 @@ symcon_spec_kernel(const T* __restrict__ x, const Index* __restrict__ species,
   const int64_t sp = static_cast<int64_t>(species[atom]);
   const bool valid = sp >= 0 && sp < num_elements;  // out-of-range element: zero row
   // the atom's rows as buffer resources: per element the lane's offset is a
-  // register and the component's offset a scalar, so the loads and stores
-  // need no per-element address arithmetic (rows stay below 2 GiB: the
-  // host uses this kernel only then)
+  // register and the component's offset a scalar, so the ir_mul loads and
+  // stores and the weight loads need no per-element address arithmetic
+  // (rows stay below 2 GiB: the host uses this kernel only then); mul_ir
+  // rows hold a channel's components of a block contiguously, so plain
+  // pointers need one address per block and load the block as one vector
   const int64_t m = mul;
-  const __amdgpu_buffer_rsrc_t xr = buf_rsrc(x + atom * (m * S::NV), m * S::NV * sizeof(T));
+  const T* xrow = x + atom * (m * S::NV);
+  T* orow = out + atom * (m * S::NO);
+  const __amdgpu_buffer_rsrc_t xr = buf_rsrc(xrow, m * S::NV * sizeof(T));
   const __amdgpu_buffer_rsrc_t wr = buf_rsrc(w + (valid ? sp : 0) * (m * S::NS), m * S::NS * sizeof(T));
-  const __amdgpu_buffer_rsrc_t orr = buf_rsrc(out + atom * (m * S::NO), m * S::NO * sizeof(T));
+  const __amdgpu_buffer_rsrc_t orr = buf_rsrc(orow, m * S::NO * sizeof(T));
 #pragma unroll
   for (int c = 0; c < CPL; ++c) {
     const int u = tile0 + c * kSymconWave + lane;
@@ -57,7 +61,10 @@ symcon_spec_kernel(const T* __restrict__ x, const Index* __restrict__ species,
       if (valid) {
         T v[S::NV];
         T wv[S::NS];
-        S::template load_v_b<T, LAYOUT>(xr, mul, u, v);
+        if constexpr (LAYOUT == kIrMul)
+          S::template load_v_b<T, LAYOUT>(xr, mul, u, v);
+        else
+          S::template load_v<T, LAYOUT>(xrow, mul, u, v);
 #pragma unroll
         for (int s = 0; s < S::NS; ++s)
           wv[s] = buf_load_s<T>(wr, static_cast<uint32_t>(u) * sizeof(T), static_cast<uint32_t>(s * mul) * sizeof(T));
@@ -66,7 +73,10 @@ symcon_spec_kernel(const T* __restrict__ x, const Index* __restrict__ species,
 #pragma unroll
         for (int k = 0; k < S::NO; ++k) o[k] = T(0);
       }
-      S::template store_b<T, LAYOUT>(orr, mul, u, o);
+      if constexpr (LAYOUT == kIrMul)
+        S::template store_b<T, LAYOUT>(orr, mul, u, o);
+      else
+        S::template store<T, LAYOUT>(orow, mul, u, o);
     }
   }
 }
