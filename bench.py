@@ -337,9 +337,9 @@ def main():
                     "frac": s_bytes / (k3 * 1e-3) / 1e9 / HBM_PEAK_GBPS, "algorithmic_bytes": s_bytes},
             "alu": {"achieved": s_flops / (k3 * 1e-3) / 1e12, "peak": FP32_PUBLISHED_TFLOPS, "unit": "TFLOP/s",
                     "frac": s_flops / (k3 * 1e-3) / 1e12 / FP32_PUBLISHED_TFLOPS, "algorithmic_flops": s_flops,
-                    "peak_kind": "published MI355X FP32 vector figure; the kernel issues 0.36 wave64 VALU "
-                                 "instructions per SIMD-cycle (counters), above what a 16-lane derivation "
-                                 "(78.6 TFLOP/s) would allow",
+                    "peak_kind": "published MI355X FP32 vector figure; plain FP32 issues faster than a "
+                                 "16-lane derivation (78.6 TFLOP/s) assumes: the counters show up to 0.36 "
+                                 "wave64 VALU instructions per SIMD-cycle against its 0.25",
                     "frac_of_16_lane_derivation": s_flops / (k3 * 1e-3) / 1e12 / FP32_VALU_PEAK_TFLOPS},
         }
         # backward of the symmetric contraction on the same atoms
