@@ -142,6 +142,15 @@ def test_symcon_workload5_specialized():
     assert h.specialized
     assert h.weight_numel == 3712 and h.num_couplings == 29
     assert h.num_terms == 550
+    # the specialised kernel addresses an atom's rows with 32-bit buffer
+    # offsets: a row of 2 GiB or more (here 20M channels x 29 weights x 4 B)
+    # takes the table-driven kernel
+    m = 20_000_000
+    big = sp.symcon_create(f"{m}x0e+{m}x1o+{m}x2e+{m}x3o", f"{m}x0e+{m}x1o", 3, wl.num_elements, layout="ir_mul")
+    assert not big.specialized
+    m = 4_000_000  # 4M x 29 x 4 B < 2 GiB
+    ok = sp.symcon_create(f"{m}x0e+{m}x1o+{m}x2e+{m}x3o", f"{m}x0e+{m}x1o", 3, wl.num_elements, layout="ir_mul")
+    assert ok.specialized
 
 
 # ---------------------------------------------------------------- errors
