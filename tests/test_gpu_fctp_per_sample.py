@@ -44,6 +44,9 @@ CASES = [
     ("1x4e", "2x4e", "1x3e+1x4e", 6),                                # many couplings per component
     ("70x0e+5x1o", "2x0e", "3x0e+1x1o", 13),                         # three ragged chunks of pairs
     ("5x1o", "1x1o", "1x0e+1x1e+1x2e", 1),                           # one sample
+    ("2x3o", "1x3o", "3x6e", 7),                                     # l = 6 outputs (13 components)
+    ("3x2e", "2x4e", "2x6e+1x4e", 5),                                # 13 and 9 components
+    ("2x3o", "1x3e", "2x5o+1x4o", 4),                                # 11 components
 ]
 
 
