@@ -182,3 +182,42 @@ def test_full_size_workload_sampled():
         a = f.vjp(*s[:2], None, g[rows], layout=lay, absolute=True, edge_weights=s[2])
         for got, ref, sc, name in zip((g1, g2, gw), r, a, ("dx1", "dx2", "dw")):
             check_scaled(got[rows], ref, sc, "f32", f"{lay} {name} rows")
+
+
+def _random_irreps(rng, max_blocks, max_mul, max_l):
+    blocks = []
+    for _ in range(rng.integers(1, max_blocks + 1)):
+        l = int(rng.integers(0, max_l + 1))
+        p = "eo"[int(rng.integers(0, 2))]
+        blocks.append(f"{int(rng.integers(1, max_mul + 1))}x{l}{p}")
+    return "+".join(blocks)
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_descriptors(seed):
+    """Seeded random descriptors (up to three blocks per operand, l <= 3,
+    1..20 channels, either parity), both layouts, float32: the per-sample
+    tables for shapes no hand-picked case covers."""
+    sp = _sp()
+    import torch
+    rng = np.random.default_rng(100 + seed)
+    while True:
+        i1, i2, io = (_random_irreps(rng, 3, 20, 3) for _ in range(3))
+        f = ofc.FullyConnectedTP(i1, i2, io)
+        if f.weight_numel > 0:
+            break
+    n = int(rng.integers(1, 40))
+    x1, x2, w, g = _inputs(f, n, "f32", seed=seed)
+    X1, X2, W, G = dev(x1), dev(x2), dev(w), dev(g)
+    for lay in ("mul_ir", "ir_mul"):
+        h = sp.fctp_create(i1, i2, io, layout=lay, dtype="f32")
+        announce(f"fctp per-sample random {i1} | {i2} | {io} n={n} {lay}")
+        out = sp.fctp_fwd_per_sample(h, X1, X2, W)
+        g1, g2, gw = sp.fctp_bwd_per_sample(h, X1, X2, W, G)
+        torch.cuda.synchronize()
+        check_scaled(out.cpu().numpy(), f.fwd(x1, x2, w, layout=lay), f.fwd(x1, x2, w, layout=lay, absolute=True),
+                     "f32", "fwd")
+        r = f.vjp(x1, x2, None, g, layout=lay, edge_weights=w)
+        a = f.vjp(x1, x2, None, g, layout=lay, absolute=True, edge_weights=w)
+        for got, ref, sc, name in zip((g1, g2, gw), r, a, ("dx1", "dx2", "dw")):
+            check_scaled(got.cpu().numpy(), ref, sc, "f32", name)
