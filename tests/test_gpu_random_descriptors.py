@@ -1,8 +1,9 @@
 """GPU parity on seeded random descriptors: the channelwise convolution, the
-fully connected product with one shared weight row, the equivariant linear
-layer and the symmetric contraction, forward and backward, both layouts,
-float32, called through the C ABI and compared with the float64 oracle
-(scaled error, oracle.metrics, <= 1e-5).  The hand-picked cases of the
+fully connected product with one shared weight row and as a convolution
+with per-edge weights, the equivariant linear layer and the symmetric
+contraction, forward and backward, both layouts, float32, called through
+the C ABI and compared with the float64 oracle (scaled error,
+oracle.metrics, <= 1e-5).  The hand-picked cases of the
 other GPU tests cover the shapes the pages name; these cover block orders,
 channel counts and type sets that none of them picks."""
 
@@ -159,4 +160,41 @@ def test_random_symmetric_contraction(seed):
         ref = sc.eval_vjp(x, species, w, g, layout=lay)
         scale = sc.eval_vjp(x, species, w, g, layout=lay, absolute=True)
         for got, r, a, name in zip((gx, gw), ref, scale, ("dx", "dw")):
+            check_scaled(got.cpu().numpy(), r, a, "f32", name)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_random_fully_connected_convolution(seed):
+    """The fully connected product as a convolution with one weight row per
+    edge (input 2: one channel per degree), sum or mean, ragged graph."""
+    sp = _sp()
+    import torch
+    rng = np.random.default_rng(700 + seed)
+    while True:
+        i1 = _irreps(rng, 3, 24, 2)
+        i2 = "+".join(sorted(set(["0e"] + list(rng.choice(["1o", "2e", "1e"], 2)))))
+        io = _irreps(rng, 3, 24, 2)
+        f = ofc.FullyConnectedTP(i1, i2, io)
+        if f.weight_numel > 0:
+            break
+    reduce = "mean" if seed % 2 else "sum"
+    n_src, n_dst, n_e = 27, 19, int(rng.integers(40, 160))
+    src = rng.integers(0, n_src, n_e)
+    dst = np.sort(rng.integers(0, n_dst, n_e))
+    x, sh, w = _f32(rng, (n_src, f.dim_in1)), _f32(rng, (n_e, f.dim_in2)), _f32(rng, (n_e, f.weight_numel))
+    g = _f32(rng, (n_dst, f.dim_out))
+    perm = np.argsort(src, kind="stable")
+    for lay in ("mul_ir", "ir_mul"):
+        h = sp.fctp_create(i1, i2, io, layout=lay, reduce=reduce)
+        announce(f"random fully connected conv {i1} | {i2} | {io} {reduce} {lay}")
+        X, S, W, G = (dev(a, torch.float32) for a in (x, sh, w, g))
+        I, D, P = dev(src, torch.int32), dev(dst, torch.int32), dev(perm, torch.int32)
+        out = sp.fctp_conv_fwd(h, X, S, W, I, D, n_dst)
+        dx, dsh, dw = sp.fctp_conv_bwd(h, X, S, W, G, I, D, P, n_dst)
+        torch.cuda.synchronize()
+        check_scaled(out.cpu().numpy(), f.conv(x, sh, w, src, dst, n_dst, layout=lay, reduce=reduce),
+                     f.conv(x, sh, w, src, dst, n_dst, layout=lay, reduce=reduce, absolute=True), "f32", "fwd")
+        ref = f.conv_vjp(x, sh, w, src, dst, n_dst, g, layout=lay, reduce=reduce)
+        scale = f.conv_vjp(x, sh, w, src, dst, n_dst, g, layout=lay, reduce=reduce, absolute=True)
+        for got, r, a, name in zip((dx, dsh, dw), ref, scale, ("dx", "dsh", "dw")):
             check_scaled(got.cpu().numpy(), r, a, "f32", name)
