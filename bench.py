@@ -922,6 +922,18 @@ def other_workloads(torch, sp, workloads, dev, args):
             rec["hbm_GBps_algorithmic"] = b / (sum(per) / len(per) * 1e-3) / 1e9
             if not args.no_eager:
                 rec["eager_per_path"] = eager_per_path(torch, h, wl, sets[0], N, E, dev)
+        if n in (2, 3):
+            # row pointers built once per graph (timed apart) replace the
+            # per-destination range search of every call
+            t = sets[0]
+            rp = sp.tp_rowptr_build(t["dst"], N)
+            _, per_b = time_launches(torch, lambda: sp.tp_rowptr_build(t["dst"], N, out=rp), steps, args.warmup)
+            fr = lambda: sp.tp_conv_fwd_rowptr(h, t["x"], t["sh"], t["w"], t["src"], rp, out=t["out"])
+            wall_r, per_r = time_launches(torch, fr, steps, args.warmup)
+            rec["rowptr"] = {"build_kernel_us_mean": 1e3 * sum(per_b) / len(per_b),
+                             "kernel_us_mean": 1e3 * sum(per_r) / len(per_r),
+                             "us_per_call": wall_r * 1e6 / steps, "edges_per_s": E * steps / wall_r,
+                             "what": "tp_conv_fwd_rowptr with row pointers built once (input set 0, warm)"}
         if n == 2:
             # HIP graph replay of 20 calls (the path has no memset or host work)
             t = sets[0]

@@ -181,6 +181,38 @@ int tp_conv_fwd(tp_handle h, const void* x, int64_t n_src, const void* sh, const
                 void* out, void* stream);
 
 /*
+ * tp_rowptr_build: row pointers of a destination-sorted edge list (the
+ * compressed-sparse-row form of the destination ranges; the sorted
+ * destinations it is built from are those of tp_conv_fwd, after the
+ * cuequivariance-torch skill document, "SegmentedPolynomial: gather and
+ * scatter"):
+ *   row_ptr[n] = first e with dst[e] >= n, for n = 0 .. n_nodes
+ * (row_ptr[n_nodes] = n_edges when every dst is below n_nodes).
+ *   dst      [n_edges] device, sorted ascending, int32 or int64 per idx_dtype.
+ *   row_ptr  [n_nodes + 1] device, same index dtype, fully overwritten.
+ * One launch; build it once per graph and pass it to every
+ * tp_conv_fwd_rowptr call on that graph (it replaces the per-destination
+ * range search of tp_conv_fwd).  E_UNSUPPORTED for int32 with n_edges or
+ * n_nodes at 2^31 or more.
+ */
+int tp_rowptr_build(const void* dst, int idx_dtype, int64_t n_edges, int64_t n_nodes, void* row_ptr,
+                    void* stream);
+
+/*
+ * tp_conv_fwd_rowptr: tp_conv_fwd with the destination ranges given as row
+ * pointers instead of dst: destination n sums the edges
+ * [row_ptr[n], row_ptr[n + 1]) (values clamped to [0, n_edges], so
+ * inconsistent pointers cannot read outside the edge arrays; VALIDATE
+ * checks row_ptr[0] = 0, non-decreasing entries and row_ptr[n_nodes] =
+ * n_edges, E_RANGE / E_UNSORTED otherwise).  src and row_ptr are required
+ * (no batch mode); the result equals tp_conv_fwd's on the dst the pointers
+ * were built from, bit for bit.  Other arguments as tp_conv_fwd.
+ */
+int tp_conv_fwd_rowptr(tp_handle h, const void* x, int64_t n_src, const void* sh, const void* w,
+                       const void* src, const void* row_ptr, int idx_dtype, int64_t n_edges, int64_t n_nodes,
+                       void* out, void* stream);
+
+/*
  * tp_conv_bwd_workspace: bytes of device workspace tp_conv_bwd needs for
  * n_edges edges, in indexed mode (batch == 0) or batch mode (batch != 0):
  * one source message per edge (n_edges * DIM_IN1 elements of the handle's

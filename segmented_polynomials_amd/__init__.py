@@ -33,7 +33,7 @@ _DTYPES = {"f32": F32, "f64": F64}
 
 # every symbol include/segpoly.h declares
 EXPORTS = ("tp_create", "tp_query", "tp_irreps_out", "tp_path_info", "tp_path_cg", "tp_kernel_name",
-           "tp_conv_fwd", "tp_conv_fwd_vec", "tp_conv_bwd_workspace", "tp_conv_bwd", "tp_destroy", "symcon_create", "symcon_query", "symcon_coupling_info",
+           "tp_conv_fwd", "tp_conv_fwd_vec", "tp_rowptr_build", "tp_conv_fwd_rowptr", "tp_conv_bwd_workspace", "tp_conv_bwd", "tp_destroy", "symcon_create", "symcon_query", "symcon_coupling_info",
            "symcon_coupling_dense", "symcon_fwd", "symcon_bwd_workspace", "symcon_bwd", "symcon_bwd_noalloc", "symcon_destroy", "linear_create", "linear_query", "linear_fwd",
            "linear_bwd_workspace", "linear_bwd", "linear_destroy", "fctp_create", "fctp_query", "fctp_path_info",
            "fctp_fwd", "fctp_bwd_workspace", "fctp_bwd", "fctp_fwd_per_sample", "fctp_bwd_per_sample", "fctp_conv_fwd", "fctp_conv_bwd_workspace", "fctp_conv_bwd", "fctp_destroy", "edge_scalars_fwd", "edge_scalars_bwd", "sh_fwd", "sh_bwd", "segpoly_real_cg",
@@ -80,6 +80,8 @@ def _load():
         "tp_kernel_name": [vp, ctypes.c_char_p, ctypes.c_size_t],
         "tp_conv_fwd": [vp, vp, i64, vp, vp, vp, vp, c_int, i64, i64, vp, vp],
         "tp_conv_fwd_vec": [vp, vp, i64, vp, c_int, vp, vp, vp, c_int, i64, i64, vp, vp],
+        "tp_rowptr_build": [vp, c_int, i64, i64, vp, vp],
+        "tp_conv_fwd_rowptr": [vp, vp, i64, vp, vp, vp, vp, c_int, i64, i64, vp, vp],
         "tp_conv_bwd_workspace": [vp, i64, c_int, ctypes.POINTER(ctypes.c_size_t)],
         "tp_conv_bwd": [vp, vp, i64, vp, vp, vp, vp, vp, c_int, i64, i64, vp, vp, vp, vp, vp, ctypes.c_size_t, vp],
         "tp_destroy": [vp],
@@ -276,6 +278,48 @@ def tp_conv_fwd(h, x, sh, w, src=None, dst=None, n_nodes=None, out=None):
         raise ValueError("out has the wrong shape or dtype")
     _check(lib.tp_conv_fwd(h._h, _ptr(x), n_src, _ptr(sh), _ptr(w), _ptr(src), _ptr(dst), idx, n_edges,
                            n_nodes, _ptr(out), _stream_ptr(x.device)))
+    return out
+
+
+def tp_rowptr_build(dst, n_nodes, out=None):
+    """Row pointers [n_nodes + 1] of a destination-sorted edge list:
+    out[n] = first e with dst[e] >= n (same integer dtype as dst)."""
+    import torch
+    if dst.dim() != 1 or not dst.is_cuda or not dst.is_contiguous():
+        raise ValueError("dst must be a contiguous 1-d device tensor")
+    idx = _index_dtype(dst)
+    if out is None:
+        out = torch.empty(n_nodes + 1, dtype=dst.dtype, device=dst.device)
+    elif out.shape != (n_nodes + 1,) or out.dtype != dst.dtype or not out.is_contiguous():
+        raise ValueError("out must be [n_nodes + 1] of the dtype of dst")
+    _check(lib.tp_rowptr_build(_ptr(dst), idx, dst.shape[0], n_nodes, _ptr(out), _stream_ptr(dst.device)))
+    return out
+
+
+def tp_conv_fwd_rowptr(h, x, sh, w, src, row_ptr, out=None):
+    """``tp_conv_fwd`` with the destination ranges given as row pointers
+    (``tp_rowptr_build``): n_nodes = len(row_ptr) - 1."""
+    import torch
+    t = _torch_dtype(h.dtype)
+    for name, a in (("x", x), ("sh", sh), ("w", w)):
+        if a.dtype != t or not a.is_cuda or not a.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous {t} device tensor")
+    n_src, n_edges = x.shape[0], sh.shape[0]
+    if x.shape[1] != h.dim_in1 or sh.shape[1] != h.dim_in2 or w.shape[-1] != h.weight_numel:
+        raise ValueError("operand widths do not match the descriptor")
+    if w.shape[0] != (1 if h.shared_weights else n_edges):
+        raise ValueError("weights must have one row per edge (or one row when shared)")
+    if src.shape != (n_edges,) or row_ptr.dim() != 1 or src.dtype != row_ptr.dtype:
+        raise ValueError("src must be [n_edges] and row_ptr 1-d, of one integer dtype")
+    if not (src.is_cuda and row_ptr.is_cuda and src.is_contiguous() and row_ptr.is_contiguous()):
+        raise ValueError("src and row_ptr must be contiguous device tensors")
+    n_nodes = row_ptr.shape[0] - 1
+    if out is None:
+        out = torch.empty((n_nodes, h.dim_out), dtype=t, device=x.device)
+    elif out.shape != (n_nodes, h.dim_out) or out.dtype != t or not out.is_contiguous():
+        raise ValueError("out has the wrong shape or dtype")
+    _check(lib.tp_conv_fwd_rowptr(h._h, _ptr(x), n_src, _ptr(sh), _ptr(w), _ptr(src), _ptr(row_ptr),
+                                  _index_dtype(src), n_edges, n_nodes, _ptr(out), _stream_ptr(x.device)))
     return out
 
 

@@ -141,8 +141,8 @@ GenericSymconInfo generic_symcon_info(const segpoly_symcon* h, void* dp) {
 }
 
 int tp_conv_fwd_impl(tp_handle h, const void* x, int64_t n_src, const void* sh, const void* vec, int normalize,
-                     const void* w, const void* src, const void* dst, int idx_dtype, int64_t n_edges,
-                     int64_t n_nodes, void* out, void* stream);
+                     const void* w, const void* src, const void* dst, const void* row_ptr, int idx_dtype,
+                     int64_t n_edges, int64_t n_nodes, void* out, void* stream);
 }  // namespace
 
 namespace segpoly {
@@ -299,7 +299,31 @@ int tp_path_cg(tp_handle h, int p, double* out) {
 
 int tp_conv_fwd(tp_handle h, const void* x, int64_t n_src, const void* sh, const void* w, const void* src,
                 const void* dst, int idx_dtype, int64_t n_edges, int64_t n_nodes, void* out, void* stream) {
-  return tp_conv_fwd_impl(h, x, n_src, sh, nullptr, 0, w, src, dst, idx_dtype, n_edges, n_nodes, out, stream);
+  return tp_conv_fwd_impl(h, x, n_src, sh, nullptr, 0, w, src, dst, nullptr, idx_dtype, n_edges, n_nodes, out,
+                          stream);
+}
+
+int tp_conv_fwd_rowptr(tp_handle h, const void* x, int64_t n_src, const void* sh, const void* w, const void* src,
+                       const void* row_ptr, int idx_dtype, int64_t n_edges, int64_t n_nodes, void* out,
+                       void* stream) {
+  if (!h) return fail(SEGPOLY_E_INVALID, "null handle");
+  if (n_nodes > 0 && !row_ptr) return fail(SEGPOLY_E_INVALID, "null row_ptr");
+  if (n_edges > 0 && !src) return fail(SEGPOLY_E_INVALID, "null src");
+  return tp_conv_fwd_impl(h, x, n_src, sh, nullptr, 0, w, src, nullptr, row_ptr, idx_dtype, n_edges, n_nodes, out,
+                          stream);
+}
+
+int tp_rowptr_build(const void* dst, int idx_dtype, int64_t n_edges, int64_t n_nodes, void* row_ptr,
+                    void* stream) {
+  if (idx_dtype != SEGPOLY_I32 && idx_dtype != SEGPOLY_I64) return fail(SEGPOLY_E_INVALID, "bad index dtype");
+  if (n_edges < 0 || n_nodes < 0) return fail(SEGPOLY_E_INVALID, "negative size");
+  if (!row_ptr || (n_edges > 0 && !dst)) return fail(SEGPOLY_E_INVALID, "null buffer");
+  if (idx_dtype == SEGPOLY_I32 && (n_edges > 2147483647 || n_nodes > 2147483646))
+    return fail(SEGPOLY_E_UNSUPPORTED, "int32 row pointers need n_edges and n_nodes below 2^31");
+  if ((n_nodes + 1 + 255) / 256 > kMaxGrid) return fail(SEGPOLY_E_UNSUPPORTED, "too many nodes for one launch");
+  const int rc = launch_rowptr_build(dst, idx_dtype, n_edges, n_nodes, row_ptr, stream);
+  if (rc) return fail(SEGPOLY_E_HIP, std::string("row pointer launch: ") + hipGetErrorString(static_cast<hipError_t>(rc)));
+  return ok();
 }
 
 int tp_conv_fwd_vec(tp_handle h, const void* x, int64_t n_src, const void* vec, int normalize, const void* w,
@@ -315,19 +339,19 @@ int tp_conv_fwd_vec(tp_handle h, const void* x, int64_t n_src, const void* vec, 
     return fail(SEGPOLY_E_UNSUPPORTED, "harmonics degree outside [0, 6]");
   if (n_edges > 0 && !vec) return fail(SEGPOLY_E_INVALID, "null vec");
   return tp_conv_fwd_impl(h, x, n_src, nullptr, vec ? vec : reinterpret_cast<const void*>(16), normalize, w, src,
-                          dst, idx_dtype, n_edges, n_nodes, out, stream);
+                          dst, nullptr, idx_dtype, n_edges, n_nodes, out, stream);
 }
 
 }  // extern "C"
 
 namespace {
 int tp_conv_fwd_impl(tp_handle h, const void* x, int64_t n_src, const void* sh, const void* vec, int normalize,
-                     const void* w, const void* src, const void* dst, int idx_dtype, int64_t n_edges,
-                     int64_t n_nodes, void* out, void* stream) {
+                     const void* w, const void* src, const void* dst, const void* row_ptr, int idx_dtype,
+                     int64_t n_edges, int64_t n_nodes, void* out, void* stream) {
   if (!h) return fail(SEGPOLY_E_INVALID, "null handle");
   if (n_src < 0 || n_edges < 0 || n_nodes < 0) return fail(SEGPOLY_E_INVALID, "negative size");
   if (idx_dtype != SEGPOLY_I32 && idx_dtype != SEGPOLY_I64) return fail(SEGPOLY_E_INVALID, "bad index dtype");
-  if ((src == nullptr) != (dst == nullptr))
+  if (!row_ptr && (src == nullptr) != (dst == nullptr))
     return fail(SEGPOLY_E_INVALID, "src and dst must both be given or both be NULL");
   const auto& d = h->d;
   // NULL indices select batch mode, except that an empty edge list (whose
@@ -344,8 +368,13 @@ int tp_conv_fwd_impl(tp_handle h, const void* x, int64_t n_src, const void* sh, 
     if (!x && n_src > 0) return fail(SEGPOLY_E_INVALID, "null x");
   }
   if ((h->flags & SEGPOLY_VALIDATE) && !batch) {
-    int st = idx_dtype == SEGPOLY_I32 ? check_indices<int32_t>(src, dst, n_edges, n_src, n_nodes, stream)
-                                      : check_indices<int64_t>(src, dst, n_edges, n_src, n_nodes, stream);
+    int st;
+    if (row_ptr)
+      st = idx_dtype == SEGPOLY_I32 ? check_rowptr<int32_t>(src, row_ptr, n_edges, n_src, n_nodes, stream)
+                                    : check_rowptr<int64_t>(src, row_ptr, n_edges, n_src, n_nodes, stream);
+    else
+      st = idx_dtype == SEGPOLY_I32 ? check_indices<int32_t>(src, dst, n_edges, n_src, n_nodes, stream)
+                                    : check_indices<int64_t>(src, dst, n_edges, n_src, n_nodes, stream);
     if (st != SEGPOLY_OK) return st;
   }
   TPArgs a{};
@@ -354,6 +383,7 @@ int tp_conv_fwd_impl(tp_handle h, const void* x, int64_t n_src, const void* sh, 
   a.w = w;
   a.src = src;
   a.dst = dst;
+  a.row_ptr = batch ? nullptr : row_ptr;
   a.out = out;
   a.n_src = n_src;
   // without source rows no edge contributes (and x may be NULL): every

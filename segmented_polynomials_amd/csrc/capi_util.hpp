@@ -90,6 +90,26 @@ inline int check_indices(const void* dsrc, const void* ddst, int64_t n_edges, in
   return ok();
 }
 
+// VALIDATE with row pointers instead of dst: sources in range, rp[0] = 0,
+// rp non-decreasing, rp[n_nodes] = n_edges.
+template <typename Index>
+inline int check_rowptr(const void* dsrc, const void* drp, int64_t n_edges, int64_t n_src, int64_t n_nodes,
+                        void* stream) {
+  std::vector<Index> s(n_edges), r(n_nodes + 1);
+  hipError_t e = hipStreamSynchronize(static_cast<hipStream_t>(stream));
+  if (e == hipSuccess && n_edges) e = hipMemcpy(s.data(), dsrc, n_edges * sizeof(Index), hipMemcpyDeviceToHost);
+  if (e == hipSuccess) e = hipMemcpy(r.data(), drp, (n_nodes + 1) * sizeof(Index), hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return fail(SEGPOLY_E_HIP, std::string("validate copy: ") + hipGetErrorString(e));
+  for (int64_t i = 0; i < n_edges; ++i)
+    if (s[i] < 0 || static_cast<int64_t>(s[i]) >= n_src)
+      return fail(SEGPOLY_E_RANGE, "src[" + std::to_string(i) + "] = " + std::to_string(s[i]) + " outside [0, n_src)");
+  if (r[0] != 0 || static_cast<int64_t>(r[n_nodes]) != n_edges)
+    return fail(SEGPOLY_E_RANGE, "row_ptr must start at 0 and end at n_edges");
+  for (int64_t n = 0; n < n_nodes; ++n)
+    if (r[n + 1] < r[n]) return fail(SEGPOLY_E_UNSORTED, "row_ptr decreases at node " + std::to_string(n));
+  return ok();
+}
+
 // VALIDATE for the backward: perm is a permutation of the edges with
 // src[perm[.]] ascending.
 template <typename Index>

@@ -23,7 +23,7 @@ template <typename T, typename Index, int LAYOUT>
 __global__ void __launch_bounds__(kGW)
 tp_conv_generic_kernel(const T* __restrict__ x, const T* __restrict__ sh, const T* __restrict__ w,
                        const Index* __restrict__ src, const Index* __restrict__ dst,
-                       const GPath* __restrict__ paths, const GNz* __restrict__ nz, int np, int nk,
+                       const Index* __restrict__ row_ptr, const GPath* __restrict__ paths, const GNz* __restrict__ nz, int np, int nk,
                        int64_t dim1, int64_t dim2, int64_t dimo, int64_t n_src, int64_t n_edges,
                        int64_t w_stride, int batch, int mean, T* __restrict__ out) {
   extern __shared__ unsigned char smem_raw[];
@@ -34,7 +34,7 @@ tp_conv_generic_kernel(const T* __restrict__ x, const T* __restrict__ sh, const 
   for (int k = 0; k < nk; ++k) acc[k * kGW + lane] = T(0);
 
   int64_t e0, e1;
-  edge_range(dst, n_edges, batch, node, e0, e1);
+  edge_range(dst, n_edges, batch, node, e0, e1, row_ptr);
   for (int64_t e = e0; e < e1; ++e) {
     const int64_t s = batch ? e : static_cast<int64_t>(src[e]);
     if (s < 0 || s >= n_src) continue;
@@ -78,9 +78,9 @@ int tp_generic_launch(const TPArgs& a, const GenericTPInfo& g) {
   hipLaunchKernelGGL((tp_conv_generic_kernel<T, Index, LAYOUT>), grid, dim3(kGW), lds,
                      static_cast<hipStream_t>(a.stream), static_cast<const T*>(a.x),
                      static_cast<const T*>(a.sh), static_cast<const T*>(a.w),
-                     static_cast<const Index*>(a.src), static_cast<const Index*>(a.dst), g.paths, g.nz,
-                     g.np, g.nk, g.dim1, g.dim2, g.dimo, a.n_src, a.n_edges, a.w_stride, a.batch, a.mean,
-                     static_cast<T*>(a.out));
+                     static_cast<const Index*>(a.src), static_cast<const Index*>(a.dst),
+                     static_cast<const Index*>(a.row_ptr), g.paths, g.nz, g.np, g.nk, g.dim1, g.dim2, g.dimo,
+                     a.n_src, a.n_edges, a.w_stride, a.batch, a.mean, static_cast<T*>(a.out));
   return static_cast<int>(hipGetLastError());
 }
 
@@ -596,6 +596,41 @@ int launch_symcon_generic(const SymconArgs& a, const GenericSymconInfo& g) {
                               : symcon_generic_launch<double, int32_t, kIrMul>(a, g);
   return a.layout == kMulIr ? symcon_generic_launch<double, int64_t, kMulIr>(a, g)
                             : symcon_generic_launch<double, int64_t, kIrMul>(a, g);
+}
+
+namespace kern {
+
+// rp[n] = first e with dst[e] >= n, for n = 0 .. n_nodes (dst sorted
+// ascending): one thread per entry, a binary search each.
+template <typename Index>
+__global__ void __launch_bounds__(256)
+rowptr_build_kernel(const Index* __restrict__ dst, int64_t n_edges, int64_t n_nodes, Index* __restrict__ rp) {
+  const int64_t n = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (n > n_nodes) return;
+  int64_t lo = 0, hi = n_edges;
+  while (lo < hi) {
+    const int64_t mid = lo + (hi - lo) / 2;
+    if (static_cast<int64_t>(dst[mid]) < n)
+      lo = mid + 1;
+    else
+      hi = mid;
+  }
+  rp[n] = static_cast<Index>(lo);
+}
+
+}  // namespace kern
+
+int launch_rowptr_build(const void* dst, int idx, int64_t n_edges, int64_t n_nodes, void* rp, void* stream) {
+  const unsigned blocks = static_cast<unsigned>((n_nodes + 1 + 255) / 256);
+  if (idx == kI64)
+    hipLaunchKernelGGL((kern::rowptr_build_kernel<int64_t>), dim3(blocks), dim3(256), 0,
+                       static_cast<hipStream_t>(stream), static_cast<const int64_t*>(dst), n_edges, n_nodes,
+                       static_cast<int64_t*>(rp));
+  else
+    hipLaunchKernelGGL((kern::rowptr_build_kernel<int32_t>), dim3(blocks), dim3(256), 0,
+                       static_cast<hipStream_t>(stream), static_cast<const int32_t*>(dst), n_edges, n_nodes,
+                       static_cast<int32_t*>(rp));
+  return static_cast<int>(hipGetLastError());
 }
 
 }  // namespace segpoly

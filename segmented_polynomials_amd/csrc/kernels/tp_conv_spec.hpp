@@ -80,13 +80,21 @@ __device__ __forceinline__ int64_t lower_bound_wave_near(const Index* __restrict
   return lower_bound_wave(dst, lo + kWave, hi, key);
 }
 
-// Edge range of `node` (batch mode: edge e is node e).
+// Edge range of `node` (batch mode: edge e is node e).  With the caller's
+// row pointers rp (rp[n] = first edge of destination n, rp[n_nodes] =
+// n_edges) two independent loads replace the search; values are clamped to
+// 0 <= e0 <= e1 <= n_edges, so inconsistent pointers cannot reach outside
+// the edge arrays.
 template <typename Index>
 __device__ __forceinline__ void edge_range(const Index* __restrict__ dst, int64_t n_edges, int batch, int64_t node,
-                                           int64_t& e0, int64_t& e1) {
+                                           int64_t& e0, int64_t& e1, const Index* __restrict__ rp = nullptr) {
   if (batch) {
     e0 = node;
     e1 = node + 1;
+  } else if (rp) {
+    const int64_t a = static_cast<int64_t>(rp[node]), b = static_cast<int64_t>(rp[node + 1]);
+    e0 = a < 0 ? 0 : (a > n_edges ? n_edges : a);
+    e1 = b < e0 ? e0 : (b > n_edges ? n_edges : b);
   } else {
     e0 = lower_bound_wave(dst, 0, n_edges, node);
     e1 = lower_bound_wave_near(dst, e0, n_edges, node + 1);
@@ -108,8 +116,8 @@ constexpr int sh_lmax_of(int d2) {
 template <class S, typename T, typename Index, int LAYOUT, int CPL, bool NTS = false, bool SHV = false>
 __global__ void __launch_bounds__(kWave)
 tp_conv_kernel(const T* __restrict__ x, const T* __restrict__ sh, const T* __restrict__ w,
-               const Index* __restrict__ src, const Index* __restrict__ dst, int64_t n_src, int64_t n_edges,
-               int64_t w_stride, int mul, int batch, int mean, T* __restrict__ out,
+               const Index* __restrict__ src, const Index* __restrict__ dst, const Index* __restrict__ row_ptr,
+               int64_t n_src, int64_t n_edges, int64_t w_stride, int mul, int batch, int mean, T* __restrict__ out,
                const T* __restrict__ vec = nullptr, int sh_normalize = 0, ShConsts shk = {}) {
   const int64_t node = blockIdx.x;
   const int ub = blockIdx.y * (kWave * CPL) + threadIdx.x * CPL;
@@ -117,7 +125,7 @@ tp_conv_kernel(const T* __restrict__ x, const T* __restrict__ sh, const T* __res
   const int ubl = active ? ub : 0;  // idle lanes load channel 0 and store nothing
 
   int64_t e0, e1;
-  edge_range(dst, n_edges, batch, node, e0, e1);
+  edge_range(dst, n_edges, batch, node, e0, e1, row_ptr);
   const int64_t dim1 = static_cast<int64_t>(mul) * S::NX;
 
   T acc[CPL][S::NK];
@@ -217,9 +225,9 @@ constexpr int kSplitThreads = 256;
 template <class S, typename T, typename Index, int LAYOUT, int GW, bool SHV = false>
 __global__ void __launch_bounds__(kSplitThreads)
 tp_conv_split_kernel(const T* __restrict__ x, const T* __restrict__ sh, const T* __restrict__ w,
-                     const Index* __restrict__ src, const Index* __restrict__ dst, int64_t n_src, int64_t n_edges,
-                     int64_t w_stride, int mul, int mean, T* __restrict__ out, const T* __restrict__ vec = nullptr,
-                     int sh_normalize = 0, ShConsts shk = {}) {
+                     const Index* __restrict__ src, const Index* __restrict__ dst, const Index* __restrict__ row_ptr,
+                     int64_t n_src, int64_t n_edges, int64_t w_stride, int mul, int mean, T* __restrict__ out,
+                     const T* __restrict__ vec = nullptr, int sh_normalize = 0, ShConsts shk = {}) {
   constexpr int EG = kSplitThreads / GW;
   __shared__ T red[EG][S::NK][GW];
   const int64_t node = blockIdx.x;
@@ -228,7 +236,7 @@ tp_conv_split_kernel(const T* __restrict__ x, const T* __restrict__ sh, const T*
   const bool active = ul < mul;
   const int ub = active ? ul : 0;
   int64_t e0, e1;
-  edge_range(dst, n_edges, 0, node, e0, e1);  // every wave finds the same range
+  edge_range(dst, n_edges, 0, node, e0, e1, row_ptr);  // every wave finds the same range
   const int64_t dim1 = static_cast<int64_t>(mul) * S::NX;
 
   T acc[1][S::NK];
@@ -304,7 +312,8 @@ int tp_conv_split_launch(const TPArgs& a) {
       hipLaunchKernelGGL((tp_conv_split_kernel<S, T, Index, LAYOUT, GW, true>), grid, dim3(kSplitThreads), 0,
                          static_cast<hipStream_t>(a.stream), static_cast<const T*>(a.x), nullptr,
                          static_cast<const T*>(a.w), static_cast<const Index*>(a.src),
-                         static_cast<const Index*>(a.dst), a.n_src, a.n_edges, a.w_stride, a.mul, a.mean,
+                         static_cast<const Index*>(a.dst), static_cast<const Index*>(a.row_ptr), a.n_src,
+                         a.n_edges, a.w_stride, a.mul, a.mean,
                          static_cast<T*>(a.out), static_cast<const T*>(a.vec), a.sh_normalize, *a.sh_consts);
       return static_cast<int>(hipGetLastError());
     } else {
@@ -314,6 +323,7 @@ int tp_conv_split_launch(const TPArgs& a) {
   hipLaunchKernelGGL((tp_conv_split_kernel<S, T, Index, LAYOUT, GW>), grid, dim3(kSplitThreads), 0,
                      static_cast<hipStream_t>(a.stream), static_cast<const T*>(a.x), static_cast<const T*>(a.sh),
                      static_cast<const T*>(a.w), static_cast<const Index*>(a.src), static_cast<const Index*>(a.dst),
+                     static_cast<const Index*>(a.row_ptr),
                      a.n_src, a.n_edges, a.w_stride, a.mul, a.mean, static_cast<T*>(a.out));
   return static_cast<int>(hipGetLastError());
 }
@@ -328,7 +338,8 @@ int tp_conv_launch(const TPArgs& a) {
       hipLaunchKernelGGL((tp_conv_kernel<S, T, Index, LAYOUT, CPL, NTS, true>), grid, dim3(kWave), 0,
                          static_cast<hipStream_t>(a.stream), static_cast<const T*>(a.x), nullptr,
                          static_cast<const T*>(a.w), static_cast<const Index*>(a.src),
-                         static_cast<const Index*>(a.dst), a.n_src, a.n_edges, a.w_stride, a.mul, a.batch, a.mean,
+                         static_cast<const Index*>(a.dst), static_cast<const Index*>(a.row_ptr), a.n_src,
+                         a.n_edges, a.w_stride, a.mul, a.batch, a.mean,
                          static_cast<T*>(a.out), static_cast<const T*>(a.vec), a.sh_normalize, *a.sh_consts);
       return static_cast<int>(hipGetLastError());
     } else {
@@ -338,7 +349,8 @@ int tp_conv_launch(const TPArgs& a) {
   hipLaunchKernelGGL((tp_conv_kernel<S, T, Index, LAYOUT, CPL, NTS>), grid, dim3(kWave), 0,
                      static_cast<hipStream_t>(a.stream), static_cast<const T*>(a.x),
                      static_cast<const T*>(a.sh), static_cast<const T*>(a.w),
-                     static_cast<const Index*>(a.src), static_cast<const Index*>(a.dst), a.n_src,
+                     static_cast<const Index*>(a.src), static_cast<const Index*>(a.dst),
+                     static_cast<const Index*>(a.row_ptr), a.n_src,
                      a.n_edges, a.w_stride, a.mul, a.batch, a.mean, static_cast<T*>(a.out));
   return static_cast<int>(hipGetLastError());
 }

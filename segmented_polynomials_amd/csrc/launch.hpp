@@ -15,6 +15,7 @@ struct TPArgs {
   const void* w;      // [n_edges or 1, numel]
   const void* src;    // [n_edges] or null (batch mode)
   const void* dst;    // [n_edges], sorted ascending, or null (batch mode)
+  const void* row_ptr;  // [n_nodes + 1] first edge of each destination (index dtype), or null: search dst
   void* out;          // [n_nodes, dim_out]
   int64_t n_src, n_edges, n_nodes;
   int64_t w_stride;   // numel, or 0 for shared weights

@@ -363,6 +363,21 @@ def test_fctp_descriptor_matches_oracle(a, b, c):
     assert [h.path_info(p) for p in range(h.num_paths)] == [tuple(p) for p in f.paths]
 
 
+def test_rowptr_errors():
+    p = ctypes.c_void_p(16)   # never dereferenced: every call below fails validation
+    rb, rf = sp.lib.tp_rowptr_build, sp.lib.tp_conv_fwd_rowptr
+    assert rb(None, 0, 5, 3, p, None) == sp.E_INVALID          # null dst with edges
+    assert rb(p, 0, 5, 3, None, None) == sp.E_INVALID          # null row_ptr
+    assert rb(p, 7, 5, 3, p, None) == sp.E_INVALID             # index dtype
+    assert rb(p, 0, -1, 3, p, None) == sp.E_INVALID
+    assert rb(p, 0, 1 << 31, 3, p, None) == sp.E_UNSUPPORTED   # int32 pointers
+    h = sp.tp_create("8x0e+8x1o", "0e+1o", "0e+1o")
+    assert rf(None, p, 4, p, p, p, p, 0, 5, 3, p, None) == sp.E_INVALID
+    assert rf(h._h, p, 4, p, p, p, None, 0, 5, 3, p, None) == sp.E_INVALID   # null row_ptr
+    assert rf(h._h, p, 4, p, p, None, p, 0, 5, 3, p, None) == sp.E_INVALID   # null src with edges
+    assert rf(h._h, p, 4, p, p, p, p, 0, 5, 0, None, None) == sp.OK          # no destinations
+
+
 def test_fctp_errors_and_workspace():
     raw = ctypes.c_void_p()
     c = sp.lib.fctp_create

@@ -1,0 +1,126 @@
+"""GPU checks of the row-pointer form of the channelwise convolution: the
+row pointers built on the device equal a host binary search of the sorted
+destinations, and tp_conv_fwd_rowptr reproduces tp_conv_fwd bit for bit
+(the same edges in the same order) on the specialised kernels (molecular
+batch, medium graph), the destination-split kernel and the table-driven
+kernel, with sum and mean, shared weights and both index widths; the
+forward is also checked against the float64 oracle (scaled error <= 1e-5)."""
+
+import numpy as np
+import pytest
+
+import workloads
+from oracle import tp as otp
+from tests._gpu import announce, check_scaled, dev, need_gpu
+
+pytestmark = pytest.mark.gpu
+
+
+def _sp():
+    need_gpu()
+    import segmented_polynomials_amd as sp
+    return sp
+
+
+@pytest.mark.parametrize("idx", ["int32", "int64"])
+def test_rowptr_build_matches_host_search(idx):
+    sp = _sp()
+    import torch
+    rng = np.random.default_rng(81)
+    n_nodes = 1000
+    dst = np.sort(rng.integers(0, n_nodes + 5, 20000))   # some destinations past n_nodes
+    dst[:7] = 0
+    D = dev(dst, getattr(torch, idx))
+    announce(f"rowptr build {idx}")
+    rp = sp.tp_rowptr_build(D, n_nodes).cpu().numpy()
+    ref = np.searchsorted(dst, np.arange(n_nodes + 1), side="left")
+    assert rp.dtype == np.dtype(idx) and np.array_equal(rp, ref)
+    # no edges: every pointer is zero
+    E = torch.empty(0, dtype=getattr(torch, idx), device="cuda")
+    assert int(sp.tp_rowptr_build(E, 5).abs().sum()) == 0
+
+
+def _pair(sp, h, inp, it):
+    import torch
+    td = torch.float32 if h.dtype == "f32" else torch.float64
+    x, s, w = dev(inp["x"], td), dev(inp["sh"], td), dev(inp["w"], td)
+    src, dst = dev(inp["src"], it), dev(inp["dst"], it)
+    n = inp["n_nodes"]
+    a = sp.tp_conv_fwd(h, x, s, w, src, dst, n_nodes=n)
+    rp = sp.tp_rowptr_build(dst, n)
+    b = sp.tp_conv_fwd_rowptr(h, x, s, w, src, rp)
+    torch.cuda.synchronize()
+    return a.cpu().numpy(), b.cpu().numpy()
+
+
+@pytest.mark.parametrize("n", [2, 3])
+@pytest.mark.parametrize("idx", ["int32", "int64"])
+def test_workloads_rowptr_equals_search(n, idx):
+    """The molecular batch (destination-split kernel) and the medium graph
+    (one wave per destination)."""
+    sp = _sp()
+    import torch
+    wl = workloads.WORKLOADS[n]
+    o = otp.ChannelwiseTP(wl.irreps_in1, wl.irreps_in2, wl.irreps_out)
+    inp = workloads.tp_inputs(wl, o.weight_fan_in())
+    lay = wl.layouts[0]
+    h = sp.tp_create(wl.irreps_in1, wl.irreps_in2, wl.irreps_out, layout=lay)
+    announce(f"rowptr forward {wl.name} {idx} ({h.kernel_name})")
+    a, b = _pair(sp, h, inp, getattr(torch, idx))
+    assert np.array_equal(a, b)
+    args = (inp["x"], inp["sh"], inp["w"], inp["src"], inp["dst"], inp["n_nodes"])
+    check_scaled(b, o.conv(*args, layout=lay), o.conv(*args, layout=lay, absolute=True), "f32", "rowptr fwd")
+
+
+@pytest.mark.parametrize("case", [
+    dict(force_generic=True),
+    dict(reduce="mean"),
+    dict(shared_weights=True),
+])
+def test_rowptr_variants(case):
+    """Table-driven kernel, mean reduction and one shared weight row, on a
+    ragged graph with isolated destinations."""
+    sp = _sp()
+    import torch
+    in1, in2, filt = "16x0e+16x1o+16x2e", "0e+1o+2e", "0e+1o+2e"
+    o = otp.ChannelwiseTP(in1, in2, filt)
+    rng = np.random.default_rng(82)
+    n_src, n_dst, n_e = 40, 37, 400
+    src = rng.integers(0, n_src, n_e)
+    dst = np.sort(rng.integers(0, n_dst, n_e))
+    rows = 1 if case.get("shared_weights") else n_e
+    inp = dict(x=rng.standard_normal((n_src, o.dim_in1)).astype(np.float32).astype(np.float64),
+               sh=rng.standard_normal((n_e, o.dim_in2)).astype(np.float32).astype(np.float64),
+               w=rng.standard_normal((rows, o.weight_numel)).astype(np.float32).astype(np.float64),
+               src=src, dst=dst, n_nodes=n_dst)
+    h = sp.tp_create(in1, in2, filt, layout="ir_mul", **case)
+    announce(f"rowptr variant {case} ({h.kernel_name})")
+    a, b = _pair(sp, h, inp, torch.int32)
+    assert np.array_equal(a, b)
+    args = (inp["x"], inp["sh"], inp["w"], src, dst, n_dst)
+    red = case.get("reduce", "sum")
+    ref = o.conv(*args, layout="ir_mul", reduce=red)
+    scale = o.conv(*args, layout="ir_mul", reduce=red, absolute=True)
+    check_scaled(b, ref, scale, "f32", "rowptr variant")
+
+
+def test_rowptr_validate():
+    """With VALIDATE the pointers are checked on the host: a decreasing
+    entry is E_UNSORTED, a wrong end is E_RANGE."""
+    sp = _sp()
+    import torch
+    h = sp.tp_create("8x0e+8x1o", "0e+1o", "0e+1o", validate=True)
+    n_e, n = 30, 6
+    x = torch.zeros((10, h.dim_in1), device="cuda")
+    s = torch.zeros((n_e, h.dim_in2), device="cuda")
+    w = torch.zeros((n_e, h.weight_numel), device="cuda")
+    src = torch.zeros(n_e, dtype=torch.int32, device="cuda")
+    good = torch.tensor([0, 5, 10, 15, 20, 25, 30], dtype=torch.int32, device="cuda")
+    announce("rowptr validate")
+    sp.tp_conv_fwd_rowptr(h, x, s, w, src, good)
+    bad = torch.tensor([0, 5, 4, 15, 20, 25, 30], dtype=torch.int32, device="cuda")
+    with pytest.raises(sp.SegpolyError, match="-4"):
+        sp.tp_conv_fwd_rowptr(h, x, s, w, src, bad)
+    end = torch.tensor([0, 5, 10, 15, 20, 25, 29], dtype=torch.int32, device="cuda")
+    with pytest.raises(sp.SegpolyError, match="-7"):
+        sp.tp_conv_fwd_rowptr(h, x, s, w, src, end)
