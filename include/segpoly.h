@@ -213,6 +213,22 @@ int tp_conv_fwd_rowptr(tp_handle h, const void* x, int64_t n_src, const void* sh
                        void* out, void* stream);
 
 /*
+ * tp_src_rowptr_build: row pointers of the sources in src_perm order (the
+ * gathered input's gradient sums over the edges that read it, after the
+ * cuequivariance-torch skill document, "SegmentedPolynomial: gather and
+ * scatter"; tp_conv_bwd visits each source's edges in this order):
+ *   src_row_ptr[s] = first i with src[src_perm[i]] >= s, for s = 0 .. n_src
+ * (an entry of src_perm outside [0, n_edges) counts as past every source).
+ *   src, src_perm  [n_edges] device, as tp_conv_bwd (src_perm a stable
+ *                  argsort of src).
+ *   src_row_ptr    [n_src + 1] device, same index dtype, fully overwritten.
+ * One launch; build it once per graph for tp_conv_bwd_rowptr.  Errors as
+ * tp_rowptr_build (with n_src in the place of n_nodes).
+ */
+int tp_src_rowptr_build(const void* src, const void* src_perm, int idx_dtype, int64_t n_edges, int64_t n_src,
+                        void* src_row_ptr, void* stream);
+
+/*
  * tp_conv_bwd_workspace: bytes of device workspace tp_conv_bwd needs for
  * n_edges edges, in indexed mode (batch == 0) or batch mode (batch != 0):
  * one source message per edge (n_edges * DIM_IN1 elements of the handle's
@@ -269,6 +285,27 @@ int tp_conv_bwd(tp_handle h, const void* x, int64_t n_src, const void* sh, const
                 const void* dst, const void* src_perm, int idx_dtype, int64_t n_edges, int64_t n_nodes,
                 const void* grad_out, void* grad_x, void* grad_sh, void* grad_w, void* workspace,
                 size_t workspace_bytes, void* stream);
+
+/*
+ * tp_conv_bwd_rowptr: tp_conv_bwd with both edge ranges given as row
+ * pointers: destination n's edges are [row_ptr[n], row_ptr[n + 1])
+ * (tp_rowptr_build) and source s's are src_perm[src_row_ptr[s] ..
+ * src_row_ptr[s + 1]) (tp_src_rowptr_build), both clamped to
+ * [0, n_edges], so inconsistent pointers cannot read outside the edge
+ * arrays.  No range search runs and the sorted-source keys are not built
+ * (two launches fewer for a reused graph).  src, dst (still read by the
+ * table-driven kernels), src_perm and both pointer arrays are required (no
+ * batch mode).  With VALIDATE, besides tp_conv_bwd's checks, each pointer
+ * array must equal the one its builder gives (E_RANGE otherwise).  The
+ * results equal tp_conv_bwd's bit for bit; other arguments, the workspace
+ * (same size) and the errors as tp_conv_bwd.
+ *   row_ptr      [n_nodes + 1] device, idx_dtype.
+ *   src_row_ptr  [n_src + 1] device, idx_dtype.
+ */
+int tp_conv_bwd_rowptr(tp_handle h, const void* x, int64_t n_src, const void* sh, const void* w, const void* src,
+                       const void* dst, const void* src_perm, const void* row_ptr, const void* src_row_ptr,
+                       int idx_dtype, int64_t n_edges, int64_t n_nodes, const void* grad_out, void* grad_x,
+                       void* grad_sh, void* grad_w, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * tp_conv_fwd_vec: tp_conv_fwd with the second operand computed in the

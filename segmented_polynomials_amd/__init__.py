@@ -33,7 +33,7 @@ _DTYPES = {"f32": F32, "f64": F64}
 
 # every symbol include/segpoly.h declares
 EXPORTS = ("tp_create", "tp_query", "tp_irreps_out", "tp_path_info", "tp_path_cg", "tp_kernel_name",
-           "tp_conv_fwd", "tp_conv_fwd_vec", "tp_rowptr_build", "tp_conv_fwd_rowptr", "tp_conv_bwd_workspace", "tp_conv_bwd", "tp_destroy", "symcon_create", "symcon_query", "symcon_coupling_info",
+           "tp_conv_fwd", "tp_conv_fwd_vec", "tp_rowptr_build", "tp_conv_fwd_rowptr", "tp_src_rowptr_build", "tp_conv_bwd_workspace", "tp_conv_bwd", "tp_conv_bwd_rowptr", "tp_destroy", "symcon_create", "symcon_query", "symcon_coupling_info",
            "symcon_coupling_dense", "symcon_fwd", "symcon_bwd_workspace", "symcon_bwd", "symcon_bwd_noalloc", "symcon_destroy", "linear_create", "linear_query", "linear_fwd",
            "linear_bwd_workspace", "linear_bwd", "linear_destroy", "fctp_create", "fctp_query", "fctp_path_info",
            "fctp_fwd", "fctp_bwd_workspace", "fctp_bwd", "fctp_fwd_per_sample", "fctp_bwd_per_sample", "fctp_conv_fwd", "fctp_conv_bwd_workspace", "fctp_conv_bwd", "fctp_destroy", "edge_scalars_fwd", "edge_scalars_bwd", "sh_fwd", "sh_bwd", "segpoly_real_cg",
@@ -84,6 +84,9 @@ def _load():
         "tp_conv_fwd_rowptr": [vp, vp, i64, vp, vp, vp, vp, c_int, i64, i64, vp, vp],
         "tp_conv_bwd_workspace": [vp, i64, c_int, ctypes.POINTER(ctypes.c_size_t)],
         "tp_conv_bwd": [vp, vp, i64, vp, vp, vp, vp, vp, c_int, i64, i64, vp, vp, vp, vp, vp, ctypes.c_size_t, vp],
+        "tp_src_rowptr_build": [vp, vp, c_int, i64, i64, vp, vp],
+        "tp_conv_bwd_rowptr": [vp, vp, i64, vp, vp, vp, vp, vp, vp, vp, c_int, i64, i64, vp, vp, vp, vp, vp,
+                               ctypes.c_size_t, vp],
         "tp_destroy": [vp],
         "symcon_create": [ctypes.c_char_p, ctypes.c_char_p, c_int, c_int, c_int, c_int, c_uint, ctypes.POINTER(vp)],
         "symcon_query": [vp, c_int, p64],
@@ -296,6 +299,23 @@ def tp_rowptr_build(dst, n_nodes, out=None):
     return out
 
 
+def tp_src_rowptr_build(src, src_perm, n_src, out=None):
+    """Row pointers [n_src + 1] of the sources in src_perm order:
+    out[s] = first i with src[src_perm[i]] >= s (same integer dtype)."""
+    import torch
+    for name, a in (("src", src), ("src_perm", src_perm)):
+        if a.dim() != 1 or not a.is_cuda or not a.is_contiguous() or a.shape != src.shape or a.dtype != src.dtype:
+            raise ValueError(f"{name} must be a contiguous 1-d device tensor like src")
+    idx = _index_dtype(src)
+    if out is None:
+        out = torch.empty(n_src + 1, dtype=src.dtype, device=src.device)
+    elif out.shape != (n_src + 1,) or out.dtype != src.dtype or not out.is_contiguous():
+        raise ValueError("out must be [n_src + 1] of the dtype of src")
+    _check(lib.tp_src_rowptr_build(_ptr(src), _ptr(src_perm), idx, src.shape[0], n_src, _ptr(out),
+                                   _stream_ptr(src.device)))
+    return out
+
+
 def tp_conv_fwd_rowptr(h, x, sh, w, src, row_ptr, out=None):
     """``tp_conv_fwd`` with the destination ranges given as row pointers
     (``tp_rowptr_build``): n_nodes = len(row_ptr) - 1."""
@@ -366,6 +386,25 @@ def tp_conv_bwd(h, x, sh, w, grad_out, src=None, dst=None, src_perm=None, n_node
     gradient ``grad_out`` [n_nodes, dim_out].  ``src_perm`` lists the edge ids
     ordered by src (a stable argsort of src), part of the graph like the
     sorted dst.  The workspace and the gradients are allocated if not given."""
+    return _tp_conv_bwd(h, x, sh, w, grad_out, src, dst, src_perm, n_nodes, workspace, grad_x, grad_sh, grad_w)
+
+
+def tp_conv_bwd_rowptr(h, x, sh, w, grad_out, src, dst, src_perm, row_ptr, src_row_ptr, workspace=None,
+                       grad_x=None, grad_sh=None, grad_w=None):
+    """``tp_conv_bwd`` with the destination ranges as row pointers
+    (``tp_rowptr_build``) and the source ranges as row pointers over
+    src_perm order (``tp_src_rowptr_build``): n_nodes = len(row_ptr) - 1."""
+    for name, a, n in (("row_ptr", row_ptr, None), ("src_row_ptr", src_row_ptr, x.shape[0] + 1)):
+        if a.dim() != 1 or not a.is_cuda or not a.is_contiguous() or a.dtype != src.dtype:
+            raise ValueError(f"{name} must be a contiguous 1-d device tensor of the dtype of src")
+        if n is not None and a.shape[0] != n:
+            raise ValueError("src_row_ptr must be [n_src + 1]")
+    return _tp_conv_bwd(h, x, sh, w, grad_out, src, dst, src_perm, row_ptr.shape[0] - 1, workspace, grad_x,
+                        grad_sh, grad_w, row_ptr=row_ptr, src_row_ptr=src_row_ptr)
+
+
+def _tp_conv_bwd(h, x, sh, w, grad_out, src, dst, src_perm, n_nodes, workspace, grad_x, grad_sh, grad_w,
+                 row_ptr=None, src_row_ptr=None):
     import torch
     t = _torch_dtype(h.dtype)
     for name, a in (("x", x), ("sh", sh), ("w", w), ("grad_out", grad_out)):
@@ -399,9 +438,15 @@ def tp_conv_bwd(h, x, sh, w, grad_out, src=None, dst=None, src_perm=None, n_node
     if workspace is None and need:
         workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
     wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check(lib.tp_conv_bwd(h._h, _ptr(x), n_src, _ptr(sh), _ptr(w), _ptr(src), _ptr(dst), _ptr(src_perm), idx,
-                           n_edges, n_nodes, _ptr(grad_out), _ptr(gx), _ptr(gsh), _ptr(gw), _ptr(workspace),
-                           wbytes, _stream_ptr(x.device)))
+    if row_ptr is None:
+        _check(lib.tp_conv_bwd(h._h, _ptr(x), n_src, _ptr(sh), _ptr(w), _ptr(src), _ptr(dst), _ptr(src_perm), idx,
+                               n_edges, n_nodes, _ptr(grad_out), _ptr(gx), _ptr(gsh), _ptr(gw), _ptr(workspace),
+                               wbytes, _stream_ptr(x.device)))
+    else:
+        _check(lib.tp_conv_bwd_rowptr(h._h, _ptr(x), n_src, _ptr(sh), _ptr(w), _ptr(src), _ptr(dst), _ptr(src_perm),
+                                      _ptr(row_ptr), _ptr(src_row_ptr), idx, n_edges, n_nodes, _ptr(grad_out),
+                                      _ptr(gx), _ptr(gsh), _ptr(gw), _ptr(workspace), wbytes,
+                                      _stream_ptr(x.device)))
     return gx, gsh, gw
 
 

@@ -321,7 +321,20 @@ int tp_rowptr_build(const void* dst, int idx_dtype, int64_t n_edges, int64_t n_n
   if (idx_dtype == SEGPOLY_I32 && (n_edges > 2147483647 || n_nodes > 2147483646))
     return fail(SEGPOLY_E_UNSUPPORTED, "int32 row pointers need n_edges and n_nodes below 2^31");
   if ((n_nodes + 1 + 255) / 256 > kMaxGrid) return fail(SEGPOLY_E_UNSUPPORTED, "too many nodes for one launch");
-  const int rc = launch_rowptr_build(dst, idx_dtype, n_edges, n_nodes, row_ptr, stream);
+  const int rc = launch_rowptr_build(dst, nullptr, idx_dtype, n_edges, n_nodes, row_ptr, stream);
+  if (rc) return fail(SEGPOLY_E_HIP, std::string("row pointer launch: ") + hipGetErrorString(static_cast<hipError_t>(rc)));
+  return ok();
+}
+
+int tp_src_rowptr_build(const void* src, const void* src_perm, int idx_dtype, int64_t n_edges, int64_t n_src,
+                        void* row_ptr, void* stream) {
+  if (idx_dtype != SEGPOLY_I32 && idx_dtype != SEGPOLY_I64) return fail(SEGPOLY_E_INVALID, "bad index dtype");
+  if (n_edges < 0 || n_src < 0) return fail(SEGPOLY_E_INVALID, "negative size");
+  if (!row_ptr || (n_edges > 0 && (!src || !src_perm))) return fail(SEGPOLY_E_INVALID, "null buffer");
+  if (idx_dtype == SEGPOLY_I32 && (n_edges > 2147483647 || n_src > 2147483646))
+    return fail(SEGPOLY_E_UNSUPPORTED, "int32 row pointers need n_edges and n_src below 2^31");
+  if ((n_src + 1 + 255) / 256 > kMaxGrid) return fail(SEGPOLY_E_UNSUPPORTED, "too many sources for one launch");
+  const int rc = launch_rowptr_build(src, n_edges > 0 ? src_perm : nullptr, idx_dtype, n_edges, n_src, row_ptr, stream);
   if (rc) return fail(SEGPOLY_E_HIP, std::string("row pointer launch: ") + hipGetErrorString(static_cast<hipError_t>(rc)));
   return ok();
 }
@@ -465,10 +478,11 @@ int tp_conv_bwd_workspace(tp_handle h, int64_t n_edges, int batch, size_t* bytes
   return ok();
 }
 
-int tp_conv_bwd(tp_handle h, const void* x, int64_t n_src, const void* sh, const void* w, const void* src,
-                const void* dst, const void* src_perm, int idx_dtype, int64_t n_edges, int64_t n_nodes,
-                const void* grad_out, void* grad_x, void* grad_sh, void* grad_w, void* workspace,
-                size_t workspace_bytes, void* stream) {
+static int tp_conv_bwd_impl(tp_handle h, const void* x, int64_t n_src, const void* sh, const void* w,
+                            const void* src, const void* dst, const void* src_perm, const void* row_ptr,
+                            const void* src_row_ptr, int idx_dtype, int64_t n_edges, int64_t n_nodes,
+                            const void* grad_out, void* grad_x, void* grad_sh, void* grad_w, void* workspace,
+                            size_t workspace_bytes, void* stream) {
   if (!h) return fail(SEGPOLY_E_INVALID, "null handle");
   if (n_src < 0 || n_edges < 0 || n_nodes < 0) return fail(SEGPOLY_E_INVALID, "negative size");
   if (idx_dtype != SEGPOLY_I32 && idx_dtype != SEGPOLY_I64) return fail(SEGPOLY_E_INVALID, "bad index dtype");
@@ -507,6 +521,14 @@ int tp_conv_bwd(tp_handle h, const void* x, int64_t n_src, const void* sh, const
     if (st == SEGPOLY_OK)
       st = idx_dtype == SEGPOLY_I32 ? check_perm<int32_t>(src, src_perm, n_edges, stream)
                                     : check_perm<int64_t>(src, src_perm, n_edges, stream);
+    if (st == SEGPOLY_OK && row_ptr)
+      st = idx_dtype == SEGPOLY_I32
+               ? check_rowptr_matches<int32_t>(dst, nullptr, row_ptr, n_edges, n_nodes, "row_ptr", stream)
+               : check_rowptr_matches<int64_t>(dst, nullptr, row_ptr, n_edges, n_nodes, "row_ptr", stream);
+    if (st == SEGPOLY_OK && src_row_ptr)
+      st = idx_dtype == SEGPOLY_I32
+               ? check_rowptr_matches<int32_t>(src, src_perm, src_row_ptr, n_edges, n_src, "src_row_ptr", stream)
+               : check_rowptr_matches<int64_t>(src, src_perm, src_row_ptr, n_edges, n_src, "src_row_ptr", stream);
     if (st != SEGPOLY_OK) return st;
   }
   if (n_src == 0 && n_edges == 0 && !(shared && d.numel > 0)) return ok();
@@ -526,6 +548,8 @@ int tp_conv_bwd(tp_handle h, const void* x, int64_t n_src, const void* sh, const
   a.src = src;
   a.dst = dst;
   a.perm = src_perm;
+  a.row_ptr = batch ? nullptr : row_ptr;
+  a.src_row_ptr = batch ? nullptr : src_row_ptr;
   a.g = grad_out;
   a.dx = grad_x;
   a.dsh = grad_sh;
@@ -556,6 +580,26 @@ int tp_conv_bwd(tp_handle h, const void* x, int64_t n_src, const void* sh, const
   if (rc != 0)
     return fail(SEGPOLY_E_HIP, std::string("kernel launch failed: ") + hipGetErrorString(static_cast<hipError_t>(rc)));
   return ok();
+}
+
+int tp_conv_bwd(tp_handle h, const void* x, int64_t n_src, const void* sh, const void* w, const void* src,
+                const void* dst, const void* src_perm, int idx_dtype, int64_t n_edges, int64_t n_nodes,
+                const void* grad_out, void* grad_x, void* grad_sh, void* grad_w, void* workspace,
+                size_t workspace_bytes, void* stream) {
+  return tp_conv_bwd_impl(h, x, n_src, sh, w, src, dst, src_perm, nullptr, nullptr, idx_dtype, n_edges, n_nodes,
+                          grad_out, grad_x, grad_sh, grad_w, workspace, workspace_bytes, stream);
+}
+
+int tp_conv_bwd_rowptr(tp_handle h, const void* x, int64_t n_src, const void* sh, const void* w, const void* src,
+                       const void* dst, const void* src_perm, const void* row_ptr, const void* src_row_ptr,
+                       int idx_dtype, int64_t n_edges, int64_t n_nodes, const void* grad_out, void* grad_x,
+                       void* grad_sh, void* grad_w, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!h) return fail(SEGPOLY_E_INVALID, "null handle");
+  if (n_edges > 0 && (!src || !dst || !src_perm))
+    return fail(SEGPOLY_E_INVALID, "the row-pointer backward needs src, dst and src_perm");
+  if (!row_ptr || !src_row_ptr) return fail(SEGPOLY_E_INVALID, "null row_ptr or src_row_ptr");
+  return tp_conv_bwd_impl(h, x, n_src, sh, w, src, dst, src_perm, row_ptr, src_row_ptr, idx_dtype, n_edges, n_nodes,
+                          grad_out, grad_x, grad_sh, grad_w, workspace, workspace_bytes, stream);
 }
 
 int tp_destroy(tp_handle h) {

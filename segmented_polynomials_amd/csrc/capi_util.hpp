@@ -131,6 +131,28 @@ inline int check_perm(const void* dsrc, const void* dperm, int64_t n_edges, void
   return ok();
 }
 
+// VALIDATE for the backward's row pointers: rp[n] is the first position i
+// with key(i) >= n, key(i) = keys[i], or keys[perm[i]] when perm is given
+// (dst and src_perm have been checked already).
+template <typename Index>
+inline int check_rowptr_matches(const void* dkeys, const void* dperm, const void* drp, int64_t n_edges, int64_t n,
+                                const char* what, void* stream) {
+  std::vector<Index> k(n_edges), p(dperm ? n_edges : 0), r(n + 1);
+  hipError_t e = hipStreamSynchronize(static_cast<hipStream_t>(stream));
+  if (e == hipSuccess && n_edges) e = hipMemcpy(k.data(), dkeys, n_edges * sizeof(Index), hipMemcpyDeviceToHost);
+  if (e == hipSuccess && dperm && n_edges)
+    e = hipMemcpy(p.data(), dperm, n_edges * sizeof(Index), hipMemcpyDeviceToHost);
+  if (e == hipSuccess) e = hipMemcpy(r.data(), drp, (n + 1) * sizeof(Index), hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return fail(SEGPOLY_E_HIP, std::string("validate copy: ") + hipGetErrorString(e));
+  int64_t i = 0;
+  for (int64_t v = 0; v <= n; ++v) {
+    while (i < n_edges && static_cast<int64_t>(k[dperm ? static_cast<int64_t>(p[i]) : i]) < v) ++i;
+    if (static_cast<int64_t>(r[v]) != i)
+      return fail(SEGPOLY_E_RANGE, std::string(what) + "[" + std::to_string(v) + "] does not match the indices");
+  }
+  return ok();
+}
+
 constexpr int64_t kMaxGridX = 2147483647;
 
 struct ShConsts;

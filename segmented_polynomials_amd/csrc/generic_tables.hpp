@@ -54,8 +54,11 @@ int launch_symcon_generic(const SymconArgs& a, const GenericSymconInfo& g);
 // backward of the table-driven products (no workspace but the shared-weight
 // rows and their chunk sums, laid out as for the generated kernels)
 int launch_tp_generic_bwd(const TPBwdArgs& a, const GenericTPInfo& g);
-// rp[n] = first edge with dst >= n, n = 0 .. n_nodes (sorted dst)
-int launch_rowptr_build(const void* dst, int idx, int64_t n_edges, int64_t n_nodes, void* rp, void* stream);
+// rp[n] = first i with key(i) >= n, n = 0 .. n_nodes; key(i) = keys[i]
+// (sorted destinations), or keys[perm[i]] when perm is given (the sources
+// in src_perm order)
+int launch_rowptr_build(const void* keys, const void* perm, int idx, int64_t n_edges, int64_t n_nodes, void* rp,
+                        void* stream);
 int launch_symcon_generic_bwd(const SymconBwdArgs& a, const GenericSymconInfo& g);
 // LDS the table-driven backward kernels need (bytes), for the C ABI's checks
 size_t tp_generic_bwd_lds(int nx, int64_t dim2, int dtype);

@@ -181,7 +181,8 @@ __device__ __forceinline__ T wave_total(T v) {
 template <typename T, typename Index, int LAYOUT>
 __global__ void __launch_bounds__(kGW)
 tp_generic_bwd_edge_kernel(const T* __restrict__ x, const T* __restrict__ sh, const T* __restrict__ w,
-                           const Index* __restrict__ src, const Index* __restrict__ dst, const T* __restrict__ g,
+                           const Index* __restrict__ src, const Index* __restrict__ dst,
+                           const Index* __restrict__ row_ptr, const T* __restrict__ g,
                            const GPath* __restrict__ paths, const GNz* __restrict__ nz, int np, int tiles,
                            int64_t dim1, int64_t dim2, int64_t dimo, int64_t numel, int64_t n_src,
                            int64_t n_edges, int64_t n_nodes, int64_t w_stride, int batch, int mean,
@@ -191,7 +192,7 @@ tp_generic_bwd_edge_kernel(const T* __restrict__ x, const T* __restrict__ sh, co
   const int64_t node = blockIdx.x;
   const int lane = threadIdx.x;
   int64_t e0, e1;
-  edge_range(dst, n_edges, batch, node, e0, e1);
+  edge_range(dst, n_edges, batch, node, e0, e1, row_ptr);
   auto zero_edge = [&](int64_t e) {
     for (int64_t c = lane; c < numel; c += kGW) dw[e * numel + c] = T(0);
     for (int64_t j = lane; j < dim2; j += kGW) dsh[e * dim2 + j] = T(0);
@@ -245,7 +246,9 @@ tp_generic_bwd_edge_kernel(const T* __restrict__ x, const T* __restrict__ sh, co
 template <typename T, typename Index, int LAYOUT>
 __global__ void __launch_bounds__(kGW)
 tp_generic_bwd_src_kernel(const T* __restrict__ sh, const T* __restrict__ w, const Index* __restrict__ src,
-                          const Index* __restrict__ dst, const Index* __restrict__ perm, const T* __restrict__ g,
+                          const Index* __restrict__ dst, const Index* __restrict__ row_ptr,
+                          const Index* __restrict__ src_row_ptr, const Index* __restrict__ perm,
+                          const T* __restrict__ g,
                           const GPath* __restrict__ paths, const GNz* __restrict__ nz, int np,
                           const GIn* __restrict__ in, int n_in, int nx, int64_t dim1, int64_t dim2, int64_t dimo,
                           int64_t n_edges, int64_t n_nodes, int64_t w_stride, int batch, int mean,
@@ -260,6 +263,11 @@ tp_generic_bwd_src_kernel(const T* __restrict__ sh, const T* __restrict__ w, con
   if (batch) {
     i0 = s;
     i1 = s < n_edges ? s + 1 : s;
+  } else if (src_row_ptr) {  // the caller's row pointers, clamped to [0, n_edges]
+    const int64_t r0 = static_cast<int64_t>(src_row_ptr[s]);
+    const int64_t r1 = static_cast<int64_t>(src_row_ptr[s + 1]);
+    i0 = r0 < 0 ? 0 : (r0 > n_edges ? n_edges : r0);
+    i1 = r1 < i0 ? i0 : (r1 > n_edges ? n_edges : r1);
   } else {
     i0 = lower_bound_perm(src, perm, n_edges, 0, n_edges, s);
     i1 = lower_bound_perm(src, perm, n_edges, i0, n_edges, s + 1);
@@ -272,7 +280,7 @@ tp_generic_bwd_src_kernel(const T* __restrict__ sh, const T* __restrict__ w, con
     T scale = T(1);
     if (mean && !batch) {
       int64_t d0, d1;
-      edge_range(dst, n_edges, 0, d, d0, d1);
+      edge_range(dst, n_edges, 0, d, d0, d1, row_ptr);
       scale = T(1) / static_cast<T>(d1 - d0);
     }
     const T* grow = g + d * dimo;
@@ -321,7 +329,8 @@ int tp_generic_bwd_launch(const TPBwdArgs& a, const GenericTPInfo& g) {
   hipLaunchKernelGGL((tp_generic_bwd_edge_kernel<T, Index, LAYOUT>), dim3(static_cast<unsigned>(a.n_nodes)),
                      dim3(kGW), static_cast<size_t>(g.dim2 > 0 ? g.dim2 : 1) * kGW * sizeof(T), st,
                      static_cast<const T*>(a.x), static_cast<const T*>(a.sh), static_cast<const T*>(a.w),
-                     static_cast<const Index*>(a.src), static_cast<const Index*>(a.dst), static_cast<const T*>(a.g),
+                     static_cast<const Index*>(a.src), static_cast<const Index*>(a.dst),
+                     static_cast<const Index*>(a.row_ptr), static_cast<const T*>(a.g),
                      g.paths, g.nz, g.np, tiles, g.dim1, g.dim2, g.dimo, g.numel, a.n_src, a.n_edges, a.n_nodes,
                      w_stride, a.batch, a.mean, dwe, dsh);
   int rc = static_cast<int>(hipGetLastError());
@@ -344,7 +353,8 @@ int tp_generic_bwd_launch(const TPBwdArgs& a, const GenericTPInfo& g) {
                        dim3(static_cast<unsigned>(a.n_src), static_cast<unsigned>(tiles)), dim3(kGW),
                        static_cast<size_t>(g.nx > 0 ? g.nx : 1) * kGW * sizeof(T), st, static_cast<const T*>(a.sh),
                        static_cast<const T*>(a.w), static_cast<const Index*>(a.src),
-                       static_cast<const Index*>(a.dst), static_cast<const Index*>(a.perm),
+                       static_cast<const Index*>(a.dst), static_cast<const Index*>(a.row_ptr),
+                       static_cast<const Index*>(a.src_row_ptr), static_cast<const Index*>(a.perm),
                        static_cast<const T*>(a.g), g.paths, g.nz, g.np, g.in, g.n_in, g.nx, g.dim1, g.dim2, g.dimo,
                        a.n_edges, a.n_nodes, w_stride, a.batch, a.mean, dx);
   }
@@ -600,17 +610,28 @@ int launch_symcon_generic(const SymconArgs& a, const GenericSymconInfo& g) {
 
 namespace kern {
 
-// rp[n] = first e with dst[e] >= n, for n = 0 .. n_nodes (dst sorted
-// ascending): one thread per entry, a binary search each.
+// rp[n] = first i with key(i) >= n, for n = 0 .. n_nodes, where key(i) =
+// keys[i] (destinations sorted ascending), or keys[perm[i]] (sources in the
+// order of their stable argsort; a perm entry outside [0, n_edges) counts
+// as larger than every key): one thread per entry, a binary search each.
 template <typename Index>
 __global__ void __launch_bounds__(256)
-rowptr_build_kernel(const Index* __restrict__ dst, int64_t n_edges, int64_t n_nodes, Index* __restrict__ rp) {
+rowptr_build_kernel(const Index* __restrict__ keys, const Index* __restrict__ perm, int64_t n_edges,
+                    int64_t n_nodes, Index* __restrict__ rp) {
   const int64_t n = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
   if (n > n_nodes) return;
+  auto below = [&](int64_t i) -> bool {
+    int64_t e = i;
+    if (perm) {
+      e = static_cast<int64_t>(perm[i]);
+      if (e < 0 || e >= n_edges) return false;
+    }
+    return static_cast<int64_t>(keys[e]) < n;
+  };
   int64_t lo = 0, hi = n_edges;
   while (lo < hi) {
     const int64_t mid = lo + (hi - lo) / 2;
-    if (static_cast<int64_t>(dst[mid]) < n)
+    if (below(mid))
       lo = mid + 1;
     else
       hi = mid;
@@ -620,16 +641,17 @@ rowptr_build_kernel(const Index* __restrict__ dst, int64_t n_edges, int64_t n_no
 
 }  // namespace kern
 
-int launch_rowptr_build(const void* dst, int idx, int64_t n_edges, int64_t n_nodes, void* rp, void* stream) {
+int launch_rowptr_build(const void* keys, const void* perm, int idx, int64_t n_edges, int64_t n_nodes, void* rp,
+                        void* stream) {
   const unsigned blocks = static_cast<unsigned>((n_nodes + 1 + 255) / 256);
   if (idx == kI64)
     hipLaunchKernelGGL((kern::rowptr_build_kernel<int64_t>), dim3(blocks), dim3(256), 0,
-                       static_cast<hipStream_t>(stream), static_cast<const int64_t*>(dst), n_edges, n_nodes,
-                       static_cast<int64_t*>(rp));
+                       static_cast<hipStream_t>(stream), static_cast<const int64_t*>(keys),
+                       static_cast<const int64_t*>(perm), n_edges, n_nodes, static_cast<int64_t*>(rp));
   else
     hipLaunchKernelGGL((kern::rowptr_build_kernel<int32_t>), dim3(blocks), dim3(256), 0,
-                       static_cast<hipStream_t>(stream), static_cast<const int32_t*>(dst), n_edges, n_nodes,
-                       static_cast<int32_t*>(rp));
+                       static_cast<hipStream_t>(stream), static_cast<const int32_t*>(keys),
+                       static_cast<const int32_t*>(perm), n_edges, n_nodes, static_cast<int32_t*>(rp));
   return static_cast<int>(hipGetLastError());
 }
 

@@ -27,6 +27,10 @@
 //  K2 (source-major): one wave per (source node, channel tile) sums the
 //     messages of its edges, taken in the order of src_perm (a stable
 //     argsort of src), and writes dx[s] (zero for a source without edges).
+//     Its range of src_perm positions comes from the caller's source row
+//     pointers when given, else from a search of the sorted sources that a
+//     small kernel writes first; K1's destination ranges likewise come
+//     from row pointers or from a search of dst.
 //  Fold (several tiles only): dsh[e] = sum over tiles of part[tile][e].
 // In batch mode (edge e is node e and source e) K1 writes m[e] straight into
 // dx and K2 is not launched.
@@ -48,13 +52,17 @@ namespace kern {
 // set) and adds the partner's copy of that half; the remaining steps are a
 // plain butterfly.  D - 1 + 6 - log2(D) shuffles in all.  Afterwards every
 // lane L holds the total of value L / (64 / D).
-template <typename T, int D>
+// The same over each group of W consecutive lanes (W a power of two, D <=
+// W <= 64): afterwards lane L of a group holds the group's total of value
+// L / (W / D).
+template <typename T, int D, int W = kWave>
 __device__ __forceinline__ T wave_sum_many(T (&v)[D]) {
-  static_assert(D >= 1 && D <= kWave && (D & (D - 1)) == 0, "D must be a power of two <= 64");
+  static_assert(D >= 1 && D <= W && W <= kWave && (D & (D - 1)) == 0 && (W & (W - 1)) == 0,
+                "D and W must be powers of two, D <= W <= 64");
   const int lane = threadIdx.x % kWave;
   int n = D;
 #pragma unroll
-  for (int off = kWave / 2; off >= 1; off >>= 1) {
+  for (int off = W / 2; off >= 1; off >>= 1) {
     if (n > 1) {
       const bool upper = lane & off;
 #pragma unroll
@@ -138,9 +146,9 @@ __device__ __forceinline__ void store_msg_staged(T* __restrict__ grow, T* __rest
 template <class S, typename T, typename Index, int LAYOUT, int CPL, bool SHW>
 __global__ void __launch_bounds__(kWave)
 tp_bwd_edge_kernel(const T* __restrict__ x, const T* __restrict__ sh, const T* __restrict__ w,
-                   const Index* __restrict__ src, const Index* __restrict__ dst, const T* __restrict__ g,
-                   int64_t n_src, int64_t n_edges, int64_t n_nodes, int mul, int batch, int mean,
-                   T* __restrict__ dw, T* __restrict__ dsh_out, T* __restrict__ msg) {
+                   const Index* __restrict__ src, const Index* __restrict__ dst, const Index* __restrict__ row_ptr,
+                   const T* __restrict__ g, int64_t n_src, int64_t n_edges, int64_t n_nodes, int mul, int batch,
+                   int mean, T* __restrict__ dw, T* __restrict__ dsh_out, T* __restrict__ msg) {
   constexpr int DP = Pow2Ceil<S::D2>::value;
   constexpr bool PF = CPL == 2;
   const int64_t node = blockIdx.x;
@@ -155,7 +163,7 @@ tp_bwd_edge_kernel(const T* __restrict__ x, const T* __restrict__ sh, const T* _
   const int tile0 = blockIdx.y * (kWave * CPL);
 
   int64_t e0, e1;
-  edge_range(dst, n_edges, batch, node, e0, e1);
+  edge_range(dst, n_edges, batch, node, e0, e1, row_ptr);
 
   auto zero_edge = [&](int64_t e) {
     T z[CPL][S::NX];
@@ -281,6 +289,83 @@ tp_bwd_edge_kernel(const T* __restrict__ x, const T* __restrict__ sh, const T* _
   }
 }
 
+// Edge-parallel form of K1 for multiplicities up to 32 (one channel per
+// lane): every output of K1 belongs to one edge (dw[e], dsh[e] and the
+// message m[e] need only g[dst[e]], x[src[e]], w[e] and sh[e]), so each
+// half-wave takes one edge, with its destination's gradient row loaded per
+// edge instead of once per destination.  The destination-major walk visits
+// a destination's edges one after another, which on small graphs leaves a
+// chain of dependent loads per edge (and half the lanes idle at 32
+// channels); here every edge is in flight at once.  The harmonic gradient
+// is reduced over the half-wave's lanes.  An edge whose destination or
+// source lies outside its range gets zero gradients and a zero message.
+// With reduce="mean" the destination's edge count comes from the row
+// pointers (the host uses this form then only with them).
+constexpr int kHalfWave = 32;
+
+template <class S, typename T, typename Index, int LAYOUT, bool SHW>
+__global__ void __launch_bounds__(kWave)
+tp_bwd_edge_half_kernel(const T* __restrict__ x, const T* __restrict__ sh, const T* __restrict__ w,
+                        const Index* __restrict__ src, const Index* __restrict__ dst,
+                        const Index* __restrict__ row_ptr, const T* __restrict__ g, int64_t n_src,
+                        int64_t n_edges, int64_t n_nodes, int mul, int batch, int mean, T* __restrict__ dw,
+                        T* __restrict__ dsh, T* __restrict__ msg) {
+  constexpr int DP = Pow2Ceil<S::D2>::value;
+  static_assert(DP <= kHalfWave, "harmonics wider than a half-wave");
+  const int lane = threadIdx.x % kWave;
+  const int u = lane % kHalfWave;
+  const int64_t e = static_cast<int64_t>(blockIdx.x) * 2 + lane / kHalfWave;
+  const bool edge_ok = e < n_edges;
+  const int64_t ee = edge_ok ? e : n_edges - 1;  // the idle half of an odd count repeats the last edge's loads
+  const int ul = u < mul ? u : 0;
+  const int64_t numel = static_cast<int64_t>(mul) * S::NP;
+  const int64_t dim1 = static_cast<int64_t>(mul) * S::NX;
+  const int64_t d = batch ? ee : static_cast<int64_t>(dst[ee]);
+  const int64_t s = batch ? ee : static_cast<int64_t>(src[ee]);
+  const bool ok = d >= 0 && d < n_nodes && s >= 0 && s < n_src;
+  T gv[1][S::NK], xv[1][S::NX], wv[1][S::NP], shv[S::D2];
+  S::template load_gs<T, LAYOUT, 1>(g + (ok ? d : 0) * (static_cast<int64_t>(mul) * S::NK), mul, ul, gv);
+  S::template load_xs<T, LAYOUT, 1>(x + (ok ? s : 0) * dim1, mul, ul, xv);
+  const T* wrow = w + (SHW ? 0 : ee * numel) + ul;
+#pragma unroll
+  for (int p = 0; p < S::NP; ++p) wv[0][p] = __builtin_nontemporal_load(wrow + p * mul);
+#pragma unroll
+  for (int j = 0; j < S::D2; ++j) shv[j] = sh[ee * S::D2 + j];
+  T scale = ok ? T(1) : T(0);  // zero operands give zero gradients and message
+  if (mean && ok && row_ptr) {  // the forward divided the row by its number of edges
+    const int64_t c = static_cast<int64_t>(row_ptr[d + 1]) - static_cast<int64_t>(row_ptr[d]);
+    scale = T(1) / static_cast<T>(c > 0 ? c : 1);
+  }
+#pragma unroll
+  for (int k = 0; k < S::NK; ++k) gv[0][k] *= scale;
+  if (!ok) {
+#pragma unroll
+    for (int i = 0; i < S::NX; ++i) xv[0][i] = T(0);
+#pragma unroll
+    for (int p = 0; p < S::NP; ++p) wv[0][p] = T(0);
+#pragma unroll
+    for (int k = 0; k < S::NK; ++k) gv[0][k] = T(0);
+  }
+  T dwv[1][S::NP];
+  T mxv[1][S::NX];
+  T hsh[DP];
+  S::template bwd<T, 1>(xv, shv, wv, gv, dwv, mxv, reinterpret_cast<T(&)[S::D2]>(hsh));
+#pragma unroll
+  for (int j = S::D2; j < DP; ++j) hsh[j] = T(0);
+  if (!edge_ok || u >= mul) {
+#pragma unroll
+    for (int j = 0; j < DP; ++j) hsh[j] = T(0);
+  }
+  if (edge_ok && u < mul) {
+#pragma unroll
+    for (int p = 0; p < S::NP; ++p) st1<T, true>(dw + e * numel + p * mul + u, dwv[0][p]);
+    S::template store_xs<T, LAYOUT, 1, true>(msg + e * dim1, mul, u, mxv);
+  }
+  const T tot = wave_sum_many<T, DP, kHalfWave>(hsh);
+  constexpr int stride = kHalfWave / DP;
+  if (edge_ok && u % stride == 0 && u / stride < S::D2) dsh[e * S::D2 + u / stride] = tot;
+}
+
 // First i in [lo, hi) with src[perm[i]] >= key (src[perm[.]] ascending),
 // by the same wave-cooperative search as the forward.  perm entries outside
 // [0, n_edges) compare as +infinity.  (The source sums of the other
@@ -330,18 +415,29 @@ constexpr int kSrcBatch = 4;
 
 template <class S, typename T, typename Index, int LAYOUT, int CPL>
 __global__ void __launch_bounds__(kWave)
-tp_bwd_src_kernel(const int32_t* __restrict__ keys, const Index* __restrict__ perm, const T* __restrict__ msg,
-                  int64_t n_edges, int mul, T* __restrict__ dx) {
+tp_bwd_src_kernel(const int32_t* __restrict__ keys, const Index* __restrict__ src_row_ptr,
+                  const Index* __restrict__ perm, const T* __restrict__ msg, int64_t n_edges, int mul,
+                  T* __restrict__ dx) {
   const int64_t s = blockIdx.x;
   const int lane = threadIdx.x % kWave;
   const int ub = blockIdx.y * (kWave * CPL) + lane * CPL;
   const bool active = ub < mul;
   const int ubl = active ? ub : 0;
   const int64_t dim1 = static_cast<int64_t>(mul) * S::NX;
-  // keys ascend (src_perm sorts the sources): the same wave-cooperative
-  // search as the forward's destination ranges
-  const int64_t i0 = lower_bound_wave(keys, 0, n_edges, s);
-  const int64_t i1 = lower_bound_wave(keys, i0, n_edges, s + 1);
+  // the source's range of perm positions: two loads from the caller's row
+  // pointers (clamped to [0, n_edges]), or, as the keys ascend (src_perm
+  // sorts the sources), the same wave-cooperative search as the forward's
+  // destination ranges
+  int64_t i0, i1;
+  if (src_row_ptr) {
+    const int64_t r0 = static_cast<int64_t>(src_row_ptr[s]);
+    const int64_t r1 = static_cast<int64_t>(src_row_ptr[s + 1]);
+    i0 = r0 < 0 ? 0 : (r0 > n_edges ? n_edges : r0);
+    i1 = r1 < i0 ? i0 : (r1 > n_edges ? n_edges : r1);
+  } else {
+    i0 = lower_bound_wave(keys, 0, n_edges, s);
+    i1 = lower_bound_wave(keys, i0, n_edges, s + 1);
+  }
   T acc[CPL][S::NX];
 #pragma unroll
   for (int c = 0; c < CPL; ++c)
@@ -445,18 +541,36 @@ int tp_bwd_launch(const TPBwdArgs& a) {
   T* const part =
       tiles > 1 ? reinterpret_cast<T*>(ws + (a.batch ? 0 : round_up_256(a.n_edges * dim1 * static_cast<int64_t>(sizeof(T))))) : dsh;
   const dim3 grid(static_cast<unsigned>(a.n_nodes), static_cast<unsigned>(tiles));
-  if (a.shared_w)
+  // edge-parallel form: multiplicity up to 32, and with reduce="mean" only
+  // when row pointers give the destinations' edge counts (its grid of
+  // n_edges / 2 waves stays below 2^32 work-items up to 2^26 edges)
+  constexpr bool kHalfOk = CPL == 1 && Pow2Ceil<S::D2>::value <= kHalfWave;
+  const bool half = kHalfOk && a.mul <= kHalfWave && (!a.mean || a.row_ptr) && a.n_edges <= (int64_t(1) << 26);
+  const dim3 hgrid(static_cast<unsigned>((a.n_edges + 1) / 2));
+  if (half && a.shared_w)
+    hipLaunchKernelGGL((tp_bwd_edge_half_kernel<S, T, Index, LAYOUT, true>), hgrid, dim3(kWave), 0, st,
+                       static_cast<const T*>(a.x), static_cast<const T*>(a.sh), static_cast<const T*>(a.w),
+                       static_cast<const Index*>(a.src), static_cast<const Index*>(a.dst),
+                       static_cast<const Index*>(a.row_ptr), static_cast<const T*>(a.g), a.n_src, a.n_edges,
+                       a.n_nodes, a.mul, a.batch, a.mean, dwe, part, msg);
+  else if (half)
+    hipLaunchKernelGGL((tp_bwd_edge_half_kernel<S, T, Index, LAYOUT, false>), hgrid, dim3(kWave), 0, st,
+                       static_cast<const T*>(a.x), static_cast<const T*>(a.sh), static_cast<const T*>(a.w),
+                       static_cast<const Index*>(a.src), static_cast<const Index*>(a.dst),
+                       static_cast<const Index*>(a.row_ptr), static_cast<const T*>(a.g), a.n_src, a.n_edges,
+                       a.n_nodes, a.mul, a.batch, a.mean, dwe, part, msg);
+  else if (a.shared_w)
     hipLaunchKernelGGL((tp_bwd_edge_kernel<S, T, Index, LAYOUT, CPL, true>), grid, dim3(kWave), 0, st,
                        static_cast<const T*>(a.x), static_cast<const T*>(a.sh), static_cast<const T*>(a.w),
                        static_cast<const Index*>(a.src), static_cast<const Index*>(a.dst),
-                       static_cast<const T*>(a.g), a.n_src, a.n_edges, a.n_nodes, a.mul, a.batch, a.mean, dwe, part,
-                       msg);
+                       static_cast<const Index*>(a.row_ptr), static_cast<const T*>(a.g), a.n_src, a.n_edges,
+                       a.n_nodes, a.mul, a.batch, a.mean, dwe, part, msg);
   else
     hipLaunchKernelGGL((tp_bwd_edge_kernel<S, T, Index, LAYOUT, CPL, false>), grid, dim3(kWave), 0, st,
                        static_cast<const T*>(a.x), static_cast<const T*>(a.sh), static_cast<const T*>(a.w),
                        static_cast<const Index*>(a.src), static_cast<const Index*>(a.dst),
-                       static_cast<const T*>(a.g), a.n_src, a.n_edges, a.n_nodes, a.mul, a.batch, a.mean, dwe, part,
-                       msg);
+                       static_cast<const Index*>(a.row_ptr), static_cast<const T*>(a.g), a.n_src, a.n_edges,
+                       a.n_nodes, a.mul, a.batch, a.mean, dwe, part, msg);
   int rc = static_cast<int>(hipGetLastError());
   if (rc) return rc;
   if (a.shared_w) {
@@ -482,14 +596,16 @@ int tp_bwd_launch(const TPBwdArgs& a) {
     fill_zero(dx + a.n_edges * dim1, (a.n_src - a.n_edges) * dim1, st);
   } else if (a.n_src > 0) {
     int32_t* const keys = reinterpret_cast<int32_t*>(ws + a.keys_ws_off);
-    const int64_t blocks = (a.n_edges + 255) / 256;
-    hipLaunchKernelGGL((tp_bwd_keys_kernel<Index>), dim3(static_cast<unsigned>(blocks < 4096 ? blocks : 4096)),
-                       dim3(256), 0, st, static_cast<const Index*>(a.src), static_cast<const Index*>(a.perm),
-                       a.n_edges, a.n_src, keys);
+    if (!a.src_row_ptr) {  // the sorted sources, for the source kernel's range search
+      const int64_t blocks = (a.n_edges + 255) / 256;
+      hipLaunchKernelGGL((tp_bwd_keys_kernel<Index>), dim3(static_cast<unsigned>(blocks < 4096 ? blocks : 4096)),
+                         dim3(256), 0, st, static_cast<const Index*>(a.src), static_cast<const Index*>(a.perm),
+                         a.n_edges, a.n_src, keys);
+    }
     hipLaunchKernelGGL((tp_bwd_src_kernel<S, T, Index, LAYOUT, CPL>),
                        dim3(static_cast<unsigned>(a.n_src), static_cast<unsigned>(tiles)), dim3(kWave), 0, st,
-                       keys, static_cast<const Index*>(a.perm), static_cast<const T*>(a.workspace), a.n_edges,
-                       a.mul, dx);
+                       keys, static_cast<const Index*>(a.src_row_ptr), static_cast<const Index*>(a.perm),
+                       static_cast<const T*>(a.workspace), a.n_edges, a.mul, dx);
   }
   return static_cast<int>(hipGetLastError());
 }

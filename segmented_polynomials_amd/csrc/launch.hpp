@@ -39,6 +39,8 @@ struct TPBwdArgs {
   const void* src;    // [n_edges] or null (batch mode)
   const void* dst;    // [n_edges], sorted ascending, or null (batch mode)
   const void* perm;   // [n_edges] edge ids ordered by src, or null (batch mode)
+  const void* row_ptr;      // [n_nodes + 1] destination row pointers, or null (ranges searched in dst)
+  const void* src_row_ptr;  // [n_src + 1] source row pointers over perm order, or null (searched)
   const void* g;      // [n_nodes, dim_out] gradient of the output
   void* dx;           // [n_src, dim1]
   void* dsh;          // [n_edges, dim2]

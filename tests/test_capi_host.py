@@ -378,6 +378,30 @@ def test_rowptr_errors():
     assert rf(h._h, p, 4, p, p, p, p, 0, 5, 0, None, None) == sp.OK          # no destinations
 
 
+def test_bwd_rowptr_errors():
+    p = ctypes.c_void_p(16)   # never dereferenced: every call below fails validation or returns early
+    sb, bb = sp.lib.tp_src_rowptr_build, sp.lib.tp_conv_bwd_rowptr
+    assert sb(None, p, 0, 5, 3, p, None) == sp.E_INVALID          # null src with edges
+    assert sb(p, None, 0, 5, 3, p, None) == sp.E_INVALID          # null src_perm with edges
+    assert sb(p, p, 0, 5, 3, None, None) == sp.E_INVALID          # null row pointers
+    assert sb(p, p, 7, 5, 3, p, None) == sp.E_INVALID             # index dtype
+    assert sb(p, p, 0, 5, -1, p, None) == sp.E_INVALID
+    assert sb(p, p, 0, 1 << 31, 3, p, None) == sp.E_UNSUPPORTED   # int32 pointers
+    h = sp.tp_create("8x0e+8x1o", "0e+1o", "0e+1o")
+    args = lambda **k: [k.get(n, d) for n, d in (
+        ("h", h._h), ("x", p), ("n_src", 4), ("sh", p), ("w", p), ("src", p), ("dst", p), ("perm", p), ("rp", p),
+        ("srp", p), ("idx", 0), ("n_edges", 5), ("n_nodes", 3), ("g", p), ("gx", p), ("gsh", p), ("gw", p),
+        ("ws", p), ("wsb", 0), ("stream", None))]
+    assert bb(*args(h=None)) == sp.E_INVALID
+    assert bb(*args(rp=None)) == sp.E_INVALID                     # null row_ptr
+    assert bb(*args(srp=None)) == sp.E_INVALID                    # null src_row_ptr
+    assert bb(*args(dst=None)) == sp.E_INVALID                    # the table-driven kernels read dst
+    assert bb(*args(perm=None)) == sp.E_INVALID
+    assert bb(*args(idx=5)) == sp.E_INVALID
+    assert bb(*args(ws=None)) == sp.E_INVALID                     # workspace missing
+    assert bb(*args(n_src=0, n_edges=0, n_nodes=0)) == sp.OK      # nothing to do
+
+
 def test_fctp_errors_and_workspace():
     raw = ctypes.c_void_p()
     c = sp.lib.fctp_create

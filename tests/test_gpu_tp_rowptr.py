@@ -1,10 +1,12 @@
 """GPU checks of the row-pointer form of the channelwise convolution: the
 row pointers built on the device equal a host binary search of the sorted
-destinations, and tp_conv_fwd_rowptr reproduces tp_conv_fwd bit for bit
-(the same edges in the same order) on the specialised kernels (molecular
-batch, medium graph), the destination-split kernel and the table-driven
-kernel, with sum and mean, shared weights and both index widths; the
-forward is also checked against the float64 oracle (scaled error <= 1e-5)."""
+destinations (and of the sources in src_perm order), tp_conv_fwd_rowptr
+reproduces tp_conv_fwd and tp_conv_bwd_rowptr reproduces tp_conv_bwd bit
+for bit (the same edges in the same order) on the specialised kernels
+(molecular batch, medium graph), the destination-split kernel and the
+table-driven kernel, with sum and mean, shared weights and both index
+widths; forward and backward are also checked against the float64 oracle
+(scaled error <= 1e-5)."""
 
 import numpy as np
 import pytest
@@ -124,3 +126,120 @@ def test_rowptr_validate():
     end = torch.tensor([0, 5, 10, 15, 20, 25, 29], dtype=torch.int32, device="cuda")
     with pytest.raises(sp.SegpolyError, match="-7"):
         sp.tp_conv_fwd_rowptr(h, x, s, w, src, end)
+
+
+@pytest.mark.parametrize("idx", ["int32", "int64"])
+def test_src_rowptr_build_matches_host_search(idx):
+    sp = _sp()
+    import torch
+    rng = np.random.default_rng(83)
+    n_src, n_e = 700, 15000
+    src = rng.integers(0, n_src, n_e)
+    src[:9] = 3
+    perm = np.argsort(src, kind="stable")
+    S, P = dev(src, getattr(torch, idx)), dev(perm, getattr(torch, idx))
+    announce(f"src rowptr build {idx}")
+    rp = sp.tp_src_rowptr_build(S, P, n_src).cpu().numpy()
+    ref = np.searchsorted(src[perm], np.arange(n_src + 1), side="left")
+    assert rp.dtype == np.dtype(idx) and np.array_equal(rp, ref)
+
+
+def _bwd_pair(sp, h, inp, it, g):
+    import torch
+    td = torch.float32 if h.dtype == "f32" else torch.float64
+    x, s, w, G = dev(inp["x"], td), dev(inp["sh"], td), dev(inp["w"], td), dev(g, td)
+    src, dst = dev(inp["src"], it), dev(inp["dst"], it)
+    perm = dev(np.argsort(inp["src"], kind="stable"), it)
+    n = inp["n_nodes"]
+    a = sp.tp_conv_bwd(h, x, s, w, G, src, dst, perm, n_nodes=n)
+    rp = sp.tp_rowptr_build(dst, n)
+    srp = sp.tp_src_rowptr_build(src, perm, x.shape[0])
+    b = sp.tp_conv_bwd_rowptr(h, x, s, w, G, src, dst, perm, rp, srp)
+    torch.cuda.synchronize()
+    return [t.cpu().numpy() for t in a], [t.cpu().numpy() for t in b]
+
+
+@pytest.mark.parametrize("n", [2, 3])
+@pytest.mark.parametrize("idx", ["int32", "int64"])
+def test_workloads_bwd_rowptr_equals_search(n, idx):
+    sp = _sp()
+    import torch
+    wl = workloads.WORKLOADS[n]
+    o = otp.ChannelwiseTP(wl.irreps_in1, wl.irreps_in2, wl.irreps_out)
+    inp = workloads.tp_inputs(wl, o.weight_fan_in())
+    lay = wl.layouts[0]
+    h = sp.tp_create(wl.irreps_in1, wl.irreps_in2, wl.irreps_out, layout=lay)
+    g = workloads.output_gradient(inp["n_nodes"], h.dim_out, "f32", seed=85)
+    announce(f"rowptr backward {wl.name} {idx} ({h.kernel_name})")
+    a, b = _bwd_pair(sp, h, inp, getattr(torch, idx), g)
+    for u, v in zip(a, b):
+        assert np.array_equal(u, v)
+    args = (inp["x"], inp["sh"], inp["w"], inp["src"], inp["dst"], inp["n_nodes"], g)
+    ref = o.conv_vjp(*args, layout=lay)
+    scale = o.conv_vjp(*args, layout=lay, absolute=True)
+    for got, r, sc, name in zip(b, ref, scale, ("dx", "dsh", "dw")):
+        check_scaled(got, r, sc, "f32", f"rowptr bwd {name}")
+
+
+@pytest.mark.parametrize("case", [
+    dict(force_generic=True),
+    dict(force_generic=True, reduce="mean"),
+    dict(reduce="mean"),
+    dict(shared_weights=True),
+])
+def test_bwd_rowptr_variants(case):
+    """Table-driven kernels (sum and mean), mean reduction and one shared
+    weight row, on a ragged graph with isolated destinations and sources."""
+    sp = _sp()
+    import torch
+    in1, in2, filt = "16x0e+16x1o+16x2e", "0e+1o+2e", "0e+1o+2e"
+    o = otp.ChannelwiseTP(in1, in2, filt)
+    rng = np.random.default_rng(84)
+    n_src, n_dst, n_e = 40, 37, 400
+    src = rng.integers(0, n_src - 3, n_e)       # the last sources have no edges
+    dst = np.sort(rng.integers(0, n_dst, n_e))
+    rows = 1 if case.get("shared_weights") else n_e
+    inp = dict(x=rng.standard_normal((n_src, o.dim_in1)).astype(np.float32).astype(np.float64),
+               sh=rng.standard_normal((n_e, o.dim_in2)).astype(np.float32).astype(np.float64),
+               w=rng.standard_normal((rows, o.weight_numel)).astype(np.float32).astype(np.float64),
+               src=src, dst=dst, n_nodes=n_dst)
+    g = rng.standard_normal((n_dst, o.dim_out)).astype(np.float32).astype(np.float64)
+    h = sp.tp_create(in1, in2, filt, layout="ir_mul", **case)
+    announce(f"rowptr backward variant {case} ({h.kernel_name})")
+    a, b = _bwd_pair(sp, h, inp, torch.int32, g)
+    for u, v in zip(a, b):
+        assert np.array_equal(u, v)
+    kw = dict(layout="ir_mul", reduce=case.get("reduce", "sum"), shared_weights=case.get("shared_weights", False))
+    ref = o.conv_vjp(inp["x"], inp["sh"], inp["w"], src, dst, n_dst, g, **kw)
+    scale = o.conv_vjp(inp["x"], inp["sh"], inp["w"], src, dst, n_dst, g, absolute=True, **kw)
+    for got, r, sc, name in zip(b, ref, scale, ("dx", "dsh", "dw")):
+        check_scaled(got, r, sc, "f32", f"rowptr bwd variant {name}")
+
+
+def test_bwd_rowptr_validate():
+    """With VALIDATE each pointer array must equal what its builder gives:
+    E_RANGE for a wrong entry of either."""
+    sp = _sp()
+    import torch
+    h = sp.tp_create("8x0e+8x1o", "0e+1o", "0e+1o", validate=True)
+    n_e, n, n_src = 30, 6, 10
+    x = torch.zeros((n_src, h.dim_in1), device="cuda")
+    s = torch.zeros((n_e, h.dim_in2), device="cuda")
+    w = torch.zeros((n_e, h.weight_numel), device="cuda")
+    g = torch.zeros((n, h.dim_out), device="cuda")
+    src_h = np.arange(n_e) % n_src
+    src = dev(src_h, torch.int32)
+    dst = dev(np.repeat(np.arange(n), 5), torch.int32)
+    perm = dev(np.argsort(src_h, kind="stable"), torch.int32)
+    rp = sp.tp_rowptr_build(dst, n)
+    srp = sp.tp_src_rowptr_build(src, perm, n_src)
+    announce("rowptr backward validate")
+    sp.tp_conv_bwd_rowptr(h, x, s, w, g, src, dst, perm, rp, srp)
+    bad = rp.clone()
+    bad[2] += 1
+    with pytest.raises(sp.SegpolyError, match="-7"):
+        sp.tp_conv_bwd_rowptr(h, x, s, w, g, src, dst, perm, bad, srp)
+    bad = srp.clone()
+    bad[4] -= 1
+    with pytest.raises(sp.SegpolyError, match="-7"):
+        sp.tp_conv_bwd_rowptr(h, x, s, w, g, src, dst, perm, rp, bad)
