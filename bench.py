@@ -934,6 +934,26 @@ def other_workloads(torch, sp, workloads, dev, args):
                              "kernel_us_mean": 1e3 * sum(per_r) / len(per_r),
                              "us_per_call": wall_r * 1e6 / steps, "edges_per_s": E * steps / wall_r,
                              "what": "tp_conv_fwd_rowptr with row pointers built once (input set 0, warm)"}
+            # backward on the same graph: with the in-kernel searches, and
+            # with destination and source row pointers built once
+            g = torch.from_numpy(workloads.output_gradient(N, h.dim_out, wl.dtype, seed=74)).to(dev, t["x"].dtype)
+            perm = torch.argsort(t["src"], stable=True).to(t["src"].dtype)
+            gx, gsh, gw = torch.empty_like(t["x"]), torch.empty_like(t["sh"]), torch.empty_like(t["w"])
+            ws = torch.empty(sp.tp_conv_bwd_workspace(h, E), dtype=torch.uint8, device=dev)
+            srp = sp.tp_src_rowptr_build(t["src"], perm, t["x"].shape[0])
+            kw = dict(workspace=ws, grad_x=gx, grad_sh=gsh, grad_w=gw)
+            fb = lambda: sp.tp_conv_bwd(h, t["x"], t["sh"], t["w"], g, t["src"], t["dst"], perm, n_nodes=N, **kw)
+            fbr = lambda: sp.tp_conv_bwd_rowptr(h, t["x"], t["sh"], t["w"], g, t["src"], t["dst"], perm, rp, srp, **kw)
+            _, per_sb = time_launches(torch, lambda: sp.tp_src_rowptr_build(t["src"], perm, t["x"].shape[0], out=srp),
+                                      steps, args.warmup)
+            _, per_bw = time_launches(torch, fb, steps, args.warmup)
+            _, per_bwr = time_launches(torch, fbr, steps, args.warmup)
+            rec["backward"] = {"us_per_call_events": 1e3 * sum(per_bw) / len(per_bw),
+                               "rowptr_us_per_call_events": 1e3 * sum(per_bwr) / len(per_bwr),
+                               "src_rowptr_build_us": 1e3 * sum(per_sb) / len(per_sb),
+                               "what": "tp_conv_bwd (all launches of one call, HIP events), and "
+                                       "tp_conv_bwd_rowptr with both row pointers built once"}
+            del g, perm, gx, gsh, gw, ws, srp
         if n == 2:
             # HIP graph replay of 20 calls (the path has no memset or host work)
             t = sets[0]
