@@ -259,3 +259,43 @@ def test_shared_weights_backward(layout, dtype):
                                      grad_w=torch.full((1, h.weight_numel), 7.0, device="cuda"))
         torch.cuda.synchronize()
         assert torch.count_nonzero(dx).item() == 0 and torch.count_nonzero(dw).item() == 0
+
+
+@pytest.mark.parametrize("mul,layout,dtype,shared", [
+    (1, "ir_mul", "f32", False), (7, "mul_ir", "f64", False), (32, "ir_mul", "f32", True),
+    (19, "mul_ir", "f64", True), (32, "mul_ir", "f32", False),
+])
+def test_edge_parallel_small_multiplicities(mul, layout, dtype, shared):
+    """Multiplicities up to 32 take one edge per half-wave: an odd number of
+    edges (the last wave's second half idle), sources and destinations out
+    of range, isolated nodes, per-edge or shared weights, both layouts and
+    float64, against the oracle on the valid edges."""
+    sp = _sp()
+    in1, in2, filt = f"{mul}x0e+{mul}x1o+{mul}x2e", "0e+1o+2e+3o", "0e+1o+2e"
+    o = otp.ChannelwiseTP(in1, in2, filt)
+    h = sp.tp_create(in1, in2, filt, layout=layout, dtype=dtype, shared_weights=shared)
+    rng = np.random.default_rng(200 + mul)
+    n_src, n_dst, n_e = 23, 17, 301
+    src = rng.integers(0, n_src - 2, n_e)
+    src[::11] = n_src + 1                              # sources out of range
+    dst = np.sort(rng.integers(-1, n_dst + 1, n_e))    # destinations out of range at both ends
+    npd = np.float32 if dtype == "f32" else np.float64
+    rows = 1 if shared else n_e
+    inp = dict(x=rng.standard_normal((n_src, o.dim_in1)).astype(npd), sh=rng.standard_normal((n_e, o.dim_in2)).astype(npd),
+               w=rng.standard_normal((rows, o.weight_numel)).astype(npd),
+               src=src.astype(np.int32), dst=dst.astype(np.int32), n_nodes=n_dst)
+    g = workloads.output_gradient(n_dst, o.dim_out, dtype, seed=201)
+    announce(f"tp bwd edge-parallel mul={mul} {layout} {dtype} shared={shared}")
+    dx, dsh, dw = _bwd(sp, h, inp, g)
+    ok = (src < n_src) & (dst >= 0) & (dst < n_dst)
+    assert np.count_nonzero(dsh[~ok]) == 0
+    if not shared:
+        assert np.count_nonzero(dw[~ok]) == 0
+    sub = dict(inp, sh=inp["sh"][ok], src=inp["src"][ok], dst=inp["dst"][ok],
+               w=inp["w"] if shared else inp["w"][ok])
+    args = (sub["x"], sub["sh"], sub["w"], sub["src"], sub["dst"], n_dst, g)
+    ref = o.conv_vjp(*args, layout=layout, shared_weights=shared)
+    scale = o.conv_vjp(*args, layout=layout, shared_weights=shared, absolute=True)
+    check_scaled(dx, ref[0], scale[0], dtype, "edge-parallel dx")
+    check_scaled(dsh[ok], ref[1], scale[1], dtype, "edge-parallel dsh")
+    check_scaled(dw if shared else dw[ok], ref[2], scale[2], dtype, "edge-parallel dw")
