@@ -6,7 +6,8 @@ for bit (the same edges in the same order) on the specialised kernels
 (molecular batch, medium graph), the destination-split kernel and the
 table-driven kernel, with sum and mean, shared weights and both index
 widths; forward and backward are also checked against the float64 oracle
-(scaled error <= 1e-5)."""
+(scaled error <= 1e-5); at the large workload's full size the row-pointer
+forms match the searching ones bit for bit."""
 
 import numpy as np
 import pytest
@@ -243,3 +244,31 @@ def test_bwd_rowptr_validate():
     bad[4] -= 1
     with pytest.raises(sp.SegpolyError, match="-7"):
         sp.tp_conv_bwd_rowptr(h, x, s, w, g, src, dst, perm, rp, bad)
+
+
+def test_full_size_rowptr_equals_search():
+    """The large workload (600k edges, 20k nodes, ir_mul, two channels per
+    lane) in the benchmark's launch configuration: the row-pointer forward
+    and backward reproduce the searching ones bit for bit, and a sample of
+    destination rows matches the oracle."""
+    sp = _sp()
+    import torch
+    wl = workloads.WORKLOADS[4]
+    o = otp.ChannelwiseTP(wl.irreps_in1, wl.irreps_in2, wl.irreps_out)
+    h = sp.tp_create(wl.irreps_in1, wl.irreps_in2, wl.irreps_out, layout="ir_mul")
+    inp = workloads.tp_inputs(wl, o.weight_fan_in())
+    announce(f"rowptr full-size workload 4 ({h.kernel_name})")
+    a, b = _pair(sp, h, inp, torch.int32)
+    assert np.array_equal(a, b)
+    rng = np.random.default_rng(86)
+    nodes = np.unique(np.concatenate([[0, wl.n_nodes - 1], rng.integers(0, wl.n_nodes, 30)]))
+    sel = np.nonzero(np.isin(inp["dst"], nodes))[0]
+    args = (inp["x"], inp["sh"][sel], inp["w"][sel], inp["src"][sel], inp["dst"][sel], wl.n_nodes)
+    ref = o.conv(*args, layout="ir_mul")
+    scale = o.conv(*args, layout="ir_mul", absolute=True)
+    check_scaled(b[nodes], ref[nodes], scale[nodes], "f32", "rowptr full-size fwd")
+    del a, b
+    g = workloads.output_gradient(wl.n_nodes, h.dim_out, "f32", seed=87)
+    ga, gb = _bwd_pair(sp, h, inp, torch.int32, g)
+    for u, v in zip(ga, gb):
+        assert np.array_equal(u, v)
