@@ -915,7 +915,8 @@ def other_workloads(torch, sp, workloads, dev, args):
         wall, per = time_launches(torch, fwd, steps, args.warmup)
         rec = {"workload": wl.name, "layout": wl.layouts[0], "dtype": wl.dtype, "nodes": N, "edges": E,
                "kernel": h.kernel_name, "us_per_call": wall * 1e6 / steps,
-               "kernel_us_mean": 1e3 * sum(per) / len(per), "edges_per_s": E * steps / wall}
+               "kernel_us_mean": 1e3 * sum(per) / len(per), "kernel_us_median": 1e3 * per[len(per) // 2],
+               "edges_per_s": E * steps / wall}
         if n == 3:
             b = E * (h.weight_numel + h.dim_in2 + 2) * 4 + N * (h.dim_in1 + h.dim_out) * 4
             rec["cold_input_sets"] = len(sets)
@@ -932,6 +933,7 @@ def other_workloads(torch, sp, workloads, dev, args):
             wall_r, per_r = time_launches(torch, fr, steps, args.warmup)
             rec["rowptr"] = {"build_kernel_us_mean": 1e3 * sum(per_b) / len(per_b),
                              "kernel_us_mean": 1e3 * sum(per_r) / len(per_r),
+                             "kernel_us_median": 1e3 * per_r[len(per_r) // 2],
                              "us_per_call": wall_r * 1e6 / steps, "edges_per_s": E * steps / wall_r,
                              "what": "tp_conv_fwd_rowptr with row pointers built once (input set 0, warm)"}
             # backward on the same graph: with the in-kernel searches, and
@@ -949,7 +951,9 @@ def other_workloads(torch, sp, workloads, dev, args):
             _, per_bw = time_launches(torch, fb, steps, args.warmup)
             _, per_bwr = time_launches(torch, fbr, steps, args.warmup)
             rec["backward"] = {"us_per_call_events": 1e3 * sum(per_bw) / len(per_bw),
+                               "us_per_call_events_median": 1e3 * per_bw[len(per_bw) // 2],
                                "rowptr_us_per_call_events": 1e3 * sum(per_bwr) / len(per_bwr),
+                               "rowptr_us_per_call_events_median": 1e3 * per_bwr[len(per_bwr) // 2],
                                "src_rowptr_build_us": 1e3 * sum(per_sb) / len(per_sb),
                                "what": "tp_conv_bwd (all launches of one call, HIP events), and "
                                        "tp_conv_bwd_rowptr with both row pointers built once"}
