@@ -299,3 +299,30 @@ def test_edge_parallel_small_multiplicities(mul, layout, dtype, shared):
     check_scaled(dx, ref[0], scale[0], dtype, "edge-parallel dx")
     check_scaled(dsh[ok], ref[1], scale[1], dtype, "edge-parallel dsh")
     check_scaled(dw if shared else dw[ok], ref[2], scale[2], dtype, "edge-parallel dw")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f64"])
+def test_batch_mode_shared_weights_small_multiplicity(dtype):
+    """Batch mode (edge e is node e and source e, no indices) with one shared
+    weight row at 8 channels: the edge-parallel kernel writes per-edge weight
+    gradients that are summed in fixed chunks; 2,500 samples (three chunks,
+    the last ragged) and more source rows than samples."""
+    sp = _sp()
+    in1, in2, filt = "8x0e+8x1o", "0e+1o+2e", "0e+1o+2e"
+    o = otp.ChannelwiseTP(in1, in2, filt)
+    h = sp.tp_create(in1, in2, filt, layout="mul_ir", dtype=dtype, shared_weights=True)
+    rng = np.random.default_rng(210)
+    npd = np.float32 if dtype == "f32" else np.float64
+    n, n_src = 2500, 2600
+    inp = dict(x=rng.standard_normal((n_src, o.dim_in1)).astype(npd), sh=rng.standard_normal((n, o.dim_in2)).astype(npd),
+               w=rng.standard_normal((1, o.weight_numel)).astype(npd), src=None, dst=None, n_nodes=n)
+    g = workloads.output_gradient(n, o.dim_out, dtype, seed=211)
+    announce(f"tp bwd batch mode shared weights {dtype}")
+    dx, dsh, dw = _bwd(sp, h, inp, g)
+    assert np.count_nonzero(dx[n:]) == 0          # source rows past the batch receive nothing
+    args = (inp["x"][:n], inp["sh"], inp["w"], None, None, n, g)
+    ref = o.conv_vjp(*args, layout="mul_ir", shared_weights=True)
+    scale = o.conv_vjp(*args, layout="mul_ir", shared_weights=True, absolute=True)
+    check_scaled(dx[:n], ref[0], scale[0], dtype, "batch shared dx")
+    check_scaled(dsh, ref[1], scale[1], dtype, "batch shared dsh")
+    check_scaled(dw, ref[2], scale[2], dtype, "batch shared dw")
